@@ -1,0 +1,182 @@
+"""fp64 CPU oracle for the selective scan and the single-token decode step.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The product path
+(``selective_state_space_52_amd``) never imports it and shares no code with it.
+
+The arithmetic lives in ``mssm_oracle.c`` (plain C, fp64, sequential in time);
+this module only compiles it with gcc and marshals numpy arrays through ctypes.
+What the C code computes, and which passage of the pages each step follows, is
+written at the top of that file.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "mssm_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libmssm_oracle.so")
+_D = ctypes.POINTER(ctypes.c_double)
+
+
+def compile_source(src: str, out_path: str) -> str:
+    """Compile an oracle C source with gcc (no fast-math, no FMA contraction)."""
+    tmp = out_path + ".tmp"
+    cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+           "-shared", "-fPIC", "-std=c99", src, "-o", tmp, "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(tmp, out_path)
+    return out_path
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle/mssm_oracle.c into oracle/libmssm_oracle.so."""
+    if force or not os.path.exists(_LIB_PATH):
+        compile_source(SOURCE, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _open(path):
+    lib = ctypes.CDLL(path)
+    i64, cint = ctypes.c_int64, ctypes.c_int
+    lib.mssm_oracle_scan.argtypes = [i64, i64, i64, i64, _D, _D, _D, _D, _D,
+                                     _D, _D, _D, cint, _D, _D, _D, cint]
+    lib.mssm_oracle_scan.restype = cint
+    lib.mssm_oracle_state_update.argtypes = [i64, i64, i64, _D, _D, _D, _D, _D,
+                                             _D, _D, _D, _D, cint, _D, cint]
+    lib.mssm_oracle_state_update.restype = cint
+    lib.mssm_oracle_scan_row.argtypes = [i64, i64, _D, _D, _D, _D, _D, _D,
+                                         ctypes.c_double, ctypes.c_double,
+                                         cint, _D, _D, _D]
+    lib.mssm_oracle_scan_row.restype = None
+    return lib
+
+
+def _f64(a):
+    """Exact fp64 copy of a numpy array or a CPU torch tensor (bf16 included)."""
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor
+        import torch
+        a = a.detach().to("cpu", torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_D)
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+class Oracle:
+    """The oracle's entry points bound to one compiled library."""
+
+    def __init__(self, lib_path=None):
+        if lib_path is None:
+            lib_path = _LIB_PATH
+            if not os.path.exists(lib_path):
+                build(force=True)
+        self.lib_path = lib_path
+        self._lib = _open(lib_path)
+
+    def scan(self, u, delta, A, B, C, D=None, z=None, delta_bias=None,
+             softplus=True, h0=None, nthreads=None):
+        """Selective scan in fp64.
+
+        u, delta, z: (batch, dim, L); B, C: (batch, L, N); A: (dim, N);
+        D, delta_bias: (dim,); h0: (batch, dim, N) or None.
+        Returns (out (batch, dim, L), last_state (batch, dim, N)), both fp64.
+        """
+        u, delta, A, B, C = map(_f64, (u, delta, A, B, C))
+        D, z, delta_bias, h0 = map(_f64, (D, z, delta_bias, h0))
+        batch, dim, L = u.shape
+        N = A.shape[1]
+        assert delta.shape == u.shape and A.shape == (dim, N)
+        assert B.shape == (batch, L, N) and C.shape == (batch, L, N)
+        assert z is None or z.shape == u.shape
+        assert D is None or D.shape == (dim,)
+        assert delta_bias is None or delta_bias.shape == (dim,)
+        assert h0 is None or h0.shape == (batch, dim, N)
+        out = np.empty((batch, dim, L), dtype=np.float64)
+        last = np.empty((batch, dim, N), dtype=np.float64)
+        rc = self._lib.mssm_oracle_scan(
+            batch, dim, N, L, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+            _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)), _ptr(h0),
+            _ptr(out), _ptr(last), int(nthreads or default_threads()))
+        if rc != 0:
+            raise ValueError("oracle: unsupported dstate %d" % N)
+        return out, last
+
+    def scan_row(self, u, delta, A_row, B_b, C_b, D_d=0.0, z=None, bias_d=0.0,
+                 softplus=True, h0=None):
+        """One (batch, channel) row in fp64: u, delta, z of length L; A_row
+        (N,); B_b, C_b (L, N).  Returns (out (L,), last_state (N,))."""
+        u, delta, A_row, B_b, C_b, z, h0 = map(
+            _f64, (u, delta, A_row, B_b, C_b, z, h0))
+        L, N = u.shape[0], A_row.shape[0]
+        assert B_b.shape == (L, N) and C_b.shape == (L, N)
+        out = np.empty(L, dtype=np.float64)
+        last = np.empty(N, dtype=np.float64)
+        self._lib.mssm_oracle_scan_row(
+            L, N, _ptr(u), _ptr(delta), _ptr(z), _ptr(A_row), _ptr(B_b),
+            _ptr(C_b), float(D_d), float(bias_d), int(bool(softplus)),
+            _ptr(h0), _ptr(out), _ptr(last))
+        return out, last
+
+    def state_update(self, state, x, dt, A, B, C, D=None, z=None,
+                     dt_bias=None, softplus=True, nthreads=None):
+        """Single-token decode step in fp64.
+
+        state: (batch, dim, N); x, dt, z: (batch, dim); B, C: (batch, N).
+        Returns (out (batch, dim), new_state (batch, dim, N)); the inputs are
+        left untouched.
+        """
+        st = _f64(state).copy()
+        x, dt, A, B, C, D, z, dt_bias = map(
+            _f64, (x, dt, A, B, C, D, z, dt_bias))
+        batch, dim, N = st.shape
+        assert x.shape == (batch, dim) and dt.shape == (batch, dim)
+        assert A.shape == (dim, N) and B.shape == (batch, N)
+        assert C.shape == (batch, N)
+        out = np.empty((batch, dim), dtype=np.float64)
+        rc = self._lib.mssm_oracle_state_update(
+            batch, dim, N, _ptr(st), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+            _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), int(bool(softplus)),
+            _ptr(out), int(nthreads or default_threads()))
+        if rc != 0:
+            raise ValueError("oracle: unsupported dstate %d" % N)
+        return out, st
+
+
+_default = None
+
+
+def _get():
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def scan(*args, **kwargs):
+    """Selective scan in fp64 (see Oracle.scan)."""
+    return _get().scan(*args, **kwargs)
+
+
+def scan_row(*args, **kwargs):
+    """One row of the scan in fp64 (see Oracle.scan_row)."""
+    return _get().scan_row(*args, **kwargs)
+
+
+def state_update(*args, **kwargs):
+    """Single-token decode step in fp64 (see Oracle.state_update)."""
+    return _get().state_update(*args, **kwargs)

@@ -1,0 +1,175 @@
+/*
+ * mssm_oracle.c -- fp64 CPU oracle for the selective scan and its
+ * single-token decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * bench's CPU-baseline leg may load this library.  The product path (the HIP
+ * library under selective_state_space_52_amd/) shares no code with it and
+ * never calls it.
+ *
+ * What is computed, and where it comes from:
+ *
+ *   - The continuous model h'(t) = A h(t) + B x(t), y(t) = C h(t) + D x(t)
+ *     (page "Mamba: Selective State Space Models", section "Mathematical
+ *     Foundation / State Space Model").  D enters as a skip term on the input.
+ *   - B, C and the step size Delta depend on the token; Delta is the
+ *     activation tau_Delta applied to (parameter + projection)
+ *     (same page, "Mathematical Foundation / Selective Mechanism").  The
+ *     parameter is the per-channel delta_bias below; tau_Delta is read as
+ *     softplus(x) = log(1 + e^x) and may be switched off.
+ *   - Delta drives the discretisation (same page, "Architecture").  The pages
+ *     do not write the discrete rule out.  Reading used here: zero-order hold
+ *     on A and an Euler step on B, i.e.
+ *         h_t[n] = exp(Delta_t * A[n]) * h_{t-1}[n] + Delta_t * B_t[n] * u_t
+ *         y_t    = sum_n C_t[n] * h_t[n] + D * u_t
+ *     with y_t read from the state AFTER token t has been absorbed.
+ *   - The output is gated by silu(z) = z / (1 + e^-z); the skip term sits
+ *     inside the gate (same page, "Features": the block is gated).
+ *   - Inference runs the recurrence token by token with a fixed-size state
+ *     (same page, "Mathematical Foundation / Efficient Scan", sequential
+ *     scan with constant memory).  This file is that sequential form, plain
+ *     and in fp64.  The parallel scan of the same page reaches the same
+ *     result up to rounding order, so no parallel form is needed here.
+ *
+ * Layouts (row-major, last index fastest), for one call:
+ *   u, delta, z, out : (batch, dim, seqlen)
+ *   B, C             : (batch, seqlen, dstate)   one N-vector per token
+ *   A                : (dim, dstate)
+ *   D, delta_bias    : (dim)
+ *   h0, last_state   : (batch, dim, dstate)
+ *
+ * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+/* tau_Delta = softplus, evaluated without a large-x threshold.  For x > 0
+ * the form x + log1p(e^-x) avoids overflow; for x <= 0 log1p(e^x) keeps
+ * relative accuracy when e^x is tiny. */
+static double oracle_softplus(double x)
+{
+    if (x > 0.0)
+        return x + log1p(exp(-x));
+    return log1p(exp(x));
+}
+
+/* silu(z) = z * sigmoid(z) */
+static double oracle_silu(double z)
+{
+    return z / (1.0 + exp(-z));
+}
+
+/*
+ * One (batch, channel) row of the scan.
+ *   u, delta, z, out : seqlen values of this row (z may be NULL: no gate)
+ *   A_row            : dstate values A[d, :]
+ *   B_b, C_b         : (seqlen, dstate) for this row's batch entry
+ *   D_d, bias_d      : the channel's skip weight and delta bias
+ *   h0               : dstate initial state, or NULL for zero
+ *   last_state       : dstate final state, or NULL
+ * h0 and last_state may point to the same memory.
+ */
+void mssm_oracle_scan_row(int64_t seqlen, int64_t dstate,
+                          const double *u, const double *delta,
+                          const double *z, const double *A_row,
+                          const double *B_b, const double *C_b,
+                          double D_d, double bias_d, int softplus,
+                          const double *h0, double *out,
+                          double *last_state)
+{
+    double h[64];
+    int64_t n, t;
+    for (n = 0; n < dstate; ++n)
+        h[n] = h0 ? h0[n] : 0.0;
+
+    for (t = 0; t < seqlen; ++t) {
+        double x = delta[t] + bias_d;
+        double dt = softplus ? oracle_softplus(x) : x;
+        double y = 0.0;
+        for (n = 0; n < dstate; ++n) {
+            double decay = exp(dt * A_row[n]);            /* Abar = exp(Delta A) */
+            double drive = dt * B_b[t * dstate + n] * u[t]; /* Bbar u = Delta B u */
+            h[n] = decay * h[n] + drive;
+            y += C_b[t * dstate + n] * h[n];
+        }
+        y += D_d * u[t];
+        out[t] = z ? y * oracle_silu(z[t]) : y;
+    }
+
+    if (last_state)
+        for (n = 0; n < dstate; ++n)
+            last_state[n] = h[n];
+}
+
+/*
+ * Whole scan.  D, z, delta_bias and h0 may be NULL (zero skip, no gate, zero
+ * bias, zero initial state).  last_state may be NULL.  Rows are independent,
+ * so they are spread over nthreads OpenMP threads (nthreads <= 0: default).
+ * Returns 0, or -1 if dstate is outside 1..64.
+ */
+int mssm_oracle_scan(int64_t batch, int64_t dim, int64_t dstate,
+                     int64_t seqlen, const double *u, const double *delta,
+                     const double *A, const double *B, const double *C,
+                     const double *D, const double *z,
+                     const double *delta_bias, int softplus,
+                     const double *h0, double *out, double *last_state,
+                     int nthreads)
+{
+    int64_t rows = batch * dim;
+    int64_t r;
+    if (dstate < 1 || dstate > 64)
+        return -1;
+    if (nthreads <= 0)
+        nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (r = 0; r < rows; ++r) {
+        int64_t b = r / dim, d = r % dim;
+        size_t row = (size_t)r * (size_t)seqlen;
+        size_t bc = (size_t)b * (size_t)seqlen * (size_t)dstate;
+        mssm_oracle_scan_row(seqlen, dstate, u + row, delta + row,
+                             z ? z + row : NULL, A + d * dstate, B + bc,
+                             C + bc, D ? D[d] : 0.0,
+                             delta_bias ? delta_bias[d] : 0.0, softplus,
+                             h0 ? h0 + r * dstate : NULL, out + row,
+                             last_state ? last_state + r * dstate : NULL);
+    }
+    return 0;
+}
+
+/*
+ * Single-token decode step: the scan above with seqlen = 1, starting from
+ * `state` and writing the new state back into it (the fixed-size state that
+ * inference carries from token to token).
+ *   state            : (batch, dim, dstate), in/out
+ *   x, dt, z, out    : (batch, dim)
+ *   B, C             : (batch, dstate)
+ *   A                : (dim, dstate);  D, dt_bias : (dim)
+ */
+int mssm_oracle_state_update(int64_t batch, int64_t dim, int64_t dstate,
+                             double *state, const double *x,
+                             const double *dt, const double *A,
+                             const double *B, const double *C,
+                             const double *D, const double *z,
+                             const double *dt_bias, int softplus,
+                             double *out, int nthreads)
+{
+    int64_t rows = batch * dim;
+    int64_t r;
+    if (dstate < 1 || dstate > 64)
+        return -1;
+    if (nthreads <= 0)
+        nthreads = 1;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (r = 0; r < rows; ++r) {
+        int64_t b = r / dim, d = r % dim;
+        double *h = state + r * dstate;
+        mssm_oracle_scan_row(1, dstate, x + r, dt + r, z ? z + r : NULL,
+                             A + d * dstate, B + b * dstate, C + b * dstate,
+                             D ? D[d] : 0.0, dt_bias ? dt_bias[d] : 0.0,
+                             softplus, h, out + r, h);
+    }
+    return 0;
+}
+
+int mssm_oracle_version(void) { return 1; }

@@ -1,0 +1,335 @@
+"""Pins that tie the fp64 oracle to something other than itself.
+
+Each pin takes an ``oracle.Oracle`` and raises AssertionError when the oracle
+disagrees with a value fixed by mathematics: a hand-evaluated tiny case, a
+closed form (geometric series, convolution, step response), a library routine
+(numpy.convolve, numpy.logaddexp, scipy.special.expit), a brute-force
+"materialised" evaluation that sums every path through the recurrence
+explicitly, or an invariant (split/carry, linearity, causality, permutation).
+
+The method being pinned (the reading the oracle follows):
+  Delta_t = softplus(delta_t + bias)          (or delta_t + bias, softplus off)
+  h_t[n]  = exp(Delta_t A[n]) h_{t-1}[n] + Delta_t B_t[n] u_t
+  out_t   = (sum_n C_t[n] h_t[n] + D u_t) * silu(z_t)
+from page "Mamba: Selective State Space Models", "Mathematical Foundation"
+(continuous model, selective mechanism, sequential scan) and "Architecture"
+(Delta as the discretisation step).
+
+The pins are written so that each plausible slip in the oracle -- a dropped
+skip term, the readout taken before the update, the bias added after the
+softplus, a flipped sign on A, B and C swapped, a transposed B index, a missing
+or misplaced gate, an ignored initial state, another discretisation rule, a
+wrong activation, a lost last_state, decode wiring mistakes -- fails at least
+one of them; ``test_oracle_mutants.py`` checks exactly that by compiling such
+variants of the oracle.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import expit
+
+LN2 = math.log(2.0)
+
+
+def _close(got, want, rtol=1e-13, atol=1e-13, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    err = np.abs(got - want)
+    bound = atol + rtol * np.abs(want)
+    bad = err > bound
+    assert not bad.any(), "%s: max err %.3e (worst got %r want %r)" % (
+        what, float(err.max()), got[bad].ravel()[:3], want[bad].ravel()[:3])
+
+
+def _row_inputs(L, N, delta, A, B, C, u, D=0.0, bias=0.0):
+    """Build a batch=1, dim=1 problem from per-row values."""
+    u = np.asarray(u, dtype=np.float64).reshape(1, 1, L)
+    delta = np.asarray(delta, dtype=np.float64).reshape(1, 1, L)
+    A = np.asarray(A, dtype=np.float64).reshape(1, N)
+    B = np.asarray(B, dtype=np.float64).reshape(1, L, N)
+    C = np.asarray(C, dtype=np.float64).reshape(1, L, N)
+    return dict(u=u, delta=delta, A=A, B=B, C=C, D=np.array([D]),
+                delta_bias=np.array([bias]))
+
+
+# ---------------------------------------------------------------- hand cases
+
+def pin_h1_time_varying_delta(orc):
+    """Delta = (1, 0.5, 0.25, 2) given directly, A = -1, B = C = u = 1, D = 0.
+    Hand evaluation of the state after each token."""
+    d = [1.0, 0.5, 0.25, 2.0]
+    args = _row_inputs(4, 1, d, [-1.0], np.ones((4, 1)), np.ones((4, 1)),
+                       np.ones(4))
+    out, last = orc.scan(**args, softplus=False)
+    h1 = 1.0                               # 0 * e^-1 + 1
+    h2 = math.exp(-0.5) * h1 + 0.5
+    h3 = math.exp(-0.25) * h2 + 0.25
+    h4 = math.exp(-2.0) * h3 + 2.0
+    _close(out.ravel(), [h1, h2, h3, h4], what="h1 out")
+    _close(last.ravel(), [h4], what="h1 last_state")
+
+
+def pin_h2_softplus_gate_skip(orc):
+    """softplus(0) = ln 2 so exp(Delta A) = 1/2 for A = -1; B = 2, u = 1 gives
+    a drive of 2 ln 2 per token and the state is the geometric series
+    h_t = 4 ln2 (1 - 2^-(t+1)).  C = 1, D = 0.5, z = 2:
+    out_t = (h_t + 0.5) * 2 / (1 + e^-2)."""
+    L = 6
+    args = _row_inputs(L, 1, np.zeros(L), [-1.0], 2 * np.ones((L, 1)),
+                       np.ones((L, 1)), np.ones(L), D=0.5)
+    z = 2.0 * np.ones((1, 1, L))
+    out, last = orc.scan(**args, z=z, softplus=True)
+    t = np.arange(L)
+    h = 4 * LN2 * (1 - 0.5 ** (t + 1))
+    gate = 2.0 / (1.0 + math.exp(-2.0))
+    _close(out.ravel(), (h + 0.5) * gate, what="h2 out")
+    _close(last.ravel(), [h[-1]], what="h2 last_state")
+
+
+def pin_h3_zero_b_loaded_state(orc):
+    """B = 0 with a loaded state h0 = (1, -2), A = (-1, -3), C = (1, 1),
+    Delta = (0.5, 0.25, 0.25), u = (1, 2, 3), D = 0.5, softplus off:
+    y_t = e^-S_t - 2 e^-3S_t + 0.5 u_t with S_t the running sum of Delta."""
+    args = _row_inputs(3, 2, [0.5, 0.25, 0.25], [-1.0, -3.0],
+                       np.zeros((3, 2)), np.ones((3, 2)), [1.0, 2.0, 3.0],
+                       D=0.5)
+    h0 = np.array([1.0, -2.0]).reshape(1, 1, 2)
+    out, last = orc.scan(**args, softplus=False, h0=h0)
+    S = np.array([0.5, 0.75, 1.0])
+    y = np.exp(-S) - 2 * np.exp(-3 * S) + 0.5 * np.array([1.0, 2.0, 3.0])
+    _close(out.ravel(), y, what="h3 out")
+    _close(last.ravel(), [math.exp(-1.0), -2 * math.exp(-3.0)],
+           what="h3 last_state")
+
+
+def pin_h4_bias_inside_softplus(orc):
+    """One token, A = -1, B = C = u = 1, D = 0, no gate, so y = Delta.
+    delta = 0.5 with bias -0.5 must give softplus(0) = ln 2 (the bias is added
+    before the activation); delta = -30 gives log(1 + e^-30), evaluated from
+    its series e^-30 - e^-60/2; delta = 30 gives 30 + e^-30 - e^-60/2."""
+    for delta, bias, want in [
+            (0.5, -0.5, LN2),
+            (-30.0, 0.0, math.exp(-30) - math.exp(-60) / 2),
+            (30.0, 0.0, 30.0 + math.exp(-30) - math.exp(-60) / 2)]:
+        args = _row_inputs(1, 1, [delta], [-1.0], [[1.0]], [[1.0]], [1.0],
+                           bias=bias)
+        out, _ = orc.scan(**args, softplus=True)
+        _close(out.ravel(), [want], rtol=1e-14, atol=0.0,
+               what="softplus(%g%+g)" % (delta, bias))
+
+
+# ------------------------------------------------------------ closed forms
+
+def pin_lti_convolution(orc):
+    """Constant Delta, B, C over time make the scan time-invariant: the output
+    is D u plus the causal convolution of u with the kernel
+    K_k = sum_n C[n] exp(k Delta A[n]) Delta B[n]  (numpy.convolve).
+    Run with Delta given directly and with Delta = softplus(x + bias), the
+    latter evaluated with numpy.logaddexp(0, .)."""
+    rng = np.random.default_rng(11)
+    L, N = 50, 5
+    A = -rng.uniform(0.2, 3.0, N)
+    Bv = rng.standard_normal(N)
+    Cv = rng.standard_normal(N)
+    u = rng.standard_normal(L)
+    D = 0.7
+    for softplus, raw, bias in [(False, 0.3, 0.0), (True, -0.4, -1.1)]:
+        dt = float(np.logaddexp(0.0, raw + bias)) if softplus else raw + bias
+        args = _row_inputs(L, N, raw * np.ones(L), A, np.tile(Bv, (L, 1)),
+                           np.tile(Cv, (L, 1)), u, D=D, bias=bias)
+        out, _ = orc.scan(**args, softplus=softplus)
+        k = np.arange(L)
+        K = (Cv[None, :] * np.exp(np.outer(k, dt * A)) * dt * Bv[None, :]).sum(1)
+        want = D * u + np.convolve(u, K)[:L]
+        _close(out.ravel(), want, rtol=1e-12, atol=1e-12,
+               what="lti conv softplus=%s" % softplus)
+
+
+def pin_step_response(orc):
+    """Constant u as well: every state component follows the geometric step
+    response h_t[n] = Delta B[n] u (1 - a^(t+1)) / (1 - a), a = exp(Delta A[n])."""
+    rng = np.random.default_rng(12)
+    L, N = 37, 6
+    A = -rng.uniform(0.1, 2.0, N)
+    Bv = rng.standard_normal(N)
+    dt, u = 0.45, 1.3
+    args = _row_inputs(L, N, dt * np.ones(L), A, np.tile(Bv, (L, 1)),
+                       np.ones((L, N)), u * np.ones(L))
+    _, last = orc.scan(**args, softplus=False)
+    a = np.exp(dt * A)
+    want = dt * Bv * u * (1 - a ** L) / (1 - a)
+    _close(last.ravel(), want, rtol=1e-12, atol=1e-14, what="step response")
+
+
+def pin_zero_b(orc):
+    """B = 0 and a zero initial state: the state stays exactly 0 and
+    out = D u silu(z), silu via scipy.special.expit."""
+    rng = np.random.default_rng(13)
+    batch, dim, L, N = 2, 3, 17, 4
+    u = rng.standard_normal((batch, dim, L))
+    z = rng.standard_normal((batch, dim, L))
+    D = rng.standard_normal(dim)
+    out, last = orc.scan(u=u, delta=rng.standard_normal((batch, dim, L)),
+                         A=-rng.uniform(0.5, 2, (dim, N)),
+                         B=np.zeros((batch, L, N)),
+                         C=rng.standard_normal((batch, L, N)), D=D, z=z,
+                         delta_bias=rng.standard_normal(dim), softplus=True)
+    want = D[None, :, None] * u * z * expit(z)
+    _close(out, want, rtol=1e-14, atol=0.0, what="zero-B out")
+    assert np.all(last == 0.0), "zero-B last_state not exactly 0"
+
+
+def materialised(u, delta, A, B, C, D, z, bias, softplus, h0):
+    """Brute force: every output as an explicit sum over all earlier tokens,
+    h_t[n] = exp(A[n] S_t) h0[n] + sum_{s<=t} exp(A[n](S_t - S_s)) Delta_s
+    B_s[n] u_s with S_t the running sum of Delta.  O(L^2 N) per row."""
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    x = delta + bias[None, :, None]
+    dts = np.logaddexp(0.0, x) if softplus else x
+    out = np.empty_like(u)
+    last = np.empty((batch, dim, N))
+    for b in range(batch):
+        for d in range(dim):
+            dt = dts[b, d]
+            S = np.cumsum(dt)
+            for t in range(L):
+                h = np.exp(A[d] * S[t]) * h0[b, d]
+                for s in range(t + 1):
+                    h = h + np.exp(A[d] * (S[t] - S[s])) * dt[s] * B[b, s] * u[b, d, s]
+                y = float(C[b, t] @ h) + D[d] * u[b, d, t]
+                out[b, d, t] = y * z[b, d, t] * expit(z[b, d, t])
+                if t == L - 1:
+                    last[b, d] = h
+    return out, last
+
+
+def random_case(seed, batch=2, dim=3, L=24, N=4):
+    rng = np.random.default_rng(seed)
+    return dict(
+        u=rng.standard_normal((batch, dim, L)),
+        delta=rng.standard_normal((batch, dim, L)) - 1.0,
+        A=-rng.uniform(0.2, 4.0, (dim, N)),
+        B=rng.standard_normal((batch, L, N)),
+        C=rng.standard_normal((batch, L, N)),
+        D=rng.standard_normal(dim),
+        z=rng.standard_normal((batch, dim, L)),
+        delta_bias=rng.uniform(-2.0, 0.5, dim),
+    ), 0.5 * rng.standard_normal((batch, dim, N))
+
+
+def pin_materialised(orc):
+    """The general case (softplus, bias, gate, skip, loaded state, batch > 1
+    with a different B and C per batch entry) against the brute-force sum."""
+    for softplus in (True, False):
+        args, h0 = random_case(21 + softplus)
+        out, last = orc.scan(**args, softplus=softplus, h0=h0)
+        w_out, w_last = materialised(args["u"], args["delta"], args["A"],
+                                     args["B"], args["C"], args["D"],
+                                     args["z"], args["delta_bias"], softplus,
+                                     h0)
+        _close(out, w_out, rtol=1e-11, atol=1e-12, what="materialised out")
+        _close(last, w_last, rtol=1e-11, atol=1e-12, what="materialised last")
+
+
+# -------------------------------------------------------------- invariants
+
+def pin_split_carry(orc):
+    """Scanning tokens [0, s) and then [s, L) from the carried last_state
+    reproduces the unsplit scan, for every split point s."""
+    args, h0 = random_case(31, batch=1, dim=2, L=40, N=3)
+    out, last = orc.scan(**args, softplus=True, h0=h0)
+    for s in range(1, 40):
+        a1 = dict(args, u=args["u"][..., :s], delta=args["delta"][..., :s],
+                  z=args["z"][..., :s], B=args["B"][:, :s], C=args["C"][:, :s])
+        a2 = dict(args, u=args["u"][..., s:], delta=args["delta"][..., s:],
+                  z=args["z"][..., s:], B=args["B"][:, s:], C=args["C"][:, s:])
+        o1, l1 = orc.scan(**a1, softplus=True, h0=h0)
+        o2, l2 = orc.scan(**a2, softplus=True, h0=l1)
+        _close(np.concatenate([o1, o2], axis=-1), out, rtol=1e-13, atol=1e-14,
+               what="split at %d" % s)
+        _close(l2, last, rtol=1e-13, atol=1e-14, what="split last at %d" % s)
+
+
+def pin_limits(orc):
+    """Delta = 0 freezes the state: y = C_t . h0 + D u.  A = -1e4 makes
+    exp(Delta A) underflow to 0: y = Delta u (C_t . B_t) + D u."""
+    args, h0 = random_case(41, batch=1, dim=2, L=9, N=3)
+    a0 = dict(args, delta=np.zeros_like(args["delta"]),
+              delta_bias=np.zeros(2), z=None)
+    out, last = orc.scan(**a0, softplus=False, h0=h0)
+    want = (np.einsum("tn,dn->dt", args["C"][0], h0[0])
+            + args["D"][:, None] * args["u"][0])
+    _close(out[0], want, rtol=1e-14, atol=1e-14, what="Delta=0 out")
+    _close(last, h0, rtol=0, atol=0, what="Delta=0 last")
+    a1 = dict(args, A=-1e4 * np.ones_like(args["A"]), z=None,
+              delta=np.abs(args["delta"]) + 0.1, delta_bias=np.zeros(2))
+    out, _ = orc.scan(**a1, softplus=False, h0=h0)
+    dt = a1["delta"][0]
+    cb = np.einsum("tn,tn->t", args["C"][0], args["B"][0])
+    want = dt * args["u"][0] * cb[None, :] + args["D"][:, None] * args["u"][0]
+    _close(out[0], want, rtol=1e-13, atol=1e-14, what="A=-1e4 out")
+
+
+def pin_linearity_causality(orc):
+    """u -> out is linear for fixed delta, B, C, z (zero initial state), and a
+    change of u at token t0 leaves every earlier output untouched."""
+    args, _ = random_case(51, L=20)
+    rng = np.random.default_rng(52)
+    u1, u2 = args["u"], rng.standard_normal(args["u"].shape)
+    o1, _ = orc.scan(**args, softplus=True)
+    o2, _ = orc.scan(**dict(args, u=u2), softplus=True)
+    o3, _ = orc.scan(**dict(args, u=2.5 * u1 - 1.5 * u2), softplus=True)
+    _close(o3, 2.5 * o1 - 1.5 * o2, rtol=1e-12, atol=1e-12, what="linearity")
+    u4 = u1.copy()
+    u4[..., 11] += 3.0
+    o4, _ = orc.scan(**dict(args, u=u4), softplus=True)
+    assert np.array_equal(o4[..., :11], o1[..., :11]), "causality"
+    assert not np.allclose(o4[..., 11:], o1[..., 11:]), "u change had no effect"
+
+
+def pin_channel_permutation(orc):
+    """Permuting channels together with A, D and the bias permutes the output."""
+    args, h0 = random_case(61, dim=5, L=12)
+    out, last = orc.scan(**args, softplus=True, h0=h0)
+    p = np.array([3, 0, 4, 1, 2])
+    pa = dict(args, u=args["u"][:, p], delta=args["delta"][:, p],
+              z=args["z"][:, p], A=args["A"][p], D=args["D"][p],
+              delta_bias=args["delta_bias"][p])
+    o2, l2 = orc.scan(**pa, softplus=True, h0=h0[:, p])
+    assert np.array_equal(o2, out[:, p]) and np.array_equal(l2, last[:, p])
+
+
+def pin_decode_equals_scan(orc):
+    """L single-token decode steps from h0 reproduce the scan's outputs and
+    last_state: the sequential inference form of the same recurrence."""
+    args, h0 = random_case(71, batch=2, dim=3, L=15, N=4)
+    out, last = orc.scan(**args, softplus=True, h0=h0)
+    state = h0.copy()
+    for t in range(15):
+        y, state = orc.state_update(
+            state, args["u"][..., t], args["delta"][..., t], args["A"],
+            args["B"][:, t], args["C"][:, t], D=args["D"],
+            z=args["z"][..., t], dt_bias=args["delta_bias"], softplus=True)
+        _close(y, out[..., t], rtol=1e-15, atol=1e-15, what="decode t=%d" % t)
+    _close(state, last, rtol=1e-15, atol=1e-15, what="decode state")
+
+
+PINS = [
+    pin_h1_time_varying_delta,
+    pin_h2_softplus_gate_skip,
+    pin_h3_zero_b_loaded_state,
+    pin_h4_bias_inside_softplus,
+    pin_lti_convolution,
+    pin_step_response,
+    pin_zero_b,
+    pin_materialised,
+    pin_split_carry,
+    pin_limits,
+    pin_linearity_causality,
+    pin_channel_permutation,
+    pin_decode_equals_scan,
+]

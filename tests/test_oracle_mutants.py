@@ -1,0 +1,61 @@
+"""Plants plausible mistakes in copies of the oracle (on the CPU) and checks
+that the pins catch every one of them."""
+import os
+
+import pytest
+
+import oracle
+from tests.oracle_pins import PINS
+
+# (name, original text, mutated text) applied to oracle/mssm_oracle.c
+MUTANTS = [
+    ("drop_skip", "y += D_d * u[t];", "y += 0.0 * D_d * u[t];"),
+    ("readout_before_update",
+     "h[n] = decay * h[n] + drive;\n            y += C_b[t * dstate + n] * h[n];",
+     "y += C_b[t * dstate + n] * h[n];\n            h[n] = decay * h[n] + drive;"),
+    ("bias_after_softplus",
+     "double x = delta[t] + bias_d;\n        double dt = softplus ? oracle_softplus(x) : x;",
+     "double x = delta[t];\n        double dt = (softplus ? oracle_softplus(x) : x) + bias_d;"),
+    ("flipped_A_sign", "exp(dt * A_row[n])", "exp(-dt * A_row[n])"),
+    ("B_C_swapped", ["dt * B_b[t * dstate + n] * u[t]", "y += C_b[t * dstate + n]"],
+     ["dt * C_b[t * dstate + n] * u[t]", "y += B_b[t * dstate + n]"]),
+    ("B_transposed_index", "dt * B_b[t * dstate + n]", "dt * B_b[n * seqlen + t]"),
+    ("no_gate", "out[t] = z ? y * oracle_silu(z[t]) : y;", "out[t] = y;"),
+    ("skip_outside_gate",
+     "y += D_d * u[t];\n        out[t] = z ? y * oracle_silu(z[t]) : y;",
+     "out[t] = (z ? y * oracle_silu(z[t]) : y) + D_d * u[t];"),
+    ("h0_ignored", "h[n] = h0 ? h0[n] : 0.0;", "h[n] = 0.0;"),
+    ("euler_on_A", "double decay = exp(dt * A_row[n]);",
+     "double decay = 1.0 + dt * A_row[n];"),
+    ("full_zoh_on_B", "double drive = dt * B_b[t * dstate + n] * u[t];",
+     "double drive = (exp(dt * A_row[n]) - 1.0) / A_row[n] * B_b[t * dstate + n] * u[t];"),
+    ("sigmoid_gate", "return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
+    ("softplus_without_log", "return log1p(exp(x));", "return exp(x);"),
+    ("softplus_naive_large_x", "return x + log1p(exp(-x));", "return x;"),
+    ("last_state_lost", "last_state[n] = h[n];", "last_state[n] = 0.0;"),
+    ("decode_B_of_batch0", "B + b * dstate, C + b * dstate", "B, C"),
+    ("decode_state_not_written", "softplus, h, out + r, h);", "softplus, h, out + r, NULL);"),
+    ("decode_x_dt_swapped", "x + r, dt + r", "dt + r, x + r"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    src = open(oracle.SOURCE).read()
+    olds = old if isinstance(old, list) else [old]
+    news = new if isinstance(new, list) else [new]
+    for o, n in zip(olds, news):
+        assert src.count(o) == 1, "mutation site for %s not unique/found" % name
+        src = src.replace(o, n)
+    path = os.path.join(tmp_path, "mutant.c")
+    with open(path, "w") as f:
+        f.write(src)
+    lib = oracle.compile_source(path, os.path.join(tmp_path, "libmutant.so"))
+    orc = oracle.Oracle(lib)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, "no pin caught mutant %s" % name

@@ -1,0 +1,198 @@
+"""Seeded synthetic inputs for the selective scan and its decode step.
+
+This module draws random numbers and rounds them to the storage dtype; it holds
+none of the scan's arithmetic.  Both the oracle-side tests and the GPU path get
+their inputs from here, so that they see bit-identical values.
+
+Shapes follow the Mamba layer sizes the pages name: d_state = 16 and expand = 2
+(page "Mamba: Selective State Space Models", "Quick Start"; page "Mamba State
+Space Model", "Use the Mamba block"), so D_inner = 2 * d_model, with d_model
+768 for the 130M model and 2560 for the 2.8B model (both named as Hugging Face
+checkpoints on page "Mamba State Space Model", "Run zero-shot evaluations" and
+"Benchmark Mamba generation latency and throughput").  Parameters that the
+pages ask to keep in fp32 (page "Mamba State Space Model", "Troubleshoot model
+instability with precision settings") -- A, D and the delta bias -- and the
+recurrent state are fp32; activations are bf16 except in the tiny fp32 case.
+
+Value recipe (all workloads):
+  u, delta (raw, before bias and softplus), z, B, C ~ N(0, 1)
+  dt ~ exp(U[ln 1e-3, ln 1e-1]) per channel; delta_bias = inv_softplus(dt)
+      = log(expm1(dt)), so that softplus(0 + bias) = dt  (the bias init range
+      of page "Mamba State Space Model", "Troubleshoot initialization issues")
+  A[d, n] = -(n + 1)  (real, one N-vector per channel)
+  D ~ N(0, 1) per channel
+  decode state ~ 0.1 * N(0, 1)
+Draw order from numpy.random.default_rng(seed): u, delta, z, B, C, D, log-dt,
+then (decode only) the state.  Decode tokens use default_rng([seed, 1 + k]) for
+token k of a ring of ``tokens`` distinct tokens; step s uses token s % tokens.
+bf16 values are fp32 draws rounded to nearest-even (torch's conversion).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class ScanSpec:
+    name: str
+    batch: int
+    dim: int
+    dstate: int
+    seqlen: int
+    io: str = "bf16"          # "f32" or "bf16": dtype of u, delta, z, B, C, out
+    seed: int = 0
+    softplus: bool = True
+    has_z: bool = True
+    has_D: bool = True
+    has_bias: bool = True
+    chunk: int = 0            # >0: the workload is also run as seqlen/chunk calls
+    note: str = ""
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.dim * self.seqlen
+
+    @property
+    def state_elements(self) -> int:
+        return self.elements * self.dstate
+
+
+@dataclass(frozen=True)
+class DecodeSpec:
+    name: str
+    batch: int
+    dim: int
+    dstate: int
+    steps: int = 1000
+    tokens: int = 16          # ring of distinct seeded tokens
+    io: str = "bf16"
+    seed: int = 4
+    softplus: bool = True
+    state_std: float = 0.1
+    note: str = ""
+
+
+WORKLOADS = {
+    "tiny_f32": ScanSpec("tiny_f32", 1, 64, 16, 256, io="f32", seed=0,
+                         note="tiny fp32 scan"),
+    "mamba130m_layer": ScanSpec("mamba130m_layer", 8, 1536, 16, 2048, seed=1,
+                                note="Mamba-130M-shaped layer scan, bf16 io, "
+                                     "fp32 state, last_state out"),
+    "mamba2p8b_layer": ScanSpec("mamba2p8b_layer", 4, 5120, 16, 2048, seed=2,
+                                note="Mamba-2.8B-shaped layer scan, bf16 io"),
+    "long_chunked": ScanSpec("long_chunked", 1, 1536, 16, 131072, seed=3,
+                             chunk=2048,
+                             note="long sequence, state carried across "
+                                  "2048-step chunks"),
+    "decode": DecodeSpec("decode", 256, 5120, 16, steps=1000, seed=4,
+                         note="single-token state update, 256 sequences"),
+}
+
+
+def spec(name: str, **overrides):
+    s = WORKLOADS[name]
+    return replace(s, **overrides) if overrides else s
+
+
+def _round_io(a: np.ndarray, io: str) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    if io == "f32":
+        return t
+    if io == "bf16":
+        return t.to(torch.bfloat16)
+    raise ValueError("io dtype must be 'f32' or 'bf16', got %r" % (io,))
+
+
+def _params(rng: np.random.Generator, dim: int, dstate: int):
+    D = rng.standard_normal(dim, dtype=np.float32)
+    log_dt = rng.uniform(math.log(1e-3), math.log(1e-1), size=dim)
+    dt = np.exp(log_dt)
+    bias = np.log(np.expm1(dt)).astype(np.float32)
+    A = np.broadcast_to(-(np.arange(dstate, dtype=np.float32) + 1.0),
+                        (dim, dstate)).copy()
+    return A, D, bias
+
+
+def make_scan_inputs(s: ScanSpec) -> dict:
+    """CPU tensors for one scan call: io-dtype u, delta, z, B, C and fp32 A, D,
+    delta_bias (None where the spec switches them off)."""
+    rng = np.random.default_rng(s.seed)
+    shp = (s.batch, s.dim, s.seqlen)
+    bshp = (s.batch, s.seqlen, s.dstate)
+    u = _round_io(rng.standard_normal(shp, dtype=np.float32), s.io)
+    delta = _round_io(rng.standard_normal(shp, dtype=np.float32), s.io)
+    z = _round_io(rng.standard_normal(shp, dtype=np.float32), s.io)
+    B = _round_io(rng.standard_normal(bshp, dtype=np.float32), s.io)
+    C = _round_io(rng.standard_normal(bshp, dtype=np.float32), s.io)
+    A, D, bias = _params(rng, s.dim, s.dstate)
+    return dict(
+        u=u, delta=delta, A=torch.from_numpy(A), B=B, C=C,
+        D=torch.from_numpy(D) if s.has_D else None,
+        z=z if s.has_z else None,
+        delta_bias=torch.from_numpy(bias) if s.has_bias else None,
+        softplus=s.softplus,
+    )
+
+
+def make_initial_state(s, seed_offset: int = 7919) -> torch.Tensor:
+    """fp32 (batch, dim, N) state ~ state_std * N(0,1) for carried-state cases."""
+    rng = np.random.default_rng([s.seed, seed_offset])
+    std = getattr(s, "state_std", 0.1)
+    return torch.from_numpy(
+        (std * rng.standard_normal((s.batch, s.dim, s.dstate))).astype(np.float32))
+
+
+def make_decode_params(s: DecodeSpec) -> dict:
+    """fp32 A, D, dt_bias and the initial fp32 state for the decode workload."""
+    rng = np.random.default_rng(s.seed)
+    A, D, bias = _params(rng, s.dim, s.dstate)
+    state = (s.state_std * rng.standard_normal((s.batch, s.dim, s.dstate))
+             ).astype(np.float32)
+    return dict(A=torch.from_numpy(A), D=torch.from_numpy(D),
+                dt_bias=torch.from_numpy(bias), state=torch.from_numpy(state))
+
+
+def make_decode_token(s: DecodeSpec, k: int) -> dict:
+    """Token k of the ring: io-dtype x, dt (raw), z (batch, dim) and B, C
+    (batch, N)."""
+    rng = np.random.default_rng([s.seed, 1 + k])
+    shp = (s.batch, s.dim)
+    x = _round_io(rng.standard_normal(shp, dtype=np.float32), s.io)
+    dt = _round_io(rng.standard_normal(shp, dtype=np.float32), s.io)
+    z = _round_io(rng.standard_normal(shp, dtype=np.float32), s.io)
+    B = _round_io(rng.standard_normal((s.batch, s.dstate), dtype=np.float32), s.io)
+    C = _round_io(rng.standard_normal((s.batch, s.dstate), dtype=np.float32), s.io)
+    return dict(x=x, dt=dt, z=z, B=B, C=C)
+
+
+def scan_bytes(s: ScanSpec, load_state: bool = False, write_state: bool = True) -> int:
+    """Algorithmic HBM bytes of one scan call: every operand read once and every
+    result written once."""
+    io = 4 if s.io == "f32" else 2
+    e = s.elements
+    b = 3 * e * io if s.has_z else 2 * e * io          # u, delta, z in
+    b += e * io                                         # out
+    b += 2 * s.batch * s.seqlen * s.dstate * io         # B, C
+    b += 4 * s.dim * s.dstate                           # A
+    b += 4 * s.dim * (int(s.has_D) + int(s.has_bias))   # D, delta_bias
+    rows = s.batch * s.dim
+    if write_state:
+        b += 4 * rows * s.dstate
+    if load_state:
+        b += 4 * rows * s.dstate
+    return b
+
+
+def decode_step_bytes(s: DecodeSpec) -> int:
+    """Algorithmic HBM bytes of one decode step (state read and written once)."""
+    io = 4 if s.io == "f32" else 2
+    rows = s.batch * s.dim
+    b = 2 * 4 * rows * s.dstate            # state in + out
+    b += 4 * rows * io                     # x, dt, z in; out
+    b += 2 * s.batch * s.dstate * io       # B, C
+    b += 4 * s.dim * s.dstate + 2 * 4 * s.dim   # A, D, dt_bias
+    return b
