@@ -1,0 +1,161 @@
+/*
+ * mssm.h -- C ABI of libmssm, the gfx950 (MI355X) selective scan library.
+ *
+ * The library computes the selective state space recurrence of Mamba:
+ *   - continuous model h'(t) = A h(t) + B x(t), y(t) = C h(t) + D x(t)
+ *     (page "Mamba: Selective State Space Models", section "Mathematical
+ *     Foundation / State Space Model");
+ *   - B, C and the step Delta taken per token, Delta = tau_Delta(parameter +
+ *     projection) with tau_Delta = softplus and the parameter a per-channel
+ *     bias (same page, "Mathematical Foundation / Selective Mechanism");
+ *   - Delta as the discretisation step (same page, "Architecture"), read as
+ *     zero-order hold on A and an Euler step on B:
+ *         h_t[n] = exp(Delta_t A[d,n]) h_{t-1}[n] + Delta_t B_t[n] u_t
+ *         y_t    = sum_n C_t[n] h_t[n] + D[d] u_t
+ *         out_t  = y_t * silu(z_t)          (the gated block, same page,
+ *                                           "Features")
+ *   - the forward scan over a whole sequence, and the single-token step that
+ *     inference repeats with a fixed-size state (same page, "Mathematical
+ *     Foundation / Efficient Scan"; the exported low-level scan op of page
+ *     "Mamba State Space Model", "Use selective scan operations").
+ *
+ * Every (batch, channel) row is an independent recurrence.  A, D and the
+ * delta bias are fp32, and so is the recurrent state.  The activations use
+ * the io dtype (fp32 or bf16), which keeps parameters in fp32 as page "Mamba
+ * State Space Model", "Troubleshoot model instability with precision
+ * settings", recommends.
+ *
+ * Memory and ownership.  Every array pointer is a DEVICE pointer owned by the
+ * caller.  All arrays are contiguous, row-major, last index fastest:
+ *   u, delta, z, out   (batch, dim, seqlen)      io dtype
+ *   B, C               (batch, seqlen, dstate)   io dtype, one N-vector/token
+ *   A                  (dim, dstate)             fp32 (real; negative for a
+ *                                                 decaying state)
+ *   D, delta_bias      (dim)                     fp32
+ *   last_state         (batch, dim, dstate)      fp32
+ * Each pointer must be aligned to its element size; 16-byte alignment of every
+ * io pointer together with seqlen * sizeof(io) % 16 == 0 selects the
+ * vector-load path, anything else the element-load path (same results).
+ * The calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ * stream).  They never synchronise the host.  The forward scan may take
+ * stream-ordered workspace from HIP's default memory pool when it splits long
+ * rows in time (see mssm_selective_scan_fwd_plan); it returns it on the same
+ * stream.
+ *
+ * Errors.  Every argument is validated before the first HIP call; a call that
+ * fails validation returns a negative code and writes nothing.  A failing HIP
+ * call returns MSSM_ERR_HIP; its message is kept per thread and returned by
+ * mssm_last_error().  Non-finite inputs are not detected; they propagate
+ * through the arithmetic.
+ */
+#ifndef MSSM_H
+#define MSSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSSM_ABI_VERSION 1
+
+typedef enum { MSSM_F32 = 0, MSSM_BF16 = 1 } mssm_dtype;
+
+enum {
+  MSSM_OK = 0,
+  MSSM_ERR_NULL = -1,        /* a required pointer (or dims) is NULL        */
+  MSSM_ERR_DIMS = -2,        /* a size <= 0, decode seqlen != 1, overflow   */
+  MSSM_ERR_UNSUPPORTED = -3, /* dstate not in {1,2,4,8,16}, unknown dtype,  */
+                             /* unknown flag                                 */
+  MSSM_ERR_ALIGN = -4,       /* pointer not aligned to its element size     */
+  MSSM_ERR_ALIAS = -5,       /* an output overlaps another argument         */
+  MSSM_ERR_HIP = -6          /* a HIP runtime call or launch failed         */
+};
+
+/* fwd: last_state holds the initial state h0 on entry (in/out). */
+#define MSSM_FLAG_LOAD_STATE 1u
+
+typedef struct {
+  int64_t batch;       /* >= 1                                              */
+  int64_t dim;         /* channels (D_inner), >= 1                          */
+  int64_t dstate;      /* N, one of 1, 2, 4, 8, 16                          */
+  int64_t seqlen;      /* L >= 1 for the scan; must be 1 for state_update  */
+  int32_t io_dtype;    /* mssm_dtype of u/delta/z/B/C/out (x/dt/z/B/C/out) */
+  uint32_t flags;      /* MSSM_FLAG_*                                       */
+  int32_t time_segments; /* fwd only: 0 = the library picks; k >= 1 splits  */
+                         /* every row into k time segments (a carried state */
+                         /* joins them; results agree up to rounding)       */
+  int32_t reserved;      /* must be 0                                        */
+} mssm_dims;
+
+/*
+ * Forward selective scan (the recurrence above over t = 0..seqlen-1).
+ *   u, delta    : inputs; delta is the raw step before bias and softplus
+ *   A           : (dim, dstate) fp32
+ *   B, C        : (batch, seqlen, dstate) io dtype
+ *   D           : (dim) fp32 skip weight, or NULL for no skip term
+ *   z           : (batch, dim, seqlen) gate input, or NULL for no gate
+ *   delta_bias  : (dim) fp32, added to delta BEFORE the softplus; NULL = 0
+ *   softplus    : nonzero applies softplus to delta + bias
+ *   out         : (batch, dim, seqlen) io dtype, must not overlap any input
+ *   last_state  : (batch, dim, dstate) fp32 final state h_{L-1}, or NULL.
+ *                 With MSSM_FLAG_LOAD_STATE it is read first as h0 (required).
+ *                 Chaining calls with LOAD_STATE over consecutive pieces of a
+ *                 sequence reproduces one call over the whole sequence.
+ * Returns MSSM_OK or a negative MSSM_ERR_* code.
+ */
+int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
+                            const void* B, const void* C, const float* D,
+                            const void* z, const float* delta_bias,
+                            int softplus, void* out, float* last_state,
+                            const mssm_dims* dims, void* stream);
+
+/*
+ * Single-token decode step: the scan with seqlen = 1 starting from `state`,
+ * which is updated in place.
+ *   state       : (batch, dim, dstate) fp32, in/out
+ *   x, dt, z    : (batch, dim) io dtype; dt is the raw step; z may be NULL
+ *   B, C        : (batch, dstate) io dtype
+ *   A           : (dim, dstate) fp32;  D, dt_bias : (dim) fp32 or NULL
+ *   out         : (batch, dim) io dtype, must not overlap any input or state
+ * dims->seqlen must be 1; time_segments and flags must be 0.
+ */
+int mssm_selective_state_update(float* state, const void* x, const void* dt,
+                                const float* A, const void* B, const void* C,
+                                const float* D, const void* z,
+                                const float* dt_bias, int softplus, void* out,
+                                const mssm_dims* dims, void* stream);
+
+/* How the forward scan would run for these dims (no HIP call, no launch). */
+typedef struct {
+  int32_t groups;           /* 64-channel groups (batch * ceil(dim / 64))     */
+  int32_t whole_groups;     /* groups scanned in one piece                   */
+  int32_t split_groups;     /* groups split in time                          */
+  int32_t segments;         /* time segments of each split group             */
+  int64_t segment_len;      /* timesteps per segment (last may be shorter)   */
+  int32_t waves_per_group;  /* waves per workgroup (each owns dstate/waves   */
+                            /* of the state)                                 */
+  int32_t kernels;          /* launches per call (1, or 3 when splitting)    */
+  int64_t workspace_bytes;  /* stream-ordered workspace taken per call       */
+  int32_t vector_path;      /* 1 when the 16-byte vector-load path applies   */
+                            /* (needs aligned pointers too)                  */
+  int32_t reserved;
+} mssm_plan;
+
+int mssm_selective_scan_fwd_plan(const mssm_dims* dims, mssm_plan* plan);
+
+/* Static text for a status code. */
+const char* mssm_status_string(int status);
+
+/* Message of the last MSSM_ERR_HIP on this thread ("" if none). */
+const char* mssm_last_error(void);
+
+/* MSSM_ABI_VERSION of the loaded library. */
+int mssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSSM_H */

@@ -1,0 +1,135 @@
+"""MI355X (gfx950) selective scan: a thin torch binding over libmssm.so.
+
+Every step of the computation runs in the HIP kernels behind the C ABI in
+``include/mssm.h``; this module only checks tensors and passes their device
+pointers and the current HIP stream.  torch supplies device memory and streams.
+There is no CPU fallback: if the library is missing, or a tensor is not on a
+GPU, the call raises.
+
+The operation (page "Mamba: Selective State Space Models", "Mathematical
+Foundation"; discretisation by the step Delta, "Architecture"):
+    Delta_t = softplus(delta_t + delta_bias)
+    h_t     = exp(Delta_t A) * h_{t-1} + Delta_t B_t u_t
+    out_t   = (C_t . h_t + D u_t) * silu(z_t)
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import (MSSM_BF16, MSSM_F32, MSSM_FLAG_LOAD_STATE, Dims, MssmError,
+                   Plan, check, lib)
+
+__all__ = ["selective_scan_fwd", "selective_state_update", "scan_plan",
+           "MssmError", "abi_version"]
+
+_IO = {torch.float32: MSSM_F32, torch.bfloat16: MSSM_BF16}
+
+
+def abi_version() -> int:
+    return lib().mssm_abi_version()
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype=None, shape=None, device=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def scan_plan(batch, dim, dstate, seqlen, io_dtype=torch.bfloat16,
+              time_segments=0) -> dict:
+    """How the library splits a forward scan of this shape (no GPU needed)."""
+    dims = Dims(batch, dim, dstate, seqlen, _IO[io_dtype], 0, time_segments, 0)
+    plan = Plan()
+    check(lib().mssm_selective_scan_fwd_plan(dims, plan))
+    return plan.as_dict()
+
+
+def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                       softplus=True, last_state=None, load_state=False,
+                       out=None, time_segments=0):
+    """Forward selective scan.
+
+    u, delta, z: (batch, dim, L); B, C: (batch, L, N), all fp32 or all bf16.
+    A: (dim, N) fp32; D, delta_bias: (dim,) fp32 or None.
+    last_state: (batch, dim, N) fp32 receiving the final state (and holding
+    the initial state when load_state=True), or None.
+    Returns out (batch, dim, L) in the io dtype.
+    """
+    if u.dtype not in _IO:
+        raise ValueError("u must be float32 or bfloat16")
+    io = u.dtype
+    batch, dim, L = u.shape
+    N = A.shape[-1]
+    dev = u.device
+    _need(u, "u", io, (batch, dim, L), dev)
+    _need(delta, "delta", io, (batch, dim, L), dev)
+    _need(z, "z", io, (batch, dim, L), dev)
+    _need(B, "B", io, (batch, L, N), dev)
+    _need(C, "C", io, (batch, L, N), dev)
+    _need(A, "A", torch.float32, (dim, N), dev)
+    _need(D, "D", torch.float32, (dim,), dev)
+    _need(delta_bias, "delta_bias", torch.float32, (dim,), dev)
+    _need(last_state, "last_state", torch.float32, (batch, dim, N), dev)
+    if load_state and last_state is None:
+        raise ValueError("load_state needs last_state")
+    if out is None:
+        out = torch.empty((batch, dim, L), dtype=io, device=dev)
+    _need(out, "out", io, (batch, dim, L), dev)
+    dims = Dims(batch, dim, N, L, _IO[io],
+                MSSM_FLAG_LOAD_STATE if load_state else 0, time_segments, 0)
+    with torch.cuda.device(dev):
+        check(lib().mssm_selective_scan_fwd(
+            _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(delta_bias), int(bool(softplus)), _ptr(out), _ptr(last_state),
+            dims, _stream(dev)))
+    return out
+
+
+def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
+                           softplus=True, out=None):
+    """Single-token decode step; `state` (batch, dim, N) fp32 is updated in place.
+
+    x, dt, z: (batch, dim); B, C: (batch, N), all fp32 or all bf16.
+    Returns out (batch, dim) in the io dtype.
+    """
+    if x.dtype not in _IO:
+        raise ValueError("x must be float32 or bfloat16")
+    io = x.dtype
+    batch, dim, N = state.shape
+    dev = x.device
+    _need(state, "state", torch.float32, (batch, dim, N), dev)
+    _need(x, "x", io, (batch, dim), dev)
+    _need(dt, "dt", io, (batch, dim), dev)
+    _need(z, "z", io, (batch, dim), dev)
+    _need(B, "B", io, (batch, N), dev)
+    _need(C, "C", io, (batch, N), dev)
+    _need(A, "A", torch.float32, (dim, N), dev)
+    _need(D, "D", torch.float32, (dim,), dev)
+    _need(dt_bias, "dt_bias", torch.float32, (dim,), dev)
+    if out is None:
+        out = torch.empty((batch, dim), dtype=io, device=dev)
+    _need(out, "out", io, (batch, dim), dev)
+    dims = Dims(batch, dim, N, 1, _IO[io], 0, 0, 0)
+    with torch.cuda.device(dev):
+        check(lib().mssm_selective_state_update(
+            _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+            _ptr(z), _ptr(dt_bias), int(bool(softplus)), _ptr(out), dims,
+            _stream(dev)))
+    return out

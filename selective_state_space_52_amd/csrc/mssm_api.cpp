@@ -1,0 +1,311 @@
+// mssm_api.cpp -- the C ABI of libmssm (declared in include/mssm.h):
+// argument validation (always before the first HIP call), the work plan of
+// the forward scan, and kernel dispatch on the caller's stream.
+#include "mssm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+
+#include "mssm_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+void set_hip_error(const char* what, hipError_t e) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", what,
+                hipGetErrorString(e), (int)e);
+}
+
+constexpr int64_t kLanes = 64;
+constexpr int64_t kMinSegment = 512;  // shortest time segment worth a summary
+constexpr int kDefaultCUs = 256;      // MI355X compute units
+
+int g_cu_count = 0;  // cached compute-unit count of the current device
+
+bool valid_dstate(int64_t n) {
+  return n == 1 || n == 2 || n == 4 || n == 8 || n == 16;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes) {
+  if (!p || bytes <= 0) return Range{0, 0};
+  return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes};
+}
+
+bool overlap(Range a, Range b) {
+  return a.lo != a.hi && b.lo != b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+// Overflow-safe a * b * c <= limit for positive values.
+bool product_ok(int64_t a, int64_t b, int64_t c, int64_t limit) {
+  if (a <= 0 || b <= 0 || c <= 0) return false;
+  if (a > limit / b) return false;
+  const int64_t ab = a * b;
+  return ab <= limit / c;
+}
+
+int check_common_dims(const mssm_dims* dims) {
+  if (!dims) return MSSM_ERR_NULL;
+  if (dims->io_dtype != MSSM_F32 && dims->io_dtype != MSSM_BF16)
+    return MSSM_ERR_UNSUPPORTED;
+  if (dims->reserved != 0) return MSSM_ERR_UNSUPPORTED;
+  if (dims->batch <= 0 || dims->dim <= 0 || dims->dstate <= 0 ||
+      dims->seqlen <= 0)
+    return MSSM_ERR_DIMS;
+  if (!valid_dstate(dims->dstate)) return MSSM_ERR_UNSUPPORTED;
+  return MSSM_OK;
+}
+
+// The work plan of the forward scan (pure arithmetic, no HIP call).
+//
+// A 64-channel group scanned in one piece is one workgroup.  When the groups
+// do not fill the CUs evenly, some are cut into time segments joined by a
+// carried state: the remainder beyond a whole number of CU rounds is spread
+// over the CUs, and when there are few groups and long rows (long sequences)
+// every group is cut.  Cutting costs an extra summary pass over all but the
+// last segment, so it is only used where idle CUs would cost more.
+int make_plan(const mssm_dims* dims, int cus, mssm_plan* plan) {
+  const int64_t L = dims->seqlen;
+  const int64_t N = dims->dstate;
+  const int waves = mssm::scan_waves_per_group((int)N);
+  const int64_t tile = 8 * waves;
+  const int64_t gpb = (dims->dim + kLanes - 1) / kLanes;
+  if (gpb > INT32_MAX / dims->batch) return MSSM_ERR_DIMS;
+  const int64_t G = gpb * dims->batch;
+
+  int64_t whole = G, segments = 1;
+  if (dims->time_segments > 0) {
+    segments = dims->time_segments;
+    if (segments > 1) whole = 0;
+  } else if (L >= 2 * kMinSegment) {
+    if (G >= cus) {
+      const int64_t rest = G % cus;
+      if (rest > 0) {
+        whole = G - rest;
+        segments = std::min<int64_t>(L / kMinSegment,
+                                     std::max<int64_t>(2, (cus + rest - 1) / rest));
+      }
+    } else if (2 * G <= cus) {
+      whole = 0;
+      segments = std::min<int64_t>(L / kMinSegment, (4 * cus + G - 1) / G);
+    }
+  }
+  int64_t seg_len = L;
+  if (segments > 1) {
+    seg_len = (L + segments - 1) / segments;
+    seg_len = (seg_len + tile - 1) / tile * tile;  // whole tiles per segment
+    segments = (L + seg_len - 1) / seg_len;
+  }
+  if (segments <= 1) {
+    segments = 1;
+    whole = G;
+    seg_len = L;
+  }
+  const int64_t split = G - whole;
+  if (whole + split * segments > INT32_MAX) return MSSM_ERR_DIMS;
+
+  int64_t ws = 0;
+  if (split > 0) {
+    const int64_t rows = split * kLanes;
+    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    ws = up(rows * (segments - 1) * N * 4) + up(rows * (segments - 1) * 8) +
+         up(rows * segments * N * 4);
+  }
+  std::memset(plan, 0, sizeof(*plan));
+  plan->groups = (int32_t)G;
+  plan->whole_groups = (int32_t)whole;
+  plan->split_groups = (int32_t)split;
+  plan->segments = (int32_t)segments;
+  plan->segment_len = seg_len;
+  plan->waves_per_group = waves;
+  plan->kernels = split > 0 ? 3 : 1;
+  plan->workspace_bytes = ws;
+  const int64_t io = dims->io_dtype == MSSM_BF16 ? 2 : 4;
+  plan->vector_path = ((L * io) % 16 == 0 && (L % 8) == 0) ? 1 : 0;
+  return MSSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mssm_abi_version(void) { return MSSM_ABI_VERSION; }
+
+const char* mssm_last_error(void) { return g_last_error; }
+
+const char* mssm_status_string(int status) {
+  switch (status) {
+    case MSSM_OK: return "ok";
+    case MSSM_ERR_NULL: return "a required pointer is NULL";
+    case MSSM_ERR_DIMS: return "invalid sizes (non-positive, decode seqlen != 1, or too large)";
+    case MSSM_ERR_UNSUPPORTED: return "unsupported dstate, dtype, flag or reserved field";
+    case MSSM_ERR_ALIGN: return "a pointer is not aligned to its element size";
+    case MSSM_ERR_ALIAS: return "an output overlaps another argument";
+    case MSSM_ERR_HIP: return "a HIP runtime call failed (see mssm_last_error)";
+    default: return "unknown status";
+  }
+}
+
+int mssm_selective_scan_fwd_plan(const mssm_dims* dims, mssm_plan* plan) {
+  if (!plan) return MSSM_ERR_NULL;
+  int rc = check_common_dims(dims);
+  if (rc != MSSM_OK) return rc;
+  if (dims->time_segments < 0) return MSSM_ERR_DIMS;
+  return make_plan(dims, g_cu_count > 0 ? g_cu_count : kDefaultCUs, plan);
+}
+
+int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
+                            const void* B, const void* C, const float* D,
+                            const void* z, const float* delta_bias,
+                            int softplus, void* out, float* last_state,
+                            const mssm_dims* dims, void* stream) {
+  int rc = check_common_dims(dims);
+  if (rc != MSSM_OK) return rc;
+  if (dims->flags & ~MSSM_FLAG_LOAD_STATE) return MSSM_ERR_UNSUPPORTED;
+  if (dims->time_segments < 0) return MSSM_ERR_DIMS;
+  const bool load_state = (dims->flags & MSSM_FLAG_LOAD_STATE) != 0;
+  if (!u || !delta || !A || !B || !C || !out) return MSSM_ERR_NULL;
+  if (load_state && !last_state) return MSSM_ERR_NULL;
+
+  const int64_t batch = dims->batch, dim = dims->dim, N = dims->dstate,
+                L = dims->seqlen;
+  const size_t io = dims->io_dtype == MSSM_BF16 ? 2 : 4;
+  const int64_t lim = INT64_MAX / 16;
+  if (L > INT32_MAX || !product_ok(batch, dim, L, lim) ||
+      !product_ok(batch, L, N, lim) || !product_ok(batch, dim, N, lim))
+    return MSSM_ERR_DIMS;
+
+  const void* ios[] = {u, delta, B, C, out, z};
+  for (const void* p : ios)
+    if (p && !aligned(p, io)) return MSSM_ERR_ALIGN;
+  const void* f32s[] = {A, D, delta_bias, last_state};
+  for (const void* p : f32s)
+    if (p && !aligned(p, 4)) return MSSM_ERR_ALIGN;
+
+  const int64_t ebytes = batch * dim * L * (int64_t)io;
+  const int64_t bcbytes = batch * L * N * (int64_t)io;
+  const Range r_out = range_of(out, ebytes);
+  const Range r_state = range_of(last_state, batch * dim * N * 4);
+  const Range ins[] = {range_of(u, ebytes),      range_of(delta, ebytes),
+                       range_of(z, ebytes),      range_of(B, bcbytes),
+                       range_of(C, bcbytes),     range_of(A, dim * N * 4),
+                       range_of(D, dim * 4),     range_of(delta_bias, dim * 4)};
+  for (const Range& r : ins)
+    if (overlap(r_out, r) || overlap(r_state, r)) return MSSM_ERR_ALIAS;
+  if (overlap(r_out, r_state)) return MSSM_ERR_ALIAS;
+
+  // --- validation done; HIP calls from here on ---
+  if (g_cu_count <= 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                              dev) == hipSuccess &&
+        cus > 0)
+      g_cu_count = cus;
+  }
+  mssm_plan plan;
+  rc = make_plan(dims, g_cu_count > 0 ? g_cu_count : kDefaultCUs, &plan);
+  if (rc != MSSM_OK) return rc;
+
+  const bool vec = plan.vector_path && aligned(u, 16) && aligned(delta, 16) &&
+                   aligned(out, 16) && aligned(B, 16) && aligned(C, 16) &&
+                   (!z || aligned(z, 16));
+
+  mssm::ScanParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.u = u; p.delta = delta; p.z = z; p.A = A; p.B = B; p.C = C; p.D = D;
+  p.bias = delta_bias; p.out = out; p.last_state = last_state;
+  p.batch = batch; p.dim = dim; p.L = L;
+  p.softplus = softplus ? 1 : 0;
+  p.load_state = load_state ? 1 : 0;
+  p.groups_per_batch = (int32_t)((dim + kLanes - 1) / kLanes);
+  p.whole_groups = plan.whole_groups;
+  p.split_groups = plan.split_groups;
+  p.segments = plan.segments;
+  p.seg_len = plan.segment_len;
+
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = nullptr;
+  if (plan.split_groups > 0) {
+    hipError_t e = hipMallocAsync(&ws, (size_t)plan.workspace_bytes, st);
+    if (e != hipSuccess) {
+      set_hip_error("hipMallocAsync(workspace)", e);
+      return MSSM_ERR_HIP;
+    }
+    const int64_t rows = (int64_t)plan.split_groups * kLanes;
+    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    char* base = (char*)ws;
+    p.ws_S = (float*)base;
+    base += up(rows * (plan.segments - 1) * N * 4);
+    p.ws_sum = (double*)base;
+    base += up(rows * (plan.segments - 1) * 8);
+    p.ws_hin = (float*)base;
+  }
+  hipError_t e = mssm::launch_scan(p, (int)N, io == 2, vec, st);
+  if (e != hipSuccess) set_hip_error("scan launch", e);
+  if (ws) {
+    hipError_t f = hipFreeAsync(ws, st);
+    if (e == hipSuccess && f != hipSuccess) {
+      set_hip_error("hipFreeAsync(workspace)", f);
+      e = f;
+    }
+  }
+  return e == hipSuccess ? MSSM_OK : MSSM_ERR_HIP;
+}
+
+int mssm_selective_state_update(float* state, const void* x, const void* dt,
+                                const float* A, const void* B, const void* C,
+                                const float* D, const void* z,
+                                const float* dt_bias, int softplus, void* out,
+                                const mssm_dims* dims, void* stream) {
+  int rc = check_common_dims(dims);
+  if (rc != MSSM_OK) return rc;
+  if (dims->flags != 0) return MSSM_ERR_UNSUPPORTED;
+  if (dims->seqlen != 1 || dims->time_segments != 0) return MSSM_ERR_DIMS;
+  if (!state || !x || !dt || !A || !B || !C || !out) return MSSM_ERR_NULL;
+  const int64_t batch = dims->batch, dim = dims->dim, N = dims->dstate;
+  const size_t io = dims->io_dtype == MSSM_BF16 ? 2 : 4;
+  if (!product_ok(batch, dim, N, INT64_MAX / 16)) return MSSM_ERR_DIMS;
+
+  const void* ios[] = {x, dt, B, C, out, z};
+  for (const void* p : ios)
+    if (p && !aligned(p, io)) return MSSM_ERR_ALIGN;
+  const void* f32s[] = {state, A, D, dt_bias};
+  for (const void* p : f32s)
+    if (p && !aligned(p, 4)) return MSSM_ERR_ALIGN;
+
+  const int64_t rb = batch * dim * (int64_t)io;
+  const Range r_out = range_of(out, rb);
+  const Range r_state = range_of(state, batch * dim * N * 4);
+  const Range ins[] = {range_of(x, rb), range_of(dt, rb), range_of(z, rb),
+                       range_of(B, batch * N * (int64_t)io),
+                       range_of(C, batch * N * (int64_t)io),
+                       range_of(A, dim * N * 4), range_of(D, dim * 4),
+                       range_of(dt_bias, dim * 4)};
+  for (const Range& r : ins)
+    if (overlap(r_out, r) || overlap(r_state, r)) return MSSM_ERR_ALIAS;
+  if (overlap(r_out, r_state)) return MSSM_ERR_ALIAS;
+
+  mssm::UpdateParams p;
+  p.state = state; p.x = x; p.dt = dt; p.z = z; p.A = A; p.B = B; p.C = C;
+  p.D = D; p.bias = dt_bias; p.out = out;
+  p.batch = batch; p.dim = dim; p.softplus = softplus ? 1 : 0;
+  hipError_t e = mssm::launch_state_update(p, (int)N, io == 2,
+                                           (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_hip_error("state_update launch", e);
+    return MSSM_ERR_HIP;
+  }
+  return MSSM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// mssm_internal.h -- launch parameters shared by the host API and the kernels.
+// Not part of the public ABI (include/mssm.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mssm {
+
+// One forward-scan call, as the kernels see it.
+//
+// Work is cut into 64-channel groups: group gi covers channels
+// [64*(gi % groups_per_batch), +64) of batch gi / groups_per_batch, one lane
+// per channel.  Groups [0, whole_groups) are scanned in one piece; the other
+// groups are cut into `segments` time segments of `seg_len` steps.  For those,
+// an aggregate pass summarises every segment but the last (local end state
+// from a zero start, and the sum of Delta), a combine pass turns the summaries
+// into each segment's initial state, and the main pass then scans every
+// segment from its initial state.
+struct ScanParams {
+  const void* u;
+  const void* delta;
+  const void* z;          // may be null
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;         // may be null
+  const float* bias;      // may be null
+  void* out;
+  float* last_state;      // may be null; read first when load_state
+  int64_t batch, dim, L;
+  int32_t softplus;
+  int32_t load_state;
+  int32_t groups_per_batch;
+  int32_t whole_groups;
+  int32_t split_groups;
+  int32_t segments;
+  int64_t seg_len;
+  // workspace of the split groups, indexed by split row sr = 64*sj + lane
+  float* ws_S;            // [sr][segments-1][N]
+  double* ws_sum;         // [sr][segments-1]
+  float* ws_hin;          // [sr][segments][N]
+};
+
+struct UpdateParams {
+  float* state;
+  const void* x;
+  const void* dt;
+  const void* z;          // may be null
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;         // may be null
+  const float* bias;      // may be null
+  void* out;
+  int64_t batch, dim;
+  int32_t softplus;
+};
+
+// Waves per 64-channel workgroup: each wave owns dstate / waves states.
+int scan_waves_per_group(int N);
+
+hipError_t launch_scan(const ScanParams& p, int N, bool bf16, bool vec,
+                       hipStream_t stream);
+hipError_t launch_state_update(const UpdateParams& p, int N, bool bf16,
+                               hipStream_t stream);
+
+}  // namespace mssm

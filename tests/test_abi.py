@@ -1,0 +1,160 @@
+"""The C ABI on the CPU: the library loads, exports every symbol that
+include/mssm.h declares, and rejects bad arguments before any HIP call.
+
+No compute call is made here: every call below fails validation, which
+happens before the first HIP call, so the pointers are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mssm.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from selective_state_space_52_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from selective_state_space_52_amd import build
+        build.build(force=True)
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mssm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 6, names
+    from selective_state_space_52_amd import _lib
+    assert sorted(_lib.EXPORTS) == names
+    for n in names:
+        assert hasattr(L, n), "missing export %s" % n
+
+
+def test_version_and_strings(L):
+    assert L.mssm_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        s = L.mssm_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert L.mssm_status_string(42).decode() == "unknown status"
+    assert L.mssm_last_error() is not None
+
+
+def _dims(batch=2, dim=64, N=16, L_=128, io=1, flags=0, ts=0, reserved=0):
+    from selective_state_space_52_amd._lib import Dims
+    return Dims(batch, dim, N, L_, io, flags, ts, reserved)
+
+
+BASE = 1 << 40
+
+
+def _ptrs(n, stride=1 << 34, offset=0):
+    """n distinct, far-apart, 256-byte aligned fake addresses."""
+    return [BASE + i * stride + offset for i in range(n)]
+
+
+def _fwd(L, dims, ptrs=None, **override):
+    p = dict(zip(["u", "delta", "A", "B", "C", "D", "z", "bias", "out", "last"],
+                 ptrs or _ptrs(10)))
+    p.update(override)
+    return L.mssm_selective_scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"],
+                                     p["D"], p["z"], p["bias"], 1, p["out"],
+                                     p["last"], ctypes.byref(dims), None)
+
+
+def test_fwd_validation_codes(L):
+    assert L.mssm_selective_scan_fwd(*([None] * 8), 1, None, None, None, None) == -1
+    assert _fwd(L, _dims(), u=None) == -1
+    assert _fwd(L, _dims(), out=None) == -1
+    assert _fwd(L, _dims(flags=1), last=None) == -1       # LOAD_STATE needs it
+    for bad in (dict(batch=0), dict(dim=-1), dict(L_=0), dict(N=0)):
+        assert _fwd(L, _dims(**bad)) == -2, bad
+    assert _fwd(L, _dims(ts=-1)) == -2
+    assert _fwd(L, _dims(N=3)) == -3
+    assert _fwd(L, _dims(N=32)) == -3
+    assert _fwd(L, _dims(io=7)) == -3
+    assert _fwd(L, _dims(flags=2)) == -3
+    assert _fwd(L, _dims(reserved=1)) == -3
+    assert _fwd(L, _dims(L_=1 << 40)) == -2                 # overflow / too long
+    # bf16 pointers need 2-byte alignment, fp32 ones 4-byte alignment
+    assert _fwd(L, _dims(io=1), u=BASE + 1) == -4
+    assert _fwd(L, _dims(io=0), out=BASE + 9 * (1 << 34) + 2) == -4
+    assert _fwd(L, _dims(), A=BASE + 2 * (1 << 34) + 2) == -4
+
+
+def test_fwd_alias_checks(L):
+    p = _ptrs(10)
+    # out overlapping u
+    assert _fwd(L, _dims(), out=p[0] + 64) == -5
+    # out overlapping B
+    assert _fwd(L, _dims(), out=p[3]) == -5
+    # last_state overlapping delta
+    assert _fwd(L, _dims(), last=p[1] + 128) == -5
+    # out overlapping last_state
+    assert _fwd(L, _dims(), last=p[8] + 256) == -5
+
+
+def test_update_validation_codes(L):
+    from selective_state_space_52_amd._lib import Dims
+    p = _ptrs(11)
+
+    def upd(dims, **o):
+        q = dict(zip(["state", "x", "dt", "A", "B", "C", "D", "z", "bias", "out"], p))
+        q.update(o)
+        return L.mssm_selective_state_update(q["state"], q["x"], q["dt"], q["A"],
+                                             q["B"], q["C"], q["D"], q["z"],
+                                             q["bias"], 1, q["out"],
+                                             ctypes.byref(dims), None)
+    assert upd(Dims(4, 64, 16, 2, 1, 0, 0, 0)) == -2      # seqlen must be 1
+    assert upd(Dims(4, 64, 16, 1, 1, 1, 0, 0)) == -3      # no flags
+    assert upd(Dims(4, 64, 16, 1, 1, 0, 3, 0)) == -2      # no segments
+    assert upd(Dims(4, 64, 12, 1, 1, 0, 0, 0)) == -3
+    assert upd(Dims(4, 64, 16, 1, 1, 0, 0, 0), state=None) == -1
+    assert upd(Dims(4, 64, 16, 1, 1, 0, 0, 0), state=p[0] + 2) == -4
+    assert upd(Dims(4, 64, 16, 1, 1, 0, 0, 0), out=p[0] + 64) == -5
+    assert upd(Dims(4, 64, 16, 1, 1, 0, 0, 0), out=p[1]) == -5
+
+
+def test_plan(L):
+    from selective_state_space_52_amd._lib import Plan
+    plan = Plan()
+    # 2.8B-shaped layer: 320 groups on 256 CUs -> 64 groups cut in 4
+    assert L.mssm_selective_scan_fwd_plan(
+        ctypes.byref(_dims(4, 5120, 16, 2048)), ctypes.byref(plan)) == 0
+    assert plan.groups == 320 and plan.waves_per_group == 4
+    assert plan.whole_groups + plan.split_groups == 320
+    assert plan.split_groups * plan.segments + plan.whole_groups >= 320
+    assert plan.vector_path == 1
+    # long sequence: few groups, long rows -> every group cut, 3 launches
+    assert L.mssm_selective_scan_fwd_plan(
+        ctypes.byref(_dims(1, 1536, 16, 131072)), ctypes.byref(plan)) == 0
+    assert plan.whole_groups == 0 and plan.segments > 1 and plan.kernels == 3
+    assert (plan.segments - 1) * plan.segment_len < 131072 <= plan.segments * plan.segment_len
+    assert plan.workspace_bytes > 0
+    # forced segments
+    assert L.mssm_selective_scan_fwd_plan(
+        ctypes.byref(_dims(1, 64, 16, 1000, ts=3)), ctypes.byref(plan)) == 0
+    assert plan.segments == 3 and plan.segment_len % 32 == 0
+    # ragged length: element path
+    assert L.mssm_selective_scan_fwd_plan(
+        ctypes.byref(_dims(1, 64, 16, 7)), ctypes.byref(plan)) == 0
+    assert plan.vector_path == 0 and plan.segments == 1
+    assert L.mssm_selective_scan_fwd_plan(None, ctypes.byref(plan)) == -1
+    assert L.mssm_selective_scan_fwd_plan(ctypes.byref(_dims(N=5)),
+                                          ctypes.byref(plan)) == -3
+
+
+def test_product_path_refuses_cpu_tensors():
+    import torch
+    import selective_state_space_52_amd as m
+    x = torch.zeros(1, 4, 8)
+    with pytest.raises(ValueError):
+        m.selective_scan_fwd(x, x, torch.zeros(4, 16), torch.zeros(1, 8, 16),
+                             torch.zeros(1, 8, 16))

@@ -1,0 +1,168 @@
+"""Forward scan on the GPU (through the C ABI) against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests.gpu_common import (check_out, check_state, gpu_scan, np64,
+                              oracle_rows, oracle_scan, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(name, **over):
+    return W.make_scan_inputs(W.spec(name, **over))
+
+
+def _report(what, worst):
+    print("%-48s worst err/bar = %.3g (parity), %.3g (tight)" % (what, *worst), flush=True)
+
+
+def test_tiny_fp32_full():
+    """The tiny fp32 workload (batch 1, D 64, N 16, L 256), every output."""
+    inp = _inputs("tiny_f32")
+    out, last = gpu_scan(inp)
+    ro, rl = oracle_scan(inp)
+    _report("tiny_f32 out", check_out(out, ro, "f32", "tiny out"))
+    check_state(last, rl, "tiny last_state")
+
+
+SHAPES = [
+    # io, batch, dim, N, L   -- several tiles, ragged channel groups and tails
+    ("bf16", 3, 128, 16, 256),    # vector path, whole tiles
+    ("bf16", 2, 100, 16, 333),    # element path, ragged group and tile
+    ("bf16", 2, 130, 16, 1000),   # vector path, ragged last tile
+    ("f32", 1, 64, 16, 257),      # fp32 element path
+    ("f32", 2, 70, 16, 264),      # fp32 vector path
+    ("bf16", 1, 64, 16, 1),
+    ("bf16", 1, 64, 16, 7),
+    ("bf16", 1, 64, 16, 63),
+    ("bf16", 1, 64, 16, 64),
+    ("bf16", 1, 64, 16, 65),
+    ("bf16", 1, 5, 16, 40),       # fewer channels than a wave
+    ("bf16", 2, 96, 1, 200),
+    ("bf16", 2, 96, 2, 200),
+    ("bf16", 2, 96, 4, 200),
+    ("bf16", 2, 96, 8, 200),
+    ("f32", 2, 33, 8, 77),
+]
+
+
+@pytest.mark.parametrize("io,batch,dim,N,L", SHAPES,
+                         ids=["%s-b%d-d%d-n%d-l%d" % s for s in SHAPES])
+def test_shapes(io, batch, dim, N, L):
+    inp = _inputs("mamba130m_layer", io=io, batch=batch, dim=dim, dstate=N,
+                  seqlen=L, seed=100 + L + N)
+    out, last = gpu_scan(inp)
+    ro, rl = oracle_scan(inp)
+    _report("shape %s" % ((io, batch, dim, N, L),), check_out(out, ro, io, "out"))
+    check_state(last, rl, "last_state")
+
+
+VARIANTS = [
+    dict(has_z=False), dict(has_D=False), dict(has_bias=False),
+    dict(softplus=False, has_bias=False), dict(has_z=False, has_D=False, has_bias=False),
+]
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("var", VARIANTS, ids=lambda v: ",".join("%s=%s" % kv for kv in v.items()))
+def test_optional_operands(io, var):
+    inp = _inputs("mamba130m_layer", io=io, batch=2, dim=80, seqlen=136, seed=7, **var)
+    if not var.get("softplus", True):
+        # raw steps must stay positive without softplus: use |delta| * 0.05
+        inp["delta"] = (inp["delta"].float().abs() * 0.05).to(inp["delta"].dtype)
+    out, last = gpu_scan(inp)
+    ro, rl = oracle_scan(inp)
+    _report("variant %s %s" % (io, var), check_out(out, ro, io, "out"))
+    check_state(last, rl, "last_state")
+
+
+@pytest.mark.parametrize("L,ts", [(1000, 2), (1000, 3), (999, 7), (2048, 5), (200, 9)])
+def test_forced_time_segments(L, ts):
+    """Rows cut into time segments joined by the carried state (aggregate,
+    combine and main passes) give the oracle's result."""
+    inp = _inputs("mamba130m_layer", batch=2, dim=72, seqlen=L, seed=L + ts)
+    h0 = W.make_initial_state(W.spec("mamba130m_layer", batch=2, dim=72))
+    out, last = gpu_scan(inp, h0=h0, time_segments=ts)
+    ro, rl = oracle_scan(inp, h0=h0.double().numpy())
+    _report("segments L=%d ts=%d" % (L, ts), check_out(out, ro, "bf16", "out"))
+    check_state(last, rl, "last_state")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_load_state_chaining(io):
+    """Consecutive calls carrying last_state reproduce one call (the resume
+    path), and both match the oracle."""
+    inp = _inputs("mamba130m_layer", io=io, batch=2, dim=64, seqlen=600, seed=3)
+    full, full_last = gpu_scan(inp)
+    cuts = [0, 1, 97, 352, 600]
+    state = torch.zeros(2, 64, 16)
+    pieces = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        part = dict(inp, u=inp["u"][..., a:b].contiguous(),
+                    delta=inp["delta"][..., a:b].contiguous(),
+                    z=inp["z"][..., a:b].contiguous(),
+                    B=inp["B"][:, a:b].contiguous(), C=inp["C"][:, a:b].contiguous())
+        o, state = gpu_scan(part, h0=state)
+        pieces.append(o)
+    chained = torch.cat(pieces, dim=-1)
+    ro, rl = oracle_scan(inp)
+    check_out(chained, ro, io, "chained out")
+    check_state(state, rl, "chained last_state")
+    check_out(full, ro, io, "full out")
+    check_state(full_last, rl, "full last_state")
+
+
+def test_determinism():
+    inp = _inputs("mamba130m_layer", batch=2, dim=192, seqlen=512, seed=5)
+    o1, l1 = gpu_scan(inp)
+    o2, l2 = gpu_scan(inp)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("name", ["mamba130m_layer", "mamba2p8b_layer"])
+def test_full_size_sampled_rows(name):
+    """Full-size layer workloads in the bench's launch configuration; sampled
+    rows against the oracle, computed row by row."""
+    s = W.spec(name)
+    inp = W.make_scan_inputs(s)
+    out, last = gpu_scan(inp)
+    rows = sample_rows(s.batch, s.dim, k=40, seed=s.seed)
+    ro, rl = oracle_rows(inp, rows)
+    g = torch.stack([out[b, d] for b, d in rows])
+    gl = torch.stack([last[b, d] for b, d in rows])
+    _report("%s sampled rows" % name, check_out(g, ro, "bf16", name))
+    check_state(gl, rl, name + " last_state")
+    assert torch.isfinite(out.float()).all()
+
+
+def test_long_sequence_split_vs_unsplit():
+    """Long sequence (batch 1, D 1536, N 16, L 131072): one call (rows cut into
+    time segments inside the library) against 64 chained calls of 2048 steps
+    carrying last_state, and sampled rows against the oracle."""
+    s = W.spec("long_chunked")
+    inp = W.make_scan_inputs(s)
+    out, last = gpu_scan(inp)
+    state = torch.zeros(1, s.dim, s.dstate)
+    pieces = []
+    for a in range(0, s.seqlen, s.chunk):
+        b = a + s.chunk
+        part = dict(inp, u=inp["u"][..., a:b].contiguous(),
+                    delta=inp["delta"][..., a:b].contiguous(),
+                    z=inp["z"][..., a:b].contiguous(),
+                    B=inp["B"][:, a:b].contiguous(), C=inp["C"][:, a:b].contiguous())
+        o, state = gpu_scan(part, h0=state)
+        pieces.append(o)
+    chunked = torch.cat(pieces, dim=-1)
+    rows = sample_rows(1, s.dim, k=12, seed=3)
+    ro, rl = oracle_rows(inp, rows)
+    for got, lab in ((out, "one call"), (chunked, "chunked")):
+        g = torch.stack([got[b, d] for b, d in rows])
+        _report("long %s" % lab, check_out(g, ro, "bf16", lab))
+    check_state(torch.stack([last[b, d] for b, d in rows]), rl, "one-call last_state")
+    check_state(torch.stack([state[b, d] for b, d in rows]), rl, "chunked last_state")
+    # split vs unsplit over every row
+    check_state(last, np64(state), "split vs unsplit last_state")
+    diff = (out.float() - chunked.float()).abs()
+    assert float((diff / (2e-2 * (1 + chunked.float().abs()))).max()) <= 1.0
