@@ -37,10 +37,10 @@
  * io pointer together with seqlen * sizeof(io) % 16 == 0 selects the
  * vector-load path, anything else the element-load path (same results).
  * The calls are asynchronous on `stream` (a hipStream_t; NULL = the default
- * stream).  They never synchronise the host.  The forward scan may take
- * stream-ordered workspace from HIP's default memory pool when it splits long
- * rows in time (see mssm_selective_scan_fwd_plan); it returns it on the same
- * stream.
+ * stream).  They never synchronise the host.  The forward scan takes
+ * stream-ordered workspace from HIP's default memory pool (B and C repacked
+ * as fp32, plus the segment summaries when it splits long rows in time; the
+ * size is mssm_plan.workspace_bytes) and returns it on the same stream.
  *
  * Errors.  Every argument is validated before the first HIP call; a call that
  * fails validation returns a negative code and writes nothing.  A failing HIP
@@ -136,7 +136,7 @@ typedef struct {
   int64_t segment_len;      /* timesteps per segment (last may be shorter)   */
   int32_t waves_per_group;  /* waves per workgroup (each owns dstate/waves   */
                             /* of the state)                                 */
-  int32_t kernels;          /* launches per call (1, or 3 when splitting)    */
+  int32_t kernels;          /* launches per call (2, or 4 when splitting)    */
   int64_t workspace_bytes;  /* stream-ordered workspace taken per call       */
   int32_t vector_path;      /* 1 when the 16-byte vector-load path applies   */
                             /* (needs aligned pointers too)                  */

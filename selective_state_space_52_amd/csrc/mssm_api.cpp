@@ -77,7 +77,7 @@ int make_plan(const mssm_dims* dims, int cus, mssm_plan* plan) {
   const int64_t L = dims->seqlen;
   const int64_t N = dims->dstate;
   const int waves = mssm::scan_waves_per_group((int)N);
-  const int64_t tile = 8 * waves;
+  const int64_t tile = 32;  // timesteps per kernel tile
   const int64_t gpb = (dims->dim + kLanes - 1) / kLanes;
   if (gpb > INT32_MAX / dims->batch) return MSSM_ERR_DIMS;
   const int64_t G = gpb * dims->batch;
@@ -113,12 +113,13 @@ int make_plan(const mssm_dims* dims, int cus, mssm_plan* plan) {
   const int64_t split = G - whole;
   if (whole + split * segments > INT32_MAX) return MSSM_ERR_DIMS;
 
-  int64_t ws = 0;
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  int64_t ws = up(mssm::scan_bc_workspace_bytes(dims->batch, L, (int)N,
+                                                dims->io_dtype == MSSM_BF16));
   if (split > 0) {
     const int64_t rows = split * kLanes;
-    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
-    ws = up(rows * (segments - 1) * N * 4) + up(rows * (segments - 1) * 8) +
-         up(rows * segments * N * 4);
+    ws += up(rows * (segments - 1) * N * 4) + up(rows * (segments - 1) * 8) +
+          up(rows * segments * N * 4);
   }
   std::memset(plan, 0, sizeof(*plan));
   plan->groups = (int32_t)G;
@@ -127,7 +128,7 @@ int make_plan(const mssm_dims* dims, int cus, mssm_plan* plan) {
   plan->segments = (int32_t)segments;
   plan->segment_len = seg_len;
   plan->waves_per_group = waves;
-  plan->kernels = split > 0 ? 3 : 1;
+  plan->kernels = split > 0 ? 4 : 2;
   plan->workspace_bytes = ws;
   const int64_t io = dims->io_dtype == MSSM_BF16 ? 2 : 4;
   plan->vector_path = ((L * io) % 16 == 0 && (L % 8) == 0) ? 1 : 0;
@@ -235,15 +236,18 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
 
   hipStream_t st = (hipStream_t)stream;
   void* ws = nullptr;
-  if (plan.split_groups > 0) {
+  {
     hipError_t e = hipMallocAsync(&ws, (size_t)plan.workspace_bytes, st);
     if (e != hipSuccess) {
       set_hip_error("hipMallocAsync(workspace)", e);
       return MSSM_ERR_HIP;
     }
+  }
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  p.ws_bc = ws;
+  if (plan.split_groups > 0) {
     const int64_t rows = (int64_t)plan.split_groups * kLanes;
-    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
-    char* base = (char*)ws;
+    char* base = (char*)ws + up(mssm::scan_bc_workspace_bytes(batch, L, (int)N, io == 2));
     p.ws_S = (float*)base;
     base += up(rows * (plan.segments - 1) * N * 4);
     p.ws_sum = (double*)base;

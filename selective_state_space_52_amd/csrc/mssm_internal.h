@@ -40,6 +40,8 @@ struct ScanParams {
   float* ws_S;            // [sr][segments-1][N]
   double* ws_sum;         // [sr][segments-1]
   float* ws_hin;          // [sr][segments][N]
+  void* ws_bc;            // B, C packed per wave run, io dtype
+                          // [b][wave][t][B, C of the wave's N / waves states]
 };
 
 struct UpdateParams {
@@ -59,6 +61,8 @@ struct UpdateParams {
 
 // Waves per 64-channel workgroup: each wave owns dstate / waves states.
 int scan_waves_per_group(int N);
+// Bytes of the packed B/C runs of one forward call.
+int64_t scan_bc_workspace_bytes(int64_t batch, int64_t L, int N, bool bf16);
 
 hipError_t launch_scan(const ScanParams& p, int N, bool bf16, bool vec,
                        hipStream_t stream);

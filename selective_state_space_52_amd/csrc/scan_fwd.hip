@@ -14,13 +14,16 @@
 //     B_t and C_t are the same for every lane -- they are read with scalar
 //     loads into SGPRs and cost no vector instructions or LDS traffic;
 //   * the N states of a channel are split over the NG waves of the
-//     workgroup (NPW = N / NG each), which multiplies the parallelism by NG;
+//     workgroup (NPW = N / NG each), which multiplies the parallelism by NG
+//     and gives each SIMD two waves of one workgroup at N = 16;
 //   * per-element work (softplus of delta, Delta*u, the D skip, the silu
 //     gate, the bf16 round trip) is done once: each wave prepares and emits
-//     8 timesteps of every 8*NG-step tile, sharing (Delta, Delta*u) and the
-//     per-wave partial readouts through LDS;
-//   * each lane reads its row's u / delta / z in 16-byte pieces (8 bf16
-//     timesteps), one tile ahead of use, and writes 8 outputs per store.
+//     32 / NG timesteps of every 32-step tile, sharing (Delta, Delta*u) and
+//     the per-wave partial readouts through LDS;
+//   * B_t and C_t are repacked once per call into fp32 runs per wave, read
+//     with 64-byte scalar loads;
+//   * each lane reads its row's u / delta / z in 8- or 16-byte pieces, one
+//     tile ahead of use, and writes its outputs with the same width.
 // Long rows can be cut into time segments (aggregate -> combine -> main):
 // the recurrence is associative on (decay, offset) pairs, so a segment's
 // effect on the state is (exp(A * sum Delta), local end state from zero).
@@ -31,7 +34,13 @@ namespace mssm {
 namespace {
 
 constexpr int kLanes = 64;
-constexpr int kChunk = 8;  // timesteps a wave prepares and emits per tile
+constexpr int kTile = 32;  // timesteps per tile
+constexpr bool kWarmScalarCache = true;
+
+// Waves per 64-channel workgroup: two states per wave (one for N = 1), so a
+// group of N = 16 runs 8 waves, two per SIMD.
+template <int N>
+constexpr int kWaves = N >= 2 ? N / 2 : 1;
 
 struct ScanShape {
   int64_t dim, L;
@@ -40,141 +49,167 @@ struct ScanShape {
   int64_t seg_len;
 };
 
-template <bool BF16>
-struct Raw;  // 8 consecutive io values of one row, as loaded
-template <>
-struct Raw<true> {
-  uint32_t w[4];
-};
-template <>
-struct Raw<false> {
-  uint32_t w[8];
+// KC consecutive io values of one row, as loaded (bf16 pairs or fp32 words).
+template <bool BF16, int KC>
+struct Raw {
+  static constexpr int W = BF16 ? KC / 2 : KC;
+  uint32_t w[W];
 };
 
-template <bool BF16>
-__device__ __forceinline__ float raw_get(const Raw<BF16>& r, int k) {
+template <bool BF16, int KC>
+__device__ __forceinline__ float raw_get(const Raw<BF16, KC>& r, int k) {
   if constexpr (BF16)
     return (k & 1) ? bf16_hi(r.w[k >> 1]) : bf16_lo(r.w[k >> 1]);
   else
     return __uint_as_float(r.w[k]);
 }
 
-template <bool BF16>
-__device__ __forceinline__ void raw_zero(Raw<BF16>& r) {
+template <bool BF16, int KC>
+__device__ __forceinline__ void raw_zero(Raw<BF16, KC>& r) {
 #pragma unroll
-  for (int i = 0; i < (BF16 ? 4 : 8); ++i) r.w[i] = 0u;
+  for (int i = 0; i < Raw<BF16, KC>::W; ++i) r.w[i] = 0u;
 }
 
-// Values [t, t + 8) of a row; `nvalid` of them exist (the rest read as 0).
-// VEC: 16-byte aligned and every chunk is whole or absent.
-template <bool BF16, bool VEC>
-__device__ __forceinline__ void load_chunk(Raw<BF16>& r, const void* base,
+// Values [t, t + KC) of a row starting at element offset `off`; `nvalid` of
+// them exist (the rest read as 0).  VEC: the row and every 16-byte piece
+// (8-byte when a chunk is only 4 bf16 values) are aligned, and a piece is
+// either whole or absent.
+template <bool BF16, bool VEC, int KC>
+__device__ __forceinline__ void load_chunk(Raw<BF16, KC>& r, const void* base,
                                            int64_t off, int64_t nvalid) {
+  constexpr int W = Raw<BF16, KC>::W;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(
+      static_cast<const char*>(base) + off * (BF16 ? 2 : 4));
   if constexpr (VEC) {
-    if (nvalid > 0) {
-      if constexpr (BF16) {
-        const uint4 v = *reinterpret_cast<const uint4*>(
-            static_cast<const uint16_t*>(base) + off);
-        r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
-      } else {
-        const uint4* q = reinterpret_cast<const uint4*>(
-            static_cast<const float*>(base) + off);
-        const uint4 v0 = q[0], v1 = q[1];
-        r.w[0] = v0.x; r.w[1] = v0.y; r.w[2] = v0.z; r.w[3] = v0.w;
-        r.w[4] = v1.x; r.w[5] = v1.y; r.w[6] = v1.z; r.w[7] = v1.w;
+    constexpr int PV = BF16 ? 2 : 1;  // values per 32-bit word
+    if constexpr (W >= 4) {
+#pragma unroll
+      for (int q = 0; q < W / 4; ++q) {
+        if (4 * q * PV < nvalid) {
+          const uint4 v = reinterpret_cast<const uint4*>(src)[q];
+          r.w[4 * q] = v.x; r.w[4 * q + 1] = v.y; r.w[4 * q + 2] = v.z; r.w[4 * q + 3] = v.w;
+        } else {
+          r.w[4 * q] = r.w[4 * q + 1] = r.w[4 * q + 2] = r.w[4 * q + 3] = 0u;
+        }
       }
     } else {
-      raw_zero(r);
+      static_assert(W == 2, "chunk of 4 bf16 values");
+      if (nvalid > 0) {
+        const uint2 v = *reinterpret_cast<const uint2*>(src);
+        r.w[0] = v.x; r.w[1] = v.y;
+      } else {
+        r.w[0] = r.w[1] = 0u;
+      }
     }
   } else {
     if constexpr (BF16) {
       const uint16_t* s = static_cast<const uint16_t*>(base) + off;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < W; ++i) {
         const uint32_t lo = (2 * i < nvalid) ? s[2 * i] : 0u;
         const uint32_t hi = (2 * i + 1 < nvalid) ? s[2 * i + 1] : 0u;
         r.w[i] = lo | (hi << 16);
       }
     } else {
-      const uint32_t* s = static_cast<const uint32_t*>(base) + off;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) r.w[i] = (i < nvalid) ? s[i] : 0u;
+      for (int i = 0; i < W; ++i) r.w[i] = (i < nvalid) ? src[i] : 0u;
     }
   }
 }
 
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, int KC>
 __device__ __forceinline__ void store_chunk(void* base, int64_t off,
-                                            const float (&o)[kChunk],
+                                            const float (&o)[KC],
                                             int64_t nvalid) {
-  if constexpr (BF16) {
-    uint16_t* dst = static_cast<uint16_t*>(base) + off;
-    if (VEC && nvalid >= kChunk) {
-      uint4 v;
-      v.x = pack_bf16x2(o[0], o[1]);
-      v.y = pack_bf16x2(o[2], o[3]);
-      v.z = pack_bf16x2(o[4], o[5]);
-      v.w = pack_bf16x2(o[6], o[7]);
-      *reinterpret_cast<uint4*>(dst) = v;
-    } else {
+  if (VEC && nvalid >= KC) {
+    uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<char*>(base) +
+                                                off * (BF16 ? 2 : 4));
+    constexpr int W = BF16 ? KC / 2 : KC;
+    uint32_t w[W];
 #pragma unroll
-      for (int k = 0; k < kChunk; ++k)
-        if (k < nvalid) dst[k] = to_bf16(o[k]);
+    for (int i = 0; i < W; ++i)
+      w[i] = BF16 ? pack_bf16x2(o[2 * i], o[2 * i + 1]) : __float_as_uint(o[i]);
+    if constexpr (W >= 4) {
+#pragma unroll
+      for (int q = 0; q < W / 4; ++q)
+        reinterpret_cast<uint4*>(dst)[q] =
+            make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+    } else {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
     }
+  } else if constexpr (BF16) {
+    uint16_t* dst = static_cast<uint16_t*>(base) + off;
+#pragma unroll
+    for (int k = 0; k < KC; ++k)
+      if (k < nvalid) dst[k] = to_bf16(o[k]);
   } else {
     float* dst = static_cast<float*>(base) + off;
-    if (VEC && nvalid >= kChunk) {
-      float4* q = reinterpret_cast<float4*>(dst);
-      q[0] = make_float4(o[0], o[1], o[2], o[3]);
-      q[1] = make_float4(o[4], o[5], o[6], o[7]);
-    } else {
 #pragma unroll
-      for (int k = 0; k < kChunk; ++k)
-        if (k < nvalid) dst[k] = o[k];
-    }
+    for (int k = 0; k < KC; ++k)
+      if (k < nvalid) dst[k] = o[k];
   }
 }
 
-// NPW consecutive B (or C) values of one token, kept as the loaded 32-bit
-// words (bf16 pairs or fp32) and unpacked only where they are used, so that
-// prefetched words do not force a wait.  The address is the same for every
-// lane, so these become scalar loads.
+// B_t and C_t packed for the scan, in the io dtype, laid out
+// [b][wave g][t][B_t[n0..n0+NPW), C_t[n0..n0+NPW)] so that one wave's values
+// for a batch of consecutive tokens are one contiguous 64-byte run read by a
+// single wide scalar load (the address is the same for every lane).  bf16
+// stays packed two to a word and is widened where it is used, which keeps the
+// scalar-cache footprint of the runs small.
 template <int NPW, bool BF16>
-struct BCWords {
-  static constexpr int W = BF16 ? (NPW + 1) / 2 : NPW;
-  uint32_t w[W];
+struct BCLayout {
+  static constexpr int kWordsPerStep = BF16 ? NPW : 2 * NPW;  // 32-bit words
+  static constexpr int kSteps = 16 / kWordsPerStep;           // per 64 B batch
 };
 
-template <int NPW, bool BF16, bool VEC>
-__device__ __forceinline__ void load_bc(BCWords<NPW, BF16>& v, const void* base,
-                                        int64_t off) {
-  if constexpr (BF16) {
-    const uint16_t* s = static_cast<const uint16_t*>(base) + off;
-    if constexpr (VEC && NPW >= 2) {
-      const uint32_t* w = reinterpret_cast<const uint32_t*>(s);
-#pragma unroll
-      for (int j = 0; j < NPW / 2; ++j) v.w[j] = w[j];
-    } else {
-#pragma unroll
-      for (int j = 0; j < BCWords<NPW, BF16>::W; ++j) {
-        const uint32_t lo = s[2 * j];
-        const uint32_t hi = (2 * j + 1 < NPW) ? (uint32_t)s[2 * j + 1] : 0u;
-        v.w[j] = lo | (hi << 16);
-      }
-    }
-  } else {
-    const uint32_t* s = static_cast<const uint32_t*>(base) + off;
-#pragma unroll
-    for (int j = 0; j < NPW; ++j) v.w[j] = s[j];
-  }
+// words of one wave's run, padded to whole 64-byte batches
+__host__ __device__ inline int64_t bc_run_words(int64_t L, int words_per_step) {
+  return (L * words_per_step + 15) / 16 * 16;
 }
 
 template <int NPW, bool BF16>
-__device__ __forceinline__ float bc_get(const BCWords<NPW, BF16>& v, int j) {
-  if constexpr (BF16)
-    return (j & 1) ? bf16_hi(v.w[j >> 1]) : bf16_lo(v.w[j >> 1]);
+struct alignas(16) BCBatch {
+  uint32_t w[16];
+};
+
+// value j (B for j < NPW, C after) of token i of a batch (or a raw run)
+template <int NPW, bool BF16>
+__device__ __forceinline__ float bc_val(const uint32_t* w, int i, int j) {
+  constexpr int WPS = BCLayout<NPW, BF16>::kWordsPerStep;
+  if constexpr (BF16) {
+    const uint32_t x = w[i * WPS + (j >> 1)];
+    return (j & 1) ? bf16_hi(x) : bf16_lo(x);
+  } else {
+    return __uint_as_float(w[i * WPS + j]);
+  }
+}
+
+__global__ void __launch_bounds__(256)
+    bc_pack_kernel(const void* __restrict__ Bm, const void* __restrict__ Cm,
+                   void* __restrict__ packed, int64_t batch, int64_t L, int N,
+                   int NG, int bf16) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = batch * L * 2 * N;
+  if (i >= total) return;
+  const int npw = N / NG;
+  // i indexes the values in order [b][g][t][j], j < 2*npw
+  const int j = (int)(i % (2 * npw));
+  const int64_t r = i / (2 * npw);
+  const int64_t t = r % L;
+  const int64_t bg = r / L;
+  const int g = (int)(bg % NG);
+  const int64_t b = bg / NG;
+  const int n = g * npw + (j < npw ? j : j - npw);
+  const int64_t src = (b * L + t) * N + n;
+  const void* m = j < npw ? Bm : Cm;
+  const int wps = bf16 ? npw : 2 * npw;          // words per token
+  const int64_t vals_per_word = bf16 ? 2 : 1;
+  // destination: wave run bg, padded to whole batches
+  const int64_t dst = bg * bc_run_words(L, wps) * vals_per_word + t * 2 * npw + j;
+  if (bf16)
+    static_cast<uint16_t*>(packed)[dst] = static_cast<const uint16_t*>(m)[src];
   else
-    return __uint_as_float(v.w[j]);
+    static_cast<float*>(packed)[dst] = static_cast<const float*>(m)[src];
 }
 
 // Main pass (AGG = false): scans each task's time range from its initial
@@ -182,6 +217,13 @@ __device__ __forceinline__ float bc_get(const BCWords<NPW, BF16>& v, int j) {
 // Aggregate pass (AGG = true): scans segments 0..P-2 of the split groups from
 // a zero state and writes the end state and the sum of Delta.
 //
+// A tile of kTile timesteps is done in three phases:
+//   prep   : each wave turns KC = kTile / NG of the tile's timesteps into
+//            (Delta, Delta*u) for its 64 channels and writes them to LDS;
+//   state  : each wave advances its NPW states over all kTile timesteps and
+//            writes its partial readouts to LDS;
+//   output : each wave sums the NG partials of its KC timesteps, adds the D
+//            skip, applies the gate and stores.
 // Latency.  Scalar loads (B, C) and LDS reads (Delta, Delta*u) share one
 // wait counter and scalar loads return out of order, so every wait on them is
 // a full drain.  The state phase therefore walks a tile in batches of KB
@@ -192,14 +234,16 @@ template <int N, int NG, bool BF16, bool VEC, bool HAS_Z, bool AGG, bool SOFTPLU
 __global__ void __launch_bounds__(kLanes* NG)
     scan_kernel(const void* __restrict__ u, const void* __restrict__ delta,
                 const void* __restrict__ z, const float* __restrict__ A,
-                const void* __restrict__ Bm, const void* __restrict__ Cm,
                 const float* __restrict__ Dv, const float* __restrict__ bias,
                 void* __restrict__ out, float* __restrict__ last_state,
                 float* __restrict__ ws_S, double* __restrict__ ws_sum,
-                const float* __restrict__ ws_hin, const ScanShape s) {
+                const float* __restrict__ ws_hin,
+                const uint32_t* __restrict__ bcp, const ScanShape s) {
   constexpr int NPW = N / NG;
-  constexpr int T = kChunk * NG;
-  constexpr int KB = 4;          // timesteps per batch
+  constexpr int T = kTile;
+  constexpr int KC = T / NG;     // timesteps a wave prepares and emits
+  constexpr int WPS = BCLayout<NPW, BF16>::kWordsPerStep;
+  constexpr int KB = BCLayout<NPW, BF16>::kSteps;  // timesteps per batch
   constexpr int NB = T / KB;     // batches per tile
   __shared__ float2 s_dw[T][kLanes];                              // (Delta, Delta*u)
   __shared__ float s_y[AGG ? 1 : NG][AGG ? 1 : T][kLanes];       // partial readouts
@@ -252,31 +296,32 @@ __global__ void __launch_bounds__(kLanes* NG)
   const float Dd = (!AGG && Dv) ? Dv[dc] : 0.0f;
   double dsum = 0.0;
 
-  const int64_t bc_base = b * s.L * N + n0;  // this wave's slice of B_t, C_t
+  // this wave's packed B/C run
+  const uint32_t* __restrict__ bcw = bcp + (b * NG + g) * bc_run_words(s.L, WPS);
+  using Batch = BCBatch<NPW, BF16>;
   const int64_t rowoff = row * s.L;
 
-  Raw<BF16> ru, rd, rz, nu, nd, nz;
+  Raw<BF16, KC> ru, rd, rz, nu, nd, nz;
   raw_zero(rz);
   raw_zero(nz);
 
-  auto prep = [&](const Raw<BF16>& pu, const Raw<BF16>& pd) {
+  auto prep = [&](const Raw<BF16, KC>& pu, const Raw<BF16, KC>& pd) {
 #pragma unroll
-    for (int k = 0; k < kChunk; ++k) {
+    for (int k = 0; k < KC; ++k) {
       const float x = raw_get(pd, k) + bv_d;
       const float dl = SOFTPLUS ? softplus_f32(x) : x;
-      s_dw[g * kChunk + k][lane] = make_float2(dl, dl * raw_get(pu, k));
+      s_dw[g * KC + k][lane] = make_float2(dl, dl * raw_get(pu, k));
     }
   };
 
-  // one timestep of this wave's NPW states; returns the partial readout
-  using Words = BCWords<NPW, BF16>;
-  auto advance = [&](const float2 dw, const Words& bq, const Words& cq) -> float {
+  // one timestep of this wave's NPW states; token i of the packed words w
+  auto advance = [&](const float2 dw, const uint32_t* w, int i) -> float {
     float y = 0.0f;
 #pragma unroll
     for (int j = 0; j < NPW; ++j) {
       const float e = hw_exp2(dw.x * A2[j]);
-      h[j] = fmaf(e, h[j], dw.y * bc_get(bq, j));
-      if constexpr (!AGG) y = fmaf(bc_get(cq, j), h[j], y);
+      h[j] = fmaf(e, h[j], dw.y * bc_val<NPW, BF16>(w, i, j));
+      if constexpr (!AGG) y = fmaf(bc_val<NPW, BF16>(w, i, NPW + j), h[j], y);
     }
     if constexpr (AGG) dsum += (double)dw.x;
     return y;
@@ -284,11 +329,11 @@ __global__ void __launch_bounds__(kLanes* NG)
 
   // prologue: this wave's chunk of the first tile
   {
-    const int64_t tc = t_begin + g * kChunk;
+    const int64_t tc = t_begin + g * KC;
     const int64_t nv = t_end - tc;
-    load_chunk<BF16, VEC>(ru, u, rowoff + tc, nv);
-    load_chunk<BF16, VEC>(rd, delta, rowoff + tc, nv);
-    if (HAS_Z && !AGG) load_chunk<BF16, VEC>(rz, z, rowoff + tc, nv);
+    load_chunk<BF16, VEC, KC>(ru, u, rowoff + tc, nv);
+    load_chunk<BF16, VEC, KC>(rd, delta, rowoff + tc, nv);
+    if (HAS_Z && !AGG) load_chunk<BF16, VEC, KC>(rz, z, rowoff + tc, nv);
     prep(ru, rd);
   }
   __syncthreads();
@@ -296,52 +341,37 @@ __global__ void __launch_bounds__(kLanes* NG)
   for (int64_t tb = t_begin; tb < t_end; tb += T) {
     // prefetch this wave's chunk of the next tile
     {
-      const int64_t tc = tb + T + g * kChunk;
+      const int64_t tc = tb + T + g * KC;
       const int64_t nv = t_end - tc;
-      load_chunk<BF16, VEC>(nu, u, rowoff + tc, nv);
-      load_chunk<BF16, VEC>(nd, delta, rowoff + tc, nv);
-      if (HAS_Z && !AGG) load_chunk<BF16, VEC>(nz, z, rowoff + tc, nv);
+      load_chunk<BF16, VEC, KC>(nu, u, rowoff + tc, nv);
+      load_chunk<BF16, VEC, KC>(nd, delta, rowoff + tc, nv);
+      if (HAS_Z && !AGG) load_chunk<BF16, VEC, KC>(nz, z, rowoff + tc, nv);
     }
 
     // state phase: every wave advances its NPW states over the whole tile
     const int64_t nt = t_end - tb;
     if (nt >= T) {
       float2 dwn[KB];
-      Words bn[KB], cn[KB];
-      const int64_t off0 = bc_base + tb * N;
+      Batch bn = *reinterpret_cast<const Batch*>(bcw + tb * WPS);
 #pragma unroll
-      for (int i = 0; i < KB; ++i) {
-        dwn[i] = s_dw[i][lane];
-        load_bc<NPW, BF16, VEC>(bn[i], Bm, off0 + i * N);
-        if constexpr (!AGG) load_bc<NPW, BF16, VEC>(cn[i], Cm, off0 + i * N);
-        else cn[i] = bn[i];
-      }
+      for (int i = 0; i < KB; ++i) dwn[i] = s_dw[i][lane];
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) {
         float2 dwc[KB];
-        Words bc_[KB], cc_[KB];
 #pragma unroll
-        for (int i = 0; i < KB; ++i) {
-          dwc[i] = dwn[i];
-          bc_[i] = bn[i];
-          cc_[i] = cn[i];
-        }
+        for (int i = 0; i < KB; ++i) dwc[i] = dwn[i];
+        const Batch bc = bn;
         float yb[KB];
-        yb[0] = advance(dwc[0], bc_[0], cc_[0]);  // takes the batch's wait
+        yb[0] = advance(dwc[0], bc.w, 0);  // takes the batch's wait
         __builtin_amdgcn_sched_barrier(0);
         if (kb + 1 < NB) {
-          const int64_t offn = off0 + (int64_t)(kb + 1) * KB * N;
+          bn = *reinterpret_cast<const Batch*>(bcw + (tb + (kb + 1) * KB) * WPS);
 #pragma unroll
-          for (int i = 0; i < KB; ++i) {
-            dwn[i] = s_dw[(kb + 1) * KB + i][lane];
-            load_bc<NPW, BF16, VEC>(bn[i], Bm, offn + i * N);
-            if constexpr (!AGG) load_bc<NPW, BF16, VEC>(cn[i], Cm, offn + i * N);
-            else cn[i] = bn[i];
-          }
+          for (int i = 0; i < KB; ++i) dwn[i] = s_dw[(kb + 1) * KB + i][lane];
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 1; i < KB; ++i) yb[i] = advance(dwc[i], bc_[i], cc_[i]);
+        for (int i = 1; i < KB; ++i) yb[i] = advance(dwc[i], bc.w, i);
         if constexpr (!AGG) {
 #pragma unroll
           for (int i = 0; i < KB; ++i) s_y[g][kb * KB + i][lane] = yb[i];
@@ -350,37 +380,52 @@ __global__ void __launch_bounds__(kLanes* NG)
       }
     } else {
       for (int kk = 0; kk < nt; ++kk) {
-        Words bq, cq;
-        const int64_t off = bc_base + (tb + kk) * N;
-        load_bc<NPW, BF16, VEC>(bq, Bm, off);
-        if constexpr (!AGG) load_bc<NPW, BF16, VEC>(cq, Cm, off);
-        else cq = bq;
-        const float y = advance(s_dw[kk][lane], bq, cq);
+        uint32_t q[WPS];
+#pragma unroll
+        for (int j = 0; j < WPS; ++j) q[j] = bcw[(tb + kk) * WPS + j];
+        const float y = advance(s_dw[kk][lane], q, 0);
         if constexpr (!AGG) s_y[g][kk][lane] = y;
       }
     }
     __syncthreads();
 
+    // Warm the scalar cache with the next tile's B/C run: one dword per
+    // 64-byte line.  Scalar loads can only be waited on all together, so they
+    // are issued here, where the first wait (the output phase's LDS reads)
+    // comes after the whole prep phase.
+    uint32_t touch = 0u;
+    if (kWarmScalarCache) {
+      const int64_t last = bc_run_words(s.L, WPS) - 1;  // last word of the run
+      const int64_t f0 = (tb + T) * WPS;
+#pragma unroll
+      for (int f = 0; f < T * WPS; f += 16) touch += bcw[min(f0 + f, last)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // prep of the next tile (its Delta/Delta*u slots are free: every wave is
+    // past the state phase)
+    prep(nu, nd);
+
     if constexpr (!AGG) {
       // output phase: this wave's chunk of the tile
-      const int64_t tc = tb + g * kChunk;
-      float o[kChunk];
+      const int64_t tc = tb + g * KC;
+      float o[KC];
 #pragma unroll
-      for (int k = 0; k < kChunk; ++k) {
+      for (int k = 0; k < KC; ++k) {
         float y = 0.0f;
 #pragma unroll
-        for (int w = 0; w < NG; ++w) y += s_y[w][g * kChunk + k][lane];
+        for (int w = 0; w < NG; ++w) y += s_y[w][g * KC + k][lane];
         y = fmaf(Dd, raw_get(ru, k), y);
         if (HAS_Z) y *= silu_f32(raw_get(rz, k));
         o[k] = y;
       }
-      if (valid) store_chunk<BF16, VEC>(out, rowoff + tc, o, t_end - tc);
+      if (valid) store_chunk<BF16, VEC, KC>(out, rowoff + tc, o, t_end - tc);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::"s"(touch));  // keeps the warming loads
 
     ru = nu;
-    rd = nd;
     rz = nz;
-    prep(ru, rd);
     __syncthreads();
   }
 
@@ -433,20 +478,20 @@ hipError_t launch_one(const ScanParams& p, const ScanShape& s, int tasks,
   if (!p.softplus) {
     hipLaunchKernelGGL((scan_kernel<N, NG, BF16, VEC, HAS_Z, AGG, false>),
                        dim3(tasks), dim3(kLanes * NG), 0, stream, p.u, p.delta,
-                       p.z, p.A, p.B, p.C, p.D, p.bias, p.out, p.last_state,
-                       p.ws_S, p.ws_sum, p.ws_hin, s);
+                       p.z, p.A, p.D, p.bias, p.out, p.last_state, p.ws_S,
+                       p.ws_sum, p.ws_hin, (const uint32_t*)p.ws_bc, s);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((scan_kernel<N, NG, BF16, VEC, HAS_Z, AGG, true>), dim3(tasks),
-                     dim3(kLanes * NG), 0, stream, p.u, p.delta, p.z, p.A, p.B,
-                     p.C, p.D, p.bias, p.out, p.last_state, p.ws_S, p.ws_sum,
-                     p.ws_hin, s);
+                     dim3(kLanes * NG), 0, stream, p.u, p.delta, p.z, p.A, p.D,
+                     p.bias, p.out, p.last_state, p.ws_S, p.ws_sum, p.ws_hin,
+                     (const uint32_t*)p.ws_bc, s);
   return hipGetLastError();
 }
 
 template <int N, bool BF16, bool VEC>
 hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
-  constexpr int NG = (N >= 8) ? N / 4 : 1;
+  constexpr int NG = kWaves<N>;
   ScanShape s;
   s.dim = p.dim;
   s.L = p.L;
@@ -457,6 +502,14 @@ hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
   s.segments = p.segments;
   s.seg_len = p.seg_len;
   hipError_t e;
+  {
+    const int64_t total = p.batch * p.L * 2 * N;
+    hipLaunchKernelGGL(bc_pack_kernel, dim3((unsigned)((total + 255) / 256)),
+                       dim3(256), 0, stream, p.B, p.C, p.ws_bc, p.batch, p.L, N,
+                       NG, BF16 ? 1 : 0);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (p.split_groups > 0) {
     e = launch_one<N, NG, BF16, VEC, false, true>(
         p, s, p.split_groups * (p.segments - 1), stream);
@@ -487,7 +540,22 @@ hipError_t launch_dtype(const ScanParams& p, bool bf16, bool vec,
 
 }  // namespace
 
-int scan_waves_per_group(int N) { return (N >= 8) ? N / 4 : 1; }
+int64_t scan_bc_workspace_bytes(int64_t batch, int64_t L, int N, bool bf16) {
+  const int NG = scan_waves_per_group(N);
+  const int npw = N / NG;
+  const int wps = bf16 ? npw : 2 * npw;
+  return batch * NG * bc_run_words(L, wps) * 4;
+}
+
+int scan_waves_per_group(int N) {
+  switch (N) {
+    case 1: return kWaves<1>;
+    case 2: return kWaves<2>;
+    case 4: return kWaves<4>;
+    case 8: return kWaves<8>;
+    default: return kWaves<16>;
+  }
+}
 
 hipError_t launch_scan(const ScanParams& p, int N, bool bf16, bool vec,
                        hipStream_t stream) {

@@ -128,14 +128,14 @@ def test_plan(L):
     # 2.8B-shaped layer: 320 groups on 256 CUs -> 64 groups cut in 4
     assert L.mssm_selective_scan_fwd_plan(
         ctypes.byref(_dims(4, 5120, 16, 2048)), ctypes.byref(plan)) == 0
-    assert plan.groups == 320 and plan.waves_per_group == 4
+    assert plan.groups == 320 and plan.waves_per_group == 8
     assert plan.whole_groups + plan.split_groups == 320
     assert plan.split_groups * plan.segments + plan.whole_groups >= 320
     assert plan.vector_path == 1
     # long sequence: few groups, long rows -> every group cut, 3 launches
     assert L.mssm_selective_scan_fwd_plan(
         ctypes.byref(_dims(1, 1536, 16, 131072)), ctypes.byref(plan)) == 0
-    assert plan.whole_groups == 0 and plan.segments > 1 and plan.kernels == 3
+    assert plan.whole_groups == 0 and plan.segments > 1 and plan.kernels == 4
     assert (plan.segments - 1) * plan.segment_len < 131072 <= plan.segments * plan.segment_len
     assert plan.workspace_bytes > 0
     # forced segments
