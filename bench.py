@@ -1,17 +1,25 @@
 """Benchmark of the forward selective scan on one MI355X.
 
-One step = one forward scan call (softplus of delta, discretisation, the
+One step = one forward scan call -- softplus of delta, discretisation, the
 recurrence, the C readout with the D skip, the silu gate, the bf16 store and
-the final state) over the Mamba-2.8B-shaped layer workload (batch 4, D_inner
-5120, N 16, L 2048, bf16 activations, fp32 parameters and state), with inputs
-resident in HBM.  Prints one JSON line.
+the final state -- over the Mamba-2.8B-shaped layer workload (batch 4, D_inner
+5120, N 16, L 2048, bf16 activations, fp32 parameters and state), with every
+input already resident in HBM.  Rank 0 prints one JSON line.
 
-Inputs rotate over several buffer sets so that the 256 MB Infinity Cache
-cannot hold a step's inputs from the previous step.
+Inputs rotate over several buffer sets so that the 256 MB Infinity Cache does
+not hold a step's inputs from the step before.  The decode step (256 sequences
+x D_inner 5120, N 16, 1000 steps) is reported beside it in "decode".
+
+Other modes (used to produce the summaries under profiles/):
+  --copy-calibration      time torch's copy of a 1 GiB buffer (the plain copy
+                          kernel that scales the FETCH_SIZE/WRITE_SIZE counters)
+  --rocprof-summary DIR   print per-kernel statistics of a rocprofv3 database
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -22,7 +30,19 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 CUS, SIMDS, LANES, CLOCK_GHZ = 256, 4, 16, 2.4
+# fp32 VALU issue: one wave64 instruction per SIMD per 4 clocks = 16 lanes/clk
 VALU_PEAK_TSLOTS = CUS * SIMDS * LANES * CLOCK_GHZ / 1e3   # 39.32 T lane-slots/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_main_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "selective_state_space_52_amd", "csrc", "scan_fwd.hip")
+
+# Algorithmic VALU issue slots of the scan (fp32, one lane = one slot; a
+# transcendental occupies two slots because v_exp/v_log/v_rcp issue at half
+# rate).  Per state element: Delta*A (1), exp (2), Delta*u times B (1), the
+# state fma (1), the C readout fma (1).  Per element: delta + bias (1),
+# softplus = exp + log1p (2 + 2 + 3), Delta*u (1), D skip fma (1),
+# silu = exp + reciprocal (2 + 2 + 2), gate multiply (1).
+SLOTS_PER_STATE_ELEM = 6
+SLOTS_PER_ELEM = 18
 
 
 def parse():
@@ -34,32 +54,97 @@ def parse():
     ap.add_argument("--time-segments", type=int, default=0)
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--cpu-seconds", type=float, default=5.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--rocprof-summary", default=None)
+    ap.add_argument("--traffic-record", nargs=4, default=None,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles made and read through the HIP runtime directly (the
+    scan library records them around its main kernel; torch's Event objects
+    refuse to time events that torch did not record itself)."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        h = self.ct.c_void_p()
+        if self.hip.hipEventCreate(self.ct.byref(h)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return h.value
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+        return ms.value
+
+    def destroy(self, h):
+        self.hip.hipEventDestroy(h)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str, plan: dict):
+    """HBM bytes per main-kernel launch from the committed counter summary,
+    or None when it is missing or was taken on another version of the
+    kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = tr.get(workload)
+    if not rec or rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    if rec.get("segments") != plan["segments"]:
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def main():
     args = parse()
+    if args.rocprof_summary:
+        rocprof_summary(args.rocprof_summary)
+        return
+    if args.traffic_record:
+        traffic_record(args.workload, args.time_segments, *args.traffic_record)
+        return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(rows are independent; see DESIGN.md for how it would shard).",
-              file=sys.stderr)
+        print("bench.py measures one GPU: the scan's rows are independent and "
+              "this build has no multi-GPU path (DESIGN.md says how it would "
+              "shard); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     import workloads as W
     import selective_state_space_52_amd as m
 
     s = W.spec(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    io = torch.bfloat16 if s.io == "bf16" else torch.float32
     sets = []
     base = W.make_scan_inputs(s)
     for r in range(max(1, args.rotate)):
-        if r == 0:
-            inp = base
-        else:  # distinct buffers, same distributions (different seed)
-            inp = W.make_scan_inputs(W.spec(args.workload, seed=s.seed + 1000 * r))
+        inp = base if r == 0 else W.make_scan_inputs(W.spec(args.workload, seed=s.seed + 1000 * r))
         d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
         d["out"] = torch.empty_like(d["u"])
         d["last"] = torch.empty(s.batch, s.dim, s.dstate, device=dev)
@@ -76,41 +161,33 @@ def main():
         step(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
+    hev = HipEvents()
+    pairs = [(hev.create(), hev.create()) for _ in range(args.steps)]
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
+        m.set_scan_timing_events(*pairs[i])     # main scan kernel of this step
         step(i)
     ev1.record(stream)
     torch.cuda.synchronize()
+    m.set_scan_timing_events(None, None)
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
+    main_ms = sum(hev.elapsed_ms(a, b) for a, b in pairs) / args.steps
+    for a, b in pairs:
+        hev.destroy(a)
+        hev.destroy(b)
 
-    plan = m.scan_plan(s.batch, s.dim, s.dstate, s.seqlen,
-                       torch.bfloat16 if s.io == "bf16" else torch.float32,
-                       args.time_segments)
+    plan = m.scan_plan(s.batch, s.dim, s.dstate, s.seqlen, io, args.time_segments)
     nbytes = W.scan_bytes(s)
     gbs = nbytes / (ms * 1e-3) / 1e9
     gelem = s.state_elements / (ms * 1e-3) / 1e9
-    # algorithmic VALU issue slots: per state element one multiply (Delta*A),
-    # one exp (2 slots: v_exp_f32 issues at half rate), one multiply (Delta*u
-    # times B), two fma (state update, C readout) = 6; per element the
-    # softplus (~16), Delta*u, D skip, silu gate (~8) and bf16 conversions
-    # (~4) = 30
-    slots = s.state_elements * 6 + s.elements * 30
-    achieved_tslots = slots / (ms * 1e-3) / 1e12
-
-    traffic = None
-    try:
-        with open(args.traffic) as f:
-            tr = json.load(f)
-        key = "%s/%s" % (args.workload, plan["segments"])
-        if key in tr:
-            traffic = tr[key]
-    except (OSError, ValueError):
-        pass
+    slots = s.state_elements * SLOTS_PER_STATE_ELEM + s.elements * SLOTS_PER_ELEM
+    achieved = slots / (main_ms * 1e-3) / 1e12
+    traffic = load_traffic(args.workload, plan)
 
     res = {
         "metric": "selective-scan fwd HBM GB/s (% of peak) + Gelem/s (B*L*D_inner*N)",
@@ -125,54 +202,169 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if s.io == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": "%s: batch %d, D_inner %d, N %d, L %d, %s io, fp32 state"
-                   % (s.name, s.batch, s.dim, s.dstate, s.seqlen, s.io),
+        "config": {"workload": "%s: batch %d, D_inner %d, N %d, L %d, %s activations, "
+                               "fp32 A/D/delta_bias/state" % (s.name, s.batch, s.dim,
+                                                              s.dstate, s.seqlen, s.io),
                    "batch": s.batch, "d_inner": s.dim, "d_state": s.dstate,
-                   "seq_len": s.seqlen, "plan": plan},
+                   "seq_len": s.seqlen, "algorithmic_bytes": nbytes,
+                   "plan": plan},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "gelem_per_s": round(gelem, 2),
-        "roofline": {"bound": "alu", "achieved": round(achieved_tslots, 3),
+        "roofline": {"bound": "alu", "achieved": round(achieved, 3),
                      "peak": round(VALU_PEAK_TSLOTS, 3), "unit": "Tslot/s",
-                     "frac": round(achieved_tslots / VALU_PEAK_TSLOTS, 4),
-                     "traffic": traffic},
+                     "frac": round(achieved / VALU_PEAK_TSLOTS, 4),
+                     "traffic": traffic,
+                     "kernel": "scan_kernel (main pass)",
+                     "kernel_ms": round(main_ms, 5)},
         "wall_s": round(wall, 3),
     }
+    if not args.no_decode:
+        res["decode"] = bench_decode(torch, W, m, dev, args.decode_steps)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(s, base, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(s, base, args.cpu_seconds, nbytes)
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(s, inp, seconds):
-    """The fp64 oracle on the host cores, on a bounded sample of rows of the
-    same workload (whole rows, all L timesteps), scaled to Gelem/s."""
+def bench_decode(torch, W, m, dev, steps):
+    """The decode workload: `steps` single-token updates of one in-place fp32
+    state (84 MB, fits the 256 MB Infinity Cache, so the rate is an effective
+    one), cycling through a ring of seeded tokens."""
+    s = W.spec("decode", steps=steps)
+    par = W.make_decode_params(s)
+    toks = [{k: v.to(dev) for k, v in W.make_decode_token(s, k).items()}
+            for k in range(s.tokens)]
+    state = par["state"].to(dev)
+    A, D, bias = par["A"].to(dev), par["D"].to(dev), par["dt_bias"].to(dev)
+    out = torch.empty(s.batch, s.dim, dtype=torch.bfloat16, device=dev)
+
+    def run(n):
+        for i in range(n):
+            t = toks[i % len(toks)]
+            m.selective_state_update(state, t["x"], t["dt"], A, t["B"], t["C"], D=D,
+                                     z=t["z"], dt_bias=bias, out=out)
+    run(20)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run(steps)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nb = W.decode_step_bytes(s)
+    return {"workload": "decode: %d sequences x D_inner %d, N %d, %d steps, bf16 tokens, "
+                        "fp32 state in place" % (s.batch, s.dim, s.dstate, steps),
+            "ms_per_step": round(ms, 5), "algorithmic_bytes_per_step": nb,
+            "effective_gb_per_s": round(nb / (ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+
+
+def cpu_baseline(s, inp, seconds, nbytes):
+    """The fp64 oracle on the host cores over the whole workload (all rows,
+    all timesteps), repeated until about `seconds` of wall time, reported in
+    the GPU value's unit."""
     import oracle
-    import numpy as np
     nth = oracle.default_threads()
-    rows_total = s.batch * s.dim
-    # grow the sample until it takes about `seconds`
-    k = 64
-    while True:
-        sub = {key: v for key, v in inp.items()}
-        b_idx = 0
-        d_idx = slice(0, min(k, s.dim))
-        sub = dict(u=inp["u"][b_idx:b_idx + 1, d_idx], delta=inp["delta"][b_idx:b_idx + 1, d_idx],
-                   z=inp["z"][b_idx:b_idx + 1, d_idx], B=inp["B"][b_idx:b_idx + 1],
-                   C=inp["C"][b_idx:b_idx + 1], A=inp["A"][d_idx], D=inp["D"][d_idx],
-                   delta_bias=inp["delta_bias"][d_idx])
-        conv = {key: oracle._f64(v) for key, v in sub.items()}
+    conv = {k: oracle._f64(v) for k, v in inp.items() if k != "softplus"}
+    reps, total = 0, 0.0
+    while total < seconds:
         t0 = time.perf_counter()
-        oracle.scan(conv["u"], conv["delta"], conv["A"], conv["B"], conv["C"], D=conv["D"],
-                    z=conv["z"], delta_bias=conv["delta_bias"], softplus=s.softplus,
-                    nthreads=nth)
-        dt = time.perf_counter() - t0
-        rows = conv["u"].shape[1]
-        if dt >= seconds or rows >= s.dim:
-            break
-        k = min(s.dim, max(2 * k, int(k * seconds / max(dt, 1e-3) * 1.1)))
-    gelem = rows * s.seqlen * s.dstate / dt / 1e9
-    return {"value": round(gelem, 4), "unit": "Gelem/s", "cores": nth, "kind": "oracle",
-            "sample": "%d of %d rows (batch 0, channels 0..%d), all %d timesteps, %.1f s"
-                      % (rows, rows_total, rows - 1, s.seqlen, dt)}
+        oracle.scan(conv["u"], conv["delta"], conv["A"], conv["B"], conv["C"],
+                    D=conv["D"], z=conv["z"], delta_bias=conv["delta_bias"],
+                    softplus=s.softplus, nthreads=nth)
+        total += time.perf_counter() - t0
+        reps += 1
+    per = total / reps
+    return {"value": round(nbytes / per / 1e9, 3), "unit": "GB/s", "cores": nth,
+            "kind": "oracle", "gelem_per_s": round(s.state_elements / per / 1e9, 3),
+            "sample": "whole workload (%d rows x %d timesteps x N %d), %d run(s), "
+                      "%.2f s each, fp64" % (s.batch * s.dim, s.seqlen, s.dstate, reps, per)}
+
+
+def copy_calibration(torch):
+    """torch's device copy of a 1 GiB buffer, 5 times: 1 GiB read + 1 GiB
+    written per launch, the reference for scaling FETCH_SIZE / WRITE_SIZE."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
+
+
+def _counter_mean(d, kernel_substr, counter):
+    """Mean per-dispatch value of a counter (summed over its instances) for
+    the kernels whose name contains kernel_substr."""
+    import sqlite3
+    vals = []
+    for db in glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True):
+        c = sqlite3.connect(db)
+        vals += [v for (v,) in c.execute(
+            "select sum(counter_value) from pmc_events where counter_name = ? and "
+            "name like ? group by dispatch_id", (counter, "%" + kernel_substr + "%"))]
+    if not vals:
+        raise RuntimeError("no %s samples for %s in %s" % (counter, kernel_substr, d))
+    return sum(vals) / len(vals)
+
+
+def traffic_record(workload, time_segments, fetch_dir, write_dir, cfetch_dir, cwrite_dir):
+    """HBM bytes per launch of the main scan kernel from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
+    for torch's copy of a 1 GiB buffer (1 GiB fetched, 1 GiB written)."""
+    import workloads as W
+    copy_kib = float(1 << 20)
+    f_factor = copy_kib / _counter_mean(cfetch_dir, "copyBuffer", "FETCH_SIZE")
+    w_factor = copy_kib / _counter_mean(cwrite_dir, "copyBuffer", "WRITE_SIZE")
+    main = "scan_kernel<16, 8, true, true, true, false"   # bf16, vector path, gate, main pass
+    fk = _counter_mean(fetch_dir, main, "FETCH_SIZE")
+    wk = _counter_mean(write_dir, main, "WRITE_SIZE")
+    s = W.spec(workload)
+    import selective_state_space_52_amd as m
+    plan = m.scan_plan(s.batch, s.dim, s.dstate, s.seqlen, time_segments=time_segments)
+    rec = {workload: {
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "segments": plan["segments"],
+        "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+        "copy_fetch_factor": round(f_factor, 5), "copy_write_factor": round(w_factor, 5),
+        "hbm_bytes_per_launch": int(round((fk * f_factor + wk * w_factor) * 1024)),
+        "algorithmic_bytes": W.scan_bytes(s)}}
+    print(json.dumps(rec, indent=1))
+
+
+def _kname(name: str) -> str:
+    """Kernel name without its parameter list."""
+    return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+
+
+def rocprof_summary(d):
+    """Per-kernel launch count and duration (and counter means) of a rocprofv3
+    output directory, as text."""
+    import sqlite3
+    dbs = sorted(glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True))
+    for db in dbs:
+        c = sqlite3.connect(db)
+        print("# %s" % os.path.relpath(db, d))
+        try:
+            rows = c.execute("select name, count(*), avg(duration), min(duration), "
+                             "max(duration) from kernels group by name "
+                             "order by sum(duration) desc").fetchall()
+            print("%-70s %6s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us"))
+            for name, n, avg, mn, mx in rows:
+                print("%-70s %6d %12.2f %12.2f %12.2f" % (_kname(name)[:70], n,
+                                                          avg / 1e3, mn / 1e3, mx / 1e3))
+        except sqlite3.Error:
+            pass
+        try:
+            rows = c.execute("select name, counter_name, count(distinct dispatch_id), "
+                             "avg(v) from (select name, dispatch_id, counter_name, "
+                             "sum(counter_value) as v from pmc_events group by name, "
+                             "dispatch_id, counter_name) group by name, counter_name").fetchall()
+            if rows:
+                print("%-70s %-16s %6s %16s" % ("kernel", "counter", "n", "mean/dispatch"))
+            for name, cn, n, v in rows:
+                print("%-70s %-16s %6d %16.1f" % (_kname(name)[:70], cn, n, v))
+        except sqlite3.Error:
+            pass
 
 
 if __name__ == "__main__":

@@ -145,6 +145,15 @@ typedef struct {
 
 int mssm_selective_scan_fwd_plan(const mssm_dims* dims, mssm_plan* plan);
 
+/*
+ * Timing hook for benchmarks.  With both handles non-NULL (hipEvent_t, owned
+ * by the caller), every later forward scan issued from this thread records
+ * `start` on its stream right before the main scan kernel and `stop` right
+ * after it, so hipEventElapsedTime(start, stop) is that kernel's duration.
+ * Both NULL turns the hook off; one NULL is MSSM_ERR_NULL.  Per thread.
+ */
+int mssm_set_scan_timing_events(void* start, void* stop);
+
 /* Static text for a status code. */
 const char* mssm_status_string(int status);
 

@@ -20,13 +20,19 @@ from ._lib import (MSSM_BF16, MSSM_F32, MSSM_FLAG_LOAD_STATE, Dims, MssmError,
                    Plan, check, lib)
 
 __all__ = ["selective_scan_fwd", "selective_state_update", "scan_plan",
-           "MssmError", "abi_version"]
+           "set_scan_timing_events", "MssmError", "abi_version"]
 
 _IO = {torch.float32: MSSM_F32, torch.bfloat16: MSSM_BF16}
 
 
 def abi_version() -> int:
     return lib().mssm_abi_version()
+
+
+def set_scan_timing_events(start=None, stop=None) -> None:
+    """Record two hipEvent_t handles (ints) around the main scan kernel of the
+    following forward calls from this thread (None, None turns it off)."""
+    check(lib().mssm_set_scan_timing_events(start, stop))
 
 
 def _ptr(t):

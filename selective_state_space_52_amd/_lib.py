@@ -19,8 +19,8 @@ STATUS = {
 
 # every symbol include/mssm.h declares
 EXPORTS = ("mssm_selective_scan_fwd", "mssm_selective_state_update",
-           "mssm_selective_scan_fwd_plan", "mssm_status_string",
-           "mssm_last_error", "mssm_abi_version")
+           "mssm_selective_scan_fwd_plan", "mssm_set_scan_timing_events",
+           "mssm_status_string", "mssm_last_error", "mssm_abi_version")
 
 
 class Dims(ctypes.Structure):
@@ -68,6 +68,8 @@ def lib():
         L.mssm_status_string.restype = ctypes.c_char_p
         L.mssm_last_error.argtypes = []
         L.mssm_last_error.restype = ctypes.c_char_p
+        L.mssm_set_scan_timing_events.argtypes = [vp, vp]
+        L.mssm_set_scan_timing_events.restype = i
         L.mssm_abi_version.argtypes = []
         L.mssm_abi_version.restype = i
         _lib = L

@@ -14,6 +14,8 @@
 namespace {
 
 thread_local char g_last_error[512] = "";
+thread_local void* g_ev_start = nullptr;  // timing hook events of this thread
+thread_local void* g_ev_stop = nullptr;
 
 void set_hip_error(const char* what, hipError_t e) {
   std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", what,
@@ -141,6 +143,13 @@ extern "C" {
 
 int mssm_abi_version(void) { return MSSM_ABI_VERSION; }
 
+int mssm_set_scan_timing_events(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr)) return MSSM_ERR_NULL;
+  g_ev_start = start;
+  g_ev_stop = stop;
+  return MSSM_OK;
+}
+
 const char* mssm_last_error(void) { return g_last_error; }
 
 const char* mssm_status_string(int status) {
@@ -233,6 +242,8 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
   p.split_groups = plan.split_groups;
   p.segments = plan.segments;
   p.seg_len = plan.segment_len;
+  p.ev_start = g_ev_start;
+  p.ev_stop = g_ev_stop;
 
   hipStream_t st = (hipStream_t)stream;
   void* ws = nullptr;

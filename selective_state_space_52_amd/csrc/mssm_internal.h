@@ -42,6 +42,8 @@ struct ScanParams {
   float* ws_hin;          // [sr][segments][N]
   void* ws_bc;            // B, C packed per wave run, io dtype
                           // [b][wave][t][B, C of the wave's N / waves states]
+  void* ev_start;         // optional hipEvent_t recorded around the main
+  void* ev_stop;          // scan kernel (timing hook), or null
 };
 
 struct UpdateParams {

@@ -361,8 +361,19 @@ __global__ void __launch_bounds__(kLanes* NG)
 #pragma unroll
         for (int i = 0; i < KB; ++i) dwc[i] = dwn[i];
         const Batch bc = bn;
-        float yb[KB];
-        yb[0] = advance(dwc[0], bc.w, 0);  // takes the batch's wait
+        // pass 1: decays exp(Delta A) and drives Delta u B of the whole batch
+        // (independent of the state, so the exponentials can run ahead of
+        // the recurrence); token 0 takes the batch's wait
+        float e[KB][NPW], bw[KB][NPW];
+        auto decay_drive = [&](int i) {
+#pragma unroll
+          for (int j = 0; j < NPW; ++j) {
+            e[i][j] = hw_exp2(dwc[i].x * A2[j]);
+            bw[i][j] = dwc[i].y * bc_val<NPW, BF16>(bc.w, i, j);
+          }
+          if constexpr (AGG) dsum += (double)dwc[i].x;
+        };
+        decay_drive(0);
         __builtin_amdgcn_sched_barrier(0);
         if (kb + 1 < NB) {
           bn = *reinterpret_cast<const Batch*>(bcw + (tb + (kb + 1) * KB) * WPS);
@@ -371,10 +382,17 @@ __global__ void __launch_bounds__(kLanes* NG)
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 1; i < KB; ++i) yb[i] = advance(dwc[i], bc.w, i);
-        if constexpr (!AGG) {
+        for (int i = 1; i < KB; ++i) decay_drive(i);
+        // pass 2: the recurrence and the readout
 #pragma unroll
-          for (int i = 0; i < KB; ++i) s_y[g][kb * KB + i][lane] = yb[i];
+        for (int i = 0; i < KB; ++i) {
+          float y = 0.0f;
+#pragma unroll
+          for (int j = 0; j < NPW; ++j) {
+            h[j] = fmaf(e[i][j], h[j], bw[i][j]);
+            if constexpr (!AGG) y = fmaf(bc_val<NPW, BF16>(bc.w, i, NPW + j), h[j], y);
+          }
+          if constexpr (!AGG) s_y[g][kb * KB + i][lane] = y;
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -523,9 +541,14 @@ hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const int tasks = p.whole_groups + p.split_groups * p.segments;
-  if (p.z)
-    return launch_one<N, NG, BF16, VEC, true, false>(p, s, tasks, stream);
-  return launch_one<N, NG, BF16, VEC, false, false>(p, s, tasks, stream);
+  if (p.ev_start) {
+    e = hipEventRecord((hipEvent_t)p.ev_start, stream);
+    if (e != hipSuccess) return e;
+  }
+  e = p.z ? launch_one<N, NG, BF16, VEC, true, false>(p, s, tasks, stream)
+          : launch_one<N, NG, BF16, VEC, false, false>(p, s, tasks, stream);
+  if (e == hipSuccess && p.ev_stop) e = hipEventRecord((hipEvent_t)p.ev_stop, stream);
+  return e;
 }
 
 template <int N>
