@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "mssm_internal.h"
 
@@ -27,6 +28,36 @@ constexpr int64_t kMinSegment = 512;  // shortest time segment worth a summary
 constexpr int kDefaultCUs = 256;      // MI355X compute units
 
 int g_cu_count = 0;  // cached compute-unit count of the current device
+
+// Per device: a side stream (default priority) and fork/join events, made on
+// first use and kept until the process ends, plus a lock that keeps one
+// call's fork, side-stream work and join together.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool ready = false;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_lock[kMaxDevices];
+std::mutex g_init_lock;
+
+// The device's side stream, or nullptr if it cannot be made (the call then
+// runs on the caller's stream alone).
+SideStream* side_stream_of(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> g(g_init_lock);
+  SideStream& ss = g_side[dev];
+  if (!ss.ready) {
+    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess)
+      return nullptr;
+    if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+      return nullptr;
+    ss.ready = true;
+  }
+  return &ss;
+}
 
 bool valid_dstate(int64_t n) {
   return n == 1 || n == 2 || n == 4 || n == 8 || n == 16;
@@ -246,6 +277,18 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
   p.ev_stop = g_ev_stop;
 
   hipStream_t st = (hipStream_t)stream;
+  int dev = -1;
+  SideStream* side = nullptr;
+  std::unique_lock<std::mutex> side_guard;
+  if (plan.split_groups > 0 && plan.whole_groups > 0 && hipGetDevice(&dev) == hipSuccess) {
+    side = side_stream_of(dev);
+    if (side) {
+      side_guard = std::unique_lock<std::mutex>(g_side_lock[dev]);
+      p.side_stream = side->stream;
+      p.ev_fork = side->fork;
+      p.ev_join = side->join;
+    }
+  }
   void* ws = nullptr;
   {
     hipError_t e = hipMallocAsync(&ws, (size_t)plan.workspace_bytes, st);

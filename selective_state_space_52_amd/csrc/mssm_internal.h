@@ -44,6 +44,11 @@ struct ScanParams {
                           // [b][wave][t][B, C of the wave's N / waves states]
   void* ev_start;         // optional hipEvent_t recorded around the main
   void* ev_stop;          // scan kernel (timing hook), or null
+  // side stream and fork/join events for running the split groups beside
+  // the whole groups (null: everything on the caller's stream)
+  void* side_stream;
+  void* ev_fork;
+  void* ev_join;
 };
 
 struct UpdateParams {

@@ -231,22 +231,21 @@ __global__ void __launch_bounds__(256)
 // batch's B/C scalar loads and Delta/Delta*u LDS reads are issued, and the
 // rest of the batch computes while they are in flight.
 template <int N, int NG, bool BF16, bool VEC, bool HAS_Z, bool AGG, bool SOFTPLUS>
-__global__ void __launch_bounds__(kLanes* NG)
-    scan_kernel(const void* __restrict__ u, const void* __restrict__ delta,
-                const void* __restrict__ z, const float* __restrict__ A,
-                const float* __restrict__ Dv, const float* __restrict__ bias,
-                void* __restrict__ out, float* __restrict__ last_state,
-                float* __restrict__ ws_S, double* __restrict__ ws_sum,
-                const float* __restrict__ ws_hin,
-                const uint32_t* __restrict__ bcp, const ScanShape s) {
+__device__ __forceinline__ void scan_body(
+    const void* __restrict__ u, const void* __restrict__ delta,
+    const void* __restrict__ z, const float* __restrict__ A,
+    const float* __restrict__ Dv, const float* __restrict__ bias,
+    void* __restrict__ out, float* __restrict__ last_state,
+    float* __restrict__ ws_S, double* __restrict__ ws_sum,
+    const float* __restrict__ ws_hin, const uint32_t* __restrict__ bcp,
+    const ScanShape& s, float2 (&s_dw)[kTile][kLanes],
+    float (&s_y)[NG][kTile][kLanes], const int task) {
   constexpr int NPW = N / NG;
   constexpr int T = kTile;
   constexpr int KC = T / NG;     // timesteps a wave prepares and emits
   constexpr int WPS = BCLayout<NPW, BF16>::kWordsPerStep;
   constexpr int KB = BCLayout<NPW, BF16>::kSteps;  // timesteps per batch
   constexpr int NB = T / KB;     // batches per tile
-  __shared__ float2 s_dw[T][kLanes];                              // (Delta, Delta*u)
-  __shared__ float s_y[AGG ? 1 : NG][AGG ? 1 : T][kLanes];       // partial readouts
 
   const int lane = threadIdx.x & (kLanes - 1);
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -254,7 +253,6 @@ __global__ void __launch_bounds__(kLanes* NG)
 
   // task -> (group, segment)
   int gi, seg, nseg;
-  const int task = blockIdx.x;
   if constexpr (AGG) {
     const int per = s.segments - 1;
     gi = s.whole_groups + task / per;
@@ -460,6 +458,33 @@ __global__ void __launch_bounds__(kLanes* NG)
   }
 }
 
+// One launch runs `n_main` main-pass tasks (task = main_base + block) and,
+// after them, aggregate-pass tasks (task = block - n_main).  Putting the
+// aggregate pass of the time-split groups into the same launch as the main
+// pass of the whole groups lets it run on the CUs' spare workgroup slots.
+template <int N, int NG, bool BF16, bool VEC, bool HAS_Z, bool SOFTPLUS>
+__global__ void __launch_bounds__(kLanes* NG)
+    scan_kernel(const void* __restrict__ u, const void* __restrict__ delta,
+                const void* __restrict__ z, const float* __restrict__ A,
+                const float* __restrict__ Dv, const float* __restrict__ bias,
+                void* __restrict__ out, float* __restrict__ last_state,
+                float* __restrict__ ws_S, double* __restrict__ ws_sum,
+                const float* __restrict__ ws_hin,
+                const uint32_t* __restrict__ bcp, const ScanShape s,
+                const int n_main, const int main_base) {
+  __shared__ float2 s_dw[kTile][kLanes];        // (Delta, Delta*u) of a tile
+  __shared__ float s_y[NG][kTile][kLanes];      // per-wave partial readouts
+  const int blk = blockIdx.x;
+  if (blk < n_main)
+    scan_body<N, NG, BF16, VEC, HAS_Z, false, SOFTPLUS>(
+        u, delta, z, A, Dv, bias, out, last_state, ws_S, ws_sum, ws_hin, bcp,
+        s, s_dw, s_y, main_base + blk);
+  else
+    scan_body<N, NG, BF16, VEC, HAS_Z, true, SOFTPLUS>(
+        u, delta, z, A, Dv, bias, out, last_state, ws_S, ws_sum, ws_hin, bcp,
+        s, s_dw, s_y, blk - n_main);
+}
+
 // Initial state of every segment of the split groups, from the segment
 // summaries: h_in[0] = h0, h_in[s+1] = exp(A * sum_s Delta) h_in[s] + S_s.
 __global__ void __launch_bounds__(256)
@@ -490,21 +515,39 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-template <int N, int NG, bool BF16, bool VEC, bool HAS_Z, bool AGG>
-hipError_t launch_one(const ScanParams& p, const ScanShape& s, int tasks,
-                      hipStream_t stream) {
-  if (!p.softplus) {
-    hipLaunchKernelGGL((scan_kernel<N, NG, BF16, VEC, HAS_Z, AGG, false>),
-                       dim3(tasks), dim3(kLanes * NG), 0, stream, p.u, p.delta,
-                       p.z, p.A, p.D, p.bias, p.out, p.last_state, p.ws_S,
-                       p.ws_sum, p.ws_hin, (const uint32_t*)p.ws_bc, s);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL((scan_kernel<N, NG, BF16, VEC, HAS_Z, AGG, true>), dim3(tasks),
-                     dim3(kLanes * NG), 0, stream, p.u, p.delta, p.z, p.A, p.D,
-                     p.bias, p.out, p.last_state, p.ws_S, p.ws_sum, p.ws_hin,
-                     (const uint32_t*)p.ws_bc, s);
+hipError_t launch_combine(const ScanParams& p, const ScanShape& s, int N,
+                          hipStream_t stream) {
+  const int64_t split_rows = (int64_t)p.split_groups * kLanes;
+  const int64_t threads = split_rows * N;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((threads + 255) / 256)),
+                     dim3(256), 0, stream, p.A, p.last_state, p.ws_S, p.ws_sum,
+                     p.ws_hin, s, N, split_rows);
   return hipGetLastError();
+}
+
+template <int N, int NG, bool BF16, bool VEC, bool HAS_Z>
+hipError_t launch_one(const ScanParams& p, const ScanShape& s, int n_main,
+                      int main_base, int n_agg, hipStream_t stream) {
+  const dim3 grid(n_main + n_agg), block(kLanes * NG);
+  if (p.softplus)
+    hipLaunchKernelGGL((scan_kernel<N, NG, BF16, VEC, HAS_Z, true>), grid, block, 0,
+                       stream, p.u, p.delta, p.z, p.A, p.D, p.bias, p.out,
+                       p.last_state, p.ws_S, p.ws_sum, p.ws_hin,
+                       (const uint32_t*)p.ws_bc, s, n_main, main_base);
+  else
+    hipLaunchKernelGGL((scan_kernel<N, NG, BF16, VEC, HAS_Z, false>), grid, block, 0,
+                       stream, p.u, p.delta, p.z, p.A, p.D, p.bias, p.out,
+                       p.last_state, p.ws_S, p.ws_sum, p.ws_hin,
+                       (const uint32_t*)p.ws_bc, s, n_main, main_base);
+  return hipGetLastError();
+}
+
+template <int N, int NG, bool BF16, bool VEC>
+hipError_t launch_tasks(const ScanParams& p, const ScanShape& s, int n_main,
+                        int main_base, int n_agg, hipStream_t stream) {
+  if (p.z)
+    return launch_one<N, NG, BF16, VEC, true>(p, s, n_main, main_base, n_agg, stream);
+  return launch_one<N, NG, BF16, VEC, false>(p, s, n_main, main_base, n_agg, stream);
 }
 
 template <int N, bool BF16, bool VEC>
@@ -528,25 +571,49 @@ hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (p.split_groups > 0) {
-    e = launch_one<N, NG, BF16, VEC, false, true>(
-        p, s, p.split_groups * (p.segments - 1), stream);
+  if (p.split_groups > 0 && p.whole_groups > 0 && p.side_stream) {
+    // Two streams: the whole groups' main pass on the caller's stream, and
+    // the split groups' chain (aggregate -> combine -> main) beside it on the
+    // side stream, so that the chain runs on the CUs' spare workgroup slots.
+    hipStream_t side = (hipStream_t)p.side_stream;
+    e = hipEventRecord((hipEvent_t)p.ev_fork, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side, (hipEvent_t)p.ev_fork, 0);
     if (e != hipSuccess) return e;
-    const int64_t split_rows = (int64_t)p.split_groups * kLanes;
-    const int64_t threads = split_rows * N;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((threads + 255) / 256)),
-                       dim3(256), 0, stream, p.A, p.last_state, p.ws_S,
-                       p.ws_sum, p.ws_hin, s, N, split_rows);
-    e = hipGetLastError();
+    e = launch_tasks<N, NG, BF16, VEC>(p, s, 0, 0, p.split_groups * (p.segments - 1), side);
     if (e != hipSuccess) return e;
+    e = launch_combine(p, s, N, side);
+    if (e != hipSuccess) return e;
+    e = launch_tasks<N, NG, BF16, VEC>(p, s, p.split_groups * p.segments,
+                                       p.whole_groups, 0, side);
+    if (e != hipSuccess) return e;
+    e = hipEventRecord((hipEvent_t)p.ev_join, side);
+    if (e != hipSuccess) return e;
+    if (p.ev_start) {
+      e = hipEventRecord((hipEvent_t)p.ev_start, stream);
+      if (e != hipSuccess) return e;
+    }
+    e = launch_tasks<N, NG, BF16, VEC>(p, s, p.whole_groups, 0, 0, stream);
+    if (e == hipSuccess && p.ev_stop) e = hipEventRecord((hipEvent_t)p.ev_stop, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, (hipEvent_t)p.ev_join, 0);
+    return e;
   }
-  const int tasks = p.whole_groups + p.split_groups * p.segments;
   if (p.ev_start) {
     e = hipEventRecord((hipEvent_t)p.ev_start, stream);
     if (e != hipSuccess) return e;
   }
-  e = p.z ? launch_one<N, NG, BF16, VEC, true, false>(p, s, tasks, stream)
-          : launch_one<N, NG, BF16, VEC, false, false>(p, s, tasks, stream);
+  if (p.split_groups > 0) {
+    // one stream: whole groups' main pass + split groups' aggregate pass in
+    // one launch, then the segment initial states, then the split groups'
+    // main pass
+    e = launch_tasks<N, NG, BF16, VEC>(p, s, p.whole_groups, 0,
+                                       p.split_groups * (p.segments - 1), stream);
+    if (e == hipSuccess) e = launch_combine(p, s, N, stream);
+    if (e == hipSuccess)
+      e = launch_tasks<N, NG, BF16, VEC>(p, s, p.split_groups * p.segments,
+                                         p.whole_groups, 0, stream);
+  } else {
+    e = launch_tasks<N, NG, BF16, VEC>(p, s, p.whole_groups, 0, 0, stream);
+  }
   if (e == hipSuccess && p.ev_stop) e = hipEventRecord((hipEvent_t)p.ev_stop, stream);
   return e;
 }
