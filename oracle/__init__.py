@@ -53,6 +53,8 @@ def _open(path):
                                          ctypes.c_double, ctypes.c_double,
                                          cint, _D, _D, _D]
     lib.mssm_oracle_scan_row.restype = None
+    lib.mssm_oracle_scan_bwd.argtypes = [i64, i64, i64, i64] + [_D] * 8 + [cint] + [_D] * 12
+    lib.mssm_oracle_scan_bwd.restype = cint
     return lib
 
 
@@ -132,6 +134,33 @@ class Oracle:
             _ptr(h0), _ptr(out), _ptr(last))
         return out, last
 
+    def scan_bwd(self, u, delta, A, B, C, dout, D=None, z=None,
+                 delta_bias=None, softplus=True, h0=None, dlast=None):
+        """Gradients of the scan for the loss sum(dout * out) +
+        sum(dlast * last_state).  Returns a dict of fp64 arrays: du, ddelta
+        (batch, dim, L), dA (dim, N), dB, dC (batch, L, N), dD, ddelta_bias
+        (dim,), dz (batch, dim, L; None without z), dh0 (batch, dim, N)."""
+        u, delta, A, B, C, dout = map(_f64, (u, delta, A, B, C, dout))
+        D, z, delta_bias, h0, dlast = map(_f64, (D, z, delta_bias, h0, dlast))
+        batch, dim, L = u.shape
+        N = A.shape[1]
+        assert dout.shape == u.shape and B.shape == (batch, L, N)
+        assert dlast is None or dlast.shape == (batch, dim, N)
+        o = dict(du=np.empty_like(u), ddelta=np.empty_like(u),
+                 dz=np.empty_like(u) if z is not None else None,
+                 dA=np.empty((dim, N)), dB=np.empty((batch, L, N)),
+                 dC=np.empty((batch, L, N)), dD=np.empty(dim),
+                 ddelta_bias=np.empty(dim), dh0=np.empty((batch, dim, N)))
+        rc = self._lib.mssm_oracle_scan_bwd(
+            batch, dim, N, L, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+            _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)), _ptr(h0),
+            _ptr(dout), _ptr(dlast), _ptr(o["du"]), _ptr(o["ddelta"]),
+            _ptr(o["dz"]), _ptr(o["dA"]), _ptr(o["dB"]), _ptr(o["dC"]),
+            _ptr(o["dD"]), _ptr(o["ddelta_bias"]), _ptr(o["dh0"]))
+        if rc != 0:
+            raise ValueError("oracle: scan_bwd failed (%d)" % rc)
+        return o
+
     def state_update(self, state, x, dt, A, B, C, D=None, z=None,
                      dt_bias=None, softplus=True, nthreads=None):
         """Single-token decode step in fp64.
@@ -180,3 +209,8 @@ def scan_row(*args, **kwargs):
 def state_update(*args, **kwargs):
     """Single-token decode step in fp64 (see Oracle.state_update)."""
     return _get().state_update(*args, **kwargs)
+
+
+def scan_bwd(*args, **kwargs):
+    """Gradients of the scan in fp64 (see Oracle.scan_bwd)."""
+    return _get().scan_bwd(*args, **kwargs)

@@ -43,6 +43,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 /* tau_Delta = softplus, evaluated without a large-x threshold.  For x > 0
  * the form x + log1p(e^-x) avoids overflow; for x <= 0 log1p(e^x) keeps
@@ -169,6 +170,149 @@ int mssm_oracle_state_update(int64_t batch, int64_t dim, int64_t dstate,
                              D ? D[d] : 0.0, dt_bias ? dt_bias[d] : 0.0,
                              softplus, h, out + r, h);
     }
+    return 0;
+}
+
+/*
+ * Gradients of one row of the scan (the reverse of mssm_oracle_scan_row).
+ *
+ * With the loss sum_t dout_t * out_t + sum_n dlast[n] * last_state[n], the
+ * chain rule through the recurrence above gives, backwards in time, the
+ * total gradient of the state
+ *     g_t[n] = dy_t * C_t[n] + exp(Delta_{t+1} A[n]) * g_{t+1}[n],
+ *     g_{L-1} = dlast + dy_{L-1} C_{L-1},   dy_t = dout_t * silu(z_t),
+ * and from it every input's gradient (the derivative of each forward step
+ * written out; softplus'(x) = sigmoid(x), silu'(z) = s(z)(1 + z(1 - s(z)))):
+ *     du_t     = dy_t D + sum_n g_t[n] Delta_t B_t[n]
+ *     dDelta_t = sum_n g_t[n] (B_t[n] u_t + A[n] exp(Delta_t A[n]) h_{t-1}[n])
+ *     ddelta_t = dDelta_t * softplus'(delta_t + bias)   (or dDelta_t)
+ *     dz_t     = dout_t * y_t * silu'(z_t)
+ *     dA[n]   += sum_t g_t[n] Delta_t exp(Delta_t A[n]) h_{t-1}[n]
+ *     dB_t[n] += g_t[n] Delta_t u_t       dC_t[n] += dy_t h_t[n]
+ *     dD      += sum_t dy_t u_t           dbias   += sum_t ddelta_t
+ *     dh0[n]   = exp(Delta_0 A[n]) g_0[n]
+ * du, ddelta, dz are written; dA (dstate), dB_b, dC_b (seqlen x dstate),
+ * *dD and *dbias are ADDED to (they sum over rows).  z, h0, dlast, dz, dh0
+ * may be NULL.  Uses a scratch of 2 * seqlen * dstate + 3 * seqlen doubles.
+ */
+void mssm_oracle_scan_bwd_row(int64_t seqlen, int64_t dstate,
+                              const double *u, const double *delta,
+                              const double *z, const double *A_row,
+                              const double *B_b, const double *C_b,
+                              double D_d, double bias_d, int softplus,
+                              const double *h0, const double *dout,
+                              const double *dlast, double *du, double *ddelta,
+                              double *dz, double *dA_row, double *dB_b,
+                              double *dC_b, double *dD, double *dbias,
+                              double *dh0, double *scratch)
+{
+    double *H = scratch;                      /* h_t, seqlen x dstate */
+    double *E = H + seqlen * dstate;          /* exp(Delta_t A), same */
+    double *DT = E + seqlen * dstate;         /* Delta_t */
+    double *X = DT + seqlen;                  /* delta_t + bias */
+    double *Y = X + seqlen;                   /* y_t before the gate */
+    double g[64];
+    int64_t n, t;
+
+    /* forward again, keeping every state */
+    for (t = 0; t < seqlen; ++t) {
+        double x = delta[t] + bias_d;
+        double dt = softplus ? oracle_softplus(x) : x;
+        double y = 0.0;
+        X[t] = x;
+        DT[t] = dt;
+        for (n = 0; n < dstate; ++n) {
+            double prev = t > 0 ? H[(t - 1) * dstate + n] : (h0 ? h0[n] : 0.0);
+            double e = exp(dt * A_row[n]);
+            E[t * dstate + n] = e;
+            H[t * dstate + n] = e * prev + dt * B_b[t * dstate + n] * u[t];
+            y += C_b[t * dstate + n] * H[t * dstate + n];
+        }
+        Y[t] = y + D_d * u[t];
+    }
+
+    for (n = 0; n < dstate; ++n)
+        g[n] = dlast ? dlast[n] : 0.0;
+
+    for (t = seqlen - 1; t >= 0; --t) {
+        double dy, ddt = 0.0, dut;
+        if (z) {
+            double sg = 1.0 / (1.0 + exp(-z[t]));
+            dy = dout[t] * z[t] * sg;
+            if (dz)
+                dz[t] = dout[t] * Y[t] * sg * (1.0 + z[t] * (1.0 - sg));
+        } else {
+            dy = dout[t];
+        }
+        dut = dy * D_d;
+        *dD += dy * u[t];
+        for (n = 0; n < dstate; ++n) {
+            double prev = t > 0 ? H[(t - 1) * dstate + n] : (h0 ? h0[n] : 0.0);
+            double e = E[t * dstate + n];
+            double Bn = B_b[t * dstate + n];
+            g[n] += dy * C_b[t * dstate + n];
+            dC_b[t * dstate + n] += dy * H[t * dstate + n];
+            dB_b[t * dstate + n] += g[n] * DT[t] * u[t];
+            dut += g[n] * DT[t] * Bn;
+            ddt += g[n] * (Bn * u[t] + A_row[n] * e * prev);
+            dA_row[n] += g[n] * DT[t] * e * prev;
+            g[n] *= e;
+        }
+        du[t] = dut;
+        if (softplus)
+            ddt *= 1.0 / (1.0 + exp(-X[t]));
+        ddelta[t] = ddt;
+        *dbias += ddt;
+    }
+    if (dh0)
+        for (n = 0; n < dstate; ++n)
+            dh0[n] = g[n];
+}
+
+/*
+ * Gradients of the whole scan (serial over rows; the oracle is for tests).
+ * Shapes as mssm_oracle_scan; dout (batch, dim, seqlen); dlast, dh0
+ * (batch, dim, dstate) or NULL; outputs du, ddelta, dz (batch, dim, seqlen),
+ * dA (dim, dstate), dB, dC (batch, seqlen, dstate), dD, dbias (dim), all
+ * overwritten.  Returns 0, -1 for an unsupported dstate, -2 if out of memory.
+ */
+int mssm_oracle_scan_bwd(int64_t batch, int64_t dim, int64_t dstate,
+                         int64_t seqlen, const double *u, const double *delta,
+                         const double *A, const double *B, const double *C,
+                         const double *D, const double *z,
+                         const double *delta_bias, int softplus,
+                         const double *h0, const double *dout,
+                         const double *dlast, double *du, double *ddelta,
+                         double *dz, double *dA, double *dB, double *dC,
+                         double *dD, double *dbias, double *dh0)
+{
+    int64_t r, i;
+    double *scratch;
+    if (dstate < 1 || dstate > 64)
+        return -1;
+    scratch = (double *)malloc(sizeof(double) * (size_t)(2 * seqlen * dstate + 3 * seqlen));
+    if (!scratch)
+        return -2;
+    for (i = 0; i < dim * dstate; ++i)
+        dA[i] = 0.0;
+    for (i = 0; i < batch * seqlen * dstate; ++i)
+        dB[i] = dC[i] = 0.0;
+    for (i = 0; i < dim; ++i)
+        dD[i] = dbias[i] = 0.0;
+    for (r = 0; r < batch * dim; ++r) {
+        int64_t b = r / dim, d = r % dim;
+        size_t row = (size_t)r * (size_t)seqlen;
+        size_t bc = (size_t)b * (size_t)seqlen * (size_t)dstate;
+        mssm_oracle_scan_bwd_row(
+            seqlen, dstate, u + row, delta + row, z ? z + row : NULL,
+            A + d * dstate, B + bc, C + bc, D ? D[d] : 0.0,
+            delta_bias ? delta_bias[d] : 0.0, softplus,
+            h0 ? h0 + r * dstate : NULL, dout + row,
+            dlast ? dlast + r * dstate : NULL, du + row, ddelta + row,
+            dz ? dz + row : NULL, dA + d * dstate, dB + bc, dC + bc, dD + d,
+            dbias + d, dh0 ? dh0 + r * dstate : NULL, scratch);
+    }
+    free(scratch);
     return 0;
 }
 

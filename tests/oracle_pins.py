@@ -333,3 +333,77 @@ PINS = [
     pin_channel_permutation,
     pin_decode_equals_scan,
 ]
+
+
+# ------------------------------------------------------------- gradients
+
+def _loss(orc, args, softplus, h0, dout, dlast):
+    out, last = orc.scan(**args, softplus=softplus, h0=h0)
+    return float((dout * out).sum() + (dlast * last).sum())
+
+
+def pin_bwd_finite_differences(orc):
+    """Every gradient of the oracle's backward against central differences of
+    the (pinned) forward oracle, loss = sum(dout*out) + sum(dlast*last_state),
+    step 1e-6 (truncation error O(1e-12) relative)."""
+    for softplus in (True, False):
+        args, h0 = random_case(91 + softplus, batch=2, dim=3, L=9, N=3)
+        if not softplus:
+            args = dict(args, delta=np.abs(args["delta"]) * 0.3 + 0.05,
+                        delta_bias=np.abs(args["delta_bias"]) * 0.1)
+        rng = np.random.default_rng(93)
+        dout = rng.standard_normal(args["u"].shape)
+        dlast = rng.standard_normal(h0.shape)
+        g = orc.scan_bwd(args["u"], args["delta"], args["A"], args["B"], args["C"],
+                         dout, D=args["D"], z=args["z"],
+                         delta_bias=args["delta_bias"], softplus=softplus, h0=h0,
+                         dlast=dlast)
+        eps = 1e-6
+        pairs = [("u", "du"), ("delta", "ddelta"), ("z", "dz"), ("A", "dA"),
+                 ("B", "dB"), ("C", "dC"), ("D", "dD"),
+                 ("delta_bias", "ddelta_bias"), ("h0", "dh0")]
+        for name, gname in pairs:
+            base = h0 if name == "h0" else args[name]
+            fd = np.empty_like(base)
+            for idx in np.ndindex(base.shape):
+                p, m = base.copy(), base.copy()
+                p[idx] += eps
+                m[idx] -= eps
+                if name == "h0":
+                    lp = _loss(orc, args, softplus, p, dout, dlast)
+                    lm = _loss(orc, args, softplus, m, dout, dlast)
+                else:
+                    lp = _loss(orc, dict(args, **{name: p}), softplus, h0, dout, dlast)
+                    lm = _loss(orc, dict(args, **{name: m}), softplus, h0, dout, dlast)
+                fd[idx] = (lp - lm) / (2 * eps)
+            _close(g[gname], fd, rtol=1e-6, atol=1e-7,
+                   what="d%s softplus=%s" % (name, softplus))
+
+
+def pin_bwd_zero_b_closed_form(orc):
+    """B = 0, no gate, D = 0: out_t = sum_n C_t[n] exp(A[n] S_t) h0[n] with
+    S_t the running sum of Delta, so dC_t[n] = dout_t exp(A[n] S_t) h0[n] and
+    dh0[n] = sum_t dout_t C_t[n] exp(A[n] S_t) exactly; du = dB * 0 terms
+    vanish except du_t = sum_n g_t[n] Delta_t B_t[n] = 0."""
+    rng = np.random.default_rng(97)
+    L, N = 11, 4
+    dt = np.abs(rng.standard_normal(L)) * 0.2 + 0.01
+    A = -rng.uniform(0.3, 2.0, N)
+    C = rng.standard_normal((L, N))
+    h0 = rng.standard_normal(N)
+    dout = rng.standard_normal(L)
+    args = _row_inputs(L, N, dt, A, np.zeros((L, N)), C, rng.standard_normal(L))
+    g = orc.scan_bwd(args["u"], args["delta"], args["A"], args["B"], args["C"],
+                     dout.reshape(1, 1, L), D=np.zeros(1), z=None,
+                     delta_bias=np.zeros(1), softplus=False,
+                     h0=h0.reshape(1, 1, N), dlast=None)
+    S = np.cumsum(dt)
+    E = np.exp(np.outer(S, A))                       # (L, N)
+    _close(g["dC"][0], dout[:, None] * E * h0[None, :], rtol=1e-13, atol=1e-15,
+           what="zero-B dC")
+    _close(g["dh0"][0, 0], (dout[:, None] * C * E).sum(0), rtol=1e-13, atol=1e-15,
+           what="zero-B dh0")
+    _close(g["du"][0, 0], np.zeros(L), rtol=0, atol=1e-15, what="zero-B du")
+
+
+PINS += [pin_bwd_finite_differences, pin_bwd_zero_b_closed_form]

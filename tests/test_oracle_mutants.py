@@ -36,6 +36,23 @@ MUTANTS = [
     ("decode_B_of_batch0", "B + b * dstate, C + b * dstate", "B, C"),
     ("decode_state_not_written", "softplus, h, out + r, h);", "softplus, h, out + r, NULL);"),
     ("decode_x_dt_swapped", "x + r, dt + r", "dt + r, x + r"),
+    # backward
+    ("bwd_dy_without_gate", "dy = dout[t] * z[t] * sg;", "dy = dout[t];"),
+    ("bwd_state_grad_not_decayed", "g[n] *= e;", "g[n] *= 1.0;"),
+    ("bwd_dA_uses_new_state", "dA_row[n] += g[n] * DT[t] * e * prev;",
+     "dA_row[n] += g[n] * DT[t] * H[t * dstate + n];"),
+    ("bwd_softplus_derivative", "ddt *= 1.0 / (1.0 + exp(-X[t]));", "ddt *= exp(X[t]);"),
+    ("bwd_dC_uses_state_grad", "dC_b[t * dstate + n] += dy * H[t * dstate + n];",
+     "dC_b[t * dstate + n] += g[n] * H[t * dstate + n];"),
+    ("bwd_dB_without_delta", "dB_b[t * dstate + n] += g[n] * DT[t] * u[t];",
+     "dB_b[t * dstate + n] += g[n] * u[t];"),
+    ("bwd_dz_without_silu_derivative", "dz[t] = dout[t] * Y[t] * sg * (1.0 + z[t] * (1.0 - sg));",
+     "dz[t] = dout[t] * Y[t] * sg;"),
+    ("bwd_readout_grad_after_use",
+     "g[n] += dy * C_b[t * dstate + n];\n            dC_b[t * dstate + n] += dy * H[t * dstate + n];\n            dB_b[t * dstate + n] += g[n] * DT[t] * u[t];",
+     "dC_b[t * dstate + n] += dy * H[t * dstate + n];\n            dB_b[t * dstate + n] += g[n] * DT[t] * u[t];\n            g[n] += dy * C_b[t * dstate + n];"),
+    ("bwd_dh0_dropped", "dh0[n] = g[n];", "dh0[n] = 0.0;"),
+    ("bwd_dD_missing", "*dD += dy * u[t];", "*dD += 0.0 * u[t];"),
 ]
 
 
@@ -45,8 +62,10 @@ def test_pins_catch_mutant(tmp_path, name, old, new):
     olds = old if isinstance(old, list) else [old]
     news = new if isinstance(new, list) else [new]
     for o, n in zip(olds, news):
-        assert src.count(o) == 1, "mutation site for %s not unique/found" % name
-        src = src.replace(o, n)
+        # the first occurrence: the forward scan's own code comes before the
+        # backward's recomputation of it
+        assert src.count(o) >= 1, "mutation site for %s not found" % name
+        src = src.replace(o, n, 1)
     path = os.path.join(tmp_path, "mutant.c")
     with open(path, "w") as f:
         f.write(src)
