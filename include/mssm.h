@@ -112,6 +112,45 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
                             const mssm_dims* dims, void* stream);
 
 /*
+ * Backward of the forward scan: the gradients of
+ *     loss = sum(dout * out) + sum(dlast * h_{L-1})
+ * with respect to every input, for training through the scan (page "Mamba:
+ * Selective State Space Models", "Mathematical Foundation / Efficient Scan",
+ * which trains with the parallel scan; and "Comparison with Transformers":
+ * training memory linear in the sequence length).  The states h_t are not
+ * stored by the forward call: this call rescans the rows, keeps the state at
+ * every 16th step in workspace, and recomputes each 16-step tile from it.
+ *   u, delta, A, B, C, D, z, delta_bias, softplus : as in the forward call
+ *   h0          : (batch, dim, dstate) fp32 initial state, or NULL (zero)
+ *   dout        : (batch, dim, seqlen) io dtype, gradient of out (required)
+ *   dlast       : (batch, dim, dstate) fp32 gradient of the final state, or
+ *                 NULL (zero)
+ * Outputs (device memory owned by the caller, fully overwritten):
+ *   du, ddelta  : (batch, dim, seqlen) io dtype (ddelta is the gradient of
+ *                 the raw delta, through bias and softplus)
+ *   dz          : (batch, dim, seqlen) io dtype; required iff z != NULL
+ *   dA          : (dim, dstate) fp32, summed over the batch
+ *   dB, dC      : (batch, seqlen, dstate) fp32, summed over channels
+ *   dD, ddelta_bias : (dim) fp32 or NULL (not written), summed over batch
+ *                 and time; written even when D / delta_bias are NULL (the
+ *                 gradient at zero)
+ *   dh0         : (batch, dim, dstate) fp32 gradient of h0, or NULL
+ * No output may overlap an input or another output.  flags and
+ * time_segments must be 0.  The sums over channels and the batch are taken
+ * in a fixed order, so repeated calls give identical bits.  Stream-ordered
+ * workspace: about 4 * dstate bytes per element of u plus 8 * dstate bytes
+ * per token for each 64-channel group, returned on the same stream.
+ */
+int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
+                            const void* B, const void* C, const float* D,
+                            const void* z, const float* delta_bias,
+                            int softplus, const float* h0, const void* dout,
+                            const float* dlast, void* du, void* ddelta,
+                            float* dA, float* dB, float* dC, float* dD,
+                            void* dz, float* ddelta_bias, float* dh0,
+                            const mssm_dims* dims, void* stream);
+
+/*
  * Single-token decode step: the scan with seqlen = 1 starting from `state`,
  * which is updated in place.
  *   state       : (batch, dim, dstate) fp32, in/out
@@ -149,7 +188,8 @@ int mssm_selective_scan_fwd_plan(const mssm_dims* dims, mssm_plan* plan);
  * Timing hook for benchmarks.  With both handles non-NULL (hipEvent_t, owned
  * by the caller), every later forward scan issued from this thread records
  * `start` on its stream right before the main scan kernel and `stop` right
- * after it, so hipEventElapsedTime(start, stop) is that kernel's duration.
+ * after it (the backward call does the same around its main kernel), so
+ * hipEventElapsedTime(start, stop) is that kernel's duration.
  * Both NULL turns the hook off; one NULL is MSSM_ERR_NULL.  Per thread.
  */
 int mssm_set_scan_timing_events(void* start, void* stop);

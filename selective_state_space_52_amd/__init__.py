@@ -19,7 +19,8 @@ import torch
 from ._lib import (MSSM_BF16, MSSM_F32, MSSM_FLAG_LOAD_STATE, Dims, MssmError,
                    Plan, check, lib)
 
-__all__ = ["selective_scan_fwd", "selective_state_update", "scan_plan",
+__all__ = ["selective_scan_fwd", "selective_scan_bwd", "selective_state_update",
+           "scan_plan",
            "set_scan_timing_events", "MssmError", "abi_version"]
 
 _IO = {torch.float32: MSSM_F32, torch.bfloat16: MSSM_BF16}
@@ -106,6 +107,56 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
             _ptr(delta_bias), int(bool(softplus)), _ptr(out), _ptr(last_state),
             dims, _stream(dev)))
     return out
+
+
+def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None,
+                       delta_bias=None, softplus=True, h0=None, dlast=None,
+                       want_dh0=False):
+    """Gradients of the forward scan for the loss
+    sum(dout * out) + sum(dlast * last_state).
+
+    Inputs as in selective_scan_fwd; h0 (batch, dim, N) fp32 is the initial
+    state (None = zero), dout (batch, dim, L) in the io dtype, dlast
+    (batch, dim, N) fp32 or None.  Returns a dict: du, ddelta, dz (io dtype,
+    dz only with z), dA (dim, N), dB, dC (batch, L, N), dD, ddelta_bias (dim,)
+    and, with want_dh0, dh0 (batch, dim, N), all fp32 except the first three.
+    """
+    if u.dtype not in _IO:
+        raise ValueError("u must be float32 or bfloat16")
+    io = u.dtype
+    batch, dim, L = u.shape
+    N = A.shape[-1]
+    dev = u.device
+    _need(u, "u", io, (batch, dim, L), dev)
+    _need(delta, "delta", io, (batch, dim, L), dev)
+    _need(z, "z", io, (batch, dim, L), dev)
+    _need(dout, "dout", io, (batch, dim, L), dev)
+    _need(B, "B", io, (batch, L, N), dev)
+    _need(C, "C", io, (batch, L, N), dev)
+    _need(A, "A", torch.float32, (dim, N), dev)
+    _need(D, "D", torch.float32, (dim,), dev)
+    _need(delta_bias, "delta_bias", torch.float32, (dim,), dev)
+    _need(h0, "h0", torch.float32, (batch, dim, N), dev)
+    _need(dlast, "dlast", torch.float32, (batch, dim, N), dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(du=torch.empty((batch, dim, L), dtype=io, device=dev),
+             ddelta=torch.empty((batch, dim, L), dtype=io, device=dev),
+             dz=torch.empty((batch, dim, L), dtype=io, device=dev) if z is not None else None,
+             dA=torch.empty((dim, N), **f32),
+             dB=torch.empty((batch, L, N), **f32),
+             dC=torch.empty((batch, L, N), **f32),
+             dD=torch.empty((dim,), **f32),
+             ddelta_bias=torch.empty((dim,), **f32),
+             dh0=torch.empty((batch, dim, N), **f32) if want_dh0 else None)
+    dims = Dims(batch, dim, N, L, _IO[io], 0, 0, 0)
+    with torch.cuda.device(dev):
+        check(lib().mssm_selective_scan_bwd(
+            _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(delta_bias), int(bool(softplus)), _ptr(h0), _ptr(dout),
+            _ptr(dlast), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
+            _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
+            _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), dims, _stream(dev)))
+    return g
 
 
 def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,

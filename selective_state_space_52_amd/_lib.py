@@ -18,7 +18,8 @@ STATUS = {
 }
 
 # every symbol include/mssm.h declares
-EXPORTS = ("mssm_selective_scan_fwd", "mssm_selective_state_update",
+EXPORTS = ("mssm_selective_scan_fwd", "mssm_selective_scan_bwd",
+           "mssm_selective_state_update",
            "mssm_selective_scan_fwd_plan", "mssm_set_scan_timing_events",
            "mssm_status_string", "mssm_last_error", "mssm_abi_version")
 
@@ -58,6 +59,11 @@ def lib():
         L.mssm_selective_scan_fwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i,
                                               vp, fp, ctypes.POINTER(Dims), vp]
         L.mssm_selective_scan_fwd.restype = i
+        L.mssm_selective_scan_bwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i,
+                                              fp, vp, fp, vp, vp, fp, fp, fp,
+                                              fp, vp, fp, fp,
+                                              ctypes.POINTER(Dims), vp]
+        L.mssm_selective_scan_bwd.restype = i
         L.mssm_selective_state_update.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp,
                                                   fp, i, vp, ctypes.POINTER(Dims), vp]
         L.mssm_selective_state_update.restype = i

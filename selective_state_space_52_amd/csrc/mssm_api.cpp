@@ -320,6 +320,105 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
   return e == hipSuccess ? MSSM_OK : MSSM_ERR_HIP;
 }
 
+int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
+                            const void* B, const void* C, const float* D,
+                            const void* z, const float* delta_bias,
+                            int softplus, const float* h0, const void* dout,
+                            const float* dlast, void* du, void* ddelta,
+                            float* dA, float* dB, float* dC, float* dD,
+                            void* dz, float* ddelta_bias, float* dh0,
+                            const mssm_dims* dims, void* stream) {
+  int rc = check_common_dims(dims);
+  if (rc != MSSM_OK) return rc;
+  if (dims->flags != 0) return MSSM_ERR_UNSUPPORTED;
+  if (dims->time_segments != 0) return MSSM_ERR_DIMS;
+  if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA ||
+      !dB || !dC)
+    return MSSM_ERR_NULL;
+  if ((z == nullptr) != (dz == nullptr)) return MSSM_ERR_NULL;
+
+  const int64_t batch = dims->batch, dim = dims->dim, N = dims->dstate,
+                L = dims->seqlen;
+  const size_t io = dims->io_dtype == MSSM_BF16 ? 2 : 4;
+  const int64_t lim = INT64_MAX / 64;
+  const int64_t gpb = (dim + kLanes - 1) / kLanes;
+  if (L > INT32_MAX - 64 || !product_ok(batch, dim, L, lim) ||
+      !product_ok(batch, L, N, lim) || !product_ok(batch, dim, N, lim) ||
+      !product_ok(batch * gpb, L + 64, 2 * N * kLanes, lim) ||
+      batch * gpb > INT32_MAX)
+    return MSSM_ERR_DIMS;
+
+  const void* ios[] = {u, delta, z, dout, B, C, du, ddelta, dz};
+  for (const void* p : ios)
+    if (p && !aligned(p, io)) return MSSM_ERR_ALIGN;
+  const void* f32s[] = {A, D, delta_bias, h0, dlast, dA, dB, dC, dD,
+                        ddelta_bias, dh0};
+  for (const void* p : f32s)
+    if (p && !aligned(p, 4)) return MSSM_ERR_ALIGN;
+
+  const int64_t ebytes = batch * dim * L * (int64_t)io;
+  const int64_t bcbytes = batch * L * N * (int64_t)io;
+  const int64_t sbytes = batch * dim * N * 4;
+  const Range outs[] = {range_of(du, ebytes),          range_of(ddelta, ebytes),
+                        range_of(dz, ebytes),          range_of(dA, dim * N * 4),
+                        range_of(dB, batch * L * N * 4),
+                        range_of(dC, batch * L * N * 4), range_of(dD, dim * 4),
+                        range_of(ddelta_bias, dim * 4), range_of(dh0, sbytes)};
+  const Range ins[] = {range_of(u, ebytes),      range_of(delta, ebytes),
+                       range_of(z, ebytes),      range_of(dout, ebytes),
+                       range_of(B, bcbytes),     range_of(C, bcbytes),
+                       range_of(A, dim * N * 4), range_of(D, dim * 4),
+                       range_of(delta_bias, dim * 4), range_of(h0, sbytes),
+                       range_of(dlast, sbytes)};
+  const int n_outs = (int)(sizeof(outs) / sizeof(outs[0]));
+  for (int i = 0; i < n_outs; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return MSSM_ERR_ALIAS;
+    for (int j = i + 1; j < n_outs; ++j)
+      if (overlap(outs[i], outs[j])) return MSSM_ERR_ALIAS;
+  }
+
+  // --- validation done; HIP calls from here on ---
+  const bool vec = (L % 8) == 0 && ((L * (int64_t)io) % 16) == 0 &&
+                   aligned(u, 16) && aligned(delta, 16) && aligned(dout, 16) &&
+                   aligned(du, 16) && aligned(ddelta, 16) &&
+                   (!z || aligned(z, 16)) && (!dz || aligned(dz, 16));
+  const int tile = mssm::bwd_tile();
+  mssm::BwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.u = u; p.delta = delta; p.z = z; p.dout = dout; p.A = A; p.B = B; p.C = C;
+  p.D = D; p.bias = delta_bias; p.h0 = h0; p.dlast = dlast;
+  p.du = du; p.ddelta = ddelta; p.dz = dz; p.dA = dA; p.dB = dB; p.dC = dC;
+  p.dD = dD; p.dbias = ddelta_bias; p.dh0 = dh0;
+  p.batch = batch; p.dim = dim; p.L = L;
+  p.softplus = softplus ? 1 : 0;
+  p.groups_per_batch = (int32_t)gpb;
+  p.tiles = (int32_t)((L + tile - 1) / tile);
+  p.ev_start = g_ev_start;
+  p.ev_stop = g_ev_stop;
+
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t ws_bytes =
+      mssm::bwd_workspace(batch, dim, L, (int)N, io == 2, nullptr, nullptr);
+  void* ws = nullptr;
+  {
+    hipError_t e = hipMallocAsync(&ws, (size_t)ws_bytes, st);
+    if (e != hipSuccess) {
+      set_hip_error("hipMallocAsync(workspace)", e);
+      return MSSM_ERR_HIP;
+    }
+  }
+  mssm::bwd_workspace(batch, dim, L, (int)N, io == 2, ws, &p);
+  hipError_t e = mssm::launch_scan_bwd(p, (int)N, io == 2, vec, st);
+  if (e != hipSuccess) set_hip_error("backward scan launch", e);
+  hipError_t f = hipFreeAsync(ws, st);
+  if (e == hipSuccess && f != hipSuccess) {
+    set_hip_error("hipFreeAsync(workspace)", f);
+    e = f;
+  }
+  return e == hipSuccess ? MSSM_OK : MSSM_ERR_HIP;
+}
+
 int mssm_selective_state_update(float* state, const void* x, const void* dt,
                                 const float* A, const void* B, const void* C,
                                 const float* D, const void* z,

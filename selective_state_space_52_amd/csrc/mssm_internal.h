@@ -66,13 +66,66 @@ struct UpdateParams {
   int32_t softplus;
 };
 
+// One backward-scan call.  Gradients of sum(dout * out) + sum(dlast *
+// last_state) with respect to every input of the forward scan.
+struct BwdParams {
+  const void* u;
+  const void* delta;
+  const void* z;          // may be null (then dz is null)
+  const void* dout;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;         // may be null
+  const float* bias;      // may be null
+  const float* h0;        // may be null (zero initial state)
+  const float* dlast;     // may be null (zero)
+  void* du;
+  void* ddelta;
+  void* dz;               // may be null
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dD;              // may be null
+  float* dbias;           // may be null
+  float* dh0;             // may be null
+  int64_t batch, dim, L;
+  int32_t softplus;
+  int32_t groups_per_batch;
+  int32_t tiles;          // ceil(L / tile); runs and partials hold tiles*tile steps
+  // workspace
+  void* ws_bc;            // B, C packed per wave run, zero-padded to whole tiles
+  float* ws_ck;           // [group][tile][n][lane] state at each tile start
+  float* ws_dbc;          // [b][group in batch][t][B, C][n] channel-group sums
+  float* ws_dA;           // [b][d][n] per-batch dA
+  float* ws_dDb;          // [b][d][dD, dbias] per-batch sums
+  void* ev_start;         // optional timing events around the main kernel
+  void* ev_stop;
+};
+
 // Waves per 64-channel workgroup: each wave owns dstate / waves states.
 int scan_waves_per_group(int N);
+// Repack B and C into per-wave runs for `waves` waves per channel group:
+// `steps` (>= L) timesteps per run, zeros from L on, `run_words` 32-bit words
+// per run.
+hipError_t launch_bc_pack(const void* B, const void* C, void* packed,
+                          int64_t batch, int64_t L, int64_t steps, int N,
+                          int waves, bool bf16, int64_t run_words,
+                          hipStream_t stream);
 // Bytes of the packed B/C runs of one forward call.
 int64_t scan_bc_workspace_bytes(int64_t batch, int64_t L, int N, bool bf16);
 
 hipError_t launch_scan(const ScanParams& p, int N, bool bf16, bool vec,
                        hipStream_t stream);
+// Backward: timesteps per tile, waves per group, workspace bytes, launch.
+int bwd_tile();
+int bwd_waves_per_group(int N);
+// Workspace bytes of one backward call; with ws and p non-null also points
+// p's workspace fields into ws.
+int64_t bwd_workspace(int64_t batch, int64_t dim, int64_t L, int N, bool bf16,
+                      void* ws, BwdParams* p);
+hipError_t launch_scan_bwd(const BwdParams& p, int N, bool bf16, bool vec,
+                           hipStream_t stream);
 hipError_t launch_state_update(const UpdateParams& p, int N, bool bf16,
                                hipStream_t stream);
 

@@ -29,11 +29,11 @@
 // effect on the state is (exp(A * sum Delta), local end state from zero).
 #include "dev_math.h"
 #include "mssm_internal.h"
+#include "scan_common.h"
 
 namespace mssm {
 namespace {
 
-constexpr int kLanes = 64;
 constexpr int kTile = 32;  // timesteps per tile
 constexpr bool kWarmScalarCache = true;
 
@@ -49,167 +49,34 @@ struct ScanShape {
   int64_t seg_len;
 };
 
-// KC consecutive io values of one row, as loaded (bf16 pairs or fp32 words).
-template <bool BF16, int KC>
-struct Raw {
-  static constexpr int W = BF16 ? KC / 2 : KC;
-  uint32_t w[W];
-};
-
-template <bool BF16, int KC>
-__device__ __forceinline__ float raw_get(const Raw<BF16, KC>& r, int k) {
-  if constexpr (BF16)
-    return (k & 1) ? bf16_hi(r.w[k >> 1]) : bf16_lo(r.w[k >> 1]);
-  else
-    return __uint_as_float(r.w[k]);
-}
-
-template <bool BF16, int KC>
-__device__ __forceinline__ void raw_zero(Raw<BF16, KC>& r) {
-#pragma unroll
-  for (int i = 0; i < Raw<BF16, KC>::W; ++i) r.w[i] = 0u;
-}
-
-// Values [t, t + KC) of a row starting at element offset `off`; `nvalid` of
-// them exist (the rest read as 0).  VEC: the row and every 16-byte piece
-// (8-byte when a chunk is only 4 bf16 values) are aligned, and a piece is
-// either whole or absent.
-template <bool BF16, bool VEC, int KC>
-__device__ __forceinline__ void load_chunk(Raw<BF16, KC>& r, const void* base,
-                                           int64_t off, int64_t nvalid) {
-  constexpr int W = Raw<BF16, KC>::W;
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(
-      static_cast<const char*>(base) + off * (BF16 ? 2 : 4));
-  if constexpr (VEC) {
-    constexpr int PV = BF16 ? 2 : 1;  // values per 32-bit word
-    if constexpr (W >= 4) {
-#pragma unroll
-      for (int q = 0; q < W / 4; ++q) {
-        if (4 * q * PV < nvalid) {
-          const uint4 v = reinterpret_cast<const uint4*>(src)[q];
-          r.w[4 * q] = v.x; r.w[4 * q + 1] = v.y; r.w[4 * q + 2] = v.z; r.w[4 * q + 3] = v.w;
-        } else {
-          r.w[4 * q] = r.w[4 * q + 1] = r.w[4 * q + 2] = r.w[4 * q + 3] = 0u;
-        }
-      }
-    } else {
-      static_assert(W == 2, "chunk of 4 bf16 values");
-      if (nvalid > 0) {
-        const uint2 v = *reinterpret_cast<const uint2*>(src);
-        r.w[0] = v.x; r.w[1] = v.y;
-      } else {
-        r.w[0] = r.w[1] = 0u;
-      }
-    }
-  } else {
-    if constexpr (BF16) {
-      const uint16_t* s = static_cast<const uint16_t*>(base) + off;
-#pragma unroll
-      for (int i = 0; i < W; ++i) {
-        const uint32_t lo = (2 * i < nvalid) ? s[2 * i] : 0u;
-        const uint32_t hi = (2 * i + 1 < nvalid) ? s[2 * i + 1] : 0u;
-        r.w[i] = lo | (hi << 16);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < W; ++i) r.w[i] = (i < nvalid) ? src[i] : 0u;
-    }
-  }
-}
-
-template <bool BF16, bool VEC, int KC>
-__device__ __forceinline__ void store_chunk(void* base, int64_t off,
-                                            const float (&o)[KC],
-                                            int64_t nvalid) {
-  if (VEC && nvalid >= KC) {
-    uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<char*>(base) +
-                                                off * (BF16 ? 2 : 4));
-    constexpr int W = BF16 ? KC / 2 : KC;
-    uint32_t w[W];
-#pragma unroll
-    for (int i = 0; i < W; ++i)
-      w[i] = BF16 ? pack_bf16x2(o[2 * i], o[2 * i + 1]) : __float_as_uint(o[i]);
-    if constexpr (W >= 4) {
-#pragma unroll
-      for (int q = 0; q < W / 4; ++q)
-        reinterpret_cast<uint4*>(dst)[q] =
-            make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
-    } else {
-      *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
-    }
-  } else if constexpr (BF16) {
-    uint16_t* dst = static_cast<uint16_t*>(base) + off;
-#pragma unroll
-    for (int k = 0; k < KC; ++k)
-      if (k < nvalid) dst[k] = to_bf16(o[k]);
-  } else {
-    float* dst = static_cast<float*>(base) + off;
-#pragma unroll
-    for (int k = 0; k < KC; ++k)
-      if (k < nvalid) dst[k] = o[k];
-  }
-}
-
-// B_t and C_t packed for the scan, in the io dtype, laid out
-// [b][wave g][t][B_t[n0..n0+NPW), C_t[n0..n0+NPW)] so that one wave's values
-// for a batch of consecutive tokens are one contiguous 64-byte run read by a
-// single wide scalar load (the address is the same for every lane).  bf16
-// stays packed two to a word and is widened where it is used, which keeps the
-// scalar-cache footprint of the runs small.
-template <int NPW, bool BF16>
-struct BCLayout {
-  static constexpr int kWordsPerStep = BF16 ? NPW : 2 * NPW;  // 32-bit words
-  static constexpr int kSteps = 16 / kWordsPerStep;           // per 64 B batch
-};
-
-// words of one wave's run, padded to whole 64-byte batches
-__host__ __device__ inline int64_t bc_run_words(int64_t L, int words_per_step) {
-  return (L * words_per_step + 15) / 16 * 16;
-}
-
-template <int NPW, bool BF16>
-struct alignas(16) BCBatch {
-  uint32_t w[16];
-};
-
-// value j (B for j < NPW, C after) of token i of a batch (or a raw run)
-template <int NPW, bool BF16>
-__device__ __forceinline__ float bc_val(const uint32_t* w, int i, int j) {
-  constexpr int WPS = BCLayout<NPW, BF16>::kWordsPerStep;
-  if constexpr (BF16) {
-    const uint32_t x = w[i * WPS + (j >> 1)];
-    return (j & 1) ? bf16_hi(x) : bf16_lo(x);
-  } else {
-    return __uint_as_float(w[i * WPS + j]);
-  }
-}
-
+// Writes the packed runs of `steps` timesteps per wave (steps >= L; the
+// timesteps from L on are written as zeros) with `run_words` words per run.
 __global__ void __launch_bounds__(256)
     bc_pack_kernel(const void* __restrict__ Bm, const void* __restrict__ Cm,
-                   void* __restrict__ packed, int64_t batch, int64_t L, int N,
-                   int NG, int bf16) {
+                   void* __restrict__ packed, int64_t batch, int64_t L,
+                   int64_t steps, int N, int NG, int bf16, int64_t run_words) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = batch * L * 2 * N;
+  const int64_t total = batch * steps * 2 * N;
   if (i >= total) return;
   const int npw = N / NG;
   // i indexes the values in order [b][g][t][j], j < 2*npw
   const int j = (int)(i % (2 * npw));
   const int64_t r = i / (2 * npw);
-  const int64_t t = r % L;
-  const int64_t bg = r / L;
+  const int64_t t = r % steps;
+  const int64_t bg = r / steps;
   const int g = (int)(bg % NG);
   const int64_t b = bg / NG;
   const int n = g * npw + (j < npw ? j : j - npw);
   const int64_t src = (b * L + t) * N + n;
   const void* m = j < npw ? Bm : Cm;
-  const int wps = bf16 ? npw : 2 * npw;          // words per token
   const int64_t vals_per_word = bf16 ? 2 : 1;
-  // destination: wave run bg, padded to whole batches
-  const int64_t dst = bg * bc_run_words(L, wps) * vals_per_word + t * 2 * npw + j;
+  const int64_t dst = bg * run_words * vals_per_word + t * 2 * npw + j;
   if (bf16)
-    static_cast<uint16_t*>(packed)[dst] = static_cast<const uint16_t*>(m)[src];
+    static_cast<uint16_t*>(packed)[dst] =
+        t < L ? static_cast<const uint16_t*>(m)[src] : (uint16_t)0;
   else
-    static_cast<float*>(packed)[dst] = static_cast<const float*>(m)[src];
+    static_cast<float*>(packed)[dst] =
+        t < L ? static_cast<const float*>(m)[src] : 0.0f;
 }
 
 // Main pass (AGG = false): scans each task's time range from its initial
@@ -564,11 +431,9 @@ hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
   s.seg_len = p.seg_len;
   hipError_t e;
   {
-    const int64_t total = p.batch * p.L * 2 * N;
-    hipLaunchKernelGGL(bc_pack_kernel, dim3((unsigned)((total + 255) / 256)),
-                       dim3(256), 0, stream, p.B, p.C, p.ws_bc, p.batch, p.L, N,
-                       NG, BF16 ? 1 : 0);
-    e = hipGetLastError();
+    constexpr int WPS = BCLayout<N / NG, BF16>::kWordsPerStep;
+    e = launch_bc_pack(p.B, p.C, p.ws_bc, p.batch, p.L, p.L, N, NG, BF16,
+                       bc_run_words(p.L, WPS), stream);
     if (e != hipSuccess) return e;
   }
   if (p.split_groups > 0 && p.whole_groups > 0 && p.side_stream) {
@@ -629,6 +494,17 @@ hipError_t launch_dtype(const ScanParams& p, bool bf16, bool vec,
 }
 
 }  // namespace
+
+hipError_t launch_bc_pack(const void* B, const void* C, void* packed,
+                          int64_t batch, int64_t L, int64_t steps, int N,
+                          int waves, bool bf16, int64_t run_words,
+                          hipStream_t stream) {
+  const int64_t total = batch * steps * 2 * N;
+  hipLaunchKernelGGL(bc_pack_kernel, dim3((unsigned)((total + 255) / 256)),
+                     dim3(256), 0, stream, B, C, packed, batch, L, steps, N,
+                     waves, bf16 ? 1 : 0, run_words);
+  return hipGetLastError();
+}
 
 int64_t scan_bc_workspace_bytes(int64_t batch, int64_t L, int N, bool bf16) {
   const int NG = scan_waves_per_group(N);

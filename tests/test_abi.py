@@ -101,6 +101,41 @@ def test_fwd_alias_checks(L):
     assert _fwd(L, _dims(), last=p[8] + 256) == -5
 
 
+BWD_ARGS = ["u", "delta", "A", "B", "C", "D", "z", "bias", "h0", "dout",
+            "dlast", "du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dbias", "dh0"]
+
+
+def _bwd(L, dims, **override):
+    p = dict(zip(BWD_ARGS, _ptrs(len(BWD_ARGS))))
+    p.update(override)
+    return L.mssm_selective_scan_bwd(
+        p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["bias"], 1,
+        p["h0"], p["dout"], p["dlast"], p["du"], p["ddelta"], p["dA"], p["dB"],
+        p["dC"], p["dD"], p["dz"], p["dbias"], p["dh0"], ctypes.byref(dims), None)
+
+
+def test_bwd_validation_codes(L):
+    assert L.mssm_selective_scan_bwd(*([None] * 8), 1, *([None] * 14)) == -1
+    for name in ("u", "delta", "A", "B", "C", "dout", "du", "ddelta", "dA",
+                 "dB", "dC"):
+        assert _bwd(L, _dims(), **{name: None}) == -1, name
+    assert _bwd(L, _dims(), dz=None) == -1                  # z without dz
+    assert _bwd(L, _dims(), z=None) == -1                   # dz without z
+    assert _bwd(L, _dims(flags=1)) == -3                    # no flags
+    assert _bwd(L, _dims(ts=2)) == -2                       # no time split
+    for bad in (dict(batch=0), dict(dim=-1), dict(L_=0)):
+        assert _bwd(L, _dims(**bad)) == -2, bad
+    assert _bwd(L, _dims(N=3)) == -3
+    assert _bwd(L, _dims(L_=1 << 40)) == -2
+    assert _bwd(L, _dims(io=1), dout=BASE + 9 * (1 << 34) + 1) == -4
+    assert _bwd(L, _dims(), dB=BASE + 14 * (1 << 34) + 2) == -4
+    p = _ptrs(len(BWD_ARGS))
+    assert _bwd(L, _dims(), du=p[0] + 64) == -5             # du over u
+    assert _bwd(L, _dims(), dC=p[9]) == -5                  # dC over dout
+    assert _bwd(L, _dims(), dh0=p[13] + 4) == -5            # dh0 over dA
+    assert _bwd(L, _dims(), ddelta=p[11] + 2) == -5         # ddelta over du
+
+
 def test_update_validation_codes(L):
     from selective_state_space_52_amd._lib import Dims
     p = _ptrs(11)

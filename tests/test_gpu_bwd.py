@@ -1,0 +1,164 @@
+"""Backward scan on the GPU (through the C ABI) against the fp64 oracle.
+
+Parity bar.  Every gradient is a sum of many fp32 products (over the N states
+and a reversed recurrence over time for du, ddelta, dz, dh0; over up to
+5120 channels for dB, dC; over batch and time for dA, dD, dbias), so its
+rounding error scales with the size of the terms, not of the (possibly
+cancelling) result.  The bar is therefore taken per tensor against its RMS:
+    |gpu - ref| <= tol * (|ref| + rms(ref))        tol = 2e-4
+(fp32 accumulation of K terms errs by about sqrt(K) * 6e-8 of their RMS
+magnitude, and a sum over 5120 channels or 2048 steps of terms whose RMS is
+up to sqrt(K) times the result's gives about 2e-5 of rms(ref); 2e-4 leaves a
+factor of ten).  bf16 outputs (du, ddelta, dz with bf16 io) add one rounding:
+2^-8 |ref|.  A dropped term, wrong sign or index shifts a gradient by a
+sizable fraction of its RMS, far above the bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests.gpu_common import DEV, np64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-4
+IO_GRADS = ("du", "ddelta", "dz")
+
+
+def gpu_bwd(inp, grads, h0=None, use_dlast=True, want_dh0=True):
+    import selective_state_space_52_amd as m
+    g = m.selective_scan_bwd(
+        to_dev(inp["u"]), to_dev(inp["delta"]), to_dev(inp["A"]),
+        to_dev(inp["B"]), to_dev(inp["C"]), to_dev(grads["dout"]),
+        D=to_dev(inp["D"]), z=to_dev(inp["z"]),
+        delta_bias=to_dev(inp["delta_bias"]), softplus=inp["softplus"],
+        h0=to_dev(h0), dlast=to_dev(grads["dlast"]) if use_dlast else None,
+        want_dh0=want_dh0)
+    torch.cuda.synchronize()
+    return {k: (None if v is None else v.cpu()) for k, v in g.items()}
+
+
+def oracle_bwd(inp, grads, h0=None, use_dlast=True):
+    import oracle
+    return oracle.scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                           grads["dout"], D=inp["D"], z=inp["z"],
+                           delta_bias=inp["delta_bias"], softplus=inp["softplus"],
+                           h0=h0, dlast=grads["dlast"] if use_dlast else None)
+
+
+def check_grad(gpu, ref, io, name, key):
+    g = np64(gpu)
+    r = np.asarray(ref, np.float64)
+    assert g.shape == r.shape, (name, g.shape, r.shape)
+    assert np.isfinite(g).all(), "%s: non-finite" % name
+    if r.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(r * r)))
+    bar = TOL * (np.abs(r) + rms)
+    if io == "bf16" and key in IO_GRADS:
+        bar = bar + 2.0 ** -8 * np.abs(r)
+    err = np.abs(g - r)
+    worst = float((err / np.maximum(bar, 1e-30)).max())
+    assert worst <= 1.0, "%s: bar exceeded, worst err/bar %.3g, max err %.3g, rms %.3g" % (
+        name, worst, float(err.max()), rms)
+    return worst
+
+
+def check_all(g, r, io, what, want_dh0=True):
+    worst = {}
+    for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
+        if r[k] is None or (k == "dh0" and not want_dh0):
+            assert g.get(k) is None or k == "dh0"
+            continue
+        worst[k] = check_grad(g[k], r[k], io, "%s %s" % (what, k), k)
+    print("%-40s %s" % (what, " ".join("%s=%.2g" % kv for kv in worst.items())),
+          flush=True)
+    return worst
+
+
+def _case(name, **over):
+    s = W.spec(name, **over)
+    return s, W.make_scan_inputs(s), W.make_scan_grads(s)
+
+
+def test_bwd_tiny_f32_full():
+    s, inp, gr = _case("tiny_f32")
+    h0 = W.make_initial_state(s)
+    check_all(gpu_bwd(inp, gr, h0=h0), oracle_bwd(inp, gr, h0=h0), "f32", "tiny_f32")
+
+
+SHAPES = [
+    # io, batch, dim, N, L -- several tiles, ragged groups and tails
+    ("bf16", 3, 128, 16, 256),    # vector path, whole tiles
+    ("bf16", 2, 100, 16, 333),    # element path, ragged group and tile
+    ("bf16", 2, 130, 16, 1000),   # vector path, ragged last tile
+    ("f32", 1, 64, 16, 257),      # fp32 element path
+    ("f32", 2, 70, 16, 264),      # fp32 vector path
+    ("bf16", 1, 64, 16, 1),
+    ("bf16", 1, 64, 16, 7),
+    ("bf16", 1, 64, 16, 15),
+    ("bf16", 1, 64, 16, 16),
+    ("bf16", 1, 64, 16, 17),
+    ("bf16", 1, 5, 16, 40),       # fewer channels than a wave
+    ("bf16", 2, 96, 1, 200),
+    ("bf16", 2, 96, 2, 200),
+    ("bf16", 2, 96, 4, 200),
+    ("bf16", 2, 96, 8, 200),
+    ("f32", 2, 33, 8, 77),
+    ("f32", 2, 40, 2, 48),
+]
+
+
+@pytest.mark.parametrize("io,batch,dim,N,L", SHAPES,
+                         ids=["%s-b%d-d%d-n%d-l%d" % s for s in SHAPES])
+def test_bwd_shapes(io, batch, dim, N, L):
+    s, inp, gr = _case("mamba130m_layer", io=io, batch=batch, dim=dim, dstate=N,
+                       seqlen=L, seed=300 + L + N)
+    check_all(gpu_bwd(inp, gr), oracle_bwd(inp, gr), io,
+              "shape %s" % ((io, batch, dim, N, L),))
+
+
+VARIANTS = [
+    dict(has_z=False), dict(has_D=False), dict(has_bias=False),
+    dict(softplus=False, has_bias=False),
+    dict(has_z=False, has_D=False, has_bias=False),
+]
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("var", VARIANTS,
+                         ids=lambda v: ",".join("%s=%s" % kv for kv in v.items()))
+def test_bwd_optional_operands(io, var):
+    s, inp, gr = _case("mamba130m_layer", io=io, batch=2, dim=80, seqlen=136,
+                       seed=17, **var)
+    if not var.get("softplus", True):
+        # raw steps must stay positive without softplus: use |delta| * 0.05
+        inp["delta"] = (inp["delta"].float().abs() * 0.05).to(inp["delta"].dtype)
+    check_all(gpu_bwd(inp, gr), oracle_bwd(inp, gr), io, "variant %s %s" % (io, var))
+
+
+@pytest.mark.parametrize("use_h0,use_dlast", [(True, False), (False, True),
+                                              (False, False)])
+def test_bwd_state_gradients(use_h0, use_dlast):
+    s, inp, gr = _case("mamba130m_layer", batch=2, dim=70, seqlen=100, seed=23)
+    h0 = W.make_initial_state(s) if use_h0 else None
+    g = gpu_bwd(inp, gr, h0=h0, use_dlast=use_dlast)
+    r = oracle_bwd(inp, gr, h0=h0, use_dlast=use_dlast)
+    check_all(g, r, "bf16", "state h0=%s dlast=%s" % (use_h0, use_dlast))
+
+
+def test_bwd_deterministic():
+    s, inp, gr = _case("mamba130m_layer", batch=2, dim=200, seqlen=300, seed=29)
+    a = gpu_bwd(inp, gr)
+    b = gpu_bwd(inp, gr)
+    for k in a:
+        if a[k] is not None:
+            assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("name", ["mamba130m_layer", "mamba2p8b_layer"])
+def test_bwd_full_size(name):
+    """The layer shapes at full size: every gradient against the oracle."""
+    s, inp, gr = _case(name)
+    check_all(gpu_bwd(inp, gr), oracle_bwd(inp, gr), s.io, "full %s" % name)

@@ -23,7 +23,9 @@ Value recipe (all workloads):
   D ~ N(0, 1) per channel
   decode state ~ 0.1 * N(0, 1)
 Draw order from numpy.random.default_rng(seed): u, delta, z, B, C, D, log-dt,
-then (decode only) the state.  Decode tokens use default_rng([seed, 1 + k]) for
+then (decode only) the state.  The backward's incoming gradients use
+default_rng([seed, 104729]): dout ~ N(0, 1) in the io dtype, then dlast ~
+N(0, 1) fp32.  Decode tokens use default_rng([seed, 1 + k]) for
 token k of a ring of ``tokens`` distinct tokens; step s uses token s % tokens.
 bf16 values are fp32 draws rounded to nearest-even (torch's conversion).
 """
@@ -144,6 +146,36 @@ def make_initial_state(s, seed_offset: int = 7919) -> torch.Tensor:
     std = getattr(s, "state_std", 0.1)
     return torch.from_numpy(
         (std * rng.standard_normal((s.batch, s.dim, s.dstate))).astype(np.float32))
+
+
+def make_scan_grads(s: ScanSpec, seed_offset: int = 104729) -> dict:
+    """Incoming gradients for the backward: io-dtype dout (batch, dim, L) and
+    fp32 dlast (batch, dim, N), both ~ N(0, 1)."""
+    rng = np.random.default_rng([s.seed, seed_offset])
+    dout = _round_io(rng.standard_normal((s.batch, s.dim, s.seqlen),
+                                         dtype=np.float32), s.io)
+    dlast = torch.from_numpy(
+        rng.standard_normal((s.batch, s.dim, s.dstate), dtype=np.float32))
+    return dict(dout=dout, dlast=dlast)
+
+
+def scan_bwd_bytes(s: ScanSpec, has_h0: bool = False, has_dlast: bool = False,
+                   want_dh0: bool = False) -> int:
+    """Algorithmic HBM bytes of one backward call: the forward's operands and
+    dout read once; du, ddelta, dz (io dtype) and dA, dB, dC, dD, dbias (fp32)
+    written once."""
+    io = 4 if s.io == "f32" else 2
+    e = s.elements
+    n_in = 3 + int(s.has_z)                             # u, delta, dout, z
+    n_out = 2 + int(s.has_z)                            # du, ddelta, dz
+    b = (n_in + n_out) * e * io
+    b += 2 * s.batch * s.seqlen * s.dstate * io         # B, C in
+    b += 2 * s.batch * s.seqlen * s.dstate * 4          # dB, dC out (fp32)
+    b += 2 * 4 * s.dim * s.dstate                       # A in, dA out
+    b += 2 * 4 * s.dim * (int(s.has_D) + int(s.has_bias))  # D, bias; dD, dbias
+    rows = s.batch * s.dim
+    b += 4 * rows * s.dstate * (int(has_h0) + int(has_dlast) + int(want_dh0))
+    return b
 
 
 def make_decode_params(s: DecodeSpec) -> dict:
