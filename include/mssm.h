@@ -83,7 +83,7 @@ typedef struct {
   int64_t seqlen;      /* L >= 1 for the scan; must be 1 for state_update  */
   int32_t io_dtype;    /* mssm_dtype of u/delta/z/B/C/out (x/dt/z/B/C/out) */
   uint32_t flags;      /* MSSM_FLAG_*                                       */
-  int32_t time_segments; /* fwd only: 0 = the library picks; k >= 1 splits  */
+  int32_t time_segments; /* scan only: 0 = the library picks; k >= 1 splits */
                          /* every row into k time segments (a carried state */
                          /* joins them; results agree up to rounding)       */
   int32_t reserved;      /* must be 0                                        */
@@ -135,8 +135,11 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
  *                 and time; written even when D / delta_bias are NULL (the
  *                 gradient at zero)
  *   dh0         : (batch, dim, dstate) fp32 gradient of h0, or NULL
- * No output may overlap an input or another output.  flags and
- * time_segments must be 0.  The sums over channels and the batch are taken
+ * No output may overlap an input or another output.  flags must be 0.
+ * time_segments: 0 lets the library cut rows into time segments that run in
+ * parallel (joined by a carried state and a carried gradient); k >= 1 asks
+ * for about k segments (whole 16-step tiles each).  Results agree up to
+ * rounding.  The sums over channels and the batch are taken
  * in a fixed order, so repeated calls give identical bits.  Stream-ordered
  * workspace: about 4 * dstate bytes per element of u plus 8 * dstate bytes
  * per token for each 64-channel group, returned on the same stream.
@@ -188,8 +191,9 @@ int mssm_selective_scan_fwd_plan(const mssm_dims* dims, mssm_plan* plan);
  * Timing hook for benchmarks.  With both handles non-NULL (hipEvent_t, owned
  * by the caller), every later forward scan issued from this thread records
  * `start` on its stream right before the main scan kernel and `stop` right
- * after it (the backward call does the same around its main kernel), so
- * hipEventElapsedTime(start, stop) is that kernel's duration.
+ * after it, so hipEventElapsedTime(start, stop) is that kernel's duration.
+ * The backward call records them around its three main kernels (pass F,
+ * the segment combine and pass R).
  * Both NULL turns the hook off; one NULL is MSSM_ERR_NULL.  Per thread.
  */
 int mssm_set_scan_timing_events(void* start, void* stop);

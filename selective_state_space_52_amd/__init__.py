@@ -111,7 +111,7 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
 
 def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None,
                        delta_bias=None, softplus=True, h0=None, dlast=None,
-                       want_dh0=False):
+                       want_dh0=False, time_segments=0):
     """Gradients of the forward scan for the loss
     sum(dout * out) + sum(dlast * last_state).
 
@@ -120,6 +120,8 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None,
     (batch, dim, N) fp32 or None.  Returns a dict: du, ddelta, dz (io dtype,
     dz only with z), dA (dim, N), dB, dC (batch, L, N), dD, ddelta_bias (dim,)
     and, with want_dh0, dh0 (batch, dim, N), all fp32 except the first three.
+    time_segments: 0 = the library's split of rows into parallel time
+    segments; k >= 1 asks for about k.
     """
     if u.dtype not in _IO:
         raise ValueError("u must be float32 or bfloat16")
@@ -148,7 +150,7 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None,
              dD=torch.empty((dim,), **f32),
              ddelta_bias=torch.empty((dim,), **f32),
              dh0=torch.empty((batch, dim, N), **f32) if want_dh0 else None)
-    dims = Dims(batch, dim, N, L, _IO[io], 0, 0, 0)
+    dims = Dims(batch, dim, N, L, _IO[io], 0, time_segments, 0)
     with torch.cuda.device(dev):
         check(lib().mssm_selective_scan_bwd(
             _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),

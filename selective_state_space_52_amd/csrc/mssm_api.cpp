@@ -331,7 +331,7 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
   int rc = check_common_dims(dims);
   if (rc != MSSM_OK) return rc;
   if (dims->flags != 0) return MSSM_ERR_UNSUPPORTED;
-  if (dims->time_segments != 0) return MSSM_ERR_DIMS;
+  if (dims->time_segments < 0) return MSSM_ERR_DIMS;
   if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA ||
       !dB || !dC)
     return MSSM_ERR_NULL;
@@ -384,6 +384,19 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
                    aligned(du, 16) && aligned(ddelta, 16) &&
                    (!z || aligned(z, 16)) && (!dz || aligned(dz, 16));
   const int tile = mssm::bwd_tile();
+  if (g_cu_count <= 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                              dev) == hipSuccess &&
+        cus > 0)
+      g_cu_count = cus;
+  }
+  const int64_t tiles = (L + tile - 1) / tile;
+  const int segments =
+      mssm::bwd_segments(batch * gpb, tiles, g_cu_count > 0 ? g_cu_count : kDefaultCUs,
+                         dims->time_segments);
+  if (batch * gpb * segments > INT32_MAX) return MSSM_ERR_DIMS;
   mssm::BwdParams p;
   std::memset(&p, 0, sizeof(p));
   p.u = u; p.delta = delta; p.z = z; p.dout = dout; p.A = A; p.B = B; p.C = C;
@@ -393,13 +406,15 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
   p.batch = batch; p.dim = dim; p.L = L;
   p.softplus = softplus ? 1 : 0;
   p.groups_per_batch = (int32_t)gpb;
-  p.tiles = (int32_t)((L + tile - 1) / tile);
+  p.tiles = (int32_t)tiles;
+  p.segments = segments;
+  p.seg_tiles = (int32_t)((tiles + segments - 1) / segments);
   p.ev_start = g_ev_start;
   p.ev_stop = g_ev_stop;
 
   hipStream_t st = (hipStream_t)stream;
   const int64_t ws_bytes =
-      mssm::bwd_workspace(batch, dim, L, (int)N, io == 2, nullptr, nullptr);
+      mssm::bwd_workspace(batch, dim, L, (int)N, io == 2, segments, nullptr, nullptr);
   void* ws = nullptr;
   {
     hipError_t e = hipMallocAsync(&ws, (size_t)ws_bytes, st);
@@ -408,7 +423,7 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
       return MSSM_ERR_HIP;
     }
   }
-  mssm::bwd_workspace(batch, dim, L, (int)N, io == 2, ws, &p);
+  mssm::bwd_workspace(batch, dim, L, (int)N, io == 2, segments, ws, &p);
   hipError_t e = mssm::launch_scan_bwd(p, (int)N, io == 2, vec, st);
   if (e != hipSuccess) set_hip_error("backward scan launch", e);
   hipError_t f = hipFreeAsync(ws, st);

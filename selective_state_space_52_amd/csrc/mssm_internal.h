@@ -68,6 +68,15 @@ struct UpdateParams {
 
 // One backward-scan call.  Gradients of sum(dout * out) + sum(dlast *
 // last_state) with respect to every input of the forward scan.
+//
+// Rows are cut into `segments` time segments of `seg_tiles` tiles; a task is
+// one (64-channel group, segment).  Pass F scans every segment from a zero
+// state (all tasks in parallel), keeping the state and the running sum of
+// Delta at every tile start, the segment's end state and sum of Delta, and
+// its reverse aggregate (the gradient the segment sends to its start for a
+// zero incoming gradient).  A combine pass turns these into each segment's
+// true initial state and incoming gradient; pass R then walks each segment's
+// tiles backwards (all tasks in parallel).
 struct BwdParams {
   const void* u;
   const void* delta;
@@ -93,37 +102,51 @@ struct BwdParams {
   int32_t softplus;
   int32_t groups_per_batch;
   int32_t tiles;          // ceil(L / tile); runs and partials hold tiles*tile steps
-  // workspace
+  int32_t segments;       // time segments per row
+  int32_t seg_tiles;      // tiles per segment (the last may have fewer)
+  int32_t reserved;
+  // workspace (task = group * segments + segment; lane-contiguous rows)
   void* ws_bc;            // B, C packed per wave run, zero-padded to whole tiles
-  float* ws_ck;           // [group][tile][n][lane] state at each tile start
+  float* ws_ck;           // [group][tile][n][lane] state at tile start, from a
+                          // zero state at the segment start
+  float* ws_cd;           // [group][tile][lane] sum of Delta from the segment
+                          // start to the tile start
+  float* ws_S;            // [task][n][lane] segment end state from zero
+  float* ws_R;            // [task][n][lane] segment reverse aggregate
+  double* ws_sum;         // [task][lane] segment sum of Delta
+  float* ws_hin;          // [task][n][lane] segment initial state
+  float* ws_gin;          // [task][n][lane] gradient entering the segment end
   float* ws_dbc;          // [b][group in batch][t][B, C][n] channel-group sums
-  float* ws_dA;           // [b][d][n] per-batch dA
-  float* ws_dDb;          // [b][d][dD, dbias] per-batch sums
-  void* ev_start;         // optional timing events around the main kernel
-  void* ev_stop;
+  float* ws_dA;           // [segment][b][d][n] partial dA
+  float* ws_dDb;          // [segment][b][d][dD, dbias] partial sums
+  void* ev_start;         // optional timing events around pass F, the
+  void* ev_stop;          // combine and pass R
 };
 
 // Waves per 64-channel workgroup: each wave owns dstate / waves states.
 int scan_waves_per_group(int N);
 // Repack B and C into per-wave runs for `waves` waves per channel group:
 // `steps` (>= L) timesteps per run, zeros from L on, `run_words` 32-bit words
-// per run.
+// per run; the runs hold bf16 pairs (dst_bf16) or fp32 values.
 hipError_t launch_bc_pack(const void* B, const void* C, void* packed,
                           int64_t batch, int64_t L, int64_t steps, int N,
-                          int waves, bool bf16, int64_t run_words,
-                          hipStream_t stream);
+                          int waves, bool src_bf16, bool dst_bf16,
+                          int64_t run_words, hipStream_t stream);
 // Bytes of the packed B/C runs of one forward call.
 int64_t scan_bc_workspace_bytes(int64_t batch, int64_t L, int N, bool bf16);
 
 hipError_t launch_scan(const ScanParams& p, int N, bool bf16, bool vec,
                        hipStream_t stream);
-// Backward: timesteps per tile, waves per group, workspace bytes, launch.
+// Backward: timesteps per tile, waves per group, segments, workspace, launch.
 int bwd_tile();
 int bwd_waves_per_group(int N);
+// Time segments per row: `forced` (> 0) if given, else enough tasks to fill
+// the CUs in whole rounds, with segments of at least 4 tiles.
+int bwd_segments(int64_t groups, int64_t tiles, int cus, int forced);
 // Workspace bytes of one backward call; with ws and p non-null also points
 // p's workspace fields into ws.
 int64_t bwd_workspace(int64_t batch, int64_t dim, int64_t L, int N, bool bf16,
-                      void* ws, BwdParams* p);
+                      int segments, void* ws, BwdParams* p);
 hipError_t launch_scan_bwd(const BwdParams& p, int N, bool bf16, bool vec,
                            hipStream_t stream);
 hipError_t launch_state_update(const UpdateParams& p, int N, bool bf16,

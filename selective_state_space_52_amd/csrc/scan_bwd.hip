@@ -19,24 +19,39 @@
 //   dD       += dy_t u_t,   dbias += ddelta_t,   dh0 = e_0 g_0
 // dB, dC sum over channels and dA, dD, dbias over the batch.
 //
-// Mapping (the forward kernel's, extended):
-//   * one lane per channel, 64 channels of one batch entry per workgroup;
-//     the N states of a channel are split over NG waves (4 states each);
-//     B_t and C_t are wave-uniform and read with wide scalar loads from a
-//     per-wave packed run (zero-padded to whole tiles);
-//   * pass F scans the row forwards and stores the state at the start of
-//     every 16-step tile (workspace, lane-contiguous);
-//   * pass R walks the tiles backwards.  Per tile each wave recomputes its
-//     states' e_t and h_t from the tile's checkpoint into registers, then runs
-//     the reverse recurrence; sums over n of a channel (y, g.B, A g e h) go
-//     through LDS to the wave that owns the timestep, as in the forward
-//     output phase;
-//   * dB and dC need sums over the 64 channels of a wave: 16 values per lane
-//     are written to a per-wave LDS block and read back transposed, so each
-//     lane adds 16 values and two DPP steps finish the sum; the per-group
-//     sums go to workspace and a last kernel adds the groups (fixed order,
-//     so the result is deterministic), together with the batch sums of dA,
-//     dD and dbias.
+// Time segments.  Both recurrences are linear, so a row cut into segments
+// is joined by two carries per state: the state entering a segment and the
+// gradient entering it from the end.  For a segment scanned from zero,
+//   end state  S = h_end from h = 0,   decay over it  P = exp(A sum Delta)
+//   reverse aggregate  R = sum_t E_t dy_t C_t,  E_t = exp(A sum_{start..t} Delta)
+// (R is what the reverse recurrence carries to the segment start for a zero
+// incoming gradient; E_t is a running product, so R is formed in the forward
+// sweep and no extra reverse sweep is needed).  Then
+//   h_in[s+1] = P_s h_in[s] + S_s,      g_in[s-1] = P_s g_in[s] + R_s
+// and a state kept inside segment s at a point with running sum c is
+// h = h(from zero) + exp(A c) h_in[s].
+//
+// Kernels (all rows and segments in parallel):
+//   pass F   : scans each segment from zero with the recurrence above, keeping
+//              the state and running sum of Delta at every 16-step tile, and
+//              S, R, sum Delta of the segment;
+//   combine  : h_in and g_in of every segment (fp64 decay);
+//   pass R   : per segment, tiles in reverse: recompute e_t, h_t of the tile
+//              into registers from its corrected checkpoint, run the reverse
+//              recurrence, emit du, ddelta, dz and the partial sums;
+//   reduce   : dB, dC over channel groups; dA, dD, dbias over batch and
+//              segments (fixed order: deterministic).
+// Mapping: one lane per channel, 64 channels of one batch entry per
+// workgroup, the N states split over NG waves (4 each).  B_t and C_t are
+// wave-uniform and read with wide scalar loads from a per-wave packed run
+// (zero-padded to whole tiles); the next tile's lines are touched one tile
+// ahead so that those loads hit the scalar cache.  Sums over n of a channel
+// (y, g.B, A g e h) go through LDS to the wave that owns the timestep; dB and
+// dC need sums over the 64 channels of a wave: 16 values per lane are
+// written to a per-wave LDS block and read back transposed, so each lane adds
+// 16 values and two DPP steps finish the sum.
+#include <algorithm>
+
 #include "dev_math.h"
 #include "mssm_internal.h"
 #include "scan_common.h"
@@ -47,6 +62,7 @@ namespace {
 constexpr int kT = 16;                 // timesteps per tile (and checkpoint)
 constexpr int kRedItems = 16;          // values per lane per channel reduction
 constexpr int kRedPitch = kLanes + 4;  // padded row: conflict-free b128 reads
+constexpr int kMinSegTiles = 4;        // shortest segment the plan makes
 
 // Waves per 64-channel workgroup: four states per wave.
 template <int N>
@@ -55,16 +71,8 @@ constexpr int kBwdWaves = N >= 4 ? N / 4 : 1;
 struct BwdShape {
   int64_t dim, L;
   int32_t groups_per_batch, tiles;
-  int32_t softplus, reserved;
-};
-
-template <int NG>
-struct alignas(16) BwdSmem {
-  float2 dw[kT][kLanes];                // (Delta, Delta*u) of the tile
-  float dy[kT][kLanes];                 // dout * silu(z)
-  float y[NG][kT][kLanes];              // per-wave partial readouts
-  float2 s[NG][kT][kLanes];             // per-wave (sum g B, sum A g e h_prev)
-  float red[NG][kRedItems][kRedPitch];  // per-wave channel-sum transpose
+  int32_t segments, seg_tiles;
+  int32_t softplus, batch;
 };
 
 // LDS traffic between lanes of one wave: the wave's LDS operations complete
@@ -99,18 +107,216 @@ __device__ __forceinline__ float wave_sum_items(float (&red)[kRedItems][kRedPitc
   return s;
 }
 
+// Touch one dword in each 64-byte line of a tile's packed B/C run so that the
+// tile's wide scalar loads later hit the scalar cache.
+template <int WPS>
+__device__ __forceinline__ uint32_t warm_tile(const uint32_t* __restrict__ bcw,
+                                              int64_t tile) {
+  uint32_t touch = 0u;
+  const int64_t f0 = tile * kT * WPS;
+#pragma unroll
+  for (int f = 0; f < kT * WPS; f += 16) touch += bcw[f0 + f];
+  return touch;
+}
+
+// Per-task indices shared by both passes.
+struct Task {
+  int gi, seg;
+  int64_t b, d, dc, row, rowoff;
+  bool valid;
+  int tile_begin, tile_end;
+};
+
+__device__ __forceinline__ Task task_of(const BwdShape& s, int lane) {
+  Task k;
+  const int task = blockIdx.x;
+  k.gi = task / s.segments;
+  k.seg = task - k.gi * s.segments;
+  k.b = k.gi / s.groups_per_batch;
+  k.d = (int64_t)(k.gi % s.groups_per_batch) * kLanes + lane;
+  k.valid = k.d < s.dim;
+  k.dc = k.valid ? k.d : s.dim - 1;
+  k.row = k.b * s.dim + k.dc;
+  k.rowoff = k.row * s.L;
+  k.tile_begin = k.seg * s.seg_tiles;
+  k.tile_end = min(s.tiles, k.tile_begin + s.seg_tiles);
+  return k;
+}
+
+// ---------------------------------------------------------------- pass F ---
 template <int N, int NG, bool BF16, bool VEC, bool HAS_Z>
 __global__ void __launch_bounds__(kLanes* NG)
-    scan_bwd_kernel(const void* __restrict__ u, const void* __restrict__ delta,
-                    const void* __restrict__ z, const void* __restrict__ dout,
-                    const float* __restrict__ A, const float* __restrict__ Dv,
-                    const float* __restrict__ bias, const float* __restrict__ h0,
-                    const float* __restrict__ dlast, void* __restrict__ du,
-                    void* __restrict__ ddelta, void* __restrict__ dz,
-                    float* __restrict__ dh0, float* __restrict__ ws_ck,
-                    float* __restrict__ ws_dbc, float* __restrict__ ws_dA,
-                    float* __restrict__ ws_dDb, const uint32_t* __restrict__ bcp,
-                    const BwdShape s) {
+    bwd_pass_f_kernel(const void* __restrict__ u, const void* __restrict__ delta,
+                      const void* __restrict__ z, const void* __restrict__ dout,
+                      const float* __restrict__ A, const float* __restrict__ bias,
+                      float* __restrict__ ws_ck, float* __restrict__ ws_cd,
+                      float* __restrict__ ws_S, float* __restrict__ ws_R,
+                      double* __restrict__ ws_sum,
+                      const uint32_t* __restrict__ bcp, const BwdShape s) {
+  constexpr int NPW = N / NG;
+  constexpr int T = kT;
+  constexpr int KC = T / NG;
+  constexpr int WPS = BCLayout<NPW, BF16>::kWordsPerStep;
+  constexpr int KB = BCLayout<NPW, BF16>::kSteps;
+  constexpr int NB = T / KB;
+  using Batch = BCBatch<NPW, BF16>;
+  __shared__ float2 s_dw[2][T][kLanes];  // (Delta, Delta*u), double-buffered
+  __shared__ float s_dy[2][T][kLanes];   // dout * silu(z)
+
+  const int lane = threadIdx.x & (kLanes - 1);
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = g * NPW;
+  const Task k = task_of(s, lane);
+  const int64_t Lp = (int64_t)s.tiles * T;
+  const uint32_t* __restrict__ bcw = bcp + (k.b * NG + g) * Lp * WPS;
+  const bool sp = s.softplus != 0;
+
+  float A2[NPW];
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) A2[j] = A[k.dc * N + n0 + j] * kLog2e;
+  const float bv = bias ? bias[k.dc] : 0.0f;
+
+  Raw<BF16, KC> ru, rd, rz, ro;
+  raw_zero(rz);
+  auto load = [&](int tile) {
+    const int64_t tc = (int64_t)tile * T + g * KC;
+    const int64_t nv = s.L - tc;
+    load_chunk<BF16, VEC, KC>(ru, u, k.rowoff + tc, nv);
+    load_chunk<BF16, VEC, KC>(rd, delta, k.rowoff + tc, nv);
+    if constexpr (HAS_Z) load_chunk<BF16, VEC, KC>(rz, z, k.rowoff + tc, nv);
+    load_chunk<BF16, VEC, KC>(ro, dout, k.rowoff + tc, nv);
+  };
+  auto prep = [&](int tile, int buf) {
+    const int64_t nv = s.L - ((int64_t)tile * T + g * KC);
+#pragma unroll
+    for (int q = 0; q < KC; ++q) {
+      const bool ok = k.valid && q < nv;
+      const float x = raw_get(rd, q) + bv;
+      float dl = sp ? softplus_f32(x) : x;
+      float dyv = raw_get(ro, q);
+      if constexpr (HAS_Z) dyv *= silu_f32(raw_get(rz, q));
+      dl = ok ? dl : 0.0f;
+      dyv = ok ? dyv : 0.0f;
+      s_dw[buf][g * KC + q][lane] = make_float2(dl, dl * raw_get(ru, q));
+      s_dy[buf][g * KC + q][lane] = dyv;
+    }
+  };
+
+  float h[NPW], E[NPW], Rg[NPW];
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) {
+    h[j] = 0.0f;
+    E[j] = 1.0f;
+    Rg[j] = 0.0f;
+  }
+  double cum = 0.0;
+  float* __restrict__ ck = ws_ck + (int64_t)k.gi * s.tiles * N * kLanes;
+  float* __restrict__ cd = ws_cd + (int64_t)k.gi * s.tiles * kLanes;
+
+  load(k.tile_begin);
+  prep(k.tile_begin, 0);
+  __syncthreads();
+  for (int ti = k.tile_begin; ti < k.tile_end; ++ti) {
+    const int cur = (ti - k.tile_begin) & 1;
+    const bool more = ti + 1 < k.tile_end;
+    if (more) load(ti + 1);
+    const uint32_t touch = more ? warm_tile<WPS>(bcw, ti + 1) : 0u;
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) ck[((int64_t)ti * N + n0 + j) * kLanes + lane] = h[j];
+    if (g == 0) cd[(int64_t)ti * kLanes + lane] = (float)cum;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+      const Batch bc = *reinterpret_cast<const Batch*>(bcw + ((int64_t)ti * T + kb * KB) * WPS);
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        const float2 dw = s_dw[cur][kb * KB + i][lane];
+        const float dyv = s_dy[cur][kb * KB + i][lane];
+#pragma unroll
+        for (int j = 0; j < NPW; ++j) {
+          const float e = hw_exp2(dw.x * A2[j]);
+          h[j] = fmaf(e, h[j], dw.y * bc_val<NPW, BF16>(bc.w, i, j));
+          E[j] *= e;
+          Rg[j] = fmaf(E[j], dyv * bc_val<NPW, BF16>(bc.w, i, NPW + j), Rg[j]);
+        }
+        cum += (double)dw.x;
+      }
+    }
+    if (more) prep(ti + 1, cur ^ 1);
+    asm volatile("" ::"s"(touch));  // keeps the warming loads
+    __syncthreads();
+  }
+  const int64_t task = blockIdx.x;
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) {
+    ws_S[(task * N + n0 + j) * kLanes + lane] = h[j];
+    ws_R[(task * N + n0 + j) * kLanes + lane] = Rg[j];
+  }
+  if (g == 0) ws_sum[task * kLanes + lane] = cum;
+}
+
+// --------------------------------------------------------------- combine ---
+// Initial state and incoming end gradient of every segment, per (task row,
+// state); fp64 decay exp(A sum Delta).
+__global__ void __launch_bounds__(256)
+    bwd_combine_kernel(const float* __restrict__ A, const float* __restrict__ h0,
+                       const float* __restrict__ dlast,
+                       const float* __restrict__ ws_S,
+                       const float* __restrict__ ws_R,
+                       const double* __restrict__ ws_sum,
+                       float* __restrict__ ws_hin, float* __restrict__ ws_gin,
+                       const BwdShape s, int N, int64_t groups) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= groups * N * kLanes) return;
+  const int lane = (int)(tid % kLanes);
+  const int64_t r = tid / kLanes;
+  const int n = (int)(r % N);
+  const int64_t gi = r / N;
+  const int P = s.segments;
+  const int64_t b = gi / s.groups_per_batch;
+  const int64_t d = (gi % s.groups_per_batch) * kLanes + lane;
+  auto at = [&](int seg) { return ((gi * P + seg) * N + n) * kLanes + lane; };
+  if (d >= s.dim) {
+    for (int q = 0; q < P; ++q) ws_hin[at(q)] = ws_gin[at(q)] = 0.0f;
+    return;
+  }
+  const double a = A[d * N + n];
+  const int64_t si = (b * s.dim + d) * N + n;
+  double h = h0 ? h0[si] : 0.0;
+  for (int q = 0; q < P; ++q) {
+    ws_hin[at(q)] = (float)h;
+    h = exp(a * ws_sum[(gi * P + q) * kLanes + lane]) * h + (double)ws_S[at(q)];
+  }
+  double gr = dlast ? dlast[si] : 0.0;
+  for (int q = P - 1; q >= 0; --q) {
+    ws_gin[at(q)] = (float)gr;
+    gr = exp(a * ws_sum[(gi * P + q) * kLanes + lane]) * gr + (double)ws_R[at(q)];
+  }
+}
+
+// ---------------------------------------------------------------- pass R ---
+template <int NG>
+struct alignas(16) BwdSmem {
+  float2 dw[kT][kLanes];                // (Delta, Delta*u) of the tile
+  float dy[kT][kLanes];                 // dout * silu(z)
+  float y[NG][kT][kLanes];              // per-wave partial readouts
+  float2 s[NG][kT][kLanes];             // per-wave (sum g B, sum A g e h_prev)
+  float red[NG][kRedItems][kRedPitch];  // per-wave channel-sum transpose
+};
+
+template <int N, int NG, bool BF16, bool VEC, bool HAS_Z>
+__global__ void __launch_bounds__(kLanes* NG)
+    bwd_pass_r_kernel(const void* __restrict__ u, const void* __restrict__ delta,
+                      const void* __restrict__ z, const void* __restrict__ dout,
+                      const float* __restrict__ A, const float* __restrict__ Dv,
+                      const float* __restrict__ bias, void* __restrict__ du,
+                      void* __restrict__ ddelta, void* __restrict__ dz,
+                      float* __restrict__ dh0, const float* __restrict__ ws_ck,
+                      const float* __restrict__ ws_cd,
+                      const float* __restrict__ ws_hin,
+                      const float* __restrict__ ws_gin,
+                      float* __restrict__ ws_dbc, float* __restrict__ ws_dA,
+                      float* __restrict__ ws_dDb,
+                      const uint32_t* __restrict__ bcp, const BwdShape s) {
   constexpr int NPW = N / NG;
   constexpr int T = kT;
   constexpr int KC = T / NG;  // timesteps a wave prepares and emits per tile
@@ -125,81 +331,28 @@ __global__ void __launch_bounds__(kLanes* NG)
   const int lane = threadIdx.x & (kLanes - 1);
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = g * NPW;
-  const int gi = blockIdx.x;
-  const int64_t b = gi / s.groups_per_batch;
-  const int64_t d = (int64_t)(gi % s.groups_per_batch) * kLanes + lane;
-  const bool valid = d < s.dim;
-  const int64_t dc = valid ? d : s.dim - 1;
-  const int64_t row = b * s.dim + dc;
-  const int64_t rowoff = row * s.L;
+  const Task k = task_of(s, lane);
+  const int64_t task = blockIdx.x;
   const int64_t Lp = (int64_t)s.tiles * T;
-  const uint32_t* __restrict__ bcw = bcp + (b * NG + g) * Lp * WPS;
-  float* __restrict__ ck = ws_ck + (int64_t)gi * s.tiles * N * kLanes;
+  const uint32_t* __restrict__ bcw = bcp + (k.b * NG + g) * Lp * WPS;
+  const float* __restrict__ ck = ws_ck + (int64_t)k.gi * s.tiles * N * kLanes;
+  const float* __restrict__ cd = ws_cd + (int64_t)k.gi * s.tiles * kLanes;
   const bool sp = s.softplus != 0;
 
-  float A2[NPW], Av[NPW];
+  float A2[NPW], Av[NPW], hin[NPW];
 #pragma unroll
   for (int j = 0; j < NPW; ++j) {
-    Av[j] = A[dc * N + n0 + j];
+    Av[j] = A[k.dc * N + n0 + j];
     A2[j] = Av[j] * kLog2e;
+    hin[j] = ws_hin[(task * N + n0 + j) * kLanes + lane];
   }
-  const float bv = bias ? bias[dc] : 0.0f;
-  const float Dd = Dv ? Dv[dc] : 0.0f;
+  const float bv = bias ? bias[k.dc] : 0.0f;
+  const float Dd = Dv ? Dv[k.dc] : 0.0f;
 
-  // ---------------- pass F: the state at the start of every tile ----------
-  {
-    float h[NPW];
-#pragma unroll
-    for (int j = 0; j < NPW; ++j) h[j] = h0 ? h0[row * N + n0 + j] : 0.0f;
-    Raw<BF16, KC> ru, rd;
-    auto prep_f = [&](const Raw<BF16, KC>& pu, const Raw<BF16, KC>& pd,
-                      int64_t nv) {
-#pragma unroll
-      for (int k = 0; k < KC; ++k) {
-        const float x = raw_get(pd, k) + bv;
-        float dl = sp ? softplus_f32(x) : x;
-        dl = k < nv ? dl : 0.0f;
-        sm.dw[g * KC + k][lane] = make_float2(dl, dl * raw_get(pu, k));
-      }
-    };
-    {
-      const int64_t tc = g * KC;
-      load_chunk<BF16, VEC, KC>(ru, u, rowoff + tc, s.L - tc);
-      load_chunk<BF16, VEC, KC>(rd, delta, rowoff + tc, s.L - tc);
-      prep_f(ru, rd, s.L - tc);
-    }
-    __syncthreads();
-    for (int ti = 0; ti < s.tiles; ++ti) {
-      const int64_t tb = (int64_t)ti * T;
-      const int64_t tcn = tb + T + g * KC;
-      load_chunk<BF16, VEC, KC>(ru, u, rowoff + tcn, s.L - tcn);
-      load_chunk<BF16, VEC, KC>(rd, delta, rowoff + tcn, s.L - tcn);
-#pragma unroll
-      for (int j = 0; j < NPW; ++j)
-        ck[((int64_t)ti * N + n0 + j) * kLanes + lane] = h[j];
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb) {
-        const Batch bc = *reinterpret_cast<const Batch*>(bcw + (tb + kb * KB) * WPS);
-#pragma unroll
-        for (int i = 0; i < KB; ++i) {
-          const float2 dw = sm.dw[kb * KB + i][lane];
-#pragma unroll
-          for (int j = 0; j < NPW; ++j)
-            h[j] = fmaf(hw_exp2(dw.x * A2[j]), h[j],
-                        dw.y * bc_val<NPW, BF16>(bc.w, i, j));
-        }
-      }
-      __syncthreads();
-      prep_f(ru, rd, s.L - tcn);
-      __syncthreads();
-    }
-  }
-
-  // ---------------- pass R: tiles in reverse ------------------------------
   float gr[NPW], dA[NPW];
 #pragma unroll
   for (int j = 0; j < NPW; ++j) {
-    gr[j] = (dlast && valid) ? dlast[row * N + n0 + j] : 0.0f;
+    gr[j] = ws_gin[(task * N + n0 + j) * kLanes + lane];
     dA[j] = 0.0f;
   }
   float dDacc = 0.0f, dbacc = 0.0f;
@@ -211,19 +364,19 @@ __global__ void __launch_bounds__(kLanes* NG)
   auto prep_r = [&](int64_t tile_base) {
     const int64_t nv = s.L - (tile_base + g * KC);
 #pragma unroll
-    for (int k = 0; k < KC; ++k) {
-      const bool ok = valid && k < nv;
-      const float uu = raw_get(nu, k);
-      const float x = raw_get(nd, k) + bv;
+    for (int q = 0; q < KC; ++q) {
+      const bool ok = k.valid && q < nv;
+      const float uu = raw_get(nu, q);
+      const float x = raw_get(nd, q) + bv;
       float dl = x, sg = 1.0f;
       if (sp) {
         dl = softplus_f32(x);
         sg = hw_rcp(1.0f + hw_exp2(-x * kLog2e));
       }
-      const float o = raw_get(no, k);
+      const float o = raw_get(no, q);
       float dyv = o, dzf = 0.0f;
       if constexpr (HAS_Z) {
-        const float zz = raw_get(nz, k);
+        const float zz = raw_get(nz, q);
         const float sz = hw_rcp(1.0f + hw_exp2(-zz * kLog2e));
         dyv = o * (zz * sz);
         dzf = o * (sz * fmaf(zz, 1.0f - sz, 1.0f));
@@ -233,45 +386,52 @@ __global__ void __launch_bounds__(kLanes* NG)
         dyv = 0.0f;
         dzf = 0.0f;
       }
-      cD[k] = dl;
-      cS[k] = sg;
-      cU[k] = uu;
-      cDy[k] = dyv;
-      cDz[k] = dzf;
-      sm.dw[g * KC + k][lane] = make_float2(dl, dl * uu);
-      sm.dy[g * KC + k][lane] = dyv;
+      cD[q] = dl;
+      cS[q] = sg;
+      cU[q] = uu;
+      cDy[q] = dyv;
+      cDz[q] = dzf;
+      sm.dw[g * KC + q][lane] = make_float2(dl, dl * uu);
+      sm.dy[g * KC + q][lane] = dyv;
     }
   };
   auto load_r = [&](int64_t tile_base) {
     const int64_t tc = tile_base + g * KC;
     const int64_t nv = s.L - tc;
-    load_chunk<BF16, VEC, KC>(nu, u, rowoff + tc, nv);
-    load_chunk<BF16, VEC, KC>(nd, delta, rowoff + tc, nv);
-    if constexpr (HAS_Z) load_chunk<BF16, VEC, KC>(nz, z, rowoff + tc, nv);
-    load_chunk<BF16, VEC, KC>(no, dout, rowoff + tc, nv);
+    load_chunk<BF16, VEC, KC>(nu, u, k.rowoff + tc, nv);
+    load_chunk<BF16, VEC, KC>(nd, delta, k.rowoff + tc, nv);
+    if constexpr (HAS_Z) load_chunk<BF16, VEC, KC>(nz, z, k.rowoff + tc, nv);
+    load_chunk<BF16, VEC, KC>(no, dout, k.rowoff + tc, nv);
+  };
+  // state at the start of a tile: kept from zero, plus the decayed h_in
+  auto checkpoint = [&](int tile, float (&hc)[NPW]) {
+    const float c = cd[(int64_t)tile * kLanes + lane];
+#pragma unroll
+    for (int j = 0; j < NPW; ++j)
+      hc[j] = fmaf(hw_exp2(A2[j] * c), hin[j],
+                   ck[((int64_t)tile * N + n0 + j) * kLanes + lane]);
   };
 
-  const int last = s.tiles - 1;
+  const int last = k.tile_end - 1;
   load_r((int64_t)last * T);
   prep_r((int64_t)last * T);
   float hck[NPW];
-#pragma unroll
-  for (int j = 0; j < NPW; ++j) hck[j] = ck[((int64_t)last * N + n0 + j) * kLanes + lane];
+  checkpoint(last, hck);
   __syncthreads();
 
-  for (int ti = last; ti >= 0; --ti) {
+  for (int ti = last; ti >= k.tile_begin; --ti) {
     const int64_t tb = (int64_t)ti * T;
-    // prefetch the previous tile's inputs and checkpoint
+    const bool more = ti > k.tile_begin;
+    // prefetch the previous tile's inputs and checkpoint, warm its B/C lines
     float hnx[NPW];
-    if (ti > 0) {
+    if (more) {
       load_r(tb - T);
-#pragma unroll
-      for (int j = 0; j < NPW; ++j)
-        hnx[j] = ck[((int64_t)(ti - 1) * N + n0 + j) * kLanes + lane];
+      checkpoint(ti - 1, hnx);
     } else {
 #pragma unroll
       for (int j = 0; j < NPW; ++j) hnx[j] = 0.0f;
     }
+    const uint32_t touch = more ? warm_tile<WPS>(bcw, ti - 1) : 0u;
 
     // recompute e_t and h_t of the tile (and the partial readouts for dz)
     float e[T][NPW], H[T][NPW];
@@ -331,12 +491,12 @@ __global__ void __launch_bounds__(kLanes* NG)
         }
         const float tot = wave_sum_items(sm.red[g], pv, lane);
         if ((lane & 3) == 0) {
-          const int k = lane >> 2;
-          const int j = k % NPW;
-          const int q = (k / NPW) & 1;
-          const int ii = k / (2 * NPW);
+          const int kk = lane >> 2;
+          const int j = kk % NPW;
+          const int q = (kk / NPW) & 1;
+          const int ii = kk / (2 * NPW);
           const int64_t t_abs = tb + kb * KB + ru * RS + ii;
-          ws_dbc[((int64_t)gi * Lp + t_abs) * (2 * N) + q * N + n0 + j] = tot;
+          ws_dbc[((int64_t)k.gi * Lp + t_abs) * (2 * N) + q * N + n0 + j] = tot;
         }
       }
     }
@@ -348,8 +508,8 @@ __global__ void __launch_bounds__(kLanes* NG)
       const int64_t nv = s.L - tc;
       float odu[KC], odd[KC], odz[KC];
 #pragma unroll
-      for (int k = 0; k < KC; ++k) {
-        const int t = g * KC + k;
+      for (int q = 0; q < KC; ++q) {
+        const int t = g * KC + q;
         float y = 0.0f, s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
         for (int w = 0; w < NG; ++w) {
@@ -358,50 +518,54 @@ __global__ void __launch_bounds__(kLanes* NG)
           s1 += sv.x;
           s2 += sv.y;
         }
-        odu[k] = fmaf(cD[k], s1, Dd * cDy[k]);
-        const float ddl = fmaf(cU[k], s1, s2) * cS[k];
-        odd[k] = ddl;
-        if constexpr (HAS_Z) odz[k] = fmaf(Dd, cU[k], y) * cDz[k];
-        dDacc = fmaf(cDy[k], cU[k], dDacc);
-        dbacc += k < nv ? ddl : 0.0f;
+        odu[q] = fmaf(cD[q], s1, Dd * cDy[q]);
+        const float ddl = fmaf(cU[q], s1, s2) * cS[q];
+        odd[q] = ddl;
+        if constexpr (HAS_Z) odz[q] = fmaf(Dd, cU[q], y) * cDz[q];
+        dDacc = fmaf(cDy[q], cU[q], dDacc);
+        dbacc += q < nv ? ddl : 0.0f;
       }
-      if (valid) {
-        store_chunk<BF16, VEC, KC>(du, rowoff + tc, odu, nv);
-        store_chunk<BF16, VEC, KC>(ddelta, rowoff + tc, odd, nv);
-        if constexpr (HAS_Z) store_chunk<BF16, VEC, KC>(dz, rowoff + tc, odz, nv);
+      if (k.valid) {
+        store_chunk<BF16, VEC, KC>(du, k.rowoff + tc, odu, nv);
+        store_chunk<BF16, VEC, KC>(ddelta, k.rowoff + tc, odd, nv);
+        if constexpr (HAS_Z) store_chunk<BF16, VEC, KC>(dz, k.rowoff + tc, odz, nv);
       }
     }
-    if (ti > 0) prep_r(tb - T);
+    if (more) prep_r(tb - T);
 #pragma unroll
     for (int j = 0; j < NPW; ++j) hck[j] = hnx[j];
+    asm volatile("" ::"s"(touch));  // keeps the warming loads
     __syncthreads();
   }
 
-  if (valid) {
+  const int64_t part = (int64_t)k.seg * s.batch * s.dim + k.row;
+  if (k.valid) {
 #pragma unroll
     for (int j = 0; j < NPW; ++j) {
-      if (dh0) dh0[row * N + n0 + j] = gr[j];
-      ws_dA[row * N + n0 + j] = dA[j];
+      if (dh0 && k.seg == 0) dh0[k.row * N + n0 + j] = gr[j];
+      ws_dA[part * N + n0 + j] = dA[j];
     }
   }
   // dD and dbias: sum the waves' chunks (the loop ended on a barrier)
   sm.y[g][0][lane] = dDacc;
   sm.y[g][1][lane] = dbacc;
   __syncthreads();
-  if (g == 0 && valid) {
+  if (g == 0 && k.valid) {
     float sD = 0.0f, sb = 0.0f;
 #pragma unroll
     for (int w = 0; w < NG; ++w) {
       sD += sm.y[w][0][lane];
       sb += sm.y[w][1][lane];
     }
-    ws_dDb[row * 2 + 0] = sD;
-    ws_dDb[row * 2 + 1] = sb;
+    ws_dDb[part * 2 + 0] = sD;
+    ws_dDb[part * 2 + 1] = sb;
   }
 }
 
-// dB, dC: sum of the channel groups' sums; dA, dD, dbias: sum over the batch.
-// Every output element is one thread adding its terms in a fixed order.
+// ---------------------------------------------------------------- reduce ---
+// dB, dC: sum of the channel groups' sums; dA, dD, dbias: sum over segments
+// and the batch.  Every output element is one thread adding its terms in a
+// fixed order.
 __global__ void __launch_bounds__(256)
     bwd_reduce_kernel(const float* __restrict__ ws_dbc,
                       const float* __restrict__ ws_dA,
@@ -409,7 +573,7 @@ __global__ void __launch_bounds__(256)
                       float* __restrict__ dC, float* __restrict__ dA,
                       float* __restrict__ dD, float* __restrict__ dbias,
                       int64_t batch, int64_t dim, int64_t L, int64_t Lp, int N,
-                      int gpb) {
+                      int gpb, int segments) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t n_bc = batch * L * 2 * N;
   if (i < n_bc) {
@@ -427,33 +591,57 @@ __global__ void __launch_bounds__(256)
     return;
   }
   i -= n_bc;
+  const int64_t rows = batch * dim;
   if (i < dim * N) {
     float acc = 0.0f;
-    for (int64_t b = 0; b < batch; ++b) acc += ws_dA[b * dim * N + i];
+    for (int sg = 0; sg < segments; ++sg)
+      for (int64_t b = 0; b < batch; ++b) acc += ws_dA[(sg * rows + b * dim) * N + i];
     dA[i] = acc;
     return;
   }
   i -= dim * N;
   if (i < dim) {
     float aD = 0.0f, ab = 0.0f;
-    for (int64_t b = 0; b < batch; ++b) {
-      aD += ws_dDb[(b * dim + i) * 2 + 0];
-      ab += ws_dDb[(b * dim + i) * 2 + 1];
-    }
+    for (int sg = 0; sg < segments; ++sg)
+      for (int64_t b = 0; b < batch; ++b) {
+        aD += ws_dDb[(sg * rows + b * dim + i) * 2 + 0];
+        ab += ws_dDb[(sg * rows + b * dim + i) * 2 + 1];
+      }
     if (dD) dD[i] = aD;
     if (dbias) dbias[i] = ab;
   }
 }
 
 template <int N, bool BF16, bool VEC, bool HAS_Z>
-hipError_t launch_main(const BwdParams& p, const BwdShape& s, hipStream_t st) {
+hipError_t launch_passes(const BwdParams& p, const BwdShape& s, hipStream_t st) {
   constexpr int NG = kBwdWaves<N>;
-  const dim3 grid((unsigned)(p.batch * p.groups_per_batch)), block(kLanes * NG);
-  hipLaunchKernelGGL((scan_bwd_kernel<N, NG, BF16, VEC, HAS_Z>), grid, block, 0,
-                     st, p.u, p.delta, p.z, p.dout, p.A, p.D, p.bias, p.h0,
-                     p.dlast, p.du, p.ddelta, p.dz, p.dh0, p.ws_ck, p.ws_dbc,
-                     p.ws_dA, p.ws_dDb, (const uint32_t*)p.ws_bc, s);
-  return hipGetLastError();
+  const int64_t G = p.batch * p.groups_per_batch;
+  const dim3 grid((unsigned)(G * p.segments)), block(kLanes * NG);
+  const uint32_t* bcp = (const uint32_t*)p.ws_bc;
+  hipError_t e;
+  if (p.ev_start) {
+    e = hipEventRecord((hipEvent_t)p.ev_start, st);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((bwd_pass_f_kernel<N, NG, BF16, VEC, HAS_Z>), grid, block, 0,
+                     st, p.u, p.delta, p.z, p.dout, p.A, p.bias, p.ws_ck,
+                     p.ws_cd, p.ws_S, p.ws_R, p.ws_sum, bcp, s);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t threads = G * N * kLanes;
+  hipLaunchKernelGGL(bwd_combine_kernel, dim3((unsigned)((threads + 255) / 256)),
+                     dim3(256), 0, st, p.A, p.h0, p.dlast, p.ws_S, p.ws_R,
+                     p.ws_sum, p.ws_hin, p.ws_gin, s, N, G);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_pass_r_kernel<N, NG, BF16, VEC, HAS_Z>), grid, block, 0,
+                     st, p.u, p.delta, p.z, p.dout, p.A, p.D, p.bias, p.du,
+                     p.ddelta, p.dz, p.dh0, p.ws_ck, p.ws_cd, p.ws_hin, p.ws_gin,
+                     p.ws_dbc, p.ws_dA, p.ws_dDb, bcp, s);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.ev_stop) e = hipEventRecord((hipEvent_t)p.ev_stop, st);
+  return e;
 }
 
 template <int N, bool BF16, bool VEC>
@@ -466,27 +654,21 @@ hipError_t launch_n(const BwdParams& p, hipStream_t st) {
   s.L = p.L;
   s.groups_per_batch = p.groups_per_batch;
   s.tiles = p.tiles;
+  s.segments = p.segments;
+  s.seg_tiles = p.seg_tiles;
   s.softplus = p.softplus;
-  s.reserved = 0;
+  s.batch = (int32_t)p.batch;
   hipError_t e = launch_bc_pack(p.B, p.C, p.ws_bc, p.batch, p.L, Lp, N, NG,
-                                BF16, Lp * WPS, st);
+                                BF16, BF16, Lp * WPS, st);
   if (e != hipSuccess) return e;
-  if (p.ev_start) {
-    e = hipEventRecord((hipEvent_t)p.ev_start, st);
-    if (e != hipSuccess) return e;
-  }
-  e = p.z ? launch_main<N, BF16, VEC, true>(p, s, st)
-          : launch_main<N, BF16, VEC, false>(p, s, st);
+  e = p.z ? launch_passes<N, BF16, VEC, true>(p, s, st)
+          : launch_passes<N, BF16, VEC, false>(p, s, st);
   if (e != hipSuccess) return e;
-  if (p.ev_stop) {
-    e = hipEventRecord((hipEvent_t)p.ev_stop, st);
-    if (e != hipSuccess) return e;
-  }
   const int64_t threads = p.batch * p.L * 2 * N + p.dim * N + p.dim;
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((threads + 255) / 256)),
                      dim3(256), 0, st, p.ws_dbc, p.ws_dA, p.ws_dDb, p.dB, p.dC,
                      p.dA, p.dD, p.dbias, p.batch, p.dim, p.L, Lp, N,
-                     p.groups_per_batch);
+                     p.groups_per_batch, p.segments);
   return hipGetLastError();
 }
 
@@ -504,8 +686,41 @@ int bwd_tile() { return kT; }
 
 int bwd_waves_per_group(int N) { return N >= 4 ? N / 4 : 1; }
 
+int bwd_segments(int64_t groups, int64_t tiles, int cus, int forced) {
+  int64_t P = 1;
+  if (forced > 0) {
+    P = forced;
+  } else {
+    // Pass R holds two workgroups per CU.  Take the fewest segments that give
+    // at least two full rounds of tasks with the last round at least 90%
+    // full; else the fullest last round.
+    const int64_t slots = 2 * (int64_t)std::max(cus, 1);
+    const int64_t pmax = std::max<int64_t>(1, tiles / kMinSegTiles);
+    double best = -1.0;
+    for (int64_t q = 1; q <= pmax; ++q) {
+      const int64_t seg_tiles = (tiles + q - 1) / q;
+      const int64_t pq = (tiles + seg_tiles - 1) / seg_tiles;
+      const int64_t tasks = groups * pq;
+      const int64_t rounds = (tasks + slots - 1) / slots;
+      const double fill = (double)tasks / (double)(rounds * slots);
+      if (tasks >= 2 * slots && fill >= 0.9) {
+        P = pq;
+        break;
+      }
+      if (fill > best + 1e-9) {
+        best = fill;
+        P = pq;
+      }
+    }
+  }
+  P = std::max<int64_t>(1, std::min<int64_t>(P, tiles));
+  // whole tiles per segment; the count follows from the segment length
+  const int64_t seg_tiles = (tiles + P - 1) / P;
+  return (int)((tiles + seg_tiles - 1) / seg_tiles);
+}
+
 int64_t bwd_workspace(int64_t batch, int64_t dim, int64_t L, int N, bool bf16,
-                      void* ws, BwdParams* p) {
+                      int segments, void* ws, BwdParams* p) {
   const int NG = bwd_waves_per_group(N);
   const int npw = N / NG;
   const int wps = bf16 ? npw : 2 * npw;
@@ -513,14 +728,22 @@ int64_t bwd_workspace(int64_t batch, int64_t dim, int64_t L, int N, bool bf16,
   const int64_t Lp = tiles * kT;
   const int64_t gpb = (dim + kLanes - 1) / kLanes;
   const int64_t G = batch * gpb;
-  const int64_t sizes[5] = {
-      batch * NG * Lp * wps * 4,   // packed B/C runs
-      G * tiles * N * kLanes * 4,  // tile checkpoints
-      G * Lp * 2 * N * 4,          // channel-group dB/dC sums
-      batch * dim * N * 4,         // per-batch dA
-      batch * dim * 2 * 4};        // per-batch dD, dbias
-  int64_t off[5], total = 0;
-  for (int i = 0; i < 5; ++i) {
+  const int64_t tasks = G * segments;
+  const int64_t sizes[12] = {
+      batch * NG * Lp * wps * 4,        // packed B/C runs
+      G * tiles * N * kLanes * 4,       // tile checkpoints
+      G * tiles * kLanes * 4,           // running sums of Delta at tiles
+      tasks * N * kLanes * 4,           // segment end states
+      tasks * N * kLanes * 4,           // segment reverse aggregates
+      tasks * kLanes * 8,               // segment sums of Delta
+      tasks * N * kLanes * 4,           // segment initial states
+      tasks * N * kLanes * 4,           // segment incoming gradients
+      G * Lp * 2 * N * 4,               // channel-group dB/dC sums
+      segments * batch * dim * N * 4,   // partial dA
+      segments * batch * dim * 2 * 4,   // partial dD, dbias
+      0};
+  int64_t off[12], total = 0;
+  for (int i = 0; i < 12; ++i) {
     off[i] = total;
     total += up256(sizes[i]);
   }
@@ -528,9 +751,15 @@ int64_t bwd_workspace(int64_t batch, int64_t dim, int64_t L, int N, bool bf16,
     char* base = static_cast<char*>(ws);
     p->ws_bc = base + off[0];
     p->ws_ck = reinterpret_cast<float*>(base + off[1]);
-    p->ws_dbc = reinterpret_cast<float*>(base + off[2]);
-    p->ws_dA = reinterpret_cast<float*>(base + off[3]);
-    p->ws_dDb = reinterpret_cast<float*>(base + off[4]);
+    p->ws_cd = reinterpret_cast<float*>(base + off[2]);
+    p->ws_S = reinterpret_cast<float*>(base + off[3]);
+    p->ws_R = reinterpret_cast<float*>(base + off[4]);
+    p->ws_sum = reinterpret_cast<double*>(base + off[5]);
+    p->ws_hin = reinterpret_cast<float*>(base + off[6]);
+    p->ws_gin = reinterpret_cast<float*>(base + off[7]);
+    p->ws_dbc = reinterpret_cast<float*>(base + off[8]);
+    p->ws_dA = reinterpret_cast<float*>(base + off[9]);
+    p->ws_dDb = reinterpret_cast<float*>(base + off[10]);
   }
   return total;
 }

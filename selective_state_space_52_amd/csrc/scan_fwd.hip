@@ -51,10 +51,13 @@ struct ScanShape {
 
 // Writes the packed runs of `steps` timesteps per wave (steps >= L; the
 // timesteps from L on are written as zeros) with `run_words` words per run.
+// The source is bf16 or fp32 (src_bf16); the runs keep bf16 (dst_bf16) or
+// hold fp32.
 __global__ void __launch_bounds__(256)
     bc_pack_kernel(const void* __restrict__ Bm, const void* __restrict__ Cm,
                    void* __restrict__ packed, int64_t batch, int64_t L,
-                   int64_t steps, int N, int NG, int bf16, int64_t run_words) {
+                   int64_t steps, int N, int NG, int src_bf16, int dst_bf16,
+                   int64_t run_words) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = batch * steps * 2 * N;
   if (i >= total) return;
@@ -69,14 +72,18 @@ __global__ void __launch_bounds__(256)
   const int n = g * npw + (j < npw ? j : j - npw);
   const int64_t src = (b * L + t) * N + n;
   const void* m = j < npw ? Bm : Cm;
-  const int64_t vals_per_word = bf16 ? 2 : 1;
+  const int64_t vals_per_word = dst_bf16 ? 2 : 1;
   const int64_t dst = bg * run_words * vals_per_word + t * 2 * npw + j;
-  if (bf16)
+  if (dst_bf16) {
     static_cast<uint16_t*>(packed)[dst] =
         t < L ? static_cast<const uint16_t*>(m)[src] : (uint16_t)0;
-  else
-    static_cast<float*>(packed)[dst] =
-        t < L ? static_cast<const float*>(m)[src] : 0.0f;
+  } else {
+    float v = 0.0f;
+    if (t < L)
+      v = src_bf16 ? bf16_bits(static_cast<const uint16_t*>(m)[src])
+                   : static_cast<const float*>(m)[src];
+    static_cast<float*>(packed)[dst] = v;
+  }
 }
 
 // Main pass (AGG = false): scans each task's time range from its initial
@@ -432,7 +439,7 @@ hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
   hipError_t e;
   {
     constexpr int WPS = BCLayout<N / NG, BF16>::kWordsPerStep;
-    e = launch_bc_pack(p.B, p.C, p.ws_bc, p.batch, p.L, p.L, N, NG, BF16,
+    e = launch_bc_pack(p.B, p.C, p.ws_bc, p.batch, p.L, p.L, N, NG, BF16, BF16,
                        bc_run_words(p.L, WPS), stream);
     if (e != hipSuccess) return e;
   }
@@ -497,12 +504,12 @@ hipError_t launch_dtype(const ScanParams& p, bool bf16, bool vec,
 
 hipError_t launch_bc_pack(const void* B, const void* C, void* packed,
                           int64_t batch, int64_t L, int64_t steps, int N,
-                          int waves, bool bf16, int64_t run_words,
-                          hipStream_t stream) {
+                          int waves, bool src_bf16, bool dst_bf16,
+                          int64_t run_words, hipStream_t stream) {
   const int64_t total = batch * steps * 2 * N;
   hipLaunchKernelGGL(bc_pack_kernel, dim3((unsigned)((total + 255) / 256)),
                      dim3(256), 0, stream, B, C, packed, batch, L, steps, N,
-                     waves, bf16 ? 1 : 0, run_words);
+                     waves, src_bf16 ? 1 : 0, dst_bf16 ? 1 : 0, run_words);
   return hipGetLastError();
 }
 

@@ -122,7 +122,7 @@ def test_bwd_validation_codes(L):
     assert _bwd(L, _dims(), dz=None) == -1                  # z without dz
     assert _bwd(L, _dims(), z=None) == -1                   # dz without z
     assert _bwd(L, _dims(flags=1)) == -3                    # no flags
-    assert _bwd(L, _dims(ts=2)) == -2                       # no time split
+    assert _bwd(L, _dims(ts=-1)) == -2
     for bad in (dict(batch=0), dict(dim=-1), dict(L_=0)):
         assert _bwd(L, _dims(**bad)) == -2, bad
     assert _bwd(L, _dims(N=3)) == -3

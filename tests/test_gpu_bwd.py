@@ -26,7 +26,7 @@ TOL = 2e-4
 IO_GRADS = ("du", "ddelta", "dz")
 
 
-def gpu_bwd(inp, grads, h0=None, use_dlast=True, want_dh0=True):
+def gpu_bwd(inp, grads, h0=None, use_dlast=True, want_dh0=True, time_segments=0):
     import selective_state_space_52_amd as m
     g = m.selective_scan_bwd(
         to_dev(inp["u"]), to_dev(inp["delta"]), to_dev(inp["A"]),
@@ -34,7 +34,7 @@ def gpu_bwd(inp, grads, h0=None, use_dlast=True, want_dh0=True):
         D=to_dev(inp["D"]), z=to_dev(inp["z"]),
         delta_bias=to_dev(inp["delta_bias"]), softplus=inp["softplus"],
         h0=to_dev(h0), dlast=to_dev(grads["dlast"]) if use_dlast else None,
-        want_dh0=want_dh0)
+        want_dh0=want_dh0, time_segments=time_segments)
     torch.cuda.synchronize()
     return {k: (None if v is None else v.cpu()) for k, v in g.items()}
 
@@ -146,6 +146,28 @@ def test_bwd_state_gradients(use_h0, use_dlast):
     g = gpu_bwd(inp, gr, h0=h0, use_dlast=use_dlast)
     r = oracle_bwd(inp, gr, h0=h0, use_dlast=use_dlast)
     check_all(g, r, "bf16", "state h0=%s dlast=%s" % (use_h0, use_dlast))
+
+
+SEGMENTS = [
+    # io, batch, dim, N, L, segments -- carried state and gradient across
+    # segment ends, with h0 and dlast
+    ("bf16", 2, 96, 16, 500, 2),
+    ("bf16", 1, 70, 16, 333, 5),
+    ("f32", 1, 64, 16, 1000, 7),
+    ("bf16", 2, 64, 8, 200, 13),    # one tile per segment
+    ("f32", 1, 40, 2, 100, 3),
+]
+
+
+@pytest.mark.parametrize("io,batch,dim,N,L,P", SEGMENTS,
+                         ids=["%s-b%d-d%d-n%d-l%d-p%d" % s for s in SEGMENTS])
+def test_bwd_time_segments(io, batch, dim, N, L, P):
+    s, inp, gr = _case("mamba130m_layer", io=io, batch=batch, dim=dim, dstate=N,
+                       seqlen=L, seed=500 + P)
+    h0 = W.make_initial_state(s)
+    g = gpu_bwd(inp, gr, h0=h0, time_segments=P)
+    check_all(g, oracle_bwd(inp, gr, h0=h0), io,
+              "segments %s" % ((io, batch, dim, N, L, P),))
 
 
 def test_bwd_deterministic():
