@@ -55,6 +55,9 @@ def _open(path):
     lib.mssm_oracle_scan_row.restype = None
     lib.mssm_oracle_scan_bwd.argtypes = [i64, i64, i64, i64] + [_D] * 8 + [cint] + [_D] * 12
     lib.mssm_oracle_scan_bwd.restype = cint
+    lib.mssm_oracle_causal_conv1d.argtypes = [i64, i64, i64, i64, _D, _D, _D,
+                                              _D, cint, _D]
+    lib.mssm_oracle_causal_conv1d.restype = cint
     return lib
 
 
@@ -161,6 +164,27 @@ class Oracle:
             raise ValueError("oracle: scan_bwd failed (%d)" % rc)
         return o
 
+    def causal_conv1d(self, x, w, bias=None, init=None, silu=True):
+        """Causal depthwise convolution over time in fp64.
+
+        x: (batch, dim, L); w: (dim, K); bias: (dim,) or None; init:
+        (batch, dim, K-1) values of x before t = 0, or None for zeros.
+        Returns (batch, dim, L) fp64: silu(conv) or, with silu=False, conv.
+        """
+        x, w, bias, init = map(_f64, (x, w, bias, init))
+        batch, dim, L = x.shape
+        K = w.shape[1]
+        assert w.shape == (dim, K) and K >= 1
+        assert bias is None or bias.shape == (dim,)
+        assert init is None or init.shape == (batch, dim, K - 1)
+        out = np.empty((batch, dim, L), dtype=np.float64)
+        rc = self._lib.mssm_oracle_causal_conv1d(
+            batch, dim, L, K, _ptr(x), _ptr(w), _ptr(bias), _ptr(init),
+            int(bool(silu)), _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle: bad conv width %d" % K)
+        return out
+
     def state_update(self, state, x, dt, A, B, C, D=None, z=None,
                      dt_bias=None, softplus=True, nthreads=None):
         """Single-token decode step in fp64.
@@ -214,3 +238,8 @@ def state_update(*args, **kwargs):
 def scan_bwd(*args, **kwargs):
     """Gradients of the scan in fp64 (see Oracle.scan_bwd)."""
     return _get().scan_bwd(*args, **kwargs)
+
+
+def causal_conv1d(*args, **kwargs):
+    """Causal depthwise convolution in fp64 (see Oracle.causal_conv1d)."""
+    return _get().causal_conv1d(*args, **kwargs)

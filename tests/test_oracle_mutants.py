@@ -53,6 +53,14 @@ MUTANTS = [
      "dC_b[t * dstate + n] += dy * H[t * dstate + n];\n            dB_b[t * dstate + n] += g[n] * DT[t] * u[t];\n            g[n] += dy * C_b[t * dstate + n];"),
     ("bwd_dh0_dropped", "dh0[n] = g[n];", "dh0[n] = 0.0;"),
     ("bwd_dD_missing", "*dD += dy * u[t];", "*dD += 0.0 * u[t];"),
+    # causal conv
+    ("conv_kernel_not_flipped", "v += wr[k] * xv;", "v += wr[K - 1 - k] * xv;"),
+    ("conv_window_off_by_one", "const int64_t s = t - (K - 1) + k;",
+     "const int64_t s = t - K + k;"),
+    ("conv_bias_dropped", "double v = bias ? bias[d] : 0.0;", "double v = 0.0;"),
+    ("conv_silu_missing", "o[t] = silu ? oracle_silu(v) : v;", "o[t] = v;"),
+    ("conv_init_ignored", "else if (ir)", "else if (0 && ir)"),
+    ("conv_init_misaligned", "xv = ir[(K - 1) + s];", "xv = ir[-s - 1];"),
 ]
 
 
