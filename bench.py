@@ -54,6 +54,9 @@ SLOTS_PER_ELEM = 18
 # (1), dz (2), dD and dbias accumulates (2).
 BWD_SLOTS_PER_STATE_ELEM = 16
 BWD_SLOTS_PER_ELEM = 37
+# The width-4 causal conv in the fused path adds per element: 4 fmas and
+# silu = exp + reciprocal (2 + 2) + 3, i.e. 11 slots.
+CONV_SLOTS_PER_ELEM = 11
 
 
 def parse():
@@ -67,6 +70,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=20)
     ap.add_argument("--bwd-time-segments", type=int, default=0)
     ap.add_argument("--decode-steps", type=int, default=1000)
@@ -236,11 +240,103 @@ def main():
         res["backward"] = bench_backward(torch, W, m, dev, s, sets, hev,
                                          args.backward_steps,
                                          args.bwd_time_segments)
+    if not args.no_conv:
+        res["conv"] = bench_conv(torch, W, m, dev, s, sets, hev, ms)
     if not args.no_decode:
         res["decode"] = bench_decode(torch, W, m, dev, args.decode_steps)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(s, base, args.cpu_seconds, nbytes)
     print(json.dumps(res), flush=True)
+
+
+def _time(torch, stream, fn, steps, warmup=3):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_conv(torch, W, m, dev, s, sets, hev, scan_ms, steps=20):
+    """The causal conv (width 4, silu) ahead of the scan on the same workload:
+    the standalone conv kernel (HBM-bound) and the conv fused into the scan's
+    load stage, against running the two one after the other."""
+    stream = torch.cuda.current_stream(dev)
+    cps = [{k: v.to(dev) for k, v in
+            W.make_conv_params(W.spec(s.name, seed=s.seed + 1000 * r)).items()}
+           for r in range(len(sets))]
+    u_bufs = [torch.empty_like(d["u"]) for d in sets]
+
+    def conv(i):
+        d, c = sets[i % len(sets)], cps[i % len(sets)]
+        m.causal_conv1d_fwd(d["u"], c["weight"], c["bias"], c["init"],
+                            out=u_bufs[i % len(sets)])
+
+    def fused(i):
+        d, c = sets[i % len(sets)], cps[i % len(sets)]
+        m.selective_scan_fwd_conv(d["u"], c["weight"], d["delta"], d["A"], d["B"],
+                                  d["C"], conv_bias=c["bias"], conv_init=c["init"],
+                                  D=d["D"], z=d["z"], delta_bias=d["delta_bias"],
+                                  softplus=s.softplus, last_state=d["last"],
+                                  out=d["out"])
+
+    def separate(i):
+        conv(i)
+        d = sets[i % len(sets)]
+        m.selective_scan_fwd(u_bufs[i % len(sets)], d["delta"], d["A"], d["B"], d["C"],
+                             D=d["D"], z=d["z"], delta_bias=d["delta_bias"],
+                             softplus=s.softplus, last_state=d["last"], out=d["out"])
+
+    conv_ms = _time(torch, stream, conv, steps)
+    sep_ms = _time(torch, stream, separate, steps)
+    pairs = [(hev.create(), hev.create()) for _ in range(steps)]
+    k = [0]
+
+    def fused_timed(i):
+        if k[0] < len(pairs):
+            m.set_scan_timing_events(*pairs[k[0]])
+        k[0] += 1
+        fused(i)
+    for i in range(3):
+        fused(i)
+    torch.cuda.synchronize()
+    k[0] = 0
+    fused_ms = _time(torch, stream, fused_timed, steps, warmup=0)
+    m.set_scan_timing_events(None, None)
+    main_ms = sum(hev.elapsed_ms(a, b) for a, b in pairs) / steps
+    for a, b in pairs:
+        hev.destroy(a)
+        hev.destroy(b)
+    cb = W.conv_bytes(s)
+    cgbs = cb / (conv_ms * 1e-3) / 1e9
+    fused_bytes = W.scan_bytes(s) + 4 * s.dim * 5 + s.batch * s.dim * 3 * (2 if s.io == "bf16" else 4)
+    slots = (s.state_elements * SLOTS_PER_STATE_ELEM +
+             s.elements * (SLOTS_PER_ELEM + CONV_SLOTS_PER_ELEM))
+    achieved = slots / (main_ms * 1e-3) / 1e12
+    return {"workload": "causal conv width 4 + silu feeding the scan on %s" % s.name,
+            "conv_ms": round(conv_ms, 5),
+            "conv_roofline": {"bound": "hbm", "achieved": round(cgbs, 1),
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(cgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                              "kernel": "causal_conv1d_kernel",
+                              "algorithmic_bytes": cb},
+            "separate_conv_then_scan_ms": round(sep_ms, 5),
+            "fused_ms": round(fused_ms, 5),
+            "fused_speedup_vs_separate": round(sep_ms / fused_ms, 3),
+            "fused_extra_ms_vs_scan_alone": round(fused_ms - scan_ms, 5),
+            "fused_algorithmic_bytes": fused_bytes,
+            "fused_gb_per_s": round(fused_bytes / (fused_ms * 1e-3) / 1e9, 1),
+            "fused_roofline": {"bound": "alu", "achieved": round(achieved, 3),
+                               "peak": round(VALU_PEAK_TSLOTS, 3), "unit": "Tslot/s",
+                               "frac": round(achieved / VALU_PEAK_TSLOTS, 4),
+                               "traffic": None,
+                               "kernel": "scan_kernel with the conv (main pass)",
+                               "kernel_ms": round(main_ms, 5)}}
 
 
 def bench_backward(torch, W, m, dev, s, sets, hev, steps, time_segments=0):

@@ -112,6 +112,47 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
                             const mssm_dims* dims, void* stream);
 
 /*
+ * Causal depthwise convolution over time, the Mamba block's local
+ * convolution that feeds the scan (width d_conv = 4 on page "Mamba State
+ * Space Model", model construction; page "Mamba: Selective State Space
+ * Models", "Quick Start"; provided by the causal-conv1d package the pages
+ * name).  Per (batch, channel) row:
+ *     v_t   = bias[d] + sum_{k=0}^{width-1} weight[d,k] * x_{t-(width-1)+k}
+ *     out_t = silu(v_t) if silu, else v_t
+ * so weight[d, width-1] multiplies the current step; x at t < 0 comes from
+ * `init` or is 0.
+ *   x, out  : (batch, dim, seqlen) io dtype; out must not overlap an input
+ *   weight  : (dim, width) fp32;  bias : (dim) fp32 or NULL
+ *   init    : (batch, dim, width-1) io dtype, x at t = -(width-1) .. -1
+ *             (the last inputs of the previous piece of the sequence), or NULL
+ *   width   : 2, 3 or 4
+ * dims->dstate is ignored; flags and time_segments must be 0.
+ */
+int mssm_causal_conv1d_fwd(const void* x, const float* weight,
+                           const float* bias, const void* init, int width,
+                           int silu, void* out, const mssm_dims* dims,
+                           void* stream);
+
+/*
+ * The forward scan fed by the width-4 causal convolution: the scan input is
+ * u = silu(conv(x)) as mssm_causal_conv1d_fwd(width = 4, silu = 1) computes
+ * it, formed while the scan loads its input (u never goes to memory unless
+ * u_out is given).  Arguments as in mssm_selective_scan_fwd, with
+ *   x           : (batch, dim, seqlen) io dtype, the convolution input
+ *   conv_weight : (dim, 4) fp32 (required);  conv_bias : (dim) fp32 or NULL
+ *   conv_init   : (batch, dim, 3) io dtype x before t = 0, or NULL (zeros)
+ *   u_out       : (batch, dim, seqlen) io dtype receiving u, or NULL
+ */
+int mssm_selective_scan_fwd_conv(const void* x, const float* conv_weight,
+                                 const float* conv_bias, const void* conv_init,
+                                 const void* delta, const float* A,
+                                 const void* B, const void* C, const float* D,
+                                 const void* z, const float* delta_bias,
+                                 int softplus, void* out, float* last_state,
+                                 void* u_out, const mssm_dims* dims,
+                                 void* stream);
+
+/*
  * Backward of the forward scan: the gradients of
  *     loss = sum(dout * out) + sum(dlast * h_{L-1})
  * with respect to every input, for training through the scan (page "Mamba:

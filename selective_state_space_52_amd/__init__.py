@@ -19,8 +19,8 @@ import torch
 from ._lib import (MSSM_BF16, MSSM_F32, MSSM_FLAG_LOAD_STATE, Dims, MssmError,
                    Plan, check, lib)
 
-__all__ = ["selective_scan_fwd", "selective_scan_bwd", "selective_state_update",
-           "scan_plan",
+__all__ = ["selective_scan_fwd", "selective_scan_bwd", "selective_scan_fwd_conv",
+           "causal_conv1d_fwd", "selective_state_update", "scan_plan",
            "set_scan_timing_events", "MssmError", "abi_version"]
 
 _IO = {torch.float32: MSSM_F32, torch.bfloat16: MSSM_BF16}
@@ -106,6 +106,75 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
             _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
             _ptr(delta_bias), int(bool(softplus)), _ptr(out), _ptr(last_state),
             dims, _stream(dev)))
+    return out
+
+
+def causal_conv1d_fwd(x, weight, bias=None, init=None, silu=True, out=None):
+    """Causal depthwise convolution over time: x (batch, dim, L) fp32 or
+    bf16, weight (dim, width) fp32 with width 2..4, bias (dim,) fp32 or None,
+    init (batch, dim, width-1) in x's dtype (inputs before t = 0) or None.
+    Returns silu(conv) (or conv with silu=False) in x's dtype."""
+    if x.dtype not in _IO:
+        raise ValueError("x must be float32 or bfloat16")
+    batch, dim, L = x.shape
+    width = weight.shape[-1]
+    dev = x.device
+    _need(x, "x", x.dtype, (batch, dim, L), dev)
+    _need(weight, "weight", torch.float32, (dim, width), dev)
+    _need(bias, "bias", torch.float32, (dim,), dev)
+    _need(init, "init", x.dtype, (batch, dim, width - 1), dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", x.dtype, (batch, dim, L), dev)
+    dims = Dims(batch, dim, 0, L, _IO[x.dtype], 0, 0, 0)
+    with torch.cuda.device(dev):
+        check(lib().mssm_causal_conv1d_fwd(
+            _ptr(x), _ptr(weight), _ptr(bias), _ptr(init), int(width),
+            int(bool(silu)), _ptr(out), dims, _stream(dev)))
+    return out
+
+
+def selective_scan_fwd_conv(x, conv_weight, delta, A, B, C, conv_bias=None,
+                            conv_init=None, D=None, z=None, delta_bias=None,
+                            softplus=True, last_state=None, load_state=False,
+                            out=None, u_out=None, time_segments=0):
+    """The forward scan whose input is u = silu(causal_conv(x)) (width 4),
+    formed inside the scan kernel.  x: (batch, dim, L); conv_weight (dim, 4)
+    fp32; conv_bias (dim,) fp32 or None; conv_init (batch, dim, 3) or None;
+    the other arguments as in selective_scan_fwd.  u_out, if given, receives
+    u.  Returns out."""
+    if x.dtype not in _IO:
+        raise ValueError("x must be float32 or bfloat16")
+    io = x.dtype
+    batch, dim, L = x.shape
+    N = A.shape[-1]
+    dev = x.device
+    _need(x, "x", io, (batch, dim, L), dev)
+    _need(conv_weight, "conv_weight", torch.float32, (dim, 4), dev)
+    _need(conv_bias, "conv_bias", torch.float32, (dim,), dev)
+    _need(conv_init, "conv_init", io, (batch, dim, 3), dev)
+    _need(u_out, "u_out", io, (batch, dim, L), dev)
+    _need(delta, "delta", io, (batch, dim, L), dev)
+    _need(z, "z", io, (batch, dim, L), dev)
+    _need(B, "B", io, (batch, L, N), dev)
+    _need(C, "C", io, (batch, L, N), dev)
+    _need(A, "A", torch.float32, (dim, N), dev)
+    _need(D, "D", torch.float32, (dim,), dev)
+    _need(delta_bias, "delta_bias", torch.float32, (dim,), dev)
+    _need(last_state, "last_state", torch.float32, (batch, dim, N), dev)
+    if load_state and last_state is None:
+        raise ValueError("load_state needs last_state")
+    if out is None:
+        out = torch.empty((batch, dim, L), dtype=io, device=dev)
+    _need(out, "out", io, (batch, dim, L), dev)
+    dims = Dims(batch, dim, N, L, _IO[io],
+                MSSM_FLAG_LOAD_STATE if load_state else 0, time_segments, 0)
+    with torch.cuda.device(dev):
+        check(lib().mssm_selective_scan_fwd_conv(
+            _ptr(x), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_init),
+            _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(delta_bias), int(bool(softplus)), _ptr(out), _ptr(last_state),
+            _ptr(u_out), dims, _stream(dev)))
     return out
 
 

@@ -19,6 +19,7 @@ STATUS = {
 
 # every symbol include/mssm.h declares
 EXPORTS = ("mssm_selective_scan_fwd", "mssm_selective_scan_bwd",
+           "mssm_selective_scan_fwd_conv", "mssm_causal_conv1d_fwd",
            "mssm_selective_state_update",
            "mssm_selective_scan_fwd_plan", "mssm_set_scan_timing_events",
            "mssm_status_string", "mssm_last_error", "mssm_abi_version")
@@ -64,6 +65,13 @@ def lib():
                                               fp, vp, fp, fp,
                                               ctypes.POINTER(Dims), vp]
         L.mssm_selective_scan_bwd.restype = i
+        L.mssm_selective_scan_fwd_conv.argtypes = [vp, fp, fp, vp, vp, fp, vp, vp,
+                                                   fp, vp, fp, i, vp, fp, vp,
+                                                   ctypes.POINTER(Dims), vp]
+        L.mssm_selective_scan_fwd_conv.restype = i
+        L.mssm_causal_conv1d_fwd.argtypes = [vp, fp, fp, vp, i, i, vp,
+                                             ctypes.POINTER(Dims), vp]
+        L.mssm_causal_conv1d_fwd.restype = i
         L.mssm_selective_state_update.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp,
                                                   fp, i, vp, ctypes.POINTER(Dims), vp]
         L.mssm_selective_state_update.restype = i

@@ -19,7 +19,8 @@ LIB = os.path.join(HERE, "libmssm.so")
 OBJDIR = os.path.join(HERE, "_build")
 
 ARCH = "gfx950"
-SOURCES = ["scan_fwd.hip", "scan_bwd.hip", "state_update.hip", "mssm_api.cpp"]
+SOURCES = ["scan_fwd.hip", "scan_bwd.hip", "state_update.hip", "conv1d.hip",
+           "mssm_api.cpp"]
 
 # Packed fp32 VALU forms are switched off for every device compilation.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -204,11 +204,18 @@ int mssm_selective_scan_fwd_plan(const mssm_dims* dims, mssm_plan* plan) {
   return make_plan(dims, g_cu_count > 0 ? g_cu_count : kDefaultCUs, plan);
 }
 
-int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
-                            const void* B, const void* C, const float* D,
-                            const void* z, const float* delta_bias,
-                            int softplus, void* out, float* last_state,
-                            const mssm_dims* dims, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward scan, optionally fed by the causal conv (conv_w non-null: `u`
+// is the conv input x).
+int scan_fwd_impl(const void* u, const void* delta, const float* A,
+                  const void* B, const void* C, const float* D, const void* z,
+                  const float* delta_bias, int softplus, void* out,
+                  float* last_state, const float* conv_w, const float* conv_b,
+                  const void* conv_init, void* u_out, const mssm_dims* dims,
+                  void* stream) {
   int rc = check_common_dims(dims);
   if (rc != MSSM_OK) return rc;
   if (dims->flags & ~MSSM_FLAG_LOAD_STATE) return MSSM_ERR_UNSUPPORTED;
@@ -225,10 +232,10 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
       !product_ok(batch, L, N, lim) || !product_ok(batch, dim, N, lim))
     return MSSM_ERR_DIMS;
 
-  const void* ios[] = {u, delta, B, C, out, z};
+  const void* ios[] = {u, delta, B, C, out, z, conv_init, u_out};
   for (const void* p : ios)
     if (p && !aligned(p, io)) return MSSM_ERR_ALIGN;
-  const void* f32s[] = {A, D, delta_bias, last_state};
+  const void* f32s[] = {A, D, delta_bias, last_state, conv_w, conv_b};
   for (const void* p : f32s)
     if (p && !aligned(p, 4)) return MSSM_ERR_ALIGN;
 
@@ -236,13 +243,18 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
   const int64_t bcbytes = batch * L * N * (int64_t)io;
   const Range r_out = range_of(out, ebytes);
   const Range r_state = range_of(last_state, batch * dim * N * 4);
+  const Range r_uout = range_of(u_out, ebytes);
   const Range ins[] = {range_of(u, ebytes),      range_of(delta, ebytes),
                        range_of(z, ebytes),      range_of(B, bcbytes),
                        range_of(C, bcbytes),     range_of(A, dim * N * 4),
-                       range_of(D, dim * 4),     range_of(delta_bias, dim * 4)};
+                       range_of(D, dim * 4),     range_of(delta_bias, dim * 4),
+                       range_of(conv_w, dim * 16), range_of(conv_b, dim * 4),
+                       range_of(conv_init, batch * dim * 3 * (int64_t)io)};
   for (const Range& r : ins)
-    if (overlap(r_out, r) || overlap(r_state, r)) return MSSM_ERR_ALIAS;
-  if (overlap(r_out, r_state)) return MSSM_ERR_ALIAS;
+    if (overlap(r_out, r) || overlap(r_state, r) || overlap(r_uout, r))
+      return MSSM_ERR_ALIAS;
+  if (overlap(r_out, r_state) || overlap(r_out, r_uout) || overlap(r_state, r_uout))
+    return MSSM_ERR_ALIAS;
 
   // --- validation done; HIP calls from here on ---
   if (g_cu_count <= 0) {
@@ -259,7 +271,7 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
 
   const bool vec = plan.vector_path && aligned(u, 16) && aligned(delta, 16) &&
                    aligned(out, 16) && aligned(B, 16) && aligned(C, 16) &&
-                   (!z || aligned(z, 16));
+                   (!z || aligned(z, 16)) && (!u_out || aligned(u_out, 16));
 
   mssm::ScanParams p;
   std::memset(&p, 0, sizeof(p));
@@ -275,6 +287,10 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
   p.seg_len = plan.segment_len;
   p.ev_start = g_ev_start;
   p.ev_stop = g_ev_stop;
+  p.conv_w = conv_w;
+  p.conv_b = conv_b;
+  p.conv_init = conv_init;
+  p.u_out = u_out;
 
   hipStream_t st = (hipStream_t)stream;
   int dev = -1;
@@ -318,6 +334,78 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
     }
   }
   return e == hipSuccess ? MSSM_OK : MSSM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
+                            const void* B, const void* C, const float* D,
+                            const void* z, const float* delta_bias,
+                            int softplus, void* out, float* last_state,
+                            const mssm_dims* dims, void* stream) {
+  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, out,
+                       last_state, nullptr, nullptr, nullptr, nullptr, dims,
+                       stream);
+}
+
+int mssm_selective_scan_fwd_conv(const void* x, const float* conv_weight,
+                                 const float* conv_bias, const void* conv_init,
+                                 const void* delta, const float* A,
+                                 const void* B, const void* C, const float* D,
+                                 const void* z, const float* delta_bias,
+                                 int softplus, void* out, float* last_state,
+                                 void* u_out, const mssm_dims* dims,
+                                 void* stream) {
+  if (!conv_weight) return MSSM_ERR_NULL;
+  return scan_fwd_impl(x, delta, A, B, C, D, z, delta_bias, softplus, out,
+                       last_state, conv_weight, conv_bias, conv_init, u_out,
+                       dims, stream);
+}
+
+int mssm_causal_conv1d_fwd(const void* x, const float* weight,
+                           const float* bias, const void* init, int width,
+                           int silu, void* out, const mssm_dims* dims,
+                           void* stream) {
+  if (!dims) return MSSM_ERR_NULL;
+  if (dims->io_dtype != MSSM_F32 && dims->io_dtype != MSSM_BF16)
+    return MSSM_ERR_UNSUPPORTED;
+  if (dims->flags != 0 || dims->reserved != 0) return MSSM_ERR_UNSUPPORTED;
+  if (dims->time_segments != 0) return MSSM_ERR_DIMS;
+  if (dims->batch <= 0 || dims->dim <= 0 || dims->seqlen <= 0) return MSSM_ERR_DIMS;
+  if (width < 2 || width > 4) return MSSM_ERR_UNSUPPORTED;
+  if (!x || !weight || !out) return MSSM_ERR_NULL;
+  const int64_t batch = dims->batch, dim = dims->dim, L = dims->seqlen;
+  const size_t io = dims->io_dtype == MSSM_BF16 ? 2 : 4;
+  if (!product_ok(batch, dim, L, INT64_MAX / 16)) return MSSM_ERR_DIMS;
+  const void* ios[] = {x, init, out};
+  for (const void* p : ios)
+    if (p && !aligned(p, io)) return MSSM_ERR_ALIGN;
+  const void* f32s[] = {weight, bias};
+  for (const void* p : f32s)
+    if (p && !aligned(p, 4)) return MSSM_ERR_ALIGN;
+  const int64_t ebytes = batch * dim * L * (int64_t)io;
+  const Range r_out = range_of(out, ebytes);
+  const Range ins[] = {range_of(x, ebytes), range_of(weight, dim * width * 4),
+                       range_of(bias, dim * 4),
+                       range_of(init, batch * dim * (width - 1) * (int64_t)io)};
+  for (const Range& r : ins)
+    if (overlap(r_out, r)) return MSSM_ERR_ALIAS;
+
+  mssm::ConvParams p;
+  p.x = x; p.w = weight; p.bias = bias; p.init = init; p.out = out;
+  p.batch = batch; p.dim = dim; p.L = L;
+  p.width = width;
+  p.silu = silu ? 1 : 0;
+  const bool vec = (L % 8) == 0 && ((L * (int64_t)io) % 16) == 0 &&
+                   aligned(x, 16) && aligned(out, 16);
+  hipError_t e = mssm::launch_causal_conv1d(p, io == 2, vec, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_hip_error("causal_conv1d launch", e);
+    return MSSM_ERR_HIP;
+  }
+  return MSSM_OK;
 }
 
 int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,

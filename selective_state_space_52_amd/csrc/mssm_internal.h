@@ -49,6 +49,24 @@ struct ScanParams {
   void* side_stream;
   void* ev_fork;
   void* ev_join;
+  // causal conv feeding the scan (conv_w null: `u` is the scan input itself;
+  // otherwise `u` holds the conv input x)
+  const float* conv_w;    // (dim, 4) fp32
+  const float* conv_b;    // (dim) fp32 or null
+  const void* conv_init;  // (batch, dim, 3) io dtype or null
+  void* u_out;            // (batch, dim, L) io dtype: conv output, or null
+};
+
+// Standalone causal depthwise conv: out = act(bias + sum_k w[k] x[t-K+1+k]).
+struct ConvParams {
+  const void* x;
+  const float* w;         // (dim, width) fp32
+  const float* bias;      // (dim) fp32 or null
+  const void* init;       // (batch, dim, width-1) io dtype or null
+  void* out;
+  int64_t batch, dim, L;
+  int32_t width;          // 2, 3 or 4
+  int32_t silu;
 };
 
 struct UpdateParams {
@@ -151,5 +169,7 @@ hipError_t launch_scan_bwd(const BwdParams& p, int N, bool bf16, bool vec,
                            hipStream_t stream);
 hipError_t launch_state_update(const UpdateParams& p, int N, bool bf16,
                                hipStream_t stream);
+hipError_t launch_causal_conv1d(const ConvParams& p, bool bf16, bool vec,
+                                hipStream_t stream);
 
 }  // namespace mssm

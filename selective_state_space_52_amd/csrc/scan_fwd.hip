@@ -42,6 +42,16 @@ constexpr bool kWarmScalarCache = true;
 template <int N>
 constexpr int kWaves = N >= 2 ? N / 2 : 1;
 
+// The causal depthwise conv (width 4) that can feed the scan: u = silu(bias +
+// sum_k w[k] x[t-3+k]), x at t < 0 from init (or 0).
+struct ConvArgs {
+  const float* w;      // (dim, 4) fp32
+  const float* b;      // (dim) fp32 or null
+  const void* init;    // (batch, dim, 3) io dtype (x at t = -3..-1) or null
+  void* u_out;         // (batch, dim, L) io dtype: the conv output, or null
+};
+constexpr int kConvK = 4;
+
 struct ScanShape {
   int64_t dim, L;
   int32_t softplus, load_state;
@@ -104,7 +114,8 @@ __global__ void __launch_bounds__(256)
 // timesteps: the first timestep of a batch takes the one wait, then the next
 // batch's B/C scalar loads and Delta/Delta*u LDS reads are issued, and the
 // rest of the batch computes while they are in flight.
-template <int N, int NG, bool BF16, bool VEC, bool HAS_Z, bool AGG, bool SOFTPLUS>
+template <int N, int NG, bool BF16, bool VEC, bool HAS_Z, bool AGG, bool SOFTPLUS,
+          bool CONV>
 __device__ __forceinline__ void scan_body(
     const void* __restrict__ u, const void* __restrict__ delta,
     const void* __restrict__ z, const float* __restrict__ A,
@@ -113,7 +124,7 @@ __device__ __forceinline__ void scan_body(
     float* __restrict__ ws_S, double* __restrict__ ws_sum,
     const float* __restrict__ ws_hin, const uint32_t* __restrict__ bcp,
     const ScanShape& s, float2 (&s_dw)[kTile][kLanes],
-    float (&s_y)[NG][kTile][kLanes], const int task) {
+    float (&s_y)[NG][kTile][kLanes], const int task, const ConvArgs& cv) {
   constexpr int NPW = N / NG;
   constexpr int T = kTile;
   constexpr int KC = T / NG;     // timesteps a wave prepares and emits
@@ -168,6 +179,53 @@ __device__ __forceinline__ void scan_body(
   const float Dd = (!AGG && Dv) ? Dv[dc] : 0.0f;
   double dsum = 0.0;
 
+  // With CONV, `u` holds the conv input x; each chunk also reads the 4 x
+  // values before it (row start: the init values) and turns x into u.
+  float cw[kConvK], cbias = 0.0f;
+  Raw<BF16, kConvK> rp, np_;  // x[tc-4 .. tc-1] of the current / next chunk
+  float uc[KC], un[KC];       // u of the current / next chunk
+  if constexpr (CONV) {
+#pragma unroll
+    for (int j = 0; j < kConvK; ++j) cw[j] = cv.w[dc * kConvK + j];
+    cbias = cv.b ? cv.b[dc] : 0.0f;
+  }
+  auto load_prev = [&](Raw<BF16, kConvK>& r, int64_t tc) {
+    if (tc >= kConvK) {
+      load_chunk<BF16, VEC, kConvK>(r, u, row * s.L + tc - kConvK, s.L - (tc - kConvK));
+    } else {
+      // tc == 0 (chunks start at multiples of 4): slots 1..3 hold x[-3..-1]
+      // from init, slot 0 is never used
+      raw_zero(r);
+      if (cv.init) {
+        if constexpr (BF16) {
+          const uint16_t* ip = static_cast<const uint16_t*>(cv.init) + row * (kConvK - 1);
+          r.w[0] = (uint32_t)ip[0] << 16;
+          r.w[1] = (uint32_t)ip[1] | ((uint32_t)ip[2] << 16);
+        } else {
+          const uint32_t* ip = static_cast<const uint32_t*>(cv.init) + row * (kConvK - 1);
+          r.w[1] = ip[0];
+          r.w[2] = ip[1];
+          r.w[3] = ip[2];
+        }
+      }
+    }
+  };
+  auto conv_u = [&](const Raw<BF16, KC>& px, const Raw<BF16, kConvK>& pp,
+                    float (&uo)[KC]) {
+    float xs[KC + kConvK];
+#pragma unroll
+    for (int j = 0; j < kConvK; ++j) xs[j] = raw_get(pp, j);
+#pragma unroll
+    for (int k = 0; k < KC; ++k) xs[kConvK + k] = raw_get(px, k);
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      float v = cbias;
+#pragma unroll
+      for (int j = 0; j < kConvK; ++j) v = fmaf(cw[j], xs[k + 1 + j], v);
+      uo[k] = silu_f32(v);
+    }
+  };
+
   // this wave's packed B/C run
   const uint32_t* __restrict__ bcw = bcp + (b * NG + g) * bc_run_words(s.L, WPS);
   using Batch = BCBatch<NPW, BF16>;
@@ -177,12 +235,14 @@ __device__ __forceinline__ void scan_body(
   raw_zero(rz);
   raw_zero(nz);
 
-  auto prep = [&](const Raw<BF16, KC>& pu, const Raw<BF16, KC>& pd) {
+  auto prep = [&](const Raw<BF16, KC>& pu, const Raw<BF16, KC>& pd,
+                  const float (&uv)[KC]) {
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
       const float x = raw_get(pd, k) + bv_d;
       const float dl = SOFTPLUS ? softplus_f32(x) : x;
-      s_dw[g * KC + k][lane] = make_float2(dl, dl * raw_get(pu, k));
+      const float uk = CONV ? uv[k] : raw_get(pu, k);
+      s_dw[g * KC + k][lane] = make_float2(dl, dl * uk);
     }
   };
 
@@ -206,7 +266,11 @@ __device__ __forceinline__ void scan_body(
     load_chunk<BF16, VEC, KC>(ru, u, rowoff + tc, nv);
     load_chunk<BF16, VEC, KC>(rd, delta, rowoff + tc, nv);
     if (HAS_Z && !AGG) load_chunk<BF16, VEC, KC>(rz, z, rowoff + tc, nv);
-    prep(ru, rd);
+    if constexpr (CONV) {
+      load_prev(rp, tc);
+      conv_u(ru, rp, uc);
+    }
+    prep(ru, rd, uc);
   }
   __syncthreads();
 
@@ -218,6 +282,16 @@ __device__ __forceinline__ void scan_body(
       load_chunk<BF16, VEC, KC>(nu, u, rowoff + tc, nv);
       load_chunk<BF16, VEC, KC>(nd, delta, rowoff + tc, nv);
       if (HAS_Z && !AGG) load_chunk<BF16, VEC, KC>(nz, z, rowoff + tc, nv);
+      // tc >= kTile here, so the 4 inputs before the chunk are in the row.
+      // On the vector path the load is unconditional (a conditional one
+      // makes the compiler wait for the whole prefetch right after it): a
+      // chunk past the end reads the row's last 4 inputs, which nothing uses.
+      if constexpr (CONV) {
+        if constexpr (VEC)
+          load_chunk<BF16, true, kConvK>(np_, u, rowoff + min(tc, t_end) - kConvK, kConvK);
+        else
+          load_chunk<BF16, false, kConvK>(np_, u, rowoff + tc - kConvK, nv + kConvK);
+      }
     }
 
     // state phase: every wave advances its NPW states over the whole tile
@@ -294,7 +368,8 @@ __device__ __forceinline__ void scan_body(
 
     // prep of the next tile (its Delta/Delta*u slots are free: every wave is
     // past the state phase)
-    prep(nu, nd);
+    if constexpr (CONV) conv_u(nu, np_, un);
+    prep(nu, nd, un);
 
     if constexpr (!AGG) {
       // output phase: this wave's chunk of the tile
@@ -305,17 +380,24 @@ __device__ __forceinline__ void scan_body(
         float y = 0.0f;
 #pragma unroll
         for (int w = 0; w < NG; ++w) y += s_y[w][g * KC + k][lane];
-        y = fmaf(Dd, raw_get(ru, k), y);
+        y = fmaf(Dd, CONV ? uc[k] : raw_get(ru, k), y);
         if (HAS_Z) y *= silu_f32(raw_get(rz, k));
         o[k] = y;
       }
       if (valid) store_chunk<BF16, VEC, KC>(out, rowoff + tc, o, t_end - tc);
+      if constexpr (CONV) {
+        if (valid && cv.u_out) store_chunk<BF16, VEC, KC>(cv.u_out, rowoff + tc, uc, t_end - tc);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::"s"(touch));  // keeps the warming loads
 
     ru = nu;
     rz = nz;
+    if constexpr (CONV) {
+#pragma unroll
+      for (int k = 0; k < KC; ++k) uc[k] = un[k];
+    }
     __syncthreads();
   }
 
@@ -336,7 +418,7 @@ __device__ __forceinline__ void scan_body(
 // after them, aggregate-pass tasks (task = block - n_main).  Putting the
 // aggregate pass of the time-split groups into the same launch as the main
 // pass of the whole groups lets it run on the CUs' spare workgroup slots.
-template <int N, int NG, bool BF16, bool VEC, bool HAS_Z, bool SOFTPLUS>
+template <int N, int NG, bool BF16, bool VEC, bool HAS_Z, bool SOFTPLUS, bool CONV>
 __global__ void __launch_bounds__(kLanes* NG)
     scan_kernel(const void* __restrict__ u, const void* __restrict__ delta,
                 const void* __restrict__ z, const float* __restrict__ A,
@@ -345,18 +427,18 @@ __global__ void __launch_bounds__(kLanes* NG)
                 float* __restrict__ ws_S, double* __restrict__ ws_sum,
                 const float* __restrict__ ws_hin,
                 const uint32_t* __restrict__ bcp, const ScanShape s,
-                const int n_main, const int main_base) {
+                const int n_main, const int main_base, const ConvArgs cv) {
   __shared__ float2 s_dw[kTile][kLanes];        // (Delta, Delta*u) of a tile
   __shared__ float s_y[NG][kTile][kLanes];      // per-wave partial readouts
   const int blk = blockIdx.x;
   if (blk < n_main)
-    scan_body<N, NG, BF16, VEC, HAS_Z, false, SOFTPLUS>(
+    scan_body<N, NG, BF16, VEC, HAS_Z, false, SOFTPLUS, CONV>(
         u, delta, z, A, Dv, bias, out, last_state, ws_S, ws_sum, ws_hin, bcp,
-        s, s_dw, s_y, main_base + blk);
+        s, s_dw, s_y, main_base + blk, cv);
   else
-    scan_body<N, NG, BF16, VEC, HAS_Z, true, SOFTPLUS>(
+    scan_body<N, NG, BF16, VEC, HAS_Z, true, SOFTPLUS, CONV>(
         u, delta, z, A, Dv, bias, out, last_state, ws_S, ws_sum, ws_hin, bcp,
-        s, s_dw, s_y, blk - n_main);
+        s, s_dw, s_y, blk - n_main, cv);
 }
 
 // Initial state of every segment of the split groups, from the segment
@@ -399,32 +481,33 @@ hipError_t launch_combine(const ScanParams& p, const ScanShape& s, int N,
   return hipGetLastError();
 }
 
-template <int N, int NG, bool BF16, bool VEC, bool HAS_Z>
+template <int N, int NG, bool BF16, bool VEC, bool HAS_Z, bool CONV>
 hipError_t launch_one(const ScanParams& p, const ScanShape& s, int n_main,
                       int main_base, int n_agg, hipStream_t stream) {
   const dim3 grid(n_main + n_agg), block(kLanes * NG);
+  const ConvArgs cv{p.conv_w, p.conv_b, p.conv_init, p.u_out};
   if (p.softplus)
-    hipLaunchKernelGGL((scan_kernel<N, NG, BF16, VEC, HAS_Z, true>), grid, block, 0,
-                       stream, p.u, p.delta, p.z, p.A, p.D, p.bias, p.out,
+    hipLaunchKernelGGL((scan_kernel<N, NG, BF16, VEC, HAS_Z, true, CONV>), grid, block,
+                       0, stream, p.u, p.delta, p.z, p.A, p.D, p.bias, p.out,
                        p.last_state, p.ws_S, p.ws_sum, p.ws_hin,
-                       (const uint32_t*)p.ws_bc, s, n_main, main_base);
+                       (const uint32_t*)p.ws_bc, s, n_main, main_base, cv);
   else
-    hipLaunchKernelGGL((scan_kernel<N, NG, BF16, VEC, HAS_Z, false>), grid, block, 0,
-                       stream, p.u, p.delta, p.z, p.A, p.D, p.bias, p.out,
+    hipLaunchKernelGGL((scan_kernel<N, NG, BF16, VEC, HAS_Z, false, CONV>), grid, block,
+                       0, stream, p.u, p.delta, p.z, p.A, p.D, p.bias, p.out,
                        p.last_state, p.ws_S, p.ws_sum, p.ws_hin,
-                       (const uint32_t*)p.ws_bc, s, n_main, main_base);
+                       (const uint32_t*)p.ws_bc, s, n_main, main_base, cv);
   return hipGetLastError();
 }
 
-template <int N, int NG, bool BF16, bool VEC>
+template <int N, int NG, bool BF16, bool VEC, bool CONV>
 hipError_t launch_tasks(const ScanParams& p, const ScanShape& s, int n_main,
                         int main_base, int n_agg, hipStream_t stream) {
   if (p.z)
-    return launch_one<N, NG, BF16, VEC, true>(p, s, n_main, main_base, n_agg, stream);
-  return launch_one<N, NG, BF16, VEC, false>(p, s, n_main, main_base, n_agg, stream);
+    return launch_one<N, NG, BF16, VEC, true, CONV>(p, s, n_main, main_base, n_agg, stream);
+  return launch_one<N, NG, BF16, VEC, false, CONV>(p, s, n_main, main_base, n_agg, stream);
 }
 
-template <int N, bool BF16, bool VEC>
+template <int N, bool BF16, bool VEC, bool CONV>
 hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
   constexpr int NG = kWaves<N>;
   ScanShape s;
@@ -451,11 +534,11 @@ hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
     e = hipEventRecord((hipEvent_t)p.ev_fork, stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(side, (hipEvent_t)p.ev_fork, 0);
     if (e != hipSuccess) return e;
-    e = launch_tasks<N, NG, BF16, VEC>(p, s, 0, 0, p.split_groups * (p.segments - 1), side);
+    e = launch_tasks<N, NG, BF16, VEC, CONV>(p, s, 0, 0, p.split_groups * (p.segments - 1), side);
     if (e != hipSuccess) return e;
     e = launch_combine(p, s, N, side);
     if (e != hipSuccess) return e;
-    e = launch_tasks<N, NG, BF16, VEC>(p, s, p.split_groups * p.segments,
+    e = launch_tasks<N, NG, BF16, VEC, CONV>(p, s, p.split_groups * p.segments,
                                        p.whole_groups, 0, side);
     if (e != hipSuccess) return e;
     e = hipEventRecord((hipEvent_t)p.ev_join, side);
@@ -464,7 +547,7 @@ hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
       e = hipEventRecord((hipEvent_t)p.ev_start, stream);
       if (e != hipSuccess) return e;
     }
-    e = launch_tasks<N, NG, BF16, VEC>(p, s, p.whole_groups, 0, 0, stream);
+    e = launch_tasks<N, NG, BF16, VEC, CONV>(p, s, p.whole_groups, 0, 0, stream);
     if (e == hipSuccess && p.ev_stop) e = hipEventRecord((hipEvent_t)p.ev_stop, stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(stream, (hipEvent_t)p.ev_join, 0);
     return e;
@@ -477,27 +560,34 @@ hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
     // one stream: whole groups' main pass + split groups' aggregate pass in
     // one launch, then the segment initial states, then the split groups'
     // main pass
-    e = launch_tasks<N, NG, BF16, VEC>(p, s, p.whole_groups, 0,
+    e = launch_tasks<N, NG, BF16, VEC, CONV>(p, s, p.whole_groups, 0,
                                        p.split_groups * (p.segments - 1), stream);
     if (e == hipSuccess) e = launch_combine(p, s, N, stream);
     if (e == hipSuccess)
-      e = launch_tasks<N, NG, BF16, VEC>(p, s, p.split_groups * p.segments,
+      e = launch_tasks<N, NG, BF16, VEC, CONV>(p, s, p.split_groups * p.segments,
                                          p.whole_groups, 0, stream);
   } else {
-    e = launch_tasks<N, NG, BF16, VEC>(p, s, p.whole_groups, 0, 0, stream);
+    e = launch_tasks<N, NG, BF16, VEC, CONV>(p, s, p.whole_groups, 0, 0, stream);
   }
   if (e == hipSuccess && p.ev_stop) e = hipEventRecord((hipEvent_t)p.ev_stop, stream);
   return e;
 }
 
-template <int N>
+template <int N, bool CONV>
 hipError_t launch_dtype(const ScanParams& p, bool bf16, bool vec,
                         hipStream_t stream) {
   if (bf16)
-    return vec ? launch_n<N, true, true>(p, stream)
-               : launch_n<N, true, false>(p, stream);
-  return vec ? launch_n<N, false, true>(p, stream)
-             : launch_n<N, false, false>(p, stream);
+    return vec ? launch_n<N, true, true, CONV>(p, stream)
+               : launch_n<N, true, false, CONV>(p, stream);
+  return vec ? launch_n<N, false, true, CONV>(p, stream)
+             : launch_n<N, false, false, CONV>(p, stream);
+}
+
+template <int N>
+hipError_t launch_conv(const ScanParams& p, bool bf16, bool vec,
+                       hipStream_t stream) {
+  return p.conv_w ? launch_dtype<N, true>(p, bf16, vec, stream)
+                  : launch_dtype<N, false>(p, bf16, vec, stream);
 }
 
 }  // namespace
@@ -533,11 +623,11 @@ int scan_waves_per_group(int N) {
 hipError_t launch_scan(const ScanParams& p, int N, bool bf16, bool vec,
                        hipStream_t stream) {
   switch (N) {
-    case 1: return launch_dtype<1>(p, bf16, vec, stream);
-    case 2: return launch_dtype<2>(p, bf16, vec, stream);
-    case 4: return launch_dtype<4>(p, bf16, vec, stream);
-    case 8: return launch_dtype<8>(p, bf16, vec, stream);
-    case 16: return launch_dtype<16>(p, bf16, vec, stream);
+    case 1: return launch_conv<1>(p, bf16, vec, stream);
+    case 2: return launch_conv<2>(p, bf16, vec, stream);
+    case 4: return launch_conv<4>(p, bf16, vec, stream);
+    case 8: return launch_conv<8>(p, bf16, vec, stream);
+    case 16: return launch_conv<16>(p, bf16, vec, stream);
     default: return hipErrorInvalidValue;
   }
 }

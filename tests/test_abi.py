@@ -136,6 +136,44 @@ def test_bwd_validation_codes(L):
     assert _bwd(L, _dims(), ddelta=p[11] + 2) == -5         # ddelta over du
 
 
+def test_conv_validation_codes(L):
+    p = _ptrs(5)
+
+    def conv(dims, width=4, **o):
+        q = dict(zip(["x", "w", "b", "init", "out"], p))
+        q.update(o)
+        return L.mssm_causal_conv1d_fwd(q["x"], q["w"], q["b"], q["init"], width, 1,
+                                        q["out"], ctypes.byref(dims), None)
+    assert conv(_dims(), width=5) == -3
+    assert conv(_dims(), width=1) == -3
+    assert conv(_dims(), x=None) == -1
+    assert conv(_dims(), w=None) == -1
+    assert conv(_dims(flags=1)) == -3
+    assert conv(_dims(ts=1)) == -2
+    assert conv(_dims(L_=0)) == -2
+    assert conv(_dims(io=1), x=BASE + 1) == -4
+    assert conv(_dims(), out=p[0] + 2) == -5              # out over x
+    assert conv(_dims(), out=p[3]) == -5                  # out over init
+    q = _ptrs(17)
+
+    def fconv(dims, **o):
+        names = ["x", "w", "b", "init", "delta", "A", "B", "C", "D", "z", "bias",
+                 "out", "last", "uo"]
+        a = dict(zip(names, q))
+        a.update(o)
+        return L.mssm_selective_scan_fwd_conv(
+            a["x"], a["w"], a["b"], a["init"], a["delta"], a["A"], a["B"], a["C"],
+            a["D"], a["z"], a["bias"], 1, a["out"], a["last"], a["uo"],
+            ctypes.byref(dims), None)
+    assert fconv(_dims(), w=None) == -1
+    assert fconv(_dims(), x=None) == -1
+    assert fconv(_dims(N=3)) == -3
+    assert fconv(_dims(), uo=q[11]) == -5                 # u_out over out
+    assert fconv(_dims(), uo=q[0] + 64) == -5             # u_out over x
+    assert fconv(_dims(), out=q[3]) == -5                 # out over conv init
+    assert fconv(_dims(io=1), init=BASE + 3 * (1 << 34) + 1) == -4
+
+
 def test_update_validation_codes(L):
     from selective_state_space_52_amd._lib import Dims
     p = _ptrs(11)

@@ -25,7 +25,10 @@ Value recipe (all workloads):
 Draw order from numpy.random.default_rng(seed): u, delta, z, B, C, D, log-dt,
 then (decode only) the state.  The backward's incoming gradients use
 default_rng([seed, 104729]): dout ~ N(0, 1) in the io dtype, then dlast ~
-N(0, 1) fp32.  Decode tokens use default_rng([seed, 1 + k]) for
+N(0, 1) fp32.  The causal conv ahead of the scan (width 4) draws from
+default_rng([seed, 7717]): weight, bias ~ U(-1/2, 1/2) fp32 (a framework's
+default Conv1d range 1/sqrt(width)), then the initial inputs ~ N(0, 1) in the
+io dtype; the conv input x is the workload's u.  Decode tokens use default_rng([seed, 1 + k]) for
 token k of a ring of ``tokens`` distinct tokens; step s uses token s % tokens.
 bf16 values are fp32 draws rounded to nearest-even (torch's conversion).
 """
@@ -157,6 +160,24 @@ def make_scan_grads(s: ScanSpec, seed_offset: int = 104729) -> dict:
     dlast = torch.from_numpy(
         rng.standard_normal((s.batch, s.dim, s.dstate), dtype=np.float32))
     return dict(dout=dout, dlast=dlast)
+
+
+def make_conv_params(s: ScanSpec, width: int = 4, seed_offset: int = 7717) -> dict:
+    """fp32 weight (dim, width) and bias (dim) ~ U(-1/2, 1/2), and io-dtype
+    init (batch, dim, width - 1) ~ N(0, 1), for the causal conv."""
+    rng = np.random.default_rng([s.seed, seed_offset])
+    w = rng.uniform(-0.5, 0.5, size=(s.dim, width)).astype(np.float32)
+    b = rng.uniform(-0.5, 0.5, size=s.dim).astype(np.float32)
+    init = _round_io(rng.standard_normal((s.batch, s.dim, width - 1),
+                                         dtype=np.float32), s.io)
+    return dict(weight=torch.from_numpy(w), bias=torch.from_numpy(b), init=init)
+
+
+def conv_bytes(s: ScanSpec, width: int = 4) -> int:
+    """Algorithmic HBM bytes of the standalone conv: x read and the output
+    written once, plus the weights."""
+    io = 4 if s.io == "f32" else 2
+    return 2 * s.elements * io + 4 * s.dim * (width + 1)
 
 
 def scan_bwd_bytes(s: ScanSpec, has_h0: bool = False, has_dlast: bool = False,
