@@ -119,9 +119,10 @@ def kernel_source_hash() -> str:
 
 
 def load_traffic(workload: str, plan: dict):
-    """HBM bytes per main-kernel launch from the committed counter summary,
-    or None when it is missing or was taken on another version of the
-    kernel source."""
+    """HBM bytes per forward call (all its kernels; the timed main kernel's
+    window holds all of them but the B/C pack) from the committed counter
+    summary, or None when it is missing or was taken on another version of
+    the kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
@@ -132,7 +133,7 @@ def load_traffic(workload: str, plan: dict):
         return None
     if rec.get("segments") != plan["segments"]:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes_per_call")
 
 
 def main():
@@ -179,21 +180,26 @@ def main():
         step(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    hev = HipEvents()
-    pairs = [(hev.create(), hev.create()) for _ in range(args.steps)]
+    # pass 1: the K timed steps as a caller runs them (no timing hook)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
-        m.set_scan_timing_events(*pairs[i])     # main scan kernel of this step
         step(i)
     ev1.record(stream)
     torch.cuda.synchronize()
-    m.set_scan_timing_events(None, None)
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
+    # pass 2: the same steps with HIP events around the main scan kernel
+    hev = HipEvents()
+    pairs = [(hev.create(), hev.create()) for _ in range(args.steps)]
+    for i in range(args.steps):
+        m.set_scan_timing_events(*pairs[i])     # main scan kernel of this step
+        step(i)
+    torch.cuda.synchronize()
+    m.set_scan_timing_events(None, None)
     main_ms = sum(hev.elapsed_ms(a, b) for a, b in pairs) / args.steps
     for a, b in pairs:
         hev.destroy(a)
@@ -455,41 +461,54 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
 
 
-def _counter_mean(d, kernel_substr, counter):
-    """Mean per-dispatch value of a counter (summed over its instances) for
-    the kernels whose name contains kernel_substr."""
+def _counter_sum(d, kernel_substr, counter):
+    """(sum over dispatches, number of dispatches) of a counter (summed over
+    its instances) for the kernels whose name contains kernel_substr."""
     import sqlite3
-    vals = []
+    total, n = 0.0, 0
     for db in glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True):
         c = sqlite3.connect(db)
-        vals += [v for (v,) in c.execute(
-            "select sum(counter_value) from pmc_events where counter_name = ? and "
-            "name like ? group by dispatch_id", (counter, "%" + kernel_substr + "%"))]
-    if not vals:
+        for (v,) in c.execute(
+                "select sum(counter_value) from pmc_events where counter_name = ? and "
+                "name like ? group by dispatch_id", (counter, "%" + kernel_substr + "%")):
+            total += v
+            n += 1
+    if not n:
         raise RuntimeError("no %s samples for %s in %s" % (counter, kernel_substr, d))
-    return sum(vals) / len(vals)
+    return total, n
+
+
+def _counter_mean(d, kernel_substr, counter):
+    total, n = _counter_sum(d, kernel_substr, counter)
+    return total / n
+
+
+# the kernels of one forward call (one B/C pack per call)
+FWD_KERNELS = ("bc_pack_kernel", "scan_kernel<", "combine_kernel")
 
 
 def traffic_record(workload, time_segments, fetch_dir, write_dir, cfetch_dir, cwrite_dir):
-    """HBM bytes per launch of the main scan kernel from FETCH_SIZE and
+    """HBM bytes per forward call (all its kernels: the B/C pack, the scan
+    launches on both streams and the segment combine) from FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
     for torch's copy of a 1 GiB buffer (1 GiB fetched, 1 GiB written)."""
     import workloads as W
     copy_kib = float(1 << 20)
     f_factor = copy_kib / _counter_mean(cfetch_dir, "copyBuffer", "FETCH_SIZE")
     w_factor = copy_kib / _counter_mean(cwrite_dir, "copyBuffer", "WRITE_SIZE")
-    main = "scan_kernel<16, 8, true, true, true, false"   # bf16, vector path, gate, main pass
-    fk = _counter_mean(fetch_dir, main, "FETCH_SIZE")
-    wk = _counter_mean(write_dir, main, "WRITE_SIZE")
+    _, calls = _counter_sum(fetch_dir, "bc_pack_kernel", "FETCH_SIZE")
+    fk = sum(_counter_sum(fetch_dir, k, "FETCH_SIZE")[0] for k in FWD_KERNELS) / calls
+    wk = sum(_counter_sum(write_dir, k, "WRITE_SIZE")[0] for k in FWD_KERNELS) / calls
     s = W.spec(workload)
     import selective_state_space_52_amd as m
     plan = m.scan_plan(s.batch, s.dim, s.dstate, s.seqlen, time_segments=time_segments)
     rec = {workload: {
         "kernel_source_sha256_16": kernel_source_hash(),
         "segments": plan["segments"],
-        "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+        "calls": calls,
+        "fetch_kib_per_call": round(fk, 1), "write_kib_per_call": round(wk, 1),
         "copy_fetch_factor": round(f_factor, 5), "copy_write_factor": round(w_factor, 5),
-        "hbm_bytes_per_launch": int(round((fk * f_factor + wk * w_factor) * 1024)),
+        "hbm_bytes_per_call": int(round((fk * f_factor + wk * w_factor) * 1024)),
         "algorithmic_bytes": W.scan_bytes(s)}}
     print(json.dumps(rec, indent=1))
 
@@ -508,13 +527,15 @@ def rocprof_summary(d):
         c = sqlite3.connect(db)
         print("# %s" % os.path.relpath(db, d))
         try:
-            rows = c.execute("select name, count(*), avg(duration), min(duration), "
-                             "max(duration) from kernels group by name "
+            rows = c.execute("select name, stream_id, grid_x / workgroup_x, count(*), "
+                             "avg(duration), min(duration), max(duration) from kernels "
+                             "group by name, stream_id, grid_x / workgroup_x "
                              "order by sum(duration) desc").fetchall()
-            print("%-70s %6s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us"))
-            for name, n, avg, mn, mx in rows:
-                print("%-70s %6d %12.2f %12.2f %12.2f" % (_kname(name)[:70], n,
-                                                          avg / 1e3, mn / 1e3, mx / 1e3))
+            print("%-62s %6s %6s %6s %10s %10s %10s" % ("kernel", "stream", "wgs", "calls",
+                                                       "avg_us", "min_us", "max_us"))
+            for name, st, wgs, n, avg, mn, mx in rows:
+                print("%-62s %6s %6d %6d %10.2f %10.2f %10.2f" % (
+                    _kname(name)[:62], st, wgs, n, avg / 1e3, mn / 1e3, mx / 1e3))
         except sqlite3.Error:
             pass
         try:
