@@ -33,7 +33,11 @@ CUS, SIMDS, LANES, CLOCK_GHZ = 256, 4, 16, 2.4
 # fp32 VALU issue: one wave64 instruction per SIMD per 4 clocks = 16 lanes/clk
 VALU_PEAK_TSLOTS = CUS * SIMDS * LANES * CLOCK_GHZ / 1e3   # 39.32 T lane-slots/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_main_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "selective_state_space_52_amd", "csrc", "scan_fwd.hip")
+# the sources the forward scan kernel is built from (the traffic record is
+# tied to them)
+KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_52_amd", "csrc", f)
+                  for f in ("scan_fwd_impl.h", "scan_fwd.hip", "scan_fwd_n16.hip",
+                            "scan_common.h", "dev_math.h")]
 
 # Algorithmic VALU issue slots of the scan (fp32, one lane = one slot; a
 # transcendental occupies two slots because v_exp/v_log/v_rcp issue at half
@@ -114,8 +118,11 @@ class HipEvents:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload: str, plan: dict):

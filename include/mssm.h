@@ -66,8 +66,8 @@ enum {
   MSSM_OK = 0,
   MSSM_ERR_NULL = -1,        /* a required pointer (or dims) is NULL        */
   MSSM_ERR_DIMS = -2,        /* a size <= 0, decode seqlen != 1, overflow   */
-  MSSM_ERR_UNSUPPORTED = -3, /* dstate not in {1,2,4,8,16}, unknown dtype,  */
-                             /* unknown flag                                 */
+  MSSM_ERR_UNSUPPORTED = -3, /* dstate not in {1,2,4,...,128} (backward: up  */
+                             /* to 32), unknown dtype, unknown flag          */
   MSSM_ERR_ALIGN = -4,       /* pointer not aligned to its element size     */
   MSSM_ERR_ALIAS = -5,       /* an output overlaps another argument         */
   MSSM_ERR_HIP = -6          /* a HIP runtime call or launch failed         */
@@ -79,7 +79,7 @@ enum {
 typedef struct {
   int64_t batch;       /* >= 1                                              */
   int64_t dim;         /* channels (D_inner), >= 1                          */
-  int64_t dstate;      /* N, one of 1, 2, 4, 8, 16                          */
+  int64_t dstate;      /* N, a power of two from 1 to 128 (backward: <= 32) */
   int64_t seqlen;      /* L >= 1 for the scan; must be 1 for state_update  */
   int32_t io_dtype;    /* mssm_dtype of u/delta/z/B/C/out (x/dt/z/B/C/out) */
   uint32_t flags;      /* MSSM_FLAG_*                                       */
@@ -176,7 +176,8 @@ int mssm_selective_scan_fwd_conv(const void* x, const float* conv_weight,
  *                 and time; written even when D / delta_bias are NULL (the
  *                 gradient at zero)
  *   dh0         : (batch, dim, dstate) fp32 gradient of h0, or NULL
- * No output may overlap an input or another output.  flags must be 0.
+ * dstate is at most 32 here.  No output may overlap an input or another
+ * output.  flags must be 0.
  * time_segments: 0 lets the library cut rows into time segments that run in
  * parallel (joined by a carried state and a carried gradient); k >= 1 asks
  * for about k segments (whole 16-step tiles each).  Results agree up to

@@ -45,6 +45,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+/* largest state size the oracle's per-row arrays hold */
+#define MSSM_ORACLE_MAX_N 256
+
 /* tau_Delta = softplus, evaluated without a large-x threshold.  For x > 0
  * the form x + log1p(e^-x) avoids overflow; for x <= 0 log1p(e^x) keeps
  * relative accuracy when e^x is tiny. */
@@ -79,7 +82,7 @@ void mssm_oracle_scan_row(int64_t seqlen, int64_t dstate,
                           const double *h0, double *out,
                           double *last_state)
 {
-    double h[64];
+    double h[MSSM_ORACLE_MAX_N];
     int64_t n, t;
     for (n = 0; n < dstate; ++n)
         h[n] = h0 ? h0[n] : 0.0;
@@ -107,7 +110,7 @@ void mssm_oracle_scan_row(int64_t seqlen, int64_t dstate,
  * Whole scan.  D, z, delta_bias and h0 may be NULL (zero skip, no gate, zero
  * bias, zero initial state).  last_state may be NULL.  Rows are independent,
  * so they are spread over nthreads OpenMP threads (nthreads <= 0: default).
- * Returns 0, or -1 if dstate is outside 1..64.
+ * Returns 0, or -1 if dstate is outside 1..MSSM_ORACLE_MAX_N.
  */
 int mssm_oracle_scan(int64_t batch, int64_t dim, int64_t dstate,
                      int64_t seqlen, const double *u, const double *delta,
@@ -119,7 +122,7 @@ int mssm_oracle_scan(int64_t batch, int64_t dim, int64_t dstate,
 {
     int64_t rows = batch * dim;
     int64_t r;
-    if (dstate < 1 || dstate > 64)
+    if (dstate < 1 || dstate > MSSM_ORACLE_MAX_N)
         return -1;
     if (nthreads <= 0)
         nthreads = 1;
@@ -157,7 +160,7 @@ int mssm_oracle_state_update(int64_t batch, int64_t dim, int64_t dstate,
 {
     int64_t rows = batch * dim;
     int64_t r;
-    if (dstate < 1 || dstate > 64)
+    if (dstate < 1 || dstate > MSSM_ORACLE_MAX_N)
         return -1;
     if (nthreads <= 0)
         nthreads = 1;
@@ -211,7 +214,7 @@ void mssm_oracle_scan_bwd_row(int64_t seqlen, int64_t dstate,
     double *DT = E + seqlen * dstate;         /* Delta_t */
     double *X = DT + seqlen;                  /* delta_t + bias */
     double *Y = X + seqlen;                   /* y_t before the gate */
-    double g[64];
+    double g[MSSM_ORACLE_MAX_N];
     int64_t n, t;
 
     /* forward again, keeping every state */
@@ -288,7 +291,7 @@ int mssm_oracle_scan_bwd(int64_t batch, int64_t dim, int64_t dstate,
 {
     int64_t r, i;
     double *scratch;
-    if (dstate < 1 || dstate > 64)
+    if (dstate < 1 || dstate > MSSM_ORACLE_MAX_N)
         return -1;
     scratch = (double *)malloc(sizeof(double) * (size_t)(2 * seqlen * dstate + 3 * seqlen));
     if (!scratch)

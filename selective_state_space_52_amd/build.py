@@ -19,8 +19,9 @@ LIB = os.path.join(HERE, "libmssm.so")
 OBJDIR = os.path.join(HERE, "_build")
 
 ARCH = "gfx950"
-SOURCES = ["scan_fwd.hip", "scan_bwd.hip", "state_update.hip", "conv1d.hip",
-           "mssm_api.cpp"]
+SOURCES = ["scan_fwd.hip", "scan_fwd_n1_8.hip", "scan_fwd_n16.hip",
+           "scan_fwd_n32.hip", "scan_fwd_n64.hip", "scan_fwd_n128.hip",
+           "scan_bwd.hip", "state_update.hip", "conv1d.hip", "mssm_api.cpp"]
 
 # Packed fp32 VALU forms are switched off for every device compilation.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -49,7 +50,7 @@ def build(force: bool = True) -> str:
     if not force and os.path.exists(LIB):
         return LIB
     os.makedirs(OBJDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs

@@ -60,7 +60,8 @@ SideStream* side_stream_of(int dev) {
 }
 
 bool valid_dstate(int64_t n) {
-  return n == 1 || n == 2 || n == 4 || n == 8 || n == 16;
+  return n == 1 || n == 2 || n == 4 || n == 8 || n == 16 || n == 32 || n == 64 ||
+         n == 128;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -418,6 +419,7 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
                             const mssm_dims* dims, void* stream) {
   int rc = check_common_dims(dims);
   if (rc != MSSM_OK) return rc;
+  if (dims->dstate > 32) return MSSM_ERR_UNSUPPORTED;
   if (dims->flags != 0) return MSSM_ERR_UNSUPPORTED;
   if (dims->time_segments < 0) return MSSM_ERR_DIMS;
   if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA ||

@@ -155,6 +155,15 @@ int64_t scan_bc_workspace_bytes(int64_t batch, int64_t L, int N, bool bf16);
 
 hipError_t launch_scan(const ScanParams& p, int N, bool bf16, bool vec,
                        hipStream_t stream);
+// the forward scan per state size (one translation unit per group of sizes)
+hipError_t launch_scan_n1(const ScanParams&, bool, bool, hipStream_t);
+hipError_t launch_scan_n2(const ScanParams&, bool, bool, hipStream_t);
+hipError_t launch_scan_n4(const ScanParams&, bool, bool, hipStream_t);
+hipError_t launch_scan_n8(const ScanParams&, bool, bool, hipStream_t);
+hipError_t launch_scan_n16(const ScanParams&, bool, bool, hipStream_t);
+hipError_t launch_scan_n32(const ScanParams&, bool, bool, hipStream_t);
+hipError_t launch_scan_n64(const ScanParams&, bool, bool, hipStream_t);
+hipError_t launch_scan_n128(const ScanParams&, bool, bool, hipStream_t);
 // Backward: timesteps per tile, waves per group, segments, workspace, launch.
 int bwd_tile();
 int bwd_waves_per_group(int N);

@@ -772,6 +772,7 @@ hipError_t launch_scan_bwd(const BwdParams& p, int N, bool bf16, bool vec,
     case 4: return launch_dtype<4>(p, bf16, vec, st);
     case 8: return launch_dtype<8>(p, bf16, vec, st);
     case 16: return launch_dtype<16>(p, bf16, vec, st);
+    case 32: return launch_dtype<32>(p, bf16, vec, st);
     default: return hipErrorInvalidValue;
   }
 }

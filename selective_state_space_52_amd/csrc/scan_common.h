@@ -32,7 +32,7 @@ __device__ __forceinline__ void raw_zero(Raw<BF16, KC>& r) {
 
 // Values [t, t + KC) of a row starting at element offset `off`; `nvalid` of
 // them exist (the rest read as 0).  VEC: the row and every 16-byte piece
-// (8-byte when a chunk is only 4 bf16 values) are aligned, and a piece is
+// (the whole chunk when it is 8 or 4 bytes) are aligned, and a piece is
 // either whole or absent.
 template <bool BF16, bool VEC, int KC>
 __device__ __forceinline__ void load_chunk(Raw<BF16, KC>& r, const void* base,
@@ -52,14 +52,16 @@ __device__ __forceinline__ void load_chunk(Raw<BF16, KC>& r, const void* base,
           r.w[4 * q] = r.w[4 * q + 1] = r.w[4 * q + 2] = r.w[4 * q + 3] = 0u;
         }
       }
-    } else {
-      static_assert(W == 2, "chunk of 4 bf16 values");
+    } else if constexpr (W == 2) {
       if (nvalid > 0) {
         const uint2 v = *reinterpret_cast<const uint2*>(src);
         r.w[0] = v.x; r.w[1] = v.y;
       } else {
         r.w[0] = r.w[1] = 0u;
       }
+    } else {
+      static_assert(W == 1, "chunk of 1 word");
+      r.w[0] = nvalid > 0 ? src[0] : 0u;
     }
   } else {
     if constexpr (BF16) {
@@ -94,8 +96,10 @@ __device__ __forceinline__ void store_chunk(void* base, int64_t off,
       for (int q = 0; q < W / 4; ++q)
         reinterpret_cast<uint4*>(dst)[q] =
             make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
-    } else {
+    } else if constexpr (W == 2) {
       *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    } else {
+      dst[0] = w[0];
     }
   } else if constexpr (BF16) {
     uint16_t* dst = static_cast<uint16_t*>(base) + off;
@@ -119,7 +123,9 @@ __device__ __forceinline__ void store_chunk(void* base, int64_t off,
 template <int NPW, bool BF16>
 struct BCLayout {
   static constexpr int kWordsPerStep = BF16 ? NPW : 2 * NPW;  // 32-bit words
-  static constexpr int kSteps = 16 / kWordsPerStep;           // per 64 B batch
+  // tokens per batch: a 64-byte batch, or one token when a token is larger
+  static constexpr int kSteps = kWordsPerStep >= 16 ? 1 : 16 / kWordsPerStep;
+  static constexpr int kWordsPerBatch = kSteps * kWordsPerStep;
 };
 
 // words of one wave's run, padded to whole 64-byte batches
@@ -129,7 +135,7 @@ __host__ __device__ inline int64_t bc_run_words(int64_t L, int words_per_step) {
 
 template <int NPW, bool BF16>
 struct alignas(16) BCBatch {
-  uint32_t w[16];
+  uint32_t w[BCLayout<NPW, BF16>::kWordsPerBatch];
 };
 
 // value j (B for j < NPW, C after) of token i of a batch (or a raw run)

@@ -9,9 +9,9 @@
 //   out    = (sum_n C[b,n] h[n] + D[d] x) * silu(z)
 //
 // The step is bound by HBM: the fp32 state (64 B per row at N = 16) is read
-// and written once and dominates the bytes.  One lane owns one row; the lanes
-// of a wave own consecutive rows, so the state is streamed with 16-byte
-// accesses that together cover contiguous memory.
+// and written once and dominates the bytes.  One lane owns one row (N / 16
+// lanes above N = 16); the lanes of a wave own consecutive rows, so the state
+// is streamed with 16-byte accesses that together cover contiguous memory.
 #include "dev_math.h"
 #include "mssm_internal.h"
 
@@ -31,6 +31,12 @@ __device__ __forceinline__ float load_io(const void* base, int64_t i) {
     return static_cast<const float*>(base)[i];
 }
 
+// Lanes per row: one up to N = 16; above, N / 16 lanes each own 16 states of
+// the row (consecutive lanes, consecutive 64-byte pieces of the state), and
+// their partial readouts are summed across those lanes.
+template <int N>
+constexpr int kLanesPerRow = N > 16 ? N / 16 : 1;
+
 template <int N, bool BF16, bool VEC, bool HAS_Z>
 __global__ void __launch_bounds__(256)
     state_update_kernel(float* __restrict__ state, const void* __restrict__ x,
@@ -42,64 +48,80 @@ __global__ void __launch_bounds__(256)
                         const float* __restrict__ Dv,
                         const float* __restrict__ bias,
                         void* __restrict__ out, const UpdateShape s) {
-  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= s.batch * s.dim) return;
+  constexpr int LPR = kLanesPerRow<N>;
+  constexpr int NPL = N / LPR;  // states per lane
+  const int64_t rows = s.batch * s.dim;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t r_raw = tid / LPR;
+  const int part = (int)(tid % LPR);
+  // every lane of a row group takes part in the cross-lane sum, so lanes
+  // past the last row compute on the last row and store nothing
+  const bool active = r_raw < rows;
+  if (LPR == 1 && !active) return;
+  const int64_t r = active ? r_raw : rows - 1;
   const int64_t b = r / s.dim;
   const int64_t d = r - b * s.dim;
+  const int n0 = part * NPL;
 
   const float xv = load_io<BF16>(x, r);
   const float xr = load_io<BF16>(dt, r) + (bias ? bias[d] : 0.0f);
   const float dl = s.softplus ? softplus_f32(xr) : xr;
   const float w = dl * xv;
 
-  float h[N], a[N];
-  if constexpr (VEC && N % 4 == 0) {
-    const float4* sp = reinterpret_cast<const float4*>(state + r * N);
-    const float4* ap = reinterpret_cast<const float4*>(A + d * N);
+  float h[NPL], a[NPL];
+  float* __restrict__ sp = state + r * N + n0;
+  const float* __restrict__ ap = A + d * N + n0;
+  if constexpr (VEC && NPL % 4 == 0) {
 #pragma unroll
-    for (int q = 0; q < N / 4; ++q) {
-      const float4 hv = sp[q], av = ap[q];
+    for (int q = 0; q < NPL / 4; ++q) {
+      const float4 hv = reinterpret_cast<const float4*>(sp)[q];
+      const float4 av = reinterpret_cast<const float4*>(ap)[q];
       h[4 * q] = hv.x; h[4 * q + 1] = hv.y; h[4 * q + 2] = hv.z; h[4 * q + 3] = hv.w;
       a[4 * q] = av.x; a[4 * q + 1] = av.y; a[4 * q + 2] = av.z; a[4 * q + 3] = av.w;
     }
   } else {
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-      h[n] = state[r * N + n];
-      a[n] = A[d * N + n];
+    for (int n = 0; n < NPL; ++n) {
+      h[n] = sp[n];
+      a[n] = ap[n];
     }
   }
 
   float y = 0.0f;
 #pragma unroll
-  for (int n = 0; n < N; ++n) {
+  for (int n = 0; n < NPL; ++n) {
     const float e = hw_exp2(dl * (a[n] * kLog2e));
-    h[n] = fmaf(e, h[n], w * load_io<BF16>(Bm, b * N + n));
-    y = fmaf(load_io<BF16>(Cm, b * N + n), h[n], y);
+    h[n] = fmaf(e, h[n], w * load_io<BF16>(Bm, b * N + n0 + n));
+    y = fmaf(load_io<BF16>(Cm, b * N + n0 + n), h[n], y);
   }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off /= 2) y += __shfl_xor(y, off);
   y = fmaf(Dv ? Dv[d] : 0.0f, xv, y);
   if (HAS_Z) y *= silu_f32(load_io<BF16>(z, r));
 
-  if constexpr (VEC && N % 4 == 0) {
-    float4* sp = reinterpret_cast<float4*>(state + r * N);
+  if (!active) return;
+  if constexpr (VEC && NPL % 4 == 0) {
 #pragma unroll
-    for (int q = 0; q < N / 4; ++q)
-      sp[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+    for (int q = 0; q < NPL / 4; ++q)
+      reinterpret_cast<float4*>(sp)[q] =
+          make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
   } else {
 #pragma unroll
-    for (int n = 0; n < N; ++n) state[r * N + n] = h[n];
+    for (int n = 0; n < NPL; ++n) sp[n] = h[n];
   }
-  if constexpr (BF16)
-    static_cast<uint16_t*>(out)[r] = to_bf16(y);
-  else
-    static_cast<float*>(out)[r] = y;
+  if (part == 0) {
+    if constexpr (BF16)
+      static_cast<uint16_t*>(out)[r] = to_bf16(y);
+    else
+      static_cast<float*>(out)[r] = y;
+  }
 }
 
 template <int N, bool BF16, bool VEC>
 hipError_t launch_u(const UpdateParams& p, hipStream_t stream) {
   UpdateShape s{p.batch, p.dim, p.softplus};
-  const int64_t rows = p.batch * p.dim;
-  const dim3 grid((unsigned)((rows + 255) / 256));
+  const int64_t threads = p.batch * p.dim * kLanesPerRow<N>;
+  const dim3 grid((unsigned)((threads + 255) / 256));
   if (p.z)
     hipLaunchKernelGGL((state_update_kernel<N, BF16, VEC, true>), grid,
                        dim3(256), 0, stream, p.state, p.x, p.dt, p.z, p.A,
@@ -131,6 +153,9 @@ hipError_t launch_state_update(const UpdateParams& p, int N, bool bf16,
     case 4: return launch_un<4>(p, bf16, stream);
     case 8: return launch_un<8>(p, bf16, stream);
     case 16: return launch_un<16>(p, bf16, stream);
+    case 32: return launch_un<32>(p, bf16, stream);
+    case 64: return launch_un<64>(p, bf16, stream);
+    case 128: return launch_un<128>(p, bf16, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -233,6 +233,14 @@ def pin_materialised(orc):
                                      h0)
         _close(out, w_out, rtol=1e-11, atol=1e-12, what="materialised out")
         _close(last, w_last, rtol=1e-11, atol=1e-12, what="materialised last")
+    # the larger state sizes (up to 128 states per row)
+    args, h0 = random_case(23, batch=1, dim=2, L=10, N=128)
+    out, last = orc.scan(**args, softplus=True, h0=h0)
+    w_out, w_last = materialised(args["u"], args["delta"], args["A"], args["B"],
+                                 args["C"], args["D"], args["z"],
+                                 args["delta_bias"], True, h0)
+    _close(out, w_out, rtol=1e-11, atol=1e-12, what="materialised out N=128")
+    _close(last, w_last, rtol=1e-11, atol=1e-12, what="materialised last N=128")
 
 
 # -------------------------------------------------------------- invariants

@@ -78,7 +78,8 @@ def test_fwd_validation_codes(L):
         assert _fwd(L, _dims(**bad)) == -2, bad
     assert _fwd(L, _dims(ts=-1)) == -2
     assert _fwd(L, _dims(N=3)) == -3
-    assert _fwd(L, _dims(N=32)) == -3
+    assert _fwd(L, _dims(N=256)) == -3
+    assert _fwd(L, _dims(N=48)) == -3
     assert _fwd(L, _dims(io=7)) == -3
     assert _fwd(L, _dims(flags=2)) == -3
     assert _fwd(L, _dims(reserved=1)) == -3
@@ -126,6 +127,7 @@ def test_bwd_validation_codes(L):
     for bad in (dict(batch=0), dict(dim=-1), dict(L_=0)):
         assert _bwd(L, _dims(**bad)) == -2, bad
     assert _bwd(L, _dims(N=3)) == -3
+    assert _bwd(L, _dims(N=64)) == -3                       # backward up to 32
     assert _bwd(L, _dims(L_=1 << 40)) == -2
     assert _bwd(L, _dims(io=1), dout=BASE + 9 * (1 << 34) + 1) == -4
     assert _bwd(L, _dims(), dB=BASE + 14 * (1 << 34) + 2) == -4

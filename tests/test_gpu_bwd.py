@@ -107,6 +107,8 @@ SHAPES = [
     ("bf16", 2, 96, 8, 200),
     ("f32", 2, 33, 8, 77),
     ("f32", 2, 40, 2, 48),
+    ("bf16", 2, 96, 32, 200),     # N = 32: 8 waves of 4 states
+    ("f32", 1, 40, 32, 77),
 ]
 
 
@@ -156,6 +158,7 @@ SEGMENTS = [
     ("f32", 1, 64, 16, 1000, 7),
     ("bf16", 2, 64, 8, 200, 13),    # one tile per segment
     ("f32", 1, 40, 2, 100, 3),
+    ("bf16", 1, 64, 32, 300, 4),
 ]
 
 

@@ -90,6 +90,7 @@ FUSED = [
     ("bf16", 1, 64, 16, 1000, 3, True),     # segments start inside the row
     ("f32", 2, 40, 8, 264, 2, True),
     ("bf16", 1, 64, 4, 37, 0, True),
+    ("bf16", 1, 64, 64, 300, 2, True),
 ]
 
 

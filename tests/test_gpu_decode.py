@@ -61,7 +61,8 @@ def _run_steps(s, steps, rows=None):
 
 @pytest.mark.parametrize("io,batch,dim,N", [("bf16", 3, 200, 16), ("f32", 2, 70, 16),
                                              ("bf16", 2, 64, 1), ("bf16", 2, 64, 4),
-                                             ("f32", 5, 33, 8)])
+                                             ("f32", 5, 33, 8), ("bf16", 3, 100, 32),
+                                             ("f32", 2, 70, 64), ("bf16", 2, 66, 128)])
 def test_decode_small(io, batch, dim, N):
     s = W.spec("decode", io=io, batch=batch, dim=dim, dstate=N, tokens=5)
     state, ref_state, og, orf = _run_steps(s, steps=12)
@@ -70,10 +71,11 @@ def test_decode_small(io, batch, dim, N):
     check_state(state, ref_state, "decode state")
 
 
-def test_decode_iterated_equals_gpu_scan():
+@pytest.mark.parametrize("N", [16, 64])
+def test_decode_iterated_equals_gpu_scan(N):
     """L decode steps reproduce the forward scan's outputs and final state."""
     import selective_state_space_52_amd as m
-    s = W.spec("mamba130m_layer", batch=2, dim=96, seqlen=40, seed=9)
+    s = W.spec("mamba130m_layer", batch=2, dim=96, dstate=N, seqlen=40, seed=9)
     inp = W.make_scan_inputs(s)
     h0 = W.make_initial_state(s)
     out, last = gpu_scan(inp, h0=h0)

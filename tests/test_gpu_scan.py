@@ -45,6 +45,12 @@ SHAPES = [
     ("bf16", 2, 96, 4, 200),
     ("bf16", 2, 96, 8, 200),
     ("f32", 2, 33, 8, 77),
+    # larger states (Mamba-2 sizes): 8 waves, N / 8 states per wave
+    ("bf16", 2, 96, 32, 300),
+    ("f32", 1, 64, 64, 264),
+    ("bf16", 2, 64, 64, 1000),
+    ("bf16", 1, 70, 128, 200),
+    ("f32", 1, 40, 128, 77),      # fp32 N = 128: a token's B/C run spans 2 batches
 ]
 
 
@@ -87,6 +93,18 @@ def test_forced_time_segments(L, ts):
     out, last = gpu_scan(inp, h0=h0, time_segments=ts)
     ro, rl = oracle_scan(inp, h0=h0.double().numpy())
     _report("segments L=%d ts=%d" % (L, ts), check_out(out, ro, "bf16", "out"))
+    check_state(last, rl, "last_state")
+
+
+@pytest.mark.parametrize("io,N", [("bf16", 64), ("f32", 128)])
+def test_forced_time_segments_large_state(io, N):
+    """The segment carry with 8 states (16) per wave."""
+    s = W.spec("mamba130m_layer", io=io, batch=1, dim=72, dstate=N, seqlen=700, seed=N)
+    inp = W.make_scan_inputs(s)
+    h0 = W.make_initial_state(s)
+    out, last = gpu_scan(inp, h0=h0, time_segments=3)
+    ro, rl = oracle_scan(inp, h0=h0.double().numpy())
+    _report("segments N=%d %s" % (N, io), check_out(out, ro, io, "out"))
     check_state(last, rl, "last_state")
 
 

@@ -25,7 +25,7 @@ def test_threads_do_not_change_results(orc):
 
 
 def test_rejects_unsupported_dstate(orc):
-    args, _ = random_case(82, N=65)
+    args, _ = random_case(82, N=257, L=4)   # beyond the oracle's 256-state rows
     with pytest.raises(ValueError):
         orc.scan(**args)
 
