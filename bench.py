@@ -32,6 +32,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 CUS, SIMDS, LANES, CLOCK_GHZ = 256, 4, 16, 2.4
 # fp32 VALU issue: one wave64 instruction per SIMD per 4 clocks = 16 lanes/clk
 VALU_PEAK_TSLOTS = CUS * SIMDS * LANES * CLOCK_GHZ / 1e3   # 39.32 T lane-slots/s
+# v_exp_f32 issues at half the fma rate (measured on the MI355X: 26.6 vs 54.8
+# lane-ops per CU per clock), so the chip's exp peak is half the VALU peak
+EXP_PEAK_T = VALU_PEAK_TSLOTS / 2                          # 19.66 T exp/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_main_traffic.json")
 # the sources the forward scan kernel is built from (the traffic record is
 # tied to them)
@@ -66,9 +69,11 @@ CONV_SLOTS_PER_ELEM = 11
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mamba2p8b_layer")
+    ap.add_argument("--dstate", type=int, default=0,
+                    help="override the workload's state size (0: keep it)")
     ap.add_argument("--time-segments", type=int, default=0)
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -163,14 +168,16 @@ def main():
     import workloads as W
     import selective_state_space_52_amd as m
 
-    s = W.spec(args.workload)
+    over = {"dstate": args.dstate} if args.dstate else {}
+    s = W.spec(args.workload, **over)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     io = torch.bfloat16 if s.io == "bf16" else torch.float32
     sets = []
     base = W.make_scan_inputs(s)
     for r in range(max(1, args.rotate)):
-        inp = base if r == 0 else W.make_scan_inputs(W.spec(args.workload, seed=s.seed + 1000 * r))
+        inp = base if r == 0 else W.make_scan_inputs(
+            W.spec(args.workload, seed=s.seed + 1000 * r, **over))
         d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
         d["out"] = torch.empty_like(d["u"])
         d["last"] = torch.empty(s.batch, s.dim, s.dstate, device=dev)
@@ -207,7 +214,8 @@ def main():
         step(i)
     torch.cuda.synchronize()
     m.set_scan_timing_events(None, None)
-    main_ms = sum(hev.elapsed_ms(a, b) for a, b in pairs) / args.steps
+    per_step = sorted(hev.elapsed_ms(a, b) for a, b in pairs)
+    main_ms = sum(per_step) / args.steps
     for a, b in pairs:
         hev.destroy(a)
         hev.destroy(b)
@@ -246,10 +254,16 @@ def main():
                      "frac": round(achieved / VALU_PEAK_TSLOTS, 4),
                      "traffic": traffic,
                      "kernel": "scan_kernel (main pass)",
-                     "kernel_ms": round(main_ms, 5)},
+                     "kernel_ms": round(main_ms, 5),
+                     "kernel_ms_median": round(per_step[len(per_step) // 2], 5),
+                     "kernel_ms_min": round(per_step[0], 5)},
+        "exp_rate": {"achieved": round(s.state_elements / (main_ms * 1e-3) / 1e12, 3),
+                     "peak": round(EXP_PEAK_T, 3), "unit": "T exp/s",
+                     "frac": round(s.state_elements / (main_ms * 1e-3) / 1e12 / EXP_PEAK_T, 4)},
         "wall_s": round(wall, 3),
+        "software": software(torch),
     }
-    if not args.no_backward:
+    if not args.no_backward and s.dstate <= 32:   # the backward takes N <= 32
         res["backward"] = bench_backward(torch, W, m, dev, s, sets, hev,
                                          args.backward_steps,
                                          args.bwd_time_segments)
@@ -281,7 +295,7 @@ def bench_conv(torch, W, m, dev, s, sets, hev, scan_ms, steps=20):
     load stage, against running the two one after the other."""
     stream = torch.cuda.current_stream(dev)
     cps = [{k: v.to(dev) for k, v in
-            W.make_conv_params(W.spec(s.name, seed=s.seed + 1000 * r)).items()}
+            W.make_conv_params(W.spec(s.name, seed=s.seed + 1000 * r, dstate=s.dstate)).items()}
            for r in range(len(sets))]
     u_bufs = [torch.empty_like(d["u"]) for d in sets]
 
@@ -356,7 +370,7 @@ def bench_backward(torch, W, m, dev, s, sets, hev, steps, time_segments=0):
     """The backward of the same workload: gradients of every input for a
     seeded dout, rotating over the same input sets.  Reports the whole call
     (B/C pack, main kernel, group and batch sums) and the main kernel alone."""
-    grads = [W.make_scan_grads(W.spec(s.name, seed=s.seed + 1000 * r))["dout"].to(dev)
+    grads = [W.make_scan_grads(W.spec(s.name, seed=s.seed + 1000 * r, dstate=s.dstate))["dout"].to(dev)
              for r in range(len(sets))]
 
     def step(i):
@@ -401,6 +415,23 @@ def bench_backward(torch, W, m, dev, s, sets, hev, steps, time_segments=0):
                          "kernel_ms": round(main_ms, 5)}}
 
 
+def software(torch):
+    """Versions of the stack the numbers come from."""
+    import numpy
+    info = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+            "numpy": numpy.__version__,
+            "device": torch.cuda.get_device_properties(0).name}
+    try:
+        import subprocess
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True,
+                           text=True, timeout=30)
+        clk = [l.strip() for l in r.stdout.splitlines() if "sclk" in l]
+        info["sclk_after_run"] = clk[0] if clk else None
+    except Exception:  # the clock is informative only
+        info["sclk_after_run"] = None
+    return info
+
+
 def bench_decode(torch, W, m, dev, steps):
     """The decode workload: `steps` single-token updates of one in-place fp32
     state (84 MB, fits the 256 MB Infinity Cache, so the rate is an effective
@@ -427,11 +458,31 @@ def bench_decode(torch, W, m, dev, steps):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     nb = W.decode_step_bytes(s)
+    # the same steps over 4 state buffers in turn (336 MB, more than the
+    # 256 MB Infinity Cache holds): the rate from HBM
+    states = [par["state"].to(dev) for _ in range(4)]
+
+    def run_rot(n):
+        for i in range(n):
+            t = toks[i % len(toks)]
+            m.selective_state_update(states[i % 4], t["x"], t["dt"], A, t["B"], t["C"],
+                                     D=D, z=t["z"], dt_bias=bias, out=out)
+    run_rot(8)
+    torch.cuda.synchronize()
+    e0.record()
+    run_rot(steps)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_rot = e0.elapsed_time(e1) / steps
     return {"workload": "decode: %d sequences x D_inner %d, N %d, %d steps, bf16 tokens, "
                         "fp32 state in place" % (s.batch, s.dim, s.dstate, steps),
             "ms_per_step": round(ms, 5), "algorithmic_bytes_per_step": nb,
             "effective_gb_per_s": round(nb / (ms * 1e-3) / 1e9, 1),
-            "pct_hbm_peak": round(100 * nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+            "pct_hbm_peak": round(100 * nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "rotating_4_states": {"ms_per_step": round(ms_rot, 5),
+                                  "hbm_gb_per_s": round(nb / (ms_rot * 1e-3) / 1e9, 1),
+                                  "pct_hbm_peak": round(100 * nb / (ms_rot * 1e-3) / 1e9 /
+                                                        HBM_PEAK_GBS, 2)}}
 
 
 def cpu_baseline(s, inp, seconds, nbytes):

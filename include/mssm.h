@@ -75,6 +75,12 @@ enum {
 
 /* fwd: last_state holds the initial state h0 on entry (in/out). */
 #define MSSM_FLAG_LOAD_STATE 1u
+/* The per-element arrays (u/x, delta, z, out, u_out; dout, du, ddelta, dz)
+ * are (batch, seqlen, dim) -- the block layout (batch, length, dim) of page
+ * "Mamba: Selective State Space Models", "Quick Start" -- instead of
+ * (batch, dim, seqlen).  B and C keep (batch, seqlen, dstate).  Accepted by
+ * the forward scans, the backward and the causal conv. */
+#define MSSM_FLAG_LAYOUT_BLD 2u
 
 typedef struct {
   int64_t batch;       /* >= 1                                              */
@@ -126,7 +132,8 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
  *   init    : (batch, dim, width-1) io dtype, x at t = -(width-1) .. -1
  *             (the last inputs of the previous piece of the sequence), or NULL
  *   width   : 2, 3 or 4
- * dims->dstate is ignored; flags and time_segments must be 0.
+ * dims->dstate is ignored; flags may hold MSSM_FLAG_LAYOUT_BLD (x and out
+ * then are (batch, seqlen, dim)); time_segments must be 0.
  */
 int mssm_causal_conv1d_fwd(const void* x, const float* weight,
                            const float* bias, const void* init, int width,
@@ -177,7 +184,7 @@ int mssm_selective_scan_fwd_conv(const void* x, const float* conv_weight,
  *                 gradient at zero)
  *   dh0         : (batch, dim, dstate) fp32 gradient of h0, or NULL
  * dstate is at most 32 here.  No output may overlap an input or another
- * output.  flags must be 0.
+ * output.  flags may hold MSSM_FLAG_LAYOUT_BLD.
  * time_segments: 0 lets the library cut rows into time segments that run in
  * parallel (joined by a carried state and a carried gradient); k >= 1 asks
  * for about k segments (whole 16-step tiles each).  Results agree up to

@@ -16,8 +16,8 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import (MSSM_BF16, MSSM_F32, MSSM_FLAG_LOAD_STATE, Dims, MssmError,
-                   Plan, check, lib)
+from ._lib import (MSSM_BF16, MSSM_F32, MSSM_FLAG_LAYOUT_BLD, MSSM_FLAG_LOAD_STATE,
+                   Dims, MssmError, Plan, check, lib)
 
 __all__ = ["selective_scan_fwd", "selective_scan_bwd", "selective_scan_fwd_conv",
            "causal_conv1d_fwd", "selective_state_update", "scan_plan",
@@ -55,14 +55,37 @@ def _need(t, name, dtype=None, shape=None, device=None):
         raise ValueError("%s must be contiguous" % name)
 
 
+_LAYOUTS = ("bdl", "bld")
+
+
+def _layout(layout):
+    if layout not in _LAYOUTS:
+        raise ValueError("layout must be 'bdl' (batch, dim, L) or 'bld' (batch, L, dim)")
+    return MSSM_FLAG_LAYOUT_BLD if layout == "bld" else 0
+
+
+def _dims_of(t, layout):
+    """(batch, dim, L) of a per-element tensor in the given layout."""
+    if layout == "bld":
+        batch, L, dim = t.shape
+    else:
+        batch, dim, L = t.shape
+    return batch, dim, L
+
+
+def _eshape(batch, dim, L, layout):
+    return (batch, L, dim) if layout == "bld" else (batch, dim, L)
+
+
 def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
 def scan_plan(batch, dim, dstate, seqlen, io_dtype=torch.bfloat16,
-              time_segments=0) -> dict:
+              time_segments=0, layout="bdl") -> dict:
     """How the library splits a forward scan of this shape (no GPU needed)."""
-    dims = Dims(batch, dim, dstate, seqlen, _IO[io_dtype], 0, time_segments, 0)
+    dims = Dims(batch, dim, dstate, seqlen, _IO[io_dtype], _layout(layout),
+                time_segments, 0)
     plan = Plan()
     check(lib().mssm_selective_scan_fwd_plan(dims, plan))
     return plan.as_dict()
@@ -70,24 +93,27 @@ def scan_plan(batch, dim, dstate, seqlen, io_dtype=torch.bfloat16,
 
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                        softplus=True, last_state=None, load_state=False,
-                       out=None, time_segments=0):
+                       out=None, time_segments=0, layout="bdl"):
     """Forward selective scan.
 
     u, delta, z: (batch, dim, L); B, C: (batch, L, N), all fp32 or all bf16.
     A: (dim, N) fp32; D, delta_bias: (dim,) fp32 or None.
     last_state: (batch, dim, N) fp32 receiving the final state (and holding
     the initial state when load_state=True), or None.
-    Returns out (batch, dim, L) in the io dtype.
+    Returns out (batch, dim, L) in the io dtype.  layout="bld" takes and
+    returns u, delta, z, out as (batch, L, dim).
     """
     if u.dtype not in _IO:
         raise ValueError("u must be float32 or bfloat16")
     io = u.dtype
-    batch, dim, L = u.shape
+    lay = _layout(layout)
+    batch, dim, L = _dims_of(u, layout)
+    es = _eshape(batch, dim, L, layout)
     N = A.shape[-1]
     dev = u.device
-    _need(u, "u", io, (batch, dim, L), dev)
-    _need(delta, "delta", io, (batch, dim, L), dev)
-    _need(z, "z", io, (batch, dim, L), dev)
+    _need(u, "u", io, es, dev)
+    _need(delta, "delta", io, es, dev)
+    _need(z, "z", io, es, dev)
     _need(B, "B", io, (batch, L, N), dev)
     _need(C, "C", io, (batch, L, N), dev)
     _need(A, "A", torch.float32, (dim, N), dev)
@@ -97,10 +123,10 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     if load_state and last_state is None:
         raise ValueError("load_state needs last_state")
     if out is None:
-        out = torch.empty((batch, dim, L), dtype=io, device=dev)
-    _need(out, "out", io, (batch, dim, L), dev)
+        out = torch.empty(es, dtype=io, device=dev)
+    _need(out, "out", io, es, dev)
     dims = Dims(batch, dim, N, L, _IO[io],
-                MSSM_FLAG_LOAD_STATE if load_state else 0, time_segments, 0)
+                (MSSM_FLAG_LOAD_STATE if load_state else 0) | lay, time_segments, 0)
     with torch.cuda.device(dev):
         check(lib().mssm_selective_scan_fwd(
             _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
@@ -109,24 +135,28 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     return out
 
 
-def causal_conv1d_fwd(x, weight, bias=None, init=None, silu=True, out=None):
+def causal_conv1d_fwd(x, weight, bias=None, init=None, silu=True, out=None,
+                      layout="bdl"):
     """Causal depthwise convolution over time: x (batch, dim, L) fp32 or
     bf16, weight (dim, width) fp32 with width 2..4, bias (dim,) fp32 or None,
     init (batch, dim, width-1) in x's dtype (inputs before t = 0) or None.
-    Returns silu(conv) (or conv with silu=False) in x's dtype."""
+    Returns silu(conv) (or conv with silu=False) in x's dtype; layout="bld"
+    takes x and returns out as (batch, L, dim)."""
     if x.dtype not in _IO:
         raise ValueError("x must be float32 or bfloat16")
-    batch, dim, L = x.shape
+    lay = _layout(layout)
+    batch, dim, L = _dims_of(x, layout)
+    es = _eshape(batch, dim, L, layout)
     width = weight.shape[-1]
     dev = x.device
-    _need(x, "x", x.dtype, (batch, dim, L), dev)
+    _need(x, "x", x.dtype, es, dev)
     _need(weight, "weight", torch.float32, (dim, width), dev)
     _need(bias, "bias", torch.float32, (dim,), dev)
     _need(init, "init", x.dtype, (batch, dim, width - 1), dev)
     if out is None:
         out = torch.empty_like(x)
-    _need(out, "out", x.dtype, (batch, dim, L), dev)
-    dims = Dims(batch, dim, 0, L, _IO[x.dtype], 0, 0, 0)
+    _need(out, "out", x.dtype, es, dev)
+    dims = Dims(batch, dim, 0, L, _IO[x.dtype], lay, 0, 0)
     with torch.cuda.device(dev):
         check(lib().mssm_causal_conv1d_fwd(
             _ptr(x), _ptr(weight), _ptr(bias), _ptr(init), int(width),
@@ -137,7 +167,7 @@ def causal_conv1d_fwd(x, weight, bias=None, init=None, silu=True, out=None):
 def selective_scan_fwd_conv(x, conv_weight, delta, A, B, C, conv_bias=None,
                             conv_init=None, D=None, z=None, delta_bias=None,
                             softplus=True, last_state=None, load_state=False,
-                            out=None, u_out=None, time_segments=0):
+                            out=None, u_out=None, time_segments=0, layout="bdl"):
     """The forward scan whose input is u = silu(causal_conv(x)) (width 4),
     formed inside the scan kernel.  x: (batch, dim, L); conv_weight (dim, 4)
     fp32; conv_bias (dim,) fp32 or None; conv_init (batch, dim, 3) or None;
@@ -146,16 +176,18 @@ def selective_scan_fwd_conv(x, conv_weight, delta, A, B, C, conv_bias=None,
     if x.dtype not in _IO:
         raise ValueError("x must be float32 or bfloat16")
     io = x.dtype
-    batch, dim, L = x.shape
+    lay = _layout(layout)
+    batch, dim, L = _dims_of(x, layout)
+    es = _eshape(batch, dim, L, layout)
     N = A.shape[-1]
     dev = x.device
-    _need(x, "x", io, (batch, dim, L), dev)
+    _need(x, "x", io, es, dev)
     _need(conv_weight, "conv_weight", torch.float32, (dim, 4), dev)
     _need(conv_bias, "conv_bias", torch.float32, (dim,), dev)
     _need(conv_init, "conv_init", io, (batch, dim, 3), dev)
-    _need(u_out, "u_out", io, (batch, dim, L), dev)
-    _need(delta, "delta", io, (batch, dim, L), dev)
-    _need(z, "z", io, (batch, dim, L), dev)
+    _need(u_out, "u_out", io, es, dev)
+    _need(delta, "delta", io, es, dev)
+    _need(z, "z", io, es, dev)
     _need(B, "B", io, (batch, L, N), dev)
     _need(C, "C", io, (batch, L, N), dev)
     _need(A, "A", torch.float32, (dim, N), dev)
@@ -165,10 +197,10 @@ def selective_scan_fwd_conv(x, conv_weight, delta, A, B, C, conv_bias=None,
     if load_state and last_state is None:
         raise ValueError("load_state needs last_state")
     if out is None:
-        out = torch.empty((batch, dim, L), dtype=io, device=dev)
-    _need(out, "out", io, (batch, dim, L), dev)
+        out = torch.empty(es, dtype=io, device=dev)
+    _need(out, "out", io, es, dev)
     dims = Dims(batch, dim, N, L, _IO[io],
-                MSSM_FLAG_LOAD_STATE if load_state else 0, time_segments, 0)
+                (MSSM_FLAG_LOAD_STATE if load_state else 0) | lay, time_segments, 0)
     with torch.cuda.device(dev):
         check(lib().mssm_selective_scan_fwd_conv(
             _ptr(x), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_init),
@@ -180,7 +212,7 @@ def selective_scan_fwd_conv(x, conv_weight, delta, A, B, C, conv_bias=None,
 
 def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None,
                        delta_bias=None, softplus=True, h0=None, dlast=None,
-                       want_dh0=False, time_segments=0):
+                       want_dh0=False, time_segments=0, layout="bdl"):
     """Gradients of the forward scan for the loss
     sum(dout * out) + sum(dlast * last_state).
 
@@ -195,13 +227,15 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None,
     if u.dtype not in _IO:
         raise ValueError("u must be float32 or bfloat16")
     io = u.dtype
-    batch, dim, L = u.shape
+    lay = _layout(layout)
+    batch, dim, L = _dims_of(u, layout)
+    es = _eshape(batch, dim, L, layout)
     N = A.shape[-1]
     dev = u.device
-    _need(u, "u", io, (batch, dim, L), dev)
-    _need(delta, "delta", io, (batch, dim, L), dev)
-    _need(z, "z", io, (batch, dim, L), dev)
-    _need(dout, "dout", io, (batch, dim, L), dev)
+    _need(u, "u", io, es, dev)
+    _need(delta, "delta", io, es, dev)
+    _need(z, "z", io, es, dev)
+    _need(dout, "dout", io, es, dev)
     _need(B, "B", io, (batch, L, N), dev)
     _need(C, "C", io, (batch, L, N), dev)
     _need(A, "A", torch.float32, (dim, N), dev)
@@ -210,16 +244,16 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None,
     _need(h0, "h0", torch.float32, (batch, dim, N), dev)
     _need(dlast, "dlast", torch.float32, (batch, dim, N), dev)
     f32 = dict(dtype=torch.float32, device=dev)
-    g = dict(du=torch.empty((batch, dim, L), dtype=io, device=dev),
-             ddelta=torch.empty((batch, dim, L), dtype=io, device=dev),
-             dz=torch.empty((batch, dim, L), dtype=io, device=dev) if z is not None else None,
+    g = dict(du=torch.empty(es, dtype=io, device=dev),
+             ddelta=torch.empty(es, dtype=io, device=dev),
+             dz=torch.empty(es, dtype=io, device=dev) if z is not None else None,
              dA=torch.empty((dim, N), **f32),
              dB=torch.empty((batch, L, N), **f32),
              dC=torch.empty((batch, L, N), **f32),
              dD=torch.empty((dim,), **f32),
              ddelta_bias=torch.empty((dim,), **f32),
              dh0=torch.empty((batch, dim, N), **f32) if want_dh0 else None)
-    dims = Dims(batch, dim, N, L, _IO[io], 0, time_segments, 0)
+    dims = Dims(batch, dim, N, L, _IO[io], lay, time_segments, 0)
     with torch.cuda.device(dev):
         check(lib().mssm_selective_scan_bwd(
             _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),

@@ -10,6 +10,7 @@ LIB_PATH = os.path.join(HERE, "libmssm.so")
 MSSM_F32 = 0
 MSSM_BF16 = 1
 MSSM_FLAG_LOAD_STATE = 1
+MSSM_FLAG_LAYOUT_BLD = 2
 
 STATUS = {
     0: "MSSM_OK", -1: "MSSM_ERR_NULL", -2: "MSSM_ERR_DIMS",

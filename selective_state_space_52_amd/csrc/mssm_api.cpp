@@ -165,7 +165,8 @@ int make_plan(const mssm_dims* dims, int cus, mssm_plan* plan) {
   plan->kernels = split > 0 ? 4 : 2;
   plan->workspace_bytes = ws;
   const int64_t io = dims->io_dtype == MSSM_BF16 ? 2 : 4;
-  plan->vector_path = ((L * io) % 16 == 0 && (L % 8) == 0) ? 1 : 0;
+  plan->vector_path =
+      ((L * io) % 16 == 0 && (L % 8) == 0 && !(dims->flags & MSSM_FLAG_LAYOUT_BLD)) ? 1 : 0;
   return MSSM_OK;
 }
 
@@ -201,6 +202,8 @@ int mssm_selective_scan_fwd_plan(const mssm_dims* dims, mssm_plan* plan) {
   if (!plan) return MSSM_ERR_NULL;
   int rc = check_common_dims(dims);
   if (rc != MSSM_OK) return rc;
+  if (dims->flags & ~(MSSM_FLAG_LOAD_STATE | MSSM_FLAG_LAYOUT_BLD))
+    return MSSM_ERR_UNSUPPORTED;
   if (dims->time_segments < 0) return MSSM_ERR_DIMS;
   return make_plan(dims, g_cu_count > 0 ? g_cu_count : kDefaultCUs, plan);
 }
@@ -219,7 +222,9 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A,
                   void* stream) {
   int rc = check_common_dims(dims);
   if (rc != MSSM_OK) return rc;
-  if (dims->flags & ~MSSM_FLAG_LOAD_STATE) return MSSM_ERR_UNSUPPORTED;
+  if (dims->flags & ~(MSSM_FLAG_LOAD_STATE | MSSM_FLAG_LAYOUT_BLD))
+    return MSSM_ERR_UNSUPPORTED;
+  const bool bld = (dims->flags & MSSM_FLAG_LAYOUT_BLD) != 0;
   if (dims->time_segments < 0) return MSSM_ERR_DIMS;
   const bool load_state = (dims->flags & MSSM_FLAG_LOAD_STATE) != 0;
   if (!u || !delta || !A || !B || !C || !out) return MSSM_ERR_NULL;
@@ -270,7 +275,7 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A,
   rc = make_plan(dims, g_cu_count > 0 ? g_cu_count : kDefaultCUs, &plan);
   if (rc != MSSM_OK) return rc;
 
-  const bool vec = plan.vector_path && aligned(u, 16) && aligned(delta, 16) &&
+  const bool vec = !bld && plan.vector_path && aligned(u, 16) && aligned(delta, 16) &&
                    aligned(out, 16) && aligned(B, 16) && aligned(C, 16) &&
                    (!z || aligned(z, 16)) && (!u_out || aligned(u_out, 16));
 
@@ -292,6 +297,7 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A,
   p.conv_b = conv_b;
   p.conv_init = conv_init;
   p.u_out = u_out;
+  p.layout_bld = bld ? 1 : 0;
 
   hipStream_t st = (hipStream_t)stream;
   int dev = -1;
@@ -372,7 +378,8 @@ int mssm_causal_conv1d_fwd(const void* x, const float* weight,
   if (!dims) return MSSM_ERR_NULL;
   if (dims->io_dtype != MSSM_F32 && dims->io_dtype != MSSM_BF16)
     return MSSM_ERR_UNSUPPORTED;
-  if (dims->flags != 0 || dims->reserved != 0) return MSSM_ERR_UNSUPPORTED;
+  if ((dims->flags & ~MSSM_FLAG_LAYOUT_BLD) != 0 || dims->reserved != 0)
+    return MSSM_ERR_UNSUPPORTED;
   if (dims->time_segments != 0) return MSSM_ERR_DIMS;
   if (dims->batch <= 0 || dims->dim <= 0 || dims->seqlen <= 0) return MSSM_ERR_DIMS;
   if (width < 2 || width > 4) return MSSM_ERR_UNSUPPORTED;
@@ -399,6 +406,7 @@ int mssm_causal_conv1d_fwd(const void* x, const float* weight,
   p.batch = batch; p.dim = dim; p.L = L;
   p.width = width;
   p.silu = silu ? 1 : 0;
+  p.layout_bld = (dims->flags & MSSM_FLAG_LAYOUT_BLD) ? 1 : 0;
   const bool vec = (L % 8) == 0 && ((L * (int64_t)io) % 16) == 0 &&
                    aligned(x, 16) && aligned(out, 16);
   hipError_t e = mssm::launch_causal_conv1d(p, io == 2, vec, (hipStream_t)stream);
@@ -420,7 +428,8 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
   int rc = check_common_dims(dims);
   if (rc != MSSM_OK) return rc;
   if (dims->dstate > 32) return MSSM_ERR_UNSUPPORTED;
-  if (dims->flags != 0) return MSSM_ERR_UNSUPPORTED;
+  if (dims->flags & ~MSSM_FLAG_LAYOUT_BLD) return MSSM_ERR_UNSUPPORTED;
+  const bool bld = (dims->flags & MSSM_FLAG_LAYOUT_BLD) != 0;
   if (dims->time_segments < 0) return MSSM_ERR_DIMS;
   if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA ||
       !dB || !dC)
@@ -469,7 +478,7 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
   }
 
   // --- validation done; HIP calls from here on ---
-  const bool vec = (L % 8) == 0 && ((L * (int64_t)io) % 16) == 0 &&
+  const bool vec = !bld && (L % 8) == 0 && ((L * (int64_t)io) % 16) == 0 &&
                    aligned(u, 16) && aligned(delta, 16) && aligned(dout, 16) &&
                    aligned(du, 16) && aligned(ddelta, 16) &&
                    (!z || aligned(z, 16)) && (!dz || aligned(dz, 16));
@@ -499,6 +508,7 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
   p.tiles = (int32_t)tiles;
   p.segments = segments;
   p.seg_tiles = (int32_t)((tiles + segments - 1) / segments);
+  p.layout_bld = bld ? 1 : 0;
   p.ev_start = g_ev_start;
   p.ev_stop = g_ev_stop;
 

@@ -55,6 +55,7 @@ struct ScanParams {
   const float* conv_b;    // (dim) fp32 or null
   const void* conv_init;  // (batch, dim, 3) io dtype or null
   void* u_out;            // (batch, dim, L) io dtype: conv output, or null
+  int32_t layout_bld;     // u, delta, z, out, u_out are (batch, L, dim)
 };
 
 // Standalone causal depthwise conv: out = act(bias + sum_k w[k] x[t-K+1+k]).
@@ -67,6 +68,7 @@ struct ConvParams {
   int64_t batch, dim, L;
   int32_t width;          // 2, 3 or 4
   int32_t silu;
+  int32_t layout_bld;     // x, out are (batch, L, dim)
 };
 
 struct UpdateParams {
@@ -122,7 +124,7 @@ struct BwdParams {
   int32_t tiles;          // ceil(L / tile); runs and partials hold tiles*tile steps
   int32_t segments;       // time segments per row
   int32_t seg_tiles;      // tiles per segment (the last may have fewer)
-  int32_t reserved;
+  int32_t layout_bld;     // the per-element arrays are (batch, L, dim)
   // workspace (task = group * segments + segment; lane-contiguous rows)
   void* ws_bc;            // B, C packed per wave run, zero-padded to whole tiles
   float* ws_ck;           // [group][tile][n][lane] state at tile start, from a

@@ -70,6 +70,8 @@ constexpr int kBwdWaves = N >= 4 ? N / 4 : 1;
 
 struct BwdShape {
   int64_t dim, L;
+  int64_t ts;  // elements between consecutive timesteps of a row: 1, or dim
+               // for the (batch, length, channel) layout
   int32_t groups_per_batch, tiles;
   int32_t segments, seg_tiles;
   int32_t softplus, batch;
@@ -137,7 +139,7 @@ __device__ __forceinline__ Task task_of(const BwdShape& s, int lane) {
   k.valid = k.d < s.dim;
   k.dc = k.valid ? k.d : s.dim - 1;
   k.row = k.b * s.dim + k.dc;
-  k.rowoff = k.row * s.L;
+  k.rowoff = s.ts == 1 ? k.row * s.L : k.b * s.L * s.dim + k.dc;
   k.tile_begin = k.seg * s.seg_tiles;
   k.tile_end = min(s.tiles, k.tile_begin + s.seg_tiles);
   return k;
@@ -181,10 +183,11 @@ __global__ void __launch_bounds__(kLanes* NG)
   auto load = [&](int tile) {
     const int64_t tc = (int64_t)tile * T + g * KC;
     const int64_t nv = s.L - tc;
-    load_chunk<BF16, VEC, KC>(ru, u, k.rowoff + tc, nv);
-    load_chunk<BF16, VEC, KC>(rd, delta, k.rowoff + tc, nv);
-    if constexpr (HAS_Z) load_chunk<BF16, VEC, KC>(rz, z, k.rowoff + tc, nv);
-    load_chunk<BF16, VEC, KC>(ro, dout, k.rowoff + tc, nv);
+    const int64_t off = k.rowoff + tc * s.ts;
+    load_chunk<BF16, VEC, KC>(ru, u, off, nv, s.ts);
+    load_chunk<BF16, VEC, KC>(rd, delta, off, nv, s.ts);
+    if constexpr (HAS_Z) load_chunk<BF16, VEC, KC>(rz, z, off, nv, s.ts);
+    load_chunk<BF16, VEC, KC>(ro, dout, off, nv, s.ts);
   };
   auto prep = [&](int tile, int buf) {
     const int64_t nv = s.L - ((int64_t)tile * T + g * KC);
@@ -398,10 +401,11 @@ __global__ void __launch_bounds__(kLanes* NG)
   auto load_r = [&](int64_t tile_base) {
     const int64_t tc = tile_base + g * KC;
     const int64_t nv = s.L - tc;
-    load_chunk<BF16, VEC, KC>(nu, u, k.rowoff + tc, nv);
-    load_chunk<BF16, VEC, KC>(nd, delta, k.rowoff + tc, nv);
-    if constexpr (HAS_Z) load_chunk<BF16, VEC, KC>(nz, z, k.rowoff + tc, nv);
-    load_chunk<BF16, VEC, KC>(no, dout, k.rowoff + tc, nv);
+    const int64_t off = k.rowoff + tc * s.ts;
+    load_chunk<BF16, VEC, KC>(nu, u, off, nv, s.ts);
+    load_chunk<BF16, VEC, KC>(nd, delta, off, nv, s.ts);
+    if constexpr (HAS_Z) load_chunk<BF16, VEC, KC>(nz, z, off, nv, s.ts);
+    load_chunk<BF16, VEC, KC>(no, dout, off, nv, s.ts);
   };
   // state at the start of a tile: kept from zero, plus the decayed h_in
   auto checkpoint = [&](int tile, float (&hc)[NPW]) {
@@ -526,9 +530,10 @@ __global__ void __launch_bounds__(kLanes* NG)
         dbacc += q < nv ? ddl : 0.0f;
       }
       if (k.valid) {
-        store_chunk<BF16, VEC, KC>(du, k.rowoff + tc, odu, nv);
-        store_chunk<BF16, VEC, KC>(ddelta, k.rowoff + tc, odd, nv);
-        if constexpr (HAS_Z) store_chunk<BF16, VEC, KC>(dz, k.rowoff + tc, odz, nv);
+        const int64_t off = k.rowoff + tc * s.ts;
+        store_chunk<BF16, VEC, KC>(du, off, odu, nv, s.ts);
+        store_chunk<BF16, VEC, KC>(ddelta, off, odd, nv, s.ts);
+        if constexpr (HAS_Z) store_chunk<BF16, VEC, KC>(dz, off, odz, nv, s.ts);
       }
     }
     if (more) prep_r(tb - T);
@@ -652,6 +657,7 @@ hipError_t launch_n(const BwdParams& p, hipStream_t st) {
   BwdShape s;
   s.dim = p.dim;
   s.L = p.L;
+  s.ts = p.layout_bld ? p.dim : 1;
   s.groups_per_batch = p.groups_per_batch;
   s.tiles = p.tiles;
   s.segments = p.segments;

@@ -33,10 +33,13 @@ __device__ __forceinline__ void raw_zero(Raw<BF16, KC>& r) {
 // Values [t, t + KC) of a row starting at element offset `off`; `nvalid` of
 // them exist (the rest read as 0).  VEC: the row and every 16-byte piece
 // (the whole chunk when it is 8 or 4 bytes) are aligned, and a piece is
-// either whole or absent.
+// either whole or absent.  Without VEC, consecutive timesteps sit `ts`
+// elements apart (1 for rows stored time-fastest, the channel count for the
+// (batch, length, channel) layout).
 template <bool BF16, bool VEC, int KC>
 __device__ __forceinline__ void load_chunk(Raw<BF16, KC>& r, const void* base,
-                                           int64_t off, int64_t nvalid) {
+                                           int64_t off, int64_t nvalid,
+                                           int64_t ts = 1) {
   constexpr int W = Raw<BF16, KC>::W;
   const uint32_t* src = reinterpret_cast<const uint32_t*>(
       static_cast<const char*>(base) + off * (BF16 ? 2 : 4));
@@ -68,13 +71,14 @@ __device__ __forceinline__ void load_chunk(Raw<BF16, KC>& r, const void* base,
       const uint16_t* s = static_cast<const uint16_t*>(base) + off;
 #pragma unroll
       for (int i = 0; i < W; ++i) {
-        const uint32_t lo = (2 * i < nvalid) ? s[2 * i] : 0u;
-        const uint32_t hi = (2 * i + 1 < nvalid) ? s[2 * i + 1] : 0u;
+        const uint32_t lo = (2 * i < nvalid) ? s[2 * i * ts] : 0u;
+        const uint32_t hi = (2 * i + 1 < nvalid) ? s[(2 * i + 1) * ts] : 0u;
         r.w[i] = lo | (hi << 16);
       }
     } else {
+      const uint32_t* s = static_cast<const uint32_t*>(base) + off;
 #pragma unroll
-      for (int i = 0; i < W; ++i) r.w[i] = (i < nvalid) ? src[i] : 0u;
+      for (int i = 0; i < W; ++i) r.w[i] = (i < nvalid) ? s[i * ts] : 0u;
     }
   }
 }
@@ -82,7 +86,7 @@ __device__ __forceinline__ void load_chunk(Raw<BF16, KC>& r, const void* base,
 template <bool BF16, bool VEC, int KC>
 __device__ __forceinline__ void store_chunk(void* base, int64_t off,
                                             const float (&o)[KC],
-                                            int64_t nvalid) {
+                                            int64_t nvalid, int64_t ts = 1) {
   if (VEC && nvalid >= KC) {
     uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<char*>(base) +
                                                 off * (BF16 ? 2 : 4));
@@ -105,12 +109,12 @@ __device__ __forceinline__ void store_chunk(void* base, int64_t off,
     uint16_t* dst = static_cast<uint16_t*>(base) + off;
 #pragma unroll
     for (int k = 0; k < KC; ++k)
-      if (k < nvalid) dst[k] = to_bf16(o[k]);
+      if (k < nvalid) dst[k * ts] = to_bf16(o[k]);
   } else {
     float* dst = static_cast<float*>(base) + off;
 #pragma unroll
     for (int k = 0; k < KC; ++k)
-      if (k < nvalid) dst[k] = o[k];
+      if (k < nvalid) dst[k * ts] = o[k];
   }
 }
 

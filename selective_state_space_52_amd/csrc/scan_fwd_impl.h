@@ -60,6 +60,8 @@ constexpr int kConvK = 4;
 
 struct ScanShape {
   int64_t dim, L;
+  int64_t ts;  // elements between consecutive timesteps of a row: 1, or dim
+               // for the (batch, length, channel) layout
   int32_t softplus, load_state;
   int32_t groups_per_batch, whole_groups, segments;
   int64_t seg_len;
@@ -132,6 +134,8 @@ __device__ __forceinline__ void scan_body(
   const bool valid = d < s.dim;
   const int64_t dc = valid ? d : s.dim - 1;
   const int64_t row = b * s.dim + dc;
+  // first element of the row in u / delta / z / out
+  const int64_t rowoff = s.ts == 1 ? row * s.L : b * s.L * s.dim + dc;
   const int64_t t_begin = nseg > 1 ? (int64_t)seg * s.seg_len : 0;
   const int64_t t_end = nseg > 1 ? min(s.L, t_begin + s.seg_len) : s.L;
   const int64_t sr = (int64_t)(gi - s.whole_groups) * kLanes + lane;
@@ -165,7 +169,8 @@ __device__ __forceinline__ void scan_body(
   }
   auto load_prev = [&](Raw<BF16, kConvK>& r, int64_t tc) {
     if (tc >= kConvK) {
-      load_chunk<BF16, VEC, kConvK>(r, u, row * s.L + tc - kConvK, s.L - (tc - kConvK));
+      load_chunk<BF16, VEC, kConvK>(r, u, rowoff + (tc - kConvK) * s.ts,
+                                    s.L - (tc - kConvK), s.ts);
     } else {
       // tc == 0 (chunks start at multiples of 4): slots 1..3 hold x[-3..-1]
       // from init, slot 0 is never used
@@ -203,8 +208,6 @@ __device__ __forceinline__ void scan_body(
   // this wave's packed B/C run
   const uint32_t* __restrict__ bcw = bcp + (b * NG + g) * bc_run_words(s.L, WPS);
   using Batch = BCBatch<NPW, BF16>;
-  const int64_t rowoff = row * s.L;
-
   Raw<BF16, KC> ru, rd, rz, nu, nd, nz;
   raw_zero(rz);
   raw_zero(nz);
@@ -237,9 +240,9 @@ __device__ __forceinline__ void scan_body(
   {
     const int64_t tc = t_begin + g * KC;
     const int64_t nv = t_end - tc;
-    load_chunk<BF16, VEC, KC>(ru, u, rowoff + tc, nv);
-    load_chunk<BF16, VEC, KC>(rd, delta, rowoff + tc, nv);
-    if (HAS_Z && !AGG) load_chunk<BF16, VEC, KC>(rz, z, rowoff + tc, nv);
+    load_chunk<BF16, VEC, KC>(ru, u, rowoff + tc * s.ts, nv, s.ts);
+    load_chunk<BF16, VEC, KC>(rd, delta, rowoff + tc * s.ts, nv, s.ts);
+    if (HAS_Z && !AGG) load_chunk<BF16, VEC, KC>(rz, z, rowoff + tc * s.ts, nv, s.ts);
     if constexpr (CONV) {
       load_prev(rp, tc);
       conv_u(ru, rp, uc);
@@ -253,9 +256,9 @@ __device__ __forceinline__ void scan_body(
     {
       const int64_t tc = tb + T + g * KC;
       const int64_t nv = t_end - tc;
-      load_chunk<BF16, VEC, KC>(nu, u, rowoff + tc, nv);
-      load_chunk<BF16, VEC, KC>(nd, delta, rowoff + tc, nv);
-      if (HAS_Z && !AGG) load_chunk<BF16, VEC, KC>(nz, z, rowoff + tc, nv);
+      load_chunk<BF16, VEC, KC>(nu, u, rowoff + tc * s.ts, nv, s.ts);
+      load_chunk<BF16, VEC, KC>(nd, delta, rowoff + tc * s.ts, nv, s.ts);
+      if (HAS_Z && !AGG) load_chunk<BF16, VEC, KC>(nz, z, rowoff + tc * s.ts, nv, s.ts);
       // tc >= kTile here, so the 4 inputs before the chunk are in the row.
       // On the vector path the load is unconditional (a conditional one
       // makes the compiler wait for the whole prefetch right after it): a
@@ -264,7 +267,8 @@ __device__ __forceinline__ void scan_body(
         if constexpr (VEC)
           load_chunk<BF16, true, kConvK>(np_, u, rowoff + min(tc, t_end) - kConvK, kConvK);
         else
-          load_chunk<BF16, false, kConvK>(np_, u, rowoff + tc - kConvK, nv + kConvK);
+          load_chunk<BF16, false, kConvK>(np_, u, rowoff + (tc - kConvK) * s.ts,
+                                          nv + kConvK, s.ts);
       }
     }
 
@@ -358,9 +362,10 @@ __device__ __forceinline__ void scan_body(
         if (HAS_Z) y *= silu_f32(raw_get(rz, k));
         o[k] = y;
       }
-      if (valid) store_chunk<BF16, VEC, KC>(out, rowoff + tc, o, t_end - tc);
+      if (valid) store_chunk<BF16, VEC, KC>(out, rowoff + tc * s.ts, o, t_end - tc, s.ts);
       if constexpr (CONV) {
-        if (valid && cv.u_out) store_chunk<BF16, VEC, KC>(cv.u_out, rowoff + tc, uc, t_end - tc);
+        if (valid && cv.u_out)
+          store_chunk<BF16, VEC, KC>(cv.u_out, rowoff + tc * s.ts, uc, t_end - tc, s.ts);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -448,6 +453,7 @@ hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
   ScanShape s;
   s.dim = p.dim;
   s.L = p.L;
+  s.ts = p.layout_bld ? p.dim : 1;
   s.softplus = p.softplus;
   s.load_state = p.load_state;
   s.groups_per_batch = p.groups_per_batch;

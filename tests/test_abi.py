@@ -81,7 +81,7 @@ def test_fwd_validation_codes(L):
     assert _fwd(L, _dims(N=256)) == -3
     assert _fwd(L, _dims(N=48)) == -3
     assert _fwd(L, _dims(io=7)) == -3
-    assert _fwd(L, _dims(flags=2)) == -3
+    assert _fwd(L, _dims(flags=4)) == -3                    # unknown flag
     assert _fwd(L, _dims(reserved=1)) == -3
     assert _fwd(L, _dims(L_=1 << 40)) == -2                 # overflow / too long
     # bf16 pointers need 2-byte alignment, fp32 ones 4-byte alignment
