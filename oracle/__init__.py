@@ -43,17 +43,17 @@ def build(force: bool = True) -> str:
 def _open(path):
     lib = ctypes.CDLL(path)
     i64, cint = ctypes.c_int64, ctypes.c_int
-    lib.mssm_oracle_scan.argtypes = [i64, i64, i64, i64, _D, _D, _D, _D, _D,
+    lib.mssm_oracle_scan.argtypes = [i64, i64, i64, i64, i64, _D, _D, _D, _D, _D,
                                      _D, _D, _D, cint, _D, _D, _D, cint]
     lib.mssm_oracle_scan.restype = cint
-    lib.mssm_oracle_state_update.argtypes = [i64, i64, i64, _D, _D, _D, _D, _D,
+    lib.mssm_oracle_state_update.argtypes = [i64, i64, i64, i64, _D, _D, _D, _D, _D,
                                              _D, _D, _D, _D, cint, _D, cint]
     lib.mssm_oracle_state_update.restype = cint
     lib.mssm_oracle_scan_row.argtypes = [i64, i64, _D, _D, _D, _D, _D, _D,
                                          ctypes.c_double, ctypes.c_double,
                                          cint, _D, _D, _D]
     lib.mssm_oracle_scan_row.restype = None
-    lib.mssm_oracle_scan_bwd.argtypes = [i64, i64, i64, i64] + [_D] * 8 + [cint] + [_D] * 12
+    lib.mssm_oracle_scan_bwd.argtypes = [i64, i64, i64, i64, i64] + [_D] * 8 + [cint] + [_D] * 12
     lib.mssm_oracle_scan_bwd.restype = cint
     lib.mssm_oracle_causal_conv1d.argtypes = [i64, i64, i64, i64, _D, _D, _D,
                                               _D, cint, _D]
@@ -97,16 +97,18 @@ class Oracle:
              softplus=True, h0=None, nthreads=None):
         """Selective scan in fp64.
 
-        u, delta, z: (batch, dim, L); B, C: (batch, L, N); A: (dim, N);
-        D, delta_bias: (dim,); h0: (batch, dim, N) or None.
+        u, delta, z: (batch, dim, L); B, C: (batch, L, N), or (batch, L, G, N)
+        for G groups of channels (channel d reads group d // (dim // G));
+        A: (dim, N); D, delta_bias: (dim,); h0: (batch, dim, N) or None.
         Returns (out (batch, dim, L), last_state (batch, dim, N)), both fp64.
         """
         u, delta, A, B, C = map(_f64, (u, delta, A, B, C))
         D, z, delta_bias, h0 = map(_f64, (D, z, delta_bias, h0))
         batch, dim, L = u.shape
         N = A.shape[1]
+        G = B.shape[2] if B.ndim == 4 else 1
         assert delta.shape == u.shape and A.shape == (dim, N)
-        assert B.shape == (batch, L, N) and C.shape == (batch, L, N)
+        assert B.shape == C.shape and B.shape in ((batch, L, N), (batch, L, G, N))
         assert z is None or z.shape == u.shape
         assert D is None or D.shape == (dim,)
         assert delta_bias is None or delta_bias.shape == (dim,)
@@ -114,11 +116,11 @@ class Oracle:
         out = np.empty((batch, dim, L), dtype=np.float64)
         last = np.empty((batch, dim, N), dtype=np.float64)
         rc = self._lib.mssm_oracle_scan(
-            batch, dim, N, L, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+            batch, dim, N, L, G, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
             _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)), _ptr(h0),
             _ptr(out), _ptr(last), int(nthreads or default_threads()))
         if rc != 0:
-            raise ValueError("oracle: unsupported dstate %d" % N)
+            raise ValueError("oracle: unsupported dstate %d or groups %d" % (N, G))
         return out, last
 
     def scan_row(self, u, delta, A_row, B_b, C_b, D_d=0.0, z=None, bias_d=0.0,
@@ -141,21 +143,23 @@ class Oracle:
                  delta_bias=None, softplus=True, h0=None, dlast=None):
         """Gradients of the scan for the loss sum(dout * out) +
         sum(dlast * last_state).  Returns a dict of fp64 arrays: du, ddelta
-        (batch, dim, L), dA (dim, N), dB, dC (batch, L, N), dD, ddelta_bias
-        (dim,), dz (batch, dim, L; None without z), dh0 (batch, dim, N)."""
+        (batch, dim, L), dA (dim, N), dB, dC (B's shape: (batch, L, N) or
+        (batch, L, G, N)), dD, ddelta_bias (dim,), dz (batch, dim, L; None
+        without z), dh0 (batch, dim, N)."""
         u, delta, A, B, C, dout = map(_f64, (u, delta, A, B, C, dout))
         D, z, delta_bias, h0, dlast = map(_f64, (D, z, delta_bias, h0, dlast))
         batch, dim, L = u.shape
         N = A.shape[1]
-        assert dout.shape == u.shape and B.shape == (batch, L, N)
+        G = B.shape[2] if B.ndim == 4 else 1
+        assert dout.shape == u.shape and B.shape in ((batch, L, N), (batch, L, G, N))
         assert dlast is None or dlast.shape == (batch, dim, N)
         o = dict(du=np.empty_like(u), ddelta=np.empty_like(u),
                  dz=np.empty_like(u) if z is not None else None,
-                 dA=np.empty((dim, N)), dB=np.empty((batch, L, N)),
-                 dC=np.empty((batch, L, N)), dD=np.empty(dim),
+                 dA=np.empty((dim, N)), dB=np.empty(B.shape),
+                 dC=np.empty(B.shape), dD=np.empty(dim),
                  ddelta_bias=np.empty(dim), dh0=np.empty((batch, dim, N)))
         rc = self._lib.mssm_oracle_scan_bwd(
-            batch, dim, N, L, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+            batch, dim, N, L, G, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
             _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)), _ptr(h0),
             _ptr(dout), _ptr(dlast), _ptr(o["du"]), _ptr(o["ddelta"]),
             _ptr(o["dz"]), _ptr(o["dA"]), _ptr(o["dB"]), _ptr(o["dC"]),
@@ -189,7 +193,8 @@ class Oracle:
                      dt_bias=None, softplus=True, nthreads=None):
         """Single-token decode step in fp64.
 
-        state: (batch, dim, N); x, dt, z: (batch, dim); B, C: (batch, N).
+        state: (batch, dim, N); x, dt, z: (batch, dim); B, C: (batch, N) or
+        (batch, G, N) for G channel groups.
         Returns (out (batch, dim), new_state (batch, dim, N)); the inputs are
         left untouched.
         """
@@ -197,12 +202,13 @@ class Oracle:
         x, dt, A, B, C, D, z, dt_bias = map(
             _f64, (x, dt, A, B, C, D, z, dt_bias))
         batch, dim, N = st.shape
+        G = B.shape[1] if B.ndim == 3 else 1
         assert x.shape == (batch, dim) and dt.shape == (batch, dim)
-        assert A.shape == (dim, N) and B.shape == (batch, N)
-        assert C.shape == (batch, N)
+        assert A.shape == (dim, N) and B.shape in ((batch, N), (batch, G, N))
+        assert C.shape == B.shape
         out = np.empty((batch, dim), dtype=np.float64)
         rc = self._lib.mssm_oracle_state_update(
-            batch, dim, N, _ptr(st), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+            batch, dim, N, G, _ptr(st), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
             _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), int(bool(softplus)),
             _ptr(out), int(nthreads or default_threads()))
         if rc != 0:

@@ -107,13 +107,51 @@ void mssm_oracle_scan_row(int64_t seqlen, int64_t dstate,
 }
 
 /*
+ * B/C groups.  With ngroups = G, B and C hold G vectors per token, layout
+ * (batch, seqlen, G, dstate), and channel d reads group d / (dim / G): the
+ * first dim / G channels share group 0, and so on.  G = 1 is the single
+ * shared vector of page "Mamba: Selective State Space Models", "Mathematical
+ * Foundation / Selective Mechanism"; more groups are the layout variant of
+ * the Mamba-2 block (page "Mamba State Space Model", "Use the Mamba2 block",
+ * which takes a group count), read here as contiguous channel blocks.
+ *
+ * gather_groups copies X (batch, seqlen, G, dstate) into a new array
+ * (batch, G, seqlen, dstate), so that each (batch entry, group) is one
+ * contiguous (seqlen, dstate) block as the row routines take it.
+ */
+static double *gather_groups(const double *X, int64_t batch, int64_t seqlen,
+                             int64_t ngroups, int64_t dstate)
+{
+    double *o = (double *)malloc(sizeof(double) * (size_t)(batch * ngroups * seqlen * dstate));
+    int64_t b, t, g, n;
+    if (!o)
+        return NULL;
+    for (b = 0; b < batch; ++b)
+        for (t = 0; t < seqlen; ++t)
+            for (g = 0; g < ngroups; ++g)
+                for (n = 0; n < dstate; ++n)
+                    o[((b * ngroups + g) * seqlen + t) * dstate + n] =
+                        X[((b * seqlen + t) * ngroups + g) * dstate + n];
+    return o;
+}
+
+/* the group of channel d */
+static int64_t group_of(int64_t d, int64_t dim, int64_t ngroups)
+{
+    return d / (dim / ngroups);
+}
+
+/*
  * Whole scan.  D, z, delta_bias and h0 may be NULL (zero skip, no gate, zero
  * bias, zero initial state).  last_state may be NULL.  Rows are independent,
  * so they are spread over nthreads OpenMP threads (nthreads <= 0: default).
- * Returns 0, or -1 if dstate is outside 1..MSSM_ORACLE_MAX_N.
+ * B, C are (batch, seqlen, ngroups, dstate).
+ * Returns 0, -1 if dstate is outside 1..MSSM_ORACLE_MAX_N, -3 if ngroups
+ * does not divide dim, -2 if out of memory.
  */
 int mssm_oracle_scan(int64_t batch, int64_t dim, int64_t dstate,
-                     int64_t seqlen, const double *u, const double *delta,
+                     int64_t seqlen, int64_t ngroups, const double *u,
+                     const double *delta,
                      const double *A, const double *B, const double *C,
                      const double *D, const double *z,
                      const double *delta_bias, int softplus,
@@ -122,22 +160,35 @@ int mssm_oracle_scan(int64_t batch, int64_t dim, int64_t dstate,
 {
     int64_t rows = batch * dim;
     int64_t r;
+    double *Bg, *Cg;
     if (dstate < 1 || dstate > MSSM_ORACLE_MAX_N)
         return -1;
+    if (ngroups < 1 || dim % ngroups != 0)
+        return -3;
     if (nthreads <= 0)
         nthreads = 1;
+    Bg = gather_groups(B, batch, seqlen, ngroups, dstate);
+    Cg = gather_groups(C, batch, seqlen, ngroups, dstate);
+    if (!Bg || !Cg) {
+        free(Bg);
+        free(Cg);
+        return -2;
+    }
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
     for (r = 0; r < rows; ++r) {
         int64_t b = r / dim, d = r % dim;
         size_t row = (size_t)r * (size_t)seqlen;
-        size_t bc = (size_t)b * (size_t)seqlen * (size_t)dstate;
+        size_t bc = (size_t)(b * ngroups + group_of(d, dim, ngroups)) *
+                    (size_t)seqlen * (size_t)dstate;
         mssm_oracle_scan_row(seqlen, dstate, u + row, delta + row,
-                             z ? z + row : NULL, A + d * dstate, B + bc,
-                             C + bc, D ? D[d] : 0.0,
+                             z ? z + row : NULL, A + d * dstate, Bg + bc,
+                             Cg + bc, D ? D[d] : 0.0,
                              delta_bias ? delta_bias[d] : 0.0, softplus,
                              h0 ? h0 + r * dstate : NULL, out + row,
                              last_state ? last_state + r * dstate : NULL);
     }
+    free(Bg);
+    free(Cg);
     return 0;
 }
 
@@ -147,11 +198,11 @@ int mssm_oracle_scan(int64_t batch, int64_t dim, int64_t dstate,
  * inference carries from token to token).
  *   state            : (batch, dim, dstate), in/out
  *   x, dt, z, out    : (batch, dim)
- *   B, C             : (batch, dstate)
+ *   B, C             : (batch, ngroups, dstate)
  *   A                : (dim, dstate);  D, dt_bias : (dim)
  */
 int mssm_oracle_state_update(int64_t batch, int64_t dim, int64_t dstate,
-                             double *state, const double *x,
+                             int64_t ngroups, double *state, const double *x,
                              const double *dt, const double *A,
                              const double *B, const double *C,
                              const double *D, const double *z,
@@ -162,14 +213,17 @@ int mssm_oracle_state_update(int64_t batch, int64_t dim, int64_t dstate,
     int64_t r;
     if (dstate < 1 || dstate > MSSM_ORACLE_MAX_N)
         return -1;
+    if (ngroups < 1 || dim % ngroups != 0)
+        return -3;
     if (nthreads <= 0)
         nthreads = 1;
 #pragma omp parallel for schedule(static) num_threads(nthreads)
     for (r = 0; r < rows; ++r) {
         int64_t b = r / dim, d = r % dim;
+        int64_t bg = (b * ngroups + group_of(d, dim, ngroups)) * dstate;
         double *h = state + r * dstate;
         mssm_oracle_scan_row(1, dstate, x + r, dt + r, z ? z + r : NULL,
-                             A + d * dstate, B + b * dstate, C + b * dstate,
+                             A + d * dstate, B + bg, C + bg,
                              D ? D[d] : 0.0, dt_bias ? dt_bias[d] : 0.0,
                              softplus, h, out + r, h);
     }
@@ -276,11 +330,14 @@ void mssm_oracle_scan_bwd_row(int64_t seqlen, int64_t dstate,
  * Gradients of the whole scan (serial over rows; the oracle is for tests).
  * Shapes as mssm_oracle_scan; dout (batch, dim, seqlen); dlast, dh0
  * (batch, dim, dstate) or NULL; outputs du, ddelta, dz (batch, dim, seqlen),
- * dA (dim, dstate), dB, dC (batch, seqlen, dstate), dD, dbias (dim), all
- * overwritten.  Returns 0, -1 for an unsupported dstate, -2 if out of memory.
+ * dA (dim, dstate), dB, dC (batch, seqlen, ngroups, dstate; each group sums
+ * over its own channels), dD, dbias (dim), all overwritten.  Returns 0, -1
+ * for an unsupported dstate, -3 if ngroups does not divide dim, -2 if out of
+ * memory.
  */
 int mssm_oracle_scan_bwd(int64_t batch, int64_t dim, int64_t dstate,
-                         int64_t seqlen, const double *u, const double *delta,
+                         int64_t seqlen, int64_t ngroups, const double *u,
+                         const double *delta,
                          const double *A, const double *B, const double *C,
                          const double *D, const double *z,
                          const double *delta_bias, int softplus,
@@ -289,33 +346,59 @@ int mssm_oracle_scan_bwd(int64_t batch, int64_t dim, int64_t dstate,
                          double *dz, double *dA, double *dB, double *dC,
                          double *dD, double *dbias, double *dh0)
 {
-    int64_t r, i;
-    double *scratch;
+    int64_t r, i, b, t, g, n;
+    const int64_t nbc = batch * ngroups * seqlen * dstate;
+    double *scratch, *Bg, *Cg, *dBg, *dCg;
     if (dstate < 1 || dstate > MSSM_ORACLE_MAX_N)
         return -1;
+    if (ngroups < 1 || dim % ngroups != 0)
+        return -3;
     scratch = (double *)malloc(sizeof(double) * (size_t)(2 * seqlen * dstate + 3 * seqlen));
-    if (!scratch)
+    Bg = gather_groups(B, batch, seqlen, ngroups, dstate);
+    Cg = gather_groups(C, batch, seqlen, ngroups, dstate);
+    dBg = (double *)calloc((size_t)nbc, sizeof(double));
+    dCg = (double *)calloc((size_t)nbc, sizeof(double));
+    if (!scratch || !Bg || !Cg || !dBg || !dCg) {
+        free(scratch);
+        free(Bg);
+        free(Cg);
+        free(dBg);
+        free(dCg);
         return -2;
+    }
     for (i = 0; i < dim * dstate; ++i)
         dA[i] = 0.0;
-    for (i = 0; i < batch * seqlen * dstate; ++i)
-        dB[i] = dC[i] = 0.0;
     for (i = 0; i < dim; ++i)
         dD[i] = dbias[i] = 0.0;
     for (r = 0; r < batch * dim; ++r) {
-        int64_t b = r / dim, d = r % dim;
+        int64_t bb = r / dim, d = r % dim;
         size_t row = (size_t)r * (size_t)seqlen;
-        size_t bc = (size_t)b * (size_t)seqlen * (size_t)dstate;
+        size_t bc = (size_t)(bb * ngroups + group_of(d, dim, ngroups)) *
+                    (size_t)seqlen * (size_t)dstate;
         mssm_oracle_scan_bwd_row(
             seqlen, dstate, u + row, delta + row, z ? z + row : NULL,
-            A + d * dstate, B + bc, C + bc, D ? D[d] : 0.0,
+            A + d * dstate, Bg + bc, Cg + bc, D ? D[d] : 0.0,
             delta_bias ? delta_bias[d] : 0.0, softplus,
             h0 ? h0 + r * dstate : NULL, dout + row,
             dlast ? dlast + r * dstate : NULL, du + row, ddelta + row,
-            dz ? dz + row : NULL, dA + d * dstate, dB + bc, dC + bc, dD + d,
+            dz ? dz + row : NULL, dA + d * dstate, dBg + bc, dCg + bc, dD + d,
             dbias + d, dh0 ? dh0 + r * dstate : NULL, scratch);
     }
+    /* back to (batch, seqlen, ngroups, dstate) */
+    for (b = 0; b < batch; ++b)
+        for (t = 0; t < seqlen; ++t)
+            for (g = 0; g < ngroups; ++g)
+                for (n = 0; n < dstate; ++n) {
+                    const int64_t src = ((b * ngroups + g) * seqlen + t) * dstate + n;
+                    const int64_t dst = ((b * seqlen + t) * ngroups + g) * dstate + n;
+                    dB[dst] = dBg[src];
+                    dC[dst] = dCg[src];
+                }
     free(scratch);
+    free(Bg);
+    free(Cg);
+    free(dBg);
+    free(dCg);
     return 0;
 }
 

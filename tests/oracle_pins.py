@@ -502,3 +502,59 @@ def pin_conv_then_scan_equals_scan_of_conv(orc):
 
 PINS += [pin_conv_numpy_convolve, pin_conv_impulse_and_constant,
          pin_conv_initial_values_split, pin_conv_then_scan_equals_scan_of_conv]
+
+
+# --------------------------------------------------------------- B/C groups
+# Reading: with G groups, B, C are (batch, L, G, N) and channel d reads group
+# d // (dim // G) (contiguous channel blocks).
+
+def pin_groups_reduce_to_one_group(orc):
+    """G groups holding identical B and C give exactly the one-group result;
+    and each group's channels equal a one-group scan of just those channels
+    with just that group's B and C (forward, decode and backward)."""
+    rng = np.random.default_rng(61)
+    batch, dim, L, N, G = 2, 6, 9, 3, 3
+    args, h0 = random_case(62, batch=batch, dim=dim, L=L, N=N)
+    Bg = rng.standard_normal((batch, L, G, N))
+    Cg = rng.standard_normal((batch, L, G, N))
+    same = dict(args, B=np.repeat(args["B"][:, :, None, :], G, axis=2),
+                C=np.repeat(args["C"][:, :, None, :], G, axis=2))
+    o1, l1 = orc.scan(**args, softplus=True, h0=h0)
+    oG, lG = orc.scan(**same, softplus=True, h0=h0)
+    _close(oG, o1, 0, 0, "identical groups = one group")
+    _close(lG, l1, 0, 0, "identical groups = one group (state)")
+    gargs = dict(args, B=Bg, C=Cg)
+    out, last = orc.scan(**gargs, softplus=True, h0=h0)
+    dout = rng.standard_normal(args["u"].shape)
+    dlast = rng.standard_normal(h0.shape)
+    gb = orc.scan_bwd(gargs["u"], gargs["delta"], gargs["A"], Bg, Cg, dout,
+                      D=gargs["D"], z=gargs["z"], delta_bias=gargs["delta_bias"],
+                      h0=h0, dlast=dlast)
+    per = dim // G
+    for g in range(G):
+        ch = slice(g * per, (g + 1) * per)
+        sub = dict(u=args["u"][:, ch], delta=args["delta"][:, ch], A=args["A"][ch],
+                   B=Bg[:, :, g], C=Cg[:, :, g], D=args["D"][ch], z=args["z"][:, ch],
+                   delta_bias=args["delta_bias"][ch])
+        o, l = orc.scan(**sub, softplus=True, h0=h0[:, ch])
+        _close(out[:, ch], o, 0, 0, "group %d channels" % g)
+        _close(last[:, ch], l, 0, 0, "group %d state" % g)
+        sb = orc.scan_bwd(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"],
+                          dout[:, ch], D=sub["D"], z=sub["z"],
+                          delta_bias=sub["delta_bias"], h0=h0[:, ch],
+                          dlast=dlast[:, ch])
+        _close(gb["dB"][:, :, g], sb["dB"], 1e-13, 1e-13, "group %d dB" % g)
+        _close(gb["dC"][:, :, g], sb["dC"], 1e-13, 1e-13, "group %d dC" % g)
+        _close(gb["du"][:, ch], sb["du"], 0, 0, "group %d du" % g)
+        # decode of the first token against the group's one-group decode
+        o1s, s1s = orc.state_update(h0[:, ch], sub["u"][:, :, 0], sub["delta"][:, :, 0],
+                                    sub["A"], sub["B"][:, 0], sub["C"][:, 0], D=sub["D"],
+                                    z=sub["z"][:, :, 0], dt_bias=sub["delta_bias"])
+        oGs, sGs = orc.state_update(h0, args["u"][:, :, 0], args["delta"][:, :, 0],
+                                    args["A"], Bg[:, 0], Cg[:, 0], D=args["D"],
+                                    z=args["z"][:, :, 0], dt_bias=args["delta_bias"])
+        _close(oGs[:, ch], o1s, 0, 0, "group %d decode" % g)
+        _close(sGs[:, ch], s1s, 0, 0, "group %d decode state" % g)
+
+
+PINS += [pin_groups_reduce_to_one_group]

@@ -33,7 +33,7 @@ MUTANTS = [
     ("softplus_without_log", "return log1p(exp(x));", "return exp(x);"),
     ("softplus_naive_large_x", "return x + log1p(exp(-x));", "return x;"),
     ("last_state_lost", "last_state[n] = h[n];", "last_state[n] = 0.0;"),
-    ("decode_B_of_batch0", "B + b * dstate, C + b * dstate", "B, C"),
+    ("decode_B_of_batch0", "A + d * dstate, B + bg, C + bg,", "A + d * dstate, B, C,"),
     ("decode_state_not_written", "softplus, h, out + r, h);", "softplus, h, out + r, NULL);"),
     ("decode_x_dt_swapped", "x + r, dt + r", "dt + r, x + r"),
     # backward
@@ -53,6 +53,13 @@ MUTANTS = [
      "dC_b[t * dstate + n] += dy * H[t * dstate + n];\n            dB_b[t * dstate + n] += g[n] * DT[t] * u[t];\n            g[n] += dy * C_b[t * dstate + n];"),
     ("bwd_dh0_dropped", "dh0[n] = g[n];", "dh0[n] = 0.0;"),
     ("bwd_dD_missing", "*dD += dy * u[t];", "*dD += 0.0 * u[t];"),
+    # B/C groups
+    ("group_index_modulo", "return d / (dim / ngroups);", "return d % ngroups;"),
+    ("group_gather_transposed",
+     "X[((b * seqlen + t) * ngroups + g) * dstate + n];",
+     "X[((b * ngroups + g) * seqlen + t) * dstate + n];"),
+    ("bwd_dB_group_scatter_wrong_group", "dB[dst] = dBg[src];",
+     "dB[dst] = dBg[((b * ngroups + 0) * seqlen + t) * dstate + n];"),
     # causal conv
     ("conv_kernel_not_flipped", "v += wr[k] * xv;", "v += wr[K - 1 - k] * xv;"),
     ("conv_window_off_by_one", "const int64_t s = t - (K - 1) + k;",
