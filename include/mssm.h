@@ -29,6 +29,7 @@
  * caller.  All arrays are contiguous, row-major, last index fastest:
  *   u, delta, z, out   (batch, dim, seqlen)      io dtype
  *   B, C               (batch, seqlen, dstate)   io dtype, one N-vector/token
+ *                      (batch, seqlen, g, dstate) with mssm_dims.ngroups = g
  *   A                  (dim, dstate)             fp32 (real; negative for a
  *                                                 decaying state)
  *   D, delta_bias      (dim)                     fp32
@@ -92,7 +93,13 @@ typedef struct {
   int32_t time_segments; /* scan only: 0 = the library picks; k >= 1 splits */
                          /* every row into k time segments (a carried state */
                          /* joins them; results agree up to rounding)       */
-  int32_t reserved;      /* must be 0                                        */
+  int32_t ngroups;       /* B/C groups: 0 or 1 = one N-vector per token,     */
+                         /* shared by all channels; g > 1: B, C hold g      */
+                         /* vectors per token, (batch, seqlen, g, dstate)   */
+                         /* ((batch, g, dstate) for state_update), and      */
+                         /* channel d reads group d / (dim / g).  The scans */
+                         /* need dim % (64 g) == 0 (a 64-channel workgroup  */
+                         /* reads one group), state_update dim % g == 0.    */
 } mssm_dims;
 
 /*

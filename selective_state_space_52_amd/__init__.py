@@ -77,15 +77,27 @@ def _eshape(batch, dim, L, layout):
     return (batch, L, dim) if layout == "bld" else (batch, dim, L)
 
 
+def _groups(B, batch, L, N, token_dim=True):
+    """B/C group count from B's shape: (batch, L, N) or (batch, L, G, N) for
+    the scans (token_dim), (batch, N) or (batch, G, N) for the decode step."""
+    if token_dim:
+        return B.shape[2] if B.dim() == 4 else 1
+    return B.shape[1] if B.dim() == 3 else 1
+
+
+def _bc_shape(batch, L, G, N, grouped):
+    return (batch, L, G, N) if grouped else (batch, L, N)
+
+
 def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
 def scan_plan(batch, dim, dstate, seqlen, io_dtype=torch.bfloat16,
-              time_segments=0, layout="bdl") -> dict:
+              time_segments=0, layout="bdl", ngroups=0) -> dict:
     """How the library splits a forward scan of this shape (no GPU needed)."""
     dims = Dims(batch, dim, dstate, seqlen, _IO[io_dtype], _layout(layout),
-                time_segments, 0)
+                time_segments, ngroups)
     plan = Plan()
     check(lib().mssm_selective_scan_fwd_plan(dims, plan))
     return plan.as_dict()
@@ -114,8 +126,9 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     _need(u, "u", io, es, dev)
     _need(delta, "delta", io, es, dev)
     _need(z, "z", io, es, dev)
-    _need(B, "B", io, (batch, L, N), dev)
-    _need(C, "C", io, (batch, L, N), dev)
+    G = _groups(B, batch, L, N)
+    _need(B, "B", io, _bc_shape(batch, L, G, N, B.dim() == 4), dev)
+    _need(C, "C", io, tuple(B.shape), dev)
     _need(A, "A", torch.float32, (dim, N), dev)
     _need(D, "D", torch.float32, (dim,), dev)
     _need(delta_bias, "delta_bias", torch.float32, (dim,), dev)
@@ -126,7 +139,7 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         out = torch.empty(es, dtype=io, device=dev)
     _need(out, "out", io, es, dev)
     dims = Dims(batch, dim, N, L, _IO[io],
-                (MSSM_FLAG_LOAD_STATE if load_state else 0) | lay, time_segments, 0)
+                (MSSM_FLAG_LOAD_STATE if load_state else 0) | lay, time_segments, G)
     with torch.cuda.device(dev):
         check(lib().mssm_selective_scan_fwd(
             _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
@@ -188,8 +201,9 @@ def selective_scan_fwd_conv(x, conv_weight, delta, A, B, C, conv_bias=None,
     _need(u_out, "u_out", io, es, dev)
     _need(delta, "delta", io, es, dev)
     _need(z, "z", io, es, dev)
-    _need(B, "B", io, (batch, L, N), dev)
-    _need(C, "C", io, (batch, L, N), dev)
+    G = _groups(B, batch, L, N)
+    _need(B, "B", io, _bc_shape(batch, L, G, N, B.dim() == 4), dev)
+    _need(C, "C", io, tuple(B.shape), dev)
     _need(A, "A", torch.float32, (dim, N), dev)
     _need(D, "D", torch.float32, (dim,), dev)
     _need(delta_bias, "delta_bias", torch.float32, (dim,), dev)
@@ -200,7 +214,7 @@ def selective_scan_fwd_conv(x, conv_weight, delta, A, B, C, conv_bias=None,
         out = torch.empty(es, dtype=io, device=dev)
     _need(out, "out", io, es, dev)
     dims = Dims(batch, dim, N, L, _IO[io],
-                (MSSM_FLAG_LOAD_STATE if load_state else 0) | lay, time_segments, 0)
+                (MSSM_FLAG_LOAD_STATE if load_state else 0) | lay, time_segments, G)
     with torch.cuda.device(dev):
         check(lib().mssm_selective_scan_fwd_conv(
             _ptr(x), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_init),
@@ -236,8 +250,9 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None,
     _need(delta, "delta", io, es, dev)
     _need(z, "z", io, es, dev)
     _need(dout, "dout", io, es, dev)
-    _need(B, "B", io, (batch, L, N), dev)
-    _need(C, "C", io, (batch, L, N), dev)
+    G = _groups(B, batch, L, N)
+    _need(B, "B", io, _bc_shape(batch, L, G, N, B.dim() == 4), dev)
+    _need(C, "C", io, tuple(B.shape), dev)
     _need(A, "A", torch.float32, (dim, N), dev)
     _need(D, "D", torch.float32, (dim,), dev)
     _need(delta_bias, "delta_bias", torch.float32, (dim,), dev)
@@ -248,12 +263,12 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None,
              ddelta=torch.empty(es, dtype=io, device=dev),
              dz=torch.empty(es, dtype=io, device=dev) if z is not None else None,
              dA=torch.empty((dim, N), **f32),
-             dB=torch.empty((batch, L, N), **f32),
-             dC=torch.empty((batch, L, N), **f32),
+             dB=torch.empty(tuple(B.shape), **f32),
+             dC=torch.empty(tuple(B.shape), **f32),
              dD=torch.empty((dim,), **f32),
              ddelta_bias=torch.empty((dim,), **f32),
              dh0=torch.empty((batch, dim, N), **f32) if want_dh0 else None)
-    dims = Dims(batch, dim, N, L, _IO[io], lay, time_segments, 0)
+    dims = Dims(batch, dim, N, L, _IO[io], lay, time_segments, G)
     with torch.cuda.device(dev):
         check(lib().mssm_selective_scan_bwd(
             _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
@@ -280,15 +295,16 @@ def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
     _need(x, "x", io, (batch, dim), dev)
     _need(dt, "dt", io, (batch, dim), dev)
     _need(z, "z", io, (batch, dim), dev)
-    _need(B, "B", io, (batch, N), dev)
-    _need(C, "C", io, (batch, N), dev)
+    G = _groups(B, batch, 1, N, token_dim=False)
+    _need(B, "B", io, (batch, G, N) if B.dim() == 3 else (batch, N), dev)
+    _need(C, "C", io, tuple(B.shape), dev)
     _need(A, "A", torch.float32, (dim, N), dev)
     _need(D, "D", torch.float32, (dim,), dev)
     _need(dt_bias, "dt_bias", torch.float32, (dim,), dev)
     if out is None:
         out = torch.empty((batch, dim), dtype=io, device=dev)
     _need(out, "out", io, (batch, dim), dev)
-    dims = Dims(batch, dim, N, 1, _IO[io], 0, 0, 0)
+    dims = Dims(batch, dim, N, 1, _IO[io], 0, 0, G)
     with torch.cuda.device(dev):
         check(lib().mssm_selective_state_update(
             _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),

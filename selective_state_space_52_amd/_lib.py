@@ -30,7 +30,7 @@ class Dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("dim", ctypes.c_int64),
                 ("dstate", ctypes.c_int64), ("seqlen", ctypes.c_int64),
                 ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
-                ("time_segments", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("time_segments", ctypes.c_int32), ("ngroups", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):

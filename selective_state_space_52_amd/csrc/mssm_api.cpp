@@ -91,11 +91,21 @@ int check_common_dims(const mssm_dims* dims) {
   if (!dims) return MSSM_ERR_NULL;
   if (dims->io_dtype != MSSM_F32 && dims->io_dtype != MSSM_BF16)
     return MSSM_ERR_UNSUPPORTED;
-  if (dims->reserved != 0) return MSSM_ERR_UNSUPPORTED;
+  if (dims->ngroups < 0) return MSSM_ERR_DIMS;
   if (dims->batch <= 0 || dims->dim <= 0 || dims->dstate <= 0 ||
       dims->seqlen <= 0)
     return MSSM_ERR_DIMS;
   if (!valid_dstate(dims->dstate)) return MSSM_ERR_UNSUPPORTED;
+  return MSSM_OK;
+}
+
+// B/C groups of a call (0 means 1).
+int64_t groups_of(const mssm_dims* dims) { return dims->ngroups > 1 ? dims->ngroups : 1; }
+
+// The scans read one group per 64-channel workgroup.
+int check_scan_groups(const mssm_dims* dims) {
+  const int64_t G = groups_of(dims);
+  if (G > 1 && dims->dim % (kLanes * G) != 0) return MSSM_ERR_UNSUPPORTED;
   return MSSM_OK;
 }
 
@@ -148,8 +158,8 @@ int make_plan(const mssm_dims* dims, int cus, mssm_plan* plan) {
   if (whole + split * segments > INT32_MAX) return MSSM_ERR_DIMS;
 
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
-  int64_t ws = up(mssm::scan_bc_workspace_bytes(dims->batch, L, (int)N,
-                                                dims->io_dtype == MSSM_BF16));
+  int64_t ws = up(mssm::scan_bc_workspace_bytes(dims->batch * groups_of(dims), L,
+                                                (int)N, dims->io_dtype == MSSM_BF16));
   if (split > 0) {
     const int64_t rows = split * kLanes;
     ws += up(rows * (segments - 1) * N * 4) + up(rows * (segments - 1) * 8) +
@@ -190,7 +200,7 @@ const char* mssm_status_string(int status) {
     case MSSM_OK: return "ok";
     case MSSM_ERR_NULL: return "a required pointer is NULL";
     case MSSM_ERR_DIMS: return "invalid sizes (non-positive, decode seqlen != 1, or too large)";
-    case MSSM_ERR_UNSUPPORTED: return "unsupported dstate, dtype, flag or reserved field";
+    case MSSM_ERR_UNSUPPORTED: return "unsupported dstate, dtype, flag or group split";
     case MSSM_ERR_ALIGN: return "a pointer is not aligned to its element size";
     case MSSM_ERR_ALIAS: return "an output overlaps another argument";
     case MSSM_ERR_HIP: return "a HIP runtime call failed (see mssm_last_error)";
@@ -204,6 +214,8 @@ int mssm_selective_scan_fwd_plan(const mssm_dims* dims, mssm_plan* plan) {
   if (rc != MSSM_OK) return rc;
   if (dims->flags & ~(MSSM_FLAG_LOAD_STATE | MSSM_FLAG_LAYOUT_BLD))
     return MSSM_ERR_UNSUPPORTED;
+  rc = check_scan_groups(dims);
+  if (rc != MSSM_OK) return rc;
   if (dims->time_segments < 0) return MSSM_ERR_DIMS;
   return make_plan(dims, g_cu_count > 0 ? g_cu_count : kDefaultCUs, plan);
 }
@@ -225,6 +237,9 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A,
   if (dims->flags & ~(MSSM_FLAG_LOAD_STATE | MSSM_FLAG_LAYOUT_BLD))
     return MSSM_ERR_UNSUPPORTED;
   const bool bld = (dims->flags & MSSM_FLAG_LAYOUT_BLD) != 0;
+  rc = check_scan_groups(dims);
+  if (rc != MSSM_OK) return rc;
+  const int64_t G = groups_of(dims);
   if (dims->time_segments < 0) return MSSM_ERR_DIMS;
   const bool load_state = (dims->flags & MSSM_FLAG_LOAD_STATE) != 0;
   if (!u || !delta || !A || !B || !C || !out) return MSSM_ERR_NULL;
@@ -246,7 +261,7 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A,
     if (p && !aligned(p, 4)) return MSSM_ERR_ALIGN;
 
   const int64_t ebytes = batch * dim * L * (int64_t)io;
-  const int64_t bcbytes = batch * L * N * (int64_t)io;
+  const int64_t bcbytes = batch * L * G * N * (int64_t)io;
   const Range r_out = range_of(out, ebytes);
   const Range r_state = range_of(last_state, batch * dim * N * 4);
   const Range r_uout = range_of(u_out, ebytes);
@@ -287,6 +302,7 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A,
   p.softplus = softplus ? 1 : 0;
   p.load_state = load_state ? 1 : 0;
   p.groups_per_batch = (int32_t)((dim + kLanes - 1) / kLanes);
+  p.ngroups = (int32_t)G;
   p.whole_groups = plan.whole_groups;
   p.split_groups = plan.split_groups;
   p.segments = plan.segments;
@@ -324,7 +340,7 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A,
   p.ws_bc = ws;
   if (plan.split_groups > 0) {
     const int64_t rows = (int64_t)plan.split_groups * kLanes;
-    char* base = (char*)ws + up(mssm::scan_bc_workspace_bytes(batch, L, (int)N, io == 2));
+    char* base = (char*)ws + up(mssm::scan_bc_workspace_bytes(batch * G, L, (int)N, io == 2));
     p.ws_S = (float*)base;
     base += up(rows * (plan.segments - 1) * N * 4);
     p.ws_sum = (double*)base;
@@ -378,7 +394,7 @@ int mssm_causal_conv1d_fwd(const void* x, const float* weight,
   if (!dims) return MSSM_ERR_NULL;
   if (dims->io_dtype != MSSM_F32 && dims->io_dtype != MSSM_BF16)
     return MSSM_ERR_UNSUPPORTED;
-  if ((dims->flags & ~MSSM_FLAG_LAYOUT_BLD) != 0 || dims->reserved != 0)
+  if ((dims->flags & ~MSSM_FLAG_LAYOUT_BLD) != 0 || dims->ngroups > 1)
     return MSSM_ERR_UNSUPPORTED;
   if (dims->time_segments != 0) return MSSM_ERR_DIMS;
   if (dims->batch <= 0 || dims->dim <= 0 || dims->seqlen <= 0) return MSSM_ERR_DIMS;
@@ -430,6 +446,9 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
   if (dims->dstate > 32) return MSSM_ERR_UNSUPPORTED;
   if (dims->flags & ~MSSM_FLAG_LAYOUT_BLD) return MSSM_ERR_UNSUPPORTED;
   const bool bld = (dims->flags & MSSM_FLAG_LAYOUT_BLD) != 0;
+  rc = check_scan_groups(dims);
+  if (rc != MSSM_OK) return rc;
+  const int64_t G = groups_of(dims);
   if (dims->time_segments < 0) return MSSM_ERR_DIMS;
   if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA ||
       !dB || !dC)
@@ -456,12 +475,12 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
     if (p && !aligned(p, 4)) return MSSM_ERR_ALIGN;
 
   const int64_t ebytes = batch * dim * L * (int64_t)io;
-  const int64_t bcbytes = batch * L * N * (int64_t)io;
+  const int64_t bcbytes = batch * L * G * N * (int64_t)io;
   const int64_t sbytes = batch * dim * N * 4;
   const Range outs[] = {range_of(du, ebytes),          range_of(ddelta, ebytes),
                         range_of(dz, ebytes),          range_of(dA, dim * N * 4),
-                        range_of(dB, batch * L * N * 4),
-                        range_of(dC, batch * L * N * 4), range_of(dD, dim * 4),
+                        range_of(dB, batch * L * G * N * 4),
+                        range_of(dC, batch * L * G * N * 4), range_of(dD, dim * 4),
                         range_of(ddelta_bias, dim * 4), range_of(dh0, sbytes)};
   const Range ins[] = {range_of(u, ebytes),      range_of(delta, ebytes),
                        range_of(z, ebytes),      range_of(dout, ebytes),
@@ -505,6 +524,7 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
   p.batch = batch; p.dim = dim; p.L = L;
   p.softplus = softplus ? 1 : 0;
   p.groups_per_batch = (int32_t)gpb;
+  p.ngroups = (int32_t)G;
   p.tiles = (int32_t)tiles;
   p.segments = segments;
   p.seg_tiles = (int32_t)((tiles + segments - 1) / segments);
@@ -514,7 +534,7 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
 
   hipStream_t st = (hipStream_t)stream;
   const int64_t ws_bytes =
-      mssm::bwd_workspace(batch, dim, L, (int)N, io == 2, segments, nullptr, nullptr);
+      mssm::bwd_workspace(batch, dim, L, (int)N, io == 2, segments, G, nullptr, nullptr);
   void* ws = nullptr;
   {
     hipError_t e = hipMallocAsync(&ws, (size_t)ws_bytes, st);
@@ -523,7 +543,7 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
       return MSSM_ERR_HIP;
     }
   }
-  mssm::bwd_workspace(batch, dim, L, (int)N, io == 2, segments, ws, &p);
+  mssm::bwd_workspace(batch, dim, L, (int)N, io == 2, segments, G, ws, &p);
   hipError_t e = mssm::launch_scan_bwd(p, (int)N, io == 2, vec, st);
   if (e != hipSuccess) set_hip_error("backward scan launch", e);
   hipError_t f = hipFreeAsync(ws, st);
@@ -547,6 +567,8 @@ int mssm_selective_state_update(float* state, const void* x, const void* dt,
   const int64_t batch = dims->batch, dim = dims->dim, N = dims->dstate;
   const size_t io = dims->io_dtype == MSSM_BF16 ? 2 : 4;
   if (!product_ok(batch, dim, N, INT64_MAX / 16)) return MSSM_ERR_DIMS;
+  const int64_t G = groups_of(dims);
+  if (dim % G != 0) return MSSM_ERR_DIMS;
 
   const void* ios[] = {x, dt, B, C, out, z};
   for (const void* p : ios)
@@ -559,8 +581,8 @@ int mssm_selective_state_update(float* state, const void* x, const void* dt,
   const Range r_out = range_of(out, rb);
   const Range r_state = range_of(state, batch * dim * N * 4);
   const Range ins[] = {range_of(x, rb), range_of(dt, rb), range_of(z, rb),
-                       range_of(B, batch * N * (int64_t)io),
-                       range_of(C, batch * N * (int64_t)io),
+                       range_of(B, batch * G * N * (int64_t)io),
+                       range_of(C, batch * G * N * (int64_t)io),
                        range_of(A, dim * N * 4), range_of(D, dim * 4),
                        range_of(dt_bias, dim * 4)};
   for (const Range& r : ins)
@@ -571,6 +593,7 @@ int mssm_selective_state_update(float* state, const void* x, const void* dt,
   p.state = state; p.x = x; p.dt = dt; p.z = z; p.A = A; p.B = B; p.C = C;
   p.D = D; p.bias = dt_bias; p.out = out;
   p.batch = batch; p.dim = dim; p.softplus = softplus ? 1 : 0;
+  p.ngroups = (int32_t)G;
   hipError_t e = mssm::launch_state_update(p, (int)N, io == 2,
                                            (hipStream_t)stream);
   if (e != hipSuccess) {

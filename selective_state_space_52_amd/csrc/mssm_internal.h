@@ -56,6 +56,7 @@ struct ScanParams {
   const void* conv_init;  // (batch, dim, 3) io dtype or null
   void* u_out;            // (batch, dim, L) io dtype: conv output, or null
   int32_t layout_bld;     // u, delta, z, out, u_out are (batch, L, dim)
+  int32_t ngroups;        // B/C groups (B, C are (batch, L, ngroups, N))
 };
 
 // Standalone causal depthwise conv: out = act(bias + sum_k w[k] x[t-K+1+k]).
@@ -84,6 +85,7 @@ struct UpdateParams {
   void* out;
   int64_t batch, dim;
   int32_t softplus;
+  int32_t ngroups;        // B, C are (batch, ngroups, N)
 };
 
 // One backward-scan call.  Gradients of sum(dout * out) + sum(dlast *
@@ -125,6 +127,7 @@ struct BwdParams {
   int32_t segments;       // time segments per row
   int32_t seg_tiles;      // tiles per segment (the last may have fewer)
   int32_t layout_bld;     // the per-element arrays are (batch, L, dim)
+  int32_t ngroups;        // B/C groups (B, C, dB, dC are (batch, L, ngroups, N))
   // workspace (task = group * segments + segment; lane-contiguous rows)
   void* ws_bc;            // B, C packed per wave run, zero-padded to whole tiles
   float* ws_ck;           // [group][tile][n][lane] state at tile start, from a
@@ -145,12 +148,13 @@ struct BwdParams {
 
 // Waves per 64-channel workgroup: each wave owns dstate / waves states.
 int scan_waves_per_group(int N);
-// Repack B and C into per-wave runs for `waves` waves per channel group:
-// `steps` (>= L) timesteps per run, zeros from L on, `run_words` 32-bit words
-// per run; the runs hold bf16 pairs (dst_bf16) or fp32 values.
+// Repack B and C, (batch, L, groups, N), into per-wave runs, one per
+// (batch entry, group, wave) for `waves` waves per channel group: `steps`
+// (>= L) timesteps per run, zeros from L on, `run_words` 32-bit words per
+// run; the runs hold bf16 pairs (dst_bf16) or fp32 values.
 hipError_t launch_bc_pack(const void* B, const void* C, void* packed,
-                          int64_t batch, int64_t L, int64_t steps, int N,
-                          int waves, bool src_bf16, bool dst_bf16,
+                          int64_t batch, int64_t groups, int64_t L, int64_t steps,
+                          int N, int waves, bool src_bf16, bool dst_bf16,
                           int64_t run_words, hipStream_t stream);
 // Bytes of the packed B/C runs of one forward call.
 int64_t scan_bc_workspace_bytes(int64_t batch, int64_t L, int N, bool bf16);
@@ -175,7 +179,7 @@ int bwd_segments(int64_t groups, int64_t tiles, int cus, int forced);
 // Workspace bytes of one backward call; with ws and p non-null also points
 // p's workspace fields into ws.
 int64_t bwd_workspace(int64_t batch, int64_t dim, int64_t L, int N, bool bf16,
-                      int segments, void* ws, BwdParams* p);
+                      int segments, int64_t groups, void* ws, BwdParams* p);
 hipError_t launch_scan_bwd(const BwdParams& p, int N, bool bf16, bool vec,
                            hipStream_t stream);
 hipError_t launch_state_update(const UpdateParams& p, int N, bool bf16,

@@ -72,6 +72,7 @@ struct BwdShape {
   int64_t dim, L;
   int64_t ts;  // elements between consecutive timesteps of a row: 1, or dim
                // for the (batch, length, channel) layout
+  int32_t ngroups, reserved;  // B/C groups
   int32_t groups_per_batch, tiles;
   int32_t segments, seg_tiles;
   int32_t softplus, batch;
@@ -125,6 +126,7 @@ __device__ __forceinline__ uint32_t warm_tile(const uint32_t* __restrict__ bcw,
 struct Task {
   int gi, seg;
   int64_t b, d, dc, row, rowoff;
+  int64_t bcg;  // run of B/C: batch entry * groups + the channel group's B/C group
   bool valid;
   int tile_begin, tile_end;
 };
@@ -140,6 +142,7 @@ __device__ __forceinline__ Task task_of(const BwdShape& s, int lane) {
   k.dc = k.valid ? k.d : s.dim - 1;
   k.row = k.b * s.dim + k.dc;
   k.rowoff = s.ts == 1 ? k.row * s.L : k.b * s.L * s.dim + k.dc;
+  k.bcg = k.b * s.ngroups + (k.gi % s.groups_per_batch) / (s.groups_per_batch / s.ngroups);
   k.tile_begin = k.seg * s.seg_tiles;
   k.tile_end = min(s.tiles, k.tile_begin + s.seg_tiles);
   return k;
@@ -170,7 +173,7 @@ __global__ void __launch_bounds__(kLanes* NG)
   const int n0 = g * NPW;
   const Task k = task_of(s, lane);
   const int64_t Lp = (int64_t)s.tiles * T;
-  const uint32_t* __restrict__ bcw = bcp + (k.b * NG + g) * Lp * WPS;
+  const uint32_t* __restrict__ bcw = bcp + (k.bcg * NG + g) * Lp * WPS;
   const bool sp = s.softplus != 0;
 
   float A2[NPW];
@@ -337,7 +340,7 @@ __global__ void __launch_bounds__(kLanes* NG)
   const Task k = task_of(s, lane);
   const int64_t task = blockIdx.x;
   const int64_t Lp = (int64_t)s.tiles * T;
-  const uint32_t* __restrict__ bcw = bcp + (k.b * NG + g) * Lp * WPS;
+  const uint32_t* __restrict__ bcw = bcp + (k.bcg * NG + g) * Lp * WPS;
   const float* __restrict__ ck = ws_ck + (int64_t)k.gi * s.tiles * N * kLanes;
   const float* __restrict__ cd = ws_cd + (int64_t)k.gi * s.tiles * kLanes;
   const bool sp = s.softplus != 0;
@@ -578,21 +581,26 @@ __global__ void __launch_bounds__(256)
                       float* __restrict__ dC, float* __restrict__ dA,
                       float* __restrict__ dD, float* __restrict__ dbias,
                       int64_t batch, int64_t dim, int64_t L, int64_t Lp, int N,
-                      int gpb, int segments) {
+                      int gpb, int segments, int groups) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t n_bc = batch * L * 2 * N;
+  const int64_t n_bc = batch * L * groups * 2 * N;
   if (i < n_bc) {
+    // i -> (b, t, group, q, n) with n fastest; the group's channel groups
+    // are gpb / groups consecutive ones
     const int n = (int)(i % N);
     int64_t r = i / N;
     const int q = (int)(r % 2);
     r /= 2;
+    const int64_t grp = r % groups;
+    r /= groups;
     const int64_t t = r % L;
     const int64_t b = r / L;
-    const float* src = ws_dbc + ((b * gpb) * Lp + t) * (2 * N) + q * N + n;
+    const int per = gpb / groups;
+    const float* src = ws_dbc + ((b * gpb + grp * per) * Lp + t) * (2 * N) + q * N + n;
     const int64_t stride = Lp * 2 * N;
     float acc = 0.0f;
-    for (int k = 0; k < gpb; ++k) acc += src[k * stride];
-    (q ? dC : dB)[(b * L + t) * N + n] = acc;
+    for (int k = 0; k < per; ++k) acc += src[k * stride];
+    (q ? dC : dB)[((b * L + t) * groups + grp) * N + n] = acc;
     return;
   }
   i -= n_bc;
@@ -658,23 +666,25 @@ hipError_t launch_n(const BwdParams& p, hipStream_t st) {
   s.dim = p.dim;
   s.L = p.L;
   s.ts = p.layout_bld ? p.dim : 1;
+  s.ngroups = p.ngroups > 1 ? p.ngroups : 1;
+  s.reserved = 0;
   s.groups_per_batch = p.groups_per_batch;
   s.tiles = p.tiles;
   s.segments = p.segments;
   s.seg_tiles = p.seg_tiles;
   s.softplus = p.softplus;
   s.batch = (int32_t)p.batch;
-  hipError_t e = launch_bc_pack(p.B, p.C, p.ws_bc, p.batch, p.L, Lp, N, NG,
-                                BF16, BF16, Lp * WPS, st);
+  hipError_t e = launch_bc_pack(p.B, p.C, p.ws_bc, p.batch, s.ngroups, p.L, Lp, N,
+                                NG, BF16, BF16, Lp * WPS, st);
   if (e != hipSuccess) return e;
   e = p.z ? launch_passes<N, BF16, VEC, true>(p, s, st)
           : launch_passes<N, BF16, VEC, false>(p, s, st);
   if (e != hipSuccess) return e;
-  const int64_t threads = p.batch * p.L * 2 * N + p.dim * N + p.dim;
+  const int64_t threads = p.batch * p.L * s.ngroups * 2 * N + p.dim * N + p.dim;
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((threads + 255) / 256)),
                      dim3(256), 0, st, p.ws_dbc, p.ws_dA, p.ws_dDb, p.dB, p.dC,
                      p.dA, p.dD, p.dbias, p.batch, p.dim, p.L, Lp, N,
-                     p.groups_per_batch, p.segments);
+                     p.groups_per_batch, p.segments, s.ngroups);
   return hipGetLastError();
 }
 
@@ -726,7 +736,7 @@ int bwd_segments(int64_t groups, int64_t tiles, int cus, int forced) {
 }
 
 int64_t bwd_workspace(int64_t batch, int64_t dim, int64_t L, int N, bool bf16,
-                      int segments, void* ws, BwdParams* p) {
+                      int segments, int64_t groups, void* ws, BwdParams* p) {
   const int NG = bwd_waves_per_group(N);
   const int npw = N / NG;
   const int wps = bf16 ? npw : 2 * npw;
@@ -736,7 +746,7 @@ int64_t bwd_workspace(int64_t batch, int64_t dim, int64_t L, int N, bool bf16,
   const int64_t G = batch * gpb;
   const int64_t tasks = G * segments;
   const int64_t sizes[12] = {
-      batch * NG * Lp * wps * 4,        // packed B/C runs
+      batch * groups * NG * Lp * wps * 4,  // packed B/C runs
       G * tiles * N * kLanes * 4,       // tile checkpoints
       G * tiles * kLanes * 4,           // running sums of Delta at tiles
       tasks * N * kLanes * 4,           // segment end states

@@ -12,22 +12,24 @@ namespace fwd {
 // hold fp32.
 __global__ void __launch_bounds__(256)
     bc_pack_kernel(const void* __restrict__ Bm, const void* __restrict__ Cm,
-                   void* __restrict__ packed, int64_t batch, int64_t L,
-                   int64_t steps, int N, int NG, int src_bf16, int dst_bf16,
-                   int64_t run_words) {
+                   void* __restrict__ packed, int64_t batch, int64_t groups,
+                   int64_t L, int64_t steps, int N, int NG, int src_bf16,
+                   int dst_bf16, int64_t run_words) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = batch * steps * 2 * N;
+  const int64_t total = batch * groups * steps * 2 * N;
   if (i >= total) return;
   const int npw = N / NG;
-  // i indexes the values in order [b][g][t][j], j < 2*npw
+  // i indexes the values in order [b][group][wave][t][j], j < 2*npw
   const int j = (int)(i % (2 * npw));
   const int64_t r = i / (2 * npw);
   const int64_t t = r % steps;
-  const int64_t bg = r / steps;
+  const int64_t bg = r / steps;           // run: (b * groups + group) * NG + wave
   const int g = (int)(bg % NG);
-  const int64_t b = bg / NG;
+  const int64_t bgrp = bg / NG;
+  const int64_t grp = bgrp % groups;
+  const int64_t b = bgrp / groups;
   const int n = g * npw + (j < npw ? j : j - npw);
-  const int64_t src = (b * L + t) * N + n;
+  const int64_t src = ((b * L + t) * groups + grp) * N + n;
   const void* m = j < npw ? Bm : Cm;
   const int64_t vals_per_word = dst_bf16 ? 2 : 1;
   const int64_t dst = bg * run_words * vals_per_word + t * 2 * npw + j;
@@ -88,13 +90,13 @@ hipError_t launch_combine(const ScanParams& p, const ScanShape& s, int N,
 }  // namespace fwd
 
 hipError_t launch_bc_pack(const void* B, const void* C, void* packed,
-                          int64_t batch, int64_t L, int64_t steps, int N,
-                          int waves, bool src_bf16, bool dst_bf16,
+                          int64_t batch, int64_t groups, int64_t L, int64_t steps,
+                          int N, int waves, bool src_bf16, bool dst_bf16,
                           int64_t run_words, hipStream_t stream) {
-  const int64_t total = batch * steps * 2 * N;
+  const int64_t total = batch * groups * steps * 2 * N;
   hipLaunchKernelGGL(fwd::bc_pack_kernel, dim3((unsigned)((total + 255) / 256)),
-                     dim3(256), 0, stream, B, C, packed, batch, L, steps, N,
-                     waves, src_bf16 ? 1 : 0, dst_bf16 ? 1 : 0, run_words);
+                     dim3(256), 0, stream, B, C, packed, batch, groups, L, steps,
+                     N, waves, src_bf16 ? 1 : 0, dst_bf16 ? 1 : 0, run_words);
   return hipGetLastError();
 }
 

@@ -62,6 +62,7 @@ struct ScanShape {
   int64_t dim, L;
   int64_t ts;  // elements between consecutive timesteps of a row: 1, or dim
                // for the (batch, length, channel) layout
+  int32_t ngroups, groups_per_bc;  // B/C groups; channel groups per B/C group
   int32_t softplus, load_state;
   int32_t groups_per_batch, whole_groups, segments;
   int64_t seg_len;
@@ -206,7 +207,8 @@ __device__ __forceinline__ void scan_body(
   };
 
   // this wave's packed B/C run
-  const uint32_t* __restrict__ bcw = bcp + (b * NG + g) * bc_run_words(s.L, WPS);
+  const int64_t bcg = b * s.ngroups + (gi % s.groups_per_batch) / s.groups_per_bc;
+  const uint32_t* __restrict__ bcw = bcp + (bcg * NG + g) * bc_run_words(s.L, WPS);
   using Batch = BCBatch<NPW, BF16>;
   Raw<BF16, KC> ru, rd, rz, nu, nd, nz;
   raw_zero(rz);
@@ -454,6 +456,8 @@ hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
   s.dim = p.dim;
   s.L = p.L;
   s.ts = p.layout_bld ? p.dim : 1;
+  s.ngroups = p.ngroups > 1 ? p.ngroups : 1;
+  s.groups_per_bc = p.groups_per_batch / s.ngroups;
   s.softplus = p.softplus;
   s.load_state = p.load_state;
   s.groups_per_batch = p.groups_per_batch;
@@ -463,8 +467,8 @@ hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
   hipError_t e;
   {
     constexpr int WPS = BCLayout<N / NG, BF16>::kWordsPerStep;
-    e = launch_bc_pack(p.B, p.C, p.ws_bc, p.batch, p.L, p.L, N, NG, BF16, BF16,
-                       bc_run_words(p.L, WPS), stream);
+    e = launch_bc_pack(p.B, p.C, p.ws_bc, p.batch, s.ngroups, p.L, p.L, N, NG, BF16,
+                       BF16, bc_run_words(p.L, WPS), stream);
     if (e != hipSuccess) return e;
   }
   if (p.split_groups > 0 && p.whole_groups > 0 && p.side_stream) {

@@ -21,6 +21,7 @@ namespace {
 struct UpdateShape {
   int64_t batch, dim;
   int32_t softplus;
+  int32_t ngroups;  // B, C are (batch, ngroups, N); channel d reads d / (dim / ngroups)
 };
 
 template <bool BF16>
@@ -62,6 +63,7 @@ __global__ void __launch_bounds__(256)
   const int64_t b = r / s.dim;
   const int64_t d = r - b * s.dim;
   const int n0 = part * NPL;
+  const int64_t bc = (b * s.ngroups + d / (s.dim / s.ngroups)) * N;  // this row's B, C
 
   const float xv = load_io<BF16>(x, r);
   const float xr = load_io<BF16>(dt, r) + (bias ? bias[d] : 0.0f);
@@ -91,8 +93,8 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
   for (int n = 0; n < NPL; ++n) {
     const float e = hw_exp2(dl * (a[n] * kLog2e));
-    h[n] = fmaf(e, h[n], w * load_io<BF16>(Bm, b * N + n0 + n));
-    y = fmaf(load_io<BF16>(Cm, b * N + n0 + n), h[n], y);
+    h[n] = fmaf(e, h[n], w * load_io<BF16>(Bm, bc + n0 + n));
+    y = fmaf(load_io<BF16>(Cm, bc + n0 + n), h[n], y);
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off /= 2) y += __shfl_xor(y, off);
@@ -119,7 +121,7 @@ __global__ void __launch_bounds__(256)
 
 template <int N, bool BF16, bool VEC>
 hipError_t launch_u(const UpdateParams& p, hipStream_t stream) {
-  UpdateShape s{p.batch, p.dim, p.softplus};
+  UpdateShape s{p.batch, p.dim, p.softplus, p.ngroups > 1 ? p.ngroups : 1};
   const int64_t threads = p.batch * p.dim * kLanesPerRow<N>;
   const dim3 grid((unsigned)((threads + 255) / 256));
   if (p.z)

@@ -47,9 +47,9 @@ def test_version_and_strings(L):
     assert L.mssm_last_error() is not None
 
 
-def _dims(batch=2, dim=64, N=16, L_=128, io=1, flags=0, ts=0, reserved=0):
+def _dims(batch=2, dim=64, N=16, L_=128, io=1, flags=0, ts=0, groups=0):
     from selective_state_space_52_amd._lib import Dims
-    return Dims(batch, dim, N, L_, io, flags, ts, reserved)
+    return Dims(batch, dim, N, L_, io, flags, ts, groups)
 
 
 BASE = 1 << 40
@@ -82,7 +82,9 @@ def test_fwd_validation_codes(L):
     assert _fwd(L, _dims(N=48)) == -3
     assert _fwd(L, _dims(io=7)) == -3
     assert _fwd(L, _dims(flags=4)) == -3                    # unknown flag
-    assert _fwd(L, _dims(reserved=1)) == -3
+    assert _fwd(L, _dims(groups=-1)) == -2
+    assert _fwd(L, _dims(dim=192, groups=2)) == -3         # 96 channels per group
+    assert _fwd(L, _dims(dim=64, groups=3)) == -3
     assert _fwd(L, _dims(L_=1 << 40)) == -2                 # overflow / too long
     # bf16 pointers need 2-byte alignment, fp32 ones 4-byte alignment
     assert _fwd(L, _dims(io=1), u=BASE + 1) == -4

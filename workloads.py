@@ -162,6 +162,17 @@ def make_scan_grads(s: ScanSpec, seed_offset: int = 104729) -> dict:
     return dict(dout=dout, dlast=dlast)
 
 
+def make_group_bc(s: ScanSpec, groups: int, seed_offset: int = 3571) -> dict:
+    """io-dtype B, C (batch, L, groups, N) ~ N(0, 1) for G B/C groups (channel
+    d reads group d // (dim // groups)); draws from default_rng([seed,
+    seed_offset]), B then C."""
+    rng = np.random.default_rng([s.seed, seed_offset])
+    shp = (s.batch, s.seqlen, groups, s.dstate)
+    B = _round_io(rng.standard_normal(shp, dtype=np.float32), s.io)
+    C = _round_io(rng.standard_normal(shp, dtype=np.float32), s.io)
+    return dict(B=B, C=C)
+
+
 def make_conv_params(s: ScanSpec, width: int = 4, seed_offset: int = 7717) -> dict:
     """fp32 weight (dim, width) and bias (dim) ~ U(-1/2, 1/2), and io-dtype
     init (batch, dim, width - 1) ~ N(0, 1), for the causal conv."""
