@@ -9,11 +9,12 @@
 //   out    = (sum_n C[b,n] h[n] + D[d] x) * silu(z)
 //
 // The step is bound by HBM: the fp32 state (64 B per row at N = 16) is read
-// and written once and dominates the bytes.  One lane owns one row (N / 16
-// lanes above N = 16); the lanes of a wave own consecutive rows, so the state
-// is streamed with 16-byte accesses that together cover contiguous memory.
+// and written once and dominates the bytes.  Rows go to consecutive lanes
+// (N / 4 lanes per row from N = 8 on), so the state is streamed with 16-byte
+// accesses that cover contiguous memory.
 #include "dev_math.h"
 #include "mssm_internal.h"
+#include "scan_common.h"
 
 namespace mssm {
 namespace {
@@ -32,11 +33,12 @@ __device__ __forceinline__ float load_io(const void* base, int64_t i) {
     return static_cast<const float*>(base)[i];
 }
 
-// Lanes per row: one up to N = 16; above, N / 16 lanes each own 16 states of
-// the row (consecutive lanes, consecutive 64-byte pieces of the state), and
-// their partial readouts are summed across those lanes.
+// Lanes per row: from N = 8 on, N / 4 lanes each own 4 states of the row, so
+// consecutive lanes read consecutive 16-byte pieces of the state and one
+// load instruction of a wave covers 1 KB of contiguous memory; the partial
+// readouts are summed across the row's lanes.  Below N = 8, one lane per row.
 template <int N>
-constexpr int kLanesPerRow = N > 16 ? N / 16 : 1;
+constexpr int kLanesPerRow = N >= 8 ? N / 4 : 1;
 
 template <int N, bool BF16, bool VEC, bool HAS_Z>
 __global__ void __launch_bounds__(256)
@@ -89,12 +91,32 @@ __global__ void __launch_bounds__(256)
     }
   }
 
+  // this lane's B and C values: the same for every row of a group, read as
+  // 16-byte pieces where the layout allows (one load instead of 8 or 4)
+  float bv[NPL], cvv[NPL];
+  if constexpr (VEC && (BF16 ? NPL >= 2 : true)) {
+    Raw<BF16, NPL> rb, rc;
+    load_chunk<BF16, true, NPL>(rb, Bm, bc + n0, NPL);
+    load_chunk<BF16, true, NPL>(rc, Cm, bc + n0, NPL);
+#pragma unroll
+    for (int n = 0; n < NPL; ++n) {
+      bv[n] = raw_get(rb, n);
+      cvv[n] = raw_get(rc, n);
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < NPL; ++n) {
+      bv[n] = load_io<BF16>(Bm, bc + n0 + n);
+      cvv[n] = load_io<BF16>(Cm, bc + n0 + n);
+    }
+  }
+
   float y = 0.0f;
 #pragma unroll
   for (int n = 0; n < NPL; ++n) {
     const float e = hw_exp2(dl * (a[n] * kLog2e));
-    h[n] = fmaf(e, h[n], w * load_io<BF16>(Bm, bc + n0 + n));
-    y = fmaf(load_io<BF16>(Cm, bc + n0 + n), h[n], y);
+    h[n] = fmaf(e, h[n], w * bv[n]);
+    y = fmaf(cvv[n], h[n], y);
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off /= 2) y += __shfl_xor(y, off);
@@ -137,7 +159,10 @@ hipError_t launch_u(const UpdateParams& p, hipStream_t stream) {
 
 template <int N>
 hipError_t launch_un(const UpdateParams& p, bool bf16, hipStream_t stream) {
-  const bool vec = ((uintptr_t)p.state % 16 == 0) && ((uintptr_t)p.A % 16 == 0);
+  // 16-byte pieces: the state and A rows, and the B / C rows (their starts
+  // are multiples of N values, so 16-byte aligned bases keep them aligned)
+  const bool vec = ((uintptr_t)p.state % 16 == 0) && ((uintptr_t)p.A % 16 == 0) &&
+                   ((uintptr_t)p.B % 16 == 0) && ((uintptr_t)p.C % 16 == 0);
   if (bf16)
     return vec ? launch_u<N, true, true>(p, stream)
                : launch_u<N, true, false>(p, stream);
