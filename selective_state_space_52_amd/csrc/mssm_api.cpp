@@ -513,7 +513,7 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
   const int64_t tiles = (L + tile - 1) / tile;
   const int segments =
       mssm::bwd_segments(batch * gpb, tiles, g_cu_count > 0 ? g_cu_count : kDefaultCUs,
-                         dims->time_segments);
+                         mssm::bwd_wgs_per_cu((int)N, io == 2), dims->time_segments);
   if (batch * gpb * segments > INT32_MAX) return MSSM_ERR_DIMS;
   mssm::BwdParams p;
   std::memset(&p, 0, sizeof(p));

@@ -173,9 +173,11 @@ hipError_t launch_scan_n128(const ScanParams&, bool, bool, hipStream_t);
 // Backward: timesteps per tile, waves per group, segments, workspace, launch.
 int bwd_tile();
 int bwd_waves_per_group(int N);
+// Pass R workgroups resident per CU (runtime occupancy query, cached).
+int bwd_wgs_per_cu(int N, bool bf16);
 // Time segments per row: `forced` (> 0) if given, else enough tasks to fill
-// the CUs in whole rounds, with segments of at least 4 tiles.
-int bwd_segments(int64_t groups, int64_t tiles, int cus, int forced);
+// the CUs' workgroup slots in whole rounds, with segments of at least 4 tiles.
+int bwd_segments(int64_t groups, int64_t tiles, int cus, int wgs_per_cu, int forced);
 // Workspace bytes of one backward call; with ws and p non-null also points
 // p's workspace fields into ws.
 int64_t bwd_workspace(int64_t batch, int64_t dim, int64_t L, int N, bool bf16,

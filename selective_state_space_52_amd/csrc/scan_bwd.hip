@@ -51,6 +51,7 @@
 // written to a per-wave LDS block and read back transposed, so each lane adds
 // 16 values and two DPP steps finish the sum.
 #include <algorithm>
+#include <atomic>
 
 #include "dev_math.h"
 #include "mssm_internal.h"
@@ -702,15 +703,51 @@ int bwd_tile() { return kT; }
 
 int bwd_waves_per_group(int N) { return N >= 4 ? N / 4 : 1; }
 
-int bwd_segments(int64_t groups, int64_t tiles, int cus, int forced) {
+namespace {
+template <int N>
+hipError_t pass_r_occupancy(bool bf16, int* blocks) {
+  constexpr int NG = kBwdWaves<N>;
+  const void* f = bf16 ? reinterpret_cast<const void*>(
+                             &bwd_pass_r_kernel<N, NG, true, true, true>)
+                       : reinterpret_cast<const void*>(
+                             &bwd_pass_r_kernel<N, NG, false, true, true>);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, f, kLanes * NG, 0);
+}
+}  // namespace
+
+int bwd_wgs_per_cu(int N, bool bf16) {
+  static std::atomic<int> cache[2][6];
+  int idx = 0;
+  while (idx < 5 && (1 << idx) < N) ++idx;
+  std::atomic<int>& slot = cache[bf16 ? 1 : 0][idx];
+  int v = slot.load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int blocks = 0;
+  hipError_t e = hipErrorInvalidValue;
+  switch (N) {
+    case 1: e = pass_r_occupancy<1>(bf16, &blocks); break;
+    case 2: e = pass_r_occupancy<2>(bf16, &blocks); break;
+    case 4: e = pass_r_occupancy<4>(bf16, &blocks); break;
+    case 8: e = pass_r_occupancy<8>(bf16, &blocks); break;
+    case 16: e = pass_r_occupancy<16>(bf16, &blocks); break;
+    case 32: e = pass_r_occupancy<32>(bf16, &blocks); break;
+    default: break;
+  }
+  v = (e == hipSuccess && blocks > 0) ? blocks : 2;
+  slot.store(v, std::memory_order_relaxed);
+  return v;
+}
+
+int bwd_segments(int64_t groups, int64_t tiles, int cus, int wgs_per_cu, int forced) {
   int64_t P = 1;
   if (forced > 0) {
     P = forced;
   } else {
-    // Pass R holds two workgroups per CU.  Take the fewest segments that give
-    // at least two full rounds of tasks with the last round at least 90%
-    // full; else the fullest last round.
-    const int64_t slots = 2 * (int64_t)std::max(cus, 1);
+    // Pass R holds wgs_per_cu workgroups per CU.  Take the fewest segments
+    // that give at least two rounds of tasks, all of them full (a last round
+    // short by even a tenth cost 6% at 320 groups x 2048 steps); else the
+    // fullest last round.
+    const int64_t slots = (int64_t)std::max(wgs_per_cu, 1) * std::max(cus, 1);
     const int64_t pmax = std::max<int64_t>(1, tiles / kMinSegTiles);
     double best = -1.0;
     for (int64_t q = 1; q <= pmax; ++q) {
@@ -719,7 +756,7 @@ int bwd_segments(int64_t groups, int64_t tiles, int cus, int forced) {
       const int64_t tasks = groups * pq;
       const int64_t rounds = (tasks + slots - 1) / slots;
       const double fill = (double)tasks / (double)(rounds * slots);
-      if (tasks >= 2 * slots && fill >= 0.9) {
+      if (tasks >= 2 * slots && fill >= 0.99) {
         P = pq;
         break;
       }

@@ -100,6 +100,10 @@ SHAPES = [
     ("bf16", 1, 64, 16, 15),
     ("bf16", 1, 64, 16, 16),
     ("bf16", 1, 64, 16, 17),
+    ("bf16", 1, 64, 16, 8),       # half a tile
+    ("bf16", 1, 64, 16, 9),
+    ("bf16", 1, 64, 4, 136),      # one wave: 16-step chunks
+    ("f32", 1, 64, 4, 72),
     ("bf16", 1, 5, 16, 40),       # fewer channels than a wave
     ("bf16", 2, 96, 1, 200),
     ("bf16", 2, 96, 2, 200),
@@ -157,6 +161,7 @@ SEGMENTS = [
     ("bf16", 1, 70, 16, 333, 5),
     ("f32", 1, 64, 16, 1000, 7),
     ("bf16", 2, 64, 8, 200, 13),    # one tile per segment
+    ("bf16", 1, 64, 16, 200, 7),    # two tiles per segment
     ("f32", 1, 40, 2, 100, 3),
     ("bf16", 1, 64, 32, 300, 4),
 ]
