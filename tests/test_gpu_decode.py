@@ -106,3 +106,42 @@ def test_decode_full_size_1000_steps():
     got = torch.stack([state[b, d] for b, d in rows])
     check_state(got, ref_state[:, 0, :], "decode sampled state after 1000 steps")
     assert torch.isfinite(state).all()
+
+
+def test_decode_64bit_indices():
+    """4100 x 4096 rows of 128 states: 2.15e9 state elements (8.6 GB), past
+    2^31, so the launch takes 64-bit indices.  Rows on both sides of element
+    2^31 and at the ends follow the oracle."""
+    import oracle
+    import selective_state_space_52_amd as m
+    batch, dim, N = 4100, 4096, 128
+    assert batch * dim * N > 2 ** 31
+    print("decode 64-bit indices: batch %d dim %d N %d" % (batch, dim, N), flush=True)
+    t = W.make_large_decode_step(batch, dim, N, device=DEV)
+    rng = np.random.default_rng(12)
+    rows = [(0, 0), (0, 4095), (4095, 4095), (4096, 0), (4096, 1), (4097, 17),
+            (4099, 4095)] + [(int(b), int(d)) for b, d in
+                             zip(rng.integers(4090, 4100, 9), rng.integers(0, 4096, 9))]
+    bi = torch.tensor([b for b, _ in rows], device=DEV)
+    di = torch.tensor([d for _, d in rows], device=DEV)
+    h_before = np64(t["state"][bi, di].cpu())
+    out = m.selective_state_update(t["state"], t["x"], t["dt"], t["A"], t["B"], t["C"],
+                                   D=t["D"], z=t["z"], dt_bias=t["dt_bias"])
+    torch.cuda.synchronize()
+    got_out = out[bi, di].cpu()
+    got_state = t["state"][bi, di].cpu()
+    A, D, bias = np64(t["A"].cpu()), np64(t["D"].cpu()), np64(t["dt_bias"].cpu())
+    tok = {k: np64(t[k][bi, di].cpu()) for k in ("x", "dt", "z")}
+    Bs, Cs = np64(t["B"][bi].cpu()), np64(t["C"][bi].cpu())
+    ref_out = np.empty(len(rows))
+    ref_state = np.empty((len(rows), N))
+    for i, (b, d) in enumerate(rows):
+        o1, st1 = oracle.state_update(
+            h_before[i:i + 1, None, :], tok["x"][i:i + 1, None], tok["dt"][i:i + 1, None],
+            A[d:d + 1], Bs[i:i + 1], Cs[i:i + 1], D=D[d:d + 1], z=tok["z"][i:i + 1, None],
+            dt_bias=bias[d:d + 1], softplus=True, nthreads=1)
+        ref_out[i] = o1[0, 0]
+        ref_state[i] = st1[0, 0]
+    del t
+    check_out(got_out, ref_out, "bf16", "decode 64-bit indices out")
+    check_state(got_state, ref_state, "decode 64-bit indices state")

@@ -220,6 +220,27 @@ def make_decode_params(s: DecodeSpec) -> dict:
                 dt_bias=torch.from_numpy(bias), state=torch.from_numpy(state))
 
 
+def make_large_decode_step(batch: int, dim: int, dstate: int, seed: int = 31,
+                           device="cuda") -> dict:
+    """One bf16 decode token and an fp32 state of N(0, 0.1^2) drawn directly on
+    `device` (for sizes too large to draw on the host), with A, D and dt_bias
+    as for the other workloads."""
+    A, D, bias = _params(np.random.default_rng(seed), dim, dstate)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def normal(*shape):
+        return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return dict(state=normal(batch, dim, dstate).mul_(0.1),
+                x=normal(batch, dim).to(torch.bfloat16),
+                dt=normal(batch, dim).to(torch.bfloat16),
+                z=normal(batch, dim).to(torch.bfloat16),
+                B=normal(batch, dstate).to(torch.bfloat16),
+                C=normal(batch, dstate).to(torch.bfloat16),
+                A=torch.from_numpy(A).to(device), D=torch.from_numpy(D).to(device),
+                dt_bias=torch.from_numpy(bias).to(device))
+
+
 def make_decode_token(s: DecodeSpec, k: int) -> dict:
     """Token k of the ring: io-dtype x, dt (raw), z (batch, dim) and B, C
     (batch, N)."""
