@@ -12,6 +12,8 @@
 // owns 8 consecutive timesteps of one row (16 bytes of bf16), so a wave reads
 // and writes 1 KB contiguous pieces of a row; the K-1 inputs before a
 // thread's chunk are read again from the previous piece (an L2 hit).
+#include <type_traits>
+
 #include "dev_math.h"
 #include "mssm_internal.h"
 #include "scan_common.h"
@@ -22,27 +24,37 @@ namespace {
 constexpr int kChunk = 8;  // timesteps per thread
 constexpr int kPrev = 4;   // inputs read before a chunk (>= K - 1)
 
-template <bool BF16, bool VEC, int K>
+// Idx: uint32_t when every element index fits in 31 bits (cheap division
+// by the row length), else int64_t.  Every load of a thread is issued before
+// the first use: the inputs before the chunk come from an address clamped
+// into the row (unused at the row start, where init supplies them).
+template <bool BF16, bool VEC, int K, typename Idx>
 __global__ void __launch_bounds__(256)
     causal_conv1d_kernel(const void* __restrict__ x, const float* __restrict__ w,
                          const float* __restrict__ bias,
                          const void* __restrict__ init, void* __restrict__ out,
-                         int64_t rows, int64_t dim, int64_t L, int silu) {
+                         Idx rows, Idx dim, Idx L, int silu) {
   static_assert(K >= 1 && K - 1 <= kPrev, "width");
-  const int64_t per_row = (L + kChunk - 1) / kChunk;
-  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const Idx per_row = (L + kChunk - 1) / kChunk;
+  const Idx id = (Idx)blockIdx.x * blockDim.x + threadIdx.x;
   if (id >= rows * per_row) return;
-  const int64_t row = id / per_row;
-  const int64_t t0 = (id - row * per_row) * kChunk;
-  const int64_t d = row % dim;
-  const int64_t off = row * L;
+  const Idx row = id / per_row;
+  const Idx t0 = (id - row * per_row) * kChunk;
+  const Idx d = row % dim;
+  const Idx off = row * L;
 
   Raw<BF16, kChunk> rx;
-  load_chunk<BF16, VEC, kChunk>(rx, x, off + t0, L - t0);
+  Raw<BF16, kPrev> rp;
+  load_chunk<BF16, VEC, kChunk>(rx, x, (int64_t)(off + t0), (int64_t)(L - t0));
+  const Idx tp = t0 >= kPrev ? t0 - kPrev : 0;
+  load_chunk<BF16, VEC, kPrev>(rp, x, (int64_t)(off + tp), (int64_t)(L - tp));
+  float wk[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) wk[j] = w[d * K + j];
+  const float b = bias ? bias[d] : 0.0f;
+
   float xs[kPrev + kChunk];
   if (t0 >= kPrev) {
-    Raw<BF16, kPrev> rp;
-    load_chunk<BF16, VEC, kPrev>(rp, x, off + t0 - kPrev, kPrev);
 #pragma unroll
     for (int j = 0; j < kPrev; ++j) xs[j] = raw_get(rp, j);
   } else {
@@ -52,7 +64,7 @@ __global__ void __launch_bounds__(256)
     if (init) {
 #pragma unroll
       for (int j = 0; j < K - 1; ++j) {
-        const int64_t i = row * (K - 1) + j;
+        const Idx i = row * (K - 1) + j;
         xs[kPrev - (K - 1) + j] =
             BF16 ? bf16_bits(static_cast<const uint16_t*>(init)[i])
                  : static_cast<const float*>(init)[i];
@@ -62,10 +74,6 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
   for (int k = 0; k < kChunk; ++k) xs[kPrev + k] = raw_get(rx, k);
 
-  float wk[K];
-#pragma unroll
-  for (int j = 0; j < K; ++j) wk[j] = w[d * K + j];
-  const float b = bias ? bias[d] : 0.0f;
   float o[kChunk];
 #pragma unroll
   for (int k = 0; k < kChunk; ++k) {
@@ -74,35 +82,36 @@ __global__ void __launch_bounds__(256)
     for (int j = 0; j < K; ++j) v = fmaf(wk[j], xs[kPrev + k - (K - 1) + j], v);
     o[k] = silu ? silu_f32(v) : v;
   }
-  store_chunk<BF16, VEC, kChunk>(out, off + t0, o, L - t0);
+  store_chunk<BF16, VEC, kChunk>(out, (int64_t)(off + t0), o, (int64_t)(L - t0));
 }
 
 // The (batch, length, channel) layout: consecutive threads own consecutive
 // channels of the same kChunk timesteps, so every load and store of a wave
 // is one contiguous piece of a timestep's channels.
-template <bool BF16, int K>
+template <bool BF16, int K, typename Idx>
 __global__ void __launch_bounds__(256)
     causal_conv1d_bld_kernel(const void* __restrict__ x, const float* __restrict__ w,
                              const float* __restrict__ bias,
                              const void* __restrict__ init, void* __restrict__ out,
-                             int64_t batch, int64_t dim, int64_t L, int silu) {
-  const int64_t chunks = (L + kChunk - 1) / kChunk;
-  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+                             Idx batch, Idx dim, Idx L, int silu) {
+  using SIdx = typename std::make_signed<Idx>::type;
+  const Idx chunks = (L + kChunk - 1) / kChunk;
+  const Idx id = (Idx)blockIdx.x * blockDim.x + threadIdx.x;
   if (id >= batch * chunks * dim) return;
-  const int64_t d = id % dim;
-  const int64_t r = id / dim;
-  const int64_t c = r % chunks;
-  const int64_t b = r / chunks;
-  const int64_t t0 = c * kChunk;
-  auto at = [&](int64_t t) -> float {  // x at step t of channel d, t >= -(K-1)
-    if (t >= L) return 0.0f;
+  const Idx d = id % dim;
+  const Idx r = id / dim;
+  const Idx c = r % chunks;
+  const Idx b = r / chunks;
+  const SIdx t0 = (SIdx)(c * kChunk);
+  auto at = [&](SIdx t) -> float {  // x at step t of channel d, t >= -(K-1)
+    if (t >= (SIdx)L) return 0.0f;
     if (t >= 0) {
-      const int64_t i = (b * L + t) * dim + d;
+      const Idx i = (b * L + (Idx)t) * dim + d;
       return BF16 ? bf16_bits(static_cast<const uint16_t*>(x)[i])
                   : static_cast<const float*>(x)[i];
     }
     if (!init) return 0.0f;
-    const int64_t i = (b * dim + d) * (K - 1) + (K - 1) + t;
+    const Idx i = (Idx)((SIdx)((b * dim + d) * (K - 1) + (K - 1)) + t);
     return BF16 ? bf16_bits(static_cast<const uint16_t*>(init)[i])
                 : static_cast<const float*>(init)[i];
   };
@@ -115,12 +124,12 @@ __global__ void __launch_bounds__(256)
   const float bb = bias ? bias[d] : 0.0f;
 #pragma unroll
   for (int k = 0; k < kChunk; ++k) {
-    if (t0 + k >= L) break;
+    if (t0 + k >= (SIdx)L) break;
     float v = bb;
 #pragma unroll
     for (int j = 0; j < K; ++j) v = fmaf(wk[j], xs[k + j], v);
     v = silu ? silu_f32(v) : v;
-    const int64_t i = (b * L + t0 + k) * dim + d;
+    const Idx i = (b * L + (Idx)t0 + k) * dim + d;
     if constexpr (BF16)
       static_cast<uint16_t*>(out)[i] = to_bf16(v);
     else
@@ -128,23 +137,24 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-template <bool BF16>
+template <bool BF16, typename Idx>
 hipError_t launch_bld(const ConvParams& p, hipStream_t st) {
   const int64_t chunks = (p.L + kChunk - 1) / kChunk;
   const int64_t threads = p.batch * chunks * p.dim;
   const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  const Idx batch = (Idx)p.batch, dim = (Idx)p.dim, L = (Idx)p.L;
   switch (p.width) {
     case 2:
-      hipLaunchKernelGGL((causal_conv1d_bld_kernel<BF16, 2>), grid, block, 0, st, p.x,
-                         p.w, p.bias, p.init, p.out, p.batch, p.dim, p.L, p.silu);
+      hipLaunchKernelGGL((causal_conv1d_bld_kernel<BF16, 2, Idx>), grid, block, 0, st,
+                         p.x, p.w, p.bias, p.init, p.out, batch, dim, L, p.silu);
       break;
     case 3:
-      hipLaunchKernelGGL((causal_conv1d_bld_kernel<BF16, 3>), grid, block, 0, st, p.x,
-                         p.w, p.bias, p.init, p.out, p.batch, p.dim, p.L, p.silu);
+      hipLaunchKernelGGL((causal_conv1d_bld_kernel<BF16, 3, Idx>), grid, block, 0, st,
+                         p.x, p.w, p.bias, p.init, p.out, batch, dim, L, p.silu);
       break;
     case 4:
-      hipLaunchKernelGGL((causal_conv1d_bld_kernel<BF16, 4>), grid, block, 0, st, p.x,
-                         p.w, p.bias, p.init, p.out, p.batch, p.dim, p.L, p.silu);
+      hipLaunchKernelGGL((causal_conv1d_bld_kernel<BF16, 4, Idx>), grid, block, 0, st,
+                         p.x, p.w, p.bias, p.init, p.out, batch, dim, L, p.silu);
       break;
     default:
       return hipErrorInvalidValue;
@@ -152,38 +162,54 @@ hipError_t launch_bld(const ConvParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, typename Idx>
 hipError_t launch_k(const ConvParams& p, hipStream_t st) {
   const int64_t per_row = (p.L + kChunk - 1) / kChunk;
   const int64_t threads = p.batch * p.dim * per_row;
   const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
-  const int64_t rows = p.batch * p.dim;
+  const Idx rows = (Idx)(p.batch * p.dim), dim = (Idx)p.dim, L = (Idx)p.L;
   switch (p.width) {
     case 2:
-      hipLaunchKernelGGL((causal_conv1d_kernel<BF16, VEC, 2>), grid, block, 0, st,
-                         p.x, p.w, p.bias, p.init, p.out, rows, p.dim, p.L, p.silu);
+      hipLaunchKernelGGL((causal_conv1d_kernel<BF16, VEC, 2, Idx>), grid, block, 0, st,
+                         p.x, p.w, p.bias, p.init, p.out, rows, dim, L, p.silu);
       break;
     case 3:
-      hipLaunchKernelGGL((causal_conv1d_kernel<BF16, VEC, 3>), grid, block, 0, st,
-                         p.x, p.w, p.bias, p.init, p.out, rows, p.dim, p.L, p.silu);
+      hipLaunchKernelGGL((causal_conv1d_kernel<BF16, VEC, 3, Idx>), grid, block, 0, st,
+                         p.x, p.w, p.bias, p.init, p.out, rows, dim, L, p.silu);
       break;
     case 4:
-      hipLaunchKernelGGL((causal_conv1d_kernel<BF16, VEC, 4>), grid, block, 0, st,
-                         p.x, p.w, p.bias, p.init, p.out, rows, p.dim, p.L, p.silu);
+      hipLaunchKernelGGL((causal_conv1d_kernel<BF16, VEC, 4, Idx>), grid, block, 0, st,
+                         p.x, p.w, p.bias, p.init, p.out, rows, dim, L, p.silu);
       break;
     default:
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// 32-bit indices when every element index (and the grid's thread index, a
+// chunk of kChunk elements per thread) stays below 2^31.
+bool small_indices(const ConvParams& p) {
+  const int64_t elems = p.batch * p.dim * (p.L + kChunk);
+  return elems + 256 * kChunk < (int64_t(1) << 31);
 }
 
 }  // namespace
 
 hipError_t launch_causal_conv1d(const ConvParams& p, bool bf16, bool vec,
                                 hipStream_t st) {
-  if (p.layout_bld) return bf16 ? launch_bld<true>(p, st) : launch_bld<false>(p, st);
-  if (bf16) return vec ? launch_k<true, true>(p, st) : launch_k<true, false>(p, st);
-  return vec ? launch_k<false, true>(p, st) : launch_k<false, false>(p, st);
+  if (small_indices(p)) {
+    if (p.layout_bld)
+      return bf16 ? launch_bld<true, uint32_t>(p, st) : launch_bld<false, uint32_t>(p, st);
+    if (bf16)
+      return vec ? launch_k<true, true, uint32_t>(p, st) : launch_k<true, false, uint32_t>(p, st);
+    return vec ? launch_k<false, true, uint32_t>(p, st) : launch_k<false, false, uint32_t>(p, st);
+  }
+  if (p.layout_bld)
+    return bf16 ? launch_bld<true, int64_t>(p, st) : launch_bld<false, int64_t>(p, st);
+  if (bf16)
+    return vec ? launch_k<true, true, int64_t>(p, st) : launch_k<true, false, int64_t>(p, st);
+  return vec ? launch_k<false, true, int64_t>(p, st) : launch_k<false, false, int64_t>(p, st);
 }
 
 }  // namespace mssm
