@@ -572,55 +572,66 @@ __global__ void __launch_bounds__(kLanes* NG)
 }
 
 // ---------------------------------------------------------------- reduce ---
+// Sum of count values stride apart, added in index order; the loads of 8
+// terms are issued before they are added, so a thread waits once per 8.
+template <typename Idx>
+__device__ __forceinline__ float strided_sum(const float* __restrict__ p, Idx stride,
+                                             int count) {
+  float acc = 0.0f;
+  int k = 0;
+  for (; k + 8 <= count; k += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = p[(Idx)(k + j) * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += v[j];
+  }
+  for (; k < count; ++k) acc += p[(Idx)k * stride];
+  return acc;
+}
+
 // dB, dC: sum of the channel groups' sums; dA, dD, dbias: sum over segments
-// and the batch.  Every output element is one thread adding its terms in a
-// fixed order.
+// and the batch (partial k = segment * batch + b sits k * dim rows in).
+// Every output element is one thread adding its terms in a fixed order.
+template <int N, typename Idx>
 __global__ void __launch_bounds__(256)
     bwd_reduce_kernel(const float* __restrict__ ws_dbc,
                       const float* __restrict__ ws_dA,
                       const float* __restrict__ ws_dDb, float* __restrict__ dB,
                       float* __restrict__ dC, float* __restrict__ dA,
                       float* __restrict__ dD, float* __restrict__ dbias,
-                      int64_t batch, int64_t dim, int64_t L, int64_t Lp, int N,
-                      int gpb, int segments, int groups) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t n_bc = batch * L * groups * 2 * N;
+                      Idx batch, Idx dim, Idx L, Idx Lp, int gpb, int segments,
+                      int groups) {
+  Idx i = (Idx)blockIdx.x * blockDim.x + threadIdx.x;
+  const Idx n_bc = batch * L * (Idx)groups * 2 * N;
   if (i < n_bc) {
     // i -> (b, t, group, q, n) with n fastest; the group's channel groups
     // are gpb / groups consecutive ones
-    const int n = (int)(i % N);
-    int64_t r = i / N;
-    const int q = (int)(r % 2);
+    const Idx n = i % N;
+    Idx r = i / N;
+    const Idx q = r % 2;
     r /= 2;
-    const int64_t grp = r % groups;
-    r /= groups;
-    const int64_t t = r % L;
-    const int64_t b = r / L;
+    const Idx grp = r % (Idx)groups;
+    r /= (Idx)groups;
+    const Idx t = r % L;
+    const Idx b = r / L;
     const int per = gpb / groups;
-    const float* src = ws_dbc + ((b * gpb + grp * per) * Lp + t) * (2 * N) + q * N + n;
-    const int64_t stride = Lp * 2 * N;
-    float acc = 0.0f;
-    for (int k = 0; k < per; ++k) acc += src[k * stride];
-    (q ? dC : dB)[((b * L + t) * groups + grp) * N + n] = acc;
+    const float* src =
+        ws_dbc + ((b * (Idx)gpb + grp * (Idx)per) * Lp + t) * (2 * N) + q * N + n;
+    const float acc = strided_sum<Idx>(src, Lp * 2 * N, per);
+    (q ? dC : dB)[((b * L + t) * (Idx)groups + grp) * N + n] = acc;
     return;
   }
   i -= n_bc;
-  const int64_t rows = batch * dim;
+  const int parts = segments * (int)batch;
   if (i < dim * N) {
-    float acc = 0.0f;
-    for (int sg = 0; sg < segments; ++sg)
-      for (int64_t b = 0; b < batch; ++b) acc += ws_dA[(sg * rows + b * dim) * N + i];
-    dA[i] = acc;
+    dA[i] = strided_sum<Idx>(ws_dA + i, dim * N, parts);
     return;
   }
   i -= dim * N;
   if (i < dim) {
-    float aD = 0.0f, ab = 0.0f;
-    for (int sg = 0; sg < segments; ++sg)
-      for (int64_t b = 0; b < batch; ++b) {
-        aD += ws_dDb[(sg * rows + b * dim + i) * 2 + 0];
-        ab += ws_dDb[(sg * rows + b * dim + i) * 2 + 1];
-      }
+    const float aD = strided_sum<Idx>(ws_dDb + i * 2 + 0, dim * 2, parts);
+    const float ab = strided_sum<Idx>(ws_dDb + i * 2 + 1, dim * 2, parts);
     if (dD) dD[i] = aD;
     if (dbias) dbias[i] = ab;
   }
@@ -682,10 +693,22 @@ hipError_t launch_n(const BwdParams& p, hipStream_t st) {
           : launch_passes<N, BF16, VEC, false>(p, s, st);
   if (e != hipSuccess) return e;
   const int64_t threads = p.batch * p.L * s.ngroups * 2 * N + p.dim * N + p.dim;
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((threads + 255) / 256)),
-                     dim3(256), 0, st, p.ws_dbc, p.ws_dA, p.ws_dDb, p.dB, p.dC,
-                     p.dA, p.dD, p.dbias, p.batch, p.dim, p.L, Lp, N,
-                     p.groups_per_batch, p.segments, s.ngroups);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  // 32-bit indices when the largest workspace index and the thread count
+  // stay below 2^31
+  const int64_t G = p.batch * p.groups_per_batch;
+  const int64_t top = std::max({G * Lp * 2 * N, (int64_t)p.segments * p.batch * p.dim * N,
+                                (int64_t)p.segments * p.batch * p.dim * 2, threads + 256});
+  if (top < (int64_t(1) << 31))
+    hipLaunchKernelGGL((bwd_reduce_kernel<N, uint32_t>), grid, dim3(256), 0, st,
+                       p.ws_dbc, p.ws_dA, p.ws_dDb, p.dB, p.dC, p.dA, p.dD, p.dbias,
+                       (uint32_t)p.batch, (uint32_t)p.dim, (uint32_t)p.L, (uint32_t)Lp,
+                       p.groups_per_batch, p.segments, s.ngroups);
+  else
+    hipLaunchKernelGGL((bwd_reduce_kernel<N, int64_t>), grid, dim3(256), 0, st,
+                       p.ws_dbc, p.ws_dA, p.ws_dDb, p.dB, p.dC, p.dA, p.dD, p.dbias,
+                       p.batch, p.dim, p.L, Lp, p.groups_per_batch, p.segments,
+                       s.ngroups);
   return hipGetLastError();
 }
 
