@@ -123,6 +123,40 @@ class Oracle:
             raise ValueError("oracle: unsupported dstate %d or groups %d" % (N, G))
         return out, last
 
+    def mamba2_scan(self, x, dt, A, B, C, D=None, z=None, dt_bias=None,
+                    softplus=True, h0=None, nthreads=None):
+        """The Mamba-2 block's scan in fp64, as the selective scan above with
+        one A value, one step and one D per head (page "Mamba: Selective State
+        Space Models", "Use the Mamba2 block", names the block and its state
+        sizes; the per-head structure is the Mamba-2 architecture's).
+
+        x, z: (batch, L, H, P) with headdim P; dt: (batch, L, H); A, D,
+        dt_bias: (H,); B, C: (batch, L, G, N), heads h // (H // G) reading
+        group g; h0: (batch, H * P, N) or None.  Channel d = h * P + p of the
+        selective scan gets A[h] for every state, step dt[.., h] and D[h].
+        Returns (out (batch, L, H, P), last_state (batch, H * P, N)), fp64.
+        """
+        x, dt, A, B, C = map(_f64, (x, dt, A, B, C))
+        D, z, dt_bias, h0 = map(_f64, (D, z, dt_bias, h0))
+        batch, L, H, P = x.shape
+        G, N = B.shape[2], B.shape[3]
+        assert dt.shape == (batch, L, H) and A.shape == (H,)
+        assert B.shape == C.shape == (batch, L, G, N) and H % G == 0
+        assert z is None or z.shape == x.shape
+        dim = H * P
+
+        def channels(a):   # (batch, L, H, P) -> (batch, dim, L)
+            return np.ascontiguousarray(a.reshape(batch, L, dim).transpose(0, 2, 1))
+        u = channels(x)
+        delta = np.ascontiguousarray(np.repeat(dt, P, axis=2).transpose(0, 2, 1))
+        A_full = np.repeat(A, P)[:, None] * np.ones((1, N))
+        out, last = self.scan(
+            u, delta, A_full, B, C,
+            D=None if D is None else np.repeat(D, P), z=None if z is None else channels(z),
+            delta_bias=None if dt_bias is None else np.repeat(dt_bias, P),
+            softplus=softplus, h0=h0, nthreads=nthreads)
+        return np.ascontiguousarray(out.transpose(0, 2, 1).reshape(batch, L, H, P)), last
+
     def scan_row(self, u, delta, A_row, B_b, C_b, D_d=0.0, z=None, bias_d=0.0,
                  softplus=True, h0=None):
         """One (batch, channel) row in fp64: u, delta, z of length L; A_row
@@ -249,3 +283,8 @@ def scan_bwd(*args, **kwargs):
 def causal_conv1d(*args, **kwargs):
     """Causal depthwise convolution in fp64 (see Oracle.causal_conv1d)."""
     return _get().causal_conv1d(*args, **kwargs)
+
+
+def mamba2_scan(*args, **kwargs):
+    """The Mamba-2 block's scan in fp64 (see Oracle.mamba2_scan)."""
+    return _get().mamba2_scan(*args, **kwargs)

@@ -558,3 +558,90 @@ def pin_groups_reduce_to_one_group(orc):
 
 
 PINS += [pin_groups_reduce_to_one_group]
+
+
+# ------------------------------------------------------------ Mamba-2 scan
+# Reading: the Mamba-2 block's scan is the selective recurrence with one A,
+# one step Delta and one D per head of P channels, B and C per group of
+# heads, x and out laid out (batch, L, heads, P), the state (batch, heads * P,
+# N) with channel h * P + p.
+
+def _softplus_inv(v):
+    return math.log(math.expm1(v))
+
+
+def pin_mamba2_per_head_closed_form(orc):
+    """Constant inputs per head: every (head, channel, state) follows the
+    geometric series h_t = s (1 - e^(t+1)) / (1 - e), e = exp(Delta_h A_h),
+    s = Delta_h B_g[n] x_hp, with Delta_h from dt_bias through softplus, the
+    head's own D and the channel's own gate."""
+    batch, L, H, P, N, G = 2, 7, 4, 3, 2, 2
+    A = np.array([-0.5, -1.0, -2.0, -0.25])
+    Dh = np.array([0.5, -1.0, 2.0, 0.0])
+    step = np.array([0.3, 0.05, 0.7, 1.1])              # Delta per head
+    bias = np.array([_softplus_inv(v) for v in step])
+    Bg = np.array([[1.0, 2.0], [-0.5, 3.0]])            # per group, constant in t
+    Cg = np.array([[1.0, -1.0], [0.25, 2.0]])
+    xv = np.arange(1, batch * H * P + 1, dtype=np.float64).reshape(batch, H, P) / 7.0
+    zv = np.linspace(-2.0, 2.0, batch * H * P).reshape(batch, H, P)
+    x = np.broadcast_to(xv[:, None], (batch, L, H, P)).copy()
+    z = np.broadcast_to(zv[:, None], (batch, L, H, P)).copy()
+    dt = np.zeros((batch, L, H))
+    B = np.broadcast_to(Bg, (batch, L, G, N)).copy()
+    C = np.broadcast_to(Cg, (batch, L, G, N)).copy()
+    out, last = orc.mamba2_scan(x, dt, A, B, C, D=Dh, z=z, dt_bias=bias, softplus=True)
+    want = np.empty_like(out)
+    want_last = np.empty_like(last)
+    for b in range(batch):
+        for h in range(H):
+            g = h // (H // G)
+            e = math.exp(step[h] * A[h])
+            for p in range(P):
+                for t in range(L):
+                    hs = step[h] * Bg[g] * xv[b, h, p] * (1.0 - e ** (t + 1)) / (1.0 - e)
+                    y = float(np.dot(Cg[g], hs)) + Dh[h] * xv[b, h, p]
+                    want[b, t, h, p] = y * zv[b, h, p] * expit(zv[b, h, p])
+                want_last[b, h * P + p] = hs
+    _close(out, want, 1e-12, 1e-12, "mamba2 closed form out")
+    _close(last, want_last, 1e-12, 1e-12, "mamba2 closed form state")
+
+
+def pin_mamba2_brute_force(orc):
+    """Random tiny case, time-varying everything, loaded state, softplus off
+    and on: the recurrence evaluated with plain loops over (b, t, h, p, n)."""
+    rng = np.random.default_rng(71)
+    batch, L, H, P, N, G = 2, 5, 4, 2, 3, 2
+    x = rng.standard_normal((batch, L, H, P))
+    z = rng.standard_normal((batch, L, H, P))
+    dt = rng.uniform(0.05, 0.6, (batch, L, H))
+    A = -rng.uniform(0.2, 2.0, H)
+    B = rng.standard_normal((batch, L, G, N))
+    C = rng.standard_normal((batch, L, G, N))
+    Dh = rng.standard_normal(H)
+    bias = rng.uniform(-0.5, 0.5, H)
+    h0 = rng.standard_normal((batch, H * P, N))
+    for softplus in (False, True):
+        out, last = orc.mamba2_scan(x, dt, A, B, C, D=Dh, z=z, dt_bias=bias,
+                                    softplus=softplus, h0=h0)
+        want = np.empty((batch, L, H, P))
+        state = h0.copy()
+        for b in range(batch):
+            for h in range(H):
+                g = h // (H // G)
+                for t in range(L):
+                    v = dt[b, t, h] + bias[h]
+                    step = math.log1p(math.exp(v)) if softplus else v
+                    for p in range(P):
+                        d = h * P + p
+                        y = 0.0
+                        for n in range(N):
+                            state[b, d, n] = (math.exp(step * A[h]) * state[b, d, n]
+                                              + step * B[b, t, g, n] * x[b, t, h, p])
+                            y += C[b, t, g, n] * state[b, d, n]
+                        y += Dh[h] * x[b, t, h, p]
+                        want[b, t, h, p] = y * z[b, t, h, p] / (1.0 + math.exp(-z[b, t, h, p]))
+        _close(out, want, 1e-12, 1e-12, "mamba2 brute force out (softplus %s)" % softplus)
+        _close(last, state, 1e-12, 1e-12, "mamba2 brute force state (softplus %s)" % softplus)
+
+
+PINS += [pin_mamba2_per_head_closed_form, pin_mamba2_brute_force]
