@@ -210,6 +210,38 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
                             const mssm_dims* dims, void* stream);
 
 /*
+ * The Mamba-2 block's scan (page "Mamba: Selective State Space Models", "Use
+ * the Mamba2 block": the Mamba-2 architecture, state sizes of typically 64
+ * or 128).  The pages give the block's API, not its scan; this is the
+ * Mamba-2 architecture's: the selective recurrence with one A, one step and
+ * one D per head of `headdim` channels, and B, C shared by a group of heads.
+ * For channel p of head h (channel index d = h * headdim + p), head group
+ * g = h / (nheads / ngroups), state n:
+ *     Delta_t = softplus(dt_t[h] + dt_bias[h])   (or without softplus)
+ *     h_t[d,n] = exp(Delta_t A[h]) h_{t-1}[d,n] + Delta_t x_t[d] B_t[g,n]
+ *     out_t[d] = (sum_n C_t[g,n] h_t[d,n] + D[h] x_t[d]) * silu(z_t[d])
+ * with nheads = dims->dim / headdim.  Layouts (last index fastest):
+ *   x, z, out : (batch, seqlen, nheads, headdim) bf16; z may be NULL (no gate)
+ *   dt        : (batch, seqlen, nheads) bf16
+ *   A, D, dt_bias : (nheads) fp32; D and dt_bias may be NULL (zero)
+ *   B, C      : (batch, seqlen, ngroups, dstate) bf16 (ngroups 0 means 1)
+ *   last_state: (batch, nheads * headdim, dstate) fp32: the final state, or
+ *               NULL; with MSSM_FLAG_LOAD_STATE it holds the initial state
+ *               on entry (required then)
+ * dims: io_dtype must be MSSM_BF16, dstate 64 or 128, headdim 64, nheads a
+ * multiple of ngroups, time_segments 0; flags may hold only
+ * MSSM_FLAG_LOAD_STATE.  x, z, out, B and C must be 16-byte aligned.  out
+ * and last_state must not overlap an input or each other.  The call runs
+ * the chunked matrix form of the recurrence on the matrix cores, one
+ * workgroup per (batch entry, head); results agree with the sequential
+ * recurrence up to rounding.  It allocates nothing.
+ */
+int mssm_mamba2_scan_fwd(const void* x, const void* dt, const float* A, const void* B,
+                         const void* C, const float* D, const void* z,
+                         const float* dt_bias, int softplus, int64_t headdim, void* out,
+                         float* last_state, const mssm_dims* dims, void* stream);
+
+/*
  * Single-token decode step: the scan with seqlen = 1 starting from `state`,
  * which is updated in place.
  *   state       : (batch, dim, dstate) fp32, in/out

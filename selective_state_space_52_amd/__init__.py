@@ -20,7 +20,7 @@ from ._lib import (MSSM_BF16, MSSM_F32, MSSM_FLAG_LAYOUT_BLD, MSSM_FLAG_LOAD_STA
                    Dims, MssmError, Plan, check, lib)
 
 __all__ = ["selective_scan_fwd", "selective_scan_bwd", "selective_scan_fwd_conv",
-           "causal_conv1d_fwd", "selective_state_update", "scan_plan",
+           "causal_conv1d_fwd", "selective_state_update", "mamba2_scan_fwd", "scan_plan",
            "set_scan_timing_events", "MssmError", "abi_version"]
 
 _IO = {torch.float32: MSSM_F32, torch.bfloat16: MSSM_BF16}
@@ -309,5 +309,44 @@ def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
         check(lib().mssm_selective_state_update(
             _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
             _ptr(z), _ptr(dt_bias), int(bool(softplus)), _ptr(out), dims,
+            _stream(dev)))
+    return out
+
+
+def mamba2_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True,
+                    last_state=None, load_state=False, out=None):
+    """The Mamba-2 block's scan (mssm_mamba2_scan_fwd), bf16 activations.
+
+    x, z: (batch, L, nheads, headdim) with headdim 64; dt: (batch, L, nheads);
+    A, D, dt_bias: (nheads,) fp32; B, C: (batch, L, ngroups, N) with N 64 or
+    128; last_state: (batch, nheads * headdim, N) fp32 receiving the final
+    state (holding the initial one when load_state).  Returns out, shaped as x.
+    """
+    if x.dim() != 4 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a (batch, L, nheads, headdim) bfloat16 tensor")
+    batch, L, H, P = x.shape
+    dev = x.device
+    if B.dim() != 4:
+        raise ValueError("B must be (batch, L, ngroups, N)")
+    G, N = B.shape[2], B.shape[3]
+    _need(x, "x", torch.bfloat16, (batch, L, H, P), dev)
+    _need(z, "z", torch.bfloat16, (batch, L, H, P), dev)
+    _need(dt, "dt", torch.bfloat16, (batch, L, H), dev)
+    _need(B, "B", torch.bfloat16, (batch, L, G, N), dev)
+    _need(C, "C", torch.bfloat16, (batch, L, G, N), dev)
+    _need(A, "A", torch.float32, (H,), dev)
+    _need(D, "D", torch.float32, (H,), dev)
+    _need(dt_bias, "dt_bias", torch.float32, (H,), dev)
+    _need(last_state, "last_state", torch.float32, (batch, H * P, N), dev)
+    if load_state and last_state is None:
+        raise ValueError("load_state needs last_state")
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", torch.bfloat16, (batch, L, H, P), dev)
+    dims = Dims(batch, H * P, N, L, _IO[torch.bfloat16], 1 if load_state else 0, 0, G)
+    with torch.cuda.device(dev):
+        check(lib().mssm_mamba2_scan_fwd(
+            _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(dt_bias), int(bool(softplus)), P, _ptr(out), _ptr(last_state), dims,
             _stream(dev)))
     return out

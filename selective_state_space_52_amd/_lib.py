@@ -21,7 +21,7 @@ STATUS = {
 # every symbol include/mssm.h declares
 EXPORTS = ("mssm_selective_scan_fwd", "mssm_selective_scan_bwd",
            "mssm_selective_scan_fwd_conv", "mssm_causal_conv1d_fwd",
-           "mssm_selective_state_update",
+           "mssm_selective_state_update", "mssm_mamba2_scan_fwd",
            "mssm_selective_scan_fwd_plan", "mssm_set_scan_timing_events",
            "mssm_status_string", "mssm_last_error", "mssm_abi_version")
 
@@ -76,6 +76,10 @@ def lib():
         L.mssm_selective_state_update.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp,
                                                   fp, i, vp, ctypes.POINTER(Dims), vp]
         L.mssm_selective_state_update.restype = i
+        L.mssm_mamba2_scan_fwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i,
+                                           ctypes.c_int64, vp, fp,
+                                           ctypes.POINTER(Dims), vp]
+        L.mssm_mamba2_scan_fwd.restype = i
         L.mssm_selective_scan_fwd_plan.argtypes = [ctypes.POINTER(Dims),
                                                    ctypes.POINTER(Plan)]
         L.mssm_selective_scan_fwd_plan.restype = i

@@ -603,4 +603,71 @@ int mssm_selective_state_update(float* state, const void* x, const void* dt,
   return MSSM_OK;
 }
 
+int mssm_mamba2_scan_fwd(const void* x, const void* dt, const float* A, const void* B,
+                         const void* C, const float* D, const void* z,
+                         const float* dt_bias, int softplus, int64_t headdim, void* out,
+                         float* last_state, const mssm_dims* dims, void* stream) {
+  if (!dims) return MSSM_ERR_NULL;
+  if (dims->io_dtype != MSSM_BF16) return MSSM_ERR_UNSUPPORTED;
+  if (dims->flags & ~MSSM_FLAG_LOAD_STATE) return MSSM_ERR_UNSUPPORTED;
+  if (dims->batch <= 0 || dims->dim <= 0 || dims->seqlen <= 0 || dims->dstate <= 0 ||
+      dims->ngroups < 0 || dims->time_segments != 0 || headdim <= 0)
+    return MSSM_ERR_DIMS;
+  if (dims->dstate != 64 && dims->dstate != 128) return MSSM_ERR_UNSUPPORTED;
+  if (headdim != mssm::mamba2_headdim()) return MSSM_ERR_UNSUPPORTED;
+  if (dims->dim % headdim != 0) return MSSM_ERR_DIMS;
+  const int64_t batch = dims->batch, dim = dims->dim, N = dims->dstate,
+                L = dims->seqlen;
+  const int64_t H = dim / headdim;
+  const int64_t G = groups_of(dims);
+  if (H % G != 0) return MSSM_ERR_UNSUPPORTED;
+  const bool load_state = (dims->flags & MSSM_FLAG_LOAD_STATE) != 0;
+  if (!x || !dt || !A || !B || !C || !out) return MSSM_ERR_NULL;
+  if (load_state && !last_state) return MSSM_ERR_NULL;
+  const int64_t lim = INT64_MAX / 16;
+  if (batch * H > INT32_MAX || !product_ok(batch, dim, L, lim) ||
+      !product_ok(batch, L, G * N, lim) || !product_ok(batch, dim, N, lim))
+    return MSSM_ERR_DIMS;
+
+  // x, z, out and B, C rows are read and written in 16-byte pieces
+  const void* vecs[] = {x, B, C, out, z};
+  for (const void* p : vecs)
+    if (p && !aligned(p, 16)) return MSSM_ERR_ALIGN;
+  if (!aligned(dt, 2)) return MSSM_ERR_ALIGN;
+  const void* f32s[] = {A, D, dt_bias, last_state};
+  for (const void* p : f32s)
+    if (p && !aligned(p, 4)) return MSSM_ERR_ALIGN;
+
+  const int64_t ebytes = batch * L * dim * 2;
+  const Range r_out = range_of(out, ebytes);
+  const Range r_state = range_of(last_state, batch * dim * N * 4);
+  const Range ins[] = {range_of(x, ebytes),         range_of(z, ebytes),
+                       range_of(dt, batch * L * H * 2),
+                       range_of(B, batch * L * G * N * 2),
+                       range_of(C, batch * L * G * N * 2),
+                       range_of(A, H * 4),          range_of(D, H * 4),
+                       range_of(dt_bias, H * 4)};
+  for (const Range& r : ins)
+    if (overlap(r_out, r) || overlap(r_state, r)) return MSSM_ERR_ALIAS;
+  if (overlap(r_out, r_state)) return MSSM_ERR_ALIAS;
+
+  // --- validation done; HIP calls from here on ---
+  mssm::Mamba2Params p;
+  p.x = x; p.dt = dt; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.bias = dt_bias;
+  p.out = out; p.state = last_state;
+  p.batch = batch; p.L = L; p.nheads = H; p.ngroups = G; p.N = N;
+  p.softplus = softplus ? 1 : 0;
+  p.load_state = load_state ? 1 : 0;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (g_ev_start) e = hipEventRecord((hipEvent_t)g_ev_start, st);
+  if (e == hipSuccess) e = mssm::launch_mamba2_scan(p, st);
+  if (e == hipSuccess && g_ev_stop) e = hipEventRecord((hipEvent_t)g_ev_stop, st);
+  if (e != hipSuccess) {
+    set_hip_error("mamba2 scan launch", e);
+    return MSSM_ERR_HIP;
+  }
+  return MSSM_OK;
+}
+
 }  // extern "C"

@@ -189,4 +189,25 @@ hipError_t launch_state_update(const UpdateParams& p, int N, bool bf16,
 hipError_t launch_causal_conv1d(const ConvParams& p, bool bf16, bool vec,
                                 hipStream_t stream);
 
+// The Mamba-2 block's scan: x, z, out (batch, L, nheads, headdim) bf16; dt
+// (batch, L, nheads) bf16; A, D, bias (nheads) fp32; B, C (batch, L, ngroups,
+// N) bf16; state (batch, nheads * headdim, N) fp32, read first when
+// load_state.
+struct Mamba2Params {
+  const void* x;
+  const void* dt;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;     // may be null
+  const void* z;      // may be null
+  const float* bias;  // may be null
+  void* out;
+  float* state;       // may be null unless load_state
+  int64_t batch, L, nheads, ngroups, N;
+  int32_t softplus, load_state;
+};
+int mamba2_headdim();
+hipError_t launch_mamba2_scan(const Mamba2Params& p, hipStream_t stream);
+
 }  // namespace mssm

@@ -235,3 +235,31 @@ def test_product_path_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         m.selective_scan_fwd(x, x, torch.zeros(4, 16), torch.zeros(1, 8, 16),
                              torch.zeros(1, 8, 16))
+
+
+def test_mamba2_validation_codes(L):
+    p = _ptrs(10)
+
+    def m2(dims, headdim=64, **o):
+        q = dict(zip(["x", "dt", "A", "B", "C", "D", "z", "bias", "out", "last"], p))
+        q.update(o)
+        return L.mssm_mamba2_scan_fwd(q["x"], q["dt"], q["A"], q["B"], q["C"], q["D"],
+                                      q["z"], q["bias"], 1, headdim, q["out"], q["last"],
+                                      ctypes.byref(dims), None)
+    ok = dict(batch=2, dim=256, N=64, L_=100, io=1)      # 4 heads of 64
+    assert m2(_dims(**ok), x=None) == -1
+    assert m2(_dims(**ok), out=None) == -1
+    assert m2(_dims(**dict(ok, flags=1)), last=None) == -1   # LOAD_STATE needs it
+    assert m2(_dims(**dict(ok, io=0))) == -3                # bf16 only
+    assert m2(_dims(**dict(ok, N=16))) == -3                # dstate 64 or 128
+    assert m2(_dims(**ok), headdim=32) == -3                # headdim 64
+    assert m2(_dims(**dict(ok, dim=100))) == -2             # dim not a multiple
+    assert m2(_dims(**dict(ok, flags=2))) == -3             # no layout flag
+    assert m2(_dims(**dict(ok, ts=2))) == -2
+    assert m2(_dims(**dict(ok, groups=3))) == -3            # 4 heads, 3 groups
+    assert m2(_dims(**dict(ok, L_=0))) == -2
+    assert m2(_dims(**ok), x=BASE + 8) == -4                # 16-byte pieces
+    assert m2(_dims(**ok), dt=BASE + 1 * (1 << 34) + 1) == -4
+    assert m2(_dims(**ok), out=p[0] + 64) == -5             # out over x
+    assert m2(_dims(**ok), last=p[3]) == -5                 # state over B
+    assert m2(_dims(**ok), last=p[8] + 16) == -5            # state over out

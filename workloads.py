@@ -81,6 +81,36 @@ class DecodeSpec:
     note: str = ""
 
 
+@dataclass(frozen=True)
+class Mamba2Spec:
+    """The Mamba-2 block's scan: heads of `headdim` channels, bf16 activations."""
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    dstate: int
+    ngroups: int = 1
+    seed: int = 5
+    softplus: bool = True
+    has_z: bool = True
+    has_D: bool = True
+    has_bias: bool = True
+    note: str = ""
+
+    @property
+    def dim(self) -> int:
+        return self.nheads * self.headdim
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.seqlen * self.dim
+
+    @property
+    def state_elements(self) -> int:
+        return self.elements * self.dstate
+
+
 WORKLOADS = {
     "tiny_f32": ScanSpec("tiny_f32", 1, 64, 16, 256, io="f32", seed=0,
                          note="tiny fp32 scan"),
@@ -95,6 +125,9 @@ WORKLOADS = {
                                   "2048-step chunks"),
     "decode": DecodeSpec("decode", 256, 5120, 16, steps=1000, seed=4,
                          note="single-token state update, 256 sequences"),
+    "mamba2_2p7b_layer": Mamba2Spec("mamba2_2p7b_layer", 4, 2048, 80, 64, 128, seed=5,
+                                    note="Mamba-2-2.7B-shaped layer scan: 80 heads of "
+                                         "64 channels (D_inner 5120), N 128, one group"),
 }
 
 
@@ -281,3 +314,45 @@ def decode_step_bytes(s: DecodeSpec) -> int:
     b += 2 * s.batch * s.dstate * io       # B, C
     b += 4 * s.dim * s.dstate + 2 * 4 * s.dim   # A, D, dt_bias
     return b
+
+
+def make_mamba2_inputs(s: Mamba2Spec) -> dict:
+    """Inputs of the Mamba-2 scan: x, z (batch, L, H, P), dt (batch, L, H), B, C
+    (batch, L, G, N) ~ N(0, 1) in bf16; per head A = -U[1, 16], D ~ N(0, 1),
+    dt_bias = inv_softplus(exp(U[ln 1e-3, ln 1e-1])), all fp32.  Draw order
+    from default_rng(seed): x, dt, z, B, C, A, D, log-dt."""
+    rng = np.random.default_rng(s.seed)
+    b, L, H, P, N, G = s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups
+    f32 = np.float32
+    x = _round_io(rng.standard_normal((b, L, H, P), dtype=f32), "bf16")
+    dt = _round_io(rng.standard_normal((b, L, H), dtype=f32), "bf16")
+    z = _round_io(rng.standard_normal((b, L, H, P), dtype=f32), "bf16")
+    B = _round_io(rng.standard_normal((b, L, G, N), dtype=f32), "bf16")
+    C = _round_io(rng.standard_normal((b, L, G, N), dtype=f32), "bf16")
+    A = -rng.uniform(1.0, 16.0, H).astype(f32)
+    D = rng.standard_normal(H, dtype=f32)
+    log_dt = rng.uniform(math.log(1e-3), math.log(1e-1), size=H)
+    bias = np.log(np.expm1(np.exp(log_dt))).astype(f32)
+    return dict(x=x, dt=dt, z=z if s.has_z else None, B=B, C=C, A=torch.from_numpy(A),
+                D=torch.from_numpy(D) if s.has_D else None,
+                dt_bias=torch.from_numpy(bias) if s.has_bias else None,
+                softplus=s.softplus)
+
+
+def mamba2_initial_state(s: Mamba2Spec, seed_offset: int = 7919) -> torch.Tensor:
+    """(batch, H * P, N) fp32 initial state ~ 0.1 N(0, 1)."""
+    rng = np.random.default_rng([s.seed, seed_offset])
+    return torch.from_numpy(
+        0.1 * rng.standard_normal((s.batch, s.dim, s.dstate), dtype=np.float32))
+
+
+def mamba2_bytes(s: Mamba2Spec, load_state: bool = False) -> int:
+    """Algorithmic bytes of one Mamba-2 scan call: x, z read and out written
+    (bf16), dt (bf16), B, C (bf16), A, D, dt_bias (fp32), the final state
+    written (fp32, and read when loaded)."""
+    act = s.elements * 2 * (3 if s.has_z else 2)
+    dt = s.batch * s.seqlen * s.nheads * 2
+    bc = 2 * s.batch * s.seqlen * s.ngroups * s.dstate * 2
+    par = 3 * s.nheads * 4
+    st = s.batch * s.dim * s.dstate * 4 * (2 if load_state else 1)
+    return act + dt + bc + par + st
