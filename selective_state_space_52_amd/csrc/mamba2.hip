@@ -125,15 +125,60 @@ __global__ void __launch_bounds__(kThreads)
   };
   state_to_lds();
 
+  // Inputs of a chunk, loaded into registers one chunk ahead.  Lane = step t
+  // of the chunk (consecutive lanes write consecutive LDS addresses of the
+  // transposed tiles); wave wv takes the 16-byte pieces wv, wv + 4, ... of a
+  // row.
+  constexpr int kBPer = N / 8 / 4;   // pieces of a B (or C) row per wave
+  constexpr int kXPer = kP / 8 / 4;  // pieces of an x row per wave
+  uint4 rb[kBPer], rc[kBPer], rx[kXPer];
+  uint16_t rdt = 0;
+  uint16_t zr[16], zn[16];
+  auto load_chunk_inputs = [&](int64_t t0) {
+    // steps past L load the last step (clamped address) and are zeroed when
+    // written to LDS
+    const int64_t t = min(t0 + lane, L - 1);
+#pragma unroll
+    for (int k = 0; k < kBPer; ++k) {
+      const int n8 = (wv + 4 * k) * 8;
+      const int64_t off = ((b * L + t) * s.G + g) * N + n8;
+      rb[k] = *reinterpret_cast<const uint4*>(Bm + off);
+      rc[k] = *reinterpret_cast<const uint4*>(Cm + off);
+    }
+#pragma unroll
+    for (int k = 0; k < kXPer; ++k) {
+      const int p8 = (wv + 4 * k) * 8;
+      rx[k] = *reinterpret_cast<const uint4*>(x + ((b * L + t) * s.H + h) * kP + p8);
+    }
+    if (wv == 0) rdt = dt[(b * L + t) * s.H + h];
+    if constexpr (HAS_Z) {
+      // unconditional loads from a clamped step (a branch per load made the
+      // compiler wait for each one); steps past L are never stored
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t tz = min(t0 + 32 * tb + acc_row(v, lane), L - 1);
+        zn[v] = z[((b * L + tz) * s.H + h) * kP + 32 * pb + col];
+      }
+    }
+  };
+  auto put_t = [](uint16_t (*dst)[kQP], int r0, int t, uint4 v) {  // dst[r0 + j][t]
+    const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dst[r0 + 2 * j][t] = (uint16_t)(q[j] & 0xffffu);
+      dst[r0 + 2 * j + 1][t] = (uint16_t)(q[j] >> 16);
+    }
+  };
+
   const int64_t chunks = (L + kQ - 1) / kQ;
+  load_chunk_inputs(0);
   for (int64_t c = 0; c < chunks; ++c) {
     const int64_t t0 = c * kQ;
     // ---- phase 1: the chunk's inputs into LDS
     if (wv == 0) {
-      const int64_t t = t0 + lane;
       float dl = 0.0f;
-      if (t < L) {
-        const float v = bf16_bits(dt[(b * L + t) * s.H + h]) + bh;
+      if (t0 + lane < L) {
+        const float v = bf16_bits(rdt) + bh;
         dl = s.softplus ? softplus_f32(v) : v;
       }
       double cs = (double)(dl * Ah);
@@ -149,77 +194,61 @@ __global__ void __launch_bounds__(kThreads)
       sm.w[lane] = dl * hw_exp2((float)(end - cs) * kLog2e);
       if (lane == 0) sm.dec_end = hw_exp2((float)end * kLog2e);
     }
-    {
-      constexpr int kPer = N / 8;  // 16-byte pieces per row
-      for (int i = tid; i < kQ * kPer; i += kThreads) {
-        const int t = i / kPer, n8 = (i % kPer) * 8;
-        uint4 vb = make_uint4(0u, 0u, 0u, 0u), vc = vb;
-        if (t0 + t < L) {
-          const int64_t off = ((b * L + t0 + t) * s.G + g) * N + n8;
-          vb = *reinterpret_cast<const uint4*>(Bm + off);
-          vc = *reinterpret_cast<const uint4*>(Cm + off);
-        }
-        *reinterpret_cast<uint4*>(&sm.B[t][n8]) = vb;
-        *reinterpret_cast<uint4*>(&sm.C[t][n8]) = vc;
-        const uint32_t q[4] = {vb.x, vb.y, vb.z, vb.w};
+    const bool live = t0 + lane < L;
+    const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sm.Bt[n8 + 2 * j][t] = (uint16_t)(q[j] & 0xffffu);
-          sm.Bt[n8 + 2 * j + 1][t] = (uint16_t)(q[j] >> 16);
-        }
-      }
+    for (int k = 0; k < kBPer; ++k) {
+      const int n8 = (wv + 4 * k) * 8;
+      const uint4 vb = live ? rb[k] : zero4, vc = live ? rc[k] : zero4;
+      *reinterpret_cast<uint4*>(&sm.B[lane][n8]) = vb;
+      *reinterpret_cast<uint4*>(&sm.C[lane][n8]) = vc;
+      put_t(sm.Bt, n8, lane, vb);
     }
-    constexpr int kXPer = kQ * kP / 8 / kThreads;  // 16-byte pieces of x per thread
-    uint4 xr[kXPer];
 #pragma unroll
-    for (int k = 0; k < kXPer; ++k) {
-      const int i = tid + k * kThreads;
-      const int t = i / (kP / 8), p8 = (i % (kP / 8)) * 8;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (t0 + t < L) v = *reinterpret_cast<const uint4*>(x + ((b * L + t0 + t) * s.H + h) * kP + p8);
-      xr[k] = v;
-      const uint32_t q[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sm.Xt[p8 + 2 * j][t] = (uint16_t)(q[j] & 0xffffu);
-        sm.Xt[p8 + 2 * j + 1][t] = (uint16_t)(q[j] >> 16);
-      }
-    }
-    float zr[16];
+    for (int k = 0; k < kXPer; ++k) put_t(sm.Xt, (wv + 4 * k) * 8, lane, live ? rx[k] : zero4);
     if constexpr (HAS_Z) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t t = t0 + 32 * tb + acc_row(v, lane);
-        zr[v] = t < L ? bf16_bits(z[((b * L + t) * s.H + h) * kP + 32 * pb + col]) : 0.0f;
-      }
+      for (int v = 0; v < 16; ++v) zr[v] = zn[v];
     }
     __syncthreads();
+    if (c + 1 < chunks) load_chunk_inputs(t0 + kQ);  // lands during phases 2 and 3
 
     // ---- phase 2: x o w, L o C B^T, and the entering state's part of Y
+    {
+      // every LDS read ahead of the writes, so that one wait covers them
+      const float wt = sm.w[lane];
+      uint16_t xv[kXPer][8];
 #pragma unroll
-    for (int k = 0; k < kXPer; ++k) {
-      const int i = tid + k * kThreads;
-      const int t = i / (kP / 8), p8 = (i % (kP / 8)) * 8;
-      const float wt = sm.w[t];
-      const uint32_t q[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
+      for (int k = 0; k < kXPer; ++k)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        split(bf16_lo(q[j]) * wt, sm.Xw[0][p8 + 2 * j][t], sm.Xw[1][p8 + 2 * j][t]);
-        split(bf16_hi(q[j]) * wt, sm.Xw[0][p8 + 2 * j + 1][t], sm.Xw[1][p8 + 2 * j + 1][t]);
-      }
+        for (int j = 0; j < 8; ++j) xv[k][j] = sm.Xt[(wv + 4 * k) * 8 + j][lane];
+#pragma unroll
+      for (int k = 0; k < kXPer; ++k)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int p = (wv + 4 * k) * 8 + j;
+          split(bf16_bits(xv[k][j]) * wt, sm.Xw[0][p][lane], sm.Xw[1][p][lane]);
+        }
     }
     if (pb <= tb) {  // the block above the diagonal is all zero
-      f32x16 gacc = {};
+      f32x16 g0 = {}, g1 = {};
 #pragma unroll
-      for (int k0 = 0; k0 < N; k0 += 16)
-        gacc = mfma(lds8(&sm.C[32 * tb + col][k0 + kq]), lds8(&sm.B[32 * pb + col][k0 + kq]),
-                    gacc);
+      for (int k0 = 0; k0 < N; k0 += 32) {
+        g0 = mfma(lds8(&sm.C[32 * tb + col][k0 + kq]), lds8(&sm.B[32 * pb + col][k0 + kq]), g0);
+        g1 = mfma(lds8(&sm.C[32 * tb + col][k0 + 16 + kq]),
+                  lds8(&sm.B[32 * pb + col][k0 + 16 + kq]), g1);
+      }
+      const int sc = 32 * pb + col;
+      const double cs = sm.cum[sc];
+      const float ds = sm.delta[sc];
+      double ct[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) ct[v] = sm.cum[32 * tb + acc_row(v, lane)];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int t = 32 * tb + acc_row(v, lane), sc = 32 * pb + col;
-        float m = 0.0f;
-        if (sc <= t)
-          m = gacc[v] * hw_exp2((float)(sm.cum[t] - sm.cum[sc]) * kLog2e) * sm.delta[sc];
+        const int t = 32 * tb + acc_row(v, lane);
+        const float m = sc <= t ? (g0[v] + g1[v]) * hw_exp2((float)(ct[v] - cs) * kLog2e) * ds
+                                : 0.0f;
         split(m, sm.M[0][t][sc], sm.M[1][t][sc]);
       }
     } else {
@@ -229,44 +258,51 @@ __global__ void __launch_bounds__(kThreads)
         sm.M[0][t][sc] = sm.M[1][t][sc] = 0;
       }
     }
-    f32x16 yacc = {};
+    f32x16 ya = {}, yb = {};  // hi and lo halves of the state, summed at the end
 #pragma unroll
     for (int k0 = 0; k0 < N; k0 += 16) {
       const bf16x8 a = lds8(&sm.C[32 * tb + col][k0 + kq]);
-      yacc = mfma(a, lds8(&sm.H[0][32 * pb + col][k0 + kq]), yacc);
-      yacc = mfma(a, lds8(&sm.H[1][32 * pb + col][k0 + kq]), yacc);
+      ya = mfma(a, lds8(&sm.H[0][32 * pb + col][k0 + kq]), ya);
+      yb = mfma(a, lds8(&sm.H[1][32 * pb + col][k0 + kq]), yb);
     }
 #pragma unroll
-    for (int v = 0; v < 16; ++v) yacc[v] *= sm.ecum[32 * tb + acc_row(v, lane)];
+    for (int v = 0; v < 16; ++v) ya[v] = (ya[v] + yb[v]) * sm.ecum[32 * tb + acc_row(v, lane)];
     __syncthreads();
 
     // ---- phase 3: (L o C B^T) X, the output, and the state at the chunk end
+    yb = f32x16{};
 #pragma unroll
     for (int k0 = 0; k0 < kQ; k0 += 16) {
       const bf16x8 bx = lds8(&sm.Xt[32 * pb + col][k0 + kq]);
-      yacc = mfma(lds8(&sm.M[0][32 * tb + col][k0 + kq]), bx, yacc);
-      yacc = mfma(lds8(&sm.M[1][32 * tb + col][k0 + kq]), bx, yacc);
+      ya = mfma(lds8(&sm.M[0][32 * tb + col][k0 + kq]), bx, ya);
+      yb = mfma(lds8(&sm.M[1][32 * tb + col][k0 + kq]), bx, yb);
     }
+    uint16_t xs[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) xs[v] = sm.Xt[32 * pb + col][32 * tb + acc_row(v, lane)];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int t = 32 * tb + acc_row(v, lane), p = 32 * pb + col;
       if (t0 + t < L) {
-        float y = fmaf(Dh, bf16_bits(sm.Xt[p][t]), yacc[v]);
-        if constexpr (HAS_Z) y *= silu_f32(zr[v]);
+        float y = fmaf(Dh, bf16_bits(xs[v]), ya[v] + yb[v]);
+        if constexpr (HAS_Z) y *= silu_f32(bf16_bits(zr[v]));
         out[((b * L + t0 + t) * s.H + h) * kP + p] = to_bf16(y);
       }
     }
     const float dec = sm.dec_end;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
+      f32x16 lo = {};
 #pragma unroll
       for (int v = 0; v < 16; ++v) hacc[i][v] *= dec;
 #pragma unroll
       for (int k0 = 0; k0 < kQ; k0 += 16) {
         const bf16x8 bb = lds8(&sm.Bt[nbase + 32 * i + col][k0 + kq]);
         hacc[i] = mfma(lds8(&sm.Xw[0][32 * pb + col][k0 + kq]), bb, hacc[i]);
-        hacc[i] = mfma(lds8(&sm.Xw[1][32 * pb + col][k0 + kq]), bb, hacc[i]);
+        lo = mfma(lds8(&sm.Xw[1][32 * pb + col][k0 + kq]), bb, lo);
       }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) hacc[i][v] += lo[v];
     }
     __syncthreads();
     state_to_lds();  // read by the next chunk after its first barrier
