@@ -229,8 +229,8 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
  *               NULL; with MSSM_FLAG_LOAD_STATE it holds the initial state
  *               on entry (required then)
  * dims: io_dtype must be MSSM_BF16, dstate 64 or 128, headdim 64, nheads a
- * multiple of ngroups, time_segments 0; flags may hold only
- * MSSM_FLAG_LOAD_STATE.  x, z, out, B and C must be 16-byte aligned.  out
+ * multiple of ngroups, time_segments 0, and seqlen * dim and seqlen *
+ * ngroups * dstate below 2^31; flags may hold only MSSM_FLAG_LOAD_STATE.  x, z, out, B and C must be 16-byte aligned.  out
  * and last_state must not overlap an input or each other.  The call runs
  * the chunked matrix form of the recurrence on the matrix cores, one
  * workgroup per (batch entry, head); results agree with the sequential

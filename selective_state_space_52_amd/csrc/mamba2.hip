@@ -99,7 +99,17 @@ __global__ void __launch_bounds__(kThreads)
   const int64_t b = blockIdx.x / s.H;
   const int h = (int)(blockIdx.x - b * s.H);
   const int g = h / (s.H / s.G);
-  const int64_t L = s.L;
+  const int L = (int)s.L;
+  // this (batch, head)'s rows: step t of x, z, out at t * HP (+ channel), of
+  // B, C at t * GN (+ state), of dt at t * H; the host keeps every such
+  // offset below 2^31
+  const int HP = s.H * kP, GN = s.G * N;
+  const uint16_t* __restrict__ xb = x + ((int64_t)b * L * s.H + h) * kP;
+  const uint16_t* __restrict__ zb = HAS_Z ? z + ((int64_t)b * L * s.H + h) * kP : nullptr;
+  uint16_t* __restrict__ ob = out + ((int64_t)b * L * s.H + h) * kP;
+  const uint16_t* __restrict__ Bb = Bm + ((int64_t)b * L * s.G + g) * N;
+  const uint16_t* __restrict__ Cb = Cm + ((int64_t)b * L * s.G + g) * N;
+  const uint16_t* __restrict__ db = dt + (int64_t)b * L * s.H + h;
   const float Ah = A[h];
   const float Dh = Dv ? Dv[h] : 0.0f;
   const float bh = bias ? bias[h] : 0.0f;
@@ -134,30 +144,27 @@ __global__ void __launch_bounds__(kThreads)
   uint4 rb[kBPer], rc[kBPer], rx[kXPer];
   uint16_t rdt = 0;
   uint16_t zr[16], zn[16];
-  auto load_chunk_inputs = [&](int64_t t0) {
+  auto load_chunk_inputs = [&](int t0) {
     // steps past L load the last step (clamped address) and are zeroed when
     // written to LDS
-    const int64_t t = min(t0 + lane, L - 1);
+    const int t = min(t0 + lane, L - 1);
 #pragma unroll
     for (int k = 0; k < kBPer; ++k) {
-      const int n8 = (wv + 4 * k) * 8;
-      const int64_t off = ((b * L + t) * s.G + g) * N + n8;
-      rb[k] = *reinterpret_cast<const uint4*>(Bm + off);
-      rc[k] = *reinterpret_cast<const uint4*>(Cm + off);
+      const int off = t * GN + (wv + 4 * k) * 8;
+      rb[k] = *reinterpret_cast<const uint4*>(Bb + off);
+      rc[k] = *reinterpret_cast<const uint4*>(Cb + off);
     }
 #pragma unroll
-    for (int k = 0; k < kXPer; ++k) {
-      const int p8 = (wv + 4 * k) * 8;
-      rx[k] = *reinterpret_cast<const uint4*>(x + ((b * L + t) * s.H + h) * kP + p8);
-    }
-    if (wv == 0) rdt = dt[(b * L + t) * s.H + h];
+    for (int k = 0; k < kXPer; ++k)
+      rx[k] = *reinterpret_cast<const uint4*>(xb + t * HP + (wv + 4 * k) * 8);
+    if (wv == 0) rdt = db[t * s.H];
     if constexpr (HAS_Z) {
       // unconditional loads from a clamped step (a branch per load made the
       // compiler wait for each one); steps past L are never stored
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t tz = min(t0 + 32 * tb + acc_row(v, lane), L - 1);
-        zn[v] = z[((b * L + tz) * s.H + h) * kP + 32 * pb + col];
+        const int tz = min(t0 + 32 * tb + acc_row(v, lane), L - 1);
+        zn[v] = zb[tz * HP + 32 * pb + col];
       }
     }
   };
@@ -170,10 +177,10 @@ __global__ void __launch_bounds__(kThreads)
     }
   };
 
-  const int64_t chunks = (L + kQ - 1) / kQ;
+  const int chunks = (L + kQ - 1) / kQ;
   load_chunk_inputs(0);
-  for (int64_t c = 0; c < chunks; ++c) {
-    const int64_t t0 = c * kQ;
+  for (int c = 0; c < chunks; ++c) {
+    const int t0 = c * kQ;
     // ---- phase 1: the chunk's inputs into LDS
     if (wv == 0) {
       float dl = 0.0f;
@@ -286,7 +293,7 @@ __global__ void __launch_bounds__(kThreads)
       if (t0 + t < L) {
         float y = fmaf(Dh, bf16_bits(xs[v]), ya[v] + yb[v]);
         if constexpr (HAS_Z) y *= silu_f32(bf16_bits(zr[v]));
-        out[((b * L + t0 + t) * s.H + h) * kP + p] = to_bf16(y);
+        ob[(t0 + t) * HP + p] = to_bf16(y);
       }
     }
     const float dec = sm.dec_end;

@@ -628,6 +628,8 @@ int mssm_mamba2_scan_fwd(const void* x, const void* dt, const float* A, const vo
   if (batch * H > INT32_MAX || !product_ok(batch, dim, L, lim) ||
       !product_ok(batch, L, G * N, lim) || !product_ok(batch, dim, N, lim))
     return MSSM_ERR_DIMS;
+  // the kernel indexes one (batch, head)'s rows with 32-bit offsets
+  if (L * dim >= (int64_t(1) << 31) || L * G * N >= (int64_t(1) << 31)) return MSSM_ERR_DIMS;
 
   // x, z, out and B, C rows are read and written in 16-byte pieces
   const void* vecs[] = {x, B, C, out, z};
