@@ -15,7 +15,7 @@
 //   Y      = diag(exp(cum)) C H0^T  +  (L o C B^T) X,
 //            L[t,s] = exp(cum_t - cum_s) Delta_s for s <= t, else 0
 //   H_end  = exp(cum_end) H0  +  (X o w)^T B,  w_s = Delta_s exp(cum_end - cum_s)
-// One workgroup owns one (batch, head) and walks its chunks in order with
+// One workgroup (8 waves) owns one (batch, head) and walks its chunks in order with
 // H in registers, so no state goes to memory between chunks.  C B^T,
 // (L o C B^T) X, C H0^T and (X o w)^T B are 32x32x16 bf16 MFMAs with fp32
 // accumulation.  B, C and x are bf16 inputs and enter exactly; an fp32
@@ -34,7 +34,7 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 constexpr int kQ = 64;         // timesteps per chunk
 constexpr int kP = 64;         // channels per head
-constexpr int kThreads = 256;  // 4 waves
+constexpr int kThreads = 512;  // 8 waves: 4 for the output, 4 for the state
 constexpr int kQP = kQ + 8;    // row pitch (bf16) of [*][kQ] tiles: 16 bytes of
                                // padding keep 16-byte operand reads conflict-free
 
@@ -77,7 +77,10 @@ struct M2Shape {
   int32_t softplus, load_state;
 };
 
-// Grid: one workgroup per (batch entry, head), block = b * H + h.
+// Grid: one workgroup per (batch entry, head), block = b * H + h.  Waves
+// 0-3 own the output: each a 32 x 32 tile (t block, p block) of Y and the
+// matching tile of C B^T.  Waves 4-7 own the state: each the 32 x (N / 2)
+// block (p block, n half) of H.  Every wave loads part of each chunk.
 template <int N, bool HAS_Z>
 __global__ void __launch_bounds__(kThreads)
     mamba2_scan_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt,
@@ -86,16 +89,18 @@ __global__ void __launch_bounds__(kThreads)
                        const uint16_t* __restrict__ z, const float* __restrict__ bias,
                        uint16_t* __restrict__ out, float* __restrict__ state,
                        const M2Shape s) {
-  constexpr int NT = N / 64;  // 32 x 32 state tiles per wave
+  constexpr int NT = N / 64;  // 32 x 32 state tiles per state wave
   __shared__ Smem<N> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
+  const bool ywave = wv < 4;          // output wave (else state wave)
   const int col = lane & 31;
   const int kq = 8 * (lane >> 5);     // this lane's k offset in an operand
-  const int tb = wv >> 1;             // row block of the C B^T and Y tiles (t)
-  const int pb = wv & 1;              // p block of the Y and state tiles; s block of C B^T
-  const int nbase = (wv >> 1) * (N / 2);
+  const int r4 = wv & 3;
+  const int tb = r4 >> 1;             // output waves: t block of Y and C B^T
+  const int pb = r4 & 1;              // p block (Y, H); s block of C B^T
+  const int nbase = (r4 >> 1) * (N / 2);  // state waves: n half
   const int64_t b = blockIdx.x / s.H;
   const int h = (int)(blockIdx.x - b * s.H);
   const int g = h / (s.H / s.G);
@@ -115,13 +120,13 @@ __global__ void __launch_bounds__(kThreads)
   const float bh = bias ? bias[h] : 0.0f;
   const int64_t srow = ((int64_t)b * s.H + h) * kP;  // first state row of the head
 
-  // state tiles: rows p = 32 pb + acc_row, cols n = nbase + 32 i + col
+  // state waves: tiles rows p = 32 pb + acc_row, cols n = nbase + 32 i + col
   f32x16 hacc[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v)
-      hacc[i][v] = s.load_state
+      hacc[i][v] = (!ywave && s.load_state)
                        ? state[(srow + 32 * pb + acc_row(v, lane)) * N + nbase + 32 * i + col]
                        : 0.0f;
   auto state_to_lds = [&]() {
@@ -133,15 +138,14 @@ __global__ void __launch_bounds__(kThreads)
         split(hacc[i][v], sm.H[0][p][n], sm.H[1][p][n]);
       }
   };
-  state_to_lds();
+  if (!ywave) state_to_lds();
 
   // Inputs of a chunk, loaded into registers one chunk ahead.  Lane = step t
   // of the chunk (consecutive lanes write consecutive LDS addresses of the
-  // transposed tiles); wave wv takes the 16-byte pieces wv, wv + 4, ... of a
+  // transposed tiles); wave wv takes the 16-byte pieces wv, wv + 8, ... of a
   // row.
-  constexpr int kBPer = N / 8 / 4;   // pieces of a B (or C) row per wave
-  constexpr int kXPer = kP / 8 / 4;  // pieces of an x row per wave
-  uint4 rb[kBPer], rc[kBPer], rx[kXPer];
+  constexpr int kBPer = N / 8 / 8;   // pieces of a B (or C) row per wave
+  uint4 rb[kBPer], rc[kBPer], rx;
   uint16_t rdt = 0;
   uint16_t zr[16], zn[16];
   auto load_chunk_inputs = [&](int t0) {
@@ -150,21 +154,21 @@ __global__ void __launch_bounds__(kThreads)
     const int t = min(t0 + lane, L - 1);
 #pragma unroll
     for (int k = 0; k < kBPer; ++k) {
-      const int off = t * GN + (wv + 4 * k) * 8;
+      const int off = t * GN + (wv + 8 * k) * 8;
       rb[k] = *reinterpret_cast<const uint4*>(Bb + off);
       rc[k] = *reinterpret_cast<const uint4*>(Cb + off);
     }
-#pragma unroll
-    for (int k = 0; k < kXPer; ++k)
-      rx[k] = *reinterpret_cast<const uint4*>(xb + t * HP + (wv + 4 * k) * 8);
+    rx = *reinterpret_cast<const uint4*>(xb + t * HP + wv * 8);
     if (wv == 0) rdt = db[t * s.H];
     if constexpr (HAS_Z) {
-      // unconditional loads from a clamped step (a branch per load made the
-      // compiler wait for each one); steps past L are never stored
+      if (ywave) {
+        // unconditional loads from a clamped step (a branch per load made
+        // the compiler wait for each one); steps past L are never stored
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int tz = min(t0 + 32 * tb + acc_row(v, lane), L - 1);
-        zn[v] = zb[tz * HP + 32 * pb + col];
+        for (int v = 0; v < 16; ++v) {
+          const int tz = min(t0 + 32 * tb + acc_row(v, lane), L - 1);
+          zn[v] = zb[tz * HP + 32 * pb + col];
+        }
       }
     }
   };
@@ -205,14 +209,13 @@ __global__ void __launch_bounds__(kThreads)
     const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int k = 0; k < kBPer; ++k) {
-      const int n8 = (wv + 4 * k) * 8;
+      const int n8 = (wv + 8 * k) * 8;
       const uint4 vb = live ? rb[k] : zero4, vc = live ? rc[k] : zero4;
       *reinterpret_cast<uint4*>(&sm.B[lane][n8]) = vb;
       *reinterpret_cast<uint4*>(&sm.C[lane][n8]) = vc;
       put_t(sm.Bt, n8, lane, vb);
     }
-#pragma unroll
-    for (int k = 0; k < kXPer; ++k) put_t(sm.Xt, (wv + 4 * k) * 8, lane, live ? rx[k] : zero4);
+    put_t(sm.Xt, wv * 8, lane, live ? rx : zero4);
     if constexpr (HAS_Z) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) zr[v] = zn[v];
@@ -220,102 +223,115 @@ __global__ void __launch_bounds__(kThreads)
     __syncthreads();
     if (c + 1 < chunks) load_chunk_inputs(t0 + kQ);  // lands during phases 2 and 3
 
-    // ---- phase 2: x o w, L o C B^T, and the entering state's part of Y
-    {
-      // every LDS read ahead of the writes, so that one wait covers them
+    f32x16 ya = {}, yb = {};  // output waves: Y, as hi and lo partial sums
+    if (ywave) {
+      // ---- phase 2 (output): L o C B^T, and the entering state's part of Y
+      if (pb <= tb) {  // the block above the diagonal is all zero
+        f32x16 g0 = {}, g1 = {};
+#pragma unroll
+        for (int k0 = 0; k0 < N; k0 += 32) {
+          g0 = mfma(lds8(&sm.C[32 * tb + col][k0 + kq]), lds8(&sm.B[32 * pb + col][k0 + kq]),
+                    g0);
+          g1 = mfma(lds8(&sm.C[32 * tb + col][k0 + 16 + kq]),
+                    lds8(&sm.B[32 * pb + col][k0 + 16 + kq]), g1);
+        }
+        const int sc = 32 * pb + col;
+        const double cs = sm.cum[sc];
+        const float ds = sm.delta[sc];
+        double ct[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) ct[v] = sm.cum[32 * tb + acc_row(v, lane)];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int t = 32 * tb + acc_row(v, lane);
+          const float m =
+              sc <= t ? (g0[v] + g1[v]) * hw_exp2((float)(ct[v] - cs) * kLog2e) * ds : 0.0f;
+          split(m, sm.M[0][t][sc], sm.M[1][t][sc]);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int t = 32 * tb + acc_row(v, lane), sc = 32 * pb + col;
+          sm.M[0][t][sc] = sm.M[1][t][sc] = 0;
+        }
+      }
+#pragma unroll
+      for (int k0 = 0; k0 < N; k0 += 16) {
+        const bf16x8 a = lds8(&sm.C[32 * tb + col][k0 + kq]);
+        ya = mfma(a, lds8(&sm.H[0][32 * pb + col][k0 + kq]), ya);
+        yb = mfma(a, lds8(&sm.H[1][32 * pb + col][k0 + kq]), yb);
+      }
+      float ec[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) ec[v] = sm.ecum[32 * tb + acc_row(v, lane)];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        ya[v] = (ya[v] + yb[v]) * ec[v];
+        yb[v] = 0.0f;
+      }
+    } else {
+      // ---- phase 2 (state): x o w; every LDS read ahead of the writes
+      const int r = wv - 4;
       const float wt = sm.w[lane];
-      uint16_t xv[kXPer][8];
+      uint16_t xv[2][8];
 #pragma unroll
-      for (int k = 0; k < kXPer; ++k)
+      for (int k = 0; k < 2; ++k)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xv[k][j] = sm.Xt[(wv + 4 * k) * 8 + j][lane];
+        for (int j = 0; j < 8; ++j) xv[k][j] = sm.Xt[(r + 4 * k) * 8 + j][lane];
 #pragma unroll
-      for (int k = 0; k < kXPer; ++k)
+      for (int k = 0; k < 2; ++k)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int p = (wv + 4 * k) * 8 + j;
+          const int p = (r + 4 * k) * 8 + j;
           split(bf16_bits(xv[k][j]) * wt, sm.Xw[0][p][lane], sm.Xw[1][p][lane]);
         }
     }
-    if (pb <= tb) {  // the block above the diagonal is all zero
-      f32x16 g0 = {}, g1 = {};
-#pragma unroll
-      for (int k0 = 0; k0 < N; k0 += 32) {
-        g0 = mfma(lds8(&sm.C[32 * tb + col][k0 + kq]), lds8(&sm.B[32 * pb + col][k0 + kq]), g0);
-        g1 = mfma(lds8(&sm.C[32 * tb + col][k0 + 16 + kq]),
-                  lds8(&sm.B[32 * pb + col][k0 + 16 + kq]), g1);
-      }
-      const int sc = 32 * pb + col;
-      const double cs = sm.cum[sc];
-      const float ds = sm.delta[sc];
-      double ct[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) ct[v] = sm.cum[32 * tb + acc_row(v, lane)];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int t = 32 * tb + acc_row(v, lane);
-        const float m = sc <= t ? (g0[v] + g1[v]) * hw_exp2((float)(ct[v] - cs) * kLog2e) * ds
-                                : 0.0f;
-        split(m, sm.M[0][t][sc], sm.M[1][t][sc]);
-      }
-    } else {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int t = 32 * tb + acc_row(v, lane), sc = 32 * pb + col;
-        sm.M[0][t][sc] = sm.M[1][t][sc] = 0;
-      }
-    }
-    f32x16 ya = {}, yb = {};  // hi and lo halves of the state, summed at the end
-#pragma unroll
-    for (int k0 = 0; k0 < N; k0 += 16) {
-      const bf16x8 a = lds8(&sm.C[32 * tb + col][k0 + kq]);
-      ya = mfma(a, lds8(&sm.H[0][32 * pb + col][k0 + kq]), ya);
-      yb = mfma(a, lds8(&sm.H[1][32 * pb + col][k0 + kq]), yb);
-    }
-#pragma unroll
-    for (int v = 0; v < 16; ++v) ya[v] = (ya[v] + yb[v]) * sm.ecum[32 * tb + acc_row(v, lane)];
     __syncthreads();
 
-    // ---- phase 3: (L o C B^T) X, the output, and the state at the chunk end
-    yb = f32x16{};
-#pragma unroll
-    for (int k0 = 0; k0 < kQ; k0 += 16) {
-      const bf16x8 bx = lds8(&sm.Xt[32 * pb + col][k0 + kq]);
-      ya = mfma(lds8(&sm.M[0][32 * tb + col][k0 + kq]), bx, ya);
-      yb = mfma(lds8(&sm.M[1][32 * tb + col][k0 + kq]), bx, yb);
-    }
-    uint16_t xs[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) xs[v] = sm.Xt[32 * pb + col][32 * tb + acc_row(v, lane)];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int t = 32 * tb + acc_row(v, lane), p = 32 * pb + col;
-      if (t0 + t < L) {
-        float y = fmaf(Dh, bf16_bits(xs[v]), ya[v] + yb[v]);
-        if constexpr (HAS_Z) y *= silu_f32(bf16_bits(zr[v]));
-        ob[(t0 + t) * HP + p] = to_bf16(y);
-      }
-    }
-    const float dec = sm.dec_end;
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      f32x16 lo = {};
-#pragma unroll
-      for (int v = 0; v < 16; ++v) hacc[i][v] *= dec;
+    if (ywave) {
+      // ---- phase 3 (output): (L o C B^T) X, the skip, the gate, the store
 #pragma unroll
       for (int k0 = 0; k0 < kQ; k0 += 16) {
-        const bf16x8 bb = lds8(&sm.Bt[nbase + 32 * i + col][k0 + kq]);
-        hacc[i] = mfma(lds8(&sm.Xw[0][32 * pb + col][k0 + kq]), bb, hacc[i]);
-        lo = mfma(lds8(&sm.Xw[1][32 * pb + col][k0 + kq]), bb, lo);
+        const bf16x8 bx = lds8(&sm.Xt[32 * pb + col][k0 + kq]);
+        ya = mfma(lds8(&sm.M[0][32 * tb + col][k0 + kq]), bx, ya);
+        yb = mfma(lds8(&sm.M[1][32 * tb + col][k0 + kq]), bx, yb);
       }
+      uint16_t xs[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) hacc[i][v] += lo[v];
+      for (int v = 0; v < 16; ++v) xs[v] = sm.Xt[32 * pb + col][32 * tb + acc_row(v, lane)];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int t = 32 * tb + acc_row(v, lane), p = 32 * pb + col;
+        if (t0 + t < L) {
+          float y = fmaf(Dh, bf16_bits(xs[v]), ya[v] + yb[v]);
+          if constexpr (HAS_Z) y *= silu_f32(bf16_bits(zr[v]));
+          ob[(t0 + t) * HP + p] = to_bf16(y);
+        }
+      }
+    } else {
+      // ---- phase 3 (state): H = exp(cum_end) H + (X o w)^T B; then the new
+      // state into LDS (the output waves read the old one in phase 2)
+      const float dec = sm.dec_end;
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        f32x16 lo = {};
+#pragma unroll
+        for (int v = 0; v < 16; ++v) hacc[i][v] *= dec;
+#pragma unroll
+        for (int k0 = 0; k0 < kQ; k0 += 16) {
+          const bf16x8 bb = lds8(&sm.Bt[nbase + 32 * i + col][k0 + kq]);
+          hacc[i] = mfma(lds8(&sm.Xw[0][32 * pb + col][k0 + kq]), bb, hacc[i]);
+          lo = mfma(lds8(&sm.Xw[1][32 * pb + col][k0 + kq]), bb, lo);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) hacc[i][v] += lo[v];
+      }
+      state_to_lds();
     }
     __syncthreads();
-    state_to_lds();  // read by the next chunk after its first barrier
   }
 
-  if (state) {
+  if (!ywave && state) {
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
