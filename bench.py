@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TF = 2500.0     # MI355X dense bf16 matrix peak, TFLOP/s
 CUS, SIMDS, LANES, CLOCK_GHZ = 256, 4, 16, 2.4
 # fp32 VALU issue: one wave64 instruction per SIMD per 4 clocks = 16 lanes/clk
 VALU_PEAK_TSLOTS = CUS * SIMDS * LANES * CLOCK_GHZ / 1e3   # 39.32 T lane-slots/s
@@ -83,6 +84,8 @@ def parse():
     ap.add_argument("--backward-steps", type=int, default=20)
     ap.add_argument("--bwd-time-segments", type=int, default=0)
     ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-mamba2", action="store_true")
+    ap.add_argument("--mamba2-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=5.0)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--rocprof-summary", default=None)
@@ -271,6 +274,8 @@ def main():
         res["conv"] = bench_conv(torch, W, m, dev, s, sets, hev, ms)
     if not args.no_decode:
         res["decode"] = bench_decode(torch, W, m, dev, args.decode_steps)
+    if not args.no_mamba2:
+        res["mamba2"] = bench_mamba2(torch, W, m, dev, args.mamba2_steps)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(s, base, args.cpu_seconds, nbytes)
     print(json.dumps(res), flush=True)
@@ -287,6 +292,74 @@ def _time(torch, stream, fn, steps, warmup=3):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def mamba2_flops(s) -> float:
+    """Algorithmic matrix flops of the chunked form (64-step chunks), counting
+    each fp32 product once (not its hi/lo halves): per chunk, the causal half
+    of C B^T (Q^2 N) and of (L o C B^T) X (Q^2 P), C H^T and the state
+    update (2 Q N P each)."""
+    Q = 64
+    chunks = -(-s.seqlen // Q)
+    per = Q * Q * s.dstate + Q * Q * s.headdim + 4 * Q * s.dstate * s.headdim
+    return float(s.batch * s.nheads * chunks * per)
+
+
+def bench_mamba2(torch, W, m, dev, steps=20):
+    """The Mamba-2 block's scan (chunked matrix form on the matrix cores) on
+    the Mamba-2-2.7B-shaped layer, 3 rotating input sets, against the
+    selective scan of the same recurrence with A and the step expanded per
+    channel."""
+    s = W.spec("mamba2_2p7b_layer")
+    stream = torch.cuda.current_stream(dev)
+    sets = []
+    for r in range(3):
+        inp = W.make_mamba2_inputs(W.spec(s.name, seed=s.seed + 1000 * r))
+        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        d["last"] = torch.empty(s.batch, s.dim, s.dstate, device=dev)
+        d["out"] = torch.empty_like(d["x"])
+        sets.append(d)
+
+    def call(i):
+        d = sets[i % len(sets)]
+        m.mamba2_scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
+                          dt_bias=d["dt_bias"], softplus=s.softplus,
+                          last_state=d["last"], out=d["out"])
+    ms = _time(torch, stream, call, steps)
+    d = sets[0]
+    P = s.headdim
+    gen = dict(u=d["x"].reshape(s.batch, s.seqlen, s.dim),
+               delta=d["dt"].repeat_interleave(P, dim=2).contiguous(),
+               A=d["A"].repeat_interleave(P)[:, None].expand(s.dim, s.dstate).contiguous(),
+               D=d["D"].repeat_interleave(P).contiguous(),
+               bias=d["dt_bias"].repeat_interleave(P).contiguous(),
+               z=d["z"].reshape(s.batch, s.seqlen, s.dim),
+               B=d["B"][:, :, 0].contiguous(), C=d["C"][:, :, 0].contiguous())
+    gen_out = torch.empty_like(gen["u"])
+
+    def general(i):
+        m.selective_scan_fwd(gen["u"], gen["delta"], gen["A"], gen["B"], gen["C"],
+                             D=gen["D"], z=gen["z"], delta_bias=gen["bias"],
+                             softplus=s.softplus, last_state=d["last"], out=gen_out,
+                             layout="bld")
+    gen_ms = _time(torch, stream, general, max(3, steps // 4))
+    nbytes = W.mamba2_bytes(s)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tf = mamba2_flops(s) / (ms * 1e-3) / 1e12
+    return {"workload": "%s: batch %d, L %d, %d heads x %d channels, N %d, %d group(s), "
+                        "bf16 activations, fp32 state" % (s.name, s.batch, s.seqlen,
+                                                           s.nheads, s.headdim, s.dstate,
+                                                           s.ngroups),
+            "ms_per_step": round(ms, 5), "steps": steps,
+            "algorithmic_bytes": nbytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": None, "kernel": "mamba2_scan_kernel"},
+            "mfma": {"achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TF, "unit": "TFLOP/s",
+                     "frac": round(tf / MFMA_BF16_PEAK_TF, 4),
+                     "algorithmic_flops": mamba2_flops(s)},
+            "selective_scan_same_recurrence_ms": round(gen_ms, 5),
+            "speedup_vs_selective_scan": round(gen_ms / ms, 2)}
 
 
 def bench_conv(torch, W, m, dev, s, sets, hev, scan_ms, steps=20):
