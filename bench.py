@@ -85,6 +85,10 @@ def parse():
     ap.add_argument("--bwd-time-segments", type=int, default=0)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-mamba2", action="store_true")
+    ap.add_argument("--only-mamba2", action="store_true",
+                    help="run the Mamba-2 scan leg alone (profiling runs)")
+    ap.add_argument("--mamba2-traffic-record", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     ap.add_argument("--mamba2-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=5.0)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -125,9 +129,14 @@ class HipEvents:
         self.hip.hipEventDestroy(h)
 
 
-def kernel_source_hash() -> str:
+MAMBA2_SOURCES = [os.path.join(ROOT, "selective_state_space_52_amd", "csrc", f)
+                  for f in ("mamba2.hip", "dev_math.h")]
+MAMBA2_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mamba2_traffic.json")
+
+
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in sources or KERNEL_SOURCES:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -159,6 +168,9 @@ def main():
     if args.traffic_record:
         traffic_record(args.workload, args.time_segments, *args.traffic_record)
         return
+    if args.mamba2_traffic_record:
+        mamba2_traffic_record(*args.mamba2_traffic_record)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the scan's rows are independent and "
               "this build has no multi-GPU path (DESIGN.md says how it would "
@@ -171,6 +183,10 @@ def main():
     import workloads as W
     import selective_state_space_52_amd as m
 
+    if args.only_mamba2:
+        print(json.dumps({"mamba2": bench_mamba2(torch, W, m, torch.device("cuda:0"),
+                                                 args.mamba2_steps)}), flush=True)
+        return
     over = {"dstate": args.dstate} if args.dstate else {}
     s = W.spec(args.workload, **over)
     dev = torch.device("cuda:0")
@@ -354,7 +370,7 @@ def bench_mamba2(torch, W, m, dev, steps=20):
             "algorithmic_bytes": nbytes,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": None, "kernel": "mamba2_scan_kernel"},
+                         "traffic": load_mamba2_traffic(), "kernel": "mamba2_scan_kernel"},
             "mfma": {"achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TF, "unit": "TFLOP/s",
                      "frac": round(tf / MFMA_BF16_PEAK_TF, 4),
                      "algorithmic_flops": mamba2_flops(s)},
@@ -642,6 +658,38 @@ def traffic_record(workload, time_segments, fetch_dir, write_dir, cfetch_dir, cw
         "hbm_bytes_per_call": int(round((fk * f_factor + wk * w_factor) * 1024)),
         "algorithmic_bytes": W.scan_bytes(s)}}
     print(json.dumps(rec, indent=1))
+
+
+def mamba2_traffic_record(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
+    """HBM bytes per Mamba-2 scan call (one kernel) from FETCH_SIZE and
+    WRITE_SIZE, scaled as for the forward scan by torch's 1 GiB copy."""
+    import workloads as W
+    copy_kib = float(1 << 20)
+    f_factor = copy_kib / _counter_mean(cfetch_dir, "copyBuffer", "FETCH_SIZE")
+    w_factor = copy_kib / _counter_mean(cwrite_dir, "copyBuffer", "WRITE_SIZE")
+    fk, calls = _counter_sum(fetch_dir, "mamba2_scan_kernel", "FETCH_SIZE")
+    wk, _ = _counter_sum(write_dir, "mamba2_scan_kernel", "WRITE_SIZE")
+    s = W.spec("mamba2_2p7b_layer")
+    rec = {"mamba2_2p7b_layer": {
+        "kernel_source_sha256_16": kernel_source_hash(MAMBA2_SOURCES),
+        "calls": calls,
+        "fetch_kib_per_call": round(fk / calls, 1), "write_kib_per_call": round(wk / calls, 1),
+        "copy_fetch_factor": round(f_factor, 5), "copy_write_factor": round(w_factor, 5),
+        "hbm_bytes_per_call": int(round((fk * f_factor + wk * w_factor) / calls * 1024)),
+        "algorithmic_bytes": W.mamba2_bytes(s)}}
+    print(json.dumps(rec, indent=1))
+
+
+def load_mamba2_traffic():
+    """The recorded HBM bytes per Mamba-2 call, if taken with this kernel source."""
+    try:
+        with open(MAMBA2_TRAFFIC_FILE) as f:
+            rec = json.load(f).get("mamba2_2p7b_layer")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_source_sha256_16") != kernel_source_hash(MAMBA2_SOURCES):
+        return None
+    return rec.get("hbm_bytes_per_call")
 
 
 def _kname(name: str) -> str:
