@@ -229,12 +229,18 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
  *               NULL; with MSSM_FLAG_LOAD_STATE it holds the initial state
  *               on entry (required then)
  * dims: io_dtype must be MSSM_BF16, dstate 64 or 128, headdim 64, nheads a
- * multiple of ngroups, time_segments 0, and seqlen * dim and seqlen *
- * ngroups * dstate below 2^31; flags may hold only MSSM_FLAG_LOAD_STATE.  x, z, out, B and C must be 16-byte aligned.  out
- * and last_state must not overlap an input or each other.  The call runs
- * the chunked matrix form of the recurrence on the matrix cores, one
- * workgroup per (batch entry, head); results agree with the sequential
- * recurrence up to rounding.  It allocates nothing.
+ * multiple of ngroups, and seqlen * dim and seqlen * ngroups * dstate below
+ * 2^31; flags may hold only MSSM_FLAG_LOAD_STATE.  x, z, out, B and C must
+ * be 16-byte aligned.  out and last_state must not overlap an input or each
+ * other.  The call runs the chunked matrix form of the recurrence on the
+ * matrix cores, one workgroup per (batch entry, head) and time segment;
+ * results agree with the sequential recurrence up to rounding.
+ * time_segments: 0 lets the library cut the rows of the (batch, head) pairs
+ * beyond whole rounds of compute units (all pairs, when there are fewer
+ * than compute units) into time segments joined by a carried state; k >= 1
+ * cuts every pair into about k segments of whole 64-step chunks (1: none).
+ * Segments take a stream-ordered workspace of about 8 * 64 * dstate bytes
+ * per segment, returned on the same stream; unsplit calls allocate nothing.
  */
 int mssm_mamba2_scan_fwd(const void* x, const void* dt, const float* A, const void* B,
                          const void* C, const float* D, const void* z,

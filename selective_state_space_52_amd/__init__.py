@@ -314,13 +314,15 @@ def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
 
 
 def mamba2_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True,
-                    last_state=None, load_state=False, out=None):
+                    last_state=None, load_state=False, out=None, time_segments=0):
     """The Mamba-2 block's scan (mssm_mamba2_scan_fwd), bf16 activations.
 
     x, z: (batch, L, nheads, headdim) with headdim 64; dt: (batch, L, nheads);
     A, D, dt_bias: (nheads,) fp32; B, C: (batch, L, ngroups, N) with N 64 or
     128; last_state: (batch, nheads * headdim, N) fp32 receiving the final
-    state (holding the initial one when load_state).  Returns out, shaped as x.
+    state (holding the initial one when load_state).  time_segments: 0 lets
+    the library cut rows in time to fill the GPU, k >= 1 asks for k segments.
+    Returns out, shaped as x.
     """
     if x.dim() != 4 or x.dtype != torch.bfloat16:
         raise ValueError("x must be a (batch, L, nheads, headdim) bfloat16 tensor")
@@ -343,7 +345,8 @@ def mamba2_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True,
     if out is None:
         out = torch.empty_like(x)
     _need(out, "out", torch.bfloat16, (batch, L, H, P), dev)
-    dims = Dims(batch, H * P, N, L, _IO[torch.bfloat16], 1 if load_state else 0, 0, G)
+    dims = Dims(batch, H * P, N, L, _IO[torch.bfloat16], 1 if load_state else 0,
+                int(time_segments), G)
     with torch.cuda.device(dev):
         check(lib().mssm_mamba2_scan_fwd(
             _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),

@@ -23,6 +23,8 @@
 // lo = RNE(v - hi)), which keeps 16 mantissa bits, and costs a second MFMA.
 // The cumulative sums are kept in fp64, so the decay between two steps
 // carries the rounding of that difference only.
+#include <algorithm>
+
 #include "dev_math.h"
 #include "mssm_internal.h"
 
@@ -51,7 +53,7 @@ __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {  // 16-byte aligned
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ void split(float v, uint16_t& hi, uint16_t& lo) {
+__device__ __forceinline__ void split_hl(float v, uint16_t& hi, uint16_t& lo) {
   hi = to_bf16(v);
   lo = to_bf16(v - bf16_bits(hi));
 }
@@ -75,6 +77,18 @@ struct M2Shape {
   int64_t L;
   int32_t H, G;  // heads, B/C groups
   int32_t softplus, load_state;
+  // Time split: (batch, head) pairs [0, whole) are scanned whole; the others
+  // are cut into P segments of seg_chunks chunks.  Pass 0 runs n_agg
+  // aggregate tasks (segments 0 .. P-2 of the split pairs, from a zero state,
+  // state only) ahead of the whole pairs; pass 1 runs every segment of the
+  // split pairs from its entering state.
+  int32_t whole, P, seg_chunks, n_agg, pass;
+};
+
+struct M2Work {
+  float* S;         // aggregate tasks' end states, (split, P - 1, 64, N)
+  double* sum;      // aggregate tasks' sums of Delta A, (split, P - 1)
+  const float* hin; // segments' entering states, (split, P, 64, N)
 };
 
 // Grid: one workgroup per (batch entry, head), block = b * H + h.  Waves
@@ -88,7 +102,7 @@ __global__ void __launch_bounds__(kThreads)
                        const uint16_t* __restrict__ Cm, const float* __restrict__ Dv,
                        const uint16_t* __restrict__ z, const float* __restrict__ bias,
                        uint16_t* __restrict__ out, float* __restrict__ state,
-                       const M2Shape s) {
+                       const M2Shape s, const M2Work ws) {
   constexpr int NT = N / 64;  // 32 x 32 state tiles per state wave
   __shared__ Smem<N> sm;
   const int tid = threadIdx.x;
@@ -101,10 +115,31 @@ __global__ void __launch_bounds__(kThreads)
   const int tb = r4 >> 1;             // output waves: t block of Y and C B^T
   const int pb = r4 & 1;              // p block (Y, H); s block of C B^T
   const int nbase = (r4 >> 1) * (N / 2);  // state waves: n half
-  const int64_t b = blockIdx.x / s.H;
-  const int h = (int)(blockIdx.x - b * s.H);
+  // task -> (pair, segment, kind)
+  int pair, seg = 0;
+  bool agg = false, split = false;
+  if (s.pass == 0) {
+    if ((int)blockIdx.x < s.n_agg) {
+      agg = true;
+      pair = s.whole + (int)blockIdx.x / (s.P - 1);
+      seg = (int)blockIdx.x % (s.P - 1);
+    } else {
+      pair = (int)blockIdx.x - s.n_agg;
+    }
+  } else {
+    split = true;
+    pair = s.whole + (int)blockIdx.x / s.P;
+    seg = (int)blockIdx.x % s.P;
+  }
+  const int sp = pair - s.whole;  // index among the split pairs
+  const int64_t b = pair / s.H;
+  const int h = pair - (int)b * s.H;
   const int g = h / (s.H / s.G);
   const int L = (int)s.L;
+  const int t_begin = (agg || split) ? seg * s.seg_chunks * kQ : 0;
+  const int t_end = (agg || split) ? min(L, t_begin + s.seg_chunks * kQ) : L;
+  const bool emit = !agg;  // outputs are written (not by aggregate tasks)
+  const int64_t seg_elems = (int64_t)kP * N;
   // this (batch, head)'s rows: step t of x, z, out at t * HP (+ channel), of
   // B, C at t * GN (+ state), of dt at t * H; the host keeps every such
   // offset below 2^31
@@ -120,14 +155,18 @@ __global__ void __launch_bounds__(kThreads)
   const float bh = bias ? bias[h] : 0.0f;
   const int64_t srow = ((int64_t)b * s.H + h) * kP;  // first state row of the head
 
-  // state waves: tiles rows p = 32 pb + acc_row, cols n = nbase + 32 i + col
+  // state waves: tiles rows p = 32 pb + acc_row, cols n = nbase + 32 i + col;
+  // the entering state is the caller's (whole pairs), zero (aggregate
+  // tasks) or the segment's entering state (split pairs)
+  const float* h_in = split ? ws.hin + ((int64_t)sp * s.P + seg) * seg_elems
+                            : (s.load_state && !agg ? state + srow * N : nullptr);
   f32x16 hacc[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v)
-      hacc[i][v] = (!ywave && s.load_state)
-                       ? state[(srow + 32 * pb + acc_row(v, lane)) * N + nbase + 32 * i + col]
+      hacc[i][v] = (!ywave && h_in)
+                       ? h_in[(32 * pb + acc_row(v, lane)) * N + nbase + 32 * i + col]
                        : 0.0f;
   auto state_to_lds = [&]() {
 #pragma unroll
@@ -135,7 +174,7 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int p = 32 * pb + acc_row(v, lane), n = nbase + 32 * i + col;
-        split(hacc[i][v], sm.H[0][p][n], sm.H[1][p][n]);
+        split_hl(hacc[i][v], sm.H[0][p][n], sm.H[1][p][n]);
       }
   };
   if (!ywave) state_to_lds();
@@ -149,9 +188,9 @@ __global__ void __launch_bounds__(kThreads)
   uint16_t rdt = 0;
   uint16_t zr[16], zn[16];
   auto load_chunk_inputs = [&](int t0) {
-    // steps past L load the last step (clamped address) and are zeroed when
-    // written to LDS
-    const int t = min(t0 + lane, L - 1);
+    // steps past the task's end load its last step (clamped address) and
+    // are zeroed when written to LDS
+    const int t = min(t0 + lane, t_end - 1);
 #pragma unroll
     for (int k = 0; k < kBPer; ++k) {
       const int off = t * GN + (wv + 8 * k) * 8;
@@ -166,7 +205,7 @@ __global__ void __launch_bounds__(kThreads)
         // the compiler wait for each one); steps past L are never stored
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int tz = min(t0 + 32 * tb + acc_row(v, lane), L - 1);
+          const int tz = min(t0 + 32 * tb + acc_row(v, lane), t_end - 1);
           zn[v] = zb[tz * HP + 32 * pb + col];
         }
       }
@@ -181,14 +220,15 @@ __global__ void __launch_bounds__(kThreads)
     }
   };
 
-  const int chunks = (L + kQ - 1) / kQ;
-  load_chunk_inputs(0);
+  const int chunks = (t_end - t_begin + kQ - 1) / kQ;
+  double seg_sum = 0.0;  // aggregate tasks: sum of Delta A over the segment
+  load_chunk_inputs(t_begin);
   for (int c = 0; c < chunks; ++c) {
-    const int t0 = c * kQ;
+    const int t0 = t_begin + c * kQ;
     // ---- phase 1: the chunk's inputs into LDS
     if (wv == 0) {
       float dl = 0.0f;
-      if (t0 + lane < L) {
+      if (t0 + lane < t_end) {
         const float v = bf16_bits(rdt) + bh;
         dl = s.softplus ? softplus_f32(v) : v;
       }
@@ -204,8 +244,9 @@ __global__ void __launch_bounds__(kThreads)
       sm.ecum[lane] = hw_exp2((float)cs * kLog2e);
       sm.w[lane] = dl * hw_exp2((float)(end - cs) * kLog2e);
       if (lane == 0) sm.dec_end = hw_exp2((float)end * kLog2e);
+      seg_sum += end;
     }
-    const bool live = t0 + lane < L;
+    const bool live = t0 + lane < t_end;
     const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int k = 0; k < kBPer; ++k) {
@@ -224,7 +265,7 @@ __global__ void __launch_bounds__(kThreads)
     if (c + 1 < chunks) load_chunk_inputs(t0 + kQ);  // lands during phases 2 and 3
 
     f32x16 ya = {}, yb = {};  // output waves: Y, as hi and lo partial sums
-    if (ywave) {
+    if (ywave && emit) {
       // ---- phase 2 (output): L o C B^T, and the entering state's part of Y
       if (pb <= tb) {  // the block above the diagonal is all zero
         f32x16 g0 = {}, g1 = {};
@@ -246,7 +287,7 @@ __global__ void __launch_bounds__(kThreads)
           const int t = 32 * tb + acc_row(v, lane);
           const float m =
               sc <= t ? (g0[v] + g1[v]) * hw_exp2((float)(ct[v] - cs) * kLog2e) * ds : 0.0f;
-          split(m, sm.M[0][t][sc], sm.M[1][t][sc]);
+          split_hl(m, sm.M[0][t][sc], sm.M[1][t][sc]);
         }
       } else {
 #pragma unroll
@@ -269,7 +310,7 @@ __global__ void __launch_bounds__(kThreads)
         ya[v] = (ya[v] + yb[v]) * ec[v];
         yb[v] = 0.0f;
       }
-    } else {
+    } else if (!ywave) {
       // ---- phase 2 (state): x o w; every LDS read ahead of the writes
       const int r = wv - 4;
       const float wt = sm.w[lane];
@@ -283,12 +324,12 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int p = (r + 4 * k) * 8 + j;
-          split(bf16_bits(xv[k][j]) * wt, sm.Xw[0][p][lane], sm.Xw[1][p][lane]);
+          split_hl(bf16_bits(xv[k][j]) * wt, sm.Xw[0][p][lane], sm.Xw[1][p][lane]);
         }
     }
     __syncthreads();
 
-    if (ywave) {
+    if (ywave && emit) {
       // ---- phase 3 (output): (L o C B^T) X, the skip, the gate, the store
 #pragma unroll
       for (int k0 = 0; k0 < kQ; k0 += 16) {
@@ -302,13 +343,13 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int t = 32 * tb + acc_row(v, lane), p = 32 * pb + col;
-        if (t0 + t < L) {
+        if (t0 + t < t_end) {
           float y = fmaf(Dh, bf16_bits(xs[v]), ya[v] + yb[v]);
           if constexpr (HAS_Z) y *= silu_f32(bf16_bits(zr[v]));
           ob[(t0 + t) * HP + p] = to_bf16(y);
         }
       }
-    } else {
+    } else if (!ywave) {
       // ---- phase 3 (state): H = exp(cum_end) H + (X o w)^T B; then the new
       // state into LDS (the output waves read the old one in phase 2)
       const float dec = sm.dec_end;
@@ -331,37 +372,138 @@ __global__ void __launch_bounds__(kThreads)
     __syncthreads();
   }
 
-  if (!ywave && state) {
+  // the end state: the caller's (whole pairs, a split pair's last segment)
+  // or the aggregate task's
+  float* h_out = agg ? ws.S + ((int64_t)sp * (s.P - 1) + seg) * seg_elems
+                     : ((!split || seg == s.P - 1) && state ? state + srow * N : nullptr);
+  if (!ywave && h_out) {
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        state[(srow + 32 * pb + acc_row(v, lane)) * N + nbase + 32 * i + col] = hacc[i][v];
+        h_out[(32 * pb + acc_row(v, lane)) * N + nbase + 32 * i + col] = hacc[i][v];
   }
+  if (agg && tid == 0) ws.sum[(int64_t)sp * (s.P - 1) + seg] = seg_sum;
+}
+
+// Entering state of every segment of the split pairs, per (split pair, state
+// element): h_in[0] = the caller's initial state (or 0), h_in[k + 1] =
+// exp(sum_k) h_in[k] + S_k, in fp64.
+__global__ void __launch_bounds__(256)
+    mamba2_combine_kernel(const float* __restrict__ state, const float* __restrict__ S,
+                          const double* __restrict__ sum, float* __restrict__ hin,
+                          int whole, int split, int P, int64_t seg_elems, int load_state) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)split * seg_elems) return;
+  const int sp = (int)(i / seg_elems);
+  const int64_t e = i - (int64_t)sp * seg_elems;
+  double h = load_state ? (double)state[(int64_t)(whole + sp) * seg_elems + e] : 0.0;
+  for (int k = 0; k < P; ++k) {
+    hin[((int64_t)sp * P + k) * seg_elems + e] = (float)h;
+    if (k + 1 < P)
+      h = exp(sum[(int64_t)sp * (P - 1) + k]) * h +
+          (double)S[((int64_t)sp * (P - 1) + k) * seg_elems + e];
+  }
+}
+
+template <int N, bool HAS_Z>
+hipError_t launch_pass(const Mamba2Params& p, const M2Shape& s, const M2Work& ws,
+                       int grid, hipStream_t st) {
+  hipLaunchKernelGGL((mamba2_scan_kernel<N, HAS_Z>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     st, static_cast<const uint16_t*>(p.x), static_cast<const uint16_t*>(p.dt),
+                     p.A, static_cast<const uint16_t*>(p.B), static_cast<const uint16_t*>(p.C),
+                     p.D, static_cast<const uint16_t*>(p.z), p.bias,
+                     static_cast<uint16_t*>(p.out), p.state, s, ws);
+  return hipGetLastError();
 }
 
 template <int N>
 hipError_t launch_n(const Mamba2Params& p, hipStream_t st) {
-  const M2Shape s{p.L, (int32_t)p.nheads, (int32_t)p.ngroups, p.softplus, p.load_state};
-  const dim3 grid((unsigned)(p.batch * p.nheads)), block(kThreads);
-  const auto* x = static_cast<const uint16_t*>(p.x);
-  const auto* dt = static_cast<const uint16_t*>(p.dt);
-  const auto* B = static_cast<const uint16_t*>(p.B);
-  const auto* C = static_cast<const uint16_t*>(p.C);
-  const auto* z = static_cast<const uint16_t*>(p.z);
-  auto* out = static_cast<uint16_t*>(p.out);
-  if (p.z)
-    hipLaunchKernelGGL((mamba2_scan_kernel<N, true>), grid, block, 0, st, x, dt, p.A, B, C,
-                       p.D, z, p.bias, out, p.state, s);
-  else
-    hipLaunchKernelGGL((mamba2_scan_kernel<N, false>), grid, block, 0, st, x, dt, p.A, B,
-                       C, p.D, z, p.bias, out, p.state, s);
-  return hipGetLastError();
+  M2Shape s{p.L, (int32_t)p.nheads, (int32_t)p.ngroups, p.softplus, p.load_state,
+            (int32_t)p.whole, p.segments, p.seg_chunks, 0, 0};
+  const int split = (int)(p.batch * p.nheads - p.whole);
+  const M2Work ws{p.ws_S, p.ws_sum, p.ws_hin};
+  s.n_agg = split > 0 ? split * (p.segments - 1) : 0;
+  auto pass = [&](int grid) {
+    return p.z ? launch_pass<N, true>(p, s, ws, grid, st)
+               : launch_pass<N, false>(p, s, ws, grid, st);
+  };
+  hipError_t e = hipSuccess;
+  if (s.n_agg + s.whole > 0) {
+    s.pass = 0;
+    e = pass(s.n_agg + s.whole);
+  }
+  if (e == hipSuccess && split > 0) {
+    const int64_t seg_elems = (int64_t)kP * N;
+    const int64_t threads = split * seg_elems;
+    hipLaunchKernelGGL(mamba2_combine_kernel, dim3((unsigned)((threads + 255) / 256)),
+                       dim3(256), 0, st, p.state, p.ws_S, p.ws_sum, p.ws_hin, (int)p.whole,
+                       split, p.segments, seg_elems, p.load_state);
+    e = hipGetLastError();
+    if (e == hipSuccess) {
+      s.pass = 1;
+      e = pass(split * p.segments);
+    }
+  }
+  return e;
 }
 
 }  // namespace
 
 int mamba2_headdim() { return kP; }
+
+// The time split (pure arithmetic).  A workgroup scans its rows in a fixed
+// time per chunk whatever the load, so pairs beyond whole rounds of CUs (or
+// all pairs, when there are fewer than CUs) are cut into segments that fill
+// the CUs, at the cost of a state-only pass over all but their last segment.
+void mamba2_plan(int64_t pairs, int64_t L, int cus, int forced, Mamba2Params* p) {
+  const int64_t chunks = (L + kQ - 1) / kQ;
+  int64_t whole = pairs, P = 1;
+  if (forced > 0) {
+    P = forced;
+    if (P > 1) whole = 0;
+  } else if (pairs >= cus) {
+    const int64_t rest = pairs % cus;
+    if (rest > 0) {
+      P = cus / rest;
+      if (P > 1) whole = pairs - rest;
+    }
+  } else {
+    P = cus / pairs;
+    if (P > 1) whole = 0;
+  }
+  P = std::min<int64_t>(P, chunks);
+  int64_t seg_chunks = chunks;
+  if (P > 1) {
+    seg_chunks = (chunks + P - 1) / P;
+    P = (chunks + seg_chunks - 1) / seg_chunks;  // whole chunks per segment
+  }
+  if (P < 2) {
+    whole = pairs;
+    P = 1;
+    seg_chunks = chunks;
+  }
+  p->whole = whole;
+  p->segments = (int32_t)P;
+  p->seg_chunks = (int32_t)seg_chunks;
+}
+
+int64_t mamba2_workspace(const Mamba2Params& p, void* ws, Mamba2Params* q) {
+  const int64_t split = p.batch * p.nheads - p.whole;
+  if (split <= 0) return 0;
+  const int64_t seg = (int64_t)kP * p.N;
+  const int64_t bS = split * (p.segments - 1) * seg * 4;
+  const int64_t bsum = split * (p.segments - 1) * 8;
+  const int64_t bhin = split * p.segments * seg * 4;
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  if (ws && q) {
+    char* base = static_cast<char*>(ws);
+    q->ws_S = reinterpret_cast<float*>(base);
+    q->ws_sum = reinterpret_cast<double*>(base + up(bS));
+    q->ws_hin = reinterpret_cast<float*>(base + up(bS) + up(bsum));
+  }
+  return up(bS) + up(bsum) + up(bhin);
+}
 
 hipError_t launch_mamba2_scan(const Mamba2Params& p, hipStream_t st) {
   switch (p.N) {

@@ -611,7 +611,7 @@ int mssm_mamba2_scan_fwd(const void* x, const void* dt, const float* A, const vo
   if (dims->io_dtype != MSSM_BF16) return MSSM_ERR_UNSUPPORTED;
   if (dims->flags & ~MSSM_FLAG_LOAD_STATE) return MSSM_ERR_UNSUPPORTED;
   if (dims->batch <= 0 || dims->dim <= 0 || dims->seqlen <= 0 || dims->dstate <= 0 ||
-      dims->ngroups < 0 || dims->time_segments != 0 || headdim <= 0)
+      dims->ngroups < 0 || dims->time_segments < 0 || headdim <= 0)
     return MSSM_ERR_DIMS;
   if (dims->dstate != 64 && dims->dstate != 128) return MSSM_ERR_UNSUPPORTED;
   if (headdim != mssm::mamba2_headdim()) return MSSM_ERR_UNSUPPORTED;
@@ -654,22 +654,47 @@ int mssm_mamba2_scan_fwd(const void* x, const void* dt, const float* A, const vo
   if (overlap(r_out, r_state)) return MSSM_ERR_ALIAS;
 
   // --- validation done; HIP calls from here on ---
+  if (g_cu_count <= 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) ==
+            hipSuccess &&
+        cus > 0)
+      g_cu_count = cus;
+  }
   mssm::Mamba2Params p;
+  std::memset(&p, 0, sizeof(p));
   p.x = x; p.dt = dt; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.bias = dt_bias;
   p.out = out; p.state = last_state;
   p.batch = batch; p.L = L; p.nheads = H; p.ngroups = G; p.N = N;
   p.softplus = softplus ? 1 : 0;
   p.load_state = load_state ? 1 : 0;
+  mssm::mamba2_plan(batch * H, L, g_cu_count > 0 ? g_cu_count : kDefaultCUs,
+                    dims->time_segments, &p);
   hipStream_t st = (hipStream_t)stream;
+  const int64_t ws_bytes = mssm::mamba2_workspace(p, nullptr, nullptr);
+  void* ws = nullptr;
   hipError_t e = hipSuccess;
+  if (ws_bytes > 0) {
+    e = hipMallocAsync(&ws, (size_t)ws_bytes, st);
+    if (e != hipSuccess) {
+      set_hip_error("hipMallocAsync(workspace)", e);
+      return MSSM_ERR_HIP;
+    }
+    mssm::mamba2_workspace(p, ws, &p);
+  }
   if (g_ev_start) e = hipEventRecord((hipEvent_t)g_ev_start, st);
   if (e == hipSuccess) e = mssm::launch_mamba2_scan(p, st);
   if (e == hipSuccess && g_ev_stop) e = hipEventRecord((hipEvent_t)g_ev_stop, st);
-  if (e != hipSuccess) {
-    set_hip_error("mamba2 scan launch", e);
-    return MSSM_ERR_HIP;
+  if (e != hipSuccess) set_hip_error("mamba2 scan launch", e);
+  if (ws) {
+    const hipError_t f = hipFreeAsync(ws, st);
+    if (e == hipSuccess && f != hipSuccess) {
+      set_hip_error("hipFreeAsync(workspace)", f);
+      e = f;
+    }
   }
-  return MSSM_OK;
+  return e == hipSuccess ? MSSM_OK : MSSM_ERR_HIP;
 }
 
 }  // extern "C"

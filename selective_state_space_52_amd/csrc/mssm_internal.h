@@ -206,8 +206,20 @@ struct Mamba2Params {
   float* state;       // may be null unless load_state
   int64_t batch, L, nheads, ngroups, N;
   int32_t softplus, load_state;
+  // time split (mamba2_plan) and its workspace (mamba2_workspace)
+  int64_t whole;
+  int32_t segments, seg_chunks;
+  float* ws_S;
+  double* ws_sum;
+  float* ws_hin;
 };
 int mamba2_headdim();
+// Pairs scanned whole, segments and chunks per segment of the rest; forced
+// > 0 asks for that many segments of every pair.
+void mamba2_plan(int64_t pairs, int64_t L, int cus, int forced, Mamba2Params* p);
+// Workspace bytes of the split; with ws and q non-null also points q's
+// workspace fields into ws.
+int64_t mamba2_workspace(const Mamba2Params& p, void* ws, Mamba2Params* q);
 hipError_t launch_mamba2_scan(const Mamba2Params& p, hipStream_t stream);
 
 }  // namespace mssm

@@ -255,7 +255,7 @@ def test_mamba2_validation_codes(L):
     assert m2(_dims(**ok), headdim=32) == -3                # headdim 64
     assert m2(_dims(**dict(ok, dim=100))) == -2             # dim not a multiple
     assert m2(_dims(**dict(ok, flags=2))) == -3             # no layout flag
-    assert m2(_dims(**dict(ok, ts=2))) == -2
+    assert m2(_dims(**dict(ok, ts=-1))) == -2
     assert m2(_dims(**dict(ok, groups=3))) == -3            # 4 heads, 3 groups
     assert m2(_dims(**dict(ok, L_=0))) == -2
     assert m2(_dims(**ok), x=BASE + 8) == -4                # 16-byte pieces

@@ -21,7 +21,7 @@ def _report(what, worst):
     print("%-56s worst err/bar = %.3g (parity), %.3g (tight)" % (what, *worst), flush=True)
 
 
-def _run(inp, h0=None):
+def _run(inp, h0=None, time_segments=0):
     import selective_state_space_52_amd as m
     x = to_dev(inp["x"])
     batch, L, H, P = x.shape
@@ -31,7 +31,8 @@ def _run(inp, h0=None):
     out = m.mamba2_scan_fwd(x, to_dev(inp["dt"]), to_dev(inp["A"]), to_dev(inp["B"]),
                             to_dev(inp["C"]), D=to_dev(inp["D"]), z=to_dev(inp["z"]),
                             dt_bias=to_dev(inp["dt_bias"]), softplus=inp["softplus"],
-                            last_state=last, load_state=h0 is not None)
+                            last_state=last, load_state=h0 is not None,
+                            time_segments=time_segments)
     torch.cuda.synchronize()
     return out.cpu(), last.cpu()
 
@@ -105,6 +106,30 @@ def test_mamba2_loaded_state_and_split(N):
     o2, l2 = _run(second, h0=l1)
     check_out(torch.cat([o1, o2], dim=1), ro, "bf16", "split out")
     check_state(l2, rl, "split last_state")
+
+
+SEGMENTS = [
+    # batch, L, heads, N, segments -- 1: no split; ragged last segments
+    (2, 200, 4, 64, 1),
+    (1, 1000, 2, 128, 1),
+    (2, 300, 3, 64, 2),
+    (1, 333, 2, 128, 3),
+    (1, 640, 2, 64, 10),   # one chunk per segment
+]
+
+
+@pytest.mark.parametrize("batch,L,H,N,P", SEGMENTS,
+                         ids=["b%d-l%d-h%d-n%d-p%d" % c for c in SEGMENTS])
+def test_mamba2_time_segments(batch, L, H, N, P):
+    """Rows cut into forced time segments (a state-only pass, the combine and
+    the segments from their entering states), with a loaded initial state."""
+    s = W.spec("mamba2_2p7b_layer", batch=batch, seqlen=L, nheads=H, dstate=N, seed=950 + P)
+    inp = W.make_mamba2_inputs(s)
+    h0 = W.mamba2_initial_state(s)
+    out, last = _run(inp, h0=h0, time_segments=P)
+    ro, rl = _oracle(inp, h0=h0)
+    _report("mamba2 segments %s" % ((batch, L, H, N, P),), check_out(out, ro, "bf16", "out"))
+    check_state(last, rl, "last_state")
 
 
 def test_mamba2_full_size_sampled_heads():
