@@ -412,32 +412,37 @@ __global__ void __launch_bounds__(kLanes* NG)
     load_chunk<BF16, VEC, KC>(no, dout, off, nv, s.ts);
   };
   // state at the start of a tile: kept from zero, plus the decayed h_in
-  auto checkpoint = [&](int tile, float (&hc)[NPW]) {
-    const float c = cd[(int64_t)tile * kLanes + lane];
+  // The checkpoint is loaded a tile ahead and combined where it is used: an
+  // arithmetic use right after the load would wait for every load in flight.
+  auto load_checkpoint = [&](int tile, float (&raw)[NPW + 1]) {
 #pragma unroll
-    for (int j = 0; j < NPW; ++j)
-      hc[j] = fmaf(hw_exp2(A2[j] * c), hin[j],
-                   ck[((int64_t)tile * N + n0 + j) * kLanes + lane]);
+    for (int j = 0; j < NPW; ++j) raw[j] = ck[((int64_t)tile * N + n0 + j) * kLanes + lane];
+    raw[NPW] = cd[(int64_t)tile * kLanes + lane];
+  };
+  auto finish_checkpoint = [&](const float (&raw)[NPW + 1], float (&hc)[NPW]) {
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) hc[j] = fmaf(hw_exp2(A2[j] * raw[NPW]), hin[j], raw[j]);
   };
 
   const int last = k.tile_end - 1;
   load_r((int64_t)last * T);
   prep_r((int64_t)last * T);
   float hck[NPW];
-  checkpoint(last, hck);
+  {
+    float raw[NPW + 1];
+    load_checkpoint(last, raw);
+    finish_checkpoint(raw, hck);
+  }
   __syncthreads();
 
   for (int ti = last; ti >= k.tile_begin; --ti) {
     const int64_t tb = (int64_t)ti * T;
     const bool more = ti > k.tile_begin;
     // prefetch the previous tile's inputs and checkpoint, warm its B/C lines
-    float hnx[NPW];
+    float hraw[NPW + 1];
     if (more) {
       load_r(tb - T);
-      checkpoint(ti - 1, hnx);
-    } else {
-#pragma unroll
-      for (int j = 0; j < NPW; ++j) hnx[j] = 0.0f;
+      load_checkpoint(ti - 1, hraw);
     }
     const uint32_t touch = more ? warm_tile<WPS>(bcw, ti - 1) : 0u;
 
@@ -533,6 +538,12 @@ __global__ void __launch_bounds__(kLanes* NG)
         dDacc = fmaf(cDy[q], cU[q], dDacc);
         dbacc += q < nv ? ddl : 0.0f;
       }
+      // the prefetched inputs and checkpoint are consumed before the stores:
+      // the counter a load's wait reads also counts stores issued after it
+      if (more) {
+        prep_r(tb - T);
+        finish_checkpoint(hraw, hck);
+      }
       if (k.valid) {
         const int64_t off = k.rowoff + tc * s.ts;
         store_chunk<BF16, VEC, KC>(du, off, odu, nv, s.ts);
@@ -540,9 +551,6 @@ __global__ void __launch_bounds__(kLanes* NG)
         if constexpr (HAS_Z) store_chunk<BF16, VEC, KC>(dz, off, odz, nv, s.ts);
       }
     }
-    if (more) prep_r(tb - T);
-#pragma unroll
-    for (int j = 0; j < NPW; ++j) hck[j] = hnx[j];
     asm volatile("" ::"s"(touch));  // keeps the warming loads
     __syncthreads();
   }
