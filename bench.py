@@ -172,9 +172,9 @@ def main():
         mamba2_traffic_record(*args.mamba2_traffic_record)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: the scan's rows are independent and "
-              "this build has no multi-GPU path (DESIGN.md says how it would "
-              "shard); run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the scan's rows are independent, so a "
+              "multi-GPU run would shard them with no exchange, and this library "
+              "has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
     if args.copy_calibration:

@@ -63,7 +63,7 @@ def build(force: bool = True) -> str:
 
 
 def asm(src: str = "scan_fwd.hip", out: str = None) -> str:
-    """gfx950 assembly of one source (for reading this build's own code)."""
+    """gfx950 assembly of one source (for reading the library's own generated code)."""
     out = out or os.path.join(OBJDIR, os.path.basename(src) + ".s")
     os.makedirs(os.path.dirname(out), exist_ok=True)
     cmd = [hipcc(), "-S", "--cuda-device-only", os.path.join(CSRC, src), "-o", out] \
