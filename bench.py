@@ -661,14 +661,19 @@ def traffic_record(workload, time_segments, fetch_dir, write_dir, cfetch_dir, cw
 
 
 def mamba2_traffic_record(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
-    """HBM bytes per Mamba-2 scan call (one kernel) from FETCH_SIZE and
+    """HBM bytes per Mamba-2 scan call (all its kernels: the scan launches
+    and, when rows are cut in time, the combine) from FETCH_SIZE and
     WRITE_SIZE, scaled as for the forward scan by torch's 1 GiB copy."""
     import workloads as W
     copy_kib = float(1 << 20)
     f_factor = copy_kib / _counter_mean(cfetch_dir, "copyBuffer", "FETCH_SIZE")
     w_factor = copy_kib / _counter_mean(cwrite_dir, "copyBuffer", "WRITE_SIZE")
-    fk, calls = _counter_sum(fetch_dir, "mamba2_scan_kernel", "FETCH_SIZE")
-    wk, _ = _counter_sum(write_dir, "mamba2_scan_kernel", "WRITE_SIZE")
+    try:   # one combine per call when the rows are cut in time
+        _, calls = _counter_sum(fetch_dir, "mamba2_combine_kernel", "FETCH_SIZE")
+    except RuntimeError:
+        _, calls = _counter_sum(fetch_dir, "mamba2_scan_kernel", "FETCH_SIZE")
+    fk, _ = _counter_sum(fetch_dir, "mamba2_", "FETCH_SIZE")
+    wk, _ = _counter_sum(write_dir, "mamba2_", "WRITE_SIZE")
     s = W.spec("mamba2_2p7b_layer")
     rec = {"mamba2_2p7b_layer": {
         "kernel_source_sha256_16": kernel_source_hash(MAMBA2_SOURCES),
