@@ -723,14 +723,21 @@ def rocprof_summary(d):
         except sqlite3.Error:
             pass
         try:
-            rows = c.execute("select name, counter_name, count(distinct dispatch_id), "
-                             "avg(v) from (select name, dispatch_id, counter_name, "
-                             "sum(counter_value) as v from pmc_events group by name, "
-                             "dispatch_id, counter_name) group by name, counter_name").fetchall()
+            # one line per kernel, stream and grid: launches of one kernel
+            # with different roles (a main pass, an aggregate pass) apart
+            rows = c.execute(
+                "select p.name, k.stream_id, k.grid_x / k.workgroup_x, p.counter_name, "
+                "count(*), avg(p.v), avg(k.duration) from (select name, dispatch_id, "
+                "counter_name, sum(counter_value) as v from pmc_events group by name, "
+                "dispatch_id, counter_name) p join kernels k on k.dispatch_id = "
+                "p.dispatch_id group by p.name, k.stream_id, k.grid_x / k.workgroup_x, "
+                "p.counter_name order by p.name, k.stream_id, 3, p.counter_name").fetchall()
             if rows:
-                print("%-70s %-16s %6s %16s" % ("kernel", "counter", "n", "mean/dispatch"))
-            for name, cn, n, v in rows:
-                print("%-70s %-16s %6d %16.1f" % (_kname(name)[:70], cn, n, v))
+                print("%-62s %6s %6s %-24s %6s %16s %10s" % (
+                    "kernel", "stream", "wgs", "counter", "n", "mean/dispatch", "avg_us"))
+            for name, st, wgs, cn, n, v, dur in rows:
+                print("%-62s %6s %6d %-24s %6d %16.1f %10.2f" % (
+                    _kname(name)[:62], st, wgs, cn, n, v, dur / 1e3))
         except sqlite3.Error:
             pass
 
