@@ -33,16 +33,18 @@ __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf
 __device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|).
-// With e = e^-|x| in (0, 1]: for e < 1/16 a five-term series of log1p
-// (truncation below 2e-7 relative, from the e^6/6 term); otherwise
-// log2(1 + e) * ln 2, where the rounding of 1 + e costs at most 1.5e-6
-// relative because log1p(e) >= 0.06 there.  No threshold on large x is
-// needed: e underflows smoothly and the series returns e.
+// With e = e^-|x| in (0, 1] and u = 1 + e rounded to fp32, c = e - (u - 1)
+// is the rounding error of u, exactly (|e| <= 1, so the two subtractions are
+// exact), and log1p(e) = log(u) + log(1 + c / u) = log(u) + c to within
+// |c| e, i.e. below 6e-8 relative.  v_log_f32 measured at most 1.2e-7
+// relative error on every u = 1 + k 2^-23 in [1, 2), so the form is accurate
+// for tiny e as well, without a series branch.  No threshold on large x is
+// needed: e underflows smoothly and log1p(e) = c = e there.
 __device__ __forceinline__ float softplus_f32(float x) {
   const float e = hw_exp2(-fabsf(x) * kLog2e);
-  const float ser = e * (1.0f - e * (0.5f - e * (0.33333334f - e * (0.25f - e * 0.2f))));
-  const float lg = hw_log2(1.0f + e) * kLn2;
-  return fmaxf(x, 0.0f) + (e < 0.0625f ? ser : lg);
+  const float u = 1.0f + e;
+  const float c = e - (u - 1.0f);
+  return fmaxf(x, 0.0f) + fmaf(hw_log2(u), kLn2, c);
 }
 
 // silu(z) = z / (1 + e^-z); e^-z overflows to +inf for very negative z and

@@ -357,9 +357,9 @@ __device__ __forceinline__ void scan_body(
       float o[KC];
 #pragma unroll
       for (int k = 0; k < KC; ++k) {
-        float y = 0.0f;
+        float y = s_y[0][g * KC + k][lane];
 #pragma unroll
-        for (int w = 0; w < NG; ++w) y += s_y[w][g * KC + k][lane];
+        for (int w = 1; w < NG; ++w) y += s_y[w][g * KC + k][lane];
         y = fmaf(Dd, CONV ? uc[k] : raw_get(ru, k), y);
         if (HAS_Z) y *= silu_f32(raw_get(rz, k));
         o[k] = y;

@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import workloads as W
-from tests.gpu_common import (check_out, check_state, gpu_scan, np64,
+from tests.gpu_common import (DEV, check_out, check_state, gpu_scan, np64,
                               oracle_rows, oracle_scan, sample_rows)
 
 pytestmark = pytest.mark.gpu
@@ -184,3 +184,38 @@ def test_long_sequence_split_vs_unsplit():
     check_state(last, np64(state), "split vs unsplit last_state")
     diff = (out.float() - chunked.float()).abs()
     assert float((diff / (2e-2 * (1 + chunked.float().abs()))).max()) <= 1.0
+
+
+def test_softplus_relative_accuracy():
+    """Delta itself, through the scan and the decode step: with A = 0, one
+    state, B = C = u = 1 and no skip or gate, out = softplus(delta).  Checks
+    the relative error of the kernels' softplus over delta in [-80, 40],
+    where the absolute parity bar would not see errors on tiny Delta.  The
+    bound allows the fp32 rounding of -|x| log2(e) (about 6e-8 |x| relative
+    in e^-|x|) plus a few units of the last place."""
+    import oracle
+    import selective_state_space_52_amd as m
+    n = 8192
+    x = torch.linspace(-80.0, 40.0, n, dtype=torch.float32)
+    one = torch.ones(1, n, 1, dtype=torch.float32)
+    A = torch.zeros(n, 1, dtype=torch.float32)
+    inp = {"u": one.clone(), "delta": x.reshape(1, n, 1), "A": A,
+           "B": torch.ones(1, 1, 1), "C": torch.ones(1, 1, 1), "D": None, "z": None,
+           "delta_bias": None, "softplus": True}
+    ref, _ = oracle_scan(inp)
+    ref = np.asarray(ref, dtype=np.float64).reshape(n)
+    bound = (5e-7 + 1e-7 * np.abs(np64(x))) * ref
+    out, _ = gpu_scan(inp, want_state=False)
+    err = np.abs(np64(out).reshape(n) - ref)
+    _report("softplus via scan, rel err/bound", (float((err / bound).max()), 0.0))
+    assert (err <= bound).all(), "scan softplus off at delta=%g" % float(x[int(np.argmax(err / bound))])
+    # the decode step: state 0 -> state = out = Delta
+    state = torch.zeros(1, n, 1, device=DEV)
+    out = m.selective_state_update(state, torch.ones(1, n, device=DEV), x.reshape(1, n).to(DEV),
+                                   A.to(DEV), torch.ones(1, 1, device=DEV),
+                                   torch.ones(1, 1, device=DEV), softplus=True)
+    torch.cuda.synchronize()
+    for what, got in (("out", out), ("state", state)):
+        err = np.abs(np64(got).reshape(n) - ref)
+        assert (err <= bound).all(), "decode softplus (%s) off at delta=%g" % (
+            what, float(x[int(np.argmax(err / bound))]))
