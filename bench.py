@@ -631,7 +631,20 @@ def _counter_mean(d, kernel_substr, counter):
 
 
 # the kernels of one forward call (one B/C pack per call)
-FWD_KERNELS = ("bc_pack_kernel", "scan_kernel<", "combine_kernel")
+FWD_KERNELS = ("mssm::fwd::bc_pack_kernel", "mssm::fwd::scan_kernel<",
+               "mssm::fwd::combine_kernel")
+
+
+def _library_kernels(d, counter):
+    """Names of the library's kernels with samples of a counter in a run."""
+    import sqlite3
+    names = set()
+    for db in glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True):
+        c = sqlite3.connect(db)
+        names.update(n for (n,) in c.execute(
+            "select distinct name from pmc_events where counter_name = ?", (counter,))
+            if "mssm::" in n)
+    return names
 
 
 def traffic_record(workload, time_segments, fetch_dir, write_dir, cfetch_dir, cwrite_dir):
@@ -643,10 +656,21 @@ def traffic_record(workload, time_segments, fetch_dir, write_dir, cfetch_dir, cw
     copy_kib = float(1 << 20)
     f_factor = copy_kib / _counter_mean(cfetch_dir, "copyBuffer", "FETCH_SIZE")
     w_factor = copy_kib / _counter_mean(cwrite_dir, "copyBuffer", "WRITE_SIZE")
-    _, calls = _counter_sum(fetch_dir, "bc_pack_kernel", "FETCH_SIZE")
+    s = W.spec(workload)
+    # the counter runs must hold this workload's forward calls only: another
+    # forward scan (another state size) or another kernel of the library
+    # would be counted as part of the call or change the call count
+    scan_n = "mssm::fwd::scan_kernel<%d," % s.dstate
+    for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        foreign = sorted(n for n in _library_kernels(d, counter)
+                         if not any(k in n for k in FWD_KERNELS)
+                         or ("fwd::scan_kernel<" in n and scan_n not in n))
+        if foreign:
+            raise RuntimeError("%s holds other kernels of the library (%s): profile the "
+                               "forward of %s alone" % (d, foreign[0][:80], workload))
+    _, calls = _counter_sum(fetch_dir, FWD_KERNELS[0], "FETCH_SIZE")
     fk = sum(_counter_sum(fetch_dir, k, "FETCH_SIZE")[0] for k in FWD_KERNELS) / calls
     wk = sum(_counter_sum(write_dir, k, "WRITE_SIZE")[0] for k in FWD_KERNELS) / calls
-    s = W.spec(workload)
     import selective_state_space_52_amd as m
     plan = m.scan_plan(s.batch, s.dim, s.dstate, s.seqlen, time_segments=time_segments)
     rec = {workload: {
