@@ -16,12 +16,14 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_bits(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+// Two fp32 -> packed bf16 pair, round to nearest even: converted as one
+// two-element vector, so both halves go through a single v_cvt_pk_bf16_f32
+// (element-wise conversions and a shift/or cost four instructions).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo;
-  __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 __device__ __forceinline__ uint16_t to_bf16(float f) {
   __bf16 a = (__bf16)f;

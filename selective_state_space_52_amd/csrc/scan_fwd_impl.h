@@ -162,7 +162,7 @@ __device__ __forceinline__ void scan_body(
   // values before it (row start: the init values) and turns x into u.
   float cw[kConvK], cbias = 0.0f;
   Raw<BF16, kConvK> rp, np_;  // x[tc-4 .. tc-1] of the current / next chunk
-  float uc[KC], un[KC];       // u of the current / next chunk
+  float uc[KC], un[KC];       // u of the current / next chunk, as fp32
   if constexpr (CONV) {
 #pragma unroll
     for (int j = 0; j < kConvK; ++j) cw[j] = cv.w[dc * kConvK + j];
@@ -214,14 +214,15 @@ __device__ __forceinline__ void scan_body(
   raw_zero(rz);
   raw_zero(nz);
 
-  auto prep = [&](const Raw<BF16, KC>& pu, const Raw<BF16, KC>& pd,
-                  const float (&uv)[KC]) {
+  // (Delta, Delta*u) of this wave's chunk into LDS; without the conv, u is
+  // unpacked here once and kept (uv) for the chunk's D skip
+  auto prep = [&](const Raw<BF16, KC>& pu, const Raw<BF16, KC>& pd, float (&uv)[KC]) {
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
       const float x = raw_get(pd, k) + bv_d;
       const float dl = SOFTPLUS ? softplus_f32(x) : x;
-      const float uk = CONV ? uv[k] : raw_get(pu, k);
-      s_dw[g * KC + k][lane] = make_float2(dl, dl * uk);
+      if constexpr (!CONV) uv[k] = raw_get(pu, k);
+      s_dw[g * KC + k][lane] = make_float2(dl, dl * uv[k]);
     }
   };
 
@@ -360,7 +361,7 @@ __device__ __forceinline__ void scan_body(
         float y = s_y[0][g * KC + k][lane];
 #pragma unroll
         for (int w = 1; w < NG; ++w) y += s_y[w][g * KC + k][lane];
-        y = fmaf(Dd, CONV ? uc[k] : raw_get(ru, k), y);
+        y = fmaf(Dd, uc[k], y);
         if (HAS_Z) y *= silu_f32(raw_get(rz, k));
         o[k] = y;
       }
@@ -373,12 +374,9 @@ __device__ __forceinline__ void scan_body(
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::"s"(touch));  // keeps the warming loads
 
-    ru = nu;
     rz = nz;
-    if constexpr (CONV) {
 #pragma unroll
-      for (int k = 0; k < KC; ++k) uc[k] = un[k];
-    }
+    for (int k = 0; k < KC; ++k) uc[k] = un[k];
     __syncthreads();
   }
 
