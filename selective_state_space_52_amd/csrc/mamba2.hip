@@ -58,6 +58,24 @@ __device__ __forceinline__ void split_hl(float v, uint16_t& hi, uint16_t& lo) {
   lo = to_bf16(v - bf16_bits(hi));
 }
 
+// A double moved across lanes by DPP: lanes the pattern gives no source (or
+// rows outside row_mask) read 0.  The chunk's inclusive sum over its 64 steps
+// (one per lane) is then four row_shr steps within each row of 16 lanes and
+// two row broadcasts across rows, with no trip through LDS.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROWS, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROWS, 0xf, false);
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ double lane_f64(double v, int l) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 template <int N>
 struct alignas(16) Smem {
   static constexpr int NP = N + 8;
@@ -233,12 +251,13 @@ __global__ void __launch_bounds__(kThreads)
         dl = s.softplus ? softplus_f32(v) : v;
       }
       double cs = (double)(dl * Ah);
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const double o = __shfl_up(cs, off);
-        if (lane >= off) cs += o;
-      }
-      const double end = __shfl(cs, 63);
+      cs += dpp_f64<0x111, 0xf>(cs);  // row_shr:1
+      cs += dpp_f64<0x112, 0xf>(cs);  // row_shr:2
+      cs += dpp_f64<0x114, 0xf>(cs);  // row_shr:4
+      cs += dpp_f64<0x118, 0xf>(cs);  // row_shr:8
+      cs += dpp_f64<0x142, 0xa>(cs);  // row_bcast:15 into rows 1 and 3
+      cs += dpp_f64<0x143, 0xc>(cs);  // row_bcast:31 into rows 2 and 3
+      const double end = lane_f64(cs, 63);
       sm.cum[lane] = cs;
       sm.delta[lane] = dl;
       sm.ecum[lane] = hw_exp2((float)cs * kLog2e);
