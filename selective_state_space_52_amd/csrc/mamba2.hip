@@ -16,8 +16,8 @@
 //            L[t,s] = exp(cum_t - cum_s) Delta_s for s <= t, else 0
 //   H_end  = exp(cum_end) H0  +  (X o w)^T B,  w_s = Delta_s exp(cum_end - cum_s)
 // One workgroup (8 waves) owns one (batch, head) and walks its chunks in order with
-// H in registers, so no state goes to memory between chunks.  C B^T,
-// (L o C B^T) X, C H0^T and (X o w)^T B are 32x32x16 bf16 MFMAs with fp32
+// H in registers (as H^T), so no state goes to memory between chunks.  C B^T,
+// (L o C B^T) X, C H0^T and B^T (X o w) are 32x32x16 bf16 MFMAs with fp32
 // accumulation.  B, C and x are bf16 inputs and enter exactly; an fp32
 // operand (L o C B^T, X o w, H0) enters as hi + lo bf16 halves (hi = RNE(v),
 // lo = RNE(v - hi)), which keeps 16 mantissa bits, and costs a second MFMA.
@@ -173,9 +173,11 @@ __global__ void __launch_bounds__(kThreads)
   const float bh = bias ? bias[h] : 0.0f;
   const int64_t srow = ((int64_t)b * s.H + h) * kP;  // first state row of the head
 
-  // state waves: tiles rows p = 32 pb + acc_row, cols n = nbase + 32 i + col;
-  // the entering state is the caller's (whole pairs), zero (aggregate
-  // tasks) or the segment's entering state (split pairs)
+  // state waves: the state is held transposed, tiles of rows n = nbase +
+  // 32 i + acc_row and cols p = 32 pb + col, so each group of 4 registers of
+  // a lane is 4 consecutive n of one channel p: one 8-byte LDS write per
+  // group and half.  The entering state is the caller's (whole pairs), zero
+  // (aggregate tasks) or the segment's entering state (split pairs).
   const float* h_in = split ? ws.hin + ((int64_t)sp * s.P + seg) * seg_elems
                             : (s.load_state && !agg ? state + srow * N : nullptr);
   f32x16 hacc[NT];
@@ -184,15 +186,22 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
     for (int v = 0; v < 16; ++v)
       hacc[i][v] = (!ywave && h_in)
-                       ? h_in[(32 * pb + acc_row(v, lane)) * N + nbase + 32 * i + col]
+                       ? h_in[(32 * pb + col) * N + nbase + 32 * i + acc_row(v, lane)]
                        : 0.0f;
   auto state_to_lds = [&]() {
+    const int p = 32 * pb + col;
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int p = 32 * pb + acc_row(v, lane), n = nbase + 32 * i + col;
-        split_hl(hacc[i][v], sm.H[0][p][n], sm.H[1][p][n]);
+      for (int q = 0; q < 4; ++q) {
+        const int n = nbase + 32 * i + acc_row(4 * q, lane);  // .. n + 3
+        const float v0 = hacc[i][4 * q], v1 = hacc[i][4 * q + 1];
+        const float v2 = hacc[i][4 * q + 2], v3 = hacc[i][4 * q + 3];
+        const uint32_t h01 = pack_bf16x2(v0, v1), h23 = pack_bf16x2(v2, v3);
+        const uint32_t l01 = pack_bf16x2(v0 - bf16_lo(h01), v1 - bf16_hi(h01));
+        const uint32_t l23 = pack_bf16x2(v2 - bf16_lo(h23), v3 - bf16_hi(h23));
+        *reinterpret_cast<uint2*>(&sm.H[0][p][n]) = make_uint2(h01, h23);
+        *reinterpret_cast<uint2*>(&sm.H[1][p][n]) = make_uint2(l01, l23);
       }
   };
   if (!ywave) state_to_lds();
@@ -330,21 +339,34 @@ __global__ void __launch_bounds__(kThreads)
         yb[v] = 0.0f;
       }
     } else if (!ywave) {
-      // ---- phase 2 (state): x o w; every LDS read ahead of the writes
-      const int r = wv - 4;
-      const float wt = sm.w[lane];
-      uint16_t xv[2][8];
+      // ---- phase 2 (state): x o w.  A lane takes 16 consecutive steps of
+      // one channel, so its reads and writes are 16-byte pieces (10 LDS
+      // operations instead of 48 single values).
+      const int L = (wv - 4) * 64 + lane;  // 0 .. 255
+      const int p = L >> 2, tq = (L & 3) * 16;
+      const uint4 xq[2] = {*reinterpret_cast<const uint4*>(&sm.Xt[p][tq]),
+                           *reinterpret_cast<const uint4*>(&sm.Xt[p][tq + 8])};
+      float wts[16];
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
+      for (int q = 0; q < 4; ++q) {
+        const float4 f = *reinterpret_cast<const float4*>(&sm.w[tq + 4 * q]);
+        wts[4 * q] = f.x; wts[4 * q + 1] = f.y; wts[4 * q + 2] = f.z; wts[4 * q + 3] = f.w;
+      }
+      uint32_t hw[8], lw[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xv[k][j] = sm.Xt[(r + 4 * k) * 8 + j][lane];
+      for (int i = 0; i < 8; ++i) {
+        const uint4 v4 = xq[i >> 2];
+        const uint32_t word = (i & 3) == 0 ? v4.x : (i & 3) == 1 ? v4.y : (i & 3) == 2 ? v4.z : v4.w;
+        const float a = bf16_lo(word) * wts[2 * i], c = bf16_hi(word) * wts[2 * i + 1];
+        hw[i] = pack_bf16x2(a, c);
+        lw[i] = pack_bf16x2(a - bf16_lo(hw[i]), c - bf16_hi(hw[i]));
+      }
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int p = (r + 4 * k) * 8 + j;
-          split_hl(bf16_bits(xv[k][j]) * wt, sm.Xw[0][p][lane], sm.Xw[1][p][lane]);
-        }
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t* src = h ? lw : hw;
+        *reinterpret_cast<uint4*>(&sm.Xw[h][p][tq]) = make_uint4(src[0], src[1], src[2], src[3]);
+        *reinterpret_cast<uint4*>(&sm.Xw[h][p][tq + 8]) = make_uint4(src[4], src[5], src[6], src[7]);
+      }
     }
     __syncthreads();
 
@@ -369,8 +391,8 @@ __global__ void __launch_bounds__(kThreads)
         }
       }
     } else if (!ywave) {
-      // ---- phase 3 (state): H = exp(cum_end) H + (X o w)^T B; then the new
-      // state into LDS (the output waves read the old one in phase 2)
+      // ---- phase 3 (state): H^T = exp(cum_end) H^T + B^T (X o w); then the
+      // new state into LDS (the output waves read the old one in phase 2)
       const float dec = sm.dec_end;
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
@@ -380,8 +402,8 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
         for (int k0 = 0; k0 < kQ; k0 += 16) {
           const bf16x8 bb = lds8(&sm.Bt[nbase + 32 * i + col][k0 + kq]);
-          hacc[i] = mfma(lds8(&sm.Xw[0][32 * pb + col][k0 + kq]), bb, hacc[i]);
-          lo = mfma(lds8(&sm.Xw[1][32 * pb + col][k0 + kq]), bb, lo);
+          hacc[i] = mfma(bb, lds8(&sm.Xw[0][32 * pb + col][k0 + kq]), hacc[i]);
+          lo = mfma(bb, lds8(&sm.Xw[1][32 * pb + col][k0 + kq]), lo);
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) hacc[i][v] += lo[v];
@@ -400,7 +422,7 @@ __global__ void __launch_bounds__(kThreads)
     for (int i = 0; i < NT; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        h_out[(32 * pb + acc_row(v, lane)) * N + nbase + 32 * i + col] = hacc[i][v];
+        h_out[(32 * pb + col) * N + nbase + 32 * i + acc_row(v, lane)] = hacc[i][v];
   }
   if (agg && tid == 0) ws.sum[(int64_t)sp * (s.P - 1) + seg] = seg_sum;
 }
