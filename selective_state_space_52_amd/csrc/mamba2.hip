@@ -205,6 +205,15 @@ __global__ void __launch_bounds__(kThreads)
       }
   };
   if (!ywave) state_to_lds();
+  // The block of M above the diagonal (t block 0, s block 1) is zero in every
+  // chunk, and no other step writes it: it is cleared once here.
+  if (ywave && pb > tb) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int t = 32 * tb + acc_row(v, lane), sc = 32 * pb + col;
+      sm.M[0][t][sc] = sm.M[1][t][sc] = 0;
+    }
+  }
 
   // Inputs of a chunk, loaded into registers one chunk ahead.  Lane = step t
   // of the chunk (consecutive lanes write consecutive LDS addresses of the
@@ -316,12 +325,6 @@ __global__ void __launch_bounds__(kThreads)
           const float m =
               sc <= t ? (g0[v] + g1[v]) * hw_exp2((float)(ct[v] - cs) * kLog2e) * ds : 0.0f;
           split_hl(m, sm.M[0][t][sc], sm.M[1][t][sc]);
-        }
-      } else {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int t = 32 * tb + acc_row(v, lane), sc = 32 * pb + col;
-          sm.M[0][t][sc] = sm.M[1][t][sc] = 0;
         }
       }
 #pragma unroll
