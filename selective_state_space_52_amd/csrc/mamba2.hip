@@ -381,9 +381,18 @@ __global__ void __launch_bounds__(kThreads)
         ya = mfma(lds8(&sm.M[0][32 * tb + col][k0 + kq]), bx, ya);
         yb = mfma(lds8(&sm.M[1][32 * tb + col][k0 + kq]), bx, yb);
       }
+      // x for the D skip: each group of 4 result registers is 4 consecutive
+      // steps of this lane's channel, one 8-byte read
       uint16_t xs[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) xs[v] = sm.Xt[32 * pb + col][32 * tb + acc_row(v, lane)];
+      for (int q = 0; q < 4; ++q) {
+        const uint2 x4 = *reinterpret_cast<const uint2*>(
+            &sm.Xt[32 * pb + col][32 * tb + acc_row(4 * q, lane)]);
+        xs[4 * q] = (uint16_t)(x4.x & 0xffffu);
+        xs[4 * q + 1] = (uint16_t)(x4.x >> 16);
+        xs[4 * q + 2] = (uint16_t)(x4.y & 0xffffu);
+        xs[4 * q + 3] = (uint16_t)(x4.y >> 16);
+      }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int t = 32 * tb + acc_row(v, lane), p = 32 * pb + col;
