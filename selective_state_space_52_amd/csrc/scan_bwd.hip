@@ -93,13 +93,16 @@ __device__ __forceinline__ float dpp_quad(float v) {
       __builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
-// Sum of v[k] over the 64 lanes of the wave, for k < kRedItems; lanes
-// 4k .. 4k+3 return the sum of item k.
-__device__ __forceinline__ float wave_sum_items(float (&red)[kRedItems][kRedPitch],
-                                                const float (&v)[kRedItems],
-                                                int lane) {
+// Sum of v[k] over the 64 lanes of the wave, for k < kRedItems, in two
+// halves: red_put writes the items, red_take (any time later, before the
+// next red_put) reads them back transposed and returns, in lanes 4k .. 4k+3,
+// the sum of item k.  Work placed between the two hides the writes' latency.
+__device__ __forceinline__ void red_put(float (&red)[kRedItems][kRedPitch],
+                                        const float (&v)[kRedItems], int lane) {
 #pragma unroll
   for (int k = 0; k < kRedItems; ++k) red[k][lane] = v[k];
+}
+__device__ __forceinline__ float red_take(float (&red)[kRedItems][kRedPitch], int lane) {
   wave_lds_sync();
   const float4* row = reinterpret_cast<const float4*>(&red[lane >> 2][16 * (lane & 3)]);
   const float4 a = row[0], b = row[1], c = row[2], d = row[3];
@@ -472,7 +475,20 @@ __global__ void __launch_bounds__(kLanes* NG)
       }
     }
 
-    // reverse recurrence over the tile
+    // reverse recurrence over the tile.  The channel sums of dB and dC of a
+    // unit of RS steps are taken back while the next unit computes.
+    int pend_t = -1;  // first step of the unit whose sums are in flight
+    auto take_sums = [&]() {
+      const float tot = red_take(sm.red[g], lane);
+      if ((lane & 3) == 0) {
+        const int kk = lane >> 2;
+        const int j = kk % NPW;
+        const int q = (kk / NPW) & 1;
+        const int ii = kk / (2 * NPW);
+        const int64_t t_abs = tb + pend_t + ii;
+        ws_dbc[((int64_t)k.gi * Lp + t_abs) * (2 * N) + q * N + n0 + j] = tot;
+      }
+    };
 #pragma unroll
     for (int kb = NB - 1; kb >= 0; --kb) {
       const Batch bc = *reinterpret_cast<const Batch*>(bcw + (tb + kb * KB) * WPS);
@@ -502,17 +518,12 @@ __global__ void __launch_bounds__(kLanes* NG)
           }
           sm.s[g][t][lane] = make_float2(s1, s2);
         }
-        const float tot = wave_sum_items(sm.red[g], pv, lane);
-        if ((lane & 3) == 0) {
-          const int kk = lane >> 2;
-          const int j = kk % NPW;
-          const int q = (kk / NPW) & 1;
-          const int ii = kk / (2 * NPW);
-          const int64_t t_abs = tb + kb * KB + ru * RS + ii;
-          ws_dbc[((int64_t)k.gi * Lp + t_abs) * (2 * N) + q * N + n0 + j] = tot;
-        }
+        if (pend_t >= 0) take_sums();
+        red_put(sm.red[g], pv, lane);
+        pend_t = kb * KB + ru * RS;
       }
     }
+    take_sums();
     __syncthreads();
 
     // output phase: this wave's chunk of the tile
