@@ -215,14 +215,20 @@ __device__ __forceinline__ void scan_body(
   raw_zero(nz);
 
   // (Delta, Delta*u) of this wave's chunk into LDS; without the conv, u is
-  // unpacked here once and kept (uv) for the chunk's D skip
-  auto prep = [&](const Raw<BF16, KC>& pu, const Raw<BF16, KC>& pd, float (&uv)[KC]) {
+  // unpacked here once and kept (uv) for the chunk's D skip.  The aggregate
+  // pass also sums Delta over the wave's own steps of the segment (dsum);
+  // the waves' sums are added at the end.
+  auto prep = [&](const Raw<BF16, KC>& pu, const Raw<BF16, KC>& pd, float (&uv)[KC],
+                  int64_t tile) {
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
       const float x = raw_get(pd, k) + bv_d;
       const float dl = SOFTPLUS ? softplus_f32(x) : x;
       if constexpr (!CONV) uv[k] = raw_get(pu, k);
       s_dw[g * KC + k][lane] = make_float2(dl, dl * uv[k]);
+      if constexpr (AGG) {
+        if (tile + g * KC + k < t_end) dsum += (double)dl;
+      }
     }
   };
 
@@ -235,7 +241,6 @@ __device__ __forceinline__ void scan_body(
       h[j] = fmaf(e, h[j], dw.y * bc_val<NPW, BF16>(w, i, j));
       if constexpr (!AGG) y = fmaf(bc_val<NPW, BF16>(w, i, NPW + j), h[j], y);
     }
-    if constexpr (AGG) dsum += (double)dw.x;
     return y;
   };
 
@@ -250,7 +255,7 @@ __device__ __forceinline__ void scan_body(
       load_prev(rp, tc);
       conv_u(ru, rp, uc);
     }
-    prep(ru, rd, uc);
+    prep(ru, rd, uc, t_begin);
   }
   __syncthreads();
 
@@ -298,7 +303,6 @@ __device__ __forceinline__ void scan_body(
             e[i][j] = hw_exp2(dwc[i].x * A2[j]);
             bw[i][j] = dwc[i].y * bc_val<NPW, BF16>(bc.w, i, j);
           }
-          if constexpr (AGG) dsum += (double)dwc[i].x;
         };
         decay_drive(0);
         __builtin_amdgcn_sched_barrier(0);
@@ -350,7 +354,7 @@ __device__ __forceinline__ void scan_body(
     // prep of the next tile (its Delta/Delta*u slots are free: every wave is
     // past the state phase)
     if constexpr (CONV) conv_u(nu, np_, un);
-    prep(nu, nd, un);
+    prep(nu, nd, un, tb + T);
 
     if constexpr (!AGG) {
       // output phase: this wave's chunk of the tile
@@ -384,7 +388,17 @@ __device__ __forceinline__ void scan_body(
     const int per = nseg - 1;
 #pragma unroll
     for (int j = 0; j < NPW; ++j) ws_S[(sr * per + seg) * N + n0 + j] = h[j];
-    if (g == 0) ws_sum[sr * per + seg] = dsum;
+    // the segment's sum of Delta: the waves' sums over their own steps, added
+    // in wave order (s_y is free: the loop ended on a barrier)
+    double* part = reinterpret_cast<double*>(&s_y[0][0][0]);
+    part[g * kLanes + lane] = dsum;
+    __syncthreads();
+    if (g == 0) {
+      double tot = 0.0;
+#pragma unroll
+      for (int w = 0; w < NG; ++w) tot += part[w * kLanes + lane];
+      ws_sum[sr * per + seg] = tot;
+    }
   } else {
     if (last_state && valid && seg == nseg - 1) {
 #pragma unroll
