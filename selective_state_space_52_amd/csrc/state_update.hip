@@ -23,7 +23,41 @@ struct UpdateShape {
   int64_t batch, dim;
   int32_t softplus;
   int32_t ngroups;  // B, C are (batch, ngroups, N); channel d reads d / (dim / ngroups)
+  // row / dim for rows below 2^31 as (row * dim_magic) >> dim_shift (set for
+  // the 32-bit index path): with l = ceil(log2 dim), shift = 31 + l and
+  // magic = ceil(2^shift / dim), the error magic * dim - 2^shift is below
+  // dim <= 2^l, so for row < 2^31 the product overshoots row / dim by less
+  // than 1 / dim and the floor is exact (division by an invariant integer,
+  // Granlund and Montgomery, 1994).  magic < 2^32.
+  uint32_t dim_magic, dim_shift;
 };
+
+void set_dim_divider(UpdateShape& s) {
+  uint32_t l = 0;
+  while ((int64_t(1) << l) < s.dim) ++l;
+  const uint64_t p2 = uint64_t(1) << (31 + l);
+  s.dim_shift = 31 + l;
+  s.dim_magic = (uint32_t)((p2 + (uint64_t)s.dim - 1) / (uint64_t)s.dim);
+}
+
+// Sum of y over the LPR lanes of a row (aligned groups of LPR lanes), with
+// every lane of the row getting the sum.  Up to 16 lanes the steps are DPP
+// moves within a row of 16 lanes (no trip through LDS): the lane two and one
+// away inside a quad, then the mirrored lane inside each 8 and each 16; a
+// 32-lane row adds the lane 16 away.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int LPR>
+__device__ __forceinline__ float row_sum(float y) {
+  if constexpr (LPR >= 32) y += __shfl_xor(y, 16);
+  if constexpr (LPR >= 16) y += dpp_mov<0x140>(y);  // row_mirror
+  if constexpr (LPR >= 8) y += dpp_mov<0x141>(y);   // row_half_mirror
+  if constexpr (LPR >= 4) y += dpp_mov<0x4E>(y);    // quad_perm [2,3,0,1]
+  if constexpr (LPR >= 2) y += dpp_mov<0xB1>(y);    // quad_perm [1,0,3,2]
+  return y;
+}
 
 template <bool BF16>
 __device__ __forceinline__ float load_io(const void* base, int64_t i) {
@@ -67,7 +101,8 @@ __global__ void __launch_bounds__(kBlock)
   constexpr bool VEC_BC = VEC && (BF16 ? NPL >= 2 : true);
   const Idx dim = (Idx)s.dim;
   const Idx rows = (Idx)s.batch * dim;
-  const Idx cpg = dim / (Idx)s.ngroups;  // channels per B/C group
+  // channels per B/C group (one group: no division)
+  const Idx cpg = s.ngroups > 1 ? dim / (Idx)s.ngroups : dim;
   const Idx first = (Idx)blockIdx.x * (kBlock * kItems) +
                     (Idx)(threadIdx.x >> 6) * (kLanes * kItems) + (threadIdx.x & (kLanes - 1));
 
@@ -86,9 +121,14 @@ __global__ void __launch_bounds__(kBlock)
     // last row, and store nothing
     r[it] = active[it] ? r_raw : rows - 1;
     n0[it] = (int)(v % LPR) * NPL;
-    const Idx b = r[it] / dim;
+    Idx b;
+    if constexpr (sizeof(Idx) == 4)
+      b = (Idx)(((uint64_t)r[it] * s.dim_magic) >> s.dim_shift);
+    else
+      b = r[it] / dim;
     d[it] = r[it] - b * dim;
-    const Idx bc = (b * (Idx)s.ngroups + d[it] / cpg) * N + n0[it];  // this lane's B, C
+    const Idx grp = s.ngroups > 1 ? d[it] / cpg : (Idx)0;
+    const Idx bc = (b * (Idx)s.ngroups + grp) * N + n0[it];  // this lane's B, C
     const float* sp = state + r[it] * N + n0[it];
     const float* ap = A + d[it] * N + n0[it];
     if constexpr (VEC_STATE) {
@@ -144,8 +184,7 @@ __global__ void __launch_bounds__(kBlock)
       h[it][n] = fmaf(e, h[it][n], w * bv[it][n]);
       y = fmaf(cv[it][n], h[it][n], y);
     }
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off /= 2) y += __shfl_xor(y, off);
+    y = row_sum<LPR>(y);
     y = fmaf(Dd[it], xv[it], y);
     if (HAS_Z) y *= silu_f32(zv[it]);
 
@@ -171,7 +210,8 @@ __global__ void __launch_bounds__(kBlock)
 
 template <int N, bool BF16, bool VEC, typename Idx>
 hipError_t launch_u(const UpdateParams& p, hipStream_t stream) {
-  UpdateShape s{p.batch, p.dim, p.softplus, p.ngroups > 1 ? p.ngroups : 1};
+  UpdateShape s{p.batch, p.dim, p.softplus, p.ngroups > 1 ? p.ngroups : 1, 0u, 0u};
+  if (sizeof(Idx) == 4) set_dim_divider(s);
   const int64_t threads = p.batch * p.dim * kLanesPerRow<N>;
   const int64_t per_block = (int64_t)kBlock * kItems;
   const dim3 grid((unsigned)((threads + per_block - 1) / per_block));

@@ -62,7 +62,11 @@ def _run_steps(s, steps, rows=None):
 @pytest.mark.parametrize("io,batch,dim,N", [("bf16", 3, 200, 16), ("f32", 2, 70, 16),
                                              ("bf16", 2, 64, 1), ("bf16", 2, 64, 4),
                                              ("f32", 5, 33, 8), ("bf16", 3, 100, 32),
-                                             ("f32", 2, 70, 64), ("bf16", 2, 66, 128)])
+                                             ("f32", 2, 70, 64), ("bf16", 2, 66, 128),
+                                             # the row -> (batch, channel) split at
+                                             # dim 1, just above a power of two, odd
+                                             ("bf16", 7, 1, 16), ("bf16", 4, 4097, 16),
+                                             ("f32", 3, 7777, 8)])
 def test_decode_small(io, batch, dim, N):
     s = W.spec("decode", io=io, batch=batch, dim=dim, dstate=N, tokens=5)
     state, ref_state, og, orf = _run_steps(s, steps=12)
