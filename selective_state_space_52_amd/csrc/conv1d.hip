@@ -33,14 +33,22 @@ __global__ void __launch_bounds__(256)
     causal_conv1d_kernel(const void* __restrict__ x, const float* __restrict__ w,
                          const float* __restrict__ bias,
                          const void* __restrict__ init, void* __restrict__ out,
-                         Idx rows, Idx dim, Idx L, int silu) {
+                         Idx rows, Idx dim, Idx L, int silu, U32Div per_row_div,
+                         U32Div dim_div) {
   static_assert(K >= 1 && K - 1 <= kPrev, "width");
   const Idx per_row = (L + kChunk - 1) / kChunk;
   const Idx id = (Idx)blockIdx.x * blockDim.x + threadIdx.x;
   if (id >= rows * per_row) return;
-  const Idx row = id / per_row;
+  // 32-bit indices: the two divisions by kernel constants as multiplies
+  Idx row, d;
+  if constexpr (sizeof(Idx) == 4) {
+    row = udiv(id, per_row_div);
+    d = row - udiv(row, dim_div) * dim;
+  } else {
+    row = id / per_row;
+    d = row % dim;
+  }
   const Idx t0 = (id - row * per_row) * kChunk;
-  const Idx d = row % dim;
   const Idx off = row * L;
 
   Raw<BF16, kChunk> rx;
@@ -168,18 +176,20 @@ hipError_t launch_k(const ConvParams& p, hipStream_t st) {
   const int64_t threads = p.batch * p.dim * per_row;
   const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
   const Idx rows = (Idx)(p.batch * p.dim), dim = (Idx)p.dim, L = (Idx)p.L;
+  const U32Div prd = sizeof(Idx) == 4 ? make_u32div((uint32_t)per_row) : U32Div{1u, 0u};
+  const U32Div dd = sizeof(Idx) == 4 ? make_u32div((uint32_t)p.dim) : U32Div{1u, 0u};
   switch (p.width) {
     case 2:
       hipLaunchKernelGGL((causal_conv1d_kernel<BF16, VEC, 2, Idx>), grid, block, 0, st,
-                         p.x, p.w, p.bias, p.init, p.out, rows, dim, L, p.silu);
+                         p.x, p.w, p.bias, p.init, p.out, rows, dim, L, p.silu, prd, dd);
       break;
     case 3:
       hipLaunchKernelGGL((causal_conv1d_kernel<BF16, VEC, 3, Idx>), grid, block, 0, st,
-                         p.x, p.w, p.bias, p.init, p.out, rows, dim, L, p.silu);
+                         p.x, p.w, p.bias, p.init, p.out, rows, dim, L, p.silu, prd, dd);
       break;
     case 4:
       hipLaunchKernelGGL((causal_conv1d_kernel<BF16, VEC, 4, Idx>), grid, block, 0, st,
-                         p.x, p.w, p.bias, p.init, p.out, rows, dim, L, p.silu);
+                         p.x, p.w, p.bias, p.init, p.out, rows, dim, L, p.silu, prd, dd);
       break;
     default:
       return hipErrorInvalidValue;

@@ -30,6 +30,24 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, a);
 }
 
+// n / d for n < 2^31 and 1 <= d < 2^31 as (n * magic) >> shift (division by
+// an invariant integer, Granlund and Montgomery, 1994): with l = ceil(log2 d),
+// shift = 31 + l and magic = ceil(2^shift / d), the error magic * d - 2^shift
+// is below d <= 2^l, so n * magic / 2^shift overshoots n / d by less than
+// 1 / d and its floor is exact.  magic < 2^32.  Set up on the host.
+struct U32Div {
+  uint32_t magic, shift;
+};
+inline U32Div make_u32div(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  const uint64_t p2 = uint64_t(1) << (31 + l);
+  return U32Div{(uint32_t)((p2 + d - 1) / d), 31 + l};
+}
+__device__ __forceinline__ uint32_t udiv(uint32_t n, U32Div v) {
+  return (uint32_t)(((uint64_t)n * v.magic) >> v.shift);
+}
+
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }

@@ -23,22 +23,8 @@ struct UpdateShape {
   int64_t batch, dim;
   int32_t softplus;
   int32_t ngroups;  // B, C are (batch, ngroups, N); channel d reads d / (dim / ngroups)
-  // row / dim for rows below 2^31 as (row * dim_magic) >> dim_shift (set for
-  // the 32-bit index path): with l = ceil(log2 dim), shift = 31 + l and
-  // magic = ceil(2^shift / dim), the error magic * dim - 2^shift is below
-  // dim <= 2^l, so for row < 2^31 the product overshoots row / dim by less
-  // than 1 / dim and the floor is exact (division by an invariant integer,
-  // Granlund and Montgomery, 1994).  magic < 2^32.
-  uint32_t dim_magic, dim_shift;
+  U32Div dim_div;  // row / dim on the 32-bit index path (rows below 2^31)
 };
-
-void set_dim_divider(UpdateShape& s) {
-  uint32_t l = 0;
-  while ((int64_t(1) << l) < s.dim) ++l;
-  const uint64_t p2 = uint64_t(1) << (31 + l);
-  s.dim_shift = 31 + l;
-  s.dim_magic = (uint32_t)((p2 + (uint64_t)s.dim - 1) / (uint64_t)s.dim);
-}
 
 // Sum of y over the LPR lanes of a row (aligned groups of LPR lanes), with
 // every lane of the row getting the sum.  Up to 16 lanes the steps are DPP
@@ -123,7 +109,7 @@ __global__ void __launch_bounds__(kBlock)
     n0[it] = (int)(v % LPR) * NPL;
     Idx b;
     if constexpr (sizeof(Idx) == 4)
-      b = (Idx)(((uint64_t)r[it] * s.dim_magic) >> s.dim_shift);
+      b = udiv(r[it], s.dim_div);
     else
       b = r[it] / dim;
     d[it] = r[it] - b * dim;
@@ -210,8 +196,8 @@ __global__ void __launch_bounds__(kBlock)
 
 template <int N, bool BF16, bool VEC, typename Idx>
 hipError_t launch_u(const UpdateParams& p, hipStream_t stream) {
-  UpdateShape s{p.batch, p.dim, p.softplus, p.ngroups > 1 ? p.ngroups : 1, 0u, 0u};
-  if (sizeof(Idx) == 4) set_dim_divider(s);
+  UpdateShape s{p.batch, p.dim, p.softplus, p.ngroups > 1 ? p.ngroups : 1, U32Div{1u, 0u}};
+  if (sizeof(Idx) == 4) s.dim_div = make_u32div((uint32_t)p.dim);
   const int64_t threads = p.batch * p.dim * kLanesPerRow<N>;
   const int64_t per_block = (int64_t)kBlock * kItems;
   const dim3 grid((unsigned)((threads + per_block - 1) / per_block));
