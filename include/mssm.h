@@ -87,7 +87,8 @@ typedef struct {
   int64_t batch;       /* >= 1                                              */
   int64_t dim;         /* channels (D_inner), >= 1                          */
   int64_t dstate;      /* N, a power of two from 1 to 128 (backward: <= 32) */
-  int64_t seqlen;      /* L >= 1 for the scan; must be 1 for state_update  */
+  int64_t seqlen;      /* L >= 1 for the scan (at most 2^31 - 65); must be */
+                       /* 1 for state_update                               */
   int32_t io_dtype;    /* mssm_dtype of u/delta/z/B/C/out (x/dt/z/B/C/out) */
   uint32_t flags;      /* MSSM_FLAG_*                                       */
   int32_t time_segments; /* scan only: 0 = the library picks; k >= 1 splits */

@@ -249,7 +249,7 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A,
                 L = dims->seqlen;
   const size_t io = dims->io_dtype == MSSM_BF16 ? 2 : 4;
   const int64_t lim = INT64_MAX / 16;
-  if (L > INT32_MAX || !product_ok(batch, dim, L, lim) ||
+  if (L > INT32_MAX - 64 || !product_ok(batch, dim, L, lim) ||
       !product_ok(batch, L, N, lim) || !product_ok(batch, dim, N, lim))
     return MSSM_ERR_DIMS;
 

@@ -118,6 +118,54 @@ __device__ __forceinline__ void store_chunk(void* base, int64_t off,
   }
 }
 
+// Vector-path loads and stores from a lane's own row pointer `row` (bytes):
+// values [t, t + KC) of the row, t uniform across the wave.  The caller keeps
+// [t, t + KC) inside the row and 16-byte aligned pieces (8-byte for a 4-value
+// bf16 chunk), so the only per-tile vector work is one 64-bit address add.
+template <bool BF16, int KC>
+__device__ __forceinline__ void load_chunk_row(Raw<BF16, KC>& r, const char* row, int t) {
+  constexpr int W = Raw<BF16, KC>::W;
+  const uint32_t* src =
+      reinterpret_cast<const uint32_t*>(row + (int64_t)t * (BF16 ? 2 : 4));
+  if constexpr (W >= 4) {
+#pragma unroll
+    for (int q = 0; q < W / 4; ++q) {
+      const uint4 v = reinterpret_cast<const uint4*>(src)[q];
+      r.w[4 * q] = v.x; r.w[4 * q + 1] = v.y; r.w[4 * q + 2] = v.z; r.w[4 * q + 3] = v.w;
+    }
+  } else if constexpr (W == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(src);
+    r.w[0] = v.x; r.w[1] = v.y;
+  } else {
+    r.w[0] = src[0];
+  }
+}
+
+// Stores the whole chunk [t, t + KC) when `nvalid` > 0: on the vector path a
+// row's length and its time segments are multiples of the chunk, so a chunk
+// is either whole or past the end.
+template <bool BF16, int KC>
+__device__ __forceinline__ void store_chunk_row(char* row, int t, const float (&o)[KC],
+                                                int nvalid) {
+  if (nvalid <= 0) return;
+  uint32_t* dst = reinterpret_cast<uint32_t*>(row + (int64_t)t * (BF16 ? 2 : 4));
+  constexpr int W = BF16 ? KC / 2 : KC;
+  uint32_t w[W];
+#pragma unroll
+  for (int i = 0; i < W; ++i)
+    w[i] = BF16 ? pack_bf16x2(o[2 * i], o[2 * i + 1]) : __float_as_uint(o[i]);
+  if constexpr (W >= 4) {
+#pragma unroll
+    for (int q = 0; q < W / 4; ++q)
+      reinterpret_cast<uint4*>(dst)[q] =
+          make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+  } else if constexpr (W == 2) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  } else {
+    dst[0] = w[0];
+  }
+}
+
 // B_t and C_t packed for the scan, in the io dtype, laid out
 // [b][wave g][t][B_t[n0..n0+NPW), C_t[n0..n0+NPW)] so that one wave's values
 // for a batch of consecutive tokens are one contiguous 64-byte run read by a

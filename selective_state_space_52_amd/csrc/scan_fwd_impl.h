@@ -137,9 +137,23 @@ __device__ __forceinline__ void scan_body(
   const int64_t row = b * s.dim + dc;
   // first element of the row in u / delta / z / out
   const int64_t rowoff = s.ts == 1 ? row * s.L : b * s.L * s.dim + dc;
-  const int64_t t_begin = nseg > 1 ? (int64_t)seg * s.seg_len : 0;
-  const int64_t t_end = nseg > 1 ? min(s.L, t_begin + s.seg_len) : s.L;
+  // Time indices are 32-bit (the host keeps L below 2^31 - 64), so their
+  // compares run on the scalar unit.
+  const int Lr = (int)s.L;
+  const int t_begin = nseg > 1 ? seg * (int)s.seg_len : 0;
+  const int t_end = nseg > 1 ? (int)min(s.L, (int64_t)t_begin + s.seg_len) : Lr;
   const int64_t sr = (int64_t)(gi - s.whole_groups) * kLanes + lane;
+  // Vector path with chunks of at most 8 steps (N >= 8): each lane keeps
+  // pointers to its own rows, and the next tile's chunk start is clamped to
+  // the row's last chunk (L is a multiple of 8, so L >= KC), so the loads
+  // need neither a branch nor 64-bit index work.  A clamped chunk past the
+  // end reads values of the row that nothing uses.
+  constexpr bool kRowPtr = VEC && KC <= 8;
+  constexpr int64_t kEs = BF16 ? 2 : 4;
+  const char* const pu = static_cast<const char*>(u) + rowoff * kEs;
+  const char* const pdl = static_cast<const char*>(delta) + rowoff * kEs;
+  const char* const pz = HAS_Z ? static_cast<const char*>(z) + rowoff * kEs : nullptr;
+  char* const po = AGG ? nullptr : static_cast<char*>(out) + rowoff * kEs;
 
   float A2[NPW], h[NPW];
 #pragma unroll
@@ -168,7 +182,7 @@ __device__ __forceinline__ void scan_body(
     for (int j = 0; j < kConvK; ++j) cw[j] = cv.w[dc * kConvK + j];
     cbias = cv.b ? cv.b[dc] : 0.0f;
   }
-  auto load_prev = [&](Raw<BF16, kConvK>& r, int64_t tc) {
+  auto load_prev = [&](Raw<BF16, kConvK>& r, int tc) {
     if (tc >= kConvK) {
       load_chunk<BF16, VEC, kConvK>(r, u, rowoff + (tc - kConvK) * s.ts,
                                     s.L - (tc - kConvK), s.ts);
@@ -219,7 +233,7 @@ __device__ __forceinline__ void scan_body(
   // pass also sums Delta over the wave's own steps of the segment (dsum);
   // the waves' sums are added at the end.
   auto prep = [&](const Raw<BF16, KC>& pu, const Raw<BF16, KC>& pd, float (&uv)[KC],
-                  int64_t tile) {
+                  int tile) {
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
       const float x = raw_get(pd, k) + bv_d;
@@ -246,8 +260,8 @@ __device__ __forceinline__ void scan_body(
 
   // prologue: this wave's chunk of the first tile
   {
-    const int64_t tc = t_begin + g * KC;
-    const int64_t nv = t_end - tc;
+    const int tc = t_begin + g * KC;
+    const int nv = t_end - tc;
     load_chunk<BF16, VEC, KC>(ru, u, rowoff + tc * s.ts, nv, s.ts);
     load_chunk<BF16, VEC, KC>(rd, delta, rowoff + tc * s.ts, nv, s.ts);
     if (HAS_Z && !AGG) load_chunk<BF16, VEC, KC>(rz, z, rowoff + tc * s.ts, nv, s.ts);
@@ -259,11 +273,21 @@ __device__ __forceinline__ void scan_body(
   }
   __syncthreads();
 
-  for (int64_t tb = t_begin; tb < t_end; tb += T) {
+  for (int tb = t_begin; tb < t_end; tb += T) {
     // prefetch this wave's chunk of the next tile
-    {
-      const int64_t tc = tb + T + g * KC;
-      const int64_t nv = t_end - tc;
+    if constexpr (kRowPtr) {
+      const int tc = tb + T + g * KC;
+      const int tl = min(tc, Lr - KC);
+      // z first: loads complete in issue order, so the prep's wait for u and
+      // delta also covers z, and nothing later waits behind the tile's stores
+      if (HAS_Z && !AGG) load_chunk_row<BF16, KC>(nz, pz, tl);
+      load_chunk_row<BF16, KC>(nu, pu, tl);
+      load_chunk_row<BF16, KC>(nd, pdl, tl);
+      // tc >= kTile here, so the 4 inputs before the chunk are in the row
+      if constexpr (CONV) load_chunk_row<BF16, kConvK>(np_, pu, min(tc, t_end) - kConvK);
+    } else {
+      const int tc = tb + T + g * KC;
+      const int nv = t_end - tc;
       load_chunk<BF16, VEC, KC>(nu, u, rowoff + tc * s.ts, nv, s.ts);
       load_chunk<BF16, VEC, KC>(nd, delta, rowoff + tc * s.ts, nv, s.ts);
       if (HAS_Z && !AGG) load_chunk<BF16, VEC, KC>(nz, z, rowoff + tc * s.ts, nv, s.ts);
@@ -281,10 +305,10 @@ __device__ __forceinline__ void scan_body(
     }
 
     // state phase: every wave advances its NPW states over the whole tile
-    const int64_t nt = t_end - tb;
+    const int nt = t_end - tb;
     if (nt >= T) {
       float2 dwn[KB];
-      Batch bn = *reinterpret_cast<const Batch*>(bcw + tb * WPS);
+      Batch bn = *reinterpret_cast<const Batch*>(bcw + (int64_t)tb * WPS);
 #pragma unroll
       for (int i = 0; i < KB; ++i) dwn[i] = s_dw[i][lane];
 #pragma unroll
@@ -307,7 +331,7 @@ __device__ __forceinline__ void scan_body(
         decay_drive(0);
         __builtin_amdgcn_sched_barrier(0);
         if (kb + 1 < NB) {
-          bn = *reinterpret_cast<const Batch*>(bcw + (tb + (kb + 1) * KB) * WPS);
+          bn = *reinterpret_cast<const Batch*>(bcw + ((int64_t)tb + (kb + 1) * KB) * WPS);
 #pragma unroll
           for (int i = 0; i < KB; ++i) dwn[i] = s_dw[(kb + 1) * KB + i][lane];
         }
@@ -331,7 +355,7 @@ __device__ __forceinline__ void scan_body(
       for (int kk = 0; kk < nt; ++kk) {
         uint32_t q[WPS];
 #pragma unroll
-        for (int j = 0; j < WPS; ++j) q[j] = bcw[(tb + kk) * WPS + j];
+        for (int j = 0; j < WPS; ++j) q[j] = bcw[((int64_t)tb + kk) * WPS + j];
         const float y = advance(s_dw[kk][lane], q, 0);
         if constexpr (!AGG) s_y[g][kk][lane] = y;
       }
@@ -345,7 +369,7 @@ __device__ __forceinline__ void scan_body(
     uint32_t touch = 0u;
     if (kWarmScalarCache) {
       const int64_t last = bc_run_words(s.L, WPS) - 1;  // last word of the run
-      const int64_t f0 = (tb + T) * WPS;
+      const int64_t f0 = ((int64_t)tb + T) * WPS;
 #pragma unroll
       for (int f = 0; f < T * WPS; f += 16) touch += bcw[min(f0 + f, last)];
     }
@@ -358,7 +382,7 @@ __device__ __forceinline__ void scan_body(
 
     if constexpr (!AGG) {
       // output phase: this wave's chunk of the tile
-      const int64_t tc = tb + g * KC;
+      const int tc = tb + g * KC;
       float o[KC];
 #pragma unroll
       for (int k = 0; k < KC; ++k) {
@@ -369,10 +393,19 @@ __device__ __forceinline__ void scan_body(
         if (HAS_Z) y *= silu_f32(raw_get(rz, k));
         o[k] = y;
       }
-      if (valid) store_chunk<BF16, VEC, KC>(out, rowoff + tc * s.ts, o, t_end - tc, s.ts);
-      if constexpr (CONV) {
-        if (valid && cv.u_out)
-          store_chunk<BF16, VEC, KC>(cv.u_out, rowoff + tc * s.ts, uc, t_end - tc, s.ts);
+      if constexpr (kRowPtr) {
+        if (valid) store_chunk_row<BF16, KC>(po, tc, o, t_end - tc);
+        if constexpr (CONV) {
+          if (valid && cv.u_out)
+            store_chunk_row<BF16, KC>(static_cast<char*>(cv.u_out) + rowoff * kEs, tc, uc,
+                                      t_end - tc);
+        }
+      } else {
+        if (valid) store_chunk<BF16, VEC, KC>(out, rowoff + tc * s.ts, o, t_end - tc, s.ts);
+        if constexpr (CONV) {
+          if (valid && cv.u_out)
+            store_chunk<BF16, VEC, KC>(cv.u_out, rowoff + tc * s.ts, uc, t_end - tc, s.ts);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
