@@ -507,18 +507,9 @@ def bench_backward(torch, W, m, dev, s, sets, hev, steps, time_segments=0):
 def software(torch):
     """Versions of the stack the numbers come from."""
     import numpy
-    info = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+    return {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
             "numpy": numpy.__version__,
             "device": torch.cuda.get_device_properties(0).name}
-    try:
-        import subprocess
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True,
-                           text=True, timeout=30)
-        clk = [l.strip() for l in r.stdout.splitlines() if "sclk" in l]
-        info["sclk_after_run"] = clk[0] if clk else None
-    except Exception:  # the clock is informative only
-        info["sclk_after_run"] = None
-    return info
 
 
 def bench_decode(torch, W, m, dev, steps):

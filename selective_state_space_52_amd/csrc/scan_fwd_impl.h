@@ -145,9 +145,10 @@ __device__ __forceinline__ void scan_body(
   const int64_t sr = (int64_t)(gi - s.whole_groups) * kLanes + lane;
   // Vector path with chunks of at most 8 steps (N >= 8): each lane keeps
   // pointers to its own rows, and the next tile's chunk start is clamped to
-  // the row's last chunk (L is a multiple of 8, so L >= KC), so the loads
-  // need neither a branch nor 64-bit index work.  A clamped chunk past the
-  // end reads values of the row that nothing uses.
+  // the task's last chunk (t_end is L, a multiple of 8, or a segment end, a
+  // multiple of the tile, so t_end >= KC), so the loads need neither a
+  // branch nor 64-bit index work.  A clamped chunk past the end re-reads
+  // values of the task that nothing uses.
   constexpr bool kRowPtr = VEC && KC <= 8;
   constexpr int64_t kEs = BF16 ? 2 : 4;
   const char* const pu = static_cast<const char*>(u) + rowoff * kEs;
@@ -277,7 +278,7 @@ __device__ __forceinline__ void scan_body(
     // prefetch this wave's chunk of the next tile
     if constexpr (kRowPtr) {
       const int tc = tb + T + g * KC;
-      const int tl = min(tc, Lr - KC);
+      const int tl = min(tc, t_end - KC);
       // z first: loads complete in issue order, so the prep's wait for u and
       // delta also covers z, and nothing later waits behind the tile's stores
       if (HAS_Z && !AGG) load_chunk_row<BF16, KC>(nz, pz, tl);
