@@ -171,6 +171,7 @@ __global__ void __launch_bounds__(kLanes* NG)
   using Batch = BCBatch<NPW, BF16>;
   __shared__ float2 s_dw[2][T][kLanes];  // (Delta, Delta*u), double-buffered
   __shared__ float s_dy[2][T][kLanes];   // dout * silu(z)
+  __shared__ double s_ds[2][NG][kLanes];  // each wave's sum of its steps' Delta
 
   const int lane = threadIdx.x & (kLanes - 1);
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -187,17 +188,40 @@ __global__ void __launch_bounds__(kLanes* NG)
 
   Raw<BF16, KC> ru, rd, rz, ro;
   raw_zero(rz);
+  // Time indices are 32-bit (the host keeps L below 2^31 - 64).  On the
+  // vector path with chunks of at most 8 steps (L a multiple of 8, so
+  // L >= KC) each lane keeps pointers to its own rows and a chunk's start is
+  // clamped to the row's last chunk: no branch or 64-bit compare per load;
+  // prep zeroes the steps past L.
+  constexpr bool kRowPtr = VEC && KC <= 8;
+  const int Lr = (int)s.L;
+  constexpr int64_t kEs = BF16 ? 2 : 4;
+  const char* const pu = static_cast<const char*>(u) + k.rowoff * kEs;
+  const char* const pdl = static_cast<const char*>(delta) + k.rowoff * kEs;
+  const char* const pz = HAS_Z ? static_cast<const char*>(z) + k.rowoff * kEs : nullptr;
+  const char* const pdo = static_cast<const char*>(dout) + k.rowoff * kEs;
   auto load = [&](int tile) {
-    const int64_t tc = (int64_t)tile * T + g * KC;
-    const int64_t nv = s.L - tc;
-    const int64_t off = k.rowoff + tc * s.ts;
-    load_chunk<BF16, VEC, KC>(ru, u, off, nv, s.ts);
-    load_chunk<BF16, VEC, KC>(rd, delta, off, nv, s.ts);
-    if constexpr (HAS_Z) load_chunk<BF16, VEC, KC>(rz, z, off, nv, s.ts);
-    load_chunk<BF16, VEC, KC>(ro, dout, off, nv, s.ts);
+    const int tc = tile * T + g * KC;
+    if constexpr (kRowPtr) {
+      const int tl = min(tc, Lr - KC);
+      load_chunk_row<BF16, KC>(ru, pu, tl);
+      load_chunk_row<BF16, KC>(rd, pdl, tl);
+      if constexpr (HAS_Z) load_chunk_row<BF16, KC>(rz, pz, tl);
+      load_chunk_row<BF16, KC>(ro, pdo, tl);
+    } else {
+      const int nv = Lr - tc;
+      const int64_t off = k.rowoff + (int64_t)tc * s.ts;
+      load_chunk<BF16, VEC, KC>(ru, u, off, nv, s.ts);
+      load_chunk<BF16, VEC, KC>(rd, delta, off, nv, s.ts);
+      if constexpr (HAS_Z) load_chunk<BF16, VEC, KC>(rz, z, off, nv, s.ts);
+      load_chunk<BF16, VEC, KC>(ro, dout, off, nv, s.ts);
+    }
   };
+  // (Delta, Delta*u) and dout*silu(z) of this wave's chunk into LDS, and the
+  // fp64 sum of the chunk's Delta (the waves' sums give the tile's sum)
   auto prep = [&](int tile, int buf) {
-    const int64_t nv = s.L - ((int64_t)tile * T + g * KC);
+    const int nv = Lr - (tile * T + g * KC);
+    double ds = 0.0;
 #pragma unroll
     for (int q = 0; q < KC; ++q) {
       const bool ok = k.valid && q < nv;
@@ -209,7 +233,9 @@ __global__ void __launch_bounds__(kLanes* NG)
       dyv = ok ? dyv : 0.0f;
       s_dw[buf][g * KC + q][lane] = make_float2(dl, dl * raw_get(ru, q));
       s_dy[buf][g * KC + q][lane] = dyv;
+      ds += (double)dl;
     }
+    s_ds[buf][g][lane] = ds;
   };
 
   float h[NPW], E[NPW], Rg[NPW];
@@ -248,9 +274,11 @@ __global__ void __launch_bounds__(kLanes* NG)
           E[j] *= e;
           Rg[j] = fmaf(E[j], dyv * bc_val<NPW, BF16>(bc.w, i, NPW + j), Rg[j]);
         }
-        cum += (double)dw.x;
       }
     }
+    // the tile's sum of Delta, the waves' chunk sums in wave order
+#pragma unroll
+    for (int w = 0; w < NG; ++w) cum += s_ds[cur][w][lane];
     if (more) prep(ti + 1, cur ^ 1);
     asm volatile("" ::"s"(touch));  // keeps the warming loads
     __syncthreads();
