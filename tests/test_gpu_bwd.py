@@ -101,6 +101,7 @@ SHAPES = [
     ("bf16", 1, 64, 16, 16),
     ("bf16", 1, 64, 16, 17),
     ("bf16", 1, 64, 16, 8),       # half a tile
+    ("bf16", 2, 64, 8, 8),        # half a tile, 8-step chunks
     ("bf16", 1, 64, 16, 9),
     ("bf16", 1, 64, 4, 136),      # one wave: 16-step chunks
     ("f32", 1, 64, 4, 72),

@@ -40,6 +40,9 @@ SHAPES = [
     ("bf16", 1, 64, 16, 64),
     ("bf16", 1, 64, 16, 65),
     ("bf16", 1, 5, 16, 40),       # fewer channels than a wave
+    ("bf16", 1, 64, 16, 8),       # shortest vector-path row: one ragged tile
+    ("bf16", 2, 64, 8, 8),        # the same with 8-step chunks
+    ("bf16", 2, 96, 32, 296),     # N = 32 on the vector path, ragged last tile
     ("bf16", 2, 96, 1, 200),
     ("bf16", 2, 96, 2, 200),
     ("bf16", 2, 96, 4, 200),
