@@ -38,10 +38,24 @@
  * io pointer together with seqlen * sizeof(io) % 16 == 0 selects the
  * vector-load path, anything else the element-load path (same results).
  * The calls are asynchronous on `stream` (a hipStream_t; NULL = the default
- * stream).  They never synchronise the host.  The forward scan takes
- * stream-ordered workspace from HIP's default memory pool (B and C repacked
- * as fp32, plus the segment summaries when it splits long rows in time; the
- * size is mssm_plan.workspace_bytes) and returns it on the same stream.
+ * stream).  They never synchronise the host.
+ *
+ * Workspace.  The forward scans, the backward and the Mamba-2 scan need
+ * device scratch memory (B and C repacked per wave, and the summaries of rows
+ * split in time).  Each comes in two forms:
+ *   - the *_ws call takes it from the caller (`workspace`, at least
+ *     mssm_workspace_size() bytes, 256-byte aligned, owned by the caller and
+ *     not touched by any other work until the call's kernels have finished on
+ *     `stream`); these calls allocate, free and synchronise nothing;
+ *   - the plain call takes it stream-ordered from HIP's default memory pool
+ *     (hipMallocAsync / hipFreeAsync on `stream`) for the duration of the
+ *     call.
+ * When a forward call splits some rows in time while others run whole, it
+ * runs the split rows' chain on a second, library-owned stream of the same
+ * device (created at the first such call, default priority, kept until the
+ * process ends), forked from `stream` by an event and joined back into it by
+ * another before the call returns, so that the call is still ordered on
+ * `stream` as one unit.
  *
  * Errors.  Every argument is validated before the first HIP call; a call that
  * fails validation returns a negative code and writes nothing.  A failing HIP
@@ -59,7 +73,7 @@
 extern "C" {
 #endif
 
-#define MSSM_ABI_VERSION 1
+#define MSSM_ABI_VERSION 2
 
 typedef enum { MSSM_F32 = 0, MSSM_BF16 = 1 } mssm_dtype;
 
@@ -71,7 +85,8 @@ enum {
                              /* to 32), unknown dtype, unknown flag          */
   MSSM_ERR_ALIGN = -4,       /* pointer not aligned to its element size     */
   MSSM_ERR_ALIAS = -5,       /* an output overlaps another argument         */
-  MSSM_ERR_HIP = -6          /* a HIP runtime call or launch failed         */
+  MSSM_ERR_HIP = -6,         /* a HIP runtime call or launch failed         */
+  MSSM_ERR_WORKSPACE = -7    /* workspace missing, too small or misaligned  */
 };
 
 /* fwd: last_state holds the initial state h0 on entry (in/out). */
@@ -211,9 +226,8 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
                             const mssm_dims* dims, void* stream);
 
 /*
- * The Mamba-2 block's scan (page "Mamba: Selective State Space Models", "Use
- * the Mamba2 block": the Mamba-2 architecture, state sizes of typically 64
- * or 128).  The pages give the block's API, not its scan; this is the
+ * The Mamba-2 block's scan (page "Mamba State Space Model", "Use the Mamba2
+ * block": the Mamba-2 architecture, state sizes of typically 64 or 128).  The pages give the block's API, not its scan; this is the
  * Mamba-2 architecture's: the selective recurrence with one A, one step and
  * one D per head of `headdim` channels, and B, C shared by a group of heads.
  * For channel p of head h (channel index d = h * headdim + p), head group
@@ -264,6 +278,64 @@ int mssm_selective_state_update(float* state, const void* x, const void* dt,
                                 const float* dt_bias, int softplus, void* out,
                                 const mssm_dims* dims, void* stream);
 
+/* Same as mssm_selective_scan_fwd, with the caller's workspace (see
+ * "Workspace" above; workspace_bytes >= mssm_workspace_size(MSSM_OP_SCAN_FWD)).
+ * A call that needs no workspace accepts NULL. */
+int mssm_selective_scan_fwd_ws(const void* u, const void* delta, const float* A,
+                               const void* B, const void* C, const float* D,
+                               const void* z, const float* delta_bias, int softplus,
+                               void* out, float* last_state, void* workspace,
+                               int64_t workspace_bytes, const mssm_dims* dims,
+                               void* stream);
+
+/* Same as mssm_selective_scan_fwd_conv, with the caller's workspace
+ * (mssm_workspace_size(MSSM_OP_SCAN_FWD_CONV)). */
+int mssm_selective_scan_fwd_conv_ws(const void* x, const float* conv_weight,
+                                    const float* conv_bias, const void* conv_init,
+                                    const void* delta, const float* A, const void* B,
+                                    const void* C, const float* D, const void* z,
+                                    const float* delta_bias, int softplus, void* out,
+                                    float* last_state, void* u_out, void* workspace,
+                                    int64_t workspace_bytes, const mssm_dims* dims,
+                                    void* stream);
+
+/* Same as mssm_selective_scan_bwd, with the caller's workspace
+ * (mssm_workspace_size(MSSM_OP_SCAN_BWD)). */
+int mssm_selective_scan_bwd_ws(const void* u, const void* delta, const float* A,
+                               const void* B, const void* C, const float* D,
+                               const void* z, const float* delta_bias,
+                               int softplus, const float* h0, const void* dout,
+                               const float* dlast, void* du, void* ddelta,
+                               float* dA, float* dB, float* dC, float* dD,
+                               void* dz, float* ddelta_bias, float* dh0,
+                               void* workspace, int64_t workspace_bytes,
+                               const mssm_dims* dims, void* stream);
+
+/* Same as mssm_mamba2_scan_fwd, with the caller's workspace
+ * (mssm_workspace_size(MSSM_OP_MAMBA2_FWD, headdim)); NULL when the call
+ * needs none. */
+int mssm_mamba2_scan_fwd_ws(const void* x, const void* dt, const float* A,
+                            const void* B, const void* C, const float* D,
+                            const void* z, const float* dt_bias, int softplus,
+                            int64_t headdim, void* out, float* last_state,
+                            void* workspace, int64_t workspace_bytes,
+                            const mssm_dims* dims, void* stream);
+
+/* Operations for mssm_workspace_size. */
+enum {
+  MSSM_OP_SCAN_FWD = 0,
+  MSSM_OP_SCAN_FWD_CONV = 1,
+  MSSM_OP_SCAN_BWD = 2,
+  MSSM_OP_MAMBA2_FWD = 3
+};
+
+/* Workspace bytes (*bytes; 0 when none is needed) of one call of `op` with
+ * these dims (and headdim, for MSSM_OP_MAMBA2_FWD; ignored otherwise).  The
+ * split of rows in time depends on the current device's compute-unit count
+ * (and, for the backward, on its occupancy), so the size is for calls on the
+ * device that is current here.  Validates dims like the call itself. */
+int mssm_workspace_size(int op, const mssm_dims* dims, int64_t headdim, int64_t* bytes);
+
 /* How the forward scan would run for these dims (no HIP call, no launch). */
 typedef struct {
   int32_t groups;           /* 64-channel groups (batch * ceil(dim / 64))     */
@@ -274,7 +346,7 @@ typedef struct {
   int32_t waves_per_group;  /* waves per workgroup (each owns dstate/waves   */
                             /* of the state)                                 */
   int32_t kernels;          /* launches per call (2, or 4 when splitting)    */
-  int64_t workspace_bytes;  /* stream-ordered workspace taken per call       */
+  int64_t workspace_bytes;  /* workspace a call needs (mssm_workspace_size)  */
   int32_t vector_path;      /* 1 when the 16-byte vector-load path applies   */
                             /* (needs aligned pointers too)                  */
   int32_t reserved;

@@ -126,9 +126,9 @@ class Oracle:
     def mamba2_scan(self, x, dt, A, B, C, D=None, z=None, dt_bias=None,
                     softplus=True, h0=None, nthreads=None):
         """The Mamba-2 block's scan in fp64, as the selective scan above with
-        one A value, one step and one D per head (page "Mamba: Selective State
-        Space Models", "Use the Mamba2 block", names the block and its state
-        sizes; the per-head structure is the Mamba-2 architecture's).
+        one A value, one step and one D per head (page "Mamba State Space
+        Model", "Use the Mamba2 block", names the block and its state sizes;
+        the per-head structure is the Mamba-2 architecture's).
 
         x, z: (batch, L, H, P) with headdim P; dt: (batch, L, H); A, D,
         dt_bias: (H,); B, C: (batch, L, G, N), heads h // (H // G) reading

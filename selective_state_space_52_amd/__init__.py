@@ -16,12 +16,15 @@ from __future__ import annotations
 
 import torch
 
+import ctypes
+
 from ._lib import (MSSM_BF16, MSSM_F32, MSSM_FLAG_LAYOUT_BLD, MSSM_FLAG_LOAD_STATE,
-                   Dims, MssmError, Plan, check, lib)
+                   MSSM_OP_MAMBA2_FWD, MSSM_OP_SCAN_BWD, MSSM_OP_SCAN_FWD,
+                   MSSM_OP_SCAN_FWD_CONV, Dims, MssmError, Plan, check, lib)
 
 __all__ = ["selective_scan_fwd", "selective_scan_bwd", "selective_scan_fwd_conv",
            "causal_conv1d_fwd", "selective_state_update", "mamba2_scan_fwd", "scan_plan",
-           "set_scan_timing_events", "MssmError", "abi_version"]
+           "workspace_size", "set_scan_timing_events", "MssmError", "abi_version"]
 
 _IO = {torch.float32: MSSM_F32, torch.bfloat16: MSSM_BF16}
 
@@ -93,6 +96,34 @@ def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def workspace_size(op, dims, headdim=0) -> int:
+    """Workspace bytes of one call (mssm_workspace_size) on the current device."""
+    n = ctypes.c_int64(0)
+    check(lib().mssm_workspace_size(int(op), dims, int(headdim), ctypes.byref(n)))
+    return int(n.value)
+
+
+# One workspace per (device, stream), grown on demand from torch's caching
+# allocator: calls on one stream run in order, so they can share it, and a
+# grown buffer's old block returns to torch's pool on that same stream.
+_WS = {}
+
+
+def _workspace(op, dims, dev, stream, headdim=0):
+    """(pointer, bytes) of a workspace for this call (None, 0 when none is needed)."""
+    need = workspace_size(op, dims, headdim)
+    if need <= 0:
+        return None, 0
+    key = (dev.index if dev.index is not None else torch.cuda.current_device(), stream)
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < need:
+        buf = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+        _WS[key] = buf
+    ptr = buf.data_ptr()
+    ptr += (-ptr) % 256
+    return ptr, need
+
+
 def scan_plan(batch, dim, dstate, seqlen, io_dtype=torch.bfloat16,
               time_segments=0, layout="bdl", ngroups=0) -> dict:
     """How the library splits a forward scan of this shape (no GPU needed)."""
@@ -141,10 +172,12 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     dims = Dims(batch, dim, N, L, _IO[io],
                 (MSSM_FLAG_LOAD_STATE if load_state else 0) | lay, time_segments, G)
     with torch.cuda.device(dev):
-        check(lib().mssm_selective_scan_fwd(
+        st = _stream(dev)
+        ws, nws = _workspace(MSSM_OP_SCAN_FWD, dims, dev, st)
+        check(lib().mssm_selective_scan_fwd_ws(
             _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
             _ptr(delta_bias), int(bool(softplus)), _ptr(out), _ptr(last_state),
-            dims, _stream(dev)))
+            ws, nws, dims, st))
     return out
 
 
@@ -216,11 +249,13 @@ def selective_scan_fwd_conv(x, conv_weight, delta, A, B, C, conv_bias=None,
     dims = Dims(batch, dim, N, L, _IO[io],
                 (MSSM_FLAG_LOAD_STATE if load_state else 0) | lay, time_segments, G)
     with torch.cuda.device(dev):
-        check(lib().mssm_selective_scan_fwd_conv(
+        st = _stream(dev)
+        ws, nws = _workspace(MSSM_OP_SCAN_FWD_CONV, dims, dev, st)
+        check(lib().mssm_selective_scan_fwd_conv_ws(
             _ptr(x), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_init),
             _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
             _ptr(delta_bias), int(bool(softplus)), _ptr(out), _ptr(last_state),
-            _ptr(u_out), dims, _stream(dev)))
+            _ptr(u_out), ws, nws, dims, st))
     return out
 
 
@@ -270,12 +305,14 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None,
              dh0=torch.empty((batch, dim, N), **f32) if want_dh0 else None)
     dims = Dims(batch, dim, N, L, _IO[io], lay, time_segments, G)
     with torch.cuda.device(dev):
-        check(lib().mssm_selective_scan_bwd(
+        st = _stream(dev)
+        ws, nws = _workspace(MSSM_OP_SCAN_BWD, dims, dev, st)
+        check(lib().mssm_selective_scan_bwd_ws(
             _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
             _ptr(delta_bias), int(bool(softplus)), _ptr(h0), _ptr(dout),
             _ptr(dlast), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
             _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
-            _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), dims, _stream(dev)))
+            _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), ws, nws, dims, st))
     return g
 
 
@@ -348,8 +385,10 @@ def mamba2_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True,
     dims = Dims(batch, H * P, N, L, _IO[torch.bfloat16], 1 if load_state else 0,
                 int(time_segments), G)
     with torch.cuda.device(dev):
-        check(lib().mssm_mamba2_scan_fwd(
+        st = _stream(dev)
+        ws, nws = _workspace(MSSM_OP_MAMBA2_FWD, dims, dev, st, headdim=P)
+        check(lib().mssm_mamba2_scan_fwd_ws(
             _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-            _ptr(dt_bias), int(bool(softplus)), P, _ptr(out), _ptr(last_state), dims,
-            _stream(dev)))
+            _ptr(dt_bias), int(bool(softplus)), P, _ptr(out), _ptr(last_state),
+            ws, nws, dims, st))
     return out

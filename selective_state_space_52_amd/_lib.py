@@ -15,15 +15,23 @@ MSSM_FLAG_LAYOUT_BLD = 2
 STATUS = {
     0: "MSSM_OK", -1: "MSSM_ERR_NULL", -2: "MSSM_ERR_DIMS",
     -3: "MSSM_ERR_UNSUPPORTED", -4: "MSSM_ERR_ALIGN", -5: "MSSM_ERR_ALIAS",
-    -6: "MSSM_ERR_HIP",
+    -6: "MSSM_ERR_HIP", -7: "MSSM_ERR_WORKSPACE",
 }
+
+MSSM_OP_SCAN_FWD = 0
+MSSM_OP_SCAN_FWD_CONV = 1
+MSSM_OP_SCAN_BWD = 2
+MSSM_OP_MAMBA2_FWD = 3
 
 # every symbol include/mssm.h declares
 EXPORTS = ("mssm_selective_scan_fwd", "mssm_selective_scan_bwd",
            "mssm_selective_scan_fwd_conv", "mssm_causal_conv1d_fwd",
            "mssm_selective_state_update", "mssm_mamba2_scan_fwd",
            "mssm_selective_scan_fwd_plan", "mssm_set_scan_timing_events",
-           "mssm_status_string", "mssm_last_error", "mssm_abi_version")
+           "mssm_status_string", "mssm_last_error", "mssm_abi_version",
+           "mssm_selective_scan_fwd_ws", "mssm_selective_scan_fwd_conv_ws",
+           "mssm_selective_scan_bwd_ws", "mssm_mamba2_scan_fwd_ws",
+           "mssm_workspace_size")
 
 
 class Dims(ctypes.Structure):
@@ -80,6 +88,26 @@ def lib():
                                            ctypes.c_int64, vp, fp,
                                            ctypes.POINTER(Dims), vp]
         L.mssm_mamba2_scan_fwd.restype = i
+        i64 = ctypes.c_int64
+        L.mssm_selective_scan_fwd_ws.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i,
+                                                 vp, fp, vp, i64, ctypes.POINTER(Dims), vp]
+        L.mssm_selective_scan_fwd_ws.restype = i
+        L.mssm_selective_scan_fwd_conv_ws.argtypes = [vp, fp, fp, vp, vp, fp, vp, vp,
+                                                      fp, vp, fp, i, vp, fp, vp, vp, i64,
+                                                      ctypes.POINTER(Dims), vp]
+        L.mssm_selective_scan_fwd_conv_ws.restype = i
+        L.mssm_selective_scan_bwd_ws.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i,
+                                                 fp, vp, fp, vp, vp, fp, fp, fp,
+                                                 fp, vp, fp, fp, vp, i64,
+                                                 ctypes.POINTER(Dims), vp]
+        L.mssm_selective_scan_bwd_ws.restype = i
+        L.mssm_mamba2_scan_fwd_ws.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i,
+                                              i64, vp, fp, vp, i64,
+                                              ctypes.POINTER(Dims), vp]
+        L.mssm_mamba2_scan_fwd_ws.restype = i
+        L.mssm_workspace_size.argtypes = [i, ctypes.POINTER(Dims), i64,
+                                          ctypes.POINTER(i64)]
+        L.mssm_workspace_size.restype = i
         L.mssm_selective_scan_fwd_plan.argtypes = [ctypes.POINTER(Dims),
                                                    ctypes.POINTER(Plan)]
         L.mssm_selective_scan_fwd_plan.restype = i
@@ -99,7 +127,7 @@ class MssmError(RuntimeError):
     def __init__(self, code: int):
         L = lib()
         msg = L.mssm_status_string(code).decode()
-        if code == -6:
+        if code in (-6, -7):
             msg += ": " + L.mssm_last_error().decode()
         super().__init__("%s (%d): %s" % (STATUS.get(code, "?"), code, msg))
         self.code = code

@@ -2,10 +2,9 @@
 // form on the matrix cores (MFMA).
 //
 // The recurrence is the selective scan's with one A, one step and one D per
-// head of P channels, B and C shared by a group of heads (page "Mamba:
-// Selective State Space Models", "Use the Mamba2 block", names the block and
-// its state sizes of 64 or 128; the per-head structure is the Mamba-2
-// architecture's).  For channel p of head h, group g(h), state n:
+// head of P channels, B and C shared by a group of heads (page "Mamba State
+// Space Model", "Use the Mamba2 block", names the block and its state sizes
+// of 64 or 128; the per-head structure is the Mamba-2 architecture's).  For channel p of head h, group g(h), state n:
 //   Delta_t = softplus(dt_t + bias_h),   a_t = Delta_t A_h
 //   H_t[p,n] = exp(a_t) H_{t-1}[p,n] + Delta_t x_t[p] B_t[n]
 //   y_t[p]   = sum_n C_t[n] H_t[p,n] + D_h x_t[p],   out = y silu(z)

@@ -29,6 +29,17 @@ constexpr int kDefaultCUs = 256;      // MI355X compute units
 
 int g_cu_count = 0;  // cached compute-unit count of the current device
 
+// Caches the current device's compute-unit count (first HIP call of a call
+// that launches work; validation has finished by then).
+void refresh_cu_count() {
+  if (g_cu_count > 0) return;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      cus > 0)
+    g_cu_count = cus;
+}
+
 // Per device: a side stream (default priority) and fork/join events, made on
 // first use and kept until the process ends, plus a lock that keeps one
 // call's fork, side-stream work and join together.
@@ -96,6 +107,19 @@ int check_common_dims(const mssm_dims* dims) {
       dims->seqlen <= 0)
     return MSSM_ERR_DIMS;
   if (!valid_dstate(dims->dstate)) return MSSM_ERR_UNSUPPORTED;
+  return MSSM_OK;
+}
+
+// A caller-supplied workspace: present, 256-byte aligned and large enough
+// when the call needs one (need > 0).
+int check_workspace(const void* ws, int64_t ws_bytes, int64_t need) {
+  if (need <= 0) return MSSM_OK;
+  if (!ws || ws_bytes < need || !aligned(ws, 256)) {
+    std::snprintf(g_last_error, sizeof(g_last_error),
+                  "workspace %p of %lld bytes; the call needs %lld bytes, 256-byte aligned",
+                  ws, (long long)ws_bytes, (long long)need);
+    return MSSM_ERR_WORKSPACE;
+  }
   return MSSM_OK;
 }
 
@@ -204,6 +228,8 @@ const char* mssm_status_string(int status) {
     case MSSM_ERR_ALIGN: return "a pointer is not aligned to its element size";
     case MSSM_ERR_ALIAS: return "an output overlaps another argument";
     case MSSM_ERR_HIP: return "a HIP runtime call failed (see mssm_last_error)";
+    case MSSM_ERR_WORKSPACE:
+      return "workspace missing, too small or not 256-byte aligned (see mssm_last_error)";
     default: return "unknown status";
   }
 }
@@ -222,16 +248,19 @@ int mssm_selective_scan_fwd_plan(const mssm_dims* dims, mssm_plan* plan) {
 
 }  // extern "C"
 
-namespace {
+namespace mssm {
 
 // The forward scan, optionally fed by the causal conv (conv_w non-null: `u`
-// is the conv input x).
-int scan_fwd_impl(const void* u, const void* delta, const float* A,
-                  const void* B, const void* C, const float* D, const void* z,
-                  const float* delta_bias, int softplus, void* out,
-                  float* last_state, const float* conv_w, const float* conv_b,
-                  const void* conv_init, void* u_out, const mssm_dims* dims,
-                  void* stream) {
+// is the conv input x).  Workspace: `ws` (ws_bytes long) from the caller, or
+// with ws == nullptr and WsMode::kAllocate taken stream-ordered from HIP's
+// pool for this call.  WsMode::kOneStream runs every launch on the caller's
+// stream (no side stream, no events).
+int scan_fwd_entry(const void* u, const void* delta, const float* A,
+                   const void* B, const void* C, const float* D, const void* z,
+                   const float* delta_bias, int softplus, void* out,
+                   float* last_state, const float* conv_w, const float* conv_b,
+                   const void* conv_init, void* u_out, void* ws_in, int64_t ws_bytes,
+                   WsMode mode, const mssm_dims* dims, void* stream) {
   int rc = check_common_dims(dims);
   if (rc != MSSM_OK) return rc;
   if (dims->flags & ~(MSSM_FLAG_LOAD_STATE | MSSM_FLAG_LAYOUT_BLD))
@@ -278,14 +307,7 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A,
     return MSSM_ERR_ALIAS;
 
   // --- validation done; HIP calls from here on ---
-  if (g_cu_count <= 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
-                              dev) == hipSuccess &&
-        cus > 0)
-      g_cu_count = cus;
-  }
+  refresh_cu_count();
   mssm_plan plan;
   rc = make_plan(dims, g_cu_count > 0 ? g_cu_count : kDefaultCUs, &plan);
   if (rc != MSSM_OK) return rc;
@@ -315,11 +337,16 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A,
   p.u_out = u_out;
   p.layout_bld = bld ? 1 : 0;
 
+  if (mode != WsMode::kAllocate) {
+    rc = check_workspace(ws_in, ws_bytes, plan.workspace_bytes);
+    if (rc != MSSM_OK) return rc;
+  }
   hipStream_t st = (hipStream_t)stream;
   int dev = -1;
   SideStream* side = nullptr;
   std::unique_lock<std::mutex> side_guard;
-  if (plan.split_groups > 0 && plan.whole_groups > 0 && hipGetDevice(&dev) == hipSuccess) {
+  if (mode != WsMode::kOneStream && plan.split_groups > 0 && plan.whole_groups > 0 &&
+      hipGetDevice(&dev) == hipSuccess) {
     side = side_stream_of(dev);
     if (side) {
       side_guard = std::unique_lock<std::mutex>(g_side_lock[dev]);
@@ -328,8 +355,8 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A,
       p.ev_join = side->join;
     }
   }
-  void* ws = nullptr;
-  {
+  void* ws = ws_in;
+  if (mode == WsMode::kAllocate) {
     hipError_t e = hipMallocAsync(&ws, (size_t)plan.workspace_bytes, st);
     if (e != hipSuccess) {
       set_hip_error("hipMallocAsync(workspace)", e);
@@ -349,7 +376,7 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A,
   }
   hipError_t e = mssm::launch_scan(p, (int)N, io == 2, vec, st);
   if (e != hipSuccess) set_hip_error("scan launch", e);
-  if (ws) {
+  if (mode == WsMode::kAllocate && ws) {
     hipError_t f = hipFreeAsync(ws, st);
     if (e == hipSuccess && f != hipSuccess) {
       set_hip_error("hipFreeAsync(workspace)", f);
@@ -359,7 +386,10 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A,
   return e == hipSuccess ? MSSM_OK : MSSM_ERR_HIP;
 }
 
-}  // namespace
+}  // namespace mssm
+
+using mssm::WsMode;
+using mssm::scan_fwd_entry;
 
 extern "C" {
 
@@ -368,9 +398,20 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
                             const void* z, const float* delta_bias,
                             int softplus, void* out, float* last_state,
                             const mssm_dims* dims, void* stream) {
-  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, out,
-                       last_state, nullptr, nullptr, nullptr, nullptr, dims,
-                       stream);
+  return scan_fwd_entry(u, delta, A, B, C, D, z, delta_bias, softplus, out,
+                        last_state, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                        WsMode::kAllocate, dims, stream);
+}
+
+int mssm_selective_scan_fwd_ws(const void* u, const void* delta, const float* A,
+                               const void* B, const void* C, const float* D,
+                               const void* z, const float* delta_bias, int softplus,
+                               void* out, float* last_state, void* workspace,
+                               int64_t workspace_bytes, const mssm_dims* dims,
+                               void* stream) {
+  return scan_fwd_entry(u, delta, A, B, C, D, z, delta_bias, softplus, out,
+                        last_state, nullptr, nullptr, nullptr, nullptr, workspace,
+                        workspace_bytes, WsMode::kCaller, dims, stream);
 }
 
 int mssm_selective_scan_fwd_conv(const void* x, const float* conv_weight,
@@ -382,9 +423,23 @@ int mssm_selective_scan_fwd_conv(const void* x, const float* conv_weight,
                                  void* u_out, const mssm_dims* dims,
                                  void* stream) {
   if (!conv_weight) return MSSM_ERR_NULL;
-  return scan_fwd_impl(x, delta, A, B, C, D, z, delta_bias, softplus, out,
-                       last_state, conv_weight, conv_bias, conv_init, u_out,
-                       dims, stream);
+  return scan_fwd_entry(x, delta, A, B, C, D, z, delta_bias, softplus, out,
+                        last_state, conv_weight, conv_bias, conv_init, u_out, nullptr, 0,
+                        WsMode::kAllocate, dims, stream);
+}
+
+int mssm_selective_scan_fwd_conv_ws(const void* x, const float* conv_weight,
+                                    const float* conv_bias, const void* conv_init,
+                                    const void* delta, const float* A, const void* B,
+                                    const void* C, const float* D, const void* z,
+                                    const float* delta_bias, int softplus, void* out,
+                                    float* last_state, void* u_out, void* workspace,
+                                    int64_t workspace_bytes, const mssm_dims* dims,
+                                    void* stream) {
+  if (!conv_weight) return MSSM_ERR_NULL;
+  return scan_fwd_entry(x, delta, A, B, C, D, z, delta_bias, softplus, out,
+                        last_state, conv_weight, conv_bias, conv_init, u_out, workspace,
+                        workspace_bytes, WsMode::kCaller, dims, stream);
 }
 
 int mssm_causal_conv1d_fwd(const void* x, const float* weight,
@@ -433,14 +488,37 @@ int mssm_causal_conv1d_fwd(const void* x, const float* weight,
   return MSSM_OK;
 }
 
-int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
-                            const void* B, const void* C, const float* D,
-                            const void* z, const float* delta_bias,
-                            int softplus, const float* h0, const void* dout,
-                            const float* dlast, void* du, void* ddelta,
-                            float* dA, float* dB, float* dC, float* dD,
-                            void* dz, float* ddelta_bias, float* dh0,
-                            const mssm_dims* dims, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Backward work split and workspace size for dims (HIP calls: the CU count
+// and pass R's occupancy); returns MSSM_OK or MSSM_ERR_DIMS.
+int bwd_layout(const mssm_dims* dims, int* segments, int64_t* ws_bytes) {
+  const int64_t batch = dims->batch, dim = dims->dim, N = dims->dstate, L = dims->seqlen;
+  const int64_t gpb = (dim + kLanes - 1) / kLanes;
+  const bool bf16 = dims->io_dtype == MSSM_BF16;
+  const int tile = mssm::bwd_tile();
+  refresh_cu_count();
+  const int64_t tiles = (L + tile - 1) / tile;
+  const int seg = mssm::bwd_segments(batch * gpb, tiles, g_cu_count > 0 ? g_cu_count : kDefaultCUs,
+                                     mssm::bwd_wgs_per_cu((int)N, bf16), dims->time_segments);
+  if (batch * gpb * seg > INT32_MAX) return MSSM_ERR_DIMS;
+  *segments = seg;
+  *ws_bytes = mssm::bwd_workspace(batch, dim, L, (int)N, bf16, seg, groups_of(dims), nullptr,
+                                  nullptr);
+  return MSSM_OK;
+}
+
+int scan_bwd_entry(const void* u, const void* delta, const float* A,
+                   const void* B, const void* C, const float* D,
+                   const void* z, const float* delta_bias,
+                   int softplus, const float* h0, const void* dout,
+                   const float* dlast, void* du, void* ddelta,
+                   float* dA, float* dB, float* dC, float* dD,
+                   void* dz, float* ddelta_bias, float* dh0, void* ws_in,
+                   int64_t ws_in_bytes, bool allocate, const mssm_dims* dims,
+                   void* stream) {
   int rc = check_common_dims(dims);
   if (rc != MSSM_OK) return rc;
   if (dims->dstate > 32) return MSSM_ERR_UNSUPPORTED;
@@ -502,19 +580,15 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
                    aligned(du, 16) && aligned(ddelta, 16) &&
                    (!z || aligned(z, 16)) && (!dz || aligned(dz, 16));
   const int tile = mssm::bwd_tile();
-  if (g_cu_count <= 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
-                              dev) == hipSuccess &&
-        cus > 0)
-      g_cu_count = cus;
-  }
   const int64_t tiles = (L + tile - 1) / tile;
-  const int segments =
-      mssm::bwd_segments(batch * gpb, tiles, g_cu_count > 0 ? g_cu_count : kDefaultCUs,
-                         mssm::bwd_wgs_per_cu((int)N, io == 2), dims->time_segments);
-  if (batch * gpb * segments > INT32_MAX) return MSSM_ERR_DIMS;
+  int segments = 1;
+  int64_t ws_bytes = 0;
+  rc = bwd_layout(dims, &segments, &ws_bytes);
+  if (rc != MSSM_OK) return rc;
+  if (!allocate) {
+    rc = check_workspace(ws_in, ws_in_bytes, ws_bytes);
+    if (rc != MSSM_OK) return rc;
+  }
   mssm::BwdParams p;
   std::memset(&p, 0, sizeof(p));
   p.u = u; p.delta = delta; p.z = z; p.dout = dout; p.A = A; p.B = B; p.C = C;
@@ -533,10 +607,8 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
   p.ev_stop = g_ev_stop;
 
   hipStream_t st = (hipStream_t)stream;
-  const int64_t ws_bytes =
-      mssm::bwd_workspace(batch, dim, L, (int)N, io == 2, segments, G, nullptr, nullptr);
-  void* ws = nullptr;
-  {
+  void* ws = ws_in;
+  if (allocate) {
     hipError_t e = hipMallocAsync(&ws, (size_t)ws_bytes, st);
     if (e != hipSuccess) {
       set_hip_error("hipMallocAsync(workspace)", e);
@@ -546,12 +618,45 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
   mssm::bwd_workspace(batch, dim, L, (int)N, io == 2, segments, G, ws, &p);
   hipError_t e = mssm::launch_scan_bwd(p, (int)N, io == 2, vec, st);
   if (e != hipSuccess) set_hip_error("backward scan launch", e);
-  hipError_t f = hipFreeAsync(ws, st);
-  if (e == hipSuccess && f != hipSuccess) {
-    set_hip_error("hipFreeAsync(workspace)", f);
-    e = f;
+  if (allocate) {
+    hipError_t f = hipFreeAsync(ws, st);
+    if (e == hipSuccess && f != hipSuccess) {
+      set_hip_error("hipFreeAsync(workspace)", f);
+      e = f;
+    }
   }
   return e == hipSuccess ? MSSM_OK : MSSM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A,
+                            const void* B, const void* C, const float* D,
+                            const void* z, const float* delta_bias,
+                            int softplus, const float* h0, const void* dout,
+                            const float* dlast, void* du, void* ddelta,
+                            float* dA, float* dB, float* dC, float* dD,
+                            void* dz, float* ddelta_bias, float* dh0,
+                            const mssm_dims* dims, void* stream) {
+  return scan_bwd_entry(u, delta, A, B, C, D, z, delta_bias, softplus, h0, dout, dlast,
+                        du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, nullptr, 0,
+                        true, dims, stream);
+}
+
+int mssm_selective_scan_bwd_ws(const void* u, const void* delta, const float* A,
+                               const void* B, const void* C, const float* D,
+                               const void* z, const float* delta_bias,
+                               int softplus, const float* h0, const void* dout,
+                               const float* dlast, void* du, void* ddelta,
+                               float* dA, float* dB, float* dC, float* dD,
+                               void* dz, float* ddelta_bias, float* dh0,
+                               void* workspace, int64_t workspace_bytes,
+                               const mssm_dims* dims, void* stream) {
+  return scan_bwd_entry(u, delta, A, B, C, D, z, delta_bias, softplus, h0, dout, dlast,
+                        du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, workspace,
+                        workspace_bytes, false, dims, stream);
 }
 
 int mssm_selective_state_update(float* state, const void* x, const void* dt,
@@ -603,10 +708,15 @@ int mssm_selective_state_update(float* state, const void* x, const void* dt,
   return MSSM_OK;
 }
 
-int mssm_mamba2_scan_fwd(const void* x, const void* dt, const float* A, const void* B,
-                         const void* C, const float* D, const void* z,
-                         const float* dt_bias, int softplus, int64_t headdim, void* out,
-                         float* last_state, const mssm_dims* dims, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int mamba2_entry(const void* x, const void* dt, const float* A, const void* B,
+                 const void* C, const float* D, const void* z,
+                 const float* dt_bias, int softplus, int64_t headdim, void* out,
+                 float* last_state, void* ws_in, int64_t ws_in_bytes, bool allocate,
+                 const mssm_dims* dims, void* stream) {
   if (!dims) return MSSM_ERR_NULL;
   if (dims->io_dtype != MSSM_BF16) return MSSM_ERR_UNSUPPORTED;
   if (dims->flags & ~MSSM_FLAG_LOAD_STATE) return MSSM_ERR_UNSUPPORTED;
@@ -654,14 +764,7 @@ int mssm_mamba2_scan_fwd(const void* x, const void* dt, const float* A, const vo
   if (overlap(r_out, r_state)) return MSSM_ERR_ALIAS;
 
   // --- validation done; HIP calls from here on ---
-  if (g_cu_count <= 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) ==
-            hipSuccess &&
-        cus > 0)
-      g_cu_count = cus;
-  }
+  refresh_cu_count();
   mssm::Mamba2Params p;
   std::memset(&p, 0, sizeof(p));
   p.x = x; p.dt = dt; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.bias = dt_bias;
@@ -673,13 +776,21 @@ int mssm_mamba2_scan_fwd(const void* x, const void* dt, const float* A, const vo
                     dims->time_segments, &p);
   hipStream_t st = (hipStream_t)stream;
   const int64_t ws_bytes = mssm::mamba2_workspace(p, nullptr, nullptr);
+  if (!allocate) {
+    const int rc = check_workspace(ws_in, ws_in_bytes, ws_bytes);
+    if (rc != MSSM_OK) return rc;
+  }
   void* ws = nullptr;
   hipError_t e = hipSuccess;
   if (ws_bytes > 0) {
-    e = hipMallocAsync(&ws, (size_t)ws_bytes, st);
-    if (e != hipSuccess) {
-      set_hip_error("hipMallocAsync(workspace)", e);
-      return MSSM_ERR_HIP;
+    if (allocate) {
+      e = hipMallocAsync(&ws, (size_t)ws_bytes, st);
+      if (e != hipSuccess) {
+        set_hip_error("hipMallocAsync(workspace)", e);
+        return MSSM_ERR_HIP;
+      }
+    } else {
+      ws = ws_in;
     }
     mssm::mamba2_workspace(p, ws, &p);
   }
@@ -687,7 +798,7 @@ int mssm_mamba2_scan_fwd(const void* x, const void* dt, const float* A, const vo
   if (e == hipSuccess) e = mssm::launch_mamba2_scan(p, st);
   if (e == hipSuccess && g_ev_stop) e = hipEventRecord((hipEvent_t)g_ev_stop, st);
   if (e != hipSuccess) set_hip_error("mamba2 scan launch", e);
-  if (ws) {
+  if (allocate && ws) {
     const hipError_t f = hipFreeAsync(ws, st);
     if (e == hipSuccess && f != hipSuccess) {
       set_hip_error("hipFreeAsync(workspace)", f);
@@ -695,6 +806,81 @@ int mssm_mamba2_scan_fwd(const void* x, const void* dt, const float* A, const vo
     }
   }
   return e == hipSuccess ? MSSM_OK : MSSM_ERR_HIP;
+}
+
+// The Mamba-2 scan's time split and workspace for dims (HIP call: the CU count).
+int64_t mamba2_ws_bytes(const mssm_dims* dims, int64_t headdim) {
+  refresh_cu_count();
+  mssm::Mamba2Params p;
+  std::memset(&p, 0, sizeof(p));
+  p.batch = dims->batch;
+  p.L = dims->seqlen;
+  p.nheads = dims->dim / headdim;
+  p.N = dims->dstate;
+  mssm::mamba2_plan(p.batch * p.nheads, p.L, g_cu_count > 0 ? g_cu_count : kDefaultCUs,
+                    dims->time_segments, &p);
+  return mssm::mamba2_workspace(p, nullptr, nullptr);
+}
+
+}  // namespace
+
+extern "C" {
+
+int mssm_mamba2_scan_fwd(const void* x, const void* dt, const float* A, const void* B,
+                         const void* C, const float* D, const void* z,
+                         const float* dt_bias, int softplus, int64_t headdim, void* out,
+                         float* last_state, const mssm_dims* dims, void* stream) {
+  return mamba2_entry(x, dt, A, B, C, D, z, dt_bias, softplus, headdim, out, last_state,
+                      nullptr, 0, true, dims, stream);
+}
+
+int mssm_mamba2_scan_fwd_ws(const void* x, const void* dt, const float* A, const void* B,
+                            const void* C, const float* D, const void* z,
+                            const float* dt_bias, int softplus, int64_t headdim, void* out,
+                            float* last_state, void* workspace, int64_t workspace_bytes,
+                            const mssm_dims* dims, void* stream) {
+  return mamba2_entry(x, dt, A, B, C, D, z, dt_bias, softplus, headdim, out, last_state,
+                      workspace, workspace_bytes, false, dims, stream);
+}
+
+int mssm_workspace_size(int op, const mssm_dims* dims, int64_t headdim, int64_t* bytes) {
+  if (!bytes) return MSSM_ERR_NULL;
+  *bytes = 0;
+  int rc = MSSM_OK;
+  switch (op) {
+    case MSSM_OP_SCAN_FWD:
+    case MSSM_OP_SCAN_FWD_CONV: {
+      mssm_plan plan;
+      refresh_cu_count();
+      rc = mssm_selective_scan_fwd_plan(dims, &plan);
+      if (rc == MSSM_OK) *bytes = plan.workspace_bytes;
+      return rc;
+    }
+    case MSSM_OP_SCAN_BWD: {
+      rc = check_common_dims(dims);
+      if (rc != MSSM_OK) return rc;
+      if (dims->dstate > 32 || (dims->flags & ~MSSM_FLAG_LAYOUT_BLD)) return MSSM_ERR_UNSUPPORTED;
+      rc = check_scan_groups(dims);
+      if (rc != MSSM_OK) return rc;
+      if (dims->time_segments < 0) return MSSM_ERR_DIMS;
+      int seg = 1;
+      int64_t ws = 0;
+      rc = bwd_layout(dims, &seg, &ws);
+      if (rc == MSSM_OK) *bytes = ws;
+      return rc;
+    }
+    case MSSM_OP_MAMBA2_FWD: {
+      if (!dims) return MSSM_ERR_NULL;
+      if (dims->batch <= 0 || dims->dim <= 0 || dims->seqlen <= 0 || dims->time_segments < 0 ||
+          headdim <= 0 || dims->dim % headdim != 0)
+        return MSSM_ERR_DIMS;
+      if (dims->dstate != 64 && dims->dstate != 128) return MSSM_ERR_UNSUPPORTED;
+      *bytes = mamba2_ws_bytes(dims, headdim);
+      return MSSM_OK;
+    }
+    default:
+      return MSSM_ERR_UNSUPPORTED;
+  }
 }
 
 }  // extern "C"

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mssm.h"
+
 namespace mssm {
 
 // One forward-scan call, as the kernels see it.
@@ -145,6 +147,21 @@ struct BwdParams {
   void* ev_start;         // optional timing events around pass F, the
   void* ev_stop;          // combine and pass R
 };
+
+// Where a forward call's workspace comes from: allocated stream-ordered for
+// the call (kAllocate), supplied by the caller (kCaller), or supplied by the
+// caller with every launch kept on the caller's stream (kOneStream: no side
+// stream, no events; used where the library may create nothing).
+enum class WsMode { kAllocate, kCaller, kOneStream };
+
+// The forward scan entry shared by the C ABI's forward calls (mssm_api.cpp);
+// returns an MSSM_* status.  conv_w non-null: `u` is the conv input x.
+int scan_fwd_entry(const void* u, const void* delta, const float* A,
+                   const void* B, const void* C, const float* D, const void* z,
+                   const float* delta_bias, int softplus, void* out,
+                   float* last_state, const float* conv_w, const float* conv_b,
+                   const void* conv_init, void* u_out, void* ws, int64_t ws_bytes,
+                   WsMode mode, const ::mssm_dims* dims, void* stream);
 
 // Waves per 64-channel workgroup: each wave owns dstate / waves states.
 int scan_waves_per_group(int N);

@@ -525,23 +525,28 @@ hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
     e = hipEventRecord((hipEvent_t)p.ev_fork, stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(side, (hipEvent_t)p.ev_fork, 0);
     if (e != hipSuccess) return e;
-    e = launch_tasks<N, NG, BF16, VEC, CONV>(p, s, 0, 0, p.split_groups * (p.segments - 1), side);
-    if (e != hipSuccess) return e;
-    e = launch_combine(p, s, N, side);
-    if (e != hipSuccess) return e;
-    e = launch_tasks<N, NG, BF16, VEC, CONV>(p, s, p.split_groups * p.segments,
-                                       p.whole_groups, 0, side);
-    if (e != hipSuccess) return e;
+    // From here on the caller's stream always waits for the side stream
+    // before this returns, whatever fails: work already queued on the side
+    // stream reads and writes the workspace, so nothing the caller orders
+    // after this call (freeing or reusing the workspace) may overtake it.
+    hipError_t es = launch_tasks<N, NG, BF16, VEC, CONV>(
+        p, s, 0, 0, p.split_groups * (p.segments - 1), side);
+    if (es == hipSuccess) es = launch_combine(p, s, N, side);
+    if (es == hipSuccess)
+      es = launch_tasks<N, NG, BF16, VEC, CONV>(p, s, p.split_groups * p.segments,
+                                              p.whole_groups, 0, side);
+    if (es == hipSuccess && p.ev_start) es = hipEventRecord((hipEvent_t)p.ev_start, stream);
+    if (es == hipSuccess)
+      es = launch_tasks<N, NG, BF16, VEC, CONV>(p, s, p.whole_groups, 0, 0, stream);
+    if (es == hipSuccess && p.ev_stop) es = hipEventRecord((hipEvent_t)p.ev_stop, stream);
     e = hipEventRecord((hipEvent_t)p.ev_join, side);
-    if (e != hipSuccess) return e;
-    if (p.ev_start) {
-      e = hipEventRecord((hipEvent_t)p.ev_start, stream);
-      if (e != hipSuccess) return e;
-    }
-    e = launch_tasks<N, NG, BF16, VEC, CONV>(p, s, p.whole_groups, 0, 0, stream);
-    if (e == hipSuccess && p.ev_stop) e = hipEventRecord((hipEvent_t)p.ev_stop, stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(stream, (hipEvent_t)p.ev_join, 0);
-    return e;
+    if (e != hipSuccess) {
+      // the join could not be ordered: drain the side stream so that the
+      // workspace is idle when this returns
+      (void)hipStreamSynchronize(side);
+    }
+    return es != hipSuccess ? es : e;
   }
   if (p.ev_start) {
     e = hipEventRecord((hipEvent_t)p.ev_start, stream);

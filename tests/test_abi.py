@@ -39,8 +39,8 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.mssm_abi_version() == 1
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    assert L.mssm_abi_version() == 2
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         s = L.mssm_status_string(code).decode()
         assert s and s != "unknown status"
     assert L.mssm_status_string(42).decode() == "unknown status"
@@ -263,3 +263,49 @@ def test_mamba2_validation_codes(L):
     assert m2(_dims(**ok), out=p[0] + 64) == -5             # out over x
     assert m2(_dims(**ok), last=p[3]) == -5                 # state over B
     assert m2(_dims(**ok), last=p[8] + 16) == -5            # state over out
+
+
+def test_workspace_entry_points(L):
+    """The caller-workspace forms size their workspace like the plan and
+    refuse a missing, short or misaligned one before launching anything."""
+    from selective_state_space_52_amd._lib import Plan
+    import ctypes as ct
+    dims = _dims(4, 5120, 16, 2048)
+    plan = Plan()
+    assert L.mssm_selective_scan_fwd_plan(ct.byref(dims), ct.byref(plan)) == 0
+    n = ct.c_int64(-1)
+    assert L.mssm_workspace_size(0, ct.byref(dims), 0, ct.byref(n)) == 0
+    assert n.value == plan.workspace_bytes > 0
+    assert L.mssm_workspace_size(1, ct.byref(dims), 0, ct.byref(n)) == 0
+    assert n.value == plan.workspace_bytes
+    assert L.mssm_workspace_size(2, ct.byref(dims), 0, ct.byref(n)) == 0
+    assert n.value > 0
+    m2 = _dims(4, 5120, 128, 2048)
+    assert L.mssm_workspace_size(3, ct.byref(m2), 64, ct.byref(n)) == 0
+    assert L.mssm_workspace_size(3, ct.byref(m2), 0, ct.byref(n)) == -2
+    assert L.mssm_workspace_size(9, ct.byref(dims), 0, ct.byref(n)) == -3
+    assert L.mssm_workspace_size(0, ct.byref(dims), 0, None) == -1
+    assert L.mssm_workspace_size(2, ct.byref(_dims(N=64)), 0, ct.byref(n)) == -3
+
+    p = _ptrs(11)
+    need = plan.workspace_bytes
+
+    def fwd_ws(ws, nbytes):
+        return L.mssm_selective_scan_fwd_ws(p[0], p[1], p[2], p[3], p[4], p[5], p[6],
+                                            p[7], 1, p[8], p[9], ws, nbytes,
+                                            ct.byref(dims), None)
+    assert fwd_ws(None, 0) == -7
+    assert fwd_ws(p[10], need - 1) == -7
+    assert fwd_ws(p[10] + 128, need) == -7                  # 256-byte alignment
+    assert "needs %d bytes" % need in L.mssm_last_error().decode()
+    # validation still comes first: a bad pointer wins over the workspace
+    assert L.mssm_selective_scan_fwd_ws(None, p[1], p[2], p[3], p[4], p[5], p[6],
+                                        p[7], 1, p[8], p[9], None, 0,
+                                        ct.byref(dims), None) == -1
+    q = _ptrs(len(BWD_ARGS) + 1)
+    b = dict(zip(BWD_ARGS, q))
+    assert L.mssm_selective_scan_bwd_ws(
+        b["u"], b["delta"], b["A"], b["B"], b["C"], b["D"], b["z"], b["bias"], 1,
+        b["h0"], b["dout"], b["dlast"], b["du"], b["ddelta"], b["dA"], b["dB"],
+        b["dC"], b["dD"], b["dz"], b["dbias"], b["dh0"], None, 0, ct.byref(dims),
+        None) == -7

@@ -128,25 +128,13 @@ def test_fused_scan_conv_chained():
     check_out(whole, ro, "bf16", "whole out")
 
 
-def test_fused_full_size_sampled_rows():
+def test_fused_full_size_every_element():
     """The 2.8B-shaped layer with the conv, in the launch configuration the
-    bench times; rows sampled at group edges and at random."""
-    import oracle
+    bench times: every output and final state against the oracle's conv then
+    scan."""
     s, inp, cp = _case("mamba2p8b_layer")
+    print("fused full size: batch %d dim %d L %d" % (s.batch, s.dim, s.seqlen), flush=True)
     out, last, _ = _fused(inp, cp)
-    rows = sample_rows(s.batch, s.dim, k=24, seed=3)
-    outs, lasts = [], []
-    for b, d in rows:
-        u = oracle.causal_conv1d(inp["u"][b:b + 1, d:d + 1], cp["weight"][d:d + 1],
-                                 cp["bias"][d:d + 1], cp["init"][b:b + 1, d:d + 1])[0, 0]
-        o, l = oracle.scan_row(u, inp["delta"][b, d], inp["A"][d], inp["B"][b],
-                               inp["C"][b], D_d=float(inp["D"][d]), z=inp["z"][b, d],
-                               bias_d=float(inp["delta_bias"][d]),
-                               softplus=inp["softplus"])
-        outs.append(o)
-        lasts.append(l)
-    bi = [b for b, _ in rows]
-    di = [d for _, d in rows]
-    _report("fused full size (24 rows)",
-            check_out(out[bi, di], np.stack(outs), "bf16", "out rows"))
-    check_state(last[bi, di], np.stack(lasts), "last rows")
+    _, ro, rl = _oracle_fused(inp, cp)
+    _report("fused full size every element", check_out(out, ro, "bf16", "out"))
+    check_state(last, rl, "last_state")

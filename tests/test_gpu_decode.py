@@ -98,18 +98,37 @@ def test_decode_iterated_equals_gpu_scan(N):
 
 
 def test_decode_full_size_1000_steps():
-    """The decode workload (256 sequences x D 5120, N 16) for 1000 steps; the
-    oracle follows 24 sampled rows through all 1000 steps."""
+    """The decode workload (256 sequences x D 5120, N 16) for 1000 steps, each
+    on one in-place state; the oracle follows every row, and every output and
+    every state element is compared after steps 1, 500 and 1000."""
+    import oracle
+    import selective_state_space_52_amd as m
     s = W.spec("decode")
-    rows = [(0, 0), (255, 5119), (17, 64), (128, 2559)] + [
-        (int(b), int(d)) for b, d in zip(np.random.default_rng(4).integers(0, 256, 20),
-                                         np.random.default_rng(5).integers(0, 5120, 20))]
-    state, ref_state, og, orf = _run_steps(s, steps=s.steps, rows=rows)
-    for k, (g, r) in enumerate(zip(og, orf)):
-        check_out(g, r, "bf16", "decode sampled out %d" % k)
-    got = torch.stack([state[b, d] for b, d in rows])
-    check_state(got, ref_state[:, 0, :], "decode sampled state after 1000 steps")
-    assert torch.isfinite(state).all()
+    print("decode full size: %d x %d, N %d, %d steps" % (s.batch, s.dim, s.dstate,
+                                                         s.steps), flush=True)
+    par = W.make_decode_params(s)
+    toks = [W.make_decode_token(s, k) for k in range(s.tokens)]
+    dtoks = [{k: to_dev(v) for k, v in t.items()} for t in toks]
+    toks64 = [{k: np64(v) for k, v in t.items()} for t in toks]
+    par64 = {k: np64(v) for k, v in par.items()}
+    state = to_dev(par["state"]).clone()
+    A, D, bias = to_dev(par["A"]), to_dev(par["D"]), to_dev(par["dt_bias"])
+    ref_state = par64["state"]
+    checks = {1, s.steps // 2, s.steps}
+    done = 0
+    for step in range(1, s.steps + 1):
+        t, dt_ = toks64[(step - 1) % len(toks)], dtoks[(step - 1) % len(toks)]
+        out = m.selective_state_update(state, dt_["x"], dt_["dt"], A, dt_["B"], dt_["C"],
+                                       D=D, z=dt_["z"], dt_bias=bias, softplus=s.softplus)
+        ro, ref_state = oracle.state_update(
+            ref_state, t["x"], t["dt"], par64["A"], t["B"], t["C"], D=par64["D"],
+            z=t["z"], dt_bias=par64["dt_bias"], softplus=s.softplus)
+        if step in checks:
+            check_out(out.cpu(), ro, "bf16", "decode out after step %d" % step)
+            check_state(state.cpu(), ref_state, "decode state after step %d" % step)
+            done += 1
+            print("decode step %d: every row within the bars" % step, flush=True)
+    assert done == 3
 
 
 def test_decode_64bit_indices():

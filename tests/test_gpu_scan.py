@@ -5,7 +5,7 @@ import torch
 
 import workloads as W
 from tests.gpu_common import (DEV, check_out, check_state, gpu_scan, np64,
-                              oracle_rows, oracle_scan, sample_rows)
+                              oracle_scan)
 
 pytestmark = pytest.mark.gpu
 
@@ -143,26 +143,63 @@ def test_determinism():
 
 
 @pytest.mark.parametrize("name", ["mamba130m_layer", "mamba2p8b_layer"])
-def test_full_size_sampled_rows(name):
-    """Full-size layer workloads in the bench's launch configuration; sampled
-    rows against the oracle, computed row by row."""
+def test_full_size_every_element(name):
+    """Full-size layer workloads in the launch configuration the bench times
+    (at the 2.8B-shaped layer on 256 CUs: 256 whole channel groups on the
+    caller's stream and 64 groups cut into time segments on the side stream),
+    every output and every final state against the oracle; then a second and
+    a third call must reproduce the first bit for bit."""
+    import selective_state_space_52_amd as m
     s = W.spec(name)
+    print("full size %s: batch %d dim %d N %d L %d" % (name, s.batch, s.dim, s.dstate,
+                                                    s.seqlen), flush=True)
+    plan = m.scan_plan(s.batch, s.dim, s.dstate, s.seqlen)
+    print("plan", plan, flush=True)
+    if name == "mamba2p8b_layer" and torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert plan["whole_groups"] == 256 and plan["split_groups"] == 64
     inp = W.make_scan_inputs(s)
     out, last = gpu_scan(inp)
-    rows = sample_rows(s.batch, s.dim, k=40, seed=s.seed)
-    ro, rl = oracle_rows(inp, rows)
-    g = torch.stack([out[b, d] for b, d in rows])
-    gl = torch.stack([last[b, d] for b, d in rows])
-    _report("%s sampled rows" % name, check_out(g, ro, "bf16", name))
-    check_state(gl, rl, name + " last_state")
-    assert torch.isfinite(out.float()).all()
+    ro, rl = oracle_scan(inp)
+    _report("%s every element" % name, check_out(out, ro, "bf16", name))
+    check_state(last, rl, name + " last_state")
+    for k in range(2):
+        o2, l2 = gpu_scan(inp)
+        assert torch.equal(o2, out) and torch.equal(l2, last), "repeat %d differs" % (k + 1)
+
+
+def test_two_stream_plan_small():
+    """A shape small enough for the oracle in a second that still takes the
+    bench's two-stream plan: 5 x 3328 channels = 260 groups of 64, so on 256
+    CUs 256 groups run whole on the caller's stream and 4 are cut into time
+    segments (aggregate, combine and main pass on the side stream).  Every
+    element against the oracle, a loaded initial state, and repeat calls bit
+    for bit."""
+    import selective_state_space_52_amd as m
+    batch, dim, N, L = 5, 3328, 16, 1024
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = m.scan_plan(batch, dim, N, L)
+    print("two-stream plan on %d CUs: %s" % (cus, plan), flush=True)
+    if cus == 256:
+        assert plan["whole_groups"] == 256 and plan["split_groups"] == 4
+        assert plan["segments"] >= 2
+    s = W.spec("mamba130m_layer", batch=batch, dim=dim, seqlen=L, seed=260)
+    inp = W.make_scan_inputs(s)
+    h0 = W.make_initial_state(s)
+    out, last = gpu_scan(inp, h0=h0)
+    ro, rl = oracle_scan(inp, h0=h0.double().numpy())
+    _report("two-stream plan every element", check_out(out, ro, "bf16", "out"))
+    check_state(last, rl, "last_state")
+    for k in range(3):
+        o2, l2 = gpu_scan(inp, h0=h0)
+        assert torch.equal(o2, out) and torch.equal(l2, last), "repeat %d differs" % (k + 1)
 
 
 def test_long_sequence_split_vs_unsplit():
     """Long sequence (batch 1, D 1536, N 16, L 131072): one call (rows cut into
     time segments inside the library) against 64 chained calls of 2048 steps
-    carrying last_state, and sampled rows against the oracle."""
+    carrying last_state, both against the oracle on every element."""
     s = W.spec("long_chunked")
+    print("long sequence: dim %d L %d" % (s.dim, s.seqlen), flush=True)
     inp = W.make_scan_inputs(s)
     out, last = gpu_scan(inp)
     state = torch.zeros(1, s.dim, s.dstate)
@@ -176,13 +213,11 @@ def test_long_sequence_split_vs_unsplit():
         o, state = gpu_scan(part, h0=state)
         pieces.append(o)
     chunked = torch.cat(pieces, dim=-1)
-    rows = sample_rows(1, s.dim, k=12, seed=3)
-    ro, rl = oracle_rows(inp, rows)
+    ro, rl = oracle_scan(inp)
     for got, lab in ((out, "one call"), (chunked, "chunked")):
-        g = torch.stack([got[b, d] for b, d in rows])
-        _report("long %s" % lab, check_out(g, ro, "bf16", lab))
-    check_state(torch.stack([last[b, d] for b, d in rows]), rl, "one-call last_state")
-    check_state(torch.stack([state[b, d] for b, d in rows]), rl, "chunked last_state")
+        _report("long %s every element" % lab, check_out(got, ro, "bf16", lab))
+    check_state(last, rl, "one-call last_state")
+    check_state(state, rl, "chunked last_state")
     # split vs unsplit over every row
     check_state(last, np64(state), "split vs unsplit last_state")
     diff = (out.float() - chunked.float()).abs()
