@@ -81,6 +81,10 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other forward workloads and the 1-thread oracle runs")
+    ap.add_argument("--only-forward", action="store_true",
+                    help="time the workload's forward calls alone (profiling runs)")
     ap.add_argument("--backward-steps", type=int, default=20)
     ap.add_argument("--bwd-time-segments", type=int, default=0)
     ap.add_argument("--decode-steps", type=int, default=1000)
@@ -90,7 +94,7 @@ def parse():
     ap.add_argument("--mamba2-traffic-record", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     ap.add_argument("--mamba2-steps", type=int, default=20)
-    ap.add_argument("--cpu-seconds", type=float, default=5.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--rocprof-summary", default=None)
     ap.add_argument("--traffic-record", nargs=4, default=None,
@@ -142,11 +146,11 @@ def kernel_source_hash(sources=None) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, plan: dict):
-    """HBM bytes per forward call (all its kernels; the timed main kernel's
-    window holds all of them but the B/C pack) from the committed counter
-    summary, or None when it is missing or was taken on another version of
-    the kernel source."""
+def load_traffic(workload: str, plan: dict, key: str = "main_pass_hbm_bytes_per_launch"):
+    """HBM bytes from the committed counter record of this workload's forward:
+    per launch of the scan kernel (the kernel the roofline is about; one per
+    call), or per call (the B/C pack and the scan launch).  None when the
+    record is missing or was taken on another version of the kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
@@ -157,7 +161,110 @@ def load_traffic(workload: str, plan: dict):
         return None
     if rec.get("segments") != plan["segments"]:
         return None
-    return rec.get("hbm_bytes_per_call")
+    return rec.get(key)
+
+
+def hbm_roofline(nbytes: float, ms: float, kernel: str, kernel_ms: float, traffic=None):
+    """HBM roofline entry: algorithmic bytes of one launch over its duration."""
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+            "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes_per_launch": int(nbytes)}
+
+
+def alu_figures(slots: float, ms: float, nbytes: float):
+    """Algorithmic VALU issue slots against the chip's issue peak, and the HBM
+    fraction those slots allow at 100% issue (the path's ALU ceiling)."""
+    t_alu = slots / (VALU_PEAK_TSLOTS * 1e12)                 # s at full issue
+    ceiling = nbytes / t_alu / 1e9 / HBM_PEAK_GBS
+    achieved = slots / (ms * 1e-3) / 1e12
+    return {"achieved": round(achieved, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
+            "unit": "Tslot/s", "frac": round(achieved / VALU_PEAK_TSLOTS, 4),
+            "slots_per_element": None, "ceiling_frac_of_hbm_peak": round(ceiling, 4)}
+
+
+def scan_slots(s) -> float:
+    return s.state_elements * SLOTS_PER_STATE_ELEM + s.elements * SLOTS_PER_ELEM
+
+
+def make_sets(torch, W, dev, name, rotate, **over):
+    s = W.spec(name, **over)
+    sets = []
+    for r in range(max(1, rotate)):
+        inp = W.make_scan_inputs(s if r == 0 else W.spec(name, seed=s.seed + 1000 * r, **over))
+        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        d["out"] = torch.empty_like(d["u"])
+        d["last"] = torch.empty(s.batch, s.dim, s.dstate, device=dev)
+        sets.append(d)
+    return s, sets
+
+
+def scan_leg(torch, W, m, dev, hev, s, sets, steps, warmup, time_segments=0):
+    """One forward workload: W untimed calls, then exactly `steps` timed calls
+    (events on the caller's stream around them, synchronised on both sides),
+    then the same calls again with HIP events around the scan kernel (the
+    call's one launch after the B/C pack) for its own duration."""
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        d = sets[i % len(sets)]
+        m.selective_scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], D=d["D"],
+                             z=d["z"], delta_bias=d["delta_bias"],
+                             softplus=s.softplus, last_state=d["last"],
+                             out=d["out"], time_segments=time_segments)
+    settle_gpu(torch, dev)
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    pairs = [(hev.create(), hev.create()) for _ in range(steps)]
+    for i in range(steps):
+        m.set_scan_timing_events(*pairs[i])
+        step(i)
+    torch.cuda.synchronize()
+    m.set_scan_timing_events(None, None)
+    per = sorted(hev.elapsed_ms(a, b) for a, b in pairs)
+    for a, b in pairs:
+        hev.destroy(a)
+        hev.destroy(b)
+    io = torch.bfloat16 if s.io == "bf16" else torch.float32
+    plan = m.scan_plan(s.batch, s.dim, s.dstate, s.seqlen, io, time_segments)
+    nbytes = W.scan_bytes(s)
+    kernel_ms = sum(per) / len(per)
+    # the timed kernel is the call's one scan launch (every task of the call;
+    # only the B/C pack runs before it)
+    share = 1.0
+    slots = scan_slots(s)
+    alu = alu_figures(slots * share, kernel_ms, nbytes * share)
+    alu["slots_per_element"] = round(slots / s.elements, 2)
+    return {"ms": ms, "wall_s": wall, "kernel_ms": kernel_ms,
+            "kernel_ms_median": per[len(per) // 2], "kernel_ms_min": per[0],
+            "plan": plan, "bytes": nbytes, "share": share, "alu": alu,
+            "alu_call": alu_figures(slots, ms, nbytes)}
+
+
+def config_entry(s, W, r, ms_key="ms"):
+    """Extra-key summary of one forward workload."""
+    ms = r[ms_key]
+    gbs = r["bytes"] / (ms * 1e-3) / 1e9
+    return {"workload": "%s: batch %d, D_inner %d, N %d, L %d, %s" % (
+                s.name, s.batch, s.dim, s.dstate, s.seqlen, s.io),
+            "ms_per_call": round(ms, 5), "gb_per_s": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "gelem_per_s": round(s.state_elements / (ms * 1e-3) / 1e9, 2),
+            "alu_frac": r["alu_call"]["frac"],
+            "alu_ceiling_frac_of_hbm_peak": r["alu_call"]["ceiling_frac_of_hbm_peak"],
+            "main_kernel_ms": round(r["kernel_ms"], 5), "plan": r["plan"],
+            "algorithmic_bytes": r["bytes"]}
 
 
 def main():
@@ -183,70 +290,57 @@ def main():
     import workloads as W
     import selective_state_space_52_amd as m
 
-    if args.only_mamba2:
-        print(json.dumps({"mamba2": bench_mamba2(torch, W, m, torch.device("cuda:0"),
-                                                 args.mamba2_steps)}), flush=True)
-        return
-    over = {"dstate": args.dstate} if args.dstate else {}
-    s = W.spec(args.workload, **over)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    io = torch.bfloat16 if s.io == "bf16" else torch.float32
-    sets = []
-    base = W.make_scan_inputs(s)
-    for r in range(max(1, args.rotate)):
-        inp = base if r == 0 else W.make_scan_inputs(
-            W.spec(args.workload, seed=s.seed + 1000 * r, **over))
-        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
-        d["out"] = torch.empty_like(d["u"])
-        d["last"] = torch.empty(s.batch, s.dim, s.dstate, device=dev)
-        sets.append(d)
-
-    def step(i):
-        d = sets[i % len(sets)]
-        m.selective_scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], D=d["D"],
-                             z=d["z"], delta_bias=d["delta_bias"],
-                             softplus=s.softplus, last_state=d["last"],
-                             out=d["out"], time_segments=args.time_segments)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    # pass 1: the K timed steps as a caller runs them (no timing hook)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
-    # pass 2: the same steps with HIP events around the main scan kernel
     hev = HipEvents()
-    pairs = [(hev.create(), hev.create()) for _ in range(args.steps)]
-    for i in range(args.steps):
-        m.set_scan_timing_events(*pairs[i])     # main scan kernel of this step
-        step(i)
-    torch.cuda.synchronize()
-    m.set_scan_timing_events(None, None)
-    per_step = sorted(hev.elapsed_ms(a, b) for a, b in pairs)
-    main_ms = sum(per_step) / args.steps
-    for a, b in pairs:
-        hev.destroy(a)
-        hev.destroy(b)
+    if args.only_mamba2:
+        print(json.dumps({"mamba2": bench_mamba2(torch, W, m, dev, args.mamba2_steps)}),
+              flush=True)
+        return
+    if args.only_forward:
+        # profiling runs: the headline workload's forward calls alone
+        over = {"dstate": args.dstate} if args.dstate else {}
+        s, sets = make_sets(torch, W, dev, args.workload, args.rotate, **over)
+        r = scan_leg(torch, W, m, dev, hev, s, sets, args.steps, args.warmup,
+                     args.time_segments)
+        print(json.dumps(config_entry(s, W, r)), flush=True)
+        return
 
-    plan = m.scan_plan(s.batch, s.dim, s.dstate, s.seqlen, io, args.time_segments)
-    nbytes = W.scan_bytes(s)
+    over = {"dstate": args.dstate} if args.dstate else {}
+    s, sets = make_sets(torch, W, dev, args.workload, args.rotate, **over)
+    extra = {}
+    # The other legs run first: the headline is then timed on a GPU whose
+    # clocks have left their idle state (the first ~100 calls of a fresh
+    # process run ~10% slower).
+    if not args.no_decode:
+        extra["decode"] = bench_decode(torch, W, m, dev, args.decode_steps)
+    if not args.no_backward and s.dstate <= 32:   # the backward takes N <= 32
+        extra["backward"] = bench_backward(torch, W, m, dev, s, sets, hev,
+                                           args.backward_steps, args.bwd_time_segments)
+    if not args.no_conv:
+        extra["conv"] = bench_conv(torch, W, m, dev, s, sets, hev)
+    if not args.no_mamba2:
+        extra["mamba2"] = bench_mamba2(torch, W, m, dev, args.mamba2_steps)
+    if not args.no_configs:
+        extra["configs"] = bench_other_configs(torch, W, m, dev, hev, args)
+
+    r = scan_leg(torch, W, m, dev, hev, s, sets, args.steps, args.warmup, args.time_segments)
+    clock = shader_clock_mhz()
+    ms = r["ms"]
+    nbytes = r["bytes"]
     gbs = nbytes / (ms * 1e-3) / 1e9
-    gelem = s.state_elements / (ms * 1e-3) / 1e9
-    slots = s.state_elements * SLOTS_PER_STATE_ELEM + s.elements * SLOTS_PER_ELEM
-    achieved = slots / (main_ms * 1e-3) / 1e12
+    plan = r["plan"]
     traffic = load_traffic(args.workload, plan)
-
+    traffic_call = load_traffic(args.workload, plan, "hbm_bytes_per_call")
+    roof = hbm_roofline(nbytes * r["share"], r["kernel_ms"],
+                        "scan_kernel: the call's one scan launch (%d whole channel groups, "
+                        "%d groups cut into %d time segments with their aggregates)" % (
+                            plan["whole_groups"], plan["split_groups"], plan["segments"]),
+                        r["kernel_ms"], traffic)
+    roof["kernel_ms_median"] = round(r["kernel_ms_median"], 5)
+    roof["kernel_ms_min"] = round(r["kernel_ms_min"], 5)
+    roof["alu"] = r["alu"]
+    roof["binding_resource"] = "valu"
     res = {
         "metric": "selective-scan fwd HBM GB/s (% of peak) + Gelem/s (B*L*D_inner*N)",
         "value": round(gbs, 2),
@@ -267,34 +361,65 @@ def main():
                    "seq_len": s.seqlen, "algorithmic_bytes": nbytes,
                    "plan": plan},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "gelem_per_s": round(gelem, 2),
-        "roofline": {"bound": "alu", "achieved": round(achieved, 3),
-                     "peak": round(VALU_PEAK_TSLOTS, 3), "unit": "Tslot/s",
-                     "frac": round(achieved / VALU_PEAK_TSLOTS, 4),
-                     "traffic": traffic,
-                     "kernel": "scan_kernel (main pass)",
-                     "kernel_ms": round(main_ms, 5),
-                     "kernel_ms_median": round(per_step[len(per_step) // 2], 5),
-                     "kernel_ms_min": round(per_step[0], 5)},
-        "exp_rate": {"achieved": round(s.state_elements / (main_ms * 1e-3) / 1e12, 3),
-                     "peak": round(EXP_PEAK_T, 3), "unit": "T exp/s",
-                     "frac": round(s.state_elements / (main_ms * 1e-3) / 1e12 / EXP_PEAK_T, 4)},
-        "wall_s": round(wall, 3),
+        "gelem_per_s": round(s.state_elements / (ms * 1e-3) / 1e9, 2),
+        "roofline": roof,
+        "alu_call": r["alu_call"],
+        "call_minus_kernel_ms": round(ms - r["kernel_ms"], 5),
+        "exp_rate": {"achieved": round(s.state_elements * r["share"] /
+                                       (r["kernel_ms"] * 1e-3) / 1e12, 3),
+                     "peak": round(EXP_PEAK_T, 3), "unit": "T exp/s"},
+        "wall_s": round(r["wall_s"], 3),
         "software": software(torch),
+        "copy_ceiling": copy_ceiling(torch, dev),
+        "shader_clock_mhz": clock,
     }
-    if not args.no_backward and s.dstate <= 32:   # the backward takes N <= 32
-        res["backward"] = bench_backward(torch, W, m, dev, s, sets, hev,
-                                         args.backward_steps,
-                                         args.bwd_time_segments)
-    if not args.no_conv:
-        res["conv"] = bench_conv(torch, W, m, dev, s, sets, hev, ms)
-    if not args.no_decode:
-        res["decode"] = bench_decode(torch, W, m, dev, args.decode_steps)
-    if not args.no_mamba2:
-        res["mamba2"] = bench_mamba2(torch, W, m, dev, args.mamba2_steps)
+    res["roofline"]["traffic_per_call"] = traffic_call
+    res["roofline"]["frac_of_copy_ceiling"] = round(
+        roof["achieved"] / res["copy_ceiling"]["gb_per_s"], 4)
+    res.update(extra)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(s, base, args.cpu_seconds, nbytes)
+        res["cpu_baseline"] = cpu_baseline(W, s, sets, args.cpu_seconds, nbytes)
+        if not args.no_configs:
+            res["cpu_baseline"]["single_thread"] = cpu_single_thread(W)
     print(json.dumps(res), flush=True)
+
+
+def bench_other_configs(torch, W, m, dev, hev, args):
+    """The other forward workloads, each timed as the headline is: the tiny
+    fp32 case, the 130M-shaped layer and the long sequence in one call and as
+    64 chained calls of 2048 steps carrying last_state."""
+    out = {}
+    for name, rot, steps in (("tiny_f32", 1, 50), ("mamba130m_layer", 3, 50),
+                             ("long_chunked", 1, 5)):
+        s, sets = make_sets(torch, W, dev, name, rot)
+        r = scan_leg(torch, W, m, dev, hev, s, sets, steps, 3)
+        e = config_entry(s, W, r)
+        if name == "long_chunked":
+            d = sets[0]
+            stream = torch.cuda.current_stream(dev)
+            pieces = [(a, min(s.seqlen, a + s.chunk)) for a in range(0, s.seqlen, s.chunk)]
+            parts = [{k: (d[k][..., a:b].contiguous() if k in ("u", "delta", "z") else
+                          d[k][:, a:b].contiguous() if k in ("B", "C") else d[k])
+                      for k in ("u", "delta", "z", "B", "C")} for a, b in pieces]
+            outs = [torch.empty_like(p["u"]) for p in parts]
+            state = torch.zeros(s.batch, s.dim, s.dstate, device=dev)
+
+            def chained(_):
+                state.zero_()
+                for p, o in zip(parts, outs):
+                    m.selective_scan_fwd(p["u"], p["delta"], d["A"], p["B"], p["C"], D=d["D"],
+                                         z=p["z"], delta_bias=d["delta_bias"],
+                                         softplus=s.softplus, last_state=state,
+                                         load_state=True, out=o)
+            settle_gpu(torch, dev)
+            cms = _time(torch, stream, chained, 3, warmup=1)
+            e["chained_2048_step_calls_ms"] = round(cms, 5)
+            e["chained_hbm_frac"] = round(r["bytes"] / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+            del parts, outs
+        out[name] = e
+        del sets
+        torch.cuda.empty_cache()
+    return out
 
 
 def _time(torch, stream, fn, steps, warmup=3):
@@ -341,6 +466,7 @@ def bench_mamba2(torch, W, m, dev, steps=20):
         m.mamba2_scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
                           dt_bias=d["dt_bias"], softplus=s.softplus,
                           last_state=d["last"], out=d["out"])
+    settle_gpu(torch, dev)
     ms = _time(torch, stream, call, steps)
     d = sets[0]
     P = s.headdim
@@ -378,7 +504,7 @@ def bench_mamba2(torch, W, m, dev, steps=20):
             "speedup_vs_selective_scan": round(gen_ms / ms, 2)}
 
 
-def bench_conv(torch, W, m, dev, s, sets, hev, scan_ms, steps=20):
+def bench_conv(torch, W, m, dev, s, sets, hev, steps=20):
     """The causal conv (width 4, silu) ahead of the scan on the same workload:
     the standalone conv kernel (HBM-bound) and the conv fused into the scan's
     load stage, against running the two one after the other."""
@@ -408,8 +534,16 @@ def bench_conv(torch, W, m, dev, s, sets, hev, scan_ms, steps=20):
                              D=d["D"], z=d["z"], delta_bias=d["delta_bias"],
                              softplus=s.softplus, last_state=d["last"], out=d["out"])
 
+    def scan_alone(i):
+        d = sets[i % len(sets)]
+        m.selective_scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"],
+                             D=d["D"], z=d["z"], delta_bias=d["delta_bias"],
+                             softplus=s.softplus, last_state=d["last"], out=d["out"])
+
+    settle_gpu(torch, dev)
     conv_ms = _time(torch, stream, conv, steps)
     sep_ms = _time(torch, stream, separate, steps)
+    scan_ms = _time(torch, stream, scan_alone, steps)
     pairs = [(hev.create(), hev.create()) for _ in range(steps)]
     k = [0]
 
@@ -444,15 +578,22 @@ def bench_conv(torch, W, m, dev, s, sets, hev, scan_ms, steps=20):
             "separate_conv_then_scan_ms": round(sep_ms, 5),
             "fused_ms": round(fused_ms, 5),
             "fused_speedup_vs_separate": round(sep_ms / fused_ms, 3),
+            "scan_alone_ms": round(scan_ms, 5),
             "fused_extra_ms_vs_scan_alone": round(fused_ms - scan_ms, 5),
             "fused_algorithmic_bytes": fused_bytes,
             "fused_gb_per_s": round(fused_bytes / (fused_ms * 1e-3) / 1e9, 1),
-            "fused_roofline": {"bound": "alu", "achieved": round(achieved, 3),
-                               "peak": round(VALU_PEAK_TSLOTS, 3), "unit": "Tslot/s",
-                               "frac": round(achieved / VALU_PEAK_TSLOTS, 4),
+            "fused_roofline": {"bound": "hbm",
+                               "achieved": round(fused_bytes / (fused_ms * 1e-3) / 1e9, 1),
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": round(fused_bytes / (fused_ms * 1e-3) / 1e9 /
+                                             HBM_PEAK_GBS, 4),
                                "traffic": None,
                                "kernel": "scan_kernel with the conv (main pass)",
-                               "kernel_ms": round(main_ms, 5)}}
+                               "kernel_ms": round(main_ms, 5),
+                               "alu": {"achieved": round(achieved, 3),
+                                       "peak": round(VALU_PEAK_TSLOTS, 3),
+                                       "unit": "Tslot/s",
+                                       "frac": round(achieved / VALU_PEAK_TSLOTS, 4)}}}
 
 
 def bench_backward(torch, W, m, dev, s, sets, hev, steps, time_segments=0):
@@ -468,6 +609,7 @@ def bench_backward(torch, W, m, dev, s, sets, hev, steps, time_segments=0):
                                     grads[i % len(sets)], D=d["D"], z=d["z"],
                                     delta_bias=d["delta_bias"], softplus=s.softplus,
                                     time_segments=time_segments)
+    settle_gpu(torch, dev)
     for i in range(3):
         step(i)
     torch.cuda.synchronize()
@@ -496,12 +638,17 @@ def bench_backward(torch, W, m, dev, s, sets, hev, steps, time_segments=0):
             "algorithmic_bytes": nb,
             "effective_gb_per_s": round(nb / (ms * 1e-3) / 1e9, 1),
             "gelem_per_s": round(s.state_elements / (ms * 1e-3) / 1e9, 2),
-            "roofline": {"bound": "alu", "achieved": round(achieved, 3),
-                         "peak": round(VALU_PEAK_TSLOTS, 3), "unit": "Tslot/s",
-                         "frac": round(achieved / VALU_PEAK_TSLOTS, 4),
+            "roofline": {"bound": "hbm",
+                         "achieved": round(nb / (ms * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "traffic": None,
-                         "kernel": "bwd_pass_f + bwd_combine + bwd_pass_r",
-                         "kernel_ms": round(main_ms, 5)}}
+                         "kernel": "whole backward call",
+                         "passes_ms": round(main_ms, 5),
+                         "alu": {"achieved": round(achieved, 3),
+                                 "peak": round(VALU_PEAK_TSLOTS, 3), "unit": "Tslot/s",
+                                 "frac": round(achieved / VALU_PEAK_TSLOTS, 4),
+                                 "kernels": "bwd_pass_f + bwd_combine + bwd_pass_r"}}}
 
 
 def software(torch):
@@ -529,6 +676,7 @@ def bench_decode(torch, W, m, dev, steps):
             t = toks[i % len(toks)]
             m.selective_state_update(state, t["x"], t["dt"], A, t["B"], t["C"], D=D,
                                      z=t["z"], dt_bias=bias, out=out)
+    settle_gpu(torch, dev)
     run(20)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -554,6 +702,23 @@ def bench_decode(torch, W, m, dev, steps):
     e1.record()
     torch.cuda.synchronize()
     ms_rot = e0.elapsed_time(e1) / steps
+    # The same rotating loop as one captured HIP graph of 64 steps, replayed:
+    # the host enqueues one graph launch per 64 steps instead of 64 calls.
+    G = 64
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_rot(G)
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // G)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_graph = e0.elapsed_time(e1) / (reps * G)
+    del graph
     return {"workload": "decode: %d sequences x D_inner %d, N %d, %d steps, bf16 tokens, "
                         "fp32 state in place" % (s.batch, s.dim, s.dstate, steps),
             "ms_per_step": round(ms, 5), "algorithmic_bytes_per_step": nb,
@@ -562,16 +727,22 @@ def bench_decode(torch, W, m, dev, steps):
             "rotating_4_states": {"ms_per_step": round(ms_rot, 5),
                                   "hbm_gb_per_s": round(nb / (ms_rot * 1e-3) / 1e9, 1),
                                   "pct_hbm_peak": round(100 * nb / (ms_rot * 1e-3) / 1e9 /
-                                                        HBM_PEAK_GBS, 2)}}
+                                                        HBM_PEAK_GBS, 2)},
+            "rotating_4_states_graph": {
+                "ms_per_step": round(ms_graph, 5), "steps_per_graph": G,
+                "hbm_gb_per_s": round(nb / (ms_graph * 1e-3) / 1e9, 1),
+                "pct_hbm_peak": round(100 * nb / (ms_graph * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}}
 
 
-def cpu_baseline(s, inp, seconds, nbytes):
+def cpu_baseline(W, s, sets, seconds, nbytes):
     """The fp64 oracle on the host cores over the whole workload (all rows,
-    all timesteps), repeated until about `seconds` of wall time, reported in
-    the GPU value's unit."""
+    all timesteps, the first input set), repeated until about `seconds` of
+    wall time, reported in the GPU value's unit."""
     import oracle
     nth = oracle.default_threads()
-    conv = {k: oracle._f64(v) for k, v in inp.items() if k != "softplus"}
+    d = sets[0]
+    conv = {k: oracle._f64(d[k].cpu()) for k in ("u", "delta", "A", "B", "C", "D", "z",
+                                                  "delta_bias")}
     reps, total = 0, 0.0
     while total < seconds:
         t0 = time.perf_counter()
@@ -584,7 +755,75 @@ def cpu_baseline(s, inp, seconds, nbytes):
     return {"value": round(nbytes / per / 1e9, 3), "unit": "GB/s", "cores": nth,
             "kind": "oracle", "gelem_per_s": round(s.state_elements / per / 1e9, 3),
             "sample": "whole workload (%d rows x %d timesteps x N %d), %d run(s), "
-                      "%.2f s each, fp64" % (s.batch * s.dim, s.seqlen, s.dstate, reps, per)}
+                      "%.2f s each, fp64, %d threads" % (s.batch * s.dim, s.seqlen, s.dstate,
+                                                         reps, per, nth)}
+
+
+def cpu_single_thread(W):
+    """The oracle on one host thread, one run over each of the tiny, 130M- and
+    2.8B-shaped workloads."""
+    import oracle
+    out = {}
+    for name in ("tiny_f32", "mamba130m_layer", "mamba2p8b_layer"):
+        s = W.spec(name)
+        inp = W.make_scan_inputs(s)
+        c = {k: oracle._f64(inp[k]) for k in ("u", "delta", "A", "B", "C", "D", "z",
+                                               "delta_bias")}
+        t0 = time.perf_counter()
+        oracle.scan(c["u"], c["delta"], c["A"], c["B"], c["C"], D=c["D"], z=c["z"],
+                    delta_bias=c["delta_bias"], softplus=s.softplus, nthreads=1)
+        dt = time.perf_counter() - t0
+        out[name] = {"s": round(dt, 3), "gb_per_s": round(W.scan_bytes(s) / dt / 1e9, 4),
+                     "gelem_per_s": round(s.state_elements / dt / 1e9, 4)}
+    return out
+
+
+_COPY = {}
+
+
+def settle_gpu(torch, dev, seconds=0.6):
+    """Keep the GPU busy with device copies of 1 GiB for about `seconds`, and
+    time the last of them: the HBM rate a plain streaming kernel reaches here
+    (1 GiB read + 1 GiB written per copy).  A GPU that has idled (the host
+    drawing inputs) runs the scan ~10% slower for its first few hundred
+    milliseconds of work, so every timed leg starts right after this."""
+    n = 1 << 30
+    if "a" not in _COPY:
+        _COPY["a"] = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        _COPY["b"] = torch.empty_like(_COPY["a"])
+    a, b = _COPY["a"], _COPY["b"]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            b.copy_(a)
+        torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ms = _time(torch, stream, lambda i: b.copy_(a), 20, warmup=0)
+    _COPY["last"] = {"gb_per_s": round(2 * n / (ms * 1e-3) / 1e9, 1), "ms": round(ms, 4),
+                     "kernel": "torch copy_ of 1 GiB"}
+    return _COPY["last"]
+
+
+def copy_ceiling(torch, dev):
+    """The copy rate measured by the last settle_gpu (the plain streaming
+    kernel's HBM rate on this GPU)."""
+    return _COPY.get("last") or settle_gpu(torch, dev)
+
+
+def shader_clock_mhz():
+    """The shader clock level the driver reports as current (sysfs
+    pp_dpm_sclk), read right after the headline timing, or None."""
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if "*" in line:
+                        tok = line.split(":", 1)[1].strip().split()[0].lower()
+                        return int(float(tok.replace("mhz", "")))
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
 
 
 def copy_calibration(torch):
@@ -621,9 +860,8 @@ def _counter_mean(d, kernel_substr, counter):
     return total / n
 
 
-# the kernels of one forward call (one B/C pack per call)
-FWD_KERNELS = ("mssm::fwd::bc_pack_kernel", "mssm::fwd::scan_kernel<",
-               "mssm::fwd::combine_kernel")
+# the kernels of one forward call (one B/C pack per call, then one scan launch)
+FWD_KERNELS = ("mssm::fwd::bc_pack_kernel", "mssm::fwd::scan_kernel<")
 
 
 def _library_kernels(d, counter):
@@ -638,11 +876,29 @@ def _library_kernels(d, counter):
     return names
 
 
+def _dispatches(d, counter):
+    """(dispatch_id, kernel name, stream_id, workgroups, counter value summed
+    over its instances) of every dispatch in a counter run, in dispatch order."""
+    import sqlite3
+    rows = []
+    for db in glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True):
+        c = sqlite3.connect(db)
+        rows += c.execute(
+            "select p.dispatch_id, p.name, k.stream_id, k.grid_x / k.workgroup_x, "
+            "sum(p.counter_value) from pmc_events p join kernels k on "
+            "k.dispatch_id = p.dispatch_id where p.counter_name = ? "
+            "group by p.dispatch_id order by p.dispatch_id", (counter,)).fetchall()
+    if not rows:
+        raise RuntimeError("no %s samples in %s" % (counter, d))
+    return rows
+
+
 def traffic_record(workload, time_segments, fetch_dir, write_dir, cfetch_dir, cwrite_dir):
-    """HBM bytes per forward call (all its kernels: the B/C pack, the scan
-    launches on both streams and the segment combine) from FETCH_SIZE and
-    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
-    for torch's copy of a 1 GiB buffer (1 GiB fetched, 1 GiB written)."""
+    """HBM bytes of the forward from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for torch's copy of
+    a 1 GiB buffer (1 GiB fetched, 1 GiB written): per launch of the scan
+    kernel (one per call, every task of the call), and per call (the B/C pack
+    and the scan launch)."""
     import workloads as W
     copy_kib = float(1 << 20)
     f_factor = copy_kib / _counter_mean(cfetch_dir, "copyBuffer", "FETCH_SIZE")
@@ -659,19 +915,34 @@ def traffic_record(workload, time_segments, fetch_dir, write_dir, cfetch_dir, cw
         if foreign:
             raise RuntimeError("%s holds other kernels of the library (%s): profile the "
                                "forward of %s alone" % (d, foreign[0][:80], workload))
-    _, calls = _counter_sum(fetch_dir, FWD_KERNELS[0], "FETCH_SIZE")
-    fk = sum(_counter_sum(fetch_dir, k, "FETCH_SIZE")[0] for k in FWD_KERNELS) / calls
-    wk = sum(_counter_sum(write_dir, k, "WRITE_SIZE")[0] for k in FWD_KERNELS) / calls
     import selective_state_space_52_amd as m
     plan = m.scan_plan(s.batch, s.dim, s.dstate, s.seqlen, time_segments=time_segments)
+    per = {}
+    for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        rows = _dispatches(d, counter)
+        lib = [r for r in rows if "mssm::" in r[1]]
+        packs = [r for r in lib if FWD_KERNELS[0] in r[1]]
+        mains = [r for r in lib if FWD_KERNELS[1] in r[1]]
+        per[counter] = {"calls": len(packs),
+                        "call_kib": sum(r[4] for r in lib) / len(packs),
+                        "main_kib": sum(r[4] for r in mains) / max(1, len(mains)),
+                        "main_launches": len(mains)}
+    fk, wk = per["FETCH_SIZE"], per["WRITE_SIZE"]
     rec = {workload: {
         "kernel_source_sha256_16": kernel_source_hash(),
         "segments": plan["segments"],
-        "calls": calls,
-        "fetch_kib_per_call": round(fk, 1), "write_kib_per_call": round(wk, 1),
+        "calls": fk["calls"], "main_pass_launches": fk["main_launches"],
+        "fetch_kib_per_call": round(fk["call_kib"], 1),
+        "write_kib_per_call": round(wk["call_kib"], 1),
+        "main_pass_fetch_kib_per_launch": round(fk["main_kib"], 1),
+        "main_pass_write_kib_per_launch": round(wk["main_kib"], 1),
         "copy_fetch_factor": round(f_factor, 5), "copy_write_factor": round(w_factor, 5),
-        "hbm_bytes_per_call": int(round((fk * f_factor + wk * w_factor) * 1024)),
-        "algorithmic_bytes": W.scan_bytes(s)}}
+        "hbm_bytes_per_call": int(round((fk["call_kib"] * f_factor +
+                                         wk["call_kib"] * w_factor) * 1024)),
+        "main_pass_hbm_bytes_per_launch": int(round((fk["main_kib"] * f_factor +
+                                                     wk["main_kib"] * w_factor) * 1024)),
+        "algorithmic_bytes": W.scan_bytes(s),
+        "main_pass_algorithmic_bytes": W.scan_bytes(s)}}
     print(json.dumps(rec, indent=1))
 
 

@@ -50,12 +50,8 @@
  *   - the plain call takes it stream-ordered from HIP's default memory pool
  *     (hipMallocAsync / hipFreeAsync on `stream`) for the duration of the
  *     call.
- * When a forward call splits some rows in time while others run whole, it
- * runs the split rows' chain on a second, library-owned stream of the same
- * device (created at the first such call, default priority, kept until the
- * process ends), forked from `stream` by an event and joined back into it by
- * another before the call returns, so that the call is still ordered on
- * `stream` as one unit.
+ * Every launch of a call is on `stream`; the library creates no stream and
+ * records no event of its own.
  *
  * Errors.  Every argument is validated before the first HIP call; a call that
  * fails validation returns a negative code and writes nothing.  A failing HIP
@@ -345,7 +341,7 @@ typedef struct {
   int64_t segment_len;      /* timesteps per segment (last may be shorter)   */
   int32_t waves_per_group;  /* waves per workgroup (each owns dstate/waves   */
                             /* of the state)                                 */
-  int32_t kernels;          /* launches per call (2, or 4 when splitting)    */
+  int32_t kernels;          /* launches per call: the B/C pack and the scan  */
   int64_t workspace_bytes;  /* workspace a call needs (mssm_workspace_size)  */
   int32_t vector_path;      /* 1 when the 16-byte vector-load path applies   */
                             /* (needs aligned pointers too)                  */
@@ -357,8 +353,10 @@ int mssm_selective_scan_fwd_plan(const mssm_dims* dims, mssm_plan* plan);
 /*
  * Timing hook for benchmarks.  With both handles non-NULL (hipEvent_t, owned
  * by the caller), every later forward scan issued from this thread records
- * `start` on its stream right before the main scan kernel and `stop` right
- * after it, so hipEventElapsedTime(start, stop) is that kernel's duration.
+ * `start` on its stream right before its scan kernel (the one launch after
+ * the B/C pack) and `stop` right after it, so hipEventElapsedTime(start,
+ * stop) is that kernel's duration.  The Mamba-2 scan records them around its
+ * launches.
  * The backward call records them around its three main kernels (pass F,
  * the segment combine and pass R).
  * Both NULL turns the hook off; one NULL is MSSM_ERR_NULL.  Per thread.

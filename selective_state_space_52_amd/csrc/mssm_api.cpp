@@ -40,36 +40,6 @@ void refresh_cu_count() {
     g_cu_count = cus;
 }
 
-// Per device: a side stream (default priority) and fork/join events, made on
-// first use and kept until the process ends, plus a lock that keeps one
-// call's fork, side-stream work and join together.
-struct SideStream {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool ready = false;
-};
-constexpr int kMaxDevices = 64;
-SideStream g_side[kMaxDevices];
-std::mutex g_side_lock[kMaxDevices];
-std::mutex g_init_lock;
-
-// The device's side stream, or nullptr if it cannot be made (the call then
-// runs on the caller's stream alone).
-SideStream* side_stream_of(int dev) {
-  if (dev < 0 || dev >= kMaxDevices) return nullptr;
-  std::lock_guard<std::mutex> g(g_init_lock);
-  SideStream& ss = g_side[dev];
-  if (!ss.ready) {
-    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess)
-      return nullptr;
-    if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
-      return nullptr;
-    ss.ready = true;
-  }
-  return &ss;
-}
-
 bool valid_dstate(int64_t n) {
   return n == 1 || n == 2 || n == 4 || n == 8 || n == 16 || n == 32 || n == 64 ||
          n == 128;
@@ -133,6 +103,30 @@ int check_scan_groups(const mssm_dims* dims) {
   return MSSM_OK;
 }
 
+// Layout of the forward's workspace: the packed B/C runs, then for the split
+// groups' rows the segment end states, the segment sums of Delta, the kept
+// initial states and one flag per aggregate.  Sets *bytes, and with p
+// non-null points p's workspace fields into ws.
+void fwd_workspace(int64_t bc_batches, int64_t L, int N, bool bf16, int64_t split,
+                   int64_t segments, void* ws, int64_t* bytes, mssm::ScanParams* p) {
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  int64_t off = up(mssm::scan_bc_workspace_bytes(bc_batches, L, N, bf16));
+  char* base = static_cast<char*>(ws);
+  if (p) p->ws_bc = ws;
+  if (split > 0) {
+    const int64_t rows = split * kLanes;
+    if (p) p->ws_S = reinterpret_cast<float*>(base + off);
+    off += up(rows * (segments - 1) * N * 4);
+    if (p) p->ws_sum = reinterpret_cast<double*>(base + off);
+    off += up(rows * (segments - 1) * 8);
+    if (p) p->ws_h0 = reinterpret_cast<float*>(base + off);
+    off += up(rows * N * 4);
+    if (p) p->ws_flags = reinterpret_cast<uint32_t*>(base + off);
+    off += up(split * (segments - 1) * 4);
+  }
+  *bytes = off;
+}
+
 // The work plan of the forward scan (pure arithmetic, no HIP call).
 //
 // A 64-channel group scanned in one piece is one workgroup.  When the groups
@@ -181,14 +175,9 @@ int make_plan(const mssm_dims* dims, int cus, mssm_plan* plan) {
   const int64_t split = G - whole;
   if (whole + split * segments > INT32_MAX) return MSSM_ERR_DIMS;
 
-  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
-  int64_t ws = up(mssm::scan_bc_workspace_bytes(dims->batch * groups_of(dims), L,
-                                                (int)N, dims->io_dtype == MSSM_BF16));
-  if (split > 0) {
-    const int64_t rows = split * kLanes;
-    ws += up(rows * (segments - 1) * N * 4) + up(rows * (segments - 1) * 8) +
-          up(rows * segments * N * 4);
-  }
+  int64_t ws = 0;
+  fwd_workspace(dims->batch * groups_of(dims), L, (int)N, dims->io_dtype == MSSM_BF16,
+                split, segments, nullptr, &ws, nullptr);
   std::memset(plan, 0, sizeof(*plan));
   plan->groups = (int32_t)G;
   plan->whole_groups = (int32_t)whole;
@@ -196,7 +185,7 @@ int make_plan(const mssm_dims* dims, int cus, mssm_plan* plan) {
   plan->segments = (int32_t)segments;
   plan->segment_len = seg_len;
   plan->waves_per_group = waves;
-  plan->kernels = split > 0 ? 4 : 2;
+  plan->kernels = 2;
   plan->workspace_bytes = ws;
   const int64_t io = dims->io_dtype == MSSM_BF16 ? 2 : 4;
   plan->vector_path =
@@ -253,8 +242,7 @@ namespace mssm {
 // The forward scan, optionally fed by the causal conv (conv_w non-null: `u`
 // is the conv input x).  Workspace: `ws` (ws_bytes long) from the caller, or
 // with ws == nullptr and WsMode::kAllocate taken stream-ordered from HIP's
-// pool for this call.  WsMode::kOneStream runs every launch on the caller's
-// stream (no side stream, no events).
+// pool for this call.
 int scan_fwd_entry(const void* u, const void* delta, const float* A,
                    const void* B, const void* C, const float* D, const void* z,
                    const float* delta_bias, int softplus, void* out,
@@ -337,24 +325,11 @@ int scan_fwd_entry(const void* u, const void* delta, const float* A,
   p.u_out = u_out;
   p.layout_bld = bld ? 1 : 0;
 
-  if (mode != WsMode::kAllocate) {
+  if (mode == WsMode::kCaller) {
     rc = check_workspace(ws_in, ws_bytes, plan.workspace_bytes);
     if (rc != MSSM_OK) return rc;
   }
   hipStream_t st = (hipStream_t)stream;
-  int dev = -1;
-  SideStream* side = nullptr;
-  std::unique_lock<std::mutex> side_guard;
-  if (mode != WsMode::kOneStream && plan.split_groups > 0 && plan.whole_groups > 0 &&
-      hipGetDevice(&dev) == hipSuccess) {
-    side = side_stream_of(dev);
-    if (side) {
-      side_guard = std::unique_lock<std::mutex>(g_side_lock[dev]);
-      p.side_stream = side->stream;
-      p.ev_fork = side->fork;
-      p.ev_join = side->join;
-    }
-  }
   void* ws = ws_in;
   if (mode == WsMode::kAllocate) {
     hipError_t e = hipMallocAsync(&ws, (size_t)plan.workspace_bytes, st);
@@ -363,16 +338,10 @@ int scan_fwd_entry(const void* u, const void* delta, const float* A,
       return MSSM_ERR_HIP;
     }
   }
-  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
-  p.ws_bc = ws;
-  if (plan.split_groups > 0) {
-    const int64_t rows = (int64_t)plan.split_groups * kLanes;
-    char* base = (char*)ws + up(mssm::scan_bc_workspace_bytes(batch * G, L, (int)N, io == 2));
-    p.ws_S = (float*)base;
-    base += up(rows * (plan.segments - 1) * N * 4);
-    p.ws_sum = (double*)base;
-    base += up(rows * (plan.segments - 1) * 8);
-    p.ws_hin = (float*)base;
+  {
+    int64_t nb = 0;
+    fwd_workspace(batch * G, L, (int)N, io == 2, plan.split_groups, plan.segments, ws, &nb,
+                  &p);
   }
   hipError_t e = mssm::launch_scan(p, (int)N, io == 2, vec, st);
   if (e != hipSuccess) set_hip_error("scan launch", e);

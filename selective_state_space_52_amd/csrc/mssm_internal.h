@@ -15,10 +15,12 @@ namespace mssm {
 // [64*(gi % groups_per_batch), +64) of batch gi / groups_per_batch, one lane
 // per channel.  Groups [0, whole_groups) are scanned in one piece; the other
 // groups are cut into `segments` time segments of `seg_len` steps.  For those,
-// an aggregate pass summarises every segment but the last (local end state
-// from a zero start, and the sum of Delta), a combine pass turns the summaries
-// into each segment's initial state, and the main pass then scans every
-// segment from its initial state.
+// aggregate tasks summarise every segment but the last (its end state and its
+// sum of Delta; segment 0 from the initial state, the others from zero), and
+// each segment's main task folds the summaries of the segments before it into
+// its initial state.  Aggregate and main tasks run in one launch; an
+// aggregate task publishes its summary through a flag that the main tasks
+// after it wait for.
 struct ScanParams {
   const void* u;
   const void* delta;
@@ -39,18 +41,15 @@ struct ScanParams {
   int32_t segments;
   int64_t seg_len;
   // workspace of the split groups, indexed by split row sr = 64*sj + lane
-  float* ws_S;            // [sr][segments-1][N]
-  double* ws_sum;         // [sr][segments-1]
-  float* ws_hin;          // [sr][segments][N]
+  float* ws_S;            // [sr][segments-1][N] segment end states
+  double* ws_sum;         // [sr][segments-1] segment sums of Delta
+  float* ws_h0;           // [sr][N] initial state (with load_state)
+  uint32_t* ws_flags;     // [segment][split group] summary published; zeroed
+                          // by the B/C pack ahead of every scan launch
   void* ws_bc;            // B, C packed per wave run, io dtype
                           // [b][wave][t][B, C of the wave's N / waves states]
-  void* ev_start;         // optional hipEvent_t recorded around the main
-  void* ev_stop;          // scan kernel (timing hook), or null
-  // side stream and fork/join events for running the split groups beside
-  // the whole groups (null: everything on the caller's stream)
-  void* side_stream;
-  void* ev_fork;
-  void* ev_join;
+  void* ev_start;         // optional hipEvent_t recorded around the scan
+  void* ev_stop;          // kernel (timing hook), or null
   // causal conv feeding the scan (conv_w null: `u` is the scan input itself;
   // otherwise `u` holds the conv input x)
   const float* conv_w;    // (dim, 4) fp32
@@ -149,10 +148,8 @@ struct BwdParams {
 };
 
 // Where a forward call's workspace comes from: allocated stream-ordered for
-// the call (kAllocate), supplied by the caller (kCaller), or supplied by the
-// caller with every launch kept on the caller's stream (kOneStream: no side
-// stream, no events; used where the library may create nothing).
-enum class WsMode { kAllocate, kCaller, kOneStream };
+// the call (kAllocate) or supplied by the caller (kCaller).
+enum class WsMode { kAllocate, kCaller };
 
 // The forward scan entry shared by the C ABI's forward calls (mssm_api.cpp);
 // returns an MSSM_* status.  conv_w non-null: `u` is the conv input x.
@@ -168,11 +165,13 @@ int scan_waves_per_group(int N);
 // Repack B and C, (batch, L, groups, N), into per-wave runs, one per
 // (batch entry, group, wave) for `waves` waves per channel group: `steps`
 // (>= L) timesteps per run, zeros from L on, `run_words` 32-bit words per
-// run; the runs hold bf16 pairs (dst_bf16) or fp32 values.
+// run; the runs hold bf16 pairs (dst_bf16) or fp32 values.  The same launch
+// zeroes `nflags` words at `flags` (may be 0 / null).
 hipError_t launch_bc_pack(const void* B, const void* C, void* packed,
                           int64_t batch, int64_t groups, int64_t L, int64_t steps,
                           int N, int waves, bool src_bf16, bool dst_bf16,
-                          int64_t run_words, hipStream_t stream);
+                          int64_t run_words, uint32_t* flags, int64_t nflags,
+                          hipStream_t stream);
 // Bytes of the packed B/C runs of one forward call.
 int64_t scan_bc_workspace_bytes(int64_t batch, int64_t L, int N, bool bf16);
 

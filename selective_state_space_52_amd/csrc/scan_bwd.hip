@@ -734,7 +734,7 @@ hipError_t launch_n(const BwdParams& p, hipStream_t st) {
   s.softplus = p.softplus;
   s.batch = (int32_t)p.batch;
   hipError_t e = launch_bc_pack(p.B, p.C, p.ws_bc, p.batch, s.ngroups, p.L, Lp, N,
-                                NG, BF16, BF16, Lp * WPS, st);
+                                NG, BF16, BF16, Lp * WPS, nullptr, 0, st);
   if (e != hipSuccess) return e;
   e = p.z ? launch_passes<N, BF16, VEC, true>(p, s, st)
           : launch_passes<N, BF16, VEC, false>(p, s, st);

@@ -1,6 +1,6 @@
 // scan_fwd.hip -- the forward scan's non-template parts: the B/C pack, the
-// combine of segment summaries, the work split helpers and the dispatch over
-// state sizes (whose kernels are instantiated in scan_fwd_n*.hip).
+// work split helpers and the dispatch over state sizes (whose kernels are
+// instantiated in scan_fwd_n*.hip).
 #include "scan_fwd_impl.h"
 
 namespace mssm {
@@ -9,13 +9,17 @@ namespace fwd {
 // Writes the packed runs of `steps` timesteps per wave (steps >= L; the
 // timesteps from L on are written as zeros) with `run_words` words per run.
 // The source is bf16 or fp32 (src_bf16); the runs keep bf16 (dst_bf16) or
-// hold fp32.
+// hold fp32.  Threads i < nflags also zero flags[i]: the scan launch that
+// follows on the same stream finds its summary flags cleared, with no
+// separate fill.
 __global__ void __launch_bounds__(256)
     bc_pack_kernel(const void* __restrict__ Bm, const void* __restrict__ Cm,
                    void* __restrict__ packed, int64_t batch, int64_t groups,
                    int64_t L, int64_t steps, int N, int NG, int src_bf16,
-                   int dst_bf16, int64_t run_words) {
+                   int dst_bf16, int64_t run_words, uint32_t* __restrict__ flags,
+                   int64_t nflags) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nflags) flags[i] = 0u;
   const int64_t total = batch * groups * steps * 2 * N;
   if (i >= total) return;
   const int npw = N / NG;
@@ -46,57 +50,18 @@ __global__ void __launch_bounds__(256)
 }
 
 
-// Initial state of every segment of the split groups, from the segment
-// summaries: h_in[0] = h0, h_in[s+1] = exp(A * sum_s Delta) h_in[s] + S_s.
-__global__ void __launch_bounds__(256)
-    combine_kernel(const float* __restrict__ A, const float* __restrict__ h0,
-                   const float* __restrict__ ws_S,
-                   const double* __restrict__ ws_sum,
-                   float* __restrict__ ws_hin, const ScanShape s, int N,
-                   int64_t split_rows) {
-  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (tid >= split_rows * N) return;
-  const int64_t sr = tid / N;
-  const int n = (int)(tid - sr * N);
-  const int P = s.segments;
-  const int64_t gi = s.whole_groups + sr / kLanes;
-  const int64_t b = gi / s.groups_per_batch;
-  const int64_t d = (gi % s.groups_per_batch) * kLanes + (sr % kLanes);
-  if (d >= s.dim) {
-    for (int q = 0; q < P; ++q) ws_hin[(sr * P + q) * N + n] = 0.0f;
-    return;
-  }
-  const double a = A[d * N + n];
-  double h = (s.load_state && h0) ? h0[(b * s.dim + d) * N + n] : 0.0;
-  for (int q = 0; q < P; ++q) {
-    ws_hin[(sr * P + q) * N + n] = (float)h;
-    if (q < P - 1)
-      h = exp(a * ws_sum[sr * (P - 1) + q]) * h +
-          (double)ws_S[(sr * (P - 1) + q) * N + n];
-  }
-}
-
-hipError_t launch_combine(const ScanParams& p, const ScanShape& s, int N,
-                          hipStream_t stream) {
-  const int64_t split_rows = (int64_t)p.split_groups * kLanes;
-  const int64_t threads = split_rows * N;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((threads + 255) / 256)),
-                     dim3(256), 0, stream, p.A, p.last_state, p.ws_S, p.ws_sum,
-                     p.ws_hin, s, N, split_rows);
-  return hipGetLastError();
-}
-
-
 }  // namespace fwd
 
 hipError_t launch_bc_pack(const void* B, const void* C, void* packed,
                           int64_t batch, int64_t groups, int64_t L, int64_t steps,
                           int N, int waves, bool src_bf16, bool dst_bf16,
-                          int64_t run_words, hipStream_t stream) {
-  const int64_t total = batch * groups * steps * 2 * N;
+                          int64_t run_words, uint32_t* flags, int64_t nflags,
+                          hipStream_t stream) {
+  const int64_t total = std::max<int64_t>(batch * groups * steps * 2 * N, nflags);
   hipLaunchKernelGGL(fwd::bc_pack_kernel, dim3((unsigned)((total + 255) / 256)),
                      dim3(256), 0, stream, B, C, packed, batch, groups, L, steps,
-                     N, waves, src_bf16 ? 1 : 0, dst_bf16 ? 1 : 0, run_words);
+                     N, waves, src_bf16 ? 1 : 0, dst_bf16 ? 1 : 0, run_words, flags,
+                     flags ? nflags : (int64_t)0);
   return hipGetLastError();
 }
 

@@ -25,9 +25,10 @@
 //     with 64-byte scalar loads;
 //   * each lane reads its row's u / delta / z in 8- or 16-byte pieces, one
 //     tile ahead of use, and writes its outputs with the same width.
-// Long rows can be cut into time segments (aggregate -> combine -> main):
-// the recurrence is associative on (decay, offset) pairs, so a segment's
-// effect on the state is (exp(A * sum Delta), local end state from zero).
+// Long rows can be cut into time segments (aggregate tasks, then main tasks
+// that fold the aggregates, in one launch): the recurrence is associative on
+// (decay, offset) pairs, so a segment's effect on the state is
+// (exp(A * sum Delta), local end state from zero).
 #pragma once
 
 #include <algorithm>
@@ -64,19 +65,30 @@ struct ScanShape {
                // for the (batch, length, channel) layout
   int32_t ngroups, groups_per_bc;  // B/C groups; channel groups per B/C group
   int32_t softplus, load_state;
-  int32_t groups_per_batch, whole_groups, segments;
+  int32_t groups_per_batch, whole_groups, split_groups, segments;
   int64_t seg_len;
 };
 
+// A main task waits for the aggregate tasks before it by polling their flags;
+// each poll sleeps about 64 clocks.  The aggregates of its own launch are
+// ahead of it in dispatch order and wait for nothing, so the wait ends; the
+// limit (2^20 polls, well under a second) only bounds it should that ever
+// fail, and the task then goes on with whatever the summaries hold.
+constexpr uint32_t kFlagSpinLimit = 1u << 20;
+// s_waitcnt operand waiting for every outstanding vector memory operation of
+// the wave (vmcnt 0; the export and LDS/scalar counters left at their maxima)
+constexpr int kWaitVmem0 = 0x0F70;
 
-// Initial states of the split groups' segments (scan_fwd.hip).
-hipError_t launch_combine(const ScanParams& p, const ScanShape& s, int N,
-                          hipStream_t stream);
-
-// Main pass (AGG = false): scans each task's time range from its initial
-// state and writes out (and last_state after the final segment).
-// Aggregate pass (AGG = true): scans segments 0..P-2 of the split groups from
-// a zero state and writes the end state and the sum of Delta.
+// Main task (AGG = false): scans the task's time range from its initial
+// state and writes out (and last_state after the final segment).  A task of
+// segment k > 0 of a split group waits for the aggregates of segments
+// 0..k-1 and folds them into its initial state, h = S_0 and then
+// h = exp(A * sum_j Delta) h + S_j for j = 1..k-1, in fp64.
+// Aggregate task (AGG = true): scans segment k < P-1 of a split group -- from
+// the initial state for k = 0, from zero otherwise -- writes its end state
+// S_k and its sum of Delta, then publishes them through the segment's flag
+// (each wave's stores are made visible device-wide by a release fence before
+// the workgroup barrier, and the flag is stored with release semantics).
 //
 // A tile of kTile timesteps is done in three phases:
 //   prep   : each wave turns KC = kTile / NG of the tile's timesteps into
@@ -99,7 +111,8 @@ __device__ __forceinline__ void scan_body(
     const float* __restrict__ Dv, const float* __restrict__ bias,
     void* __restrict__ out, float* __restrict__ last_state,
     float* __restrict__ ws_S, double* __restrict__ ws_sum,
-    const float* __restrict__ ws_hin, const uint32_t* __restrict__ bcp,
+    float* __restrict__ ws_h0, uint32_t* __restrict__ ws_flags,
+    const uint32_t* __restrict__ bcp,
     const ScanShape& s, float2 (&s_dw)[kTile][kLanes],
     float (&s_y)[NG][kTile][kLanes], const int task, const ConvArgs& cv) {
   constexpr int NPW = N / NG;
@@ -113,12 +126,14 @@ __device__ __forceinline__ void scan_body(
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = g * NPW;
 
-  // task -> (group, segment)
-  int gi, seg, nseg;
+  // task -> (group, segment); the split groups' tasks are segment-major, so
+  // that the earliest segments' aggregates, and the main tasks that need the
+  // fewest of them, come first in dispatch order
+  int gi, seg, nseg, sg = 0;
   if constexpr (AGG) {
-    const int per = s.segments - 1;
-    gi = s.whole_groups + task / per;
-    seg = task % per;
+    seg = task / s.split_groups;
+    sg = task % s.split_groups;
+    gi = s.whole_groups + sg;
     nseg = s.segments;
   } else if (task < s.whole_groups) {
     gi = task;
@@ -126,8 +141,9 @@ __device__ __forceinline__ void scan_body(
     nseg = 1;
   } else {
     const int j = task - s.whole_groups;
-    gi = s.whole_groups + j / s.segments;
-    seg = j % s.segments;
+    seg = j / s.split_groups;
+    sg = j % s.split_groups;
+    gi = s.whole_groups + sg;
     nseg = s.segments;
   }
   const int64_t b = gi / s.groups_per_batch;
@@ -160,14 +176,56 @@ __device__ __forceinline__ void scan_body(
 #pragma unroll
   for (int j = 0; j < NPW; ++j) {
     A2[j] = A[dc * N + n0 + j] * kLog2e;
-    if (AGG)
-      h[j] = 0.0f;
-    else if (nseg > 1)
-      h[j] = ws_hin[(sr * nseg + seg) * N + n0 + j];
-    else if (s.load_state)
-      h[j] = last_state[row * N + n0 + j];
-    else
-      h[j] = 0.0f;
+    h[j] = 0.0f;
+  }
+  const int per = nseg - 1;  // aggregates of a split group
+  if constexpr (AGG) {
+    // segment 0 starts from the loaded state, and keeps it for its main task
+    // (the final segment's main task overwrites last_state)
+    if (seg == 0 && s.load_state) {
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) {
+        h[j] = last_state[row * N + n0 + j];
+        ws_h0[sr * N + n0 + j] = h[j];
+      }
+    }
+  } else if (nseg == 1) {
+    if (s.load_state) {
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) h[j] = last_state[row * N + n0 + j];
+    }
+  } else if (seg > 0 || s.load_state) {
+    // wait for the summaries of the segments before this one (segment 0: the
+    // kept initial state, published with segment 0's summary)
+    if (threadIdx.x == 0) {
+      const int nw = seg > 0 ? seg : 1;
+      for (int q = 0; q < nw; ++q) {
+        uint32_t it = 0;
+        while (__hip_atomic_load(&ws_flags[q * s.split_groups + sg], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT) == 0u &&
+               ++it < kFlagSpinLimit)
+          __builtin_amdgcn_s_sleep(1);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    if (seg == 0) {
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) h[j] = ws_h0[sr * N + n0 + j];
+    } else {
+      double hd[NPW];
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) hd[j] = (double)ws_S[(sr * per + 0) * N + n0 + j];
+      for (int q = 1; q < seg; ++q) {
+        const double sum = ws_sum[sr * per + q];
+#pragma unroll
+        for (int j = 0; j < NPW; ++j)
+          hd[j] = exp((double)A[dc * N + n0 + j] * sum) * hd[j] +
+                  (double)ws_S[(sr * per + q) * N + n0 + j];
+      }
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) h[j] = (float)hd[j];
+    }
   }
   const float bv_d = bias ? bias[dc] : 0.0f;
   const float Dd = (!AGG && Dv) ? Dv[dc] : 0.0f;
@@ -419,7 +477,6 @@ __device__ __forceinline__ void scan_body(
   }
 
   if constexpr (AGG) {
-    const int per = nseg - 1;
 #pragma unroll
     for (int j = 0; j < NPW; ++j) ws_S[(sr * per + seg) * N + n0 + j] = h[j];
     // the segment's sum of Delta: the waves' sums over their own steps, added
@@ -433,6 +490,13 @@ __device__ __forceinline__ void scan_body(
       for (int w = 0; w < NG; ++w) tot += part[w * kLanes + lane];
       ws_sum[sr * per + seg] = tot;
     }
+    // publish: every wave waits for its own summary stores to complete, then
+    // one release (write-back of this XCD's L2) ahead of the flag
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&ws_flags[seg * s.split_groups + sg], 1u, __ATOMIC_RELEASE,
+                         __HIP_MEMORY_SCOPE_AGENT);
   } else {
     if (last_state && valid && seg == nseg - 1) {
 #pragma unroll
@@ -441,10 +505,12 @@ __device__ __forceinline__ void scan_body(
   }
 }
 
-// One launch runs `n_main` main-pass tasks (task = main_base + block) and,
-// after them, aggregate-pass tasks (task = block - n_main).  Putting the
-// aggregate pass of the time-split groups into the same launch as the main
-// pass of the whole groups lets it run on the CUs' spare workgroup slots.
+// One launch runs every task of a call: blocks [0, whole) are the whole
+// groups' main tasks, the next n_agg blocks the split groups' aggregate
+// tasks, the rest the split groups' main tasks.  The whole groups come first
+// so that the dispatcher spreads them over the CUs, one each, ahead of the
+// shorter split work; a main task only ever waits for aggregates, which are
+// ahead of it in dispatch order and wait for nothing.
 template <int N, int NG, bool BF16, bool VEC, bool HAS_Z, bool SOFTPLUS, bool CONV>
 __global__ void __launch_bounds__(kLanes* NG)
     scan_kernel(const void* __restrict__ u, const void* __restrict__ delta,
@@ -452,47 +518,48 @@ __global__ void __launch_bounds__(kLanes* NG)
                 const float* __restrict__ Dv, const float* __restrict__ bias,
                 void* __restrict__ out, float* __restrict__ last_state,
                 float* __restrict__ ws_S, double* __restrict__ ws_sum,
-                const float* __restrict__ ws_hin,
+                float* __restrict__ ws_h0, uint32_t* __restrict__ ws_flags,
                 const uint32_t* __restrict__ bcp, const ScanShape s,
-                const int n_main, const int main_base, const ConvArgs cv) {
+                const int n_agg, const ConvArgs cv) {
   __shared__ float2 s_dw[kTile][kLanes];        // (Delta, Delta*u) of a tile
   __shared__ float s_y[NG][kTile][kLanes];      // per-wave partial readouts
   const int blk = blockIdx.x;
-  if (blk < n_main)
-    scan_body<N, NG, BF16, VEC, HAS_Z, false, SOFTPLUS, CONV>(
-        u, delta, z, A, Dv, bias, out, last_state, ws_S, ws_sum, ws_hin, bcp,
-        s, s_dw, s_y, main_base + blk, cv);
-  else
+  const int a = blk - s.whole_groups;  // aggregate task, when in [0, n_agg)
+  if (a >= 0 && a < n_agg)
     scan_body<N, NG, BF16, VEC, HAS_Z, true, SOFTPLUS, CONV>(
-        u, delta, z, A, Dv, bias, out, last_state, ws_S, ws_sum, ws_hin, bcp,
-        s, s_dw, s_y, blk - n_main, cv);
+        u, delta, z, A, Dv, bias, out, last_state, ws_S, ws_sum, ws_h0, ws_flags, bcp,
+        s, s_dw, s_y, a, cv);
+  else
+    scan_body<N, NG, BF16, VEC, HAS_Z, false, SOFTPLUS, CONV>(
+        u, delta, z, A, Dv, bias, out, last_state, ws_S, ws_sum, ws_h0, ws_flags, bcp,
+        s, s_dw, s_y, a < 0 ? blk : blk - n_agg, cv);
 }
 
 
 template <int N, int NG, bool BF16, bool VEC, bool HAS_Z, bool CONV>
-hipError_t launch_one(const ScanParams& p, const ScanShape& s, int n_main,
-                      int main_base, int n_agg, hipStream_t stream) {
+hipError_t launch_one(const ScanParams& p, const ScanShape& s, int n_main, int n_agg,
+                      hipStream_t stream) {
   const dim3 grid(n_main + n_agg), block(kLanes * NG);
   const ConvArgs cv{p.conv_w, p.conv_b, p.conv_init, p.u_out};
   if (p.softplus)
     hipLaunchKernelGGL((scan_kernel<N, NG, BF16, VEC, HAS_Z, true, CONV>), grid, block,
                        0, stream, p.u, p.delta, p.z, p.A, p.D, p.bias, p.out,
-                       p.last_state, p.ws_S, p.ws_sum, p.ws_hin,
-                       (const uint32_t*)p.ws_bc, s, n_main, main_base, cv);
+                       p.last_state, p.ws_S, p.ws_sum, p.ws_h0, p.ws_flags,
+                       (const uint32_t*)p.ws_bc, s, n_agg, cv);
   else
     hipLaunchKernelGGL((scan_kernel<N, NG, BF16, VEC, HAS_Z, false, CONV>), grid, block,
                        0, stream, p.u, p.delta, p.z, p.A, p.D, p.bias, p.out,
-                       p.last_state, p.ws_S, p.ws_sum, p.ws_hin,
-                       (const uint32_t*)p.ws_bc, s, n_main, main_base, cv);
+                       p.last_state, p.ws_S, p.ws_sum, p.ws_h0, p.ws_flags,
+                       (const uint32_t*)p.ws_bc, s, n_agg, cv);
   return hipGetLastError();
 }
 
 template <int N, int NG, bool BF16, bool VEC, bool CONV>
-hipError_t launch_tasks(const ScanParams& p, const ScanShape& s, int n_main,
-                        int main_base, int n_agg, hipStream_t stream) {
+hipError_t launch_tasks(const ScanParams& p, const ScanShape& s, int n_main, int n_agg,
+                        hipStream_t stream) {
   if (p.z)
-    return launch_one<N, NG, BF16, VEC, true, CONV>(p, s, n_main, main_base, n_agg, stream);
-  return launch_one<N, NG, BF16, VEC, false, CONV>(p, s, n_main, main_base, n_agg, stream);
+    return launch_one<N, NG, BF16, VEC, true, CONV>(p, s, n_main, n_agg, stream);
+  return launch_one<N, NG, BF16, VEC, false, CONV>(p, s, n_main, n_agg, stream);
 }
 
 template <int N, bool BF16, bool VEC, bool CONV>
@@ -508,63 +575,24 @@ hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
   s.load_state = p.load_state;
   s.groups_per_batch = p.groups_per_batch;
   s.whole_groups = p.whole_groups;
+  s.split_groups = p.split_groups;
   s.segments = p.segments;
   s.seg_len = p.seg_len;
+  const int n_agg = p.split_groups > 0 ? p.split_groups * (p.segments - 1) : 0;
+  const int n_main = p.whole_groups + p.split_groups * p.segments;
   hipError_t e;
   {
+    // the pack also clears the aggregates' flags for the launch after it
     constexpr int WPS = BCLayout<N / NG, BF16>::kWordsPerStep;
     e = launch_bc_pack(p.B, p.C, p.ws_bc, p.batch, s.ngroups, p.L, p.L, N, NG, BF16,
-                       BF16, bc_run_words(p.L, WPS), stream);
+                       BF16, bc_run_words(p.L, WPS), p.ws_flags, n_agg, stream);
     if (e != hipSuccess) return e;
-  }
-  if (p.split_groups > 0 && p.whole_groups > 0 && p.side_stream) {
-    // Two streams: the whole groups' main pass on the caller's stream, and
-    // the split groups' chain (aggregate -> combine -> main) beside it on the
-    // side stream, so that the chain runs on the CUs' spare workgroup slots.
-    hipStream_t side = (hipStream_t)p.side_stream;
-    e = hipEventRecord((hipEvent_t)p.ev_fork, stream);
-    if (e == hipSuccess) e = hipStreamWaitEvent(side, (hipEvent_t)p.ev_fork, 0);
-    if (e != hipSuccess) return e;
-    // From here on the caller's stream always waits for the side stream
-    // before this returns, whatever fails: work already queued on the side
-    // stream reads and writes the workspace, so nothing the caller orders
-    // after this call (freeing or reusing the workspace) may overtake it.
-    hipError_t es = launch_tasks<N, NG, BF16, VEC, CONV>(
-        p, s, 0, 0, p.split_groups * (p.segments - 1), side);
-    if (es == hipSuccess) es = launch_combine(p, s, N, side);
-    if (es == hipSuccess)
-      es = launch_tasks<N, NG, BF16, VEC, CONV>(p, s, p.split_groups * p.segments,
-                                              p.whole_groups, 0, side);
-    if (es == hipSuccess && p.ev_start) es = hipEventRecord((hipEvent_t)p.ev_start, stream);
-    if (es == hipSuccess)
-      es = launch_tasks<N, NG, BF16, VEC, CONV>(p, s, p.whole_groups, 0, 0, stream);
-    if (es == hipSuccess && p.ev_stop) es = hipEventRecord((hipEvent_t)p.ev_stop, stream);
-    e = hipEventRecord((hipEvent_t)p.ev_join, side);
-    if (e == hipSuccess) e = hipStreamWaitEvent(stream, (hipEvent_t)p.ev_join, 0);
-    if (e != hipSuccess) {
-      // the join could not be ordered: drain the side stream so that the
-      // workspace is idle when this returns
-      (void)hipStreamSynchronize(side);
-    }
-    return es != hipSuccess ? es : e;
   }
   if (p.ev_start) {
     e = hipEventRecord((hipEvent_t)p.ev_start, stream);
     if (e != hipSuccess) return e;
   }
-  if (p.split_groups > 0) {
-    // one stream: whole groups' main pass + split groups' aggregate pass in
-    // one launch, then the segment initial states, then the split groups'
-    // main pass
-    e = launch_tasks<N, NG, BF16, VEC, CONV>(p, s, p.whole_groups, 0,
-                                       p.split_groups * (p.segments - 1), stream);
-    if (e == hipSuccess) e = launch_combine(p, s, N, stream);
-    if (e == hipSuccess)
-      e = launch_tasks<N, NG, BF16, VEC, CONV>(p, s, p.split_groups * p.segments,
-                                         p.whole_groups, 0, stream);
-  } else {
-    e = launch_tasks<N, NG, BF16, VEC, CONV>(p, s, p.whole_groups, 0, 0, stream);
-  }
+  e = launch_tasks<N, NG, BF16, VEC, CONV>(p, s, n_main, n_agg, stream);
   if (e == hipSuccess && p.ev_stop) e = hipEventRecord((hipEvent_t)p.ev_stop, stream);
   return e;
 }

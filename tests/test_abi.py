@@ -209,10 +209,11 @@ def test_plan(L):
     assert plan.whole_groups + plan.split_groups == 320
     assert plan.split_groups * plan.segments + plan.whole_groups >= 320
     assert plan.vector_path == 1
-    # long sequence: few groups, long rows -> every group cut, 3 launches
+    # long sequence: few groups, long rows -> every group cut; the pack and one
+    # launch for all of the aggregate and main tasks
     assert L.mssm_selective_scan_fwd_plan(
         ctypes.byref(_dims(1, 1536, 16, 131072)), ctypes.byref(plan)) == 0
-    assert plan.whole_groups == 0 and plan.segments > 1 and plan.kernels == 4
+    assert plan.whole_groups == 0 and plan.segments > 1 and plan.kernels == 2
     assert (plan.segments - 1) * plan.segment_len < 131072 <= plan.segments * plan.segment_len
     assert plan.workspace_bytes > 0
     # forced segments
@@ -309,3 +310,4 @@ def test_workspace_entry_points(L):
         b["h0"], b["dout"], b["dlast"], b["du"], b["ddelta"], b["dA"], b["dB"],
         b["dC"], b["dD"], b["dz"], b["dbias"], b["dh0"], None, 0, ct.byref(dims),
         None) == -7
+

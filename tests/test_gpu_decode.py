@@ -168,3 +168,53 @@ def test_decode_64bit_indices():
     del t
     check_out(got_out, ref_out, "bf16", "decode 64-bit indices out")
     check_state(got_state, ref_state, "decode 64-bit indices state")
+
+
+def test_decode_graph_replays_match_eager():
+    """Decode steps captured in one HIP graph (as the bench replays its
+    rotating loop): each of several replays, with eager launches and
+    synchronisations between them, gives the bit-identical outputs and states
+    of the same steps run eagerly from the same starting states."""
+    import selective_state_space_52_amd as m
+    s = W.spec("decode", batch=8, dim=640, tokens=3)
+    par = W.make_decode_params(s)
+    toks = [{k: to_dev(v) for k, v in W.make_decode_token(s, k).items()}
+            for k in range(s.tokens)]
+    A, D, bias = to_dev(par["A"]), to_dev(par["D"]), to_dev(par["dt_bias"])
+    states = [to_dev(par["state"]).clone() for _ in range(2)]
+    outs = [torch.empty(s.batch, s.dim, dtype=torch.bfloat16, device=DEV) for _ in range(6)]
+    steps = 6
+
+    def run():
+        for i in range(steps):
+            t = toks[i % len(toks)]
+            m.selective_state_update(states[i % 2], t["x"], t["dt"], A, t["B"], t["C"], D=D,
+                                     z=t["z"], dt_bias=bias, out=outs[i])
+
+    graph = torch.cuda.CUDAGraph()
+    start = [st.clone() for st in states]
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        begin = [st.clone() for st in states]
+        graph.replay()
+        torch.cuda.synchronize()
+        g_outs = [o.clone() for o in outs]
+        g_states = [st.clone() for st in states]
+        # the same steps eagerly from the same starting states
+        for st, b0 in zip(states, begin):
+            st.copy_(b0)
+        run()
+        torch.cuda.synchronize()
+        for k in range(steps):
+            assert torch.equal(g_outs[k], outs[k]), "replay %d, step %d out" % (rep, k)
+        for k in range(2):
+            assert torch.equal(g_states[k], states[k]), "replay %d, state %d" % (rep, k)
+        # eager work between replays: a plain call on another state
+        scratch_state = start[0].clone()
+        t = toks[0]
+        m.selective_state_update(scratch_state, t["x"], t["dt"], A, t["B"], t["C"], D=D,
+                                 z=t["z"], dt_bias=bias)
+        torch.cuda.synchronize()
+    del graph
