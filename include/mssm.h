@@ -83,6 +83,8 @@ enum {
   MSSM_ERR_ALIAS = -5,       /* an output overlaps another argument         */
   MSSM_ERR_HIP = -6,         /* a HIP runtime call or launch failed         */
   MSSM_ERR_WORKSPACE = -7    /* workspace missing, too small or misaligned  */
+                             /* (or, for the allocation-free call, larger    */
+                             /* than the library's fixed scratch)            */
 };
 
 /* fwd: last_state holds the initial state h0 on entry (in/out). */
@@ -331,6 +333,28 @@ enum {
  * (and, for the backward, on its occupancy), so the size is for calls on the
  * device that is current here.  Validates dims like the call itself. */
 int mssm_workspace_size(int op, const mssm_dims* dims, int64_t headdim, int64_t* bytes);
+
+/*
+ * Allocation-free forward scan, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Arguments, results and errors as in
+ * mssm_selective_scan_fwd.  Its workspace is a fixed scratch array of
+ * MSSM_NOALLOC_SCRATCH_BYTES per device, built into the library (each device
+ * holds its copy until the process ends); a call whose workspace
+ * (mssm_workspace_size(MSSM_OP_SCAN_FWD)) is larger returns
+ * MSSM_ERR_WORKSPACE and launches nothing.  The call allocates, frees and
+ * synchronises nothing.  The first call
+ * on a device looks up that device's scratch address (a HIP symbol query);
+ * later calls make no such query.  Every call on a device shares that
+ * device's scratch: calls that overlap in time on one device (on different
+ * streams, or from several threads) race and give wrong results; order them.
+ */
+#define MSSM_NOALLOC_SCRATCH_BYTES (32ll << 20)
+int mssm_selective_scan_fwd_noalloc(const void* u, const void* delta, const float* A,
+                                    const void* B, const void* C, const float* D,
+                                    const void* z, const float* delta_bias,
+                                    int softplus, void* out, float* last_state,
+                                    const mssm_dims* dims, void* stream);
 
 /* How the forward scan would run for these dims (no HIP call, no launch). */
 typedef struct {

@@ -31,7 +31,7 @@ EXPORTS = ("mssm_selective_scan_fwd", "mssm_selective_scan_bwd",
            "mssm_status_string", "mssm_last_error", "mssm_abi_version",
            "mssm_selective_scan_fwd_ws", "mssm_selective_scan_fwd_conv_ws",
            "mssm_selective_scan_bwd_ws", "mssm_mamba2_scan_fwd_ws",
-           "mssm_workspace_size")
+           "mssm_workspace_size", "mssm_selective_scan_fwd_noalloc")
 
 
 class Dims(ctypes.Structure):
@@ -105,6 +105,9 @@ def lib():
                                               i64, vp, fp, vp, i64,
                                               ctypes.POINTER(Dims), vp]
         L.mssm_mamba2_scan_fwd_ws.restype = i
+        L.mssm_selective_scan_fwd_noalloc.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i,
+                                                      vp, fp, ctypes.POINTER(Dims), vp]
+        L.mssm_selective_scan_fwd_noalloc.restype = i
         L.mssm_workspace_size.argtypes = [i, ctypes.POINTER(Dims), i64,
                                           ctypes.POINTER(i64)]
         L.mssm_workspace_size.restype = i

@@ -242,7 +242,8 @@ namespace mssm {
 // The forward scan, optionally fed by the causal conv (conv_w non-null: `u`
 // is the conv input x).  Workspace: `ws` (ws_bytes long) from the caller, or
 // with ws == nullptr and WsMode::kAllocate taken stream-ordered from HIP's
-// pool for this call.
+// pool for this call, or (WsMode::kScratch) the library's fixed scratch array
+// of ws_bytes.
 int scan_fwd_entry(const void* u, const void* delta, const float* A,
                    const void* B, const void* C, const float* D, const void* z,
                    const float* delta_bias, int softplus, void* out,
@@ -328,6 +329,22 @@ int scan_fwd_entry(const void* u, const void* delta, const float* A,
   if (mode == WsMode::kCaller) {
     rc = check_workspace(ws_in, ws_bytes, plan.workspace_bytes);
     if (rc != MSSM_OK) return rc;
+  } else if (mode == WsMode::kScratch) {
+    if (plan.workspace_bytes > ws_bytes) {
+      std::snprintf(g_last_error, sizeof(g_last_error),
+                    "the call needs %lld bytes of workspace; the allocation-free entry "
+                    "point's scratch holds %lld",
+                    (long long)plan.workspace_bytes, (long long)ws_bytes);
+      return MSSM_ERR_WORKSPACE;
+    }
+    if (plan.workspace_bytes > 0) {
+      hipError_t e = hipSuccess;
+      ws_in = mssm::noalloc_scratch(&e);
+      if (!ws_in) {
+        set_hip_error("hipGetSymbolAddress(scratch)", e);
+        return MSSM_ERR_HIP;
+      }
+    }
   }
   hipStream_t st = (hipStream_t)stream;
   void* ws = ws_in;

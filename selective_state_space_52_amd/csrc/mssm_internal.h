@@ -148,8 +148,14 @@ struct BwdParams {
 };
 
 // Where a forward call's workspace comes from: allocated stream-ordered for
-// the call (kAllocate) or supplied by the caller (kCaller).
-enum class WsMode { kAllocate, kCaller };
+// the call (kAllocate), supplied by the caller (kCaller), or the library's
+// fixed scratch array of the current device (kScratch: ws_bytes is its size).
+enum class WsMode { kAllocate, kCaller, kScratch };
+
+// Device address of the current device's allocation-free scratch array
+// (noalloc.hip), looked up on the first call per device; nullptr and *err set
+// if the lookup fails.
+void* noalloc_scratch(hipError_t* err);
 
 // The forward scan entry shared by the C ABI's forward calls (mssm_api.cpp);
 // returns an MSSM_* status.  conv_w non-null: `u` is the conv input x.

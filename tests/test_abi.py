@@ -311,3 +311,21 @@ def test_workspace_entry_points(L):
         b["dC"], b["dD"], b["dz"], b["dbias"], b["dh0"], None, 0, ct.byref(dims),
         None) == -7
 
+
+def test_noalloc_refuses_oversized_call(L):
+    """The allocation-free forward refuses a call whose workspace exceeds its
+    fixed scratch, before launching anything (no pointer is dereferenced)."""
+    import ctypes as ct
+    from selective_state_space_52_amd._lib import Plan
+    big = _dims(64, 64, 16, 1 << 17)          # 64 groups x 131072 steps of B/C runs
+    plan = Plan()
+    assert L.mssm_selective_scan_fwd_plan(ct.byref(big), ct.byref(plan)) == 0
+    assert plan.workspace_bytes > (32 << 20)
+    p = _ptrs(10)
+    rc = L.mssm_selective_scan_fwd_noalloc(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], 1,
+                                           p[8], p[9], ct.byref(big), None)
+    assert rc == -7
+    assert "scratch" in L.mssm_last_error().decode()
+    # validation still comes first
+    assert L.mssm_selective_scan_fwd_noalloc(None, p[1], p[2], p[3], p[4], p[5], p[6], p[7],
+                                             1, p[8], p[9], ct.byref(big), None) == -1
