@@ -30,6 +30,7 @@
  *   u, delta, z, out   (batch, dim, seqlen)      io dtype
  *   B, C               (batch, seqlen, dstate)   io dtype, one N-vector/token
  *                      (batch, seqlen, g, dstate) with mssm_dims.ngroups = g
+ *                      (batch, [g,] dstate, seqlen) with MSSM_FLAG_BC_STATE_MAJOR
  *   A                  (dim, dstate)             fp32 (real; negative for a
  *                                                 decaying state)
  *   D, delta_bias      (dim)                     fp32
@@ -95,6 +96,13 @@ enum {
  * (batch, dim, seqlen).  B and C keep (batch, seqlen, dstate).  Accepted by
  * the forward scans, the backward and the causal conv. */
 #define MSSM_FLAG_LAYOUT_BLD 2u
+/* B and C are (batch, dstate, seqlen), (batch, g, dstate, seqlen) with
+ * ngroups = g -- each state's values over time contiguous, the layout of the
+ * exported low-level scan op (page "Mamba State Space Model", "Use selective
+ * scan operations") -- instead of (batch, seqlen, dstate).  The backward
+ * writes dB and dC in the same layout.  Accepted by the forward scans and the
+ * backward; the results do not depend on the layout. */
+#define MSSM_FLAG_BC_STATE_MAJOR 4u
 
 typedef struct {
   int64_t batch;       /* >= 1                                              */

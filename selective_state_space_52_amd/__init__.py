@@ -18,7 +18,8 @@ import torch
 
 import ctypes
 
-from ._lib import (MSSM_BF16, MSSM_F32, MSSM_FLAG_LAYOUT_BLD, MSSM_FLAG_LOAD_STATE,
+from ._lib import (MSSM_BF16, MSSM_F32, MSSM_FLAG_BC_STATE_MAJOR, MSSM_FLAG_LAYOUT_BLD,
+                   MSSM_FLAG_LOAD_STATE,
                    MSSM_OP_MAMBA2_FWD, MSSM_OP_SCAN_BWD, MSSM_OP_SCAN_FWD,
                    MSSM_OP_SCAN_FWD_CONV, Dims, MssmError, Plan, check, lib)
 
@@ -80,15 +81,30 @@ def _eshape(batch, dim, L, layout):
     return (batch, L, dim) if layout == "bld" else (batch, dim, L)
 
 
-def _groups(B, batch, L, N, token_dim=True):
+_BC_LAYOUTS = ("token", "state")
+
+
+def _bc_flag(bc_layout):
+    if bc_layout not in _BC_LAYOUTS:
+        raise ValueError("bc_layout must be 'token' (batch, L, [G,] N) or "
+                         "'state' (batch, [G,] N, L)")
+    return MSSM_FLAG_BC_STATE_MAJOR if bc_layout == "state" else 0
+
+
+def _groups(B, batch, L, N, token_dim=True, bc_layout="token"):
     """B/C group count from B's shape: (batch, L, N) or (batch, L, G, N) for
-    the scans (token_dim), (batch, N) or (batch, G, N) for the decode step."""
+    the scans (token_dim; (batch, N, L) or (batch, G, N, L) with bc_layout
+    'state'), (batch, N) or (batch, G, N) for the decode step."""
     if token_dim:
-        return B.shape[2] if B.dim() == 4 else 1
+        if B.dim() != 4:
+            return 1
+        return B.shape[1] if bc_layout == "state" else B.shape[2]
     return B.shape[1] if B.dim() == 3 else 1
 
 
-def _bc_shape(batch, L, G, N, grouped):
+def _bc_shape(batch, L, G, N, grouped, bc_layout="token"):
+    if bc_layout == "state":
+        return (batch, G, N, L) if grouped else (batch, N, L)
     return (batch, L, G, N) if grouped else (batch, L, N)
 
 
@@ -136,10 +152,11 @@ def scan_plan(batch, dim, dstate, seqlen, io_dtype=torch.bfloat16,
 
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                        softplus=True, last_state=None, load_state=False,
-                       out=None, time_segments=0, layout="bdl"):
+                       out=None, time_segments=0, layout="bdl", bc_layout="token"):
     """Forward selective scan.
 
-    u, delta, z: (batch, dim, L); B, C: (batch, L, N), all fp32 or all bf16.
+    u, delta, z: (batch, dim, L); B, C: (batch, L, N) (bc_layout="state":
+    (batch, N, L)), all fp32 or all bf16.
     A: (dim, N) fp32; D, delta_bias: (dim,) fp32 or None.
     last_state: (batch, dim, N) fp32 receiving the final state (and holding
     the initial state when load_state=True), or None.
@@ -157,8 +174,8 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     _need(u, "u", io, es, dev)
     _need(delta, "delta", io, es, dev)
     _need(z, "z", io, es, dev)
-    G = _groups(B, batch, L, N)
-    _need(B, "B", io, _bc_shape(batch, L, G, N, B.dim() == 4), dev)
+    G = _groups(B, batch, L, N, bc_layout=bc_layout)
+    _need(B, "B", io, _bc_shape(batch, L, G, N, B.dim() == 4, bc_layout), dev)
     _need(C, "C", io, tuple(B.shape), dev)
     _need(A, "A", torch.float32, (dim, N), dev)
     _need(D, "D", torch.float32, (dim,), dev)
@@ -170,7 +187,8 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         out = torch.empty(es, dtype=io, device=dev)
     _need(out, "out", io, es, dev)
     dims = Dims(batch, dim, N, L, _IO[io],
-                (MSSM_FLAG_LOAD_STATE if load_state else 0) | lay, time_segments, G)
+                (MSSM_FLAG_LOAD_STATE if load_state else 0) | lay | _bc_flag(bc_layout),
+                time_segments, G)
     with torch.cuda.device(dev):
         st = _stream(dev)
         ws, nws = _workspace(MSSM_OP_SCAN_FWD, dims, dev, st)
@@ -213,7 +231,8 @@ def causal_conv1d_fwd(x, weight, bias=None, init=None, silu=True, out=None,
 def selective_scan_fwd_conv(x, conv_weight, delta, A, B, C, conv_bias=None,
                             conv_init=None, D=None, z=None, delta_bias=None,
                             softplus=True, last_state=None, load_state=False,
-                            out=None, u_out=None, time_segments=0, layout="bdl"):
+                            out=None, u_out=None, time_segments=0, layout="bdl",
+                            bc_layout="token"):
     """The forward scan whose input is u = silu(causal_conv(x)) (width 4),
     formed inside the scan kernel.  x: (batch, dim, L); conv_weight (dim, 4)
     fp32; conv_bias (dim,) fp32 or None; conv_init (batch, dim, 3) or None;
@@ -234,8 +253,8 @@ def selective_scan_fwd_conv(x, conv_weight, delta, A, B, C, conv_bias=None,
     _need(u_out, "u_out", io, es, dev)
     _need(delta, "delta", io, es, dev)
     _need(z, "z", io, es, dev)
-    G = _groups(B, batch, L, N)
-    _need(B, "B", io, _bc_shape(batch, L, G, N, B.dim() == 4), dev)
+    G = _groups(B, batch, L, N, bc_layout=bc_layout)
+    _need(B, "B", io, _bc_shape(batch, L, G, N, B.dim() == 4, bc_layout), dev)
     _need(C, "C", io, tuple(B.shape), dev)
     _need(A, "A", torch.float32, (dim, N), dev)
     _need(D, "D", torch.float32, (dim,), dev)
@@ -247,7 +266,8 @@ def selective_scan_fwd_conv(x, conv_weight, delta, A, B, C, conv_bias=None,
         out = torch.empty(es, dtype=io, device=dev)
     _need(out, "out", io, es, dev)
     dims = Dims(batch, dim, N, L, _IO[io],
-                (MSSM_FLAG_LOAD_STATE if load_state else 0) | lay, time_segments, G)
+                (MSSM_FLAG_LOAD_STATE if load_state else 0) | lay | _bc_flag(bc_layout),
+                time_segments, G)
     with torch.cuda.device(dev):
         st = _stream(dev)
         ws, nws = _workspace(MSSM_OP_SCAN_FWD_CONV, dims, dev, st)
@@ -261,14 +281,14 @@ def selective_scan_fwd_conv(x, conv_weight, delta, A, B, C, conv_bias=None,
 
 def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None,
                        delta_bias=None, softplus=True, h0=None, dlast=None,
-                       want_dh0=False, time_segments=0, layout="bdl"):
+                       want_dh0=False, time_segments=0, layout="bdl", bc_layout="token"):
     """Gradients of the forward scan for the loss
     sum(dout * out) + sum(dlast * last_state).
 
     Inputs as in selective_scan_fwd; h0 (batch, dim, N) fp32 is the initial
     state (None = zero), dout (batch, dim, L) in the io dtype, dlast
     (batch, dim, N) fp32 or None.  Returns a dict: du, ddelta, dz (io dtype,
-    dz only with z), dA (dim, N), dB, dC (batch, L, N), dD, ddelta_bias (dim,)
+    dz only with z), dA (dim, N), dB, dC (shaped as B), dD, ddelta_bias (dim,)
     and, with want_dh0, dh0 (batch, dim, N), all fp32 except the first three.
     time_segments: 0 = the library's split of rows into parallel time
     segments; k >= 1 asks for about k.
@@ -285,8 +305,8 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None,
     _need(delta, "delta", io, es, dev)
     _need(z, "z", io, es, dev)
     _need(dout, "dout", io, es, dev)
-    G = _groups(B, batch, L, N)
-    _need(B, "B", io, _bc_shape(batch, L, G, N, B.dim() == 4), dev)
+    G = _groups(B, batch, L, N, bc_layout=bc_layout)
+    _need(B, "B", io, _bc_shape(batch, L, G, N, B.dim() == 4, bc_layout), dev)
     _need(C, "C", io, tuple(B.shape), dev)
     _need(A, "A", torch.float32, (dim, N), dev)
     _need(D, "D", torch.float32, (dim,), dev)
@@ -303,7 +323,7 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None,
              dD=torch.empty((dim,), **f32),
              ddelta_bias=torch.empty((dim,), **f32),
              dh0=torch.empty((batch, dim, N), **f32) if want_dh0 else None)
-    dims = Dims(batch, dim, N, L, _IO[io], lay, time_segments, G)
+    dims = Dims(batch, dim, N, L, _IO[io], lay | _bc_flag(bc_layout), time_segments, G)
     with torch.cuda.device(dev):
         st = _stream(dev)
         ws, nws = _workspace(MSSM_OP_SCAN_BWD, dims, dev, st)

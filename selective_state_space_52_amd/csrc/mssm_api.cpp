@@ -227,7 +227,7 @@ int mssm_selective_scan_fwd_plan(const mssm_dims* dims, mssm_plan* plan) {
   if (!plan) return MSSM_ERR_NULL;
   int rc = check_common_dims(dims);
   if (rc != MSSM_OK) return rc;
-  if (dims->flags & ~(MSSM_FLAG_LOAD_STATE | MSSM_FLAG_LAYOUT_BLD))
+  if (dims->flags & ~(MSSM_FLAG_LOAD_STATE | MSSM_FLAG_LAYOUT_BLD | MSSM_FLAG_BC_STATE_MAJOR))
     return MSSM_ERR_UNSUPPORTED;
   rc = check_scan_groups(dims);
   if (rc != MSSM_OK) return rc;
@@ -252,7 +252,7 @@ int scan_fwd_entry(const void* u, const void* delta, const float* A,
                    WsMode mode, const mssm_dims* dims, void* stream) {
   int rc = check_common_dims(dims);
   if (rc != MSSM_OK) return rc;
-  if (dims->flags & ~(MSSM_FLAG_LOAD_STATE | MSSM_FLAG_LAYOUT_BLD))
+  if (dims->flags & ~(MSSM_FLAG_LOAD_STATE | MSSM_FLAG_LAYOUT_BLD | MSSM_FLAG_BC_STATE_MAJOR))
     return MSSM_ERR_UNSUPPORTED;
   const bool bld = (dims->flags & MSSM_FLAG_LAYOUT_BLD) != 0;
   rc = check_scan_groups(dims);
@@ -325,6 +325,7 @@ int scan_fwd_entry(const void* u, const void* delta, const float* A,
   p.conv_init = conv_init;
   p.u_out = u_out;
   p.layout_bld = bld ? 1 : 0;
+  p.bc_state_major = (dims->flags & MSSM_FLAG_BC_STATE_MAJOR) ? 1 : 0;
 
   if (mode == WsMode::kCaller) {
     rc = check_workspace(ws_in, ws_bytes, plan.workspace_bytes);
@@ -508,7 +509,8 @@ int scan_bwd_entry(const void* u, const void* delta, const float* A,
   int rc = check_common_dims(dims);
   if (rc != MSSM_OK) return rc;
   if (dims->dstate > 32) return MSSM_ERR_UNSUPPORTED;
-  if (dims->flags & ~MSSM_FLAG_LAYOUT_BLD) return MSSM_ERR_UNSUPPORTED;
+  if (dims->flags & ~(MSSM_FLAG_LAYOUT_BLD | MSSM_FLAG_BC_STATE_MAJOR))
+    return MSSM_ERR_UNSUPPORTED;
   const bool bld = (dims->flags & MSSM_FLAG_LAYOUT_BLD) != 0;
   rc = check_scan_groups(dims);
   if (rc != MSSM_OK) return rc;
@@ -589,6 +591,7 @@ int scan_bwd_entry(const void* u, const void* delta, const float* A,
   p.segments = segments;
   p.seg_tiles = (int32_t)((tiles + segments - 1) / segments);
   p.layout_bld = bld ? 1 : 0;
+  p.bc_state_major = (dims->flags & MSSM_FLAG_BC_STATE_MAJOR) ? 1 : 0;
   p.ev_start = g_ev_start;
   p.ev_stop = g_ev_stop;
 
@@ -845,7 +848,8 @@ int mssm_workspace_size(int op, const mssm_dims* dims, int64_t headdim, int64_t*
     case MSSM_OP_SCAN_BWD: {
       rc = check_common_dims(dims);
       if (rc != MSSM_OK) return rc;
-      if (dims->dstate > 32 || (dims->flags & ~MSSM_FLAG_LAYOUT_BLD)) return MSSM_ERR_UNSUPPORTED;
+      if (dims->dstate > 32 || (dims->flags & ~(MSSM_FLAG_LAYOUT_BLD | MSSM_FLAG_BC_STATE_MAJOR)))
+        return MSSM_ERR_UNSUPPORTED;
       rc = check_scan_groups(dims);
       if (rc != MSSM_OK) return rc;
       if (dims->time_segments < 0) return MSSM_ERR_DIMS;

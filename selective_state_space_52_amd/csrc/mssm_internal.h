@@ -58,6 +58,7 @@ struct ScanParams {
   void* u_out;            // (batch, dim, L) io dtype: conv output, or null
   int32_t layout_bld;     // u, delta, z, out, u_out are (batch, L, dim)
   int32_t ngroups;        // B/C groups (B, C are (batch, L, ngroups, N))
+  int32_t bc_state_major; // B, C are (batch, ngroups, N, L)
 };
 
 // Standalone causal depthwise conv: out = act(bias + sum_k w[k] x[t-K+1+k]).
@@ -129,6 +130,7 @@ struct BwdParams {
   int32_t seg_tiles;      // tiles per segment (the last may have fewer)
   int32_t layout_bld;     // the per-element arrays are (batch, L, dim)
   int32_t ngroups;        // B/C groups (B, C, dB, dC are (batch, L, ngroups, N))
+  int32_t bc_state_major; // B, C, dB, dC are (batch, ngroups, N, L)
   // workspace (task = group * segments + segment; lane-contiguous rows)
   void* ws_bc;            // B, C packed per wave run, zero-padded to whole tiles
   float* ws_ck;           // [group][tile][n][lane] state at tile start, from a
@@ -171,13 +173,14 @@ int scan_waves_per_group(int N);
 // Repack B and C, (batch, L, groups, N), into per-wave runs, one per
 // (batch entry, group, wave) for `waves` waves per channel group: `steps`
 // (>= L) timesteps per run, zeros from L on, `run_words` 32-bit words per
-// run; the runs hold bf16 pairs (dst_bf16) or fp32 values.  The same launch
+// run; the runs hold bf16 pairs (dst_bf16) or fp32 values.  With
+// state_major, B and C are (batch, groups, N, L) instead.  The same launch
 // zeroes `nflags` words at `flags` (may be 0 / null).
 hipError_t launch_bc_pack(const void* B, const void* C, void* packed,
                           int64_t batch, int64_t groups, int64_t L, int64_t steps,
                           int N, int waves, bool src_bf16, bool dst_bf16,
                           int64_t run_words, uint32_t* flags, int64_t nflags,
-                          hipStream_t stream);
+                          bool state_major, hipStream_t stream);
 // Bytes of the packed B/C runs of one forward call.
 int64_t scan_bc_workspace_bytes(int64_t batch, int64_t L, int N, bool bf16);
 

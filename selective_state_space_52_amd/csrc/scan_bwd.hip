@@ -648,7 +648,7 @@ __global__ void __launch_bounds__(256)
                       float* __restrict__ dC, float* __restrict__ dA,
                       float* __restrict__ dD, float* __restrict__ dbias,
                       Idx batch, Idx dim, Idx L, Idx Lp, int gpb, int segments,
-                      int groups) {
+                      int groups, int state_major) {
   Idx i = (Idx)blockIdx.x * blockDim.x + threadIdx.x;
   const Idx n_bc = batch * L * (Idx)groups * 2 * N;
   if (i < n_bc) {
@@ -666,7 +666,8 @@ __global__ void __launch_bounds__(256)
     const float* src =
         ws_dbc + ((b * (Idx)gpb + grp * (Idx)per) * Lp + t) * (2 * N) + q * N + n;
     const float acc = strided_sum<Idx>(src, Lp * 2 * N, per);
-    (q ? dC : dB)[((b * L + t) * (Idx)groups + grp) * N + n] = acc;
+    (q ? dC : dB)[state_major ? ((b * (Idx)groups + grp) * N + n) * L + t
+                              : ((b * L + t) * (Idx)groups + grp) * N + n] = acc;
     return;
   }
   i -= n_bc;
@@ -734,7 +735,8 @@ hipError_t launch_n(const BwdParams& p, hipStream_t st) {
   s.softplus = p.softplus;
   s.batch = (int32_t)p.batch;
   hipError_t e = launch_bc_pack(p.B, p.C, p.ws_bc, p.batch, s.ngroups, p.L, Lp, N,
-                                NG, BF16, BF16, Lp * WPS, nullptr, 0, st);
+                                NG, BF16, BF16, Lp * WPS, nullptr, 0,
+                                p.bc_state_major != 0, st);
   if (e != hipSuccess) return e;
   e = p.z ? launch_passes<N, BF16, VEC, true>(p, s, st)
           : launch_passes<N, BF16, VEC, false>(p, s, st);
@@ -750,12 +752,12 @@ hipError_t launch_n(const BwdParams& p, hipStream_t st) {
     hipLaunchKernelGGL((bwd_reduce_kernel<N, uint32_t>), grid, dim3(256), 0, st,
                        p.ws_dbc, p.ws_dA, p.ws_dDb, p.dB, p.dC, p.dA, p.dD, p.dbias,
                        (uint32_t)p.batch, (uint32_t)p.dim, (uint32_t)p.L, (uint32_t)Lp,
-                       p.groups_per_batch, p.segments, s.ngroups);
+                       p.groups_per_batch, p.segments, s.ngroups, p.bc_state_major);
   else
     hipLaunchKernelGGL((bwd_reduce_kernel<N, int64_t>), grid, dim3(256), 0, st,
                        p.ws_dbc, p.ws_dA, p.ws_dDb, p.dB, p.dC, p.dA, p.dD, p.dbias,
                        p.batch, p.dim, p.L, Lp, p.groups_per_batch, p.segments,
-                       s.ngroups);
+                       s.ngroups, p.bc_state_major);
   return hipGetLastError();
 }
 

@@ -9,15 +9,16 @@ namespace fwd {
 // Writes the packed runs of `steps` timesteps per wave (steps >= L; the
 // timesteps from L on are written as zeros) with `run_words` words per run.
 // The source is bf16 or fp32 (src_bf16); the runs keep bf16 (dst_bf16) or
-// hold fp32.  Threads i < nflags also zero flags[i]: the scan launch that
-// follows on the same stream finds its summary flags cleared, with no
-// separate fill.
+// hold fp32.  B and C are (batch, L, groups, N), or with state_major
+// (batch, groups, N, L).  Threads i < nflags also zero flags[i]: the scan
+// launch that follows on the same stream finds its summary flags cleared,
+// with no separate fill.
 __global__ void __launch_bounds__(256)
     bc_pack_kernel(const void* __restrict__ Bm, const void* __restrict__ Cm,
                    void* __restrict__ packed, int64_t batch, int64_t groups,
                    int64_t L, int64_t steps, int N, int NG, int src_bf16,
                    int dst_bf16, int64_t run_words, uint32_t* __restrict__ flags,
-                   int64_t nflags) {
+                   int64_t nflags, int state_major) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < nflags) flags[i] = 0u;
   const int64_t total = batch * groups * steps * 2 * N;
@@ -33,7 +34,8 @@ __global__ void __launch_bounds__(256)
   const int64_t grp = bgrp % groups;
   const int64_t b = bgrp / groups;
   const int n = g * npw + (j < npw ? j : j - npw);
-  const int64_t src = ((b * L + t) * groups + grp) * N + n;
+  const int64_t src = state_major ? ((b * groups + grp) * N + n) * L + t
+                                  : ((b * L + t) * groups + grp) * N + n;
   const void* m = j < npw ? Bm : Cm;
   const int64_t vals_per_word = dst_bf16 ? 2 : 1;
   const int64_t dst = bg * run_words * vals_per_word + t * 2 * npw + j;
@@ -56,12 +58,12 @@ hipError_t launch_bc_pack(const void* B, const void* C, void* packed,
                           int64_t batch, int64_t groups, int64_t L, int64_t steps,
                           int N, int waves, bool src_bf16, bool dst_bf16,
                           int64_t run_words, uint32_t* flags, int64_t nflags,
-                          hipStream_t stream) {
+                          bool state_major, hipStream_t stream) {
   const int64_t total = std::max<int64_t>(batch * groups * steps * 2 * N, nflags);
   hipLaunchKernelGGL(fwd::bc_pack_kernel, dim3((unsigned)((total + 255) / 256)),
                      dim3(256), 0, stream, B, C, packed, batch, groups, L, steps,
                      N, waves, src_bf16 ? 1 : 0, dst_bf16 ? 1 : 0, run_words, flags,
-                     flags ? nflags : (int64_t)0);
+                     flags ? nflags : (int64_t)0, state_major ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -585,7 +585,8 @@ hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
     // the pack also clears the aggregates' flags for the launch after it
     constexpr int WPS = BCLayout<N / NG, BF16>::kWordsPerStep;
     e = launch_bc_pack(p.B, p.C, p.ws_bc, p.batch, s.ngroups, p.L, p.L, N, NG, BF16,
-                       BF16, bc_run_words(p.L, WPS), p.ws_flags, n_agg, stream);
+                       BF16, bc_run_words(p.L, WPS), p.ws_flags, n_agg,
+                       p.bc_state_major != 0, stream);
     if (e != hipSuccess) return e;
   }
   if (p.ev_start) {

@@ -81,7 +81,7 @@ def test_fwd_validation_codes(L):
     assert _fwd(L, _dims(N=256)) == -3
     assert _fwd(L, _dims(N=48)) == -3
     assert _fwd(L, _dims(io=7)) == -3
-    assert _fwd(L, _dims(flags=4)) == -3                    # unknown flag
+    assert _fwd(L, _dims(flags=8)) == -3                    # unknown flag
     assert _fwd(L, _dims(groups=-1)) == -2
     assert _fwd(L, _dims(dim=192, groups=2)) == -3         # 96 channels per group
     assert _fwd(L, _dims(dim=64, groups=3)) == -3
@@ -329,3 +329,24 @@ def test_noalloc_refuses_oversized_call(L):
     # validation still comes first
     assert L.mssm_selective_scan_fwd_noalloc(None, p[1], p[2], p[3], p[4], p[5], p[6], p[7],
                                              1, p[8], p[9], ct.byref(big), None) == -1
+
+
+def test_state_major_flag(L):
+    """MSSM_FLAG_BC_STATE_MAJOR is accepted by the forward scans and the
+    backward (validation passes up to the workspace check) and refused by the
+    decode step; the workspace does not depend on it."""
+    import ctypes as ct
+    from selective_state_space_52_amd._lib import Plan, MSSM_FLAG_BC_STATE_MAJOR as F
+    a, b = Plan(), Plan()
+    assert L.mssm_selective_scan_fwd_plan(ct.byref(_dims(4, 5120, 16, 2048)), ct.byref(a)) == 0
+    assert L.mssm_selective_scan_fwd_plan(ct.byref(_dims(4, 5120, 16, 2048, flags=F)),
+                                          ct.byref(b)) == 0
+    assert a.workspace_bytes == b.workspace_bytes and a.segments == b.segments
+    n = ct.c_int64(0)
+    assert L.mssm_workspace_size(2, ct.byref(_dims(flags=F | 2)), 0, ct.byref(n)) == 0
+    # validation with the flag set still catches bad arguments first (no
+    # call here reaches a launch)
+    assert _fwd(L, _dims(flags=F | 1), u=None) == -1
+    assert _fwd(L, _dims(flags=F | 8)) == -3
+    assert _bwd(L, _dims(flags=F | 1)) == -3          # no load-state flag in the backward
+    assert _bwd(L, _dims(flags=F), dB=None) == -1

@@ -111,3 +111,47 @@ def test_decode_groups(io, batch, dim, N, G):
                                  D=par["D"], z=tok["z"], dt_bias=par["dt_bias"])
     _report("groups decode %s" % ((io, batch, dim, N, G),), check_out(out.cpu(), ro, io, "out"))
     check_state(state.cpu(), rs, "state")
+
+
+@pytest.mark.parametrize("groups", [1, 2])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_state_major_bc_layout(io, groups):
+    """B and C given state-major, (batch, [G,] N, L), give bit for bit the
+    token-major call's forward outputs and final state, and the backward's
+    gradients with dB and dC in the state-major layout; both against the
+    oracle."""
+    import oracle
+    import selective_state_space_52_amd as m
+    s = W.spec("mamba130m_layer", io=io, batch=2, dim=128 * groups, seqlen=300, seed=61 + groups)
+    inp = W.make_scan_inputs(s)
+    if groups > 1:
+        inp.update(W.make_group_bc(s, groups))
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    if groups > 1:
+        Bs = d["B"].permute(0, 2, 3, 1).contiguous()    # (batch, G, N, L)
+        Cs = d["C"].permute(0, 2, 3, 1).contiguous()
+    else:
+        Bs = d["B"].transpose(1, 2).contiguous()        # (batch, N, L)
+        Cs = d["C"].transpose(1, 2).contiguous()
+    outs = {}
+    for lay, Bx, Cx in (("token", d["B"], d["C"]), ("state", Bs, Cs)):
+        last = torch.empty(s.batch, s.dim, s.dstate, device=DEV)
+        o = m.selective_scan_fwd(d["u"], d["delta"], d["A"], Bx, Cx, D=d["D"], z=d["z"],
+                                 delta_bias=d["delta_bias"], last_state=last,
+                                 bc_layout=lay)
+        g = m.selective_scan_bwd(d["u"], d["delta"], d["A"], Bx, Cx, d["u"], D=d["D"],
+                                 z=d["z"], delta_bias=d["delta_bias"], bc_layout=lay)
+        torch.cuda.synchronize()
+        outs[lay] = (o.cpu(), last.cpu(), {k: v.cpu() for k, v in g.items() if v is not None})
+    (o_t, l_t, g_t), (o_s, l_s, g_s) = outs["token"], outs["state"]
+    assert torch.equal(o_t, o_s) and torch.equal(l_t, l_s)
+    for k in g_t:
+        if k in ("dB", "dC"):
+            back = g_s[k].permute(0, 3, 1, 2) if groups > 1 else g_s[k].transpose(1, 2)
+            assert torch.equal(g_t[k], back.contiguous()), k
+        else:
+            assert torch.equal(g_t[k], g_s[k]), k
+    ro, rl = oracle.scan(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"],
+                         z=inp["z"], delta_bias=inp["delta_bias"])
+    check_out(o_s, ro, io, "state-major out")
+    check_state(l_s, rl, "state-major last_state")
