@@ -97,6 +97,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--rocprof-summary", default=None)
+    ap.add_argument("--call-breakdown", default=None, metavar="KERNEL_TRACE_DIR",
+                    help="per-call timeline of the 2.8B-shaped forward calls in a "
+                         "rocprofv3 kernel trace (B/C pack, gap, scan launch)")
     ap.add_argument("--traffic-record", nargs=4, default=None,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     return ap.parse_args()
@@ -271,6 +274,9 @@ def main():
     args = parse()
     if args.rocprof_summary:
         rocprof_summary(args.rocprof_summary)
+        return
+    if args.call_breakdown:
+        call_breakdown(args.call_breakdown)
         return
     if args.traffic_record:
         traffic_record(args.workload, args.time_segments, *args.traffic_record)
@@ -986,6 +992,42 @@ def load_mamba2_traffic():
 def _kname(name: str) -> str:
     """Kernel name without its parameter list."""
     return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+
+
+def call_breakdown(d, scan_prefix="mssm::fwd::scan_kernel<16, 8, true, true, true, true, false>"):
+    """Per-call timeline of back-to-back forward calls of one workload in a
+    rocprofv3 kernel trace: each B/C pack followed directly by that call's
+    scan launch on the same stream.  Prints the pack's duration, the gap from
+    the pack's end to the scan's start, the scan's duration, and the gap from
+    the scan's end to the next call's pack (the host keeps the queue fed when
+    that gap is a launch latency), in microseconds."""
+    import sqlite3
+    rows = []
+    for db in glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True):
+        c = sqlite3.connect(db)
+        rows += c.execute("select name, start, end, stream_id from kernels "
+                          "order by start").fetchall()
+    calls = []
+    for i in range(len(rows) - 1):
+        a, b = rows[i], rows[i + 1]
+        if "fwd::bc_pack_kernel" in a[0] and _kname(b[0]).startswith(scan_prefix) and a[3] == b[3]:
+            calls.append((a, b))
+    if not calls:
+        raise RuntimeError("no pack + scan pairs of %s in %s" % (scan_prefix, d))
+    pack = [(a[2] - a[1]) / 1e3 for a, b in calls]
+    gap = [(b[1] - a[2]) / 1e3 for a, b in calls]
+    scan = [(b[2] - b[1]) / 1e3 for a, b in calls]
+    # gaps to the next call's pack, for calls followed directly by another
+    nxt = []
+    for (a, b), (a2, _) in zip(calls, calls[1:]):
+        if a2[1] > b[2]:
+            nxt.append((a2[1] - b[2]) / 1e3)
+    med = lambda v: sorted(v)[len(v) // 2]
+    print("calls %d" % len(calls))
+    for lab, v in (("pack_us", pack), ("pack_to_scan_gap_us", gap), ("scan_us", scan),
+                   ("scan_to_next_pack_gap_us", nxt)):
+        if v:
+            print("%-26s median %8.2f  min %8.2f  max %8.2f" % (lab, med(v), min(v), max(v)))
 
 
 def rocprof_summary(d):
