@@ -511,8 +511,12 @@ __device__ __forceinline__ void scan_body(
 // so that the dispatcher spreads them over the CUs, one each, ahead of the
 // shorter split work; a main task only ever waits for aggregates, which are
 // ahead of it in dispatch order and wait for nothing.
+//
+// The work plan counts on two workgroups per CU (16 waves, 4 per SIMD), so
+// the kernel is held to 128 VGPRs.  At N = 128 that moves a few values of the
+// fp64 fold in the prologue to scratch, once per task; the tile loop fits.
 template <int N, int NG, bool BF16, bool VEC, bool HAS_Z, bool SOFTPLUS, bool CONV>
-__global__ void __launch_bounds__(kLanes* NG)
+__global__ void __launch_bounds__(kLanes* NG) __attribute__((amdgpu_waves_per_eu(4)))
     scan_kernel(const void* __restrict__ u, const void* __restrict__ delta,
                 const void* __restrict__ z, const float* __restrict__ A,
                 const float* __restrict__ Dv, const float* __restrict__ bias,
