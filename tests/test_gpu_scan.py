@@ -89,8 +89,9 @@ def test_optional_operands(io, var):
 
 @pytest.mark.parametrize("L,ts", [(1000, 2), (1000, 3), (999, 7), (2048, 5), (200, 9)])
 def test_forced_time_segments(L, ts):
-    """Rows cut into time segments joined by the carried state (aggregate,
-    combine and main passes) give the oracle's result."""
+    """Rows cut into time segments joined by the carried state (aggregate
+    tasks publish each segment's summary, later segments fold them into
+    their entering state) give the oracle's result."""
     inp = _inputs("mamba130m_layer", batch=2, dim=72, seqlen=L, seed=L + ts)
     h0 = W.make_initial_state(W.spec("mamba130m_layer", batch=2, dim=72))
     out, last = gpu_scan(inp, h0=h0, time_segments=ts)
@@ -145,8 +146,8 @@ def test_determinism():
 @pytest.mark.parametrize("name", ["mamba130m_layer", "mamba2p8b_layer"])
 def test_full_size_every_element(name):
     """Full-size layer workloads in the launch configuration the bench times
-    (at the 2.8B-shaped layer on 256 CUs: 256 whole channel groups on the
-    caller's stream and 64 groups cut into time segments on the side stream),
+    (at the 2.8B-shaped layer on 256 CUs: 256 whole channel groups and 64
+    groups cut into time segments, all in one launch),
     every output and every final state against the oracle; then a second and
     a third call must reproduce the first bit for bit."""
     import selective_state_space_52_amd as m
@@ -167,18 +168,19 @@ def test_full_size_every_element(name):
         assert torch.equal(o2, out) and torch.equal(l2, last), "repeat %d differs" % (k + 1)
 
 
-def test_two_stream_plan_small():
+def test_split_plan_small():
     """A shape small enough for the oracle in a second that still takes the
-    bench's two-stream plan: 5 x 3328 channels = 260 groups of 64, so on 256
-    CUs 256 groups run whole on the caller's stream and 4 are cut into time
-    segments (aggregate, combine and main pass on the side stream).  Every
-    element against the oracle, a loaded initial state, and repeat calls bit
-    for bit."""
+    bench's kind of plan: 5 x 3328 channels = 260 groups of 64, so on 256
+    CUs 256 groups run whole and 4 are cut into time segments whose
+    aggregates publish summaries that the later segments wait for, in the
+    same launch.  Every element against the oracle, a loaded initial state
+    (read by the first aggregate and the first segment), and repeat calls
+    bit for bit."""
     import selective_state_space_52_amd as m
     batch, dim, N, L = 5, 3328, 16, 1024
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     plan = m.scan_plan(batch, dim, N, L)
-    print("two-stream plan on %d CUs: %s" % (cus, plan), flush=True)
+    print("split plan on %d CUs: %s" % (cus, plan), flush=True)
     if cus == 256:
         assert plan["whole_groups"] == 256 and plan["split_groups"] == 4
         assert plan["segments"] >= 2
@@ -187,7 +189,7 @@ def test_two_stream_plan_small():
     h0 = W.make_initial_state(s)
     out, last = gpu_scan(inp, h0=h0)
     ro, rl = oracle_scan(inp, h0=h0.double().numpy())
-    _report("two-stream plan every element", check_out(out, ro, "bf16", "out"))
+    _report("split plan every element", check_out(out, ro, "bf16", "out"))
     check_state(last, rl, "last_state")
     for k in range(3):
         o2, l2 = gpu_scan(inp, h0=h0)

@@ -2,8 +2,7 @@
 the C ABI: its outputs against those of the caller-workspace forward,
 mssm_selective_scan_fwd_ws, on the same inputs, for two calls in a row (the
 second smaller), to the parity bar -- and bit for bit, since both run the same
-kernels on the same work split (the allocation-free call keeps the split rows'
-chain on the caller's stream)."""
+kernels on the same work split."""
 import ctypes
 
 import pytest
@@ -39,7 +38,7 @@ def _run(entry, d, s, io):
     return out.cpu(), last.cpu()
 
 
-# first a shape whose split rows run a chain of three launches (260 channel
+# first a shape whose plan cuts rows in time (260 channel
 # groups on 256 CUs), then a smaller one on the element-load path
 CASES = [("bf16", 5, 3328, 16, 1024), ("f32", 2, 96, 16, 300)]
 
