@@ -82,9 +82,13 @@ struct alignas(16) Smem {
   uint16_t Bt[N][kQP];       // the same, [n][t]
   uint16_t C[kQ][NP];        // C_t[n], [t][n]
   uint16_t Xt[kP][kQP];      // x_t[p], [p][t]
+  uint16_t Zt[kP][kQP];      // z_t[p], [p][t]
+  uint16_t Yo[kQ][kP + 8];   // the chunk's outputs, [t][p], staged for 16-byte stores
   uint16_t Xw[2][kP][kQP];   // x_t[p] w_t, hi / lo, [p][t]
   uint16_t M[2][kQ][kQP];    // (L o C B^T)[t][s], hi / lo
-  uint16_t H[2][kP][NP];     // state entering the chunk, hi / lo, [p][n]
+  // the entering state's part of Y, C H^T, one partial per n half of the
+  // state, in the MFMA result layout: [n half][t block][p block][v / 4][lane]
+  float4 Yp[2][2][2][4][64];
   double cum[kQ];            // inclusive sum of a over the chunk
   float delta[kQ], ecum[kQ], w[kQ];
   float dec_end;             // exp(cum_end)
@@ -173,10 +177,9 @@ __global__ void __launch_bounds__(kThreads)
   const int64_t srow = ((int64_t)b * s.H + h) * kP;  // first state row of the head
 
   // state waves: the state is held transposed, tiles of rows n = nbase +
-  // 32 i + acc_row and cols p = 32 pb + col, so each group of 4 registers of
-  // a lane is 4 consecutive n of one channel p: one 8-byte LDS write per
-  // group and half.  The entering state is the caller's (whole pairs), zero
-  // (aggregate tasks) or the segment's entering state (split pairs).
+  // 32 i + acc_row and cols p = 32 pb + col.  The entering state is the
+  // caller's (whole pairs), zero (aggregate tasks) or the segment's entering
+  // state (split pairs).
   const float* h_in = split ? ws.hin + ((int64_t)sp * s.P + seg) * seg_elems
                             : (s.load_state && !agg ? state + srow * N : nullptr);
   f32x16 hacc[NT];
@@ -187,23 +190,6 @@ __global__ void __launch_bounds__(kThreads)
       hacc[i][v] = (!ywave && h_in)
                        ? h_in[(32 * pb + col) * N + nbase + 32 * i + acc_row(v, lane)]
                        : 0.0f;
-  auto state_to_lds = [&]() {
-    const int p = 32 * pb + col;
-#pragma unroll
-    for (int i = 0; i < NT; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = nbase + 32 * i + acc_row(4 * q, lane);  // .. n + 3
-        const float v0 = hacc[i][4 * q], v1 = hacc[i][4 * q + 1];
-        const float v2 = hacc[i][4 * q + 2], v3 = hacc[i][4 * q + 3];
-        const uint32_t h01 = pack_bf16x2(v0, v1), h23 = pack_bf16x2(v2, v3);
-        const uint32_t l01 = pack_bf16x2(v0 - bf16_lo(h01), v1 - bf16_hi(h01));
-        const uint32_t l23 = pack_bf16x2(v2 - bf16_lo(h23), v3 - bf16_hi(h23));
-        *reinterpret_cast<uint2*>(&sm.H[0][p][n]) = make_uint2(h01, h23);
-        *reinterpret_cast<uint2*>(&sm.H[1][p][n]) = make_uint2(l01, l23);
-      }
-  };
-  if (!ywave) state_to_lds();
   // The block of M above the diagonal (t block 0, s block 1) is zero in every
   // chunk, and no other step writes it: it is cleared once here.
   if (ywave && pb > tb) {
@@ -216,34 +202,33 @@ __global__ void __launch_bounds__(kThreads)
 
   // Inputs of a chunk, loaded into registers one chunk ahead.  Lane = step t
   // of the chunk (consecutive lanes write consecutive LDS addresses of the
-  // transposed tiles); wave wv takes the 16-byte pieces wv, wv + 8, ... of a
-  // row.
-  constexpr int kBPer = N / 8 / 8;   // pieces of a B (or C) row per wave
-  uint4 rb[kBPer], rc[kBPer], rx;
+  // transposed tiles).  The output waves load x and z (16-byte pieces 2 wv
+  // and 2 wv + 1 of a row, and dt in wave 0) at the start of phase 2; the
+  // state waves load B and C (pieces r, r + 4, ... for state wave r), which
+  // every head of a batch shares and mostly finds in L2, at the end of
+  // phase 3.  Issued all at one point, the CU's loads queued behind each
+  // other for thousands of cycles.
+  constexpr int kBPer = N / 8 / 4;   // pieces of a B (or C) row per state wave
+  uint4 rb[kBPer], rc[kBPer], rx[2], rz[2];
   uint16_t rdt = 0;
-  uint16_t zr[16], zn[16];
-  auto load_chunk_inputs = [&](int t0) {
-    // steps past the task's end load its last step (clamped address) and
-    // are zeroed when written to LDS
+  // steps past the task's end load its last step (clamped address) and are
+  // zeroed when written to LDS
+  auto load_xz = [&](int t0) {
+    const int t = min(t0 + lane, t_end - 1);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      rx[k] = *reinterpret_cast<const uint4*>(xb + t * HP + (2 * wv + k) * 8);
+      if constexpr (HAS_Z) rz[k] = *reinterpret_cast<const uint4*>(zb + t * HP + (2 * wv + k) * 8);
+    }
+    if (wv == 0) rdt = db[t * s.H];
+  };
+  auto load_bc = [&](int t0) {
     const int t = min(t0 + lane, t_end - 1);
 #pragma unroll
     for (int k = 0; k < kBPer; ++k) {
-      const int off = t * GN + (wv + 8 * k) * 8;
+      const int off = t * GN + (r4 + 4 * k) * 8;
       rb[k] = *reinterpret_cast<const uint4*>(Bb + off);
       rc[k] = *reinterpret_cast<const uint4*>(Cb + off);
-    }
-    rx = *reinterpret_cast<const uint4*>(xb + t * HP + wv * 8);
-    if (wv == 0) rdt = db[t * s.H];
-    if constexpr (HAS_Z) {
-      if (ywave) {
-        // unconditional loads from a clamped step (a branch per load made
-        // the compiler wait for each one); steps past L are never stored
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int tz = min(t0 + 32 * tb + acc_row(v, lane), t_end - 1);
-          zn[v] = zb[tz * HP + 32 * pb + col];
-        }
-      }
     }
   };
   auto put_t = [](uint16_t (*dst)[kQP], int r0, int t, uint4 v) {  // dst[r0 + j][t]
@@ -257,7 +242,10 @@ __global__ void __launch_bounds__(kThreads)
 
   const int chunks = (t_end - t_begin + kQ - 1) / kQ;
   double seg_sum = 0.0;  // aggregate tasks: sum of Delta A over the segment
-  load_chunk_inputs(t_begin);
+  if (ywave)
+    load_xz(t_begin);
+  else
+    load_bc(t_begin);
   for (int c = 0; c < chunks; ++c) {
     const int t0 = t_begin + c * kQ;
     // ---- phase 1: the chunk's inputs into LDS
@@ -284,25 +272,28 @@ __global__ void __launch_bounds__(kThreads)
     }
     const bool live = t0 + lane < t_end;
     const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+    if (ywave) {
 #pragma unroll
-    for (int k = 0; k < kBPer; ++k) {
-      const int n8 = (wv + 8 * k) * 8;
-      const uint4 vb = live ? rb[k] : zero4, vc = live ? rc[k] : zero4;
-      *reinterpret_cast<uint4*>(&sm.B[lane][n8]) = vb;
-      *reinterpret_cast<uint4*>(&sm.C[lane][n8]) = vc;
-      put_t(sm.Bt, n8, lane, vb);
-    }
-    put_t(sm.Xt, wv * 8, lane, live ? rx : zero4);
-    if constexpr (HAS_Z) {
+      for (int k = 0; k < 2; ++k) {
+        put_t(sm.Xt, (2 * wv + k) * 8, lane, live ? rx[k] : zero4);
+        if constexpr (HAS_Z) put_t(sm.Zt, (2 * wv + k) * 8, lane, live ? rz[k] : zero4);
+      }
+    } else {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) zr[v] = zn[v];
+      for (int k = 0; k < kBPer; ++k) {
+        const int n8 = (r4 + 4 * k) * 8;
+        const uint4 vb = live ? rb[k] : zero4, vc = live ? rc[k] : zero4;
+        *reinterpret_cast<uint4*>(&sm.B[lane][n8]) = vb;
+        *reinterpret_cast<uint4*>(&sm.C[lane][n8]) = vc;
+        put_t(sm.Bt, n8, lane, vb);
+      }
     }
     __syncthreads();
-    if (c + 1 < chunks) load_chunk_inputs(t0 + kQ);  // lands during phases 2 and 3
+    if (ywave && c + 1 < chunks) load_xz(t0 + kQ);  // lands during phases 2 and 3
 
     f32x16 ya = {}, yb = {};  // output waves: Y, as hi and lo partial sums
     if (ywave && emit) {
-      // ---- phase 2 (output): L o C B^T, and the entering state's part of Y
+      // ---- phase 2 (output): L o C B^T
       if (pb <= tb) {  // the block above the diagonal is all zero
         f32x16 g0 = {}, g1 = {};
 #pragma unroll
@@ -325,20 +316,6 @@ __global__ void __launch_bounds__(kThreads)
               sc <= t ? (g0[v] + g1[v]) * hw_exp2((float)(ct[v] - cs) * kLog2e) * ds : 0.0f;
           split_hl(m, sm.M[0][t][sc], sm.M[1][t][sc]);
         }
-      }
-#pragma unroll
-      for (int k0 = 0; k0 < N; k0 += 16) {
-        const bf16x8 a = lds8(&sm.C[32 * tb + col][k0 + kq]);
-        ya = mfma(a, lds8(&sm.H[0][32 * pb + col][k0 + kq]), ya);
-        yb = mfma(a, lds8(&sm.H[1][32 * pb + col][k0 + kq]), yb);
-      }
-      float ec[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) ec[v] = sm.ecum[32 * tb + acc_row(v, lane)];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        ya[v] = (ya[v] + yb[v]) * ec[v];
-        yb[v] = 0.0f;
       }
     } else if (!ywave) {
       // ---- phase 2 (state): x o w.  A lane takes 16 consecutive steps of
@@ -369,41 +346,114 @@ __global__ void __launch_bounds__(kThreads)
         *reinterpret_cast<uint4*>(&sm.Xw[h][p][tq]) = make_uint4(src[0], src[1], src[2], src[3]);
         *reinterpret_cast<uint4*>(&sm.Xw[h][p][tq + 8]) = make_uint4(src[4], src[5], src[6], src[7]);
       }
+      if (emit) {
+        // the entering state's part of Y over this wave's n half,
+        // C[t][n] H[p][n] summed over n, taken straight from the state
+        // registers.  Registers 8 q .. 8 q + 7 of tile i hold, in lane half
+        // hl, the states n = 32 i + 16 q + 4 hl + (0..3) and the same + 8:
+        // those are the lane's 8 k values of a 16-deep product, so the C
+        // operand is read in that order (two 8-byte pieces) and the state
+        // enters as hi + lo bf16 halves without a trip through LDS.
+        const int hl4 = 4 * (lane >> 5);
+        bf16x8 bh[NT][2], bl[NT][2];
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            uint32_t hw4[4], lw4[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float v0 = hacc[i][8 * q + 2 * j], v1 = hacc[i][8 * q + 2 * j + 1];
+              hw4[j] = pack_bf16x2(v0, v1);
+              lw4[j] = pack_bf16x2(v0 - bf16_lo(hw4[j]), v1 - bf16_hi(hw4[j]));
+            }
+            bh[i][q] = __builtin_bit_cast(bf16x8, make_uint4(hw4[0], hw4[1], hw4[2], hw4[3]));
+            bl[i][q] = __builtin_bit_cast(bf16x8, make_uint4(lw4[0], lw4[1], lw4[2], lw4[3]));
+          }
+        const int nh = wv >= 6 ? 1 : 0;  // this wave's n half
+#pragma unroll
+        for (int tbk = 0; tbk < 2; ++tbk) {
+          f32x16 acc = {};
+#pragma unroll
+          for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const uint16_t* cp = &sm.C[32 * tbk + col][nbase + 32 * i + 16 * q + hl4];
+              const uint2 c0 = *reinterpret_cast<const uint2*>(cp);
+              const uint2 c1 = *reinterpret_cast<const uint2*>(cp + 8);
+              const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(c0.x, c0.y, c1.x, c1.y));
+              acc = mfma(a, bh[i][q], acc);
+              acc = mfma(a, bl[i][q], acc);
+            }
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            sm.Yp[nh][tbk][pb][q4][lane] =
+                make_float4(acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]);
+        }
+      }
     }
     __syncthreads();
 
     if (ywave && emit) {
-      // ---- phase 3 (output): (L o C B^T) X, the skip, the gate, the store
+      // ---- phase 3 (output): the entering state's part (the state waves'
+      // two partials, decayed to each step), (L o C B^T) X, the skip, the
+      // gate, the store
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 p0 = sm.Yp[0][tb][pb][q4][lane], p1 = sm.Yp[1][tb][pb][q4][lane];
+        const float4 e4 = *reinterpret_cast<const float4*>(&sm.ecum[32 * tb + acc_row(4 * q4, lane)]);
+        ya[4 * q4] = (p0.x + p1.x) * e4.x;
+        ya[4 * q4 + 1] = (p0.y + p1.y) * e4.y;
+        ya[4 * q4 + 2] = (p0.z + p1.z) * e4.z;
+        ya[4 * q4 + 3] = (p0.w + p1.w) * e4.w;
+      }
 #pragma unroll
       for (int k0 = 0; k0 < kQ; k0 += 16) {
         const bf16x8 bx = lds8(&sm.Xt[32 * pb + col][k0 + kq]);
         ya = mfma(lds8(&sm.M[0][32 * tb + col][k0 + kq]), bx, ya);
         yb = mfma(lds8(&sm.M[1][32 * tb + col][k0 + kq]), bx, yb);
       }
-      // x for the D skip: each group of 4 result registers is 4 consecutive
-      // steps of this lane's channel, one 8-byte read
-      uint16_t xs[16];
+      // x for the D skip and z for the gate: each group of 4 result
+      // registers is 4 consecutive steps of this lane's channel, one 8-byte
+      // read each
+      uint16_t xs[16], zs[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint2 x4 = *reinterpret_cast<const uint2*>(
-            &sm.Xt[32 * pb + col][32 * tb + acc_row(4 * q, lane)]);
+        const int t4 = 32 * tb + acc_row(4 * q, lane);
+        const uint2 x4 = *reinterpret_cast<const uint2*>(&sm.Xt[32 * pb + col][t4]);
         xs[4 * q] = (uint16_t)(x4.x & 0xffffu);
         xs[4 * q + 1] = (uint16_t)(x4.x >> 16);
         xs[4 * q + 2] = (uint16_t)(x4.y & 0xffffu);
         xs[4 * q + 3] = (uint16_t)(x4.y >> 16);
-      }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int t = 32 * tb + acc_row(v, lane), p = 32 * pb + col;
-        if (t0 + t < t_end) {
-          float y = fmaf(Dh, bf16_bits(xs[v]), ya[v] + yb[v]);
-          if constexpr (HAS_Z) y *= silu_f32(bf16_bits(zr[v]));
-          ob[(t0 + t) * HP + p] = to_bf16(y);
+        if constexpr (HAS_Z) {
+          const uint2 z4 = *reinterpret_cast<const uint2*>(&sm.Zt[32 * pb + col][t4]);
+          zs[4 * q] = (uint16_t)(z4.x & 0xffffu);
+          zs[4 * q + 1] = (uint16_t)(z4.x >> 16);
+          zs[4 * q + 2] = (uint16_t)(z4.y & 0xffffu);
+          zs[4 * q + 3] = (uint16_t)(z4.y >> 16);
         }
       }
+      // the wave's 32 x 32 tile of outputs goes through LDS so that it
+      // leaves as 16-byte pieces (8 channels of one step) rather than 2-byte
+      // stores; only this wave touches its tile of Yo
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float y = fmaf(Dh, bf16_bits(xs[v]), ya[v] + yb[v]);
+        if constexpr (HAS_Z) y *= silu_f32(bf16_bits(zs[v]));
+        sm.Yo[32 * tb + acc_row(v, lane)][32 * pb + col] = to_bf16(y);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int piece = lane + 64 * k;          // 128 pieces: 32 steps x 4
+        const int t = 32 * tb + (piece >> 2), p = 32 * pb + 8 * (piece & 3);
+        const uint4 v = *reinterpret_cast<const uint4*>(&sm.Yo[t][p]);
+        if (t0 + t < t_end) *reinterpret_cast<uint4*>(ob + (t0 + t) * HP + p) = v;
+      }
     } else if (!ywave) {
-      // ---- phase 3 (state): H^T = exp(cum_end) H^T + B^T (X o w); then the
-      // new state into LDS (the output waves read the old one in phase 2)
+      // ---- phase 3 (state): H^T = exp(cum_end) H^T + B^T (X o w)
       const float dec = sm.dec_end;
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
@@ -419,8 +469,8 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
         for (int v = 0; v < 16; ++v) hacc[i][v] += lo[v];
       }
-      state_to_lds();
     }
+    if (!ywave && c + 1 < chunks) load_bc(t0 + kQ);  // lands during the barrier wait
     __syncthreads();
   }
 
