@@ -371,25 +371,31 @@ __global__ void __launch_bounds__(kThreads)
             bl[i][q] = __builtin_bit_cast(bf16x8, make_uint4(lw4[0], lw4[1], lw4[2], lw4[3]));
           }
         const int nh = wv >= 6 ? 1 : 0;  // this wave's n half
+        // both t blocks at once: two independent accumulator chains
+        f32x16 acc[2] = {};
 #pragma unroll
-        for (int tbk = 0; tbk < 2; ++tbk) {
-          f32x16 acc = {};
+        for (int i = 0; i < NT; ++i)
 #pragma unroll
-          for (int i = 0; i < NT; ++i)
+          for (int q = 0; q < 2; ++q) {
+            bf16x8 a[2];
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
+            for (int tbk = 0; tbk < 2; ++tbk) {
               const uint16_t* cp = &sm.C[32 * tbk + col][nbase + 32 * i + 16 * q + hl4];
               const uint2 c0 = *reinterpret_cast<const uint2*>(cp);
               const uint2 c1 = *reinterpret_cast<const uint2*>(cp + 8);
-              const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(c0.x, c0.y, c1.x, c1.y));
-              acc = mfma(a, bh[i][q], acc);
-              acc = mfma(a, bl[i][q], acc);
+              a[tbk] = __builtin_bit_cast(bf16x8, make_uint4(c0.x, c0.y, c1.x, c1.y));
             }
+            acc[0] = mfma(a[0], bh[i][q], acc[0]);
+            acc[1] = mfma(a[1], bh[i][q], acc[1]);
+            acc[0] = mfma(a[0], bl[i][q], acc[0]);
+            acc[1] = mfma(a[1], bl[i][q], acc[1]);
+          }
+#pragma unroll
+        for (int tbk = 0; tbk < 2; ++tbk)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4)
-            sm.Yp[nh][tbk][pb][q4][lane] =
-                make_float4(acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]);
-        }
+            sm.Yp[nh][tbk][pb][q4][lane] = make_float4(acc[tbk][4 * q4], acc[tbk][4 * q4 + 1],
+                                                       acc[tbk][4 * q4 + 2], acc[tbk][4 * q4 + 3]);
       }
     }
     __syncthreads();

@@ -332,13 +332,14 @@ __global__ void __launch_bounds__(256)
 }
 
 // ---------------------------------------------------------------- pass R ---
-template <int NG>
+template <int N, int NG>
 struct alignas(16) BwdSmem {
   float2 dw[kT][kLanes];                // (Delta, Delta*u) of the tile
   float dy[kT][kLanes];                 // dout * silu(z)
   float y[NG][kT][kLanes];              // per-wave partial readouts
   float2 s[NG][kT][kLanes];             // per-wave (sum g B, sum A g e h_prev)
   float red[NG][kRedItems][kRedPitch];  // per-wave channel-sum transpose
+  float dbc[kT][2 * N];                 // the tile's channel sums of dB, dC
 };
 
 template <int N, int NG, bool BF16, bool VEC, bool HAS_Z>
@@ -364,7 +365,7 @@ __global__ void __launch_bounds__(kLanes* NG)
   constexpr int RS = kRedItems / (2 * NPW);  // timesteps per channel reduction
   static_assert(T % KB == 0 && KB % RS == 0, "tile, batch and reduction nest");
   using Batch = BCBatch<NPW, BF16>;
-  __shared__ BwdSmem<NG> sm;
+  __shared__ BwdSmem<N, NG> sm;
 
   const int lane = threadIdx.x & (kLanes - 1);
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -513,8 +514,7 @@ __global__ void __launch_bounds__(kLanes* NG)
         const int j = kk % NPW;
         const int q = (kk / NPW) & 1;
         const int ii = kk / (2 * NPW);
-        const int64_t t_abs = tb + pend_t + ii;
-        ws_dbc[((int64_t)k.gi * Lp + t_abs) * (2 * N) + q * N + n0 + j] = tot;
+        sm.dbc[pend_t + ii][q * N + n0 + j] = tot;
       }
     };
 #pragma unroll
@@ -553,6 +553,15 @@ __global__ void __launch_bounds__(kLanes* NG)
     }
     take_sums();
     __syncthreads();
+
+    // the tile's dB, dC sums are one contiguous block of the workspace:
+    // stored as 8-byte pieces from LDS (scattered 4-byte stores from the
+    // reduction lanes kept the CU's store queue full)
+    {
+      float2* dst = reinterpret_cast<float2*>(ws_dbc + ((int64_t)k.gi * Lp + tb) * (2 * N));
+      const float2* src = reinterpret_cast<const float2*>(&sm.dbc[0][0]);
+      for (int idx = threadIdx.x; idx < T * N; idx += kLanes * NG) dst[idx] = src[idx];
+    }
 
     // output phase: this wave's chunk of the tile
     {
