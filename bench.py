@@ -696,11 +696,11 @@ def bench_decode(torch, W, m, dev, steps):
     # 256 MB Infinity Cache holds): the rate from HBM
     states = [par["state"].to(dev) for _ in range(4)]
 
-    def run_rot(n):
+    def run_rot(n, stream=False):
         for i in range(n):
             t = toks[i % len(toks)]
             m.selective_state_update(states[i % 4], t["x"], t["dt"], A, t["B"], t["C"],
-                                     D=D, z=t["z"], dt_bias=bias, out=out)
+                                     D=D, z=t["z"], dt_bias=bias, out=out, stream_state=stream)
     run_rot(8)
     torch.cuda.synchronize()
     e0.record()
@@ -708,6 +708,15 @@ def bench_decode(torch, W, m, dev, steps):
     e1.record()
     torch.cuda.synchronize()
     ms_rot = e0.elapsed_time(e1) / steps
+    # the same with the state streamed (non-temporal loads and stores, the
+    # caller's hint for states that do not stay in the caches between steps)
+    run_rot(8, True)
+    torch.cuda.synchronize()
+    e0.record()
+    run_rot(steps, True)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_rot_nt = e0.elapsed_time(e1) / steps
     # The same rotating loop as one captured HIP graph of 64 steps, replayed:
     # the host enqueues one graph launch per 64 steps instead of 64 calls.
     G = 64
@@ -734,6 +743,10 @@ def bench_decode(torch, W, m, dev, steps):
                                   "hbm_gb_per_s": round(nb / (ms_rot * 1e-3) / 1e9, 1),
                                   "pct_hbm_peak": round(100 * nb / (ms_rot * 1e-3) / 1e9 /
                                                         HBM_PEAK_GBS, 2)},
+            "rotating_4_states_stream_hint": {
+                "ms_per_step": round(ms_rot_nt, 5),
+                "hbm_gb_per_s": round(nb / (ms_rot_nt * 1e-3) / 1e9, 1),
+                "pct_hbm_peak": round(100 * nb / (ms_rot_nt * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)},
             "rotating_4_states_graph": {
                 "ms_per_step": round(ms_graph, 5), "steps_per_graph": G,
                 "hbm_gb_per_s": round(nb / (ms_graph * 1e-3) / 1e9, 1),

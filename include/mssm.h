@@ -103,6 +103,14 @@ enum {
  * writes dB and dC in the same layout.  Accepted by the forward scans and the
  * backward; the results do not depend on the layout. */
 #define MSSM_FLAG_BC_STATE_MAJOR 4u
+/* Decode step only: the state is read and written with non-temporal
+ * (streaming) hints.  For callers whose states do not stay in the GPU's
+ * caches from one step to the next -- many layers, or more sequences than
+ * the caches hold -- this keeps the state traffic from evicting other data
+ * and streams it at a higher rate.  A state that is reused from the cache
+ * (one layer's state, resident in the 256 MB Infinity Cache) is faster
+ * without it.  The results do not depend on it. */
+#define MSSM_FLAG_STATE_STREAM 8u
 
 typedef struct {
   int64_t batch;       /* >= 1                                              */
@@ -276,7 +284,8 @@ int mssm_mamba2_scan_fwd(const void* x, const void* dt, const float* A, const vo
  *   B, C        : (batch, dstate) io dtype
  *   A           : (dim, dstate) fp32;  D, dt_bias : (dim) fp32 or NULL
  *   out         : (batch, dim) io dtype, must not overlap any input or state
- * dims->seqlen must be 1; time_segments and flags must be 0.
+ * dims->seqlen must be 1 and time_segments 0; flags is 0 or
+ * MSSM_FLAG_STATE_STREAM.
  */
 int mssm_selective_state_update(float* state, const void* x, const void* dt,
                                 const float* A, const void* B, const void* C,

@@ -19,7 +19,7 @@ import torch
 import ctypes
 
 from ._lib import (MSSM_BF16, MSSM_F32, MSSM_FLAG_BC_STATE_MAJOR, MSSM_FLAG_LAYOUT_BLD,
-                   MSSM_FLAG_LOAD_STATE,
+                   MSSM_FLAG_LOAD_STATE, MSSM_FLAG_STATE_STREAM,
                    MSSM_OP_MAMBA2_FWD, MSSM_OP_SCAN_BWD, MSSM_OP_SCAN_FWD,
                    MSSM_OP_SCAN_FWD_CONV, Dims, MssmError, Plan, check, lib)
 
@@ -337,10 +337,13 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None,
 
 
 def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
-                           softplus=True, out=None):
+                           softplus=True, out=None, stream_state=False):
     """Single-token decode step; `state` (batch, dim, N) fp32 is updated in place.
 
     x, dt, z: (batch, dim); B, C: (batch, N), all fp32 or all bf16.
+    stream_state: read and write the state with non-temporal hints
+    (MSSM_FLAG_STATE_STREAM), for states that do not stay in the GPU's caches
+    between steps; same results.
     Returns out (batch, dim) in the io dtype.
     """
     if x.dtype not in _IO:
@@ -361,7 +364,7 @@ def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
     if out is None:
         out = torch.empty((batch, dim), dtype=io, device=dev)
     _need(out, "out", io, (batch, dim), dev)
-    dims = Dims(batch, dim, N, 1, _IO[io], 0, 0, G)
+    dims = Dims(batch, dim, N, 1, _IO[io], MSSM_FLAG_STATE_STREAM if stream_state else 0, 0, G)
     with torch.cuda.device(dev):
         check(lib().mssm_selective_state_update(
             _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),

@@ -12,6 +12,7 @@ MSSM_BF16 = 1
 MSSM_FLAG_LOAD_STATE = 1
 MSSM_FLAG_LAYOUT_BLD = 2
 MSSM_FLAG_BC_STATE_MAJOR = 4
+MSSM_FLAG_STATE_STREAM = 8
 
 STATUS = {
     0: "MSSM_OK", -1: "MSSM_ERR_NULL", -2: "MSSM_ERR_DIMS",

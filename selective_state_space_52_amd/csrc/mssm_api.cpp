@@ -655,7 +655,7 @@ int mssm_selective_state_update(float* state, const void* x, const void* dt,
                                 const mssm_dims* dims, void* stream) {
   int rc = check_common_dims(dims);
   if (rc != MSSM_OK) return rc;
-  if (dims->flags != 0) return MSSM_ERR_UNSUPPORTED;
+  if (dims->flags & ~MSSM_FLAG_STATE_STREAM) return MSSM_ERR_UNSUPPORTED;
   if (dims->seqlen != 1 || dims->time_segments != 0) return MSSM_ERR_DIMS;
   if (!state || !x || !dt || !A || !B || !C || !out) return MSSM_ERR_NULL;
   const int64_t batch = dims->batch, dim = dims->dim, N = dims->dstate;
@@ -688,6 +688,7 @@ int mssm_selective_state_update(float* state, const void* x, const void* dt,
   p.D = D; p.bias = dt_bias; p.out = out;
   p.batch = batch; p.dim = dim; p.softplus = softplus ? 1 : 0;
   p.ngroups = (int32_t)G;
+  p.stream_state = (dims->flags & MSSM_FLAG_STATE_STREAM) ? 1 : 0;
   hipError_t e = mssm::launch_state_update(p, (int)N, io == 2,
                                            (hipStream_t)stream);
   if (e != hipSuccess) {

@@ -88,6 +88,7 @@ struct UpdateParams {
   int64_t batch, dim;
   int32_t softplus;
   int32_t ngroups;        // B, C are (batch, ngroups, N)
+  int32_t stream_state;   // the state with non-temporal loads and stores
 };
 
 // One backward-scan call.  Gradients of sum(dout * out) + sum(dlast *

@@ -70,7 +70,38 @@ constexpr int kBlock = 256;
 
 // Idx: uint32_t when every row, state and B/C index fits in 31 bits (the
 // common case: cheap division by the channel count), else int64_t.
-template <int N, bool BF16, bool VEC, bool HAS_Z, typename Idx>
+// The state's loads and stores, with non-temporal (streaming) hints when NT.
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __forceinline__ float4 state_load4(const float* p) {
+  if constexpr (NT) {
+    const f32x4v v = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+  } else {
+    return *reinterpret_cast<const float4*>(p);
+  }
+}
+template <bool NT>
+__device__ __forceinline__ void state_store4(float* p, float a, float b, float c, float d) {
+  if constexpr (NT) {
+    const f32x4v v = {a, b, c, d};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4v*>(p));
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+  }
+}
+template <bool NT>
+__device__ __forceinline__ float state_load1(const float* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void state_store1(float* p, float v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+template <int N, bool BF16, bool VEC, bool HAS_Z, bool NT, typename Idx>
 __global__ void __launch_bounds__(kBlock)
     state_update_kernel(float* __restrict__ state, const void* __restrict__ x,
                         const void* __restrict__ dt,
@@ -120,7 +151,7 @@ __global__ void __launch_bounds__(kBlock)
     if constexpr (VEC_STATE) {
 #pragma unroll
       for (int q = 0; q < NPL / 4; ++q) {
-        const float4 hv = reinterpret_cast<const float4*>(sp)[q];
+        const float4 hv = state_load4<NT>(sp + 4 * q);
         const float4 av = reinterpret_cast<const float4*>(ap)[q];
         h[it][4 * q] = hv.x; h[it][4 * q + 1] = hv.y; h[it][4 * q + 2] = hv.z; h[it][4 * q + 3] = hv.w;
         a[it][4 * q] = av.x; a[it][4 * q + 1] = av.y; a[it][4 * q + 2] = av.z; a[it][4 * q + 3] = av.w;
@@ -128,7 +159,7 @@ __global__ void __launch_bounds__(kBlock)
     } else {
 #pragma unroll
       for (int n = 0; n < NPL; ++n) {
-        h[it][n] = sp[n];
+        h[it][n] = state_load1<NT>(sp + n);
         a[it][n] = ap[n];
       }
     }
@@ -179,11 +210,11 @@ __global__ void __launch_bounds__(kBlock)
     if constexpr (VEC_STATE) {
 #pragma unroll
       for (int q = 0; q < NPL / 4; ++q)
-        reinterpret_cast<float4*>(sp)[q] =
-            make_float4(h[it][4 * q], h[it][4 * q + 1], h[it][4 * q + 2], h[it][4 * q + 3]);
+        state_store4<NT>(sp + 4 * q, h[it][4 * q], h[it][4 * q + 1], h[it][4 * q + 2],
+                         h[it][4 * q + 3]);
     } else {
 #pragma unroll
-      for (int n = 0; n < NPL; ++n) sp[n] = h[it][n];
+      for (int n = 0; n < NPL; ++n) state_store1<NT>(sp + n, h[it][n]);
     }
     if (n0[it] == 0) {
       if constexpr (BF16)
@@ -201,14 +232,18 @@ hipError_t launch_u(const UpdateParams& p, hipStream_t stream) {
   const int64_t threads = p.batch * p.dim * kLanesPerRow<N>;
   const int64_t per_block = (int64_t)kBlock * kItems;
   const dim3 grid((unsigned)((threads + per_block - 1) / per_block));
-  if (p.z)
-    hipLaunchKernelGGL((state_update_kernel<N, BF16, VEC, true, Idx>), grid,
-                       dim3(kBlock), 0, stream, p.state, p.x, p.dt, p.z, p.A,
-                       p.B, p.C, p.D, p.bias, p.out, s);
-  else
-    hipLaunchKernelGGL((state_update_kernel<N, BF16, VEC, false, Idx>), grid,
-                       dim3(kBlock), 0, stream, p.state, p.x, p.dt, p.z, p.A,
-                       p.B, p.C, p.D, p.bias, p.out, s);
+#define MSSM_UPDATE_LAUNCH(Z, NT)                                                 \
+  hipLaunchKernelGGL((state_update_kernel<N, BF16, VEC, Z, NT, Idx>), grid, dim3(kBlock), \
+                     0, stream, p.state, p.x, p.dt, p.z, p.A, p.B, p.C, p.D, p.bias,  \
+                     p.out, s)
+  if (p.z) {
+    if (p.stream_state) MSSM_UPDATE_LAUNCH(true, true);
+    else MSSM_UPDATE_LAUNCH(true, false);
+  } else {
+    if (p.stream_state) MSSM_UPDATE_LAUNCH(false, true);
+    else MSSM_UPDATE_LAUNCH(false, false);
+  }
+#undef MSSM_UPDATE_LAUNCH
   return hipGetLastError();
 }
 

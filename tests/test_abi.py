@@ -190,7 +190,12 @@ def test_update_validation_codes(L):
                                              q["bias"], 1, q["out"],
                                              ctypes.byref(dims), None)
     assert upd(Dims(4, 64, 16, 2, 1, 0, 0, 0)) == -2      # seqlen must be 1
-    assert upd(Dims(4, 64, 16, 1, 1, 1, 0, 0)) == -3      # no flags
+    assert upd(Dims(4, 64, 16, 1, 1, 1, 0, 0)) == -3      # no scan flags
+    assert upd(Dims(4, 64, 16, 1, 1, 16, 0, 0)) == -3     # unknown flag
+    assert upd(Dims(4, 64, 16, 1, 1, 8 | 1, 0, 0)) == -3
+    # the streaming hint passes the flag check; validation goes on
+    assert upd(Dims(4, 64, 16, 1, 1, 8, 0, 0), state=None) == -1
+    assert upd(Dims(4, 64, 16, 1, 1, 8, 0, 0), out=p[1]) == -5
     assert upd(Dims(4, 64, 16, 1, 1, 0, 3, 0)) == -2      # no segments
     assert upd(Dims(4, 64, 12, 1, 1, 0, 0, 0)) == -3
     assert upd(Dims(4, 64, 16, 1, 1, 0, 0, 0), state=None) == -1

@@ -218,3 +218,36 @@ def test_decode_graph_replays_match_eager():
                                  z=t["z"], dt_bias=bias)
         torch.cuda.synchronize()
     del graph
+
+
+@pytest.mark.parametrize("io,batch,dim,N", [("bf16", 3, 200, 16), ("f32", 2, 70, 4),
+                                             ("bf16", 2, 66, 128), ("f32", 5, 33, 8)])
+def test_decode_stream_state_hint(io, batch, dim, N):
+    """The streaming hint (MSSM_FLAG_STATE_STREAM: non-temporal loads and
+    stores of the state) gives the same bits as the default, step after step,
+    and both match the oracle."""
+    import oracle
+    import selective_state_space_52_amd as m
+    s = W.spec("decode", io=io, batch=batch, dim=dim, dstate=N, tokens=4, seed=61)
+    par = W.make_decode_params(s)
+    toks = [W.make_decode_token(s, k) for k in range(s.tokens)]
+    dtoks = [{k: to_dev(v) for k, v in t.items()} for t in toks]
+    A, D, bias = to_dev(par["A"]), to_dev(par["D"]), to_dev(par["dt_bias"])
+    st_a = to_dev(par["state"]).clone()
+    st_b = to_dev(par["state"]).clone()
+    ref_state = np64(par["state"])
+    print("stream hint %s batch %d dim %d N %d" % (io, batch, dim, N), flush=True)
+    for step in range(6):
+        t, d = toks[step % len(toks)], dtoks[step % len(toks)]
+        oa = m.selective_state_update(st_a, d["x"], d["dt"], A, d["B"], d["C"], D=D,
+                                      z=d["z"], dt_bias=bias)
+        ob = m.selective_state_update(st_b, d["x"], d["dt"], A, d["B"], d["C"], D=D,
+                                      z=d["z"], dt_bias=bias, stream_state=True)
+        ro, ref_state = oracle.state_update(
+            ref_state, t["x"], t["dt"], par["A"], t["B"], t["C"], D=par["D"],
+            z=t["z"], dt_bias=par["dt_bias"], softplus=s.softplus)
+        torch.cuda.synchronize()
+        assert torch.equal(oa.cpu(), ob.cpu()), "step %d out differs" % step
+        assert torch.equal(st_a.cpu(), st_b.cpu()), "step %d state differs" % step
+        check_out(ob.cpu(), ro, io, "decode stream out step %d" % step)
+    check_state(st_b.cpu(), ref_state, "decode stream state")
