@@ -427,10 +427,14 @@ __device__ __forceinline__ void scan_body(
     // comes after the whole prep phase.
     uint32_t touch = 0u;
     if (kWarmScalarCache) {
-      const int64_t last = bc_run_words(s.L, WPS) - 1;  // last word of the run
-      const int64_t f0 = ((int64_t)tb + T) * WPS;
+      // clamped to the row's steps in 32-bit arithmetic (L < 2^31 - 64): a
+      // 64-bit clamp on word indices has no scalar compare and went to the VALU
+      const int left = (int)s.L - (tb + T);  // steps of the next tile in the row
+      const int tn = min(tb + T, (int)s.L - 1);
+      const int fend = max(min(left, T) * WPS - 1, 0);
+      const uint32_t* __restrict__ nb = bcw + (int64_t)tn * WPS;
 #pragma unroll
-      for (int f = 0; f < T * WPS; f += 16) touch += bcw[min(f0 + f, last)];
+      for (int f = 0; f < T * WPS; f += 16) touch += nb[min(f, fend)];
     }
     __builtin_amdgcn_sched_barrier(0);
 
