@@ -259,3 +259,35 @@ def test_softplus_relative_accuracy():
         err = np.abs(np64(got).reshape(n) - ref)
         assert (err <= bound).all(), "decode softplus (%s) off at delta=%g" % (
             what, float(x[int(np.argmax(err / bound))]))
+
+
+def test_forward_64bit_element_offsets():
+    """A forward call of more than 2^31 elements (batch 2 x 36864 channels x
+    32768 steps), so row offsets pass 2^31: every step of sampled rows on both
+    sides of element 2^31 -- which are also the first rows of the groups the
+    plan cuts in time -- the first and last rows, against the oracle."""
+    import oracle
+    import selective_state_space_52_amd as m
+    batch, dim, L, N = 2, 36864, 32768, 16
+    assert batch * dim * L > 2 ** 31
+    plan = m.scan_plan(batch, dim, N, L)
+    print("forward 64-bit offsets: batch %d dim %d L %d plan %s" % (batch, dim, L, plan),
+          flush=True)
+    d = W.make_large_scan_inputs(batch, dim, L, N, device=DEV)
+    last = torch.full((batch, dim, N), float("nan"), device=DEV)
+    out = m.selective_scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], D=d["D"],
+                               z=d["z"], delta_bias=d["delta_bias"], last_state=last)
+    torch.cuda.synchronize()
+    r0 = 2 ** 31 // L                     # first row past element 2^31
+    rows = sorted({0, r0 - 65, r0 - 1, r0, r0 + 1, r0 + 63, r0 + 64, r0 + 4000,
+                   batch * dim - 1})
+    for r in rows:
+        b, c = divmod(r, dim)
+        ro, rl = oracle.scan(d["u"][b:b + 1, c:c + 1].cpu(), d["delta"][b:b + 1, c:c + 1].cpu(),
+                             d["A"][c:c + 1].cpu(), d["B"][b:b + 1].cpu(), d["C"][b:b + 1].cpu(),
+                             D=d["D"][c:c + 1].cpu(), z=d["z"][b:b + 1, c:c + 1].cpu(),
+                             delta_bias=d["delta_bias"][c:c + 1].cpu(), softplus=True)
+        check_out(out[b:b + 1, c:c + 1].cpu(), ro, "bf16", "row %d out" % r)
+        check_state(last[b:b + 1, c:c + 1].cpu(), rl, "row %d last_state" % r)
+    del d, out, last
+    torch.cuda.empty_cache()

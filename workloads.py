@@ -274,6 +274,28 @@ def make_large_decode_step(batch: int, dim: int, dstate: int, seed: int = 31,
                 dt_bias=torch.from_numpy(bias).to(device))
 
 
+def make_large_scan_inputs(batch: int, dim: int, seqlen: int, dstate: int = 16,
+                           seed: int = 33, device="cuda") -> dict:
+    """bf16 u, delta, z (batch, dim, L) and B, C (batch, L, N) ~ N(0, 1) drawn
+    directly on `device` (for sizes too large to draw on the host), one batch
+    entry at a time, with A, D and delta_bias as for the other workloads."""
+    A, D, bias = _params(np.random.default_rng(seed), dim, dstate)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = {}
+    for name in ("u", "delta", "z"):
+        t = torch.empty(batch, dim, seqlen, dtype=torch.bfloat16, device=device)
+        for b in range(batch):
+            t[b] = torch.randn(dim, seqlen, generator=g, device=device, dtype=torch.float32)
+        out[name] = t
+    for name in ("B", "C"):
+        out[name] = torch.randn(batch, seqlen, dstate, generator=g, device=device,
+                                dtype=torch.float32).to(torch.bfloat16)
+    out.update(A=torch.from_numpy(A).to(device), D=torch.from_numpy(D).to(device),
+               delta_bias=torch.from_numpy(bias).to(device))
+    return out
+
+
 def make_decode_token(s: DecodeSpec, k: int) -> dict:
     """Token k of the ring: io-dtype x, dt (raw), z (batch, dim) and B, C
     (batch, N)."""
