@@ -193,3 +193,34 @@ def test_bwd_full_size(name):
     """The layer shapes at full size: every gradient against the oracle."""
     s, inp, gr = _case(name)
     check_all(gpu_bwd(inp, gr), oracle_bwd(inp, gr), s.io, "full %s" % name)
+
+
+def test_backward_64bit_element_offsets():
+    """A backward call of more than 2^31 elements (batch 2 x 36864 channels x
+    32768 steps): for channels whose rows lie on both sides of element 2^31,
+    du, ddelta and dz of both rows and dA, dD, ddelta_bias of the channel
+    against the oracle on those two rows (the channel's gradients need no
+    other channel; dB and dC sum over all channels and are not checked here)."""
+    import oracle
+    import selective_state_space_52_amd as m
+    batch, dim, L, N = 2, 36864, 32768, 16
+    assert batch * dim * L > 2 ** 31
+    print("backward 64-bit offsets: batch %d dim %d L %d" % (batch, dim, L), flush=True)
+    d = W.make_large_scan_inputs(batch, dim, L, N, seed=35, device=DEV)
+    dout = W.make_large_scan_dout(batch, dim, L, device=DEV)
+    g = m.selective_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], dout, D=d["D"],
+                             z=d["z"], delta_bias=d["delta_bias"], softplus=True)
+    torch.cuda.synchronize()
+    r0 = 2 ** 31 // L - dim               # channel of the first row past element 2^31
+    for c in sorted({0, r0 - 1, r0, r0 + 1, dim - 1}):
+        sl = slice(c, c + 1)
+        ref = oracle.scan_bwd(d["u"][:, sl].cpu(), d["delta"][:, sl].cpu(), d["A"][sl].cpu(),
+                              d["B"].cpu(), d["C"].cpu(), dout[:, sl].cpu(), D=d["D"][sl].cpu(),
+                              z=d["z"][:, sl].cpu(), delta_bias=d["delta_bias"][sl].cpu(),
+                              softplus=True)
+        for k in ("du", "ddelta", "dz"):
+            check_grad(g[k][:, sl].cpu(), ref[k], "bf16", "channel %d %s" % (c, k), k)
+        for k in ("dA", "dD", "ddelta_bias"):
+            check_grad(g[k][sl].cpu(), ref[k], "bf16", "channel %d %s" % (c, k), k)
+    del d, dout, g
+    torch.cuda.empty_cache()

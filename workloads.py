@@ -296,6 +296,18 @@ def make_large_scan_inputs(batch: int, dim: int, seqlen: int, dstate: int = 16,
     return out
 
 
+def make_large_scan_dout(batch: int, dim: int, seqlen: int, seed: int = 34,
+                         device="cuda") -> torch.Tensor:
+    """bf16 incoming gradient dout (batch, dim, L) ~ N(0, 1), drawn on `device`
+    one batch entry at a time."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    t = torch.empty(batch, dim, seqlen, dtype=torch.bfloat16, device=device)
+    for b in range(batch):
+        t[b] = torch.randn(dim, seqlen, generator=g, device=device, dtype=torch.float32)
+    return t
+
+
 def make_decode_token(s: DecodeSpec, k: int) -> dict:
     """Token k of the ring: io-dtype x, dt (raw), z (batch, dim) and B, C
     (batch, N)."""
