@@ -138,3 +138,28 @@ def test_fused_full_size_every_element():
     _, ro, rl = _oracle_fused(inp, cp)
     _report("fused full size every element", check_out(out, ro, "bf16", "out"))
     check_state(last, rl, "last_state")
+
+
+def test_conv_64bit_element_offsets():
+    """The standalone conv on more than 2^31 elements (batch 2 x 36864 x
+    32768): rows on both sides of element 2^31, and the first and last rows,
+    against the oracle."""
+    import oracle
+    import selective_state_space_52_amd as m
+    batch, dim, L = 2, 36864, 32768
+    assert batch * dim * L > 2 ** 31
+    print("conv 64-bit offsets: batch %d dim %d L %d" % (batch, dim, L), flush=True)
+    x = W.make_large_scan_inputs(batch, dim, L, device=DEV)["u"]
+    cp = W.make_conv_params(W.spec("mamba130m_layer", batch=batch, dim=dim, seqlen=L, seed=37))
+    w, bias, init = (to_dev(cp["weight"]), to_dev(cp["bias"]), to_dev(cp["init"]))
+    out = m.causal_conv1d_fwd(x, w, bias=bias, init=init, silu=True)
+    torch.cuda.synchronize()
+    r0 = 2 ** 31 // L
+    for r in sorted({0, r0 - 1, r0, r0 + 1, batch * dim - 1}):
+        b, c = divmod(r, dim)
+        ref = oracle.causal_conv1d(x[b:b + 1, c:c + 1].cpu(), cp["weight"][c:c + 1],
+                                   bias=cp["bias"][c:c + 1], init=cp["init"][b:b + 1, c:c + 1],
+                                   silu=True)
+        check_out(out[b:b + 1, c:c + 1].cpu(), ref, "bf16", "conv row %d" % r)
+    del x, out
+    torch.cuda.empty_cache()

@@ -152,3 +152,31 @@ def test_mamba2_full_size_sampled_heads():
                 check_out(out[b:b + 1, :, h:h + 1], ro, "bf16", "out b%d h%d" % (b, h)))
         check_state(last[b:b + 1, h * P:(h + 1) * P], rl, "state b%d h%d" % (b, h))
     assert torch.isfinite(out.float()).all()
+
+
+def test_mamba2_64bit_element_offsets():
+    """A Mamba-2 scan of more than 2^31 elements per tensor (batch 8 x L 32768
+    x 160 heads x 64 channels): every step of (batch, head) pairs whose
+    elements lie on both sides of element 2^31 (batch entry 6), and of the
+    first and last pairs, against the oracle on each pair alone."""
+    import oracle
+    import selective_state_space_52_amd as m
+    batch, L, H, P, N = 8, 32768, 160, 64, 128
+    assert batch * L * H * P > 2 ** 31
+    print("Mamba-2 64-bit offsets: batch %d L %d heads %d" % (batch, L, H), flush=True)
+    d = W.make_large_mamba2_inputs(batch, L, H, P, N, device=DEV)
+    last = torch.full((batch, H * P, N), float("nan"), device=DEV)
+    out = m.mamba2_scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
+                            dt_bias=d["dt_bias"], softplus=True, last_state=last)
+    torch.cuda.synchronize()
+    b6 = 2 ** 31 // (L * H * P)
+    for b, h in [(0, 0), (b6, 0), (b6, 77), (b6, H - 1), (batch - 1, H - 1)]:
+        hs = slice(h, h + 1)
+        ro, rl = oracle.mamba2_scan(d["x"][b:b + 1, :, hs].cpu(), d["dt"][b:b + 1, :, hs].cpu(),
+                                    d["A"][hs].cpu(), d["B"][b:b + 1].cpu(), d["C"][b:b + 1].cpu(),
+                                    D=d["D"][hs].cpu(), z=d["z"][b:b + 1, :, hs].cpu(),
+                                    dt_bias=d["dt_bias"][hs].cpu(), softplus=True)
+        check_out(out[b:b + 1, :, hs].cpu(), ro, "bf16", "pair (%d, %d) out" % (b, h))
+        check_state(last[b:b + 1, h * P:(h + 1) * P].cpu(), rl, "pair (%d, %d) state" % (b, h))
+    del d, out, last
+    torch.cuda.empty_cache()

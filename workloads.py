@@ -308,6 +308,32 @@ def make_large_scan_dout(batch: int, dim: int, seqlen: int, seed: int = 34,
     return t
 
 
+def make_large_mamba2_inputs(batch: int, seqlen: int, nheads: int, headdim: int = 64,
+                             dstate: int = 128, ngroups: int = 1, seed: int = 36,
+                             device="cuda") -> dict:
+    """The Mamba-2 scan's inputs drawn on `device` (x, z, dt, B, C ~ N(0, 1) in
+    bf16, one batch entry at a time) with the per-head A, D and dt_bias of
+    make_mamba2_inputs drawn on the host."""
+    rng = np.random.default_rng(seed)
+    A = -rng.uniform(1.0, 16.0, nheads).astype(np.float32)
+    D = rng.standard_normal(nheads, dtype=np.float32)
+    log_dt = rng.uniform(math.log(1e-3), math.log(1e-1), size=nheads)
+    bias = np.log(np.expm1(np.exp(log_dt))).astype(np.float32)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def draw(*shape):
+        t = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        for b in range(shape[0]):
+            t[b] = torch.randn(shape[1:], generator=g, device=device, dtype=torch.float32)
+        return t
+    return dict(x=draw(batch, seqlen, nheads, headdim), dt=draw(batch, seqlen, nheads),
+                z=draw(batch, seqlen, nheads, headdim),
+                B=draw(batch, seqlen, ngroups, dstate), C=draw(batch, seqlen, ngroups, dstate),
+                A=torch.from_numpy(A).to(device), D=torch.from_numpy(D).to(device),
+                dt_bias=torch.from_numpy(bias).to(device), softplus=True)
+
+
 def make_decode_token(s: DecodeSpec, k: int) -> dict:
     """Token k of the ring: io-dtype x, dt (raw), z (batch, dim) and B, C
     (batch, N)."""
