@@ -21,8 +21,9 @@
 //     gate, the bf16 round trip) is done once: each wave prepares and emits
 //     32 / NG timesteps of every 32-step tile, sharing (Delta, Delta*u) and
 //     the per-wave partial readouts through LDS;
-//   * B_t and C_t are repacked once per call into fp32 runs per wave, read
-//     with 64-byte scalar loads;
+//   * B_t and C_t are repacked once per call into one run per wave (the
+//     wave's states of every token, in the io dtype), read with 64-byte
+//     scalar loads;
 //   * each lane reads its row's u / delta / z in 8- or 16-byte pieces, one
 //     tile ahead of use, and writes its outputs with the same width.
 // Long rows can be cut into time segments (aggregate tasks, then main tasks
@@ -86,9 +87,10 @@ constexpr int kWaitVmem0 = 0x0F70;
 // h = exp(A * sum_j Delta) h + S_j for j = 1..k-1, in fp64.
 // Aggregate task (AGG = true): scans segment k < P-1 of a split group -- from
 // the initial state for k = 0, from zero otherwise -- writes its end state
-// S_k and its sum of Delta, then publishes them through the segment's flag
-// (each wave's stores are made visible device-wide by a release fence before
-// the workgroup barrier, and the flag is stored with release semantics).
+// S_k and its sum of Delta, then publishes them through the segment's flag:
+// every wave waits for its own stores to complete, the workgroup meets at a
+// barrier, and one thread stores the flag with an agent-scope release (one
+// write-back of the XCD's L2 per aggregate rather than one per wave).
 //
 // A tile of kTile timesteps is done in three phases:
 //   prep   : each wave turns KC = kTile / NG of the tile's timesteps into
