@@ -384,8 +384,12 @@ typedef struct {
                             /* of the state)                                 */
   int32_t kernels;          /* launches per call: the B/C pack and the scan  */
   int64_t workspace_bytes;  /* workspace a call needs (mssm_workspace_size)  */
-  int32_t vector_path;      /* 1 when the 16-byte vector-load path applies   */
-                            /* (needs aligned pointers too)                  */
+  int32_t vector_path;      /* 1 when a vector-load path applies: rows of   */
+                            /* (batch, dim, L) with L % 8 == 0 read in       */
+                            /* 16-byte pieces (pointers 16-byte aligned), or */
+                            /* (batch, L, dim) with dim % 4 == 0 read as 4   */
+                            /* channels of a step (pointers aligned to 4     */
+                            /* values; not for the conv-fed forward)         */
   int32_t reserved;
 } mssm_plan;
 

@@ -188,8 +188,12 @@ int make_plan(const mssm_dims* dims, int cus, mssm_plan* plan) {
   plan->kernels = 2;
   plan->workspace_bytes = ws;
   const int64_t io = dims->io_dtype == MSSM_BF16 ? 2 : 4;
-  plan->vector_path =
-      ((L * io) % 16 == 0 && (L % 8) == 0 && !(dims->flags & MSSM_FLAG_LAYOUT_BLD)) ? 1 : 0;
+  // (batch, dim, L): 8- or 16-byte pieces of a row; (batch, L, dim): 4
+  // adjacent channels of one step per lane
+  if (dims->flags & MSSM_FLAG_LAYOUT_BLD)
+    plan->vector_path = (dims->dim % 4 == 0 && dims->dim * io <= INT32_MAX) ? 1 : 0;
+  else
+    plan->vector_path = ((L * io) % 16 == 0 && (L % 8) == 0) ? 1 : 0;
   return MSSM_OK;
 }
 
@@ -301,9 +305,14 @@ int scan_fwd_entry(const void* u, const void* delta, const float* A,
   rc = make_plan(dims, g_cu_count > 0 ? g_cu_count : kDefaultCUs, &plan);
   if (rc != MSSM_OK) return rc;
 
-  const bool vec = !bld && plan.vector_path && aligned(u, 16) && aligned(delta, 16) &&
-                   aligned(out, 16) && aligned(B, 16) && aligned(C, 16) &&
-                   (!z || aligned(z, 16)) && (!u_out || aligned(u_out, 16));
+  // the (batch, L, dim) vector path reads 4 channels at once and has no conv
+  const size_t qa = 4 * io;
+  const bool vec =
+      bld ? plan.vector_path && !conv_w && aligned(u, qa) && aligned(delta, qa) &&
+                aligned(out, qa) && (!z || aligned(z, qa))
+          : plan.vector_path && aligned(u, 16) && aligned(delta, 16) && aligned(out, 16) &&
+                aligned(B, 16) && aligned(C, 16) && (!z || aligned(z, 16)) &&
+                (!u_out || aligned(u_out, 16));
 
   mssm::ScanParams p;
   std::memset(&p, 0, sizeof(p));

@@ -25,7 +25,9 @@
 //     wave's states of every token, in the io dtype), read with 64-byte
 //     scalar loads;
 //   * each lane reads its row's u / delta / z in 8- or 16-byte pieces, one
-//     tile ahead of use, and writes its outputs with the same width.
+//     tile ahead of use, and writes its outputs with the same width; in the
+//     (batch, length, channel) layout a lane instead takes 4 adjacent
+//     channels of one step in the prep and output phases (kLdQuad).
 // Long rows can be cut into time segments (aggregate tasks, then main tasks
 // that fold the aggregates, in one launch): the recurrence is associative on
 // (decay, offset) pairs, so a segment's effect on the state is
@@ -60,6 +62,20 @@ struct ConvArgs {
 };
 constexpr int kConvK = 4;
 
+// How a lane reaches a tile's u / delta / z / out in the prep and output
+// phases:
+//   kLdElem : one element at a time, any layout, length or alignment;
+//   kLdRow  : (batch, dim, L) rows, L a multiple of 8, 16-byte aligned: 8- or
+//             16-byte pieces of the lane's own row (lane = channel);
+//   kLdQuad : (batch, L, dim), dim a multiple of 4, pointers aligned to 4
+//             values: lane l takes channels 4 (l mod 16) .. +3 of the
+//             workgroup's 64 at step l / 16 (+ 4 r), so one wave load is four
+//             whole steps of the 64 channels, each one contiguous run.
+// The state phase always has one channel per lane; the phases meet in LDS.
+constexpr int kLdElem = 0;
+constexpr int kLdRow = 1;
+constexpr int kLdQuad = 2;
+
 struct ScanShape {
   int64_t dim, L;
   int64_t ts;  // elements between consecutive timesteps of a row: 1, or dim
@@ -79,6 +95,41 @@ constexpr uint32_t kFlagSpinLimit = 1u << 20;
 // s_waitcnt operand waiting for every outstanding vector memory operation of
 // the wave (vmcnt 0; the export and LDS/scalar counters left at their maxima)
 constexpr int kWaitVmem0 = 0x0F70;
+
+// kLdQuad: values 4 r .. 4 r + 3 of a chunk are the lane's 4 channels at its
+// step of round r, read from byte offset off[r] of the lane's quad pointer
+// (8 bytes in bf16, 16 in fp32).
+template <bool BF16, int KC>
+__device__ __forceinline__ void load_quads(Raw<BF16, KC>& r, const char* q,
+                                           const int64_t (&off)[KC / 4]) {
+#pragma unroll
+  for (int i = 0; i < KC / 4; ++i) {
+    if constexpr (BF16) {
+      const uint2 v = *reinterpret_cast<const uint2*>(q + off[i]);
+      r.w[2 * i] = v.x;
+      r.w[2 * i + 1] = v.y;
+    } else {
+      const uint4 v = *reinterpret_cast<const uint4*>(q + off[i]);
+      r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
+    }
+  }
+}
+
+template <bool BF16, int KC>
+__device__ __forceinline__ void store_quads(char* q, const int64_t (&off)[KC / 4],
+                                            const float (&o)[KC], const bool (&ok)[KC / 4]) {
+#pragma unroll
+  for (int i = 0; i < KC / 4; ++i) {
+    if (!ok[i]) continue;
+    if constexpr (BF16)
+      *reinterpret_cast<uint2*>(q + off[i]) =
+          make_uint2(pack_bf16x2(o[4 * i], o[4 * i + 1]), pack_bf16x2(o[4 * i + 2], o[4 * i + 3]));
+    else
+      *reinterpret_cast<uint4*>(q + off[i]) =
+          make_uint4(__float_as_uint(o[4 * i]), __float_as_uint(o[4 * i + 1]),
+                     __float_as_uint(o[4 * i + 2]), __float_as_uint(o[4 * i + 3]));
+  }
+}
 
 // Main task (AGG = false): scans the task's time range from its initial
 // state and writes out (and last_state after the final segment).  A task of
@@ -105,7 +156,7 @@ constexpr int kWaitVmem0 = 0x0F70;
 // timesteps: the first timestep of a batch takes the one wait, then the next
 // batch's B/C scalar loads and Delta/Delta*u LDS reads are issued, and the
 // rest of the batch computes while they are in flight.
-template <int N, int NG, bool BF16, bool VEC, bool HAS_Z, bool AGG, bool SOFTPLUS,
+template <int N, int NG, bool BF16, int LD, bool HAS_Z, bool AGG, bool SOFTPLUS,
           bool CONV>
 __device__ __forceinline__ void scan_body(
     const void* __restrict__ u, const void* __restrict__ delta,
@@ -123,6 +174,10 @@ __device__ __forceinline__ void scan_body(
   constexpr int WPS = BCLayout<NPW, BF16>::kWordsPerStep;
   constexpr int KB = BCLayout<NPW, BF16>::kSteps;  // timesteps per batch
   constexpr int NB = T / KB;     // batches per tile
+  constexpr bool VEC = LD == kLdRow;
+  constexpr bool QUAD = LD == kLdQuad;
+  constexpr int QR = KC / 4;     // kLdQuad: rounds of 4 steps per chunk
+  static_assert(!(QUAD && CONV), "the conv-fed scan has no channel-quad path");
 
   const int lane = threadIdx.x & (kLanes - 1);
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -169,10 +224,25 @@ __device__ __forceinline__ void scan_body(
   // values of the task that nothing uses.
   constexpr bool kRowPtr = VEC && KC <= 8;
   constexpr int64_t kEs = BF16 ? 2 : 4;
-  const char* const pu = static_cast<const char*>(u) + rowoff * kEs;
-  const char* const pdl = static_cast<const char*>(delta) + rowoff * kEs;
-  const char* const pz = HAS_Z ? static_cast<const char*>(z) + rowoff * kEs : nullptr;
-  char* const po = AGG ? nullptr : static_cast<char*>(out) + rowoff * kEs;
+  // kLdQuad: the lane's channels cq .. cq + 3 (all in range or all out, as
+  // dim is a multiple of 4; out of range reads the last 4 channels and stores
+  // nothing), at step qs of each round of 4; steps sit qstride bytes apart
+  const int qs = lane >> 4;
+  const int64_t cq = (int64_t)(gi % s.groups_per_batch) * kLanes + 4 * (lane & 15);
+  const bool qvalid = cq < s.dim;
+  const uint32_t qstride = (uint32_t)(s.dim * kEs);
+  const int64_t poff = QUAD ? b * s.L * s.dim + (qvalid ? cq : s.dim - 4) : rowoff;
+  const char* const pu = static_cast<const char*>(u) + poff * kEs;
+  const char* const pdl = static_cast<const char*>(delta) + poff * kEs;
+  const char* const pz = HAS_Z ? static_cast<const char*>(z) + poff * kEs : nullptr;
+  char* const po = AGG ? nullptr : static_cast<char*>(out) + poff * kEs;
+  // byte offsets of the rounds of the chunk at tc, the steps clamped into the
+  // task (a clamped step re-reads values that nothing uses)
+  auto quad_offsets = [&](int tc, int64_t (&off)[QR]) {
+#pragma unroll
+    for (int i = 0; i < QR; ++i)
+      off[i] = (int64_t)((uint64_t)(uint32_t)min(tc + 4 * i + qs, t_end - 1) * qstride);
+  };
 
   float A2[NPW], h[NPW];
 #pragma unroll
@@ -232,6 +302,19 @@ __device__ __forceinline__ void scan_body(
   const float bv_d = bias ? bias[dc] : 0.0f;
   const float Dd = (!AGG && Dv) ? Dv[dc] : 0.0f;
   double dsum = 0.0;
+  // kLdQuad: bias and D of the lane's 4 channels; the aggregate's sums of
+  // Delta per channel over the lane's steps
+  float bq[4], Dq[4];
+  double dq[4];
+  if constexpr (QUAD) {
+    const int64_t cqc = qvalid ? cq : s.dim - 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bq[j] = bias ? bias[cqc + j] : 0.0f;
+      Dq[j] = (!AGG && Dv) ? Dv[cqc + j] : 0.0f;
+      dq[j] = 0.0;
+    }
+  }
 
   // With CONV, `u` holds the conv input x; each chunk also reads the 4 x
   // values before it (row start: the init values) and turns x into u.
@@ -295,6 +378,28 @@ __device__ __forceinline__ void scan_body(
   // the waves' sums are added at the end.
   auto prep = [&](const Raw<BF16, KC>& pu, const Raw<BF16, KC>& pd, float (&uv)[KC],
                   int tile) {
+    if constexpr (QUAD) {
+      // round i: the lane's 4 channels at tile step k, written as 4
+      // consecutive (Delta, Delta*u) pairs of row k
+#pragma unroll
+      for (int i = 0; i < QR; ++i) {
+        const int k = g * KC + 4 * i + qs;
+        float dl[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x = raw_get(pd, 4 * i + j) + bq[j];
+          dl[j] = SOFTPLUS ? softplus_f32(x) : x;
+          uv[4 * i + j] = raw_get(pu, 4 * i + j);
+          if constexpr (AGG) {
+            if (tile + k < t_end) dq[j] += (double)dl[j];
+          }
+        }
+        float4* dst = reinterpret_cast<float4*>(&s_dw[k][4 * (lane & 15)]);
+        dst[0] = make_float4(dl[0], dl[0] * uv[4 * i], dl[1], dl[1] * uv[4 * i + 1]);
+        dst[1] = make_float4(dl[2], dl[2] * uv[4 * i + 2], dl[3], dl[3] * uv[4 * i + 3]);
+      }
+      return;
+    }
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
       const float x = raw_get(pd, k) + bv_d;
@@ -320,7 +425,14 @@ __device__ __forceinline__ void scan_body(
   };
 
   // prologue: this wave's chunk of the first tile
-  {
+  if constexpr (QUAD) {
+    int64_t off[QR];
+    quad_offsets(t_begin + g * KC, off);
+    load_quads<BF16, KC>(ru, pu, off);
+    load_quads<BF16, KC>(rd, pdl, off);
+    if (HAS_Z && !AGG) load_quads<BF16, KC>(rz, pz, off);
+    prep(ru, rd, uc, t_begin);
+  } else {
     const int tc = t_begin + g * KC;
     const int nv = t_end - tc;
     load_chunk<BF16, VEC, KC>(ru, u, rowoff + tc * s.ts, nv, s.ts);
@@ -336,7 +448,13 @@ __device__ __forceinline__ void scan_body(
 
   for (int tb = t_begin; tb < t_end; tb += T) {
     // prefetch this wave's chunk of the next tile
-    if constexpr (kRowPtr) {
+    if constexpr (QUAD) {
+      int64_t off[QR];
+      quad_offsets(tb + T + g * KC, off);
+      if (HAS_Z && !AGG) load_quads<BF16, KC>(nz, pz, off);
+      load_quads<BF16, KC>(nu, pu, off);
+      load_quads<BF16, KC>(nd, pdl, off);
+    } else if constexpr (kRowPtr) {
       const int tc = tb + T + g * KC;
       const int tl = min(tc, t_end - KC);
       // z first: loads complete in issue order, so the prep's wait for u and
@@ -445,7 +563,33 @@ __device__ __forceinline__ void scan_body(
     if constexpr (CONV) conv_u(nu, np_, un);
     prep(nu, nd, un, tb + T);
 
-    if constexpr (!AGG) {
+    if constexpr (!AGG && QUAD) {
+      // output phase, by channel quads: round i sums the partials of the
+      // lane's 4 channels at tile step k
+      float o[KC];
+      int64_t off[QR];
+      bool ok[QR];
+      quad_offsets(tb + g * KC, off);
+#pragma unroll
+      for (int i = 0; i < QR; ++i) {
+        const int k = g * KC + 4 * i + qs;
+        ok[i] = qvalid && tb + k < t_end;
+        float4 y = *reinterpret_cast<const float4*>(&s_y[0][k][4 * (lane & 15)]);
+#pragma unroll
+        for (int w = 1; w < NG; ++w) {
+          const float4 p = *reinterpret_cast<const float4*>(&s_y[w][k][4 * (lane & 15)]);
+          y.x += p.x; y.y += p.y; y.z += p.z; y.w += p.w;
+        }
+        const float ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float v = fmaf(Dq[j], uc[4 * i + j], ys[j]);
+          if (HAS_Z) v *= silu_f32(raw_get(rz, 4 * i + j));
+          o[4 * i + j] = v;
+        }
+      }
+      store_quads<BF16, KC>(po, off, o, ok);
+    } else if constexpr (!AGG) {
       // output phase: this wave's chunk of the tile
       const int tc = tb + g * KC;
       float o[KC];
@@ -488,13 +632,27 @@ __device__ __forceinline__ void scan_body(
     // the segment's sum of Delta: the waves' sums over their own steps, added
     // in wave order (s_y is free: the loop ended on a barrier)
     double* part = reinterpret_cast<double*>(&s_y[0][0][0]);
-    part[g * kLanes + lane] = dsum;
-    __syncthreads();
-    if (g == 0) {
-      double tot = 0.0;
+    if constexpr (QUAD) {
+      // per (wave, step of the round) and channel: NG * 4 * 64 doubles, within
+      // s_y's NG * 32 * 64 floats
 #pragma unroll
-      for (int w = 0; w < NG; ++w) tot += part[w * kLanes + lane];
-      ws_sum[sr * per + seg] = tot;
+      for (int j = 0; j < 4; ++j) part[(g * 4 + qs) * kLanes + 4 * (lane & 15) + j] = dq[j];
+      __syncthreads();
+      if (g == 0) {
+        double tot = 0.0;
+#pragma unroll
+        for (int w = 0; w < NG * 4; ++w) tot += part[w * kLanes + lane];
+        ws_sum[sr * per + seg] = tot;
+      }
+    } else {
+      part[g * kLanes + lane] = dsum;
+      __syncthreads();
+      if (g == 0) {
+        double tot = 0.0;
+#pragma unroll
+        for (int w = 0; w < NG; ++w) tot += part[w * kLanes + lane];
+        ws_sum[sr * per + seg] = tot;
+      }
     }
     // publish: every wave waits for its own summary stores to complete, then
     // one release (write-back of this XCD's L2) ahead of the flag
@@ -521,7 +679,7 @@ __device__ __forceinline__ void scan_body(
 // The work plan counts on two workgroups per CU (16 waves, 4 per SIMD), so
 // the kernel is held to 128 VGPRs.  At N = 128 that moves a few values of the
 // fp64 fold in the prologue to scratch, once per task; the tile loop fits.
-template <int N, int NG, bool BF16, bool VEC, bool HAS_Z, bool SOFTPLUS, bool CONV>
+template <int N, int NG, bool BF16, int LD, bool HAS_Z, bool SOFTPLUS, bool CONV>
 __global__ void __launch_bounds__(kLanes* NG) __attribute__((amdgpu_waves_per_eu(4)))
     scan_kernel(const void* __restrict__ u, const void* __restrict__ delta,
                 const void* __restrict__ z, const float* __restrict__ A,
@@ -531,48 +689,49 @@ __global__ void __launch_bounds__(kLanes* NG) __attribute__((amdgpu_waves_per_eu
                 float* __restrict__ ws_h0, uint32_t* __restrict__ ws_flags,
                 const uint32_t* __restrict__ bcp, const ScanShape s,
                 const int n_agg, const ConvArgs cv) {
-  __shared__ float2 s_dw[kTile][kLanes];        // (Delta, Delta*u) of a tile
-  __shared__ float s_y[NG][kTile][kLanes];      // per-wave partial readouts
+  // 16-byte aligned: the channel-quad path moves 4 values per lane
+  __shared__ __align__(16) float2 s_dw[kTile][kLanes];    // (Delta, Delta*u) of a tile
+  __shared__ __align__(16) float s_y[NG][kTile][kLanes];  // per-wave partial readouts
   const int blk = blockIdx.x;
   const int a = blk - s.whole_groups;  // aggregate task, when in [0, n_agg)
   if (a >= 0 && a < n_agg)
-    scan_body<N, NG, BF16, VEC, HAS_Z, true, SOFTPLUS, CONV>(
+    scan_body<N, NG, BF16, LD, HAS_Z, true, SOFTPLUS, CONV>(
         u, delta, z, A, Dv, bias, out, last_state, ws_S, ws_sum, ws_h0, ws_flags, bcp,
         s, s_dw, s_y, a, cv);
   else
-    scan_body<N, NG, BF16, VEC, HAS_Z, false, SOFTPLUS, CONV>(
+    scan_body<N, NG, BF16, LD, HAS_Z, false, SOFTPLUS, CONV>(
         u, delta, z, A, Dv, bias, out, last_state, ws_S, ws_sum, ws_h0, ws_flags, bcp,
         s, s_dw, s_y, a < 0 ? blk : blk - n_agg, cv);
 }
 
 
-template <int N, int NG, bool BF16, bool VEC, bool HAS_Z, bool CONV>
+template <int N, int NG, bool BF16, int LD, bool HAS_Z, bool CONV>
 hipError_t launch_one(const ScanParams& p, const ScanShape& s, int n_main, int n_agg,
                       hipStream_t stream) {
   const dim3 grid(n_main + n_agg), block(kLanes * NG);
   const ConvArgs cv{p.conv_w, p.conv_b, p.conv_init, p.u_out};
   if (p.softplus)
-    hipLaunchKernelGGL((scan_kernel<N, NG, BF16, VEC, HAS_Z, true, CONV>), grid, block,
+    hipLaunchKernelGGL((scan_kernel<N, NG, BF16, LD, HAS_Z, true, CONV>), grid, block,
                        0, stream, p.u, p.delta, p.z, p.A, p.D, p.bias, p.out,
                        p.last_state, p.ws_S, p.ws_sum, p.ws_h0, p.ws_flags,
                        (const uint32_t*)p.ws_bc, s, n_agg, cv);
   else
-    hipLaunchKernelGGL((scan_kernel<N, NG, BF16, VEC, HAS_Z, false, CONV>), grid, block,
+    hipLaunchKernelGGL((scan_kernel<N, NG, BF16, LD, HAS_Z, false, CONV>), grid, block,
                        0, stream, p.u, p.delta, p.z, p.A, p.D, p.bias, p.out,
                        p.last_state, p.ws_S, p.ws_sum, p.ws_h0, p.ws_flags,
                        (const uint32_t*)p.ws_bc, s, n_agg, cv);
   return hipGetLastError();
 }
 
-template <int N, int NG, bool BF16, bool VEC, bool CONV>
+template <int N, int NG, bool BF16, int LD, bool CONV>
 hipError_t launch_tasks(const ScanParams& p, const ScanShape& s, int n_main, int n_agg,
                         hipStream_t stream) {
   if (p.z)
-    return launch_one<N, NG, BF16, VEC, true, CONV>(p, s, n_main, n_agg, stream);
-  return launch_one<N, NG, BF16, VEC, false, CONV>(p, s, n_main, n_agg, stream);
+    return launch_one<N, NG, BF16, LD, true, CONV>(p, s, n_main, n_agg, stream);
+  return launch_one<N, NG, BF16, LD, false, CONV>(p, s, n_main, n_agg, stream);
 }
 
-template <int N, bool BF16, bool VEC, bool CONV>
+template <int N, bool BF16, int LD, bool CONV>
 hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
   constexpr int NG = kWaves<N>;
   ScanShape s;
@@ -603,19 +762,28 @@ hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
     e = hipEventRecord((hipEvent_t)p.ev_start, stream);
     if (e != hipSuccess) return e;
   }
-  e = launch_tasks<N, NG, BF16, VEC, CONV>(p, s, n_main, n_agg, stream);
+  e = launch_tasks<N, NG, BF16, LD, CONV>(p, s, n_main, n_agg, stream);
   if (e == hipSuccess && p.ev_stop) e = hipEventRecord((hipEvent_t)p.ev_stop, stream);
   return e;
+}
+
+// `vec`: the host found the vector path's conditions met for the call's
+// layout (kLdRow for (batch, dim, L), kLdQuad for (batch, L, dim) without
+// the conv)
+template <int N, bool BF16, bool CONV>
+hipError_t launch_ld(const ScanParams& p, bool vec, hipStream_t stream) {
+  if (vec && !p.layout_bld) return launch_n<N, BF16, kLdRow, CONV>(p, stream);
+  if constexpr (!CONV) {
+    if (vec) return launch_n<N, BF16, kLdQuad, CONV>(p, stream);
+  }
+  return launch_n<N, BF16, kLdElem, CONV>(p, stream);
 }
 
 template <int N, bool CONV>
 hipError_t launch_dtype(const ScanParams& p, bool bf16, bool vec,
                         hipStream_t stream) {
-  if (bf16)
-    return vec ? launch_n<N, true, true, CONV>(p, stream)
-               : launch_n<N, true, false, CONV>(p, stream);
-  return vec ? launch_n<N, false, true, CONV>(p, stream)
-             : launch_n<N, false, false, CONV>(p, stream);
+  return bf16 ? launch_ld<N, true, CONV>(p, vec, stream)
+              : launch_ld<N, false, CONV>(p, vec, stream);
 }
 
 template <int N>

@@ -229,6 +229,14 @@ def test_plan(L):
     assert L.mssm_selective_scan_fwd_plan(
         ctypes.byref(_dims(1, 64, 16, 7)), ctypes.byref(plan)) == 0
     assert plan.vector_path == 0 and plan.segments == 1
+    # (batch, L, dim): the channel-quad path needs dim % 4 == 0, any length
+    from selective_state_space_52_amd._lib import MSSM_FLAG_LAYOUT_BLD
+    assert L.mssm_selective_scan_fwd_plan(
+        ctypes.byref(_dims(1, 68, 16, 7, flags=MSSM_FLAG_LAYOUT_BLD)), ctypes.byref(plan)) == 0
+    assert plan.vector_path == 1
+    assert L.mssm_selective_scan_fwd_plan(
+        ctypes.byref(_dims(1, 70, 16, 64, flags=MSSM_FLAG_LAYOUT_BLD)), ctypes.byref(plan)) == 0
+    assert plan.vector_path == 0
     assert L.mssm_selective_scan_fwd_plan(None, ctypes.byref(plan)) == -1
     assert L.mssm_selective_scan_fwd_plan(ctypes.byref(_dims(N=5)),
                                           ctypes.byref(plan)) == -3

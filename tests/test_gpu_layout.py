@@ -28,11 +28,18 @@ def _report(what, worst):
 
 
 FWD = [
-    # io, batch, dim, N, L, segments
+    # io, batch, dim, N, L, segments.  dim % 4 == 0 takes the channel-quad
+    # vector path (dim 70: one element at a time); a dim that is not a
+    # multiple of 64 leaves out-of-range quads in the last group
     ("bf16", 2, 96, 16, 300, 0),
     ("f32", 1, 70, 16, 77, 0),
     ("bf16", 1, 64, 16, 1000, 3),
     ("bf16", 2, 40, 64, 130, 0),
+    ("f32", 1, 68, 16, 77, 0),
+    ("bf16", 2, 128, 4, 333, 0),
+    ("bf16", 1, 64, 1, 700, 2),
+    ("f32", 2, 72, 8, 96, 3),
+    ("bf16", 1, 100, 128, 70, 0),
 ]
 
 
@@ -56,6 +63,57 @@ def test_forward_bld(io, batch, dim, N, L, P):
                          D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"], h0=h0)
     _report("bld fwd %s" % ((io, batch, dim, N, L, P),), check_out(_bdl(out), ro, io, "out"))
     check_state(last.cpu(), rl, "last_state")
+
+
+# io, batch, dim, N, L, optional operands left out
+SAME = [
+    ("bf16", 2, 128, 16, 256, ()),
+    ("f32", 1, 68, 16, 77, ()),
+    ("bf16", 1, 100, 4, 300, ("z",)),
+    ("bf16", 1, 64, 1, 64, ("D", "delta_bias")),
+    ("f32", 2, 72, 8, 96, ("z", "D", "delta_bias")),
+    ("bf16", 1, 40, 128, 40, ()),
+]
+
+
+@pytest.mark.parametrize("io,batch,dim,N,L,drop", SAME,
+                         ids=["%s-b%d-d%d-n%d-l%d-%s" % (*c[:5], "-".join(c[5]) or "all")
+                              for c in SAME])
+def test_forward_bld_equals_bdl(io, batch, dim, N, L, drop):
+    """Without time segments, the two layouts do the same arithmetic on every
+    element in the same order (only the lanes that load and store differ), so
+    out and last_state are equal bit for bit; so is the (batch, L, dim) call
+    through the one-element-at-a-time path (u offset by one element, so not
+    aligned to 4 values)."""
+    import selective_state_space_52_amd as m
+    s = W.spec("mamba130m_layer", io=io, batch=batch, dim=dim, dstate=N, seqlen=L,
+               seed=950 + L + N)
+    inp = W.make_scan_inputs(s)
+    for k in drop:
+        inp[k] = None
+    dv = {k: (to_dev(v) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    print("bld == bdl %s %s" % ((io, batch, dim, N, L), drop), flush=True)
+
+    def run(layout, u, delta, z):
+        last = torch.full((batch, dim, N), float("nan"), device=DEV)
+        o = m.selective_scan_fwd(u, delta, dv["A"], dv["B"], dv["C"], D=dv["D"], z=z,
+                                 delta_bias=dv["delta_bias"], last_state=last,
+                                 time_segments=1, layout=layout)
+        torch.cuda.synchronize()
+        return o, last.cpu()
+
+    ref, ref_last = run("bdl", dv["u"], dv["delta"], dv["z"])
+    ub, db, zb = _bld(inp["u"]), _bld(inp["delta"]), _bld(inp["z"])
+    got, got_last = run("bld", ub, db, zb)
+    assert torch.equal(_bdl(got), ref.cpu()), "quad path out differs"
+    assert torch.equal(got_last, ref_last), "quad path last_state differs"
+    # the same u one element into a larger buffer: aligned to its element only
+    buf = torch.empty(ub.numel() + 1, dtype=ub.dtype, device=DEV)
+    ue = buf[1:].view(ub.shape)
+    ue.copy_(ub)
+    got, got_last = run("bld", ue, db, zb)
+    assert torch.equal(_bdl(got), ref.cpu()), "element path out differs"
+    assert torch.equal(got_last, ref_last), "element path last_state differs"
 
 
 def test_conv_and_fused_bld():
