@@ -75,6 +75,11 @@ constexpr int kConvK = 4;
 constexpr int kLdElem = 0;
 constexpr int kLdRow = 1;
 constexpr int kLdQuad = 2;
+// With one channel per lane in the output phase (kLdElem, kLdRow), each
+// wave's partial readouts sit in LDS as runs of 4 steps per lane
+// ([wave][step / 4][lane] float4): the state phase writes a run once per 4
+// steps and the output phase reads a wave's 4 steps with one 16-byte access.
+constexpr bool kStepRunsY = true;
 
 struct ScanShape {
   int64_t dim, L;
@@ -178,6 +183,10 @@ __device__ __forceinline__ void scan_body(
   constexpr bool QUAD = LD == kLdQuad;
   constexpr int QR = KC / 4;     // kLdQuad: rounds of 4 steps per chunk
   static_assert(!(QUAD && CONV), "the conv-fed scan has no channel-quad path");
+  constexpr bool Y4 = kStepRunsY && !QUAD;
+  // s_y as runs of 4 steps: s_y4[wave][step / 4][lane]
+  float4 (*const s_y4)[T / 4][kLanes] =
+      reinterpret_cast<float4 (*)[T / 4][kLanes]>(&s_y[0][0][0]);
 
   const int lane = threadIdx.x & (kLanes - 1);
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -486,6 +495,7 @@ __device__ __forceinline__ void scan_body(
     // state phase: every wave advances its NPW states over the whole tile
     const int nt = t_end - tb;
     if (nt >= T) {
+      float yq[4];  // Y4: the readouts of the current run of 4 steps
       float2 dwn[KB];
       Batch bn = *reinterpret_cast<const Batch*>(bcw + (int64_t)tb * WPS);
 #pragma unroll
@@ -526,7 +536,15 @@ __device__ __forceinline__ void scan_body(
             h[j] = fmaf(e[i][j], h[j], bw[i][j]);
             if constexpr (!AGG) y = fmaf(bc_val<NPW, BF16>(bc.w, i, NPW + j), h[j], y);
           }
-          if constexpr (!AGG) s_y[g][kb * KB + i][lane] = y;
+          if constexpr (!AGG) {
+            const int r = kb * KB + i;  // constant once unrolled
+            if constexpr (Y4) {
+              yq[r & 3] = y;
+              if ((r & 3) == 3) s_y4[g][r >> 2][lane] = make_float4(yq[0], yq[1], yq[2], yq[3]);
+            } else {
+              s_y[g][r][lane] = y;
+            }
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -536,7 +554,12 @@ __device__ __forceinline__ void scan_body(
 #pragma unroll
         for (int j = 0; j < WPS; ++j) q[j] = bcw[((int64_t)tb + kk) * WPS + j];
         const float y = advance(s_dw[kk][lane], q, 0);
-        if constexpr (!AGG) s_y[g][kk][lane] = y;
+        if constexpr (!AGG) {
+          if constexpr (Y4)
+            reinterpret_cast<float*>(&s_y4[g][kk >> 2][lane])[kk & 3] = y;
+          else
+            s_y[g][kk][lane] = y;
+        }
       }
     }
     __syncthreads();
@@ -592,13 +615,29 @@ __device__ __forceinline__ void scan_body(
     } else if constexpr (!AGG) {
       // output phase: this wave's chunk of the tile
       const int tc = tb + g * KC;
-      float o[KC];
+      float o[KC], ys[KC];
+      if constexpr (Y4) {
+#pragma unroll
+        for (int q = 0; q < KC / 4; ++q) {
+          float4 v = s_y4[0][g * (KC / 4) + q][lane];
+#pragma unroll
+          for (int w = 1; w < NG; ++w) {
+            const float4 p = s_y4[w][g * (KC / 4) + q][lane];
+            v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
+          }
+          ys[4 * q] = v.x; ys[4 * q + 1] = v.y; ys[4 * q + 2] = v.z; ys[4 * q + 3] = v.w;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+          ys[k] = s_y[0][g * KC + k][lane];
+#pragma unroll
+          for (int w = 1; w < NG; ++w) ys[k] += s_y[w][g * KC + k][lane];
+        }
+      }
 #pragma unroll
       for (int k = 0; k < KC; ++k) {
-        float y = s_y[0][g * KC + k][lane];
-#pragma unroll
-        for (int w = 1; w < NG; ++w) y += s_y[w][g * KC + k][lane];
-        y = fmaf(Dd, uc[k], y);
+        float y = fmaf(Dd, uc[k], ys[k]);
         if (HAS_Z) y *= silu_f32(raw_get(rz, k));
         o[k] = y;
       }
