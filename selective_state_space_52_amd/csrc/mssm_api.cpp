@@ -335,6 +335,7 @@ int scan_fwd_entry(const void* u, const void* delta, const float* A,
   p.u_out = u_out;
   p.layout_bld = bld ? 1 : 0;
   p.bc_state_major = (dims->flags & MSSM_FLAG_BC_STATE_MAJOR) ? 1 : 0;
+  p.cus = g_cu_count > 0 ? g_cu_count : kDefaultCUs;
 
   if (mode == WsMode::kCaller) {
     rc = check_workspace(ws_in, ws_bytes, plan.workspace_bytes);

@@ -59,6 +59,7 @@ struct ScanParams {
   int32_t layout_bld;     // u, delta, z, out, u_out are (batch, L, dim)
   int32_t ngroups;        // B/C groups (B, C are (batch, L, ngroups, N))
   int32_t bc_state_major; // B, C are (batch, ngroups, N, L)
+  int32_t cus;            // compute units of the device (work plan)
 };
 
 // Standalone causal depthwise conv: out = act(bias + sum_k w[k] x[t-K+1+k]).

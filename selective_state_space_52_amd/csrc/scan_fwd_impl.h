@@ -75,11 +75,21 @@ constexpr int kConvK = 4;
 constexpr int kLdElem = 0;
 constexpr int kLdRow = 1;
 constexpr int kLdQuad = 2;
+constexpr int kLdRowStaged = 3;  // kLdRow with the staged output store below
 // With one channel per lane in the output phase (kLdElem, kLdRow), each
 // wave's partial readouts sit in LDS as runs of 4 steps per lane
 // ([wave][step / 4][lane] float4): the state phase writes a run once per 4
 // steps and the output phase reads a wave's 4 steps with one 16-byte access.
 constexpr bool kStepRunsY = true;
+// kLdRowStaged (8 waves): the output phase computes a wave's 4 steps of the
+// 64 channels (lane = channel), stages them in LDS and, after a barrier,
+// stores them as wave g's 8 channels 8 g .. 8 g + 7 over the tile's 32 steps
+// (lane l: channel 8 g + l / 8, steps 4 (l mod 8) ..), so that a store
+// instruction writes 8 rows of 64 contiguous bytes (bf16) rather than 8 bytes
+// of each of 64 rows; the scattered form makes about 6 times as many L2 write
+// requests.  The extra barrier costs more than it saves when a CU holds one
+// workgroup (nothing else runs while its waves meet), so the launch takes
+// this mode only when it has more tasks than the device has CUs.
 
 struct ScanShape {
   int64_t dim, L;
@@ -179,7 +189,7 @@ __device__ __forceinline__ void scan_body(
   constexpr int WPS = BCLayout<NPW, BF16>::kWordsPerStep;
   constexpr int KB = BCLayout<NPW, BF16>::kSteps;  // timesteps per batch
   constexpr int NB = T / KB;     // batches per tile
-  constexpr bool VEC = LD == kLdRow;
+  constexpr bool VEC = LD == kLdRow || LD == kLdRowStaged;
   constexpr bool QUAD = LD == kLdQuad;
   constexpr int QR = KC / 4;     // kLdQuad: rounds of 4 steps per chunk
   static_assert(!(QUAD && CONV), "the conv-fed scan has no channel-quad path");
@@ -232,6 +242,8 @@ __device__ __forceinline__ void scan_body(
   // branch nor 64-bit index work.  A clamped chunk past the end re-reads
   // values of the task that nothing uses.
   constexpr bool kRowPtr = VEC && KC <= 8;
+  constexpr bool STAGE = LD == kLdRowStaged && kRowPtr && !AGG;
+  static_assert(!STAGE || KC == 4, "the staged store takes 4 steps per lane");
   constexpr int64_t kEs = BF16 ? 2 : 4;
   // kLdQuad: the lane's channels cq .. cq + 3 (all in range or all out, as
   // dim is a multiple of 4; out of range reads the last 4 channels and stores
@@ -245,6 +257,19 @@ __device__ __forceinline__ void scan_body(
   const char* const pdl = static_cast<const char*>(delta) + poff * kEs;
   const char* const pz = HAS_Z ? static_cast<const char*>(z) + poff * kEs : nullptr;
   char* const po = AGG ? nullptr : static_cast<char*>(out) + poff * kEs;
+  // STAGE: the staged store's channel and first step for this lane; wave g
+  // stages its outputs in s_y4[g][g] (its own partials of its own steps,
+  // which no other wave reads), at column lane ^ 2 g so that the store's
+  // reads (8 step runs of 8 channels per 16 lanes) spread over the banks
+  const int oa = lane & 7;
+  const int64_t d_o = (int64_t)(gi % s.groups_per_batch) * kLanes + 8 * g + (lane >> 3);
+  const bool valid_o = d_o < s.dim;
+  char* const po_o =
+      STAGE ? static_cast<char*>(out) +
+                  ((b * s.dim + (valid_o ? d_o : s.dim - 1)) * s.L + 4 * oa) * kEs
+            : nullptr;
+  const uint32_t stg_w = (uint32_t)((9 * g * kLanes + (lane ^ (2 * g))) * 16);
+  const uint32_t stg_r = (uint32_t)((9 * oa * kLanes + ((8 * g + (lane >> 3)) ^ (2 * oa))) * 16);
   // byte offsets of the rounds of the chunk at tc, the steps clamped into the
   // task (a clamped step re-reads values that nothing uses)
   auto quad_offsets = [&](int tc, int64_t (&off)[QR]) {
@@ -641,7 +666,19 @@ __device__ __forceinline__ void scan_body(
         if (HAS_Z) y *= silu_f32(raw_get(rz, k));
         o[k] = y;
       }
-      if constexpr (kRowPtr) {
+      if constexpr (STAGE) {
+        char* const lds_y = reinterpret_cast<char*>(&s_y[0][0][0]);
+        *reinterpret_cast<float4*>(lds_y + stg_w) = make_float4(o[0], o[1], o[2], o[3]);
+        __syncthreads();
+        const float4 v = *reinterpret_cast<const float4*>(lds_y + stg_r);
+        const float ov[4] = {v.x, v.y, v.z, v.w};
+        if (valid_o) store_chunk_row<BF16, 4>(po_o, tb, ov, t_end - tb - 4 * oa);
+        if constexpr (CONV) {
+          if (valid && cv.u_out)
+            store_chunk_row<BF16, KC>(static_cast<char*>(cv.u_out) + rowoff * kEs, tc, uc,
+                                      t_end - tc);
+        }
+      } else if constexpr (kRowPtr) {
         if (valid) store_chunk_row<BF16, KC>(po, tc, o, t_end - tc);
         if constexpr (CONV) {
           if (valid && cv.u_out)
@@ -811,7 +848,13 @@ hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
 // the conv)
 template <int N, bool BF16, bool CONV>
 hipError_t launch_ld(const ScanParams& p, bool vec, hipStream_t stream) {
-  if (vec && !p.layout_bld) return launch_n<N, BF16, kLdRow, CONV>(p, stream);
+  if (vec && !p.layout_bld) {
+    if constexpr (kWaves<N> == 8) {
+      const int64_t tasks = (int64_t)p.whole_groups + (int64_t)p.split_groups * (2 * p.segments - 1);
+      if (tasks > p.cus) return launch_n<N, BF16, kLdRowStaged, CONV>(p, stream);
+    }
+    return launch_n<N, BF16, kLdRow, CONV>(p, stream);
+  }
   if constexpr (!CONV) {
     if (vec) return launch_n<N, BF16, kLdQuad, CONV>(p, stream);
   }

@@ -73,6 +73,10 @@ SAME = [
     ("bf16", 1, 64, 1, 64, ("D", "delta_bias")),
     ("f32", 2, 72, 8, 96, ("z", "D", "delta_bias")),
     ("bf16", 1, 40, 128, 40, ()),
+    # more workgroups than CUs: the (batch, dim, L) forward stages its
+    # outputs through LDS before storing them
+    ("bf16", 5, 3328, 16, 64, ()),
+    ("f32", 5, 3328, 16, 40, ("z",)),
 ]
 
 
