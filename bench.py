@@ -30,12 +30,17 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TF = 2500.0     # MI355X dense bf16 matrix peak, TFLOP/s
-CUS, SIMDS, LANES, CLOCK_GHZ = 256, 4, 16, 2.4
-# fp32 VALU issue: one wave64 instruction per SIMD per 4 clocks = 16 lanes/clk
-VALU_PEAK_TSLOTS = CUS * SIMDS * LANES * CLOCK_GHZ / 1e3   # 39.32 T lane-slots/s
-# v_exp_f32 issues at half the fma rate (measured on the MI355X: 26.6 vs 54.8
-# lane-ops per CU per clock), so the chip's exp peak is half the VALU peak
-EXP_PEAK_T = VALU_PEAK_TSLOTS / 2                          # 19.66 T exp/s
+CUS, CLOCK_GHZ = 256, 2.4
+# fp32 VALU issue peak: 128 lanes per CU per clock (MI355X's 157.3 TFLOP/s fp32
+# vector peak counts one fma as 2 flops).  Plain, unpacked v_fma_f32 reaches
+# it only with several waves ready per SIMD: the library's probe measured 44,
+# 83, 93 and 99 fma lanes per CU per clock at 1, 2, 4 and 8 waves per SIMD
+# (bench.py --alu-probe).
+VALU_LANES_PER_CU_CLK = 128
+VALU_PEAK_TSLOTS = CUS * VALU_LANES_PER_CU_CLK * CLOCK_GHZ / 1e3   # 78.64 T lane-slots/s
+# Transcendentals (v_exp_f32, v_log_f32, v_rcp_f32) issue at a quarter of that
+# (the probe: 30 exp lanes per CU per clock at 8 waves per SIMD)
+EXP_PEAK_T = VALU_PEAK_TSLOTS / 4                          # 19.66 T exp/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_main_traffic.json")
 # the sources the forward scan kernel is built from (the traffic record is
 # tied to them)
@@ -44,27 +49,27 @@ KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_52_amd", "csrc", f)
                             "scan_common.h", "dev_math.h")]
 
 # Algorithmic VALU issue slots of the scan (fp32, one lane = one slot; a
-# transcendental occupies two slots because v_exp/v_log/v_rcp issue at half
-# rate).  Per state element: Delta*A (1), exp (2), Delta*u times B (1), the
-# state fma (1), the C readout fma (1).  Per element: delta + bias (1),
-# softplus = exp + log1p (2 + 2 + 3), Delta*u (1), D skip fma (1),
-# silu = exp + reciprocal (2 + 2 + 2), gate multiply (1).
-SLOTS_PER_STATE_ELEM = 6
-SLOTS_PER_ELEM = 18
+# transcendental occupies four slots, as v_exp/v_log/v_rcp issue at a quarter
+# of the fma rate).  Per state element: Delta*A (1), exp (4), Delta*u times B
+# (1), the state fma (1), the C readout fma (1).  Per element: delta + bias
+# (1), softplus = exp + log1p (4 + 4 + 3), Delta*u (1), D skip fma (1),
+# silu = exp + reciprocal (4 + 4 + 2), gate multiply (1), bf16 rounding (1).
+SLOTS_PER_STATE_ELEM = 8
+SLOTS_PER_ELEM = 26
 # The backward, counted the same way for the algorithm itself (one forward
 # sweep keeping h_t, one reverse sweep), not for the kernel's recompute.  Per
-# state element: the forward recurrence (5) and the C readout for dz (1); in
+# state element: the forward recurrence (7) and the C readout for dz (1); in
 # reverse g += dy C, dy h (dC term), g Delta u (dB term), sum g B, g e, (g e)
 # h_prev, sum A (g e h_prev), dA accumulate (8); one add each for the
 # channel sums of dB and dC (2).  Per element: delta + bias (1), softplus
-# (9), sigmoid of delta + bias (6), Delta*u (1), sigmoid of z (6),
+# (13), sigmoid of delta + bias (10), Delta*u (1), sigmoid of z (10),
 # dy = dout z sigmoid(z) (2), dout silu'(z) (4), du (2), dDelta (1), ddelta
 # (1), dz (2), dD and dbias accumulates (2).
-BWD_SLOTS_PER_STATE_ELEM = 16
-BWD_SLOTS_PER_ELEM = 37
+BWD_SLOTS_PER_STATE_ELEM = 18
+BWD_SLOTS_PER_ELEM = 49
 # The width-4 causal conv in the fused path adds per element: 4 fmas and
-# silu = exp + reciprocal (2 + 2) + 3, i.e. 11 slots.
-CONV_SLOTS_PER_ELEM = 11
+# silu = exp + reciprocal (4 + 4) + 3, i.e. 15 slots.
+CONV_SLOTS_PER_ELEM = 15
 
 
 def parse():
@@ -96,6 +101,8 @@ def parse():
     ap.add_argument("--mamba2-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--alu-probe", action="store_true",
+                    help="only the ALU issue-rate probes and the ceiling they give")
     ap.add_argument("--rocprof-summary", default=None)
     ap.add_argument("--call-breakdown", default=None, metavar="KERNEL_TRACE_DIR",
                     help="per-call timeline of the 2.8B-shaped forward calls in a "
@@ -303,6 +310,12 @@ def main():
         print(json.dumps({"mamba2": bench_mamba2(torch, W, m, dev, args.mamba2_steps)}),
               flush=True)
         return
+    if args.alu_probe:
+        s = W.spec(args.workload)
+        print(json.dumps({"alu_probe": alu_probe(torch, m, dev, s, W.scan_bytes(s),
+                                                 sweep=(4, 8, 16, 32))}),
+              flush=True)
+        return
     if args.only_forward:
         # profiling runs: the headline workload's forward calls alone
         over = {"dstate": args.dstate} if args.dstate else {}
@@ -379,6 +392,7 @@ def main():
         "copy_ceiling": copy_ceiling(torch, dev),
         "shader_clock_mhz": clock,
     }
+    res["alu_probe"] = alu_probe(torch, m, dev, s, nbytes * r["share"], r["kernel_ms"])
     res["roofline"]["traffic_per_call"] = traffic_call
     res["roofline"]["frac_of_copy_ceiling"] = round(
         roof["achieved"] / res["copy_ceiling"]["gb_per_s"], 4)
@@ -388,6 +402,68 @@ def main():
         if not args.no_configs:
             res["cpu_baseline"]["single_thread"] = cpu_single_thread(W)
     print(json.dumps(res), flush=True)
+
+
+def probe_rates(torch, m, dev, waves_per_cu, iters=4096, reps=10):
+    """Measured issue rates (per second) of the library's ALU probe kernels
+    at `waves_per_cu` resident waves per CU: fp32 fma (kind 0), v_exp_f32
+    (kind 1) and state elements of the scan's inner-step mix (kind 2)."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = cus * waves_per_cu // 4        # 256-thread workgroups: 4 waves
+    threads = blocks * 256
+    sink = torch.empty(threads, device=dev)
+    rates = {}
+    for kind, per_iter in ((0, 8), (1, 8), (2, 4)):
+        for _ in range(2):
+            m.valu_probe(kind, blocks, iters, sink)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            m.valu_probe(kind, blocks, iters, sink)
+        b.record()
+        torch.cuda.synchronize()
+        rates[kind] = per_iter * iters * threads * reps / (a.elapsed_time(b) * 1e-3)
+    return rates
+
+
+def alu_probe(torch, m, dev, s=None, nbytes=None, kernel_ms=None, sweep=(16, 32)):
+    """Issue rates of the vector ALU measured on this GPU with the library's
+    probe kernels (mssm_valu_probe): fp32 fma alone, v_exp_f32 alone, and the
+    scan's state-element mix (a multiply, an exponential, a multiply, the state
+    fma and the readout fma per state element), at each occupancy in `sweep`
+    (waves per CU; the forward scan runs 16: two 8-wave workgroups).  From the
+    rates at the scan's occupancy, its ALU ceiling for workload `s`: the state
+    elements at the measured mix rate plus the per-element work
+    (SLOTS_PER_ELEM fma slots) at the measured fma rate, and the fraction of
+    that ceiling the scan kernel reaches."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    settle_gpu(torch, dev)
+    res = {"launch": "CUs x waves/4 workgroups of 256 threads, 4096 iterations",
+           "by_waves_per_cu": {}}
+    at = {}
+    for w in sweep:
+        r = probe_rates(torch, m, dev, w)
+        at[w] = r
+        res["by_waves_per_cu"][str(w)] = {
+            "fma_T_per_s": round(r[0] / 1e12, 3), "exp_T_per_s": round(r[1] / 1e12, 3),
+            "state_element_mix_T_per_s": round(r[2] / 1e12, 3),
+            "fma_slots_per_state_element": round(r[0] / r[2], 3)}
+    clock = shader_clock_mhz()
+    res["shader_clock_mhz"] = clock
+    if clock:
+        for w, r in at.items():
+            per_clk = 1.0 / (cus * clock * 1e6)
+            res["by_waves_per_cu"][str(w)]["per_cu_per_clock"] = {
+                "fma": round(r[0] * per_clk, 2), "exp": round(r[1] * per_clk, 2),
+                "state_elements": round(r[2] * per_clk, 2)}
+    if s is not None:
+        r = at[16] if 16 in at else at[max(at)]
+        ceil_s = s.state_elements / r[2] + s.elements * SLOTS_PER_ELEM / r[0]
+        res["scan_ceiling_ms"] = round(ceil_s * 1e3, 5)
+        res["scan_ceiling_frac_of_hbm_peak"] = round(nbytes / ceil_s / 1e9 / HBM_PEAK_GBS, 4)
+        if kernel_ms:
+            res["scan_kernel_frac_of_ceiling"] = round(ceil_s * 1e3 / kernel_ms, 4)
+    return res
 
 
 def bench_other_configs(torch, W, m, dev, hev, args):
@@ -880,7 +956,7 @@ def _counter_mean(d, kernel_substr, counter):
 
 
 # the kernels of one forward call (one B/C pack per call, then one scan launch)
-FWD_KERNELS = ("mssm::fwd::bc_pack_kernel", "mssm::fwd::scan_kernel<")
+FWD_KERNELS = ("mssm::fwd::bc_pack", "mssm::fwd::scan_kernel<")
 
 
 def _library_kernels(d, counter):
@@ -1007,7 +1083,7 @@ def _kname(name: str) -> str:
     return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
 
 
-def call_breakdown(d, scan_prefix="mssm::fwd::scan_kernel<16, 8, true, true, true, true, false>"):
+def call_breakdown(d, scan_prefix="mssm::fwd::scan_kernel<16, 8, true, "):
     """Per-call timeline of back-to-back forward calls of one workload in a
     rocprofv3 kernel trace: each B/C pack followed directly by that call's
     scan launch on the same stream.  Prints the pack's duration, the gap from
@@ -1023,7 +1099,7 @@ def call_breakdown(d, scan_prefix="mssm::fwd::scan_kernel<16, 8, true, true, tru
     calls = []
     for i in range(len(rows) - 1):
         a, b = rows[i], rows[i + 1]
-        if "fwd::bc_pack_kernel" in a[0] and _kname(b[0]).startswith(scan_prefix) and a[3] == b[3]:
+        if "fwd::bc_pack" in a[0] and _kname(b[0]).startswith(scan_prefix) and a[3] == b[3]:
             calls.append((a, b))
     if not calls:
         raise RuntimeError("no pack + scan pairs of %s in %s" % (scan_prefix, d))

@@ -408,6 +408,25 @@ int mssm_selective_scan_fwd_plan(const mssm_dims* dims, mssm_plan* plan);
  */
 int mssm_set_scan_timing_events(void* start, void* stop);
 
+/*
+ * Issue-rate probe of the vector ALU, for the roofline of the scan, which is
+ * bound by its exponentials and fp32 multiply-adds rather than by HBM
+ * (page "What are State Space Models (SSMs)?", Key Features: the selective
+ * scan's hardware-aware algorithm).  Launches `blocks` workgroups of 256
+ * threads on `stream`; each thread runs `iters` iterations of
+ *   kind 0: 8 independent fp32 fma (v_fma_f32),
+ *   kind 1: 8 independent exponentials (v_exp_f32),
+ *   kind 2: 4 state elements of the scan's inner step, each a multiply, an
+ *           exponential, a multiply, an fma and a readout fma (the first a
+ *           multiply), plus 1 multiply per iteration (21 instructions when
+ *           iters is a multiple of 4),
+ * and writes one float per thread to `sink` (device, blocks * 256 floats,
+ * caller-owned; the values carry no meaning).  The caller times the launch
+ * (for instance with events on `stream`).  Errors: MSSM_ERR_NULL (sink),
+ * MSSM_ERR_DIMS (kind outside 0..2, blocks or iters <= 0), MSSM_ERR_HIP.
+ */
+int mssm_valu_probe(int kind, int blocks, int iters, float* sink, void* stream);
+
 /* Static text for a status code. */
 const char* mssm_status_string(int status);
 

@@ -40,6 +40,17 @@ def set_scan_timing_events(start=None, stop=None) -> None:
     check(lib().mssm_set_scan_timing_events(start, stop))
 
 
+def valu_probe(kind: int, blocks: int, iters: int, sink) -> None:
+    """Launch the library's ALU issue-rate probe on the current stream: kind
+    0 = fp32 fma, 1 = exp, 2 = the scan's state-element mix; `sink` is a
+    float32 device tensor of at least blocks * 256 values."""
+    _need(sink, "sink", torch.float32)
+    if sink.numel() < blocks * 256:
+        raise ValueError("sink holds fewer than blocks * 256 values")
+    check(lib().mssm_valu_probe(int(kind), int(blocks), int(iters), _ptr(sink),
+                                _stream(sink.device)))
+
+
 def _ptr(t):
     return None if t is None else t.data_ptr()
 

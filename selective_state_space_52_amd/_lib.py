@@ -33,7 +33,8 @@ EXPORTS = ("mssm_selective_scan_fwd", "mssm_selective_scan_bwd",
            "mssm_status_string", "mssm_last_error", "mssm_abi_version",
            "mssm_selective_scan_fwd_ws", "mssm_selective_scan_fwd_conv_ws",
            "mssm_selective_scan_bwd_ws", "mssm_mamba2_scan_fwd_ws",
-           "mssm_workspace_size", "mssm_selective_scan_fwd_noalloc")
+           "mssm_workspace_size", "mssm_selective_scan_fwd_noalloc",
+           "mssm_valu_probe")
 
 
 class Dims(ctypes.Structure):
@@ -124,6 +125,8 @@ def lib():
         L.mssm_set_scan_timing_events.restype = i
         L.mssm_abi_version.argtypes = []
         L.mssm_abi_version.restype = i
+        L.mssm_valu_probe.argtypes = [i, i, i, vp, vp]
+        L.mssm_valu_probe.restype = i
         _lib = L
     return _lib
 

@@ -22,7 +22,7 @@ ARCH = "gfx950"
 SOURCES = ["scan_fwd.hip", "scan_fwd_n1_8.hip", "scan_fwd_n16.hip",
            "scan_fwd_n32.hip", "scan_fwd_n64.hip", "scan_fwd_n128.hip",
            "scan_bwd.hip", "state_update.hip", "conv1d.hip", "mamba2.hip",
-           "noalloc.hip", "mssm_api.cpp"]
+           "noalloc.hip", "probe.hip", "mssm_api.cpp"]
 
 # Packed fp32 VALU forms are switched off for every device compilation.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -210,6 +210,18 @@ int mssm_set_scan_timing_events(void* start, void* stop) {
   return MSSM_OK;
 }
 
+int mssm_valu_probe(int kind, int blocks, int iters, float* sink, void* stream) {
+  if (sink == nullptr) return MSSM_ERR_NULL;
+  if (blocks <= 0 || iters <= 0 || kind < 0 || kind > 2) return MSSM_ERR_DIMS;
+  const hipError_t e =
+      mssm::launch_valu_probe(kind, blocks, iters, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_hip_error("probe launch", e);
+    return MSSM_ERR_HIP;
+  }
+  return MSSM_OK;
+}
+
 const char* mssm_last_error(void) { return g_last_error; }
 
 const char* mssm_status_string(int status) {

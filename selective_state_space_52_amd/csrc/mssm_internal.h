@@ -178,6 +178,10 @@ int scan_waves_per_group(int N);
 // run; the runs hold bf16 pairs (dst_bf16) or fp32 values.  With
 // state_major, B and C are (batch, groups, N, L) instead.  The same launch
 // zeroes `nflags` words at `flags` (may be 0 / null).
+// ALU issue-rate probe (kind 0: fma, 1: exp, 2: the state-element mix),
+// `blocks` workgroups of 256 threads, one float per thread into sink.
+hipError_t launch_valu_probe(int kind, int blocks, int iters, float* sink,
+                             hipStream_t stream);
 hipError_t launch_bc_pack(const void* B, const void* C, void* packed,
                           int64_t batch, int64_t groups, int64_t L, int64_t steps,
                           int N, int waves, bool src_bf16, bool dst_bf16,

@@ -52,6 +52,55 @@ __global__ void __launch_bounds__(256)
 }
 
 
+// The same runs for bf16 token-major B and C, NPW (even) states per wave:
+// one thread per (run, token), in run-major order, so a wave's stores are
+// one contiguous stretch of a run.  It reads the NPW / 2 words of its wave's
+// states from the token's B row and from its C row and writes them as one
+// piece of NPW words.  32-bit indices (the host checks the sizes); the
+// divisions by the token count and the group count are multiplies by
+// precomputed reciprocals.
+template <int NPW>
+__global__ void __launch_bounds__(256)
+    bc_pack_tokens_kernel(const uint32_t* __restrict__ Bw, const uint32_t* __restrict__ Cw,
+                          uint32_t* __restrict__ packed, uint32_t total, uint32_t steps,
+                          U32Div steps_div, uint32_t L, uint32_t groups, U32Div groups_div,
+                          uint32_t ng_log2, uint32_t run_words, uint32_t* __restrict__ flags,
+                          uint32_t nflags) {
+  static_assert(NPW % 2 == 0 && NPW <= 16, "whole bf16 pairs, at most a 64-byte piece");
+  constexpr int H = NPW / 2;  // words of B (and of C) per wave and token
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nflags) flags[i] = 0u;
+  if (i >= total) return;
+  const uint32_t run = udiv(i, steps_div);
+  const uint32_t t = i - run * steps;
+  const uint32_t g = run & ((1u << ng_log2) - 1u);
+  const uint32_t bgrp = run >> ng_log2;
+  const uint32_t b = udiv(bgrp, groups_div);
+  const uint32_t grp = bgrp - b * groups;
+  const uint32_t ng = 1u << ng_log2;
+  uint32_t v[NPW];
+  if (t < L) {
+    // words of the token's row: (b, t, grp) rows of N = NPW * ng values
+    const uint32_t src = ((b * L + t) * groups + grp) * (H * ng) + g * H;
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      v[j] = Bw[src + j];
+      v[H + j] = Cw[src + j];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) v[j] = 0u;
+  }
+  uint32_t* dst = packed + run * run_words + t * NPW;
+  if constexpr (NPW == 2) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(v[0], v[1]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < NPW; j += 4)
+      *reinterpret_cast<uint4*>(dst + j) = make_uint4(v[j], v[j + 1], v[j + 2], v[j + 3]);
+  }
+}
+
 }  // namespace fwd
 
 hipError_t launch_bc_pack(const void* B, const void* C, void* packed,
@@ -59,6 +108,39 @@ hipError_t launch_bc_pack(const void* B, const void* C, void* packed,
                           int N, int waves, bool src_bf16, bool dst_bf16,
                           int64_t run_words, uint32_t* flags, int64_t nflags,
                           bool state_major, hipStream_t stream) {
+  const int npw = N / waves;
+  const int64_t tokens = batch * groups * steps * waves;  // (run, token) pairs
+  const bool pow2 = waves > 0 && (waves & (waves - 1)) == 0;
+  const bool aligned = ((reinterpret_cast<uintptr_t>(B) | reinterpret_cast<uintptr_t>(C)) % 4 |
+                        reinterpret_cast<uintptr_t>(packed) % 16) == 0;
+  // every index of the tokens kernel below 2^31: the source words, the
+  // packed words and the thread count
+  const int64_t top = std::max({batch * groups * L * N / 2, batch * groups * waves * run_words,
+                                tokens + 256, nflags + 256});
+  if (src_bf16 && dst_bf16 && !state_major && pow2 && aligned && top < (int64_t(1) << 31) &&
+      (npw == 2 || npw == 4 || npw == 8 || npw == 16)) {
+    uint32_t lg = 0;
+    while ((1 << lg) < waves) ++lg;
+    const int64_t threads = std::max<int64_t>(tokens, nflags);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    const auto Bw = static_cast<const uint32_t*>(B);
+    const auto Cw = static_cast<const uint32_t*>(C);
+    auto pk = static_cast<uint32_t*>(packed);
+    const U32Div sd = make_u32div((uint32_t)steps), gd = make_u32div((uint32_t)groups);
+    const uint32_t nf = flags ? (uint32_t)nflags : 0u;
+#define MSSM_PACK_TOKENS(P)                                                                   \
+  hipLaunchKernelGGL(fwd::bc_pack_tokens_kernel<P>, grid, dim3(256), 0, stream, Bw, Cw, pk, \
+                     (uint32_t)tokens, (uint32_t)steps, sd, (uint32_t)L, (uint32_t)groups,  \
+                     gd, lg, (uint32_t)run_words, flags, nf)
+    switch (npw) {
+      case 2: MSSM_PACK_TOKENS(2); break;
+      case 4: MSSM_PACK_TOKENS(4); break;
+      case 8: MSSM_PACK_TOKENS(8); break;
+      default: MSSM_PACK_TOKENS(16); break;
+    }
+#undef MSSM_PACK_TOKENS
+    return hipGetLastError();
+  }
   const int64_t total = std::max<int64_t>(batch * groups * steps * 2 * N, nflags);
   hipLaunchKernelGGL(fwd::bc_pack_kernel, dim3((unsigned)((total + 255) / 256)),
                      dim3(256), 0, stream, B, C, packed, batch, groups, L, steps,

@@ -363,3 +363,12 @@ def test_state_major_flag(L):
     assert _fwd(L, _dims(flags=F | 8)) == -3
     assert _bwd(L, _dims(flags=F | 1)) == -3          # no load-state flag in the backward
     assert _bwd(L, _dims(flags=F), dB=None) == -1
+
+
+def test_valu_probe_validation_codes(L):
+    """The ALU probe refuses a missing sink and out-of-range arguments before
+    launching anything."""
+    p = _ptrs(1)
+    assert L.mssm_valu_probe(0, 8, 64, None, None) == -1
+    for kind, blocks, iters in ((3, 8, 64), (-1, 8, 64), (0, 0, 64), (2, 8, 0)):
+        assert L.mssm_valu_probe(kind, blocks, iters, p[0], None) == -2
