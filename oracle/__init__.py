@@ -58,6 +58,9 @@ def _open(path):
     lib.mssm_oracle_causal_conv1d.argtypes = [i64, i64, i64, i64, _D, _D, _D,
                                               _D, cint, _D]
     lib.mssm_oracle_causal_conv1d.restype = cint
+    lib.mssm_oracle_causal_conv1d_bwd.argtypes = [i64, i64, i64, i64, _D, _D, _D, _D,
+                                                  cint, _D, _D, _D, _D, _D]
+    lib.mssm_oracle_causal_conv1d_bwd.restype = cint
     return lib
 
 
@@ -223,6 +226,29 @@ class Oracle:
             raise ValueError("oracle: bad conv width %d" % K)
         return out
 
+    def causal_conv1d_bwd(self, x, w, dout, bias=None, init=None, silu=True):
+        """Gradients of causal_conv1d (same arguments) for dout = dLoss/dout.
+
+        Returns a dict of fp64 arrays: dx (batch, dim, L), dw (dim, K),
+        dbias (dim,) and dinit (batch, dim, K-1), the gradient of the values
+        before t = 0 (of the zeros when init is None).
+        """
+        x, w, bias, init, dout = map(_f64, (x, w, bias, init, dout))
+        batch, dim, L = x.shape
+        K = w.shape[1]
+        assert w.shape == (dim, K) and K >= 1 and dout.shape == x.shape
+        assert bias is None or bias.shape == (dim,)
+        assert init is None or init.shape == (batch, dim, K - 1)
+        o = {"dx": np.empty((batch, dim, L)), "dw": np.empty((dim, K)),
+             "dbias": np.empty(dim), "dinit": np.empty((batch, dim, K - 1))}
+        rc = self._lib.mssm_oracle_causal_conv1d_bwd(
+            batch, dim, L, K, _ptr(x), _ptr(w), _ptr(bias), _ptr(init),
+            int(bool(silu)), _ptr(dout), _ptr(o["dx"]), _ptr(o["dw"]),
+            _ptr(o["dbias"]), _ptr(o["dinit"]))
+        if rc != 0:
+            raise ValueError("oracle: bad conv width %d" % K)
+        return o
+
     def state_update(self, state, x, dt, A, B, C, D=None, z=None,
                      dt_bias=None, softplus=True, nthreads=None):
         """Single-token decode step in fp64.
@@ -283,6 +309,11 @@ def scan_bwd(*args, **kwargs):
 def causal_conv1d(*args, **kwargs):
     """Causal depthwise convolution in fp64 (see Oracle.causal_conv1d)."""
     return _get().causal_conv1d(*args, **kwargs)
+
+
+def causal_conv1d_bwd(*args, **kwargs):
+    """Gradients of the causal convolution in fp64 (see Oracle.causal_conv1d_bwd)."""
+    return _get().causal_conv1d_bwd(*args, **kwargs)
 
 
 def mamba2_scan(*args, **kwargs):

@@ -448,4 +448,82 @@ int mssm_oracle_causal_conv1d(int64_t batch, int64_t dim, int64_t seqlen,
     return 0;
 }
 
+/*
+ * Gradients of the causal convolution above for an incoming dout = dLoss/d
+ * out (the training step of the conv-fed block: the scan's backward gives
+ * du, the gradient of its input u, which is this convolution's output).
+ * Plain chain rule through v[b,d,t] = bias[d] + sum_k w[d,k] x[b,d,t-(K-1)+k]
+ * and out = silu(v) (or v):
+ *     g[t]       = dout[t] * silu'(v[t])   (or dout[t]),
+ *                  silu'(v) = s (1 + v (1 - s)),  s = 1 / (1 + e^-v)
+ *     dx[s]     += w[d,k] g[t]    for every t, k with s = t-(K-1)+k >= 0
+ *     dinit[j]  += w[d,k] g[t]    for s = t-(K-1)+k < 0, j = (K-1) + s
+ *     dw[d,k]   += g[t] x[s]      (x[s] from init, or 0, for s < 0)
+ *     dbias[d]  += g[t]
+ * dw and dbias sum over the batch and time; dx and dinit are per row.
+ *   x, dout, dx : (batch, dim, seqlen);  w, dw : (dim, K);  bias, dbias :
+ *   (dim) (bias may be NULL);  init, dinit : (batch, dim, K-1) (init may be
+ *   NULL for zeros; dinit is the gradient of those values either way)
+ */
+int mssm_oracle_causal_conv1d_bwd(int64_t batch, int64_t dim, int64_t seqlen,
+                                  int64_t K, const double *x, const double *w,
+                                  const double *bias, const double *init,
+                                  int silu, const double *dout, double *dx,
+                                  double *dw, double *dbias, double *dinit)
+{
+    if (K < 1)
+        return -1;
+    for (int64_t d = 0; d < dim; ++d) {
+        for (int64_t k = 0; k < K; ++k)
+            dw[d * K + k] = 0.0;
+        dbias[d] = 0.0;
+    }
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < dim; ++d) {
+            const double *xr = x + (b * dim + d) * seqlen;
+            const double *gr = dout + (b * dim + d) * seqlen;
+            const double *wr = w + d * K;
+            const double *ir = init ? init + (b * dim + d) * (K - 1) : NULL;
+            double *dxr = dx + (b * dim + d) * seqlen;
+            double *dir = dinit + (b * dim + d) * (K - 1);
+            for (int64_t t = 0; t < seqlen; ++t)
+                dxr[t] = 0.0;
+            for (int64_t j = 0; j < K - 1; ++j)
+                dir[j] = 0.0;
+            for (int64_t t = 0; t < seqlen; ++t) {
+                double v = bias ? bias[d] : 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    const int64_t s = t - (K - 1) + k;
+                    double xv = 0.0;
+                    if (s >= 0)
+                        xv = xr[s];
+                    else if (ir)
+                        xv = ir[(K - 1) + s];
+                    v += wr[k] * xv;
+                }
+                double g = gr[t];
+                if (silu) {
+                    const double sg = 1.0 / (1.0 + exp(-v));
+                    g *= sg * (1.0 + v * (1.0 - sg));
+                }
+                dbias[d] += g;
+                for (int64_t k = 0; k < K; ++k) {
+                    const int64_t s = t - (K - 1) + k;
+                    double xv = 0.0;
+                    if (s >= 0) {
+                        xv = xr[s];
+                        dxr[s] += wr[k] * g;
+                    } else {
+                        if (ir)
+                            xv = ir[(K - 1) + s];
+                        dir[(K - 1) + s] += wr[k] * g;
+                    }
+                    dw[d * K + k] += g * xv;
+                }
+            }
+        }
+    }
+    return 0;
+}
+
 int mssm_oracle_version(void) { return 1; }

@@ -504,6 +504,63 @@ PINS += [pin_conv_numpy_convolve, pin_conv_impulse_and_constant,
          pin_conv_initial_values_split, pin_conv_then_scan_equals_scan_of_conv]
 
 
+def pin_conv_bwd_finite_differences(orc):
+    """Every gradient of the conv's backward (x, w, bias and the values before
+    t = 0, given or zero) against central differences of the pinned forward
+    conv, loss = sum(dout * out), for widths 1..4 with and without silu;
+    step 1e-6 (truncation error O(1e-12) relative)."""
+    rng = np.random.default_rng(51)
+    batch, dim, L = 2, 2, 6
+    for K in (1, 2, 3, 4):
+        for silu in (True, False):
+            for with_init in (True, False):
+                x = rng.standard_normal((batch, dim, L))
+                w = rng.standard_normal((dim, K))
+                bias = rng.standard_normal(dim)
+                init = rng.standard_normal((batch, dim, K - 1)) if with_init else None
+                dout = rng.standard_normal((batch, dim, L))
+                g = orc.causal_conv1d_bwd(x, w, dout, bias=bias, init=init, silu=silu)
+                base = {"x": x, "w": w, "bias": bias,
+                        "init": init if with_init else np.zeros((batch, dim, K - 1))}
+
+                def loss(**over):
+                    a = dict(base, **over)
+                    return float((dout * orc.causal_conv1d(a["x"], a["w"], a["bias"],
+                                                           init=a["init"],
+                                                           silu=silu)).sum())
+                eps = 1e-6
+                for name, gname in (("x", "dx"), ("w", "dw"), ("bias", "dbias"),
+                                    ("init", "dinit")):
+                    arr = base[name]
+                    fd = np.empty_like(arr)
+                    for idx in np.ndindex(arr.shape):
+                        p, m = arr.copy(), arr.copy()
+                        p[idx] += eps
+                        m[idx] -= eps
+                        fd[idx] = (loss(**{name: p}) - loss(**{name: m})) / (2 * eps)
+                    _close(g[gname], fd, rtol=1e-6, atol=1e-8,
+                           what="conv d%s K=%d silu=%s init=%s" % (name, K, silu, with_init))
+
+
+def pin_conv_bwd_width1_closed_form(orc):
+    """Width 1 without silu is out = w x + bias per channel, so exactly
+    dx = w dout, dw = sum(dout x), dbias = sum(dout) over batch and time, and
+    no values before t = 0 are read (dinit is empty)."""
+    rng = np.random.default_rng(53)
+    batch, dim, L = 3, 4, 10
+    x = rng.standard_normal((batch, dim, L))
+    w = rng.standard_normal((dim, 1))
+    dout = rng.standard_normal((batch, dim, L))
+    g = orc.causal_conv1d_bwd(x, w, dout, bias=rng.standard_normal(dim), silu=False)
+    _close(g["dx"], w[None, :, 0:1] * dout, 1e-15, 1e-15, "width-1 dx")
+    _close(g["dw"][:, 0], (dout * x).sum(axis=(0, 2)), 1e-13, 1e-13, "width-1 dw")
+    _close(g["dbias"], dout.sum(axis=(0, 2)), 1e-13, 1e-13, "width-1 dbias")
+    assert g["dinit"].shape == (batch, dim, 0)
+
+
+PINS += [pin_conv_bwd_finite_differences, pin_conv_bwd_width1_closed_form]
+
+
 # --------------------------------------------------------------- B/C groups
 # Reading: with G groups, B, C are (batch, L, G, N) and channel d reads group
 # d // (dim // G) (contiguous channel blocks).

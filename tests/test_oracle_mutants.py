@@ -68,6 +68,12 @@ MUTANTS = [
     ("conv_silu_missing", "o[t] = silu ? oracle_silu(v) : v;", "o[t] = v;"),
     ("conv_init_ignored", "else if (ir)", "else if (0 && ir)"),
     ("conv_init_misaligned", "xv = ir[(K - 1) + s];", "xv = ir[-s - 1];"),
+    # causal conv backward
+    ("conv_bwd_silu_derivative_is_sigmoid", "g *= sg * (1.0 + v * (1.0 - sg));", "g *= sg;"),
+    ("conv_bwd_dx_kernel_not_flipped", "dxr[s] += wr[k] * g;", "dxr[s] += wr[K - 1 - k] * g;"),
+    ("conv_bwd_dw_uses_dout", "dw[d * K + k] += g * xv;", "dw[d * K + k] += gr[t] * xv;"),
+    ("conv_bwd_dinit_dropped", "dir[(K - 1) + s] += wr[k] * g;", "dir[(K - 1) + s] += 0.0 * g;"),
+    ("conv_bwd_dbias_ungated", "dbias[d] += g;", "dbias[d] += gr[t];"),
 ]
 
 
