@@ -588,8 +588,9 @@ def bench_mamba2(torch, W, m, dev, steps=20):
 
 def bench_conv(torch, W, m, dev, s, sets, hev, steps=20):
     """The causal conv (width 4, silu) ahead of the scan on the same workload:
-    the standalone conv kernel (HBM-bound) and the conv fused into the scan's
-    load stage, against running the two one after the other."""
+    the standalone conv kernel (HBM-bound), its backward (dx, dweight, dbias
+    for a dout of the same shape), and the conv fused into the scan's load
+    stage, against running the two one after the other."""
     stream = torch.cuda.current_stream(dev)
     cps = [{k: v.to(dev) for k, v in
             W.make_conv_params(W.spec(s.name, seed=s.seed + 1000 * r, dstate=s.dstate)).items()}
@@ -622,8 +623,13 @@ def bench_conv(torch, W, m, dev, s, sets, hev, steps=20):
                              D=d["D"], z=d["z"], delta_bias=d["delta_bias"],
                              softplus=s.softplus, last_state=d["last"], out=d["out"])
 
+    def conv_bwd(i):
+        d, c = sets[i % len(sets)], cps[i % len(sets)]
+        m.causal_conv1d_bwd(d["u"], c["weight"], d["z"], bias=c["bias"], init=c["init"])
+
     settle_gpu(torch, dev)
     conv_ms = _time(torch, stream, conv, steps)
+    conv_bwd_ms = _time(torch, stream, conv_bwd, steps)
     sep_ms = _time(torch, stream, separate, steps)
     scan_ms = _time(torch, stream, scan_alone, steps)
     pairs = [(hev.create(), hev.create()) for _ in range(steps)]
@@ -657,6 +663,15 @@ def bench_conv(torch, W, m, dev, s, sets, hev, steps=20):
                               "frac": round(cgbs / HBM_PEAK_GBS, 4), "traffic": None,
                               "kernel": "causal_conv1d_kernel",
                               "algorithmic_bytes": cb},
+            "conv_bwd_ms": round(conv_bwd_ms, 5),
+            "conv_bwd_roofline": {"bound": "hbm",
+                                  "achieved": round(W.conv_bwd_bytes(s) / (conv_bwd_ms * 1e-3)
+                                                    / 1e9, 1),
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(W.conv_bwd_bytes(s) / (conv_bwd_ms * 1e-3) /
+                                                1e9 / HBM_PEAK_GBS, 4),
+                                  "traffic": None, "kernel": "causal_conv1d_bwd_kernel",
+                                  "algorithmic_bytes": W.conv_bwd_bytes(s)},
             "separate_conv_then_scan_ms": round(sep_ms, 5),
             "fused_ms": round(fused_ms, 5),
             "fused_speedup_vs_separate": round(sep_ms / fused_ms, 3),

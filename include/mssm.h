@@ -178,6 +178,39 @@ int mssm_causal_conv1d_fwd(const void* x, const float* weight,
                            void* stream);
 
 /*
+ * Gradients of mssm_causal_conv1d_fwd for an incoming dout = dLoss/dout:
+ * with the scan's backward, whose du is the gradient of the convolution's
+ * output, this completes the training step of the conv-fed block (the
+ * pages' selective scan trained through its parallel scan, page "Mamba:
+ * Selective State Space Models", "Efficient Scan").  Chain rule of the
+ * forward definition, with g_t = dout_t * silu'(v_t) (or dout_t), silu'(v)
+ * = s (1 + v (1 - s)), s = sigmoid(v):
+ *     dx_s       = sum_k weight[d,k] * g_{s+(width-1)-k}  (steps inside the row)
+ *     dinit_j    = sum_{k<=j} weight[d,k] * g_{j-k}       (x at t = j-(width-1))
+ *     dweight[d,k] = sum over batch and time of g_t * x_{t-(width-1)+k}
+ *     dbias[d]   = sum over batch and time of g_t
+ *   x, dout, dx : (batch, dim, seqlen) io dtype
+ *   weight      : (dim, width) fp32;  bias : (dim) fp32 or NULL
+ *   init        : (batch, dim, width-1) io dtype or NULL (zeros), as in the
+ *                 forward call
+ *   dweight     : (dim, width) fp32, written
+ *   dbias       : (dim) fp32, written, or NULL (not computed)
+ *   dinit       : (batch, dim, width-1) io dtype, written, or NULL (not
+ *                 computed); the gradient of the values before t = 0 (of the
+ *                 zeros when init is NULL)
+ *   width       : 2, 3 or 4
+ * The outputs overwrite (no accumulation), must not overlap an input or each
+ * other, and the channel sums are added in a fixed order, so repeated calls
+ * give identical bits.  dims->dstate is ignored; flags must be 0 (the
+ * (batch, dim, seqlen) layout); time_segments must be 0.  Errors as for the
+ * forward call.  Allocates nothing; one launch on `stream`.
+ */
+int mssm_causal_conv1d_bwd(const void* x, const float* weight, const float* bias,
+                           const void* init, int width, int silu, const void* dout,
+                           void* dx, float* dweight, float* dbias, void* dinit,
+                           const mssm_dims* dims, void* stream);
+
+/*
  * The forward scan fed by the width-4 causal convolution: the scan input is
  * u = silu(conv(x)) as mssm_causal_conv1d_fwd(width = 4, silu = 1) computes
  * it, formed while the scan loads its input (u never goes to memory unless

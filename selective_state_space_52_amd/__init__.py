@@ -239,6 +239,36 @@ def causal_conv1d_fwd(x, weight, bias=None, init=None, silu=True, out=None,
     return out
 
 
+def causal_conv1d_bwd(x, weight, dout, bias=None, init=None, silu=True, dinit=False):
+    """Gradients of causal_conv1d_fwd (same x, weight, bias, init, silu) for
+    dout = dLoss/dout, all in the (batch, dim, L) layout.  Returns
+    (dx in x's dtype, dweight (dim, width) fp32, dbias (dim,) fp32, dinit)
+    where dinit is the (batch, dim, width-1) gradient of the values before
+    t = 0 in x's dtype when `dinit` is true, else None."""
+    if x.dtype not in _IO:
+        raise ValueError("x must be float32 or bfloat16")
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, dim, L)")
+    batch, dim, L = x.shape
+    width = weight.shape[-1]
+    dev = x.device
+    _need(x, "x", x.dtype, (batch, dim, L), dev)
+    _need(dout, "dout", x.dtype, (batch, dim, L), dev)
+    _need(weight, "weight", torch.float32, (dim, width), dev)
+    _need(bias, "bias", torch.float32, (dim,), dev)
+    _need(init, "init", x.dtype, (batch, dim, width - 1), dev)
+    dx = torch.empty_like(x)
+    dw = torch.empty(dim, width, dtype=torch.float32, device=dev)
+    db = torch.empty(dim, dtype=torch.float32, device=dev)
+    di = torch.empty(batch, dim, width - 1, dtype=x.dtype, device=dev) if dinit else None
+    dims = Dims(batch, dim, 0, L, _IO[x.dtype], 0, 0, 0)
+    with torch.cuda.device(dev):
+        check(lib().mssm_causal_conv1d_bwd(
+            _ptr(x), _ptr(weight), _ptr(bias), _ptr(init), int(width), int(bool(silu)),
+            _ptr(dout), _ptr(dx), _ptr(dw), _ptr(db), _ptr(di), dims, _stream(dev)))
+    return dx, dw, db, di
+
+
 def selective_scan_fwd_conv(x, conv_weight, delta, A, B, C, conv_bias=None,
                             conv_init=None, D=None, z=None, delta_bias=None,
                             softplus=True, last_state=None, load_state=False,

@@ -34,7 +34,7 @@ EXPORTS = ("mssm_selective_scan_fwd", "mssm_selective_scan_bwd",
            "mssm_selective_scan_fwd_ws", "mssm_selective_scan_fwd_conv_ws",
            "mssm_selective_scan_bwd_ws", "mssm_mamba2_scan_fwd_ws",
            "mssm_workspace_size", "mssm_selective_scan_fwd_noalloc",
-           "mssm_valu_probe")
+           "mssm_valu_probe", "mssm_causal_conv1d_bwd")
 
 
 class Dims(ctypes.Structure):
@@ -125,6 +125,9 @@ def lib():
         L.mssm_set_scan_timing_events.restype = i
         L.mssm_abi_version.argtypes = []
         L.mssm_abi_version.restype = i
+        L.mssm_causal_conv1d_bwd.argtypes = [vp, fp, fp, vp, i, i, vp, vp, fp, fp, vp,
+                                             ctypes.POINTER(Dims), vp]
+        L.mssm_causal_conv1d_bwd.restype = i
         L.mssm_valu_probe.argtypes = [i, i, i, vp, vp]
         L.mssm_valu_probe.restype = i
         _lib = L

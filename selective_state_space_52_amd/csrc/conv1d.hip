@@ -197,6 +197,155 @@ hipError_t launch_k(const ConvParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Gradients of the convolution for dout = dLoss/dout (the training step of
+// the conv-fed block: the scan's backward yields du, the gradient of this
+// convolution's output).  With g[t] = dout[t] silu'(v[t]) (or dout[t]),
+// silu'(v) = s (1 + v (1 - s)), s = sigmoid(v):
+//   dx[s]    = sum_k w[d,k] g[s + (K-1) - k]     (over steps inside the row)
+//   dinit[j] = sum_{k <= j} w[d,k] g[j - k]       (the values before t = 0)
+//   dw[d,k]  = sum_{b,t} g[t] x[t-(K-1)+k],  dbias[d] = sum_{b,t} g[t].
+// One workgroup per channel, so the channel sums need no second pass and
+// are added in a fixed order (repeated calls give the same bits): each
+// thread owns 8 consecutive steps of a row (16-byte pieces, as in the
+// forward), walks the batch and the row in strides of 256 chunks, keeps its
+// partial sums in registers, and the workgroup adds them in a tree.  A
+// thread recomputes v (hence g) for its 8 steps and the K-1 after them, so
+// it reads x from 4 steps before its chunk to 4 after, and dout to 4 after.
+template <bool BF16, bool VEC, int K>
+__global__ void __launch_bounds__(256)
+    causal_conv1d_bwd_kernel(const void* __restrict__ x, const float* __restrict__ w,
+                             const float* __restrict__ bias, const void* __restrict__ init,
+                             const void* __restrict__ dout, void* __restrict__ dx,
+                             float* __restrict__ dw, float* __restrict__ dbias,
+                             void* __restrict__ dinit, int64_t batch, int64_t dim,
+                             int64_t L, int silu) {
+  static_assert(K >= 1 && K - 1 <= kPrev, "width");
+  constexpr int kNext = 4;  // steps after a chunk (>= K - 1)
+  const int64_t d = blockIdx.x;
+  const int tid = threadIdx.x;
+  float wk[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) wk[j] = w[d * K + j];
+  const float bv = bias ? bias[d] : 0.0f;
+  float pw[K], pb = 0.0f;
+#pragma unroll
+  for (int j = 0; j < K; ++j) pw[j] = 0.0f;
+
+  for (int64_t b = 0; b < batch; ++b) {
+    const int64_t row = b * dim + d;
+    const int64_t off = row * L;
+    for (int64_t t0 = (int64_t)tid * kChunk; t0 < L; t0 += 256 * kChunk) {
+      Raw<BF16, kChunk> rx, rg;
+      Raw<BF16, kPrev> rp;
+      Raw<BF16, kNext> rxn, rgn;
+      load_chunk<BF16, VEC, kChunk>(rx, x, off + t0, L - t0);
+      load_chunk<BF16, VEC, kChunk>(rg, dout, off + t0, L - t0);
+      load_chunk<BF16, VEC, kNext>(rxn, x, off + t0 + kChunk, L - t0 - kChunk);
+      load_chunk<BF16, VEC, kNext>(rgn, dout, off + t0 + kChunk, L - t0 - kChunk);
+      if (t0 >= kPrev) load_chunk<BF16, VEC, kPrev>(rp, x, off + t0 - kPrev, kPrev);
+      // x over [t0 - 4, t0 + 12): before the row from init (or 0)
+      float xs[kPrev + kChunk + kNext];
+      if (t0 >= kPrev) {
+#pragma unroll
+        for (int j = 0; j < kPrev; ++j) xs[j] = raw_get(rp, j);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kPrev; ++j) xs[j] = 0.0f;
+        if (init) {
+#pragma unroll
+          for (int j = 0; j < K - 1; ++j) {
+            const int64_t i = row * (K - 1) + j;
+            xs[kPrev - (K - 1) + j] = BF16 ? bf16_bits(static_cast<const uint16_t*>(init)[i])
+                                           : static_cast<const float*>(init)[i];
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) xs[kPrev + j] = raw_get(rx, j);
+#pragma unroll
+      for (int j = 0; j < kNext; ++j) xs[kPrev + kChunk + j] = raw_get(rxn, j);
+      // g over [t0, t0 + 8 + K - 1); steps past the row have dout = 0
+      constexpr int NG = kChunk + K - 1;
+      float gs[NG];
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        const float go = j < kChunk ? raw_get(rg, j) : raw_get(rgn, j - kChunk);
+        float v = bv;
+#pragma unroll
+        for (int k = 0; k < K; ++k) v = fmaf(wk[k], xs[kPrev + j - (K - 1) + k], v);
+        float gv = go;
+        if (silu) {
+          const float sg = hw_rcp(1.0f + hw_exp2(-v * kLog2e));
+          gv = go * (sg * fmaf(v, 1.0f - sg, 1.0f));
+        }
+        gs[j] = gv;
+      }
+      float o[kChunk];
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) {
+        float a = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) a = fmaf(wk[k], gs[i + (K - 1) - k], a);
+        o[i] = a;
+        pb += gs[i];
+#pragma unroll
+        for (int k = 0; k < K; ++k) pw[k] = fmaf(gs[i], xs[kPrev + i - (K - 1) + k], pw[k]);
+      }
+      store_chunk<BF16, VEC, kChunk>(dx, off + t0, o, L - t0);
+      if (t0 == 0 && dinit) {
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) {
+          float a = 0.0f;
+#pragma unroll
+          for (int k = 0; k <= j; ++k) a = fmaf(wk[k], gs[j - k], a);
+          const int64_t i = row * (K - 1) + j;
+          if constexpr (BF16)
+            static_cast<uint16_t*>(dinit)[i] = to_bf16(a);
+          else
+            static_cast<float*>(dinit)[i] = a;
+        }
+      }
+    }
+  }
+
+  // channel sums: the workgroup's partials added in a fixed tree
+  __shared__ float red[K + 1][256];
+#pragma unroll
+  for (int k = 0; k < K; ++k) red[k][tid] = pw[k];
+  red[K][tid] = pb;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (tid < st) {
+#pragma unroll
+      for (int k = 0; k <= K; ++k) red[k][tid] += red[k][tid + st];
+    }
+    __syncthreads();
+  }
+  if (tid <= K) {
+    if (tid < K)
+      dw[d * K + tid] = red[tid][0];
+    else if (dbias)
+      dbias[d] = red[K][0];
+  }
+}
+
+template <bool BF16, bool VEC>
+hipError_t launch_bwd_k(const ConvBwdParams& p, hipStream_t st) {
+  const dim3 grid((unsigned)p.dim), block(256);
+#define MSSM_CONV_BWD(KW)                                                                   \
+  hipLaunchKernelGGL((causal_conv1d_bwd_kernel<BF16, VEC, KW>), grid, block, 0, st, p.x, \
+                     p.w, p.bias, p.init, p.dout, p.dx, p.dw, p.dbias, p.dinit, p.batch,  \
+                     p.dim, p.L, p.silu)
+  switch (p.width) {
+    case 2: MSSM_CONV_BWD(2); break;
+    case 3: MSSM_CONV_BWD(3); break;
+    case 4: MSSM_CONV_BWD(4); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MSSM_CONV_BWD
+  return hipGetLastError();
+}
+
 // 32-bit indices when every element index (and the grid's thread index, a
 // chunk of kChunk elements per thread) stays below 2^31.
 bool small_indices(const ConvParams& p) {
@@ -205,6 +354,12 @@ bool small_indices(const ConvParams& p) {
 }
 
 }  // namespace
+
+hipError_t launch_causal_conv1d_bwd(const ConvBwdParams& p, bool bf16, bool vec,
+                                    hipStream_t st) {
+  if (bf16) return vec ? launch_bwd_k<true, true>(p, st) : launch_bwd_k<true, false>(p, st);
+  return vec ? launch_bwd_k<false, true>(p, st) : launch_bwd_k<false, false>(p, st);
+}
 
 hipError_t launch_causal_conv1d(const ConvParams& p, bool bf16, bool vec,
                                 hipStream_t st) {

@@ -497,6 +497,57 @@ int mssm_causal_conv1d_fwd(const void* x, const float* weight,
   return MSSM_OK;
 }
 
+int mssm_causal_conv1d_bwd(const void* x, const float* weight, const float* bias,
+                           const void* init, int width, int silu, const void* dout,
+                           void* dx, float* dweight, float* dbias, void* dinit,
+                           const mssm_dims* dims, void* stream) {
+  if (!dims) return MSSM_ERR_NULL;
+  if (dims->io_dtype != MSSM_F32 && dims->io_dtype != MSSM_BF16)
+    return MSSM_ERR_UNSUPPORTED;
+  if (dims->flags != 0 || dims->ngroups > 1) return MSSM_ERR_UNSUPPORTED;
+  if (dims->time_segments != 0) return MSSM_ERR_DIMS;
+  if (dims->batch <= 0 || dims->dim <= 0 || dims->seqlen <= 0) return MSSM_ERR_DIMS;
+  if (width < 2 || width > 4) return MSSM_ERR_UNSUPPORTED;
+  if (!x || !weight || !dout || !dx || !dweight) return MSSM_ERR_NULL;
+  const int64_t batch = dims->batch, dim = dims->dim, L = dims->seqlen;
+  const size_t io = dims->io_dtype == MSSM_BF16 ? 2 : 4;
+  if (!product_ok(batch, dim, L, INT64_MAX / 16) || dim > INT32_MAX) return MSSM_ERR_DIMS;
+  const void* ios[] = {x, init, dout, dx, dinit};
+  for (const void* p : ios)
+    if (p && !aligned(p, io)) return MSSM_ERR_ALIGN;
+  const void* f32s[] = {weight, bias, dweight, dbias};
+  for (const void* p : f32s)
+    if (p && !aligned(p, 4)) return MSSM_ERR_ALIGN;
+  const int64_t ebytes = batch * dim * L * (int64_t)io;
+  const int64_t ibytes = batch * dim * (width - 1) * (int64_t)io;
+  const Range outs[] = {range_of(dx, ebytes), range_of(dweight, dim * width * 4),
+                        range_of(dbias, dim * 4), range_of(dinit, ibytes)};
+  const Range ins[] = {range_of(x, ebytes), range_of(weight, dim * width * 4),
+                       range_of(bias, dim * 4), range_of(init, ibytes),
+                       range_of(dout, ebytes)};
+  for (int i = 0; i < 4; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return MSSM_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return MSSM_ERR_ALIAS;
+  }
+
+  mssm::ConvBwdParams p;
+  p.x = x; p.w = weight; p.bias = bias; p.init = init; p.dout = dout;
+  p.dx = dx; p.dw = dweight; p.dbias = dbias; p.dinit = dinit;
+  p.batch = batch; p.dim = dim; p.L = L;
+  p.width = width;
+  p.silu = silu ? 1 : 0;
+  const bool vec = (L % 8) == 0 && ((L * (int64_t)io) % 16) == 0 && aligned(x, 16) &&
+                   aligned(dout, 16) && aligned(dx, 16);
+  hipError_t e = mssm::launch_causal_conv1d_bwd(p, io == 2, vec, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_hip_error("causal_conv1d_bwd launch", e);
+    return MSSM_ERR_HIP;
+  }
+  return MSSM_OK;
+}
+
 }  // extern "C"
 
 namespace {

@@ -75,6 +75,24 @@ struct ConvParams {
   int32_t layout_bld;     // x, out are (batch, L, dim)
 };
 
+// Gradients of the causal conv: x, dout, dx (batch, dim, L) io dtype; w
+// (dim, width) fp32; dw (dim, width) and dbias (dim) fp32 (dbias may be
+// null); init, dinit (batch, dim, width-1) io dtype (both may be null).
+struct ConvBwdParams {
+  const void* x;
+  const float* w;
+  const float* bias;
+  const void* init;
+  const void* dout;
+  void* dx;
+  float* dw;
+  float* dbias;
+  void* dinit;
+  int64_t batch, dim, L;
+  int32_t width;          // 2, 3 or 4
+  int32_t silu;
+};
+
 struct UpdateParams {
   float* state;
   const void* x;
@@ -217,6 +235,8 @@ hipError_t launch_scan_bwd(const BwdParams& p, int N, bool bf16, bool vec,
                            hipStream_t stream);
 hipError_t launch_state_update(const UpdateParams& p, int N, bool bf16,
                                hipStream_t stream);
+hipError_t launch_causal_conv1d_bwd(const ConvBwdParams& p, bool bf16, bool vec,
+                                    hipStream_t stream);
 hipError_t launch_causal_conv1d(const ConvParams& p, bool bf16, bool vec,
                                 hipStream_t stream);
 

@@ -372,3 +372,30 @@ def test_valu_probe_validation_codes(L):
     assert L.mssm_valu_probe(0, 8, 64, None, None) == -1
     for kind, blocks, iters in ((3, 8, 64), (-1, 8, 64), (0, 0, 64), (2, 8, 0)):
         assert L.mssm_valu_probe(kind, blocks, iters, p[0], None) == -2
+
+
+def test_conv_bwd_validation_codes(L):
+    """The conv backward checks its arguments before any HIP call: missing
+    required pointers, widths outside 2..4, the block layout flag, and an
+    output overlapping an input or another output."""
+    import ctypes as ct
+    d = _dims(2, 64, 0, 128)
+    p = _ptrs(11)
+    args = dict(x=p[0], w=p[1], bias=p[2], init=p[3], width=4, silu=1, dout=p[4],
+                dx=p[5], dw=p[6], db=p[7], di=p[8])
+
+    def call(dims=d, **over):
+        a = dict(args, **over)
+        return L.mssm_causal_conv1d_bwd(a["x"], a["w"], a["bias"], a["init"], a["width"],
+                                        a["silu"], a["dout"], a["dx"], a["dw"], a["db"],
+                                        a["di"], ct.byref(dims), None)
+    for k in ("x", "w", "dout", "dx", "dw"):
+        assert call(**{k: None}) == -1, k
+    assert call(width=1) == -3 and call(width=5) == -3
+    blk = _dims(2, 64, 0, 128)
+    blk.flags = 2                        # MSSM_FLAG_LAYOUT_BLD
+    assert call(dims=blk) == -3
+    assert call(dx=p[0]) == -5           # dx is x
+    assert call(dw=p[1]) == -5           # dweight is weight
+    assert call(db=p[5]) == -5           # dbias inside dx
+    assert call(dims=_dims(0, 64, 0, 128)) == -2

@@ -224,6 +224,14 @@ def conv_bytes(s: ScanSpec, width: int = 4) -> int:
     return 2 * s.elements * io + 4 * s.dim * (width + 1)
 
 
+def conv_bwd_bytes(s: ScanSpec, width: int = 4) -> int:
+    """Algorithmic HBM bytes of the conv's backward: x and dout read once, dx
+    written once, the weights and bias read and their gradients written, the
+    initial values read."""
+    io = 4 if s.io == "f32" else 2
+    return 3 * s.elements * io + 2 * 4 * s.dim * (width + 1) + s.batch * s.dim * (width - 1) * io
+
+
 def scan_bwd_bytes(s: ScanSpec, has_h0: bool = False, has_dlast: bool = False,
                    want_dh0: bool = False) -> int:
     """Algorithmic HBM bytes of one backward call: the forward's operands and
