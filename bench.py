@@ -407,13 +407,15 @@ def main():
 def probe_rates(torch, m, dev, waves_per_cu, iters=4096, reps=10):
     """Measured issue rates (per second) of the library's ALU probe kernels
     at `waves_per_cu` resident waves per CU: fp32 fma (kind 0), v_exp_f32
-    (kind 1) and state elements of the scan's inner-step mix (kind 2)."""
+    (kind 1), state elements of the scan's inner-step mix (kind 2) and state
+    elements of the same recurrence as an in-wave associative scan over 64
+    timesteps (kind 3)."""
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     blocks = cus * waves_per_cu // 4        # 256-thread workgroups: 4 waves
     threads = blocks * 256
     sink = torch.empty(threads, device=dev)
     rates = {}
-    for kind, per_iter in ((0, 8), (1, 8), (2, 4)):
+    for kind, per_iter in ((0, 8), (1, 8), (2, 4), (3, 4)):
         for _ in range(2):
             m.valu_probe(kind, blocks, iters, sink)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -447,7 +449,8 @@ def alu_probe(torch, m, dev, s=None, nbytes=None, kernel_ms=None, sweep=(16, 32)
         res["by_waves_per_cu"][str(w)] = {
             "fma_T_per_s": round(r[0] / 1e12, 3), "exp_T_per_s": round(r[1] / 1e12, 3),
             "state_element_mix_T_per_s": round(r[2] / 1e12, 3),
-            "fma_slots_per_state_element": round(r[0] / r[2], 3)}
+            "fma_slots_per_state_element": round(r[0] / r[2], 3),
+            "wave_scan_state_elements_T_per_s": round(r[3] / 1e12, 3)}
     clock = shader_clock_mhz()
     res["shader_clock_mhz"] = clock
     if clock:
@@ -455,7 +458,8 @@ def alu_probe(torch, m, dev, s=None, nbytes=None, kernel_ms=None, sweep=(16, 32)
             per_clk = 1.0 / (cus * clock * 1e6)
             res["by_waves_per_cu"][str(w)]["per_cu_per_clock"] = {
                 "fma": round(r[0] * per_clk, 2), "exp": round(r[1] * per_clk, 2),
-                "state_elements": round(r[2] * per_clk, 2)}
+                "state_elements": round(r[2] * per_clk, 2),
+                "wave_scan_state_elements": round(r[3] * per_clk, 2)}
     if s is not None:
         r = at[16] if 16 in at else at[max(at)]
         ceil_s = s.state_elements / r[2] + s.elements * SLOTS_PER_ELEM / r[0]

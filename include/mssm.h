@@ -453,10 +453,14 @@ int mssm_set_scan_timing_events(void* start, void* stop);
  *           exponential, a multiply, an fma and a readout fma (the first a
  *           multiply), plus 1 multiply per iteration (21 instructions when
  *           iters is a multiple of 4),
+ *   kind 3: the same 4 state elements per iteration computed as an inclusive
+ *           associative scan of (exp(Delta A), Delta u B) pairs across the
+ *           wave's 64 lanes (one timestep per lane: six DPP levels), then the
+ *           chunk's entering state and the readout,
  * and writes one float per thread to `sink` (device, blocks * 256 floats,
  * caller-owned; the values carry no meaning).  The caller times the launch
  * (for instance with events on `stream`).  Errors: MSSM_ERR_NULL (sink),
- * MSSM_ERR_DIMS (kind outside 0..2, blocks or iters <= 0), MSSM_ERR_HIP.
+ * MSSM_ERR_DIMS (kind outside 0..3, blocks or iters <= 0), MSSM_ERR_HIP.
  */
 int mssm_valu_probe(int kind, int blocks, int iters, float* sink, void* stream);
 
