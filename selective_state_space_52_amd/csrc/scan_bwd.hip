@@ -366,6 +366,11 @@ __global__ void __launch_bounds__(kLanes* NG)
   static_assert(T % KB == 0 && KB % RS == 0, "tile, batch and reduction nest");
   using Batch = BCBatch<NPW, BF16>;
   __shared__ BwdSmem<N, NG> sm;
+  // staged output stores: (batch, dim, L) rows of bf16, 4 waves of 4 steps
+  constexpr bool kStageOut = VEC && BF16 && NG == 4 && KC == 4;
+  constexpr int kStgPitch = 40;  // bytes per channel row of the staging area
+  static_assert(!kStageOut || 3 * kLanes * kStgPitch <= (int)sizeof(sm.red),
+                "staging fits in the reduction blocks");
 
   const int lane = threadIdx.x & (kLanes - 1);
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -592,7 +597,39 @@ __global__ void __launch_bounds__(kLanes* NG)
         prep_r(tb - T);
         finish_checkpoint(hraw, hck);
       }
-      if (k.valid) {
+      if constexpr (kStageOut) {
+        // The tile's du, ddelta, dz leave through LDS (the reduction blocks
+        // are free: the tile's sums were taken before the barrier above).
+        // Each wave stages its 4 steps of every channel, one 8-byte piece per
+        // tensor in a 40-byte row per channel; after a barrier wave g stores
+        // channels 16 g .. 16 g + 15 over the tile's 16 steps (lane l:
+        // channel 16 g + l / 4, steps 4 (l mod 4) ..), so a store
+        // instruction writes 16 rows of 32 contiguous bytes rather than 8
+        // bytes of each of 64 rows.
+        char* const stg = reinterpret_cast<char*>(&sm.red[0][0][0]);
+        auto put = [&](int tt, const float (&o)[KC]) {
+          *reinterpret_cast<uint2*>(stg + (tt * kLanes + lane) * kStgPitch + g * 8) =
+              make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+        };
+        put(0, odu);
+        put(1, odd);
+        if constexpr (HAS_Z) put(2, odz);
+        __syncthreads();
+        const int c = (kLanes / NG) * g + (lane >> 2);
+        const int q = lane & 3;
+        const int64_t d_o = (int64_t)(k.gi % s.groups_per_batch) * kLanes + c;
+        const int64_t t_o = tb + 4 * q;
+        if (d_o < s.dim && t_o < s.L) {
+          const int64_t off = ((int64_t)k.b * s.dim + d_o) * s.L + t_o;
+          auto st = [&](void* base, int tt) {
+            *reinterpret_cast<uint2*>(static_cast<char*>(base) + off * 2) =
+                *reinterpret_cast<const uint2*>(stg + (tt * kLanes + c) * kStgPitch + q * 8);
+          };
+          st(du, 0);
+          st(ddelta, 1);
+          if constexpr (HAS_Z) st(dz, 2);
+        }
+      } else if (k.valid) {
         const int64_t off = k.rowoff + tc * s.ts;
         store_chunk<BF16, VEC, KC>(du, off, odu, nv, s.ts);
         store_chunk<BF16, VEC, KC>(ddelta, off, odd, nv, s.ts);
