@@ -342,8 +342,10 @@ struct alignas(16) BwdSmem {
   float dbc[kT][2 * N];                 // the tile's channel sums of dB, dC
 };
 
+// Two waves per SIMD (two 4-wave workgroups per CU at N <= 16) need at most
+// 256 VGPRs per wave.
 template <int N, int NG, bool BF16, bool VEC, bool HAS_Z>
-__global__ void __launch_bounds__(kLanes* NG)
+__global__ void __launch_bounds__(kLanes* NG) __attribute__((amdgpu_waves_per_eu(2)))
     bwd_pass_r_kernel(const void* __restrict__ u, const void* __restrict__ delta,
                       const void* __restrict__ z, const void* __restrict__ dout,
                       const float* __restrict__ A, const float* __restrict__ Dv,
@@ -368,13 +370,26 @@ __global__ void __launch_bounds__(kLanes* NG)
   __shared__ BwdSmem<N, NG> sm;
   // staged output stores: (batch, dim, L) rows of bf16, 4 waves of 4 steps
   constexpr bool kStageOut = VEC && BF16 && NG == 4 && KC == 4;
-  constexpr int kStgPitch = 40;  // bytes per channel row of the staging area
-  static_assert(!kStageOut || 3 * kLanes * kStgPitch <= (int)sizeof(sm.red),
+  // Staging rows: per tensor (du, ddelta, dz, then u, delta, z, dout) and
+  // channel, the tile's 16 steps as four 8-byte pieces, piece p at slot
+  // p ^ ((channel / 8) mod 4) so that both access patterns below are free
+  // of bank conflicts.
+  constexpr int kStgPitch = 32;
+  static_assert(!kStageOut || 7 * kLanes * kStgPitch <= (int)sizeof(sm.red),
                 "staging fits in the reduction blocks");
+  char* const stg = reinterpret_cast<char*>(&sm.red[0][0][0]);
+  auto stg_at = [&](int tt, int c, int piece) -> uint2* {
+    return reinterpret_cast<uint2*>(stg + (tt * kLanes + c) * kStgPitch +
+                                    8 * (piece ^ ((c >> 3) & 3)));
+  };
 
   const int lane = threadIdx.x & (kLanes - 1);
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = g * NPW;
+  // the staged accesses' lane mapping: channel 16 g + lane / 4 of the
+  // group, steps 4 (lane mod 4) .. of the tile
+  const int c_st = (kLanes / NG) * g + (lane >> 2);
+  const int q_st = lane & 3;
   const Task k = task_of(s, lane);
   const int64_t task = blockIdx.x;
   const int64_t Lp = (int64_t)s.tiles * T;
@@ -439,6 +454,20 @@ __global__ void __launch_bounds__(kLanes* NG)
       sm.dy[g * KC + q][lane] = dyv;
     }
   };
+  // kStageOut: the next tile's inputs are read by channel runs (16 rows of
+  // 32 bytes per instruction) and meet the lanes that own their channels in
+  // LDS in the output phase
+  const int64_t d_st = (int64_t)(k.gi % s.groups_per_batch) * kLanes + c_st;
+  const int64_t row_st = (int64_t)k.b * s.dim + (d_st < s.dim ? d_st : s.dim - 1);
+  auto load_r_staged = [&](int64_t tile_base) {
+    const int64_t t = tile_base + 4 * q_st;
+    const int64_t nv = s.L - t;
+    const int64_t off = row_st * s.L + t;
+    load_chunk<BF16, true, KC>(nu, u, off, nv);
+    load_chunk<BF16, true, KC>(nd, delta, off, nv);
+    if constexpr (HAS_Z) load_chunk<BF16, true, KC>(nz, z, off, nv);
+    load_chunk<BF16, true, KC>(no, dout, off, nv);
+  };
   auto load_r = [&](int64_t tile_base) {
     const int64_t tc = tile_base + g * KC;
     const int64_t nv = s.L - tc;
@@ -478,7 +507,10 @@ __global__ void __launch_bounds__(kLanes* NG)
     // prefetch the previous tile's inputs and checkpoint, warm its B/C lines
     float hraw[NPW + 1];
     if (more) {
-      load_r(tb - T);
+      if constexpr (kStageOut)
+        load_r_staged(tb - T);
+      else
+        load_r(tb - T);
       load_checkpoint(ti - 1, hraw);
     }
     const uint32_t touch = more ? warm_tile<WPS>(bcw, ti - 1) : 0u;
@@ -591,49 +623,65 @@ __global__ void __launch_bounds__(kLanes* NG)
         dDacc = fmaf(cDy[q], cU[q], dDacc);
         dbacc += q < nv ? ddl : 0.0f;
       }
-      // the prefetched inputs and checkpoint are consumed before the stores:
-      // the counter a load's wait reads also counts stores issued after it
-      if (more) {
-        prep_r(tb - T);
-        finish_checkpoint(hraw, hck);
-      }
       if constexpr (kStageOut) {
-        // The tile's du, ddelta, dz leave through LDS (the reduction blocks
-        // are free: the tile's sums were taken before the barrier above).
-        // Each wave stages its 4 steps of every channel, one 8-byte piece per
-        // tensor in a 40-byte row per channel; after a barrier wave g stores
-        // channels 16 g .. 16 g + 15 over the tile's 16 steps (lane l:
-        // channel 16 g + l / 4, steps 4 (l mod 4) ..), so a store
-        // instruction writes 16 rows of 32 contiguous bytes rather than 8
-        // bytes of each of 64 rows.
-        char* const stg = reinterpret_cast<char*>(&sm.red[0][0][0]);
+        // The tile's du, ddelta, dz leave through LDS, and the next tile's
+        // inputs arrive through it (the reduction blocks are free: the tile's
+        // sums were taken before the barrier above).  Each wave stages its 4
+        // steps of every channel; after a barrier wave g stores (and has
+        // loaded) channels 16 g .. 16 g + 15 over the tile's 16 steps, so a
+        // memory instruction moves 16 rows of 32 contiguous bytes rather than
+        // 8 bytes of each of 64 rows.
         auto put = [&](int tt, const float (&o)[KC]) {
-          *reinterpret_cast<uint2*>(stg + (tt * kLanes + lane) * kStgPitch + g * 8) =
-              make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+          *stg_at(tt, lane, g) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
         };
         put(0, odu);
         put(1, odd);
         if constexpr (HAS_Z) put(2, odz);
+        if (more) {
+          *stg_at(3, c_st, q_st) = make_uint2(nu.w[0], nu.w[1]);
+          *stg_at(4, c_st, q_st) = make_uint2(nd.w[0], nd.w[1]);
+          if constexpr (HAS_Z) *stg_at(5, c_st, q_st) = make_uint2(nz.w[0], nz.w[1]);
+          *stg_at(6, c_st, q_st) = make_uint2(no.w[0], no.w[1]);
+        }
         __syncthreads();
-        const int c = (kLanes / NG) * g + (lane >> 2);
-        const int q = lane & 3;
-        const int64_t d_o = (int64_t)(k.gi % s.groups_per_batch) * kLanes + c;
-        const int64_t t_o = tb + 4 * q;
-        if (d_o < s.dim && t_o < s.L) {
-          const int64_t off = ((int64_t)k.b * s.dim + d_o) * s.L + t_o;
+        if (more) {
+          uint2 v = *stg_at(3, lane, g);
+          nu.w[0] = v.x; nu.w[1] = v.y;
+          v = *stg_at(4, lane, g);
+          nd.w[0] = v.x; nd.w[1] = v.y;
+          if constexpr (HAS_Z) {
+            v = *stg_at(5, lane, g);
+            nz.w[0] = v.x; nz.w[1] = v.y;
+          }
+          v = *stg_at(6, lane, g);
+          no.w[0] = v.x; no.w[1] = v.y;
+          prep_r(tb - T);
+          finish_checkpoint(hraw, hck);
+        }
+        const int64_t t_o = tb + 4 * q_st;
+        if (d_st < s.dim && t_o < s.L) {
+          const int64_t off = row_st * s.L + t_o;
           auto st = [&](void* base, int tt) {
-            *reinterpret_cast<uint2*>(static_cast<char*>(base) + off * 2) =
-                *reinterpret_cast<const uint2*>(stg + (tt * kLanes + c) * kStgPitch + q * 8);
+            *reinterpret_cast<uint2*>(static_cast<char*>(base) + off * 2) = *stg_at(tt, c_st, q_st);
           };
           st(du, 0);
           st(ddelta, 1);
           if constexpr (HAS_Z) st(dz, 2);
         }
-      } else if (k.valid) {
+      } else {
+        // the prefetched inputs and checkpoint are consumed before the
+        // stores: the counter a load's wait reads also counts stores issued
+        // after it
+        if (more) {
+          prep_r(tb - T);
+          finish_checkpoint(hraw, hck);
+        }
+        if (k.valid) {
         const int64_t off = k.rowoff + tc * s.ts;
         store_chunk<BF16, VEC, KC>(du, off, odu, nv, s.ts);
         store_chunk<BF16, VEC, KC>(ddelta, off, odd, nv, s.ts);
         if constexpr (HAS_Z) store_chunk<BF16, VEC, KC>(dz, off, odz, nv, s.ts);
+        }
       }
     }
     asm volatile("" ::"s"(touch));  // keeps the warming loads
