@@ -188,6 +188,50 @@ __global__ void __launch_bounds__(kLanes* NG)
 
   Raw<BF16, KC> ru, rd, rz, ro;
   raw_zero(rz);
+  // N = 16 with bf16 rows: the next tile's inputs are read by channel runs
+  // (lane l of wave g: channel 16 g + l / 4 of the group, steps 4 (l mod 4)
+  // .., so a load moves 16 rows of 32 contiguous bytes rather than 8 bytes of
+  // each of 64 rows) and meet the lanes that own their channels in LDS; the
+  // staging rows hold a channel's 16 steps as four 8-byte pieces, piece p at
+  // slot p ^ ((channel / 8) mod 4), free of bank conflicts both ways.
+  constexpr bool kStageIn = VEC && BF16 && NG == 4 && KC == 4;
+  __shared__ __align__(16) char s_stg[kStageIn ? 4 * kLanes * 32 : 16];
+  const int c_st = (kLanes / NG) * g + (lane >> 2);
+  const int q_st = lane & 3;
+  const int64_t d_st = (int64_t)(k.gi % s.groups_per_batch) * kLanes + c_st;
+  const int64_t row_st = k.b * s.dim + (d_st < s.dim ? d_st : s.dim - 1);
+  auto stg_at = [&](int tt, int c, int piece) -> uint2* {
+    return reinterpret_cast<uint2*>(s_stg + (tt * kLanes + c) * 32 + 8 * (piece ^ ((c >> 3) & 3)));
+  };
+  auto load_staged = [&](int tile) {
+    const int64_t t = (int64_t)tile * T + 4 * q_st;
+    const int64_t nv = s.L - t;
+    const int64_t off = row_st * s.L + t;
+    load_chunk<BF16, true, KC>(ru, u, off, nv);
+    load_chunk<BF16, true, KC>(rd, delta, off, nv);
+    if constexpr (HAS_Z) load_chunk<BF16, true, KC>(rz, z, off, nv);
+    load_chunk<BF16, true, KC>(ro, dout, off, nv);
+  };
+  // hand the staged pieces to their lanes (every wave, behind one barrier)
+  auto unstage = [&]() {
+    if constexpr (kStageIn) {
+      *stg_at(0, c_st, q_st) = make_uint2(ru.w[0], ru.w[1]);
+      *stg_at(1, c_st, q_st) = make_uint2(rd.w[0], rd.w[1]);
+      if constexpr (HAS_Z) *stg_at(2, c_st, q_st) = make_uint2(rz.w[0], rz.w[1]);
+      *stg_at(3, c_st, q_st) = make_uint2(ro.w[0], ro.w[1]);
+      __syncthreads();
+      uint2 v = *stg_at(0, lane, g);
+      ru.w[0] = v.x; ru.w[1] = v.y;
+      v = *stg_at(1, lane, g);
+      rd.w[0] = v.x; rd.w[1] = v.y;
+      if constexpr (HAS_Z) {
+        v = *stg_at(2, lane, g);
+        rz.w[0] = v.x; rz.w[1] = v.y;
+      }
+      v = *stg_at(3, lane, g);
+      ro.w[0] = v.x; ro.w[1] = v.y;
+    }
+  };
   // Time indices are 32-bit (the host keeps L below 2^31 - 64).  On the
   // vector path with chunks of at most 8 steps (L a multiple of 8, so
   // L >= KC) each lane keeps pointers to its own rows and a chunk's start is
@@ -255,7 +299,12 @@ __global__ void __launch_bounds__(kLanes* NG)
   for (int ti = k.tile_begin; ti < k.tile_end; ++ti) {
     const int cur = (ti - k.tile_begin) & 1;
     const bool more = ti + 1 < k.tile_end;
-    if (more) load(ti + 1);
+    if (more) {
+      if constexpr (kStageIn)
+        load_staged(ti + 1);
+      else
+        load(ti + 1);
+    }
     const uint32_t touch = more ? warm_tile<WPS>(bcw, ti + 1) : 0u;
 #pragma unroll
     for (int j = 0; j < NPW; ++j) ck[((int64_t)ti * N + n0 + j) * kLanes + lane] = h[j];
@@ -279,7 +328,10 @@ __global__ void __launch_bounds__(kLanes* NG)
     // the tile's sum of Delta, the waves' chunk sums in wave order
 #pragma unroll
     for (int w = 0; w < NG; ++w) cum += s_ds[cur][w][lane];
-    if (more) prep(ti + 1, cur ^ 1);
+    if (more) {
+      if constexpr (kStageIn) unstage();
+      prep(ti + 1, cur ^ 1);
+    }
     asm volatile("" ::"s"(touch));  // keeps the warming loads
     __syncthreads();
   }
