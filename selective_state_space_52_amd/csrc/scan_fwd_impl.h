@@ -44,7 +44,6 @@ namespace mssm {
 namespace fwd {
 
 constexpr int kTile = 32;  // timesteps per tile
-constexpr bool kWarmScalarCache = true;
 
 // Waves per 64-channel workgroup: two states per wave up to N = 16 (one for
 // N = 1), so a group of N = 16 runs 8 waves, two per SIMD; larger states keep
@@ -172,7 +171,7 @@ __device__ __forceinline__ void store_quads(char* q, const int64_t (&off)[KC / 4
 // batch's B/C scalar loads and Delta/Delta*u LDS reads are issued, and the
 // rest of the batch computes while they are in flight.
 template <int N, int NG, bool BF16, int LD, bool HAS_Z, bool AGG, bool SOFTPLUS,
-          bool CONV>
+          bool CONV, bool WARM>
 __device__ __forceinline__ void scan_body(
     const void* __restrict__ u, const void* __restrict__ delta,
     const void* __restrict__ z, const float* __restrict__ A,
@@ -592,9 +591,13 @@ __device__ __forceinline__ void scan_body(
     // Warm the scalar cache with the next tile's B/C run: one dword per
     // 64-byte line.  Scalar loads can only be waited on all together, so they
     // are issued here, where the first wait (the output phase's LDS reads)
-    // comes after the whole prep phase.
+    // comes after the whole prep phase.  WARM: plans whose groups all run
+    // whole (one workgroup per CU) gain from it; with rows cut in time (two
+    // workgroups per CU) it cost time, and so did a branch around it or the
+    // same loads aimed at lines already cached, so the host picks a kernel
+    // built with or without it.
     uint32_t touch = 0u;
-    if (kWarmScalarCache) {
+    if constexpr (WARM) {
       // clamped to the row's steps in 32-bit arithmetic (L < 2^31 - 64): a
       // 64-bit clamp on word indices has no scalar compare and went to the VALU
       const int left = (int)s.L - (tb + T);  // steps of the next tile in the row
@@ -755,7 +758,7 @@ __device__ __forceinline__ void scan_body(
 // The work plan counts on two workgroups per CU (16 waves, 4 per SIMD), so
 // the kernel is held to 128 VGPRs.  At N = 128 that moves a few values of the
 // fp64 fold in the prologue to scratch, once per task; the tile loop fits.
-template <int N, int NG, bool BF16, int LD, bool HAS_Z, bool SOFTPLUS, bool CONV>
+template <int N, int NG, bool BF16, int LD, bool HAS_Z, bool SOFTPLUS, bool CONV, bool WARM>
 __global__ void __launch_bounds__(kLanes* NG) __attribute__((amdgpu_waves_per_eu(4)))
     scan_kernel(const void* __restrict__ u, const void* __restrict__ delta,
                 const void* __restrict__ z, const float* __restrict__ A,
@@ -771,11 +774,11 @@ __global__ void __launch_bounds__(kLanes* NG) __attribute__((amdgpu_waves_per_eu
   const int blk = blockIdx.x;
   const int a = blk - s.whole_groups;  // aggregate task, when in [0, n_agg)
   if (a >= 0 && a < n_agg)
-    scan_body<N, NG, BF16, LD, HAS_Z, true, SOFTPLUS, CONV>(
+    scan_body<N, NG, BF16, LD, HAS_Z, true, SOFTPLUS, CONV, WARM>(
         u, delta, z, A, Dv, bias, out, last_state, ws_S, ws_sum, ws_h0, ws_flags, bcp,
         s, s_dw, s_y, a, cv);
   else
-    scan_body<N, NG, BF16, LD, HAS_Z, false, SOFTPLUS, CONV>(
+    scan_body<N, NG, BF16, LD, HAS_Z, false, SOFTPLUS, CONV, WARM>(
         u, delta, z, A, Dv, bias, out, last_state, ws_S, ws_sum, ws_h0, ws_flags, bcp,
         s, s_dw, s_y, a < 0 ? blk : blk - n_agg, cv);
 }
@@ -786,16 +789,25 @@ hipError_t launch_one(const ScanParams& p, const ScanShape& s, int n_main, int n
                       hipStream_t stream) {
   const dim3 grid(n_main + n_agg), block(kLanes * NG);
   const ConvArgs cv{p.conv_w, p.conv_b, p.conv_init, p.u_out};
-  if (p.softplus)
-    hipLaunchKernelGGL((scan_kernel<N, NG, BF16, LD, HAS_Z, true, CONV>), grid, block,
-                       0, stream, p.u, p.delta, p.z, p.A, p.D, p.bias, p.out,
-                       p.last_state, p.ws_S, p.ws_sum, p.ws_h0, p.ws_flags,
-                       (const uint32_t*)p.ws_bc, s, n_agg, cv);
-  else
-    hipLaunchKernelGGL((scan_kernel<N, NG, BF16, LD, HAS_Z, false, CONV>), grid, block,
-                       0, stream, p.u, p.delta, p.z, p.A, p.D, p.bias, p.out,
-                       p.last_state, p.ws_S, p.ws_sum, p.ws_h0, p.ws_flags,
-                       (const uint32_t*)p.ws_bc, s, n_agg, cv);
+  // the scalar-cache warming pays only when no group is cut in time
+  const bool warm = p.split_groups == 0;
+#define MSSM_SCAN_LAUNCH(SP, WM)                                                            \
+  hipLaunchKernelGGL((scan_kernel<N, NG, BF16, LD, HAS_Z, SP, CONV, WM>), grid, block, 0,  \
+                     stream, p.u, p.delta, p.z, p.A, p.D, p.bias, p.out, p.last_state,     \
+                     p.ws_S, p.ws_sum, p.ws_h0, p.ws_flags, (const uint32_t*)p.ws_bc, s,   \
+                     n_agg, cv)
+  if (p.softplus) {
+    if (warm)
+      MSSM_SCAN_LAUNCH(true, true);
+    else
+      MSSM_SCAN_LAUNCH(true, false);
+  } else {
+    if (warm)
+      MSSM_SCAN_LAUNCH(false, true);
+    else
+      MSSM_SCAN_LAUNCH(false, false);
+  }
+#undef MSSM_SCAN_LAUNCH
   return hipGetLastError();
 }
 
