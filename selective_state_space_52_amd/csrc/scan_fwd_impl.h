@@ -9,8 +9,9 @@
 //   out_t   = (sum_n C_t[n] h_t[n] + D[d] u_t) * silu(z_t)
 //
 // Mapping onto the chip.  The scan is not a dense contraction and is bound by
-// the vector ALU (one v_exp_f32 per state element, which issues at half rate,
-// plus four fp32 mul/fma), so the layout minimises issued VALU instructions:
+// the vector ALU (one v_exp_f32 per state element, which holds the VALU three to
+// four times as long as an fma, plus four fp32 mul/fma), so the layout minimises
+// issued VALU instructions:
 //   * one lane per channel: 64 channels of one batch entry per workgroup, so
 //     B_t and C_t are the same for every lane -- they are read with scalar
 //     loads into SGPRs and cost no vector instructions or LDS traffic;
