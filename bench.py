@@ -409,13 +409,14 @@ def probe_rates(torch, m, dev, waves_per_cu, iters=4096, reps=10):
     at `waves_per_cu` resident waves per CU: fp32 fma (kind 0), v_exp_f32
     (kind 1), state elements of the scan's inner-step mix (kind 2) and state
     elements of the same recurrence as an in-wave associative scan over 64
-    timesteps (kind 3)."""
+    timesteps (kind 3), and iterations of 8 fma plus 2 exp on independent
+    chains (kind 4)."""
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     blocks = cus * waves_per_cu // 4        # 256-thread workgroups: 4 waves
     threads = blocks * 256
     sink = torch.empty(threads, device=dev)
     rates = {}
-    for kind, per_iter in ((0, 8), (1, 8), (2, 4), (3, 4)):
+    for kind, per_iter in ((0, 8), (1, 8), (2, 4), (3, 4), (4, 1)):
         for _ in range(2):
             m.valu_probe(kind, blocks, iters, sink)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -450,7 +451,13 @@ def alu_probe(torch, m, dev, s=None, nbytes=None, kernel_ms=None, sweep=(16, 32)
             "fma_T_per_s": round(r[0] / 1e12, 3), "exp_T_per_s": round(r[1] / 1e12, 3),
             "state_element_mix_T_per_s": round(r[2] / 1e12, 3),
             "fma_slots_per_state_element": round(r[0] / r[2], 3),
-            "wave_scan_state_elements_T_per_s": round(r[3] / 1e12, 3)}
+            "wave_scan_state_elements_T_per_s": round(r[3] / 1e12, 3),
+            # 8 fma + 2 exp on independent chains: time per iteration against
+            # the two kinds' own times added (1: no overlap) and against the
+            # longer of the two (the fraction of the shorter one hidden)
+            "fma_exp_mix_time_vs_sum": round((1 / r[4]) / (8 / r[0] + 2 / r[1]), 3),
+            "fma_exp_overlap_frac": round(((8 / r[0] + 2 / r[1]) - 1 / r[4]) /
+                                          min(8 / r[0], 2 / r[1]), 3)}
     clock = shader_clock_mhz()
     res["shader_clock_mhz"] = clock
     if clock:

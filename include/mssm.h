@@ -457,10 +457,13 @@ int mssm_set_scan_timing_events(void* start, void* stop);
  *           associative scan of (exp(Delta A), Delta u B) pairs across the
  *           wave's 64 lanes (one timestep per lane: six DPP levels), then the
  *           chunk's entering state and the readout,
+ *   kind 4: 8 independent fp32 fma and 2 independent exponentials (no value
+ *           passes between the two kinds), to see whether the exponentials
+ *           overlap the fma work,
  * and writes one float per thread to `sink` (device, blocks * 256 floats,
  * caller-owned; the values carry no meaning).  The caller times the launch
  * (for instance with events on `stream`).  Errors: MSSM_ERR_NULL (sink),
- * MSSM_ERR_DIMS (kind outside 0..3, blocks or iters <= 0), MSSM_ERR_HIP.
+ * MSSM_ERR_DIMS (kind outside 0..4, blocks or iters <= 0), MSSM_ERR_HIP.
  */
 int mssm_valu_probe(int kind, int blocks, int iters, float* sink, void* stream);
 

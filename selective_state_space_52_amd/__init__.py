@@ -43,7 +43,8 @@ def set_scan_timing_events(start=None, stop=None) -> None:
 def valu_probe(kind: int, blocks: int, iters: int, sink) -> None:
     """Launch the library's ALU issue-rate probe on the current stream: kind
     0 = fp32 fma, 1 = exp, 2 = the scan's state-element mix, 3 = the same
-    recurrence as an in-wave associative scan; `sink` is a
+    recurrence as an in-wave associative scan, 4 = 8 fma and 2 exp on
+    independent chains (their overlap); `sink` is a
     float32 device tensor of at least blocks * 256 values."""
     _need(sink, "sink", torch.float32)
     if sink.numel() < blocks * 256:

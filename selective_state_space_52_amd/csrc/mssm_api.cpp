@@ -212,7 +212,7 @@ int mssm_set_scan_timing_events(void* start, void* stop) {
 
 int mssm_valu_probe(int kind, int blocks, int iters, float* sink, void* stream) {
   if (sink == nullptr) return MSSM_ERR_NULL;
-  if (blocks <= 0 || iters <= 0 || kind < 0 || kind > 3) return MSSM_ERR_DIMS;
+  if (blocks <= 0 || iters <= 0 || kind < 0 || kind > 4) return MSSM_ERR_DIMS;
   const hipError_t e =
       mssm::launch_valu_probe(kind, blocks, iters, sink, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {

@@ -14,6 +14,10 @@
 //           associative scan of (decay, drive) pairs over the wave's 64 lanes
 //           (one timestep per lane, six DPP levels), the chunk carry and the
 //           readout (see below);
+//   kind 4: 8 v_fma_f32 and 2 v_exp_f32 per iteration on independent chains
+//           (no value passes between the fma and the exp chains), so that its
+//           rate against kinds 0 and 1 shows whether the exponentials overlap
+//           the multiply-adds or take their issue slots;
 //   kind 2: the state-element mix, 4 state elements per iteration, each
 //           v_mul (Delta A) + v_exp + v_mul (Delta u B) + v_fma (state) +
 //           a readout multiply-add (the first a v_mul), plus one v_mul that
@@ -67,6 +71,22 @@ __global__ void __launch_bounds__(256) valu_probe_kernel(float* __restrict__ sin
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) r += c[j];
+  } else if constexpr (KIND == 4) {
+    float c[8], x[2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = s0 + (float)j;
+    x[0] = s0;
+    x[1] = s0 + 0.5f;
+#pragma unroll 4
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) x[j] = hw_exp2(-fabsf(x[j]));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = fmaf(c[j], 0.999f, 1e-3f);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r += c[j];
+    r += x[0] + x[1];
   } else if constexpr (KIND == 3) {
     // The same recurrence as an inclusive associative scan over a wave's 64
     // timesteps (lane = timestep), per state: a = exp(Delta A), b = Delta u B,
@@ -142,7 +162,8 @@ hipError_t launch_valu_probe(int kind, int blocks, int iters, float* sink,
     case 0: hipLaunchKernelGGL(valu_probe_kernel<0>, grid, block, 0, stream, sink, iters, 0.5f); break;
     case 1: hipLaunchKernelGGL(valu_probe_kernel<1>, grid, block, 0, stream, sink, iters, 0.5f); break;
     case 2: hipLaunchKernelGGL(valu_probe_kernel<2>, grid, block, 0, stream, sink, iters, 0.5f); break;
-    default: hipLaunchKernelGGL(valu_probe_kernel<3>, grid, block, 0, stream, sink, iters, 0.5f); break;
+    case 3: hipLaunchKernelGGL(valu_probe_kernel<3>, grid, block, 0, stream, sink, iters, 0.5f); break;
+    default: hipLaunchKernelGGL(valu_probe_kernel<4>, grid, block, 0, stream, sink, iters, 0.5f); break;
   }
   return hipGetLastError();
 }

@@ -370,7 +370,7 @@ def test_valu_probe_validation_codes(L):
     launching anything."""
     p = _ptrs(1)
     assert L.mssm_valu_probe(0, 8, 64, None, None) == -1
-    for kind, blocks, iters in ((4, 8, 64), (-1, 8, 64), (0, 0, 64), (2, 8, 0)):
+    for kind, blocks, iters in ((5, 8, 64), (-1, 8, 64), (0, 0, 64), (2, 8, 0)):
         assert L.mssm_valu_probe(kind, blocks, iters, p[0], None) == -2
 
 
