@@ -933,7 +933,7 @@ def copy_ceiling(torch, dev):
 
 
 def shader_clock_mhz():
-    """The shader clock level the driver reports as current (sysfs
+    """The shader clock level the amdgpu kernel module reports as current (sysfs
     pp_dpm_sclk), read right after the headline timing, or None."""
     for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
         try:
